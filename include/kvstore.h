@@ -1,0 +1,264 @@
+/*
+ * kvstore.h -- C ABI of the paged KV context store hot path for MI355X (gfx950).
+ *
+ * What it implements is defined by the NInfer maintainer pages
+ * ("Paged KV Context Store", "Engine Architecture", "Resource Scheduling and
+ * Context Cache").  Their headings were lost in extraction, so each entry point
+ * names the passage it follows by what that passage holds.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Every call returns kv_status.  KV_OK is success.  No C++ exception crosses
+ *   this boundary; kv_last_error_message() gives a human-readable detail for
+ *   the last failure on the calling thread.
+ * - A capacity shortfall is a status plus a deficit out-parameter, never an
+ *   exception (Paged KV Context Store page, invariant list: a shortfall does
+ *   not leave a step through an exception).
+ * - Device memory is caller-owned: plane tensors, the block-table matrix,
+ *   inputs, outputs and workspaces.  Their base addresses must stay valid and
+ *   stable for the pool's lifetime (graph-stable bases passage).  The pool owns
+ *   only host metadata (free list, references, generations, address spaces and
+ *   a host mirror of the block table).
+ * - All device work is enqueued on the caller's hipStream_t, in call order.
+ *   Nothing here synchronizes the device except kv_pool_destroy.
+ * - Pointers named d_* are device pointers; all others are host pointers.
+ * - Errors KV_E_DEVICE mean a HIP runtime call failed: treat it as an
+ *   engine-wide failure (Engine Architecture page, error classes).
+ */
+#ifndef KVSTORE_H
+#define KVSTORE_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ------------------------------------------------------------ status codes */
+typedef int32_t kv_status;
+#define KV_OK             0  /* success */
+#define KV_E_INVALID      1  /* bad argument, null pointer, unknown handle use */
+#define KV_E_GEOMETRY     2  /* geometry rejected: P != 64, C not in [1,8], M outside
+                                [max(L,C), C*L], head_dim/group mismatch, B > C, Hq % H != 0 */
+#define KV_E_CAPACITY     3  /* not enough free page groups; the deficit is reported */
+#define KV_E_STALE        4  /* sequence handle generation does not match (released) */
+#define KV_E_SHARED_WRITE 5  /* write domain touches a page with several references:
+                                copy the tail first (kv_cow_tail_page) */
+#define KV_E_UNMAPPED     6  /* commit beyond the mapped pages */
+#define KV_E_DEVICE       7  /* a HIP runtime call failed */
+#define KV_E_UNSUPPORTED  8  /* valid request this build has no kernel for */
+
+/* ------------------------------------------------ closed profiles / planes */
+/* Closed KV profiles (Paged KV Context Store page, closed-profile paragraph).
+ * K8V4 is closed and asymmetric: K = FP8-E4M3FN-row256, V = NVFP4-G16. */
+#define KV_PROFILE_BF16              0
+#define KV_PROFILE_INT8_G64          1
+#define KV_PROFILE_FP8_E4M3FN_ROW256 2
+#define KV_PROFILE_NVFP4_G16         3
+#define KV_PROFILE_K8V4              4
+
+/* Plane element types. */
+#define KV_DT_BF16     0  /* 2 bytes, stored unchanged from the bf16 input */
+#define KV_DT_I8       1  /* INT8-G64 codes */
+#define KV_DT_E4M3FN   2  /* FP8 E4M3FN codes (OCP, bias 7, saturating at +-448) */
+#define KV_DT_E2M1X2   3  /* two FP4 E2M1 codes per byte, element 2k in the low nibble */
+#define KV_DT_F32      4  /* fp32 scales (INT8-G64 per 64 elements, FP8-row per row) */
+#define KV_DT_U8_E4M3  5  /* NVFP4-G16 scales: one E4M3FN byte per 16 elements */
+
+/* Plane roles; the K and V code planes and scale planes of one layer share a
+ * page-group id (plane-grouping rule). */
+#define KV_ROLE_K_CODE  0
+#define KV_ROLE_K_SCALE 1
+#define KV_ROLE_V_CODE  2
+#define KV_ROLE_V_SCALE 3
+
+/* Expanded pool geometry (capacity-geometry equations):
+ *   L = ceil(max_context / page_size), valid M in [max(L, C), C * L]. */
+typedef struct KVPageGeometry {
+    uint32_t page_size;        /* P; must be 64 */
+    uint32_t num_kv_heads;     /* H */
+    uint32_t head_dim;         /* D; 64, 128 or 256 */
+    uint32_t num_layers;       /* layers whose planes share the page-group id */
+    uint32_t max_context;      /* S */
+    uint32_t max_concurrency;  /* C, 1..8: block-table rows */
+    uint32_t num_page_groups;  /* M */
+} KVPageGeometry;
+
+/* One plane of the page-major closed order [X, P, H, N] (first extent
+ * fastest), i.e. C-order [M][H][64][X]; element (x, o, h, g) lives at
+ * base + elem_bytes * (x + X * (o + 64 * (h + H * g)))  (address-translation
+ * equations with contiguous strides).  base is caller-owned device memory of
+ * M * H * 64 * X * elem_bytes bytes, 256-byte aligned. */
+typedef struct KVPlaneDesc {
+    uint32_t layer;
+    uint32_t role;       /* KV_ROLE_* */
+    uint32_t dtype;      /* KV_DT_* */
+    uint32_t x_extent;   /* X: D for codes, D/2 packed FP4, D/64 INT8 scales, 1 FP8 row
+                            scale, D/16 NVFP4 scales (X-extent list) */
+    uint32_t elem_bytes; /* bytes per element of dtype */
+    uint32_t reserved;
+    void*    base;       /* device pointer, caller-owned */
+} KVPlaneDesc;
+
+typedef struct kv_pool kv_pool;   /* opaque host object */
+typedef uint64_t kv_seq;          /* generation-tagged address-space handle; 0 is never valid */
+
+/* Schema of one layer of a closed profile (PagedKVStorageLayout passage: a
+ * closed profile resolves to K/V data/scale planes).  Writes up to *n_inout
+ * descriptors (layer 0, base NULL) and sets *n_inout to the count (2 or 4).
+ * KV_E_INVALID if the buffer is too small; KV_E_GEOMETRY if head_dim is not a
+ * multiple of the profile's groups. */
+kv_status kv_profile_planes(uint32_t profile, uint32_t head_dim, KVPlaneDesc* out, uint32_t* n_inout);
+
+/* Bytes of one plane slab for a geometry: M * H * 64 * X * elem_bytes. */
+kv_status kv_plane_bytes(const KVPageGeometry* geo, const KVPlaneDesc* plane, uint64_t* bytes);
+
+/* Create a homogeneous pool (Paged KV Context Store page: homogeneous pools,
+ * capacity geometry, device block-table matrix).
+ *   planes / n_planes : num_layers copies of one profile's schema, bases set.
+ *   d_block_tables    : caller-owned int32 [C][L] device matrix; set to -1
+ *                       (unmapped) on `stream`.  NULL makes a host-only pool:
+ *                       metadata and host mirror only, no device work at all,
+ *                       kernels refuse it (used to test the allocator on CPU).
+ *   free_order        : optional permutation of [0, M): page groups are taken
+ *                       from the front of a FIFO in this order and freed ones
+ *                       are appended at the back in logical-block order.  NULL
+ *                       means 0, 1, ..., M-1.  Correctness never depends on it.
+ * KV_E_GEOMETRY / KV_E_INVALID on rejected input; *out is NULL then. */
+kv_status kv_pool_create(const KVPageGeometry* geo, const KVPlaneDesc* planes, uint32_t n_planes,
+                         int32_t* d_block_tables, const int32_t* free_order, hipStream_t stream,
+                         kv_pool** out);
+
+/* Synchronize the device and free the host object.  Device memory is the
+ * caller's to free afterwards.  NULL is ignored. */
+void kv_pool_destroy(kv_pool* pool);
+
+/* Lease accounting: allocated + reserved + available == M.  Reserved is
+ * always 0 here (no entitlement reservations in this build). */
+kv_status kv_pool_stats(const kv_pool* pool, uint32_t* allocated, uint32_t* reserved, uint32_t* available);
+
+/* Copy the host mirror of the block-table matrix, int32 [C][L], into out. */
+kv_status kv_pool_table_host(const kv_pool* pool, int32_t* out, size_t n_entries);
+
+/* References held on page group g by address spaces (0 when free). */
+kv_status kv_pool_page_refs(const kv_pool* pool, uint32_t page_group, uint32_t* refs);
+
+/* New empty address space leasing block-table row `table_row`
+ * (KVAddressSpace descriptor, execution-row lease).  The row is set to -1 on
+ * `stream`.  KV_E_INVALID if the row is out of range or already leased. */
+kv_status kv_seq_open(kv_pool* pool, uint32_t table_row, hipStream_t stream, kv_seq* out);
+
+/* Fork (Paged KV Context Store page, Fork passage and worked example): a new
+ * address space on `table_row` sharing src's pages covering [0, frontier),
+ * frontier <= src's committed frontier.  Full pages gain a reference; a
+ * partial tail is shared too and must be copied with kv_cow_tail_page before
+ * any write.  The frontier is kept exactly (not rounded down to a page).  The
+ * row's mapping is published on `stream`. */
+kv_status kv_seq_fork(kv_pool* pool, kv_seq src, uint32_t frontier, uint32_t table_row,
+                      hipStream_t stream, kv_seq* out);
+
+/* ensure_mapped_to_tokens: map page groups so that positions [0, tokens) are
+ * covered.  A lower bound: never trims, never moves the frontier.  Allocates
+ * only the missing pages (ordinary decode: one page at a page crossing) and
+ * publishes the new contiguous slice of the row on `stream` before any later
+ * kernel on that stream (mapping publication order).
+ *   *deficit : set to the missing page count on KV_E_CAPACITY, else 0.
+ * KV_E_CAPACITY: nothing is allocated.  KV_E_SHARED_WRITE: the write domain
+ * [frontier, tokens) starts inside a shared partial tail (writer-cardinality
+ * rules).  KV_E_INVALID: tokens > max_context. */
+kv_status kv_seq_ensure_mapped(kv_pool* pool, kv_seq seq, uint32_t tokens, uint32_t* deficit,
+                               hipStream_t stream);
+
+/* Advance the committed frontier after the unit that wrote [old, frontier)
+ * has been enqueued (frontier commit happens at the GPU boundary).
+ * KV_E_INVALID if frontier < current; KV_E_UNMAPPED if beyond the mapping. */
+kv_status kv_seq_commit(kv_pool* pool, kv_seq seq, uint32_t frontier);
+
+/* Finish / release: drop this address space's page references (a page is
+ * freed on its last one), release its table row (set to -1 on `stream`) and
+ * retire the handle (later use returns KV_E_STALE). */
+kv_status kv_seq_release(kv_pool* pool, kv_seq seq, hipStream_t stream);
+
+/* Row, committed frontier and mapped page count of a live address space. */
+kv_status kv_seq_info(const kv_pool* pool, kv_seq seq, uint32_t* table_row, uint32_t* frontier,
+                      uint32_t* mapped_pages);
+
+/* Partial-tail COW (Fork passage: copy the tail's committed columns into a
+ * private page; Engine Architecture page: restore, tail COW and mapping
+ * upload go in order on one stream).  If the committed frontier F is not
+ * page-aligned and its tail page is shared: allocate g', copy columns
+ * [0, F mod 64) of every plane of every layer from g to g', rebind the row's
+ * entry to g' and drop the reference on g -- copy and rebind on `stream`.
+ * A no-op (KV_OK) when F is aligned or the tail is already private.
+ * KV_E_CAPACITY (deficit 1) when no page group is free. */
+kv_status kv_cow_tail_page(kv_pool* pool, kv_seq seq, hipStream_t stream);
+
+/* Persistent KV codec: quantize and write new K/V rows at their positions
+ * (Paged KV Context Store page: closed profiles, X-extent list, P=64
+ * translation; the codec header itself is not on the pages -- rounding rules:
+ * fp32 arithmetic, round half to even, saturating FP8/FP4, zero scale gives
+ * zero codes).
+ *   B                : compact batch entries; entry b uses table row
+ *                      d_table_rows[b] (PagedKVBatchLayerView: batch order,
+ *                      lane and table row may all differ).
+ *   d_pos0[B]        : position of each entry's first new row.
+ *   d_cu_tokens[B+1] : rows of entry b are [cu[b], cu[b+1]) of the inputs.
+ *   d_k, d_v         : bf16 [total_tokens][H][D], contiguous.
+ * Does not move any frontier.  Caller guarantees (wrapper validation and
+ * caller guarantees passage): every written block is mapped in a private
+ * page, rows are stable until the unit completes.  Rows whose table entry is
+ * -1 are skipped.  KV_E_GEOMETRY if B > C. */
+kv_status kv_append(const kv_pool* pool, uint32_t layer, uint32_t B, const int32_t* d_table_rows,
+                    const int32_t* d_pos0, const int32_t* d_cu_tokens, uint32_t total_tokens,
+                    const void* d_k, const void* d_v, hipStream_t stream);
+
+/* Workspace bytes paged_attn_decode / paged_attn_verify need for these bounds
+ * (split-K partials plus per-item bookkeeping).  max_q_len 0 means decode. */
+size_t paged_attn_workspace_bytes(const kv_pool* pool, uint32_t B, uint32_t Hq, uint32_t max_seq_len,
+                                  uint32_t max_q_len);
+
+/* Paged decode for a compact batch of 1..C sequences (Paged KV Context Store
+ * page: PagedKVBatchLayerView, P=64 translation, consumer rules).  Entry b's
+ * query (the step's last token, already appended) attends positions
+ * [0, d_seq_lens[b]) of table row d_table_rows[b]:
+ *     out[b][j] = sum_i softmax_i(q[b][j] . k_i * sm_scale) v_i,
+ *     KV head of query head j = j / (Hq / H).
+ * Pages are read through the block table, a page at a time; split-K over
+ * pages with a deterministic cross-split combine, so results do not depend
+ * on physical page ids.  seq_len 0 yields zeros.
+ *   d_q   : bf16 [B][Hq][D];  d_out: fp32 [B][Hq][D].
+ *   max_seq_len : host upper bound of d_seq_lens (sizes the split grid).
+ *   d_ws / ws_bytes : >= paged_attn_workspace_bytes(pool, B, Hq, max_seq_len, 0).
+ * KV_E_GEOMETRY on B > C or Hq % H != 0; KV_E_UNSUPPORTED for shapes with no
+ * kernel instance (see paged_attn_supported). */
+kv_status paged_attn_decode(const kv_pool* pool, uint32_t layer, uint32_t B, uint32_t Hq,
+                            const int32_t* d_table_rows, const int32_t* d_seq_lens, uint32_t max_seq_len,
+                            const void* d_q, float sm_scale, float* d_out, void* d_ws, size_t ws_bytes,
+                            hipStream_t stream);
+
+/* Multi-token verify / chunked prefill on paged KV (causal): chunk token i of
+ * entry b sits at position d_q_pos0[b] + i and attends [0, d_q_pos0[b] + i]
+ * (the chunk's own K/V are appended first; the mask starts at any in-page
+ * frontier).  Work is AttentionPairs = n0*T + T(T+1)/2 per head (Resource
+ * Scheduling page, prefill-work equation).  QK^T and PV run on MFMA.
+ *   d_cu_q[B+1] : rows of entry b are [cu[b], cu[b+1]) of d_q / d_out.
+ *   d_q   : bf16 [total_q][Hq][D];  d_out: fp32 [total_q][Hq][D].
+ *   max_q_len, max_seq_len : host upper bounds (max T, max n0 + T).
+ * Profiles: BF16 only in this build (KV_E_UNSUPPORTED otherwise). */
+kv_status paged_attn_verify(const kv_pool* pool, uint32_t layer, uint32_t B, uint32_t Hq,
+                            const int32_t* d_table_rows, const int32_t* d_q_pos0, const int32_t* d_cu_q,
+                            uint32_t total_q, uint32_t max_q_len, uint32_t max_seq_len, const void* d_q,
+                            float sm_scale, float* d_out, void* d_ws, size_t ws_bytes, hipStream_t stream);
+
+/* 1 if decode (max_q_len == 0) or verify has a kernel for this pool and Hq. */
+int paged_attn_supported(const kv_pool* pool, uint32_t Hq, uint32_t max_q_len);
+
+/* Detail of the last non-OK status on the calling thread ("" if none). */
+const char* kv_last_error_message(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* KVSTORE_H */

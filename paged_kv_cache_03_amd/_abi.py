@@ -1,0 +1,216 @@
+"""ctypes binding of libkvstore (include/kvstore.h): same names, marshalling only.
+
+Every function here forwards to the C entry point of the same name.  A status
+other than KV_OK raises KVError carrying the status, the library's message and,
+for a capacity shortfall, the deficit.  The library must be built
+(``python -m paged_kv_cache_03_amd.build_lib``); loading fails loudly if not.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libkvstore.so")
+
+KV_OK, KV_E_INVALID, KV_E_GEOMETRY, KV_E_CAPACITY = 0, 1, 2, 3
+KV_E_STALE, KV_E_SHARED_WRITE, KV_E_UNMAPPED, KV_E_DEVICE, KV_E_UNSUPPORTED = 4, 5, 6, 7, 8
+STATUS_NAMES = {0: "OK", 1: "INVALID", 2: "GEOMETRY", 3: "CAPACITY", 4: "STALE", 5: "SHARED_WRITE",
+                6: "UNMAPPED", 7: "DEVICE", 8: "UNSUPPORTED"}
+
+KV_PROFILE = {"BF16": 0, "INT8_G64": 1, "FP8_E4M3FN_ROW256": 2, "NVFP4_G16": 3, "K8V4": 4}
+KV_DT_BF16, KV_DT_I8, KV_DT_E4M3FN, KV_DT_E2M1X2, KV_DT_F32, KV_DT_U8_E4M3 = range(6)
+KV_ROLE_K_CODE, KV_ROLE_K_SCALE, KV_ROLE_V_CODE, KV_ROLE_V_SCALE = range(4)
+
+# exported symbols, in header order (the CPU test checks the header declares exactly these)
+EXPORTS = ["kv_profile_planes", "kv_plane_bytes", "kv_pool_create", "kv_pool_destroy", "kv_pool_stats",
+           "kv_pool_table_host", "kv_pool_page_refs", "kv_seq_open", "kv_seq_fork", "kv_seq_ensure_mapped",
+           "kv_seq_commit", "kv_seq_release", "kv_seq_info", "kv_cow_tail_page", "kv_append",
+           "paged_attn_workspace_bytes", "paged_attn_decode", "paged_attn_verify", "paged_attn_supported",
+           "kv_last_error_message"]
+
+
+class KVPageGeometry(ctypes.Structure):
+    _fields_ = [("page_size", ctypes.c_uint32), ("num_kv_heads", ctypes.c_uint32), ("head_dim", ctypes.c_uint32),
+                ("num_layers", ctypes.c_uint32), ("max_context", ctypes.c_uint32),
+                ("max_concurrency", ctypes.c_uint32), ("num_page_groups", ctypes.c_uint32)]
+
+
+class KVPlaneDesc(ctypes.Structure):
+    _fields_ = [("layer", ctypes.c_uint32), ("role", ctypes.c_uint32), ("dtype", ctypes.c_uint32),
+                ("x_extent", ctypes.c_uint32), ("elem_bytes", ctypes.c_uint32), ("reserved", ctypes.c_uint32),
+                ("base", ctypes.c_void_p)]
+
+
+class KVError(RuntimeError):
+    def __init__(self, status: int, message: str, deficit: int = 0):
+        super().__init__(f"{STATUS_NAMES.get(status, status)}: {message}")
+        self.status, self.message, self.deficit = status, message, deficit
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with `python -m paged_kv_cache_03_amd.build_lib`")
+    # One HIP runtime per process: torch ships its own libamdhip64 (soname
+    # libamdhip64.so.7) and loads it by the unversioned name.  Loading torch
+    # first makes the library's libamdhip64.so.7 dependency resolve to that same
+    # runtime, so device memory from torch and kernels from here share it.
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
+    lib = ctypes.CDLL(LIB_PATH)
+    u32, i32, vp, sz = ctypes.c_uint32, ctypes.c_int32, ctypes.c_void_p, ctypes.c_size_t
+    P = ctypes.POINTER
+    sig = {
+        "kv_profile_planes": (i32, [u32, u32, P(KVPlaneDesc), P(u32)]),
+        "kv_plane_bytes": (i32, [P(KVPageGeometry), P(KVPlaneDesc), P(ctypes.c_uint64)]),
+        "kv_pool_create": (i32, [P(KVPageGeometry), P(KVPlaneDesc), u32, vp, P(i32), vp, P(vp)]),
+        "kv_pool_destroy": (None, [vp]),
+        "kv_pool_stats": (i32, [vp, P(u32), P(u32), P(u32)]),
+        "kv_pool_table_host": (i32, [vp, P(i32), sz]),
+        "kv_pool_page_refs": (i32, [vp, u32, P(u32)]),
+        "kv_seq_open": (i32, [vp, u32, vp, P(ctypes.c_uint64)]),
+        "kv_seq_fork": (i32, [vp, ctypes.c_uint64, u32, u32, vp, P(ctypes.c_uint64)]),
+        "kv_seq_ensure_mapped": (i32, [vp, ctypes.c_uint64, u32, P(u32), vp]),
+        "kv_seq_commit": (i32, [vp, ctypes.c_uint64, u32]),
+        "kv_seq_release": (i32, [vp, ctypes.c_uint64, vp]),
+        "kv_seq_info": (i32, [vp, ctypes.c_uint64, P(u32), P(u32), P(u32)]),
+        "kv_cow_tail_page": (i32, [vp, ctypes.c_uint64, vp]),
+        "kv_append": (i32, [vp, u32, u32, vp, vp, vp, u32, vp, vp, vp]),
+        "paged_attn_workspace_bytes": (sz, [vp, u32, u32, u32, u32]),
+        "paged_attn_decode": (i32, [vp, u32, u32, u32, vp, vp, u32, vp, ctypes.c_float, vp, vp, sz, vp]),
+        "paged_attn_verify": (i32, [vp, u32, u32, u32, vp, vp, vp, u32, u32, u32, vp, ctypes.c_float, vp, vp, sz,
+                                    vp]),
+        "paged_attn_supported": (ctypes.c_int, [vp, u32, u32]),
+        "kv_last_error_message": (ctypes.c_char_p, []),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype, fn.argtypes = res, args
+    return lib
+
+
+_lib = _load()
+
+
+def _check(st: int, deficit: int = 0) -> None:
+    if st != KV_OK:
+        raise KVError(st, _lib.kv_last_error_message().decode(), deficit)
+
+
+def kv_last_error_message() -> str:
+    return _lib.kv_last_error_message().decode()
+
+
+def kv_profile_planes(profile: int, head_dim: int) -> list:
+    buf = (KVPlaneDesc * 4)()
+    n = ctypes.c_uint32(4)
+    _check(_lib.kv_profile_planes(profile, head_dim, buf, ctypes.byref(n)))
+    return [buf[i] for i in range(n.value)]
+
+
+def kv_plane_bytes(geo: KVPageGeometry, plane: KVPlaneDesc) -> int:
+    out = ctypes.c_uint64()
+    _check(_lib.kv_plane_bytes(ctypes.byref(geo), ctypes.byref(plane), ctypes.byref(out)))
+    return out.value
+
+
+def kv_pool_create(geo: KVPageGeometry, planes: list, d_block_tables: int | None, free_order=None,
+                   stream: int = 0) -> int:
+    arr = (KVPlaneDesc * len(planes))(*planes)
+    fo = None
+    if free_order is not None:
+        fo = (ctypes.c_int32 * len(free_order))(*[int(x) for x in free_order])
+    out = ctypes.c_void_p()
+    _check(_lib.kv_pool_create(ctypes.byref(geo), arr, len(planes), d_block_tables or None, fo, stream or None,
+                               ctypes.byref(out)))
+    return out.value
+
+
+def kv_pool_destroy(pool: int) -> None:
+    _lib.kv_pool_destroy(pool)
+
+
+def kv_pool_stats(pool: int) -> tuple:
+    a, r, v = ctypes.c_uint32(), ctypes.c_uint32(), ctypes.c_uint32()
+    _check(_lib.kv_pool_stats(pool, ctypes.byref(a), ctypes.byref(r), ctypes.byref(v)))
+    return a.value, r.value, v.value
+
+
+def kv_pool_table_host(pool: int, n_entries: int):
+    buf = (ctypes.c_int32 * n_entries)()
+    _check(_lib.kv_pool_table_host(pool, buf, n_entries))
+    return list(buf)
+
+
+def kv_pool_page_refs(pool: int, page_group: int) -> int:
+    out = ctypes.c_uint32()
+    _check(_lib.kv_pool_page_refs(pool, page_group, ctypes.byref(out)))
+    return out.value
+
+
+def kv_seq_open(pool: int, table_row: int, stream: int = 0) -> int:
+    out = ctypes.c_uint64()
+    _check(_lib.kv_seq_open(pool, table_row, stream or None, ctypes.byref(out)))
+    return out.value
+
+
+def kv_seq_fork(pool: int, src: int, frontier: int, table_row: int, stream: int = 0) -> int:
+    out = ctypes.c_uint64()
+    _check(_lib.kv_seq_fork(pool, src, frontier, table_row, stream or None, ctypes.byref(out)))
+    return out.value
+
+
+def kv_seq_ensure_mapped(pool: int, seq: int, tokens: int, stream: int = 0) -> None:
+    deficit = ctypes.c_uint32()
+    st = _lib.kv_seq_ensure_mapped(pool, seq, tokens, ctypes.byref(deficit), stream or None)
+    _check(st, deficit.value)
+
+
+def kv_seq_commit(pool: int, seq: int, frontier: int) -> None:
+    _check(_lib.kv_seq_commit(pool, seq, frontier))
+
+
+def kv_seq_release(pool: int, seq: int, stream: int = 0) -> None:
+    _check(_lib.kv_seq_release(pool, seq, stream or None))
+
+
+def kv_seq_info(pool: int, seq: int) -> tuple:
+    r, f, m = ctypes.c_uint32(), ctypes.c_uint32(), ctypes.c_uint32()
+    _check(_lib.kv_seq_info(pool, seq, ctypes.byref(r), ctypes.byref(f), ctypes.byref(m)))
+    return r.value, f.value, m.value
+
+
+def kv_cow_tail_page(pool: int, seq: int, stream: int = 0) -> None:
+    st = _lib.kv_cow_tail_page(pool, seq, stream or None)
+    _check(st, 1 if st == KV_E_CAPACITY else 0)
+
+
+def kv_append(pool: int, layer: int, B: int, d_table_rows: int, d_pos0: int, d_cu_tokens: int, total_tokens: int,
+              d_k: int, d_v: int, stream: int = 0) -> None:
+    _check(_lib.kv_append(pool, layer, B, d_table_rows, d_pos0, d_cu_tokens, total_tokens, d_k, d_v,
+                          stream or None))
+
+
+def paged_attn_workspace_bytes(pool: int, B: int, Hq: int, max_seq_len: int, max_q_len: int) -> int:
+    return int(_lib.paged_attn_workspace_bytes(pool, B, Hq, max_seq_len, max_q_len))
+
+
+def paged_attn_supported(pool: int, Hq: int, max_q_len: int) -> bool:
+    return bool(_lib.paged_attn_supported(pool, Hq, max_q_len))
+
+
+def paged_attn_decode(pool: int, layer: int, B: int, Hq: int, d_table_rows: int, d_seq_lens: int,
+                      max_seq_len: int, d_q: int, sm_scale: float, d_out: int, d_ws: int, ws_bytes: int,
+                      stream: int = 0) -> None:
+    _check(_lib.paged_attn_decode(pool, layer, B, Hq, d_table_rows, d_seq_lens, max_seq_len, d_q, sm_scale, d_out,
+                                  d_ws or None, ws_bytes, stream or None))
+
+
+def paged_attn_verify(pool: int, layer: int, B: int, Hq: int, d_table_rows: int, d_q_pos0: int, d_cu_q: int,
+                      total_q: int, max_q_len: int, max_seq_len: int, d_q: int, sm_scale: float, d_out: int,
+                      d_ws: int, ws_bytes: int, stream: int = 0) -> None:
+    _check(_lib.paged_attn_verify(pool, layer, B, Hq, d_table_rows, d_q_pos0, d_cu_q, total_q, max_q_len,
+                                  max_seq_len, d_q, sm_scale, d_out, d_ws or None, ws_bytes, stream or None))

@@ -1,0 +1,72 @@
+// internal.h -- structures shared by the host layer (pool.cpp) and the HIP
+// kernel launchers.  Not part of the C ABI.
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+#include <string>
+
+#include <hip/hip_runtime_api.h>
+
+#include "../../include/kvstore.h"
+
+namespace kvs {
+
+constexpr int kPage = 64;          // P (granularity table: allocation granularity 64)
+constexpr int kPageShift = 6;      // position >> 6 == logical block (P=64 translation)
+
+// Storage kind of one side (K or V) of a closed profile.
+enum Codec : int { CODEC_BF16 = 0, CODEC_INT8_G64 = 1, CODEC_FP8_ROW = 2, CODEC_NVFP4_G16 = 3 };
+
+// Device-side view of one layer's planes (PagedKVLayerView without the table row).
+struct LayerView {
+    void* k_code;
+    void* k_scale;   // nullptr for BF16
+    void* v_code;
+    void* v_scale;   // nullptr for BF16
+};
+
+// Everything a kernel needs to address a pool; passed by value.
+struct PoolView {
+    LayerView lv;
+    const int32_t* table;   // [C][L]
+    int32_t H;
+    int32_t D;
+    int32_t L;
+    int32_t C;
+    int32_t M;
+    int32_t k_codec;
+    int32_t v_codec;
+};
+
+// Launchers (defined in the .hip files).  Each returns hipSuccess or the
+// first launch error; argument validation happens in pool.cpp.
+hipError_t launch_table_fill(int32_t* d_table, int32_t n, int32_t value, hipStream_t s);
+hipError_t launch_table_publish(int32_t* d_dst, const int32_t* host_vals, int32_t n, hipStream_t s);
+
+struct CopyPlane {
+    void* base;
+    uint32_t row_bytes;   // X * elem_bytes (multiple of 4)
+};
+hipError_t launch_cow_copy(const CopyPlane* planes, int n_planes, int H, int src_g, int dst_g, int cols,
+                           hipStream_t s);
+
+hipError_t launch_append(const PoolView& pv, int B, const int32_t* table_rows, const int32_t* pos0,
+                         const int32_t* cu_tokens, int total_tokens, const void* k, const void* v,
+                         hipStream_t s);
+
+// Decode: split-K partials in ws, then a combine.  Returns hipErrorNotSupported
+// for shapes with no kernel instance.
+bool decode_supported(const PoolView& pv, int Hq);
+size_t decode_workspace_bytes(const PoolView& pv, int B, int Hq, int max_seq_len);
+hipError_t launch_decode(const PoolView& pv, int B, int Hq, const int32_t* table_rows, const int32_t* seq_lens,
+                         int max_seq_len, const void* q, float sm_scale, float* out, void* ws, size_t ws_bytes,
+                         hipStream_t s);
+
+bool verify_supported(const PoolView& pv, int Hq);
+size_t verify_workspace_bytes(const PoolView& pv, int B, int Hq, int max_seq_len, int max_q_len);
+hipError_t launch_verify(const PoolView& pv, int B, int Hq, const int32_t* table_rows, const int32_t* q_pos0,
+                         const int32_t* cu_q, int total_q, int max_q_len, int max_seq_len, const void* q,
+                         float sm_scale, float* out, void* ws, size_t ws_bytes, hipStream_t s);
+
+}  // namespace kvs

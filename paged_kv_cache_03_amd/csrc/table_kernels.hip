@@ -1,0 +1,111 @@
+// table_kernels.hip -- block-table publication and partial-tail copy.
+//
+// Mapping publication ("Paged KV Context Store" page, mapping publication
+// order): new page ids reach the device as one contiguous row slice, ordered
+// on the stream before the consumer.  The slice travels inside the kernel's
+// argument block, so the host mirror can change right after the call, no
+// pinned staging buffer or memset node is involved, and a captured graph would
+// replay the same entries.
+//
+// Tail COW (Fork passage): the committed columns [0, F mod 64) of every plane
+// slice of the shared page group g are copied into the private group g'.  In
+// the page-major order [X, P, H, N] the first `cols` columns of slice (g, h)
+// are one contiguous run of cols * X * elem_bytes bytes.
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstring>
+
+#include "internal.h"
+
+namespace kvs {
+namespace {
+
+constexpr int kPublishMax = 256;
+
+struct PublishArgs {
+    int32_t* dst;
+    int32_t n;
+    int32_t vals[kPublishMax];
+};
+
+__global__ void __launch_bounds__(256) table_publish_kernel(PublishArgs a) {
+    int i = threadIdx.x;
+    if (i < a.n) a.dst[i] = a.vals[i];
+}
+
+__global__ void __launch_bounds__(256) table_fill_kernel(int32_t* dst, int32_t n, int32_t v) {
+    int i = blockIdx.x * 256 + threadIdx.x;
+    if (i < n) dst[i] = v;
+}
+
+constexpr int kCopyMaxPlanes = 96;
+
+struct CopyArgs {
+    CopyPlane planes[kCopyMaxPlanes];
+    int32_t n_planes;
+    int32_t H;
+    int32_t src_g;
+    int32_t dst_g;
+    int32_t cols;
+};
+
+// grid (n_planes, H); block 256 threads copies one contiguous run
+__global__ void __launch_bounds__(256) cow_copy_kernel(CopyArgs a) {
+    const int pi = blockIdx.x, h = blockIdx.y;
+    const CopyPlane p = a.planes[pi];
+    const size_t slab = size_t(p.row_bytes) * kPage;
+    const char* src = static_cast<const char*>(p.base) + (size_t(a.src_g) * a.H + h) * slab;
+    char* dst = static_cast<char*>(p.base) + (size_t(a.dst_g) * a.H + h) * slab;
+    const size_t bytes = size_t(a.cols) * p.row_bytes;
+    if ((bytes & 15) == 0) {
+        const size_t n = bytes >> 4;
+        for (size_t i = threadIdx.x; i < n; i += 256)
+            reinterpret_cast<uint4*>(dst)[i] = reinterpret_cast<const uint4*>(src)[i];
+    } else {
+        const size_t n = bytes >> 2;
+        for (size_t i = threadIdx.x; i < n; i += 256)
+            reinterpret_cast<uint32_t*>(dst)[i] = reinterpret_cast<const uint32_t*>(src)[i];
+    }
+}
+
+}  // namespace
+
+hipError_t launch_table_fill(int32_t* d_table, int32_t n, int32_t value, hipStream_t s) {
+    if (n <= 0) return hipSuccess;
+    table_fill_kernel<<<(n + 255) / 256, 256, 0, s>>>(d_table, n, value);
+    return hipGetLastError();
+}
+
+hipError_t launch_table_publish(int32_t* d_dst, const int32_t* host_vals, int32_t n, hipStream_t s) {
+    for (int32_t off = 0; off < n; off += kPublishMax) {
+        PublishArgs a;
+        a.dst = d_dst + off;
+        a.n = std::min(kPublishMax, n - off);
+        std::memcpy(a.vals, host_vals + off, size_t(a.n) * sizeof(int32_t));
+        table_publish_kernel<<<1, 256, 0, s>>>(a);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
+hipError_t launch_cow_copy(const CopyPlane* planes, int n_planes, int H, int src_g, int dst_g, int cols,
+                           hipStream_t s) {
+    for (int off = 0; off < n_planes; off += kCopyMaxPlanes) {
+        CopyArgs a;
+        a.n_planes = std::min(kCopyMaxPlanes, n_planes - off);
+        for (int i = 0; i < a.n_planes; ++i) a.planes[i] = planes[off + i];
+        a.H = H;
+        a.src_g = src_g;
+        a.dst_g = dst_g;
+        a.cols = cols;
+        cow_copy_kernel<<<dim3(a.n_planes, H), 256, 0, s>>>(a);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
+}  // namespace kvs

@@ -1,0 +1,124 @@
+"""Convenience owner of a pool's device memory (torch tensors) around the C ABI.
+
+torch provides the device memory and the stream; every operation is one call
+of the C entry point with the same name (``_abi``).  Nothing here computes
+any part of the path.
+"""
+
+from __future__ import annotations
+
+import torch
+
+from . import _abi as abi
+
+_PLANE_TORCH = {abi.KV_DT_BF16: torch.int16, abi.KV_DT_I8: torch.int8, abi.KV_DT_E4M3FN: torch.uint8,
+                abi.KV_DT_E2M1X2: torch.uint8, abi.KV_DT_F32: torch.float32, abi.KV_DT_U8_E4M3: torch.uint8}
+ROLE_NAMES = {abi.KV_ROLE_K_CODE: "K_CODE", abi.KV_ROLE_K_SCALE: "K_SCALE", abi.KV_ROLE_V_CODE: "V_CODE",
+              abi.KV_ROLE_V_SCALE: "V_SCALE"}
+
+
+def _stream() -> int:
+    return torch.cuda.current_stream().cuda_stream
+
+
+def ptr(t: torch.Tensor | None) -> int:
+    return 0 if t is None else t.data_ptr()
+
+
+def i32(vals, device) -> torch.Tensor:
+    return torch.tensor([int(v) for v in vals], dtype=torch.int32, device=device)
+
+
+class DevicePool:
+    """Planes [M][H][64][X] per layer and role, the block table [C][L], and the pool handle."""
+
+    def __init__(self, profile: str, H: int, D: int, layers: int, S: int, C: int, M: int, free_order=None,
+                 host_only: bool = False, zero: bool = True, device: str = "cuda"):
+        self.profile, self.H, self.D, self.layers, self.S, self.C, self.M = profile, H, D, layers, S, C, M
+        self.L = -(-S // 64)
+        self.host_only = host_only
+        self.device = None if host_only else torch.device(device)
+        schema = abi.kv_profile_planes(abi.KV_PROFILE[profile], D)
+        self.geo = abi.KVPageGeometry(64, H, D, layers, S, C, M)
+        self.planes: list[dict] = []
+        descs = []
+        alloc = torch.zeros if zero else torch.empty
+        for layer in range(layers):
+            lp = {}
+            for p in schema:
+                t = None
+                if not host_only:
+                    t = alloc((M, H, 64, p.x_extent), dtype=_PLANE_TORCH[p.dtype], device=self.device)
+                lp[ROLE_NAMES[p.role]] = t
+                descs.append(abi.KVPlaneDesc(layer, p.role, p.dtype, p.x_extent, p.elem_bytes, 0, ptr(t) or None))
+            self.planes.append(lp)
+        self.table = None if host_only else torch.empty((C, self.L), dtype=torch.int32, device=self.device)
+        self.handle = abi.kv_pool_create(self.geo, descs, ptr(self.table) or None, free_order, self.stream)
+
+    @property
+    def stream(self) -> int:
+        return 0 if self.host_only else _stream()
+
+    def close(self) -> None:
+        if self.handle:
+            abi.kv_pool_destroy(self.handle)
+            self.handle = 0
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    # ------------------------------------------------------------- metadata --
+    def stats(self):
+        return abi.kv_pool_stats(self.handle)
+
+    def table_host(self):
+        return abi.kv_pool_table_host(self.handle, self.C * self.L)
+
+    def refs(self, g: int) -> int:
+        return abi.kv_pool_page_refs(self.handle, g)
+
+    def open(self, row: int) -> int:
+        return abi.kv_seq_open(self.handle, row, self.stream)
+
+    def fork(self, src: int, frontier: int, row: int) -> int:
+        return abi.kv_seq_fork(self.handle, src, frontier, row, self.stream)
+
+    def ensure_mapped(self, seq: int, tokens: int) -> None:
+        abi.kv_seq_ensure_mapped(self.handle, seq, tokens, self.stream)
+
+    def commit(self, seq: int, frontier: int) -> None:
+        abi.kv_seq_commit(self.handle, seq, frontier)
+
+    def release(self, seq: int) -> None:
+        abi.kv_seq_release(self.handle, seq, self.stream)
+
+    def info(self, seq: int):
+        return abi.kv_seq_info(self.handle, seq)
+
+    def cow_tail(self, seq: int) -> None:
+        abi.kv_cow_tail_page(self.handle, seq, self.stream)
+
+    # --------------------------------------------------------------- kernels --
+    def append(self, layer: int, table_rows: torch.Tensor, pos0: torch.Tensor, cu: torch.Tensor, total: int,
+               k: torch.Tensor, v: torch.Tensor) -> None:
+        abi.kv_append(self.handle, layer, table_rows.numel(), ptr(table_rows), ptr(pos0), ptr(cu), total, ptr(k),
+                      ptr(v), self.stream)
+
+    def workspace(self, B: int, Hq: int, max_seq_len: int, max_q_len: int = 0) -> torch.Tensor:
+        n = abi.paged_attn_workspace_bytes(self.handle, B, Hq, max_seq_len, max_q_len)
+        return torch.empty(max(n, 256), dtype=torch.uint8, device=self.device)
+
+    def decode(self, layer: int, Hq: int, table_rows: torch.Tensor, seq_lens: torch.Tensor, max_seq_len: int,
+               q: torch.Tensor, sm_scale: float, out: torch.Tensor, ws: torch.Tensor) -> None:
+        abi.paged_attn_decode(self.handle, layer, table_rows.numel(), Hq, ptr(table_rows), ptr(seq_lens),
+                              max_seq_len, ptr(q), sm_scale, ptr(out), ptr(ws), ws.numel(), self.stream)
+
+    def verify(self, layer: int, Hq: int, table_rows: torch.Tensor, q_pos0: torch.Tensor, cu_q: torch.Tensor,
+               total_q: int, max_q_len: int, max_seq_len: int, q: torch.Tensor, sm_scale: float, out: torch.Tensor,
+               ws: torch.Tensor) -> None:
+        abi.paged_attn_verify(self.handle, layer, table_rows.numel(), Hq, ptr(table_rows), ptr(q_pos0), ptr(cu_q),
+                              total_q, max_q_len, max_seq_len, ptr(q), sm_scale, ptr(out), ptr(ws), ws.numel(),
+                              self.stream)

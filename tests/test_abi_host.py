@@ -1,0 +1,211 @@
+"""CPU tests of the C ABI: exports, validation, and the host allocator vs the oracle.
+
+These run without a GPU: a pool created with a NULL block table is host-only
+(metadata and host mirror, no device work), so allocator, fork, COW bookkeeping
+and error paths can be compared with the oracle bit for bit.
+"""
+
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+import paged_kv_cache_03_amd._abi as abi
+from oracle import geometry as G
+from oracle.pool import OraclePool
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kvstore.h")
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return re.findall(r"^\s*(?:[A-Za-z_][\w\s\*]*?)\b([a-z_][a-z0-9_]*)\s*\(", src, flags=re.M)
+
+
+def test_header_declares_exactly_the_bound_symbols():
+    names = [n for n in _declared() if n.startswith(("kv_", "paged_attn"))]
+    assert names == abi.EXPORTS
+
+
+def test_library_exports_every_declared_symbol():
+    out = subprocess.run(["nm", "-D", "--defined-only", abi.LIB_PATH], capture_output=True, text=True).stdout
+    exported = {ln.split()[-1] for ln in out.splitlines() if ln.strip()}
+    for name in abi.EXPORTS:
+        assert name in exported, name
+        assert getattr(abi._lib, name) is not None
+
+
+@pytest.mark.parametrize("profile", list(abi.KV_PROFILE))
+@pytest.mark.parametrize("D", [64, 128, 256])
+def test_profile_planes_match_oracle_schema(profile, D):
+    got = [(p.role, p.x_extent, p.elem_bytes) for p in abi.kv_profile_planes(abi.KV_PROFILE[profile], D)]
+    roles = {"K_CODE": 0, "K_SCALE": 1, "V_CODE": 2, "V_SCALE": 3}
+    want = [(roles[s.role], s.x_extent, s.elem_bytes) for s in G.plane_schema(profile, D, 4)]
+    assert got == want
+
+
+def _host_pool(S, C, M, H=2, D=128, profile="BF16", layers=1, free_order=None):
+    planes = []
+    for layer in range(layers):
+        for p in abi.kv_profile_planes(abi.KV_PROFILE[profile], D):
+            p.layer = layer
+            planes.append(p)
+    geo = abi.KVPageGeometry(64, H, D, layers, S, C, M)
+    return abi.kv_pool_create(geo, planes, None, free_order)
+
+
+def test_geometry_rejections():
+    ok = dict(S=1024, C=2, M=16)
+    h = _host_pool(**ok)
+    abi.kv_pool_destroy(h)
+    for bad in (dict(C=9), dict(C=0), dict(M=15), dict(M=33)):
+        with pytest.raises(abi.KVError) as e:
+            _host_pool(**{**ok, **bad})
+        assert e.value.status == abi.KV_E_GEOMETRY
+    geo = abi.KVPageGeometry(32, 2, 128, 1, 1024, 2, 16)
+    with pytest.raises(abi.KVError) as e:
+        abi.kv_pool_create(geo, abi.kv_profile_planes(0, 128), None)
+    assert e.value.status == abi.KV_E_GEOMETRY
+    with pytest.raises(abi.KVError) as e:
+        abi.kv_profile_planes(abi.KV_PROFILE["INT8_G64"], 96)
+    assert e.value.status == abi.KV_E_GEOMETRY
+    with pytest.raises(abi.KVError):
+        _host_pool(1024, 2, 16, free_order=[0] * 16)          # not a permutation
+
+
+def test_mixed_profile_inventory_rejected():
+    planes = abi.kv_profile_planes(abi.KV_PROFILE["BF16"], 128)
+    v8 = [p for p in abi.kv_profile_planes(abi.KV_PROFILE["INT8_G64"], 128) if p.role >= 2]
+    with pytest.raises(abi.KVError):                        # BF16 K with INT8 V is not a closed profile
+        abi.kv_pool_create(abi.KVPageGeometry(64, 2, 128, 1, 1024, 2, 16), [planes[0]] + v8, None)
+
+
+def test_stale_handles_and_leased_rows():
+    h = _host_pool(1024, 2, 16)
+    a = abi.kv_seq_open(h, 0)
+    with pytest.raises(abi.KVError) as e:
+        abi.kv_seq_open(h, 0)
+    assert e.value.status == abi.KV_E_INVALID
+    abi.kv_seq_release(h, a)
+    for fn in (lambda: abi.kv_seq_commit(h, a, 0), lambda: abi.kv_seq_ensure_mapped(h, a, 1),
+               lambda: abi.kv_seq_release(h, a), lambda: abi.kv_cow_tail_page(h, a)):
+        with pytest.raises(abi.KVError) as e:
+            fn()
+        assert e.value.status == abi.KV_E_STALE
+    b = abi.kv_seq_open(h, 0)          # slot reused with a new generation
+    assert b != a
+    abi.kv_pool_destroy(h)
+
+
+def test_shortfall_reports_deficit_and_allocates_nothing():
+    h = _host_pool(1024, 2, 16)
+    a, b = abi.kv_seq_open(h, 0), abi.kv_seq_open(h, 1)
+    abi.kv_seq_ensure_mapped(h, a, 640)
+    before = abi.kv_pool_stats(h)
+    with pytest.raises(abi.KVError) as e:
+        abi.kv_seq_ensure_mapped(h, b, 8 * 64 + 1)
+    assert e.value.status == abi.KV_E_CAPACITY and e.value.deficit == 3
+    assert abi.kv_pool_stats(h) == before and abi.kv_seq_info(h, b)[2] == 0
+    with pytest.raises(abi.KVError) as e:
+        abi.kv_seq_commit(h, b, 1)
+    assert e.value.status == abi.KV_E_UNMAPPED
+    abi.kv_pool_destroy(h)
+
+
+def test_compute_calls_refuse_host_only_pool():
+    h = _host_pool(1024, 2, 16)
+    with pytest.raises(abi.KVError) as e:
+        abi.kv_append(h, 0, 1, 1, 1, 1, 1, 1, 1)
+    assert e.value.status == abi.KV_E_INVALID
+    abi.kv_pool_destroy(h)
+
+
+STATUS = {abi.KV_E_CAPACITY: "CAPACITY", abi.KV_E_SHARED_WRITE: "SHARED_WRITE", abi.KV_E_INVALID: "INVALID"}
+
+
+def _run_both(rng, S, C, M, n_ops=300):
+    order = rng.permutation(M)
+    o = OraclePool(S, C, M, free_order=order)
+    h = _host_pool(S, C, M, free_order=order)
+    live = {}        # oracle sid -> abi handle
+    for _ in range(n_ops):
+        op = int(rng.integers(0, 6))
+        rows = [r for r in range(C) if r not in {o.row_of(s) for s in live}]
+        if op == 0 and rows:
+            sid = o.open(rows[0])
+            live[sid] = abi.kv_seq_open(h, rows[0])
+        elif op == 1 and live:
+            sid = list(live)[int(rng.integers(len(live)))]
+            n = min(S + 5, o.frontier_of(sid) + int(rng.integers(0, 150)))
+            st, deficit = o.ensure_mapped(sid, n)
+            try:
+                abi.kv_seq_ensure_mapped(h, live[sid], n)
+                got = ("OK", 0)
+            except abi.KVError as e:
+                got = (STATUS[e.status], e.deficit)
+            assert got == (st, deficit)
+            if st == "OK":
+                f = min(n, 64 * len(o.pages_of(sid)))
+                assert o.commit(sid, f) == "OK"
+                abi.kv_seq_commit(h, live[sid], f)
+        elif op == 2 and live and rows:
+            src = list(live)[int(rng.integers(len(live)))]
+            F = int(rng.integers(0, o.frontier_of(src) + 1))
+            sid = o.fork(src, F, rows[0])
+            live[sid] = abi.kv_seq_fork(h, live[src], F, rows[0])
+        elif op == 3 and live:
+            sid = list(live)[int(rng.integers(len(live)))]
+            st, _ = o.cow_tail(sid)
+            try:
+                abi.kv_cow_tail_page(h, live[sid])
+                got = "OK"
+            except abi.KVError as e:
+                got = STATUS[e.status]
+            assert got == st
+        elif op == 4 and live:
+            sid = list(live)[int(rng.integers(len(live)))]
+            o.release(sid)
+            abi.kv_seq_release(h, live.pop(sid))
+        # bit-exact state after every operation
+        assert abi.kv_pool_stats(h) == o.stats()
+        assert np.array_equal(np.array(abi.kv_pool_table_host(h, C * o.L)).reshape(C, o.L), o.table)
+        for sid, hh in live.items():
+            assert abi.kv_seq_info(h, hh) == (o.row_of(sid), o.frontier_of(sid), len(o.pages_of(sid)))
+    for g in range(M):
+        assert abi.kv_pool_page_refs(h, g) == o.refs[g]
+    abi.kv_pool_destroy(h)
+
+
+def test_host_allocator_matches_oracle_on_random_operation_sequences():
+    rng = np.random.default_rng(21)
+    for _ in range(25):
+        C = int(rng.integers(1, 9))
+        S = int(rng.integers(64, 3000))
+        L = -(-S // 64)
+        M = int(rng.integers(max(L, C), C * L + 1))
+        _run_both(rng, S, C, M)
+
+
+def test_fork_worked_example_through_abi():
+    h = _host_pool(4096, 2, 128)
+    a = abi.kv_seq_open(h, 0)
+    abi.kv_seq_ensure_mapped(h, a, 1000)
+    abi.kv_seq_commit(h, a, 1000)
+    b = abi.kv_seq_fork(h, a, 1000, 1)
+    assert abi.kv_seq_info(h, b) == (1, 1000, 16)
+    with pytest.raises(abi.KVError) as e:
+        abi.kv_seq_ensure_mapped(h, b, 1001)
+    assert e.value.status == abi.KV_E_SHARED_WRITE
+    t = np.array(abi.kv_pool_table_host(h, 2 * 64)).reshape(2, 64)
+    tail = t[0, 15]
+    assert abi.kv_pool_page_refs(h, int(tail)) == 2
+    abi.kv_cow_tail_page(h, b)
+    t2 = np.array(abi.kv_pool_table_host(h, 2 * 64)).reshape(2, 64)
+    assert np.array_equal(t2[1, :15], t[0, :15]) and t2[1, 15] != tail
+    assert abi.kv_pool_page_refs(h, int(tail)) == 1
+    abi.kv_seq_ensure_mapped(h, b, 1001)
+    abi.kv_pool_destroy(h)

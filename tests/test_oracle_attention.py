@@ -11,6 +11,7 @@ from oracle import attention as A
 from oracle import codecs as Q
 from oracle.pool import OraclePool
 from oracle.store import OracleStore
+from tests.drivers import build_oracle
 from workloads.gen import bf16_normal, f32_to_bf16_bits, rng_for
 
 
@@ -90,38 +91,7 @@ def test_mha_is_gqa_with_one_query_head_per_kv_head():
 
 
 def _build(wl, free_order=None, privatize=False):
-    """Drive the oracle pool/store through a workload's history and step."""
-    pool = OraclePool(wl.S, wl.C, wl.M, free_order=wl.free_order if free_order is None else free_order)
-    st = OracleStore(pool, wl.profile, wl.H, wl.D, wl.layers)
-    sids = {}
-    for b in wl.order():
-        row = wl.table_rows[b]
-        if wl.fork[b] is None or privatize:
-            sids[b] = pool.open(row)
-            n_inh = 0
-        else:
-            src, F = wl.fork[b]
-            sids[b] = pool.fork(sids[src], F, row)
-            n_inh = F
-        if privatize and wl.fork[b] is not None:
-            n_inh = 0
-        if wl.hist[b] > n_inh:
-            if n_inh % 64 and pool.cow_tail(sids[b])[1] is not None:
-                raise AssertionError("workload forks at unaligned frontier with own history")
-            assert pool.ensure_mapped(sids[b], wl.hist[b]) == ("OK", 0)
-            for layer in range(wl.layers):
-                k, v = wl.logical_kv(layer, b, wl.hist[b])
-                st.append(layer, row, n_inh, k[n_inh:], v[n_inh:])
-        pool.commit(sids[b], wl.hist[b])
-    for b in range(wl.B):
-        if wl.cow[b]:
-            status, info = pool.cow_tail(sids[b])
-            if info is not None:
-                st.cow_copy(*info)
-        assert pool.ensure_mapped(sids[b], wl.hist[b] + wl.step[b]) == ("OK", 0)
-        for layer in range(wl.layers):
-            k, v = wl.step_kv(layer, b)
-            st.append(layer, wl.table_rows[b], wl.hist[b], k, v)
+    pool, st, _ = build_oracle(wl, free_order=free_order, privatize=privatize)
     return pool, st
 
 

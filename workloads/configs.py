@@ -20,6 +20,8 @@ listed in DESIGN.md):
 
 from __future__ import annotations
 
+import os
+from concurrent.futures import ThreadPoolExecutor
 from dataclasses import dataclass, field
 
 import numpy as np
@@ -97,15 +99,22 @@ class Workload:
         lo = start if lo is None else lo
         hi = self.hist[b] if hi is None else hi
         assert start <= lo <= hi <= self.hist[b]
-        ks, vs = [], []
         blk = 1024
-        for c in range(lo // blk, (hi + blk - 1) // blk):
+
+        def one(c):
             a, e = max(lo, c * blk), min(hi, (c + 1) * blk)
             r = rng_for(self.seed, 1, layer, b, c)
             k = bf16_normal(r, (blk, self.H, self.D), self.outlier_frac)
             v = bf16_normal(r, (blk, self.H, self.D), self.outlier_frac)
-            ks.append(k[a - c * blk:e - c * blk])
-            vs.append(v[a - c * blk:e - c * blk])
+            return k[a - c * blk:e - c * blk], v[a - c * blk:e - c * blk]
+
+        blocks = list(range(lo // blk, (hi + blk - 1) // blk))
+        if len(blocks) > 2:
+            with ThreadPoolExecutor(max_workers=min(16, os.cpu_count() or 1)) as ex:
+                parts = list(ex.map(one, blocks))
+        else:
+            parts = [one(c) for c in blocks]
+        ks, vs = [p[0] for p in parts], [p[1] for p in parts]
         if not ks:
             z = np.zeros((0, self.H, self.D), dtype=np.uint16)
             return z, z.copy()
