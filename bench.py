@@ -1,0 +1,226 @@
+#!/usr/bin/env python3
+"""Benchmark of the paged KV hot path on one MI355X.
+
+A step is one decode step of the whole batch through every layer:
+    for each layer: kv_append (one new token per sequence, quantized into its
+    page through the block table) + paged_attn_decode (split-K over pages and
+    the cross-split combine).
+Inputs are resident in HBM before timing; the step is idempotent (the same
+positions are re-appended, the same contexts decoded).
+
+Default workload: 8 sequences, 32 layers, 32 query / 8 KV heads, head_dim 128,
+BF16 pages, contexts U[1, 32768] with a 4096-token prefix shared by sequences
+0-3.  `value` is whole-step KV throughput in GB/s: algorithmic bytes (unique
+KV bytes read by decode, plus append rows, queries and outputs) over the
+measured step time.
+
+Prints one JSON line.  Progress goes to stderr.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "paged decode KV GB/s (% of HBM peak) + decode steps/s at C=8, 32K ctx"
+
+
+def log(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def bytes_per_token_head(profile: str, D: int) -> int:
+    from paged_kv_cache_03_amd import _abi as abi
+    return sum(p.x_extent * p.elem_bytes for p in abi.kv_profile_planes(abi.KV_PROFILE[profile], D))
+
+
+def kv_read_bytes(table, wl) -> tuple[int, int]:
+    """(unique, logical) KV bytes decode reads: every valid (page, column) of every
+    entry; a page shared by several entries counts once in `unique`."""
+    import numpy as np
+    bpth = bytes_per_token_head(wl.profile, wl.D)
+    cols = {}
+    logical = 0
+    for b, ctx in enumerate(wl.seq_lens):
+        row = table[wl.table_rows[b]]
+        for p in range((ctx + 63) // 64):
+            c = min(64, ctx - 64 * p)
+            g = int(row[p])
+            cols[g] = max(cols.get(g, 0), c)
+            logical += c
+    unique = int(np.sum(list(cols.values())))
+    return unique * wl.H * bpth, logical * wl.H * bpth
+
+
+def cpu_baseline(wl, seconds_hint: float = 20.0) -> dict:
+    """The oracle, as it stands, on a bounded sample of the same step: layer 0 of
+    the workload (append of the step rows + paged decode of every entry and head)."""
+    import numpy as np
+    from oracle import attention as A
+    from oracle.pool import OraclePool
+    from oracle.store import OracleStore
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = 1
+    log("cpu baseline: building the oracle's pool for layer 0")
+    pool = OraclePool(wl.S, wl.C, wl.M, free_order=wl.free_order)
+    st = OracleStore(pool, wl.profile, wl.H, wl.D, 1)
+    sids = {}
+    for b in wl.order():
+        row = wl.table_rows[b]
+        if wl.fork[b] is None:
+            sids[b] = pool.open(row)
+            n_inh = 0
+        else:
+            sids[b] = pool.fork(sids[wl.fork[b][0]], wl.fork[b][1], row)
+            n_inh = wl.fork[b][1]
+            if wl.hist[b] > n_inh and n_inh % 64:
+                st.cow_copy(*pool.cow_tail(sids[b])[1])
+        pool.ensure_mapped(sids[b], wl.hist[b])
+        if wl.hist[b] > n_inh:
+            k, v = wl.hist_kv(0, b)
+            st.append(0, row, n_inh, k, v)
+        pool.commit(sids[b], wl.hist[b])
+    for b in range(wl.B):
+        if wl.cow[b]:
+            _, info = pool.cow_tail(sids[b])
+            if info is not None:
+                st.cow_copy(*info)
+        pool.ensure_mapped(sids[b], wl.hist[b] + wl.step[b])
+    steps = [wl.step_kv(0, b) for b in range(wl.B)]
+    q = wl.q(0)
+    log("cpu baseline: timing the oracle")
+    reps, elapsed = 0, 0.0
+    while reps == 0 or (elapsed < seconds_hint * 0.5 and reps < 3):
+        t0 = time.perf_counter()
+        for b in range(wl.B):
+            st.append(0, wl.table_rows[b], wl.hist[b], *steps[b])
+        A.paged_decode(st, 0, wl.table_rows, wl.seq_lens, q, wl.sm_scale)
+        elapsed += time.perf_counter() - t0
+        reps += 1
+    unique, _ = kv_read_bytes(pool.table, wl)
+    per_layer = elapsed / reps
+    return {"value": round(unique / per_layer / 1e9, 4), "unit": "GB/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"layer 0 of {wl.layers}: append of the step rows + decode of all {wl.B} entries x {wl.Hq} "
+                      f"heads, {reps} rep(s), {per_layer:.2f} s per layer (KV bytes read / time)"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", type=int, default=2, help="workload number (decode workloads: 1-4)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("this build runs on one GPU only: --gpus must be 1 (the path's sharding is described in DESIGN.md)",
+              file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import workloads
+    from paged_kv_cache_03_amd.device_pool import i32
+    from workloads.device_driver import _dev, build_device
+
+    wl = workloads.get(args.config)
+    if wl.mode != "decode":
+        print("bench.py times the decode step; verify/prefill workloads are timed by their tests", file=sys.stderr)
+        return 2
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    t0 = time.time()
+    log(f"workload {wl.name}: filling {wl.layers} layer(s) of history")
+    dp, _, step_inputs = build_device(wl, zero=False)
+    log(f"history resident after {time.time() - t0:.1f} s")
+
+    rows_t, pos0_t, cu_t = i32(wl.table_rows, dev), i32(wl.hist, dev), i32(wl.cu_q, dev)
+    lens_t = i32(wl.seq_lens, dev)
+    total = int(wl.cu_q[-1])
+    max_ctx = max(wl.seq_lens)
+    qs = [_dev(wl.q(layer), dev) for layer in range(wl.layers)]
+    out = torch.empty((wl.B, wl.Hq, wl.D), dtype=torch.float32, device=dev)
+    ws = dp.workspace(wl.B, wl.Hq, max_ctx)
+
+    def step(events=None):
+        for layer in range(wl.layers):
+            kd, vd = step_inputs[layer]
+            dp.append(layer, rows_t, pos0_t, cu_t, total, kd, vd)
+            if events is not None:
+                events[layer][0].record()
+            dp.decode(layer, wl.Hq, rows_t, lens_t, max_ctx, qs[layer], wl.sm_scale, out, ws)
+            if events is not None:
+                events[layer][1].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # timed region: K whole steps, no probes inside
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for _ in range(args.steps):
+        step()
+    end.record()
+    torch.cuda.synchronize()
+    ms_per_step = start.elapsed_time(end) / args.steps
+    log(f"{ms_per_step:.4f} ms per step")
+
+    # decode launch durations: events around every paged_attn_decode call of K steps
+    evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+            for _ in range(wl.layers)] for _ in range(args.steps)]
+    for s in range(args.steps):
+        step(evs[s])
+    torch.cuda.synchronize()
+    dec_ms = float(np.mean([a.elapsed_time(b) for row in evs for (a, b) in row]))
+
+    table = dp.table.cpu().numpy()
+    unique, logical = kv_read_bytes(table, wl)
+    bpth = bytes_per_token_head(wl.profile, wl.D)
+    qo_bytes = wl.B * wl.Hq * wl.D * (2 + 4)
+    append_bytes = total * wl.H * (bpth + 2 * 2 * wl.D)
+    per_decode = unique + qo_bytes
+    per_step = wl.layers * (per_decode + append_bytes)
+    value = per_step / (ms_per_step * 1e-3) / 1e9
+    achieved = per_decode / (dec_ms * 1e-3) / 1e9
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(wl)
+
+    line = {
+        "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16" if wl.profile == "BF16" else wl.profile.lower(), "data": "synthetic",
+        "config": {"workload": wl.name, "profile": wl.profile, "batch": wl.B, "layers": wl.layers, "q_heads": wl.Hq,
+                   "kv_heads": wl.H, "head_dim": wl.D, "ctx_sum": int(sum(wl.seq_lens)), "ctx_max": int(max_ctx),
+                   "page_size": 64, "pool_pages": wl.M},
+        "steps_per_s": round(1000.0 / ms_per_step, 2),
+        "hbm_frac": round(value / HBM_PEAK_GBS, 4),
+        "kv_bytes_per_step": {"unique": wl.layers * unique, "logical": wl.layers * logical},
+        "roofline": {"kernel": "paged_attn_decode (split + combine launches)", "bound": "hbm",
+                     "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "bytes_per_launch": per_decode, "launch_ms": round(dec_ms, 5)},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+    dp.close()
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,119 @@
+"""Drive a workload through the device pool (the C ABI) in the oracle's order.
+
+History construction: roots in sequence order (open, map, append, commit),
+then forks (fork at the source's frontier; copy the tail first when own
+history starts inside it; map, append own history, commit).  Step: every
+tail copy first, then map the step's tokens, then one batched append of all
+entries' new rows per layer.  Decode reads the step's last token; verify the
+chunk.  Only the product is called here: no arithmetic of the method.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+
+def _dev(x: np.ndarray, device):
+    import torch
+    if x.dtype == np.uint16:
+        x = x.view(np.int16)
+    return torch.from_numpy(np.ascontiguousarray(x)).to(device)
+
+
+def build_device(wl, free_order=None, privatize=False, layers=None, zero=True, hist_layers_from=None,
+                 chunk_tokens=16384):
+    """Device pool holding the workload's history and step rows.
+
+    hist_layers_from: if set, every layer's history rows are the rows generated for
+    that layer (used only where the values do not matter, e.g. timing).
+    """
+    import torch
+    from paged_kv_cache_03_amd.device_pool import DevicePool, i32
+
+    layers = list(range(wl.layers)) if layers is None else list(layers)
+    dp = DevicePool(wl.profile, wl.H, wl.D, wl.layers, wl.S, wl.C, wl.M,
+                    free_order=wl.free_order if free_order is None else free_order, zero=zero)
+    dev = dp.device
+    seqs = {}
+    for b in wl.order():
+        row = wl.table_rows[b]
+        if wl.fork[b] is None or privatize:
+            seqs[b] = dp.open(row)
+            n_inh = 0
+        else:
+            src, F = wl.fork[b]
+            seqs[b] = dp.fork(seqs[src], F, row)
+            n_inh = F
+            if wl.hist[b] > F and F % 64:
+                dp.cow_tail(seqs[b])
+        if wl.hist[b] > n_inh:
+            dp.ensure_mapped(seqs[b], wl.hist[b])
+            rows_t = i32([row], dev)
+            cache = {}
+            for layer in layers:
+                src_layer = layer if hist_layers_from is None else hist_layers_from
+                if src_layer not in cache:
+                    k, v = wl.logical_kv(src_layer, b, wl.hist[b]) if privatize else wl.hist_kv(src_layer, b)
+                    if privatize:
+                        k, v = k[n_inh:], v[n_inh:]
+                    cache = {src_layer: (_dev(k, dev), _dev(v, dev))}
+                kd, vd = cache[src_layer]
+                for a in range(0, kd.shape[0], chunk_tokens):
+                    e = min(kd.shape[0], a + chunk_tokens)
+                    dp.append(layer, rows_t, i32([n_inh + a], dev), i32([0, e - a], dev), e - a,
+                              kd[a:e].contiguous(), vd[a:e].contiguous())
+            torch.cuda.synchronize()
+        dp.commit(seqs[b], wl.hist[b])
+    step_inputs = {}
+    for b in range(wl.B):
+        if wl.cow[b]:
+            dp.cow_tail(seqs[b])
+    for b in range(wl.B):
+        dp.ensure_mapped(seqs[b], wl.hist[b] + wl.step[b])
+    rows_t = i32(wl.table_rows, dev)
+    pos0_t = i32(wl.hist, dev)
+    cu_t = i32(wl.cu_q, dev)
+    for layer in layers:
+        k, v = wl.step_kv_all(layer)
+        kd, vd = _dev(k, dev), _dev(v, dev)
+        step_inputs[layer] = (kd, vd)
+        dp.append(layer, rows_t, pos0_t, cu_t, int(wl.cu_q[-1]), kd, vd)
+    torch.cuda.synchronize()
+    return dp, seqs, step_inputs
+
+
+def device_decode(dp, wl, layer, seq_lens=None):
+    import torch
+    from paged_kv_cache_03_amd.device_pool import i32
+    dev = dp.device
+    q = _dev(wl.q(layer), dev)
+    out = torch.empty((wl.B, wl.Hq, wl.D), dtype=torch.float32, device=dev)
+    lens = wl.seq_lens if seq_lens is None else seq_lens
+    msl = max(1, max(lens))
+    ws = dp.workspace(wl.B, wl.Hq, msl)
+    dp.decode(layer, wl.Hq, i32(wl.table_rows, dev), i32(lens, dev), msl, q, wl.sm_scale, out, ws)
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+def device_verify(dp, wl, layer):
+    import torch
+    from paged_kv_cache_03_amd.device_pool import i32
+    dev = dp.device
+    q = _dev(wl.q(layer), dev)
+    tq = int(wl.cu_q[-1])
+    out = torch.empty((tq, wl.Hq, wl.D), dtype=torch.float32, device=dev)
+    msl, mql = max(wl.seq_lens), max(wl.step)
+    ws = dp.workspace(wl.B, wl.Hq, msl, mql)
+    dp.verify(layer, wl.Hq, i32(wl.table_rows, dev), i32(wl.hist, dev), i32(wl.cu_q, dev), tq, mql, msl, q,
+              wl.sm_scale, out, ws)
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+def plane_np(dp, layer, role):
+    """A device plane as a NumPy array in the oracle's dtype."""
+    t = dp.planes[layer][role].cpu().numpy()
+    if t.dtype == np.int16:
+        t = t.view(np.uint16)
+    return t
