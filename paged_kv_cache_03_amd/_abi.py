@@ -3,7 +3,7 @@
 Every function here forwards to the C entry point of the same name.  A status
 other than KV_OK raises KVError carrying the status, the library's message and,
 for a capacity shortfall, the deficit.  The library must be built
-(``python -m paged_kv_cache_03_amd.build_lib``); loading fails loudly if not.
+(``python paged_kv_cache_03_amd/build_lib.py``); loading fails loudly if not.
 """
 
 from __future__ import annotations
@@ -51,7 +51,7 @@ class KVError(RuntimeError):
 
 def _load():
     if not os.path.exists(LIB_PATH):
-        raise ImportError(f"{LIB_PATH} is missing: build it with `python -m paged_kv_cache_03_amd.build_lib`")
+        raise ImportError(f"{LIB_PATH} is missing: build it with `python paged_kv_cache_03_amd/build_lib.py`")
     # One HIP runtime per process: torch ships its own libamdhip64 (soname
     # libamdhip64.so.7) and loads it by the unversioned name.  Loading torch
     # first makes the library's libamdhip64.so.7 dependency resolve to that same

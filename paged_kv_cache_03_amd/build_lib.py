@@ -1,6 +1,6 @@
 """Build libkvstore.so (HIP kernels for gfx950 + the C++ host layer) in-tree.
 
-    python -m paged_kv_cache_03_amd.build_lib
+    python paged_kv_cache_03_amd/build_lib.py
 
 Compiles every source under csrc/ with hipcc for gfx950 only.  Flags:
   * -fhip-fp32-correctly-rounded-divide-sqrt, -fno-gpu-flush-denormals-to-zero,
