@@ -215,7 +215,11 @@ kv_status kv_append(const kv_pool* pool, uint32_t layer, uint32_t B, const int32
                     const void* d_k, const void* d_v, hipStream_t stream);
 
 /* Workspace bytes paged_attn_decode / paged_attn_verify need for these bounds
- * (split-K partials plus per-item bookkeeping).  max_q_len 0 means decode. */
+ * (split-K partials plus per-segment arrival counters).  max_q_len 0 means
+ * decode.  The caller owns the workspace; it must be zero-filled once after
+ * allocation, and every call returns it with its counter area zero again, so
+ * it can be reused by later calls on the same stream.  Calls that overlap in
+ * time (other streams) need workspaces of their own. */
 size_t paged_attn_workspace_bytes(const kv_pool* pool, uint32_t B, uint32_t Hq, uint32_t max_seq_len,
                                   uint32_t max_q_len);
 

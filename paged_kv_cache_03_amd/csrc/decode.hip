@@ -1,4 +1,4 @@
-// decode.hip -- paged decode: split-K over pages, then a cross-split combine.
+// decode.hip -- paged decode (one query token per entry) on the page pool.
 //
 // NInfer "Paged KV Context Store" page: PagedKVBatchLayerView (table_rows[b]
 // selects the block-table row of compact entry b), P=64 translation
@@ -6,11 +6,17 @@
 // translation at page granularity, no gather-to-contiguous, free choice of
 // tile/split/wave/LDS scheme), wrapper validation and caller guarantees.
 //
-// Split policy: entry b's pages [0, ceil(ctx/64)) are cut into chunks of
-// `chunk_pages` consecutive logical pages.  Chunk boundaries depend only on
-// logical positions and the host-side bounds, never on physical page ids,
-// and the combine runs in a fixed order, so outputs are bitwise identical
-// under any permutation of page ids and for shared versus private pages.
+// Two kernels:
+//  * the matrix-core page stream (BF16 pages, D in {64, 128}): every page of
+//    the call in one flat list, cut into equal ranges, one 256-thread block
+//    per compute unit, with the cross-range combine in the same launch;
+//  * the split kernel (every other profile and shape): entry b's pages are
+//    cut into chunks of `chunk_pages` consecutive logical pages, one wave per
+//    (entry, KV head, chunk), then a combine launch.
+// In both, the split depends only on logical positions and the host-side
+// bounds, never on physical page ids, and the combine runs in a fixed order,
+// so outputs are bitwise identical under any permutation of page ids and for
+// shared versus private pages.
 
 #include <hip/hip_runtime.h>
 
@@ -33,6 +39,7 @@ struct DecodeArgs {
     float* out;
     float* part_ml;     // [items][GQ][2]  (running max in log2 units, sum)
     float* part_acc;    // [items][GQ][D]  (unnormalized)
+    uint32_t* arrive;   // [C*H] partials delivered per segment (page stream)
     float scale_log2;   // sm_scale * log2(e)
     int32_t B;
     int32_t Hq;
@@ -136,28 +143,7 @@ __global__ void __launch_bounds__(256) decode_split_kernel(DecodeArgs a) {
     }
 }
 
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
-    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a), __builtin_bit_cast(bf16x2_t, b), c,
-                                           false);
-}
-
-// An LDS pointer the optimizer cannot see through: reads through it stay in
-// the page loop instead of being hoisted into a query-sized register file.
-typedef const u32x4 __attribute__((address_space(3)))* lds_cu4;
-
-__device__ __forceinline__ lds_cu4 opaque_lds(lds_cu4 p) {
-    asm volatile("" : "+v"(p));
-    return p;
-}
-
-// Same, but only once `dep` is available: bounds how many chunks of query
-// reads the scheduler may issue ahead of the dot products.
-__device__ __forceinline__ lds_cu4 opaque_lds_after(lds_cu4 p, float dep) {
-    asm volatile("" : "+v"(p) : "v"(dep));
-    return p;
-}
 
 // s_waitcnt vmcnt(n) with the other counters left alone (gfx9 encoding).
 template <int N>
@@ -166,7 +152,6 @@ __device__ __forceinline__ void wait_vmcnt() {
     __builtin_amdgcn_s_waitcnt((N & 15) | (0x7 << 4) | (0xF << 8) | ((N >> 4) << 14));
 }
 
-typedef const u32x4 __attribute__((address_space(4)))* const_u4;   // read-only: scalar loads
 
 // ---------------------------------------------------------------------------
 // Flat page stream (BF16).  The work of one decode call is the ordered list of
@@ -174,10 +159,12 @@ typedef const u32x4 __attribute__((address_space(4)))* const_u4;   // read-only:
 // s = b*H + h holds ceil(ctx_b/64) consecutive pages.  Block i of G takes the
 // contiguous range [i*Q, min((i+1)*Q, total)), Q = ceil(total / G), so every
 // block streams the same number of pages whatever the length mix.  A block
-// writes one partial (m, l, acc) per segment it touches; segment s owns the
-// partial slots base(s) + (i - first(s)) for the blocks first(s)..last(s)
-// that cover it.  Ranges depend only on the context lengths, never on page
-// ids, and the combine adds the slots in block order: deterministic.
+// writes one partial (m, l, acc) per segment it touches, in slot i + s: both
+// the block and the segment index only grow along the stream, so no two
+// touched (block, segment) pairs share a slot, and G + B*H slots suffice.
+// Segment s is covered by the blocks first(s)..last(s) and owns the slots
+// first(s)+s .. last(s)+s.  Ranges depend only on the context lengths, never
+// on page ids, and the combine adds the slots in block order: deterministic.
 struct Seg {
     int b, h, n;       // entry, KV head, pages in the segment
     int start;         // first global page index of the segment
@@ -215,11 +202,6 @@ __device__ __forceinline__ EntryPages entry_pages(const DecodeArgs& a) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) e.n[i] = i < a.B ? (ctx_of(a, i) + kPage - 1) >> kPageShift : 0;
     return e;
-}
-
-__device__ __forceinline__ int page_id(const DecodeArgs& a, int b, int p) {
-    const int row = ld_uniform(a.table_rows, b);
-    return ld_uniform(a.pv.table, size_t(row) * a.pv.L + p);
 }
 
 // floor(x / Q) for 0 <= x < 2^24 through the fp32 reciprocal, corrected to
@@ -262,108 +244,207 @@ __device__ __forceinline__ void cursor_next(const DecodeArgs& a, const EntryPage
     }
 }
 
-// Ring-pipelined page stream (BF16): one 512-thread block per compute unit,
-// the same flat page partition as above.  The block's LDS holds a ring of NS
-// page stages (K slice + V slice each), so NS-1 pages are in flight while one
-// is computed -- enough outstanding bytes to cover HBM latency under load.
-// Eight waves: wave w works on query heads (w & 3) + 4r (r < HPW) for the
-// tokens [32*grp, 32*grp + 32) of each page, grp = w >> 2, so two waves share
-// every SIMD and each does half of a page's math.  The two token groups keep
-// their own online-softmax state and are merged through LDS when a segment
-// ends (same lane layout in both).
-//  * QK^T: lane l holds token l % 32 of its group and head_dim half l / 32;
-//    the two halves' dot products are added across lanes l, l ^ 32
-//    (v_permlane32_swap).
-//  * one workgroup barrier per page: after it, page u is complete in its
-//    stage for every wave and every wave is done with page u-1, whose stage
-//    is refilled with page u+NS-1;
-//  * the block's page slices are listed into LDS once before the ring
-//    starts, so issuing a page needs no dependent table loads.
-//  * query: scalar loads (outside the vector-memory counter the ring waits
-//    on), then held in vector registers: half a head per lane;
-//  * probabilities move from the QK lanes to the PV lanes with ds_bpermute;
-//  * finished segments' partials wait in registers (up to PMAX) and are
-//    written after the stream, so no store is ever pending while the ring's
-//    load counter is waited on; beyond PMAX they are stored at once and the
-//    ring is drained before its next wait.
-template <int D, int GQ>
-__global__ void __launch_bounds__(512) decode_bf16_ring_kernel(DecodeArgs a) {
-    constexpr int NCH = D / 8;                     // 16-byte chunks per row
-    constexpr int HCH = NCH / 2;                   // chunks per head_dim half
-    constexpr int TPI = 64 / NCH;                  // rows per 1 KiB
-    constexpr int NT = 512;
-    constexpr int SLOTS = 64 * NCH;                // 16-byte chunks per page slice
-    static_assert(NCH >= 8 && NCH <= 16 && GQ >= 4, "shape");
-    constexpr int PER_T = SLOTS / NT;              // DMA instructions per thread and plane
-    constexpr int STAGE_U4 = 2 * SLOTS;
-    constexpr int HPW = GQ / 4;                    // heads per wave
-    constexpr int NS = 4;                          // ring stages
-    constexpr int PMAX = HPW > 1 ? 1 : 2;          // partials held in registers
-    constexpr int LOADS_PER_PAGE = 2 * PER_T;
-    constexpr int RPG = NCH / 2;                   // PV row groups per token half
-    static_assert(LOADS_PER_PAGE * (NS - 1) < 64, "vmcnt range");
-    constexpr int PLIST = HPW > 1 ? 2048 : 4096;   // page slices listed per block
-    __shared__ u32x4 ring[NS][STAGE_U4];           // [stage][K slots | V slots]
-    __shared__ float merge[4][HPW][10][64];        // group-1 state handed to group 0
-    __shared__ int plist[PLIST];                   // slice (g*H + h) of each page of the range
+// ---------------------------------------------------------------------------
+// Matrix-core page stream (BF16 pages, D in {64, 128}, 1..8 entries).
+//
+// One 256-thread block per compute unit streams its range of the flat page
+// list through an LDS ring of NS page stages filled by direct-to-LDS loads,
+// so NS-1 pages are in flight while one is computed.  Wave w owns tokens
+// [16w, 16w+16) of every page and keeps its own online-softmax state.
+//  * QK^T on the matrix cores: S^T[16 tokens x 16] = K . Q^T with
+//    v_mfma_f32_16x16x32_bf16; the GQ query heads of the page's KV head are
+//    the columns (the other columns are padding: a column of the product
+//    only ever depends on its own column of Q^T, and no padding column is
+//    read back).
+//  * The accumulator layout of S^T (lane l: column l%16, tokens 4(l/16)+r)
+//    is the B-operand layout of v_mfma_f32_16x16x16_bf16, so P^T feeds PV
+//    in place.
+//  * PV on the matrix cores: O^T[16 dims x 16] += V^T . P^T per 16-dim tile,
+//    V^T read from LDS with the transposing 64-bit read (ds_read_b64_tr_b16:
+//    within a 16-lane row, lane i receives element i%4 of the 8-byte chunks
+//    addressed by lanes 4e + i/4).  P enters as two bf16 terms p_hi + p_lo
+//    (two products), about 2^-16 relative error instead of bf16's 2^-9.
+//  * Lazy rescaling: the exponent reference of a column moves only when a
+//    page's maximum exceeds it by more than 2^8, so the accumulators are
+//    rescaled a few times per segment instead of on every new maximum.
+//  * K rows are XOR-swizzled in 16-byte chunks, V rows in 32-byte units, so
+//    both reads are free of LDS bank conflicts.
+// Each page's slice, valid rows and segment-end flag are listed in LDS before
+// the ring starts.  When a segment ends, the four waves' states are merged
+// through the stage just consumed, and the merged partial waits in registers
+// until the stream ends (loads and stores share the vector-memory counter
+// that the ring waits on).  Then a segment that lies inside one block is
+// normalized and written out; the others are stored as partials, and the
+// block that brings the last partial of a segment (per-segment arrival
+// counter in the workspace) combines them in block order: one launch,
+// deterministic output.
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2v_t __attribute__((ext_vector_type(2)));
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef s16x4_t __attribute__((address_space(3)))* lds_s16x4_ptr;
+typedef char __attribute__((address_space(3)))* lds_byte_ptr;
 
-    const int w = __builtin_amdgcn_readfirstlane(int(threadIdx.x) >> 6);
-    const int lane = int(threadIdx.x) & 63;
+constexpr int kStreamPages = 1024;     // most pages one block of the page stream takes
+constexpr float kRescaleLog2 = 8.f;    // lazy rescale: probabilities stay below 2^8
+
+// One page into a ring stage: PER_T direct-to-LDS loads of the K slice and
+// PER_T of the V slice, 16 bytes per lane each (LDS[M0 + 16*lane] =
+// MEM[base + voff]).  The V stages sit 64 KiB above the K stages, and the k-th
+// load of a wave lands 4 KiB above its (k-1)-th.  Written as inline assembly
+// so that the compiler does not order every later LDS read after these loads
+// (it cannot tell the ring's stages apart and would wait for all loads in
+// flight); the kernel waits on the vector-memory counter itself before it
+// reads a stage.  M0 is restored afterwards: the compiler does not track it
+// through inline assembly.
+#define KVS_DMA_PAIR(K, V)                          \
+    "s_nop 0\n\t"                                   \
+    "global_load_lds_dwordx4 %[" #K "], %[kb]\n\t"  \
+    "s_add_u32 m0, m0, 0x10000\n\t"                 \
+    "s_nop 0\n\t"                                   \
+    "global_load_lds_dwordx4 %[" #V "], %[vb]\n\t"
+#define KVS_DMA_NEXT "s_sub_u32 m0, m0, 0xf000\n\t"
+
+__device__ __forceinline__ void fetch_page2(uint32_t lds_k, const void* kb, const void* vb, const uint32_t* ko,
+                                            const uint32_t* vo) {
+    uint32_t sv;
+    asm volatile("s_mov_b32 %[sv], m0\n\t"
+                 "s_mov_b32 m0, %[d]\n\t" KVS_DMA_PAIR(k0, v0) KVS_DMA_NEXT KVS_DMA_PAIR(k1, v1)
+                 "s_mov_b32 m0, %[sv]"
+                 : [sv] "=&s"(sv)
+                 : [d] "s"(lds_k), [kb] "s"(kb), [vb] "s"(vb), [k0] "v"(ko[0]), [k1] "v"(ko[1]), [v0] "v"(vo[0]),
+                   [v1] "v"(vo[1])
+                 : "memory", "scc");
+}
+
+__device__ __forceinline__ void fetch_page4(uint32_t lds_k, const void* kb, const void* vb, const uint32_t* ko,
+                                            const uint32_t* vo) {
+    uint32_t sv;
+    asm volatile("s_mov_b32 %[sv], m0\n\t"
+                 "s_mov_b32 m0, %[d]\n\t" KVS_DMA_PAIR(k0, v0) KVS_DMA_NEXT KVS_DMA_PAIR(k1, v1)
+                     KVS_DMA_NEXT KVS_DMA_PAIR(k2, v2) KVS_DMA_NEXT KVS_DMA_PAIR(k3, v3)
+                 "s_mov_b32 m0, %[sv]"
+                 : [sv] "=&s"(sv)
+                 : [d] "s"(lds_k), [kb] "s"(kb), [vb] "s"(vb), [k0] "v"(ko[0]), [k1] "v"(ko[1]), [k2] "v"(ko[2]),
+                   [k3] "v"(ko[3]), [v0] "v"(vo[0]), [v1] "v"(vo[1]), [v2] "v"(vo[2]), [v3] "v"(vo[3])
+                 : "memory", "scc");
+}
+#undef KVS_DMA_PAIR
+#undef KVS_DMA_NEXT
+
+// op over the four 16-lane rows (lanes l%16 + 16k); identical in every lane
+__device__ __forceinline__ float rows_max(float x) {
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
+__device__ __forceinline__ float rows_sum(float x) {
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+// two fp32 values as the bf16 pair (hi, lo) with hi = rne(x), lo = rne(x - hi)
+__device__ __forceinline__ void split_bf16(float x0, float x1, uint32_t& hi, uint32_t& lo) {
+    hi = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{x0, x1}, bf16x2v_t));
+    const float r0 = x0 - __uint_as_float(hi << 16);
+    const float r1 = x1 - __uint_as_float(hi & 0xFFFF0000u);
+    lo = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{r0, r1}, bf16x2v_t));
+}
+
+template <int D, int GQ>
+__global__ void __launch_bounds__(256) decode_bf16_mfma_kernel(DecodeArgs a) {
+    constexpr int NCH = D / 8;                     // 16-byte chunks per row
+    constexpr int NT = 256;
+    constexpr int SLOTS = 64 * NCH;                // chunks per page slice of one plane
+    constexpr int SLICE_BYTES = SLOTS * 16;
+    constexpr int PER_T = SLOTS / NT;              // direct-to-LDS loads per thread and plane
+    constexpr int NS = D == 128 ? 4 : 8;           // ring stages
+    constexpr int LOADS_PER_PAGE = 2 * PER_T;
+    constexpr int NC = D / 32;                     // QK products, k = 32 each
+    constexpr int NDT = D / 16;                    // PV tiles of 16 dims
+    constexpr int DPW = NDT / 4;                   // tiles each wave merges and writes
+    constexpr int WBUF = NDT * 4 * 64;             // floats of one wave's state in the merge area
+    constexpr int QSEG_RAW = 8192 / (GQ * D * 2);
+    constexpr int QSEG = QSEG_RAW < 1 ? 1 : (QSEG_RAW > 8 ? 8 : QSEG_RAW);   // segments with cached queries
+    constexpr int PMAX = 3;                        // merged partials held in registers
+    static_assert((D == 64 || D == 128) && GQ >= 1 && GQ <= 16, "shape");
+    static_assert(PER_T == 2 || PER_T == 4, "page fetch shapes");
+    static_assert(NS * SLICE_BYTES == 0x10000, "V stages sit 64 KiB above the K stages");
+    static_assert(LOADS_PER_PAGE * (NS - 1) < 64, "vmcnt range");
+    static_assert(2 * WBUF * 4 <= SLICE_BYTES, "two waves' merge state fit one slice");
+
+    __shared__ u32x4 ring[2][NS][SLOTS];           // [K | V][stage][slot]
+    __shared__ int2 pinfo[kStreamPages];           // per page of the range: (slice g*H + h or -1, meta)
+    __shared__ u32x4 qcache[QSEG][GQ * NCH];       // query rows of the first QSEG segments
+    __shared__ float mlbuf[4][16][2];              // per-wave (m, l) of every column at a segment end
+    __shared__ int4 ctask[PMAX];                   // segments the flushing block completes: (b, h, first slot, slots)
+    __shared__ int ctask_n;
+
     const int tid = int(threadIdx.x);
-    const int wh = w & 3, grp = w >> 2;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63, li = lane & 15, lg = lane >> 4;
     const int H = a.pv.H, M = a.pv.M, G = int(gridDim.x), i_blk = int(blockIdx.x);
 
     const EntryPages np = entry_pages(a);
+    if (i_blk == 0) {                              // entries with nothing to attend produce zeros
+        for (int b = 0; b < a.B; ++b)
+            if (np(b) == 0)
+                for (int x = tid; x < a.Hq * D; x += NT) a.out[size_t(b) * a.Hq * D + x] = 0.f;
+    }
     int total = 0;
     for (int b = 0; b < a.B; ++b) total += np(b) * H;
     if (total == 0) return;
-    const int Q = (total + G - 1) / G;
+    const int Q = (total + G - 1) / G;             // the host sizes G so that Q <= kStreamPages
     const Divider dq(Q);
     const int u0 = i_blk * Q;
-    const int u1 = min(u0 + Q, total);
-    if (u0 >= u1) return;
+    const int npg = min(u0 + Q, total) - u0;       // pages of this block
+    if (npg <= 0) return;
 
-    PageCursor start_c{Seg{0, 0, 0, 0}, 0};
-    int base = 0;
+    PageCursor cc{Seg{0, 0, 0, 0}, 0};             // the segment being computed
     {
-        int st = 0;
-        for (int b = 0; b < a.B && start_c.seg.n == 0; ++b) {
+        int st = 0;                                // first stream page of entry b
+        for (int b = 0; b < a.B; ++b) {
             const int n = np(b);
-            for (int h = 0; h < H; ++h) {
-                if (n > 0 && u0 < st + n) { start_c = PageCursor{Seg{b, h, n, st}, u0 - st}; break; }
-                base += seg_slots(st, n, dq);
-                st += n;
+            if (n > 0 && u0 < st + n * H) {
+                const int h = (u0 - st) / n;
+                cc = PageCursor{Seg{b, h, n, st + h * n}, u0 - st - h * n};
+                break;
             }
+            st += n * H;
         }
     }
 
-    const u32x4* kbase = static_cast<const u32x4*>(a.pv.lv.k_code);
-    const u32x4* vbase = static_cast<const u32x4*>(a.pv.lv.v_code);
-    // K row t keeps chunk x in slot x ^ swz(t); swz spreads 16 consecutive
-    // rows over all 64 LDS banks for 16-byte reads
-    auto swz = [](int t) { return NCH == 16 ? (t & 15) : ((t >> 1) & 7); };
-    int k_src[PER_T];
-#pragma unroll
-    for (int k = 0; k < PER_T; ++k) {
-        const int slot = k * NT + tid;
-        const int t = slot / NCH, x = slot % NCH;
-        k_src[k] = t * NCH + (x ^ swz(t));
-    }
-    // The range's page slices, listed once into LDS (vector loads of the
-    // block table, before the ring starts); ranges longer than the list read
-    // the table through scalar loads instead.
-    const bool listed = (u1 - u0) <= PLIST;
-    if (listed) {
-        PageCursor c = start_c;
-        int off = 0;
-        while (off < u1 - u0) {
-            const int cnt = min(c.seg.n - c.p, (u1 - u0) - off);
+    // Before the ring starts: every page's slice, valid rows and segment-end
+    // flag (meta = valid rows | 256 at a segment end), and the query rows of
+    // the first QSEG segments (later ones load theirs when they start).
+    {
+        PageCursor c = cc;
+        int off = 0, k = 0;
+        while (off < npg) {
+            const int cnt = min(c.seg.n - c.p, npg - off);
             const int row = ld_uniform(a.table_rows, c.seg.b);
-            const int32_t* trow = a.pv.table + size_t(row) * a.pv.L + c.p;
+            const int ctx = ctx_of(a, c.seg.b);
+            const int32_t* trow = a.pv.table + size_t(row) * a.pv.L;
             for (int i = tid; i < cnt; i += NT) {
-                const int g0 = trow[i];
-                plist[off + i] = (g0 >= 0 && g0 < M) ? g0 * H + c.seg.h : -1;
+                const int p = c.p + i;
+                const int g0 = trow[p];
+                const bool mapped = g0 >= 0 && g0 < M;
+                const int lim = mapped ? min(kPage, ctx - p * kPage) : 0;
+                const bool end = (p == c.seg.n - 1) || (off + i == npg - 1);
+                pinfo[off + i] = make_int2(mapped ? g0 * H + c.seg.h : -1, lim | (end ? 256 : 0));
             }
+            if (k < QSEG) {
+                const u32x4* qg = reinterpret_cast<const u32x4*>(
+                    a.q + (size_t(c.seg.b) * a.Hq + size_t(c.seg.h) * GQ) * D);
+                for (int i = tid; i < GQ * NCH; i += NT) qcache[k][i] = qg[i];
+            }
+            ++k;
             off += cnt;
             c.p += cnt - 1;
             cursor_next(a, np, c);
@@ -371,310 +452,383 @@ __global__ void __launch_bounds__(512) decode_bf16_ring_kernel(DecodeArgs a) {
         wait_vmcnt<0>();
         block_lds_barrier();
     }
-    auto slice_of = [&](const PageCursor& c, int u) {
-        if (listed) return __builtin_amdgcn_readfirstlane(plist[u - u0]);
-        const int g0 = page_id(a, c.seg.b, c.p);
-        return (g0 >= 0 && g0 < M) ? g0 * H + c.seg.h : -1;
-    };
-    auto fetch = [&](const PageCursor& c, int u, int st) {
-        const int sl = slice_of(c, u);
-        const size_t off = size_t(sl < 0 ? 0 : sl) * SLOTS;
+
+    // Stage layout: K slot s (row t = s / NCH, position x = s % NCH) holds
+    // chunk x ^ kswz(t) of row t; V slot s holds chunk x ^ vswz(t).
+    auto kswz = [](int t) __attribute__((always_inline)) { return NCH == 16 ? (t & 15) : ((t >> 1) & 7); };
+    auto vswz = [](int t) __attribute__((always_inline)) { return NCH == 16 ? ((t & 7) << 1) : (((t >> 1) & 3) << 1); };
+    const char* kplane = static_cast<const char*>(a.pv.lv.k_code);
+    const char* vplane = static_cast<const char*>(a.pv.lv.v_code);
+    uint32_t k_src[PER_T], v_src[PER_T];           // source byte offsets within a page slice
 #pragma unroll
-        for (int k = 0; k < PER_T; ++k) {
-            auto* kd = (void __attribute__((address_space(3)))*)(&ring[st][k * NT + w * 64]);
-            auto* vd = (void __attribute__((address_space(3)))*)(&ring[st][SLOTS + k * NT + w * 64]);
-            __builtin_amdgcn_global_load_lds((const void*)(kbase + off + k_src[k]), kd, 16, 0, 0);
-            __builtin_amdgcn_global_load_lds((const void*)(vbase + off + k * NT + tid), vd, 16, 0, 0);
-        }
-    };
-    auto wait_pages = [&](int n) {
-        switch (n) {
-            case 0: wait_vmcnt<0>(); break;
-            case 1: wait_vmcnt<LOADS_PER_PAGE * 1>(); break;
-            case 2: wait_vmcnt<LOADS_PER_PAGE * 2>(); break;
-            default: wait_vmcnt<LOADS_PER_PAGE * 3>(); break;
-        }
+    for (int k = 0; k < PER_T; ++k) {
+        const int s = k * NT + tid;
+        const int t = s / NCH, x = s % NCH;
+        k_src[k] = uint32_t(t * NCH + (x ^ kswz(t))) * 16u;
+        v_src[k] = uint32_t(t * NCH + (x ^ vswz(t))) * 16u;
+    }
+    const uint32_t ring_lds = uint32_t(reinterpret_cast<uintptr_t>((lds_byte_ptr)(&ring[0][0][0])));
+    // page fi of the range into stage fs
+    auto fetch = [&](int fi, int fs) __attribute__((always_inline)) {
+        const uint32_t dst = ring_lds + uint32_t(fs * SLICE_BYTES + w * 1024);
+        const int sl = __builtin_amdgcn_readfirstlane(pinfo[fi].x);
+        const size_t off = size_t(sl < 0 ? 0 : sl) * SLICE_BYTES;
+        if constexpr (PER_T == 4) fetch_page4(dst, kplane + off, vplane + off, k_src, v_src);
+        else fetch_page2(dst, kplane + off, vplane + off, k_src, v_src);
     };
 
-    // lane roles
-    const int qt = lane & 31;                      // QK: token within the group's half page
-    const int hd = lane >> 5;                      // QK: head_dim half
-    const int cpv = lane % NCH, tg = lane / NCH;   // PV: chunk and row group
+    // Per-lane LDS offsets into stage 0, fixed for the whole stream (the
+    // stage adds an immediate below 64 KiB).
+    //  QK A operand (K): row 16w + li, chunk 4c + lg (u32x4 index)
+    //  PV A operand (V^T, transposing read): lane li of row group lg points at
+    //  token 16w + 4lg + li/4, dims 16dt + 4(li%4) .. +3 (byte offset from the
+    //  K stage 0, i.e. including the 64 KiB to the V stages)
+    int koff[NC], voff[NDT];
+    {
+        const int t = 16 * w + li;
+#pragma unroll
+        for (int c = 0; c < NC; ++c) koff[c] = t * NCH + ((4 * c + lg) ^ kswz(t));
+        const int tv = 16 * w + 4 * lg + (li >> 2), qd = li & 3;
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt)
+            voff[dt] = 0x10000 + tv * NCH * 16 + (((2 * dt + (qd >> 1)) ^ vswz(tv)) * 16) + 8 * (qd & 1);
+    }
 
-    u32x4 qr[HPW][HCH];
-    auto load_q = [&](int b, int h) {
+    bf16x8_t qb[NC];                               // Q^T B operand: column li, chunk 4c + lg
+    auto load_q = [&](int k_seg, int b, int h) __attribute__((always_inline)) {
+        const int j = li < GQ ? li : GQ - 1;
+        if (k_seg < QSEG) {
 #pragma unroll
-        for (int r = 0; r < HPW; ++r) {
-            const int j = wh + 4 * r;
-            const const_u4 qg = (const_u4)(const void*)(a.q + (size_t(b) * a.Hq + size_t(h) * GQ + j) * D);
-#pragma unroll
-            for (int c = 0; c < HCH; ++c) {
-                // lanes of both halves issue the same scalar loads; select the half
-                const u32x4 lo = qg[c], hi = qg[HCH + c];
-                qr[r][c] = hd ? hi : lo;
-                asm volatile("" : "+v"(qr[r][c]));
+            for (int c = 0; c < NC; ++c) {
+                const u32x4 v = qcache[k_seg][j * NCH + 4 * c + lg];
+                qb[c] = __builtin_bit_cast(bf16x8_t, li < GQ ? v : u32x4{0u, 0u, 0u, 0u});
             }
+        } else {
+            const u32x4* qg = reinterpret_cast<const u32x4*>(a.q + (size_t(b) * a.Hq + size_t(h) * GQ + j) * D);
+#pragma unroll
+            for (int c = 0; c < NC; ++c) {
+                const u32x4 v = qg[4 * c + lg];
+                qb[c] = __builtin_bit_cast(bf16x8_t, li < GQ ? v : u32x4{0u, 0u, 0u, 0u});
+            }
+            wait_vmcnt<0>();                       // drains the ring: only past the cached segments
         }
     };
-    float m_run[HPW], l_part[HPW], acc[HPW][8];
-    auto reset = [&]() {
-#pragma unroll
-        for (int r = 0; r < HPW; ++r) {
-            m_run[r] = -INFINITY;
-            l_part[r] = 0.f;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) acc[r][e] = 0.f;
-        }
-    };
-    reset();
 
-    float pend_acc[PMAX][HPW][8], pend_m[PMAX][HPW], pend_l[PMAX][HPW];
-    int pend_slot[PMAX];
+    f32x4_t acc[NDT];
+    float m_ref, l_part;
+    auto reset = [&]() __attribute__((always_inline)) {
+        m_ref = -INFINITY;
+        l_part = 0.f;
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) acc[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    };
+
+    // merged partials waiting for the end of the stream
+    f32x4_t pend_acc[PMAX][DPW];
+    float pend_m[PMAX], pend_l[PMAX];
+    int pend_b[PMAX], pend_h[PMAX], pend_first[PMAX], pend_nsl[PMAX];   // pend_first: first slot of the segment
     int npend = 0;
-    auto store_partial = [&](int slot, const float (&ac)[HPW][8], const float (&mm)[HPW], const float (&ll)[HPW]) {
-#pragma unroll
-        for (int r = 0; r < HPW; ++r) {
-            const size_t it = size_t(slot) * GQ + (wh + 4 * r);
-            if (tg == 0) {
-                float4* dst = reinterpret_cast<float4*>(a.part_acc + it * D + cpv * 8);
-                dst[0] = make_float4(ac[r][0], ac[r][1], ac[r][2], ac[r][3]);
-                dst[1] = make_float4(ac[r][4], ac[r][5], ac[r][6], ac[r][7]);
-            }
-            if (lane == 0) {
-                a.part_ml[it * 2] = mm[r];
-                a.part_ml[it * 2 + 1] = ll[r];
-            }
-        }
+
+    // Partials cross blocks (and the L2s of different dies) as device-scope
+    // relaxed atomic stores and loads, which are coherent without cache
+    // write-back or invalidation (device-scope fences are L2-wide maintenance
+    // operations here, costly for every block on the die).  A block counts
+    // its arrival only after its partial stores completed (vmcnt 0), and the
+    // last block loads the partials only after its increment returned.
+    auto st_dev = [](float* p, float v) __attribute__((always_inline)) {
+        __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     };
-    bool stores_pending = false;
-    // segment end: sum row groups, merge the two token groups, keep or store
-    auto finish_segment = [&](int slot) {
-        float ac[HPW][8], ll[HPW], mm[HPW];
+    auto ld_dev = [](const float* p) __attribute__((always_inline)) {
+        return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    };
+    float combine_m[(GQ * D + NT - 1) / NT], combine_l[(GQ * D + NT - 1) / NT], combine_a[(GQ * D + NT - 1) / NT];
+    // The combine issues every load of a thread before it uses any (one
+    // memory round trip for up to four partials per element).
+    auto combine = [&](int b, int h, int first, int nsl) __attribute__((always_inline)) {
+        constexpr int CMAX = 4;
+        constexpr int XPT = (GQ * D + NT - 1) / NT;   // outputs per thread
+        for (int k0 = 0; k0 < nsl; k0 += CMAX) {     // more than CMAX partials: folded in rounds
+            const int kn = min(CMAX, nsl - k0);
+            float mk[XPT][CMAX], lk[XPT][CMAX], ak[XPT][CMAX];
 #pragma unroll
-        for (int r = 0; r < HPW; ++r) {
+            for (int xi = 0; xi < XPT; ++xi) {
+                const int x = tid + xi * NT;
+                const int j = x / D, d = x % D;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                float x = acc[r][e];
-#pragma unroll
-                for (int o = NCH; o < 64; o <<= 1) x += __shfl_xor(x, o, 64);
-                ac[r][e] = x;
-            }
-            ll[r] = wave_sum(l_part[r]) * 0.5f;     // both head_dim halves counted each p
-            mm[r] = m_run[r];
-        }
-        if (grp == 1) {
-#pragma unroll
-            for (int r = 0; r < HPW; ++r) {
-#pragma unroll
-                for (int e = 0; e < 8; ++e) merge[wh][r][e][lane] = ac[r][e];
-                merge[wh][r][8][lane] = mm[r];
-                merge[wh][r][9][lane] = ll[r];
-            }
-        }
-        block_lds_barrier();
-        if (grp == 0) {
-#pragma unroll
-            for (int r = 0; r < HPW; ++r) {
-                const float m1 = merge[wh][r][8][lane], l1 = merge[wh][r][9][lane];
-                const float mx = fmaxf(mm[r], m1);
-                const float w0 = mx == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mm[r] - mx);
-                const float w1 = mx == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m1 - mx);
-#pragma unroll
-                for (int e = 0; e < 8; ++e) ac[r][e] = ac[r][e] * w0 + merge[wh][r][e][lane] * w1;
-                ll[r] = ll[r] * w0 + l1 * w1;
-                mm[r] = mx;
-            }
-            if (npend < PMAX) {
-#pragma unroll
-                for (int k = 0; k < PMAX; ++k) {
-                    if (k == npend) {
-#pragma unroll
-                        for (int r = 0; r < HPW; ++r) {
-#pragma unroll
-                            for (int e = 0; e < 8; ++e) pend_acc[k][r][e] = ac[r][e];
-                            pend_m[k][r] = mm[r];
-                            pend_l[k][r] = ll[r];
-                        }
-                        pend_slot[k] = slot;
+                for (int k = 0; k < CMAX; ++k) {
+                    if (x < GQ * D && k < kn) {
+                        const size_t it = size_t(first + k0 + k) * GQ + j;
+                        mk[xi][k] = ld_dev(a.part_ml + it * 2);
+                        lk[xi][k] = ld_dev(a.part_ml + it * 2 + 1);
+                        ak[xi][k] = ld_dev(a.part_acc + it * D + d);
                     }
                 }
-            } else {
-                store_partial(slot, ac, mm, ll);
+            }
+#pragma unroll
+            for (int xi = 0; xi < XPT; ++xi) {
+                const int x = tid + xi * NT;
+                if (x >= GQ * D) continue;
+                const int j = x / D, d = x % D;
+                float* o = a.out + (size_t(b) * a.Hq + size_t(h) * GQ + j) * D + d;
+                float mx = -INFINITY;
+#pragma unroll
+                for (int k = 0; k < CMAX; ++k)
+                    if (k < kn) mx = fmaxf(mx, mk[xi][k]);
+                float l = 0.f, acc_x = 0.f;
+                if (k0 > 0) {                          // fold in the earlier rounds
+                    mx = fmaxf(mx, combine_m[xi]);
+                }
+#pragma unroll
+                for (int k = 0; k < CMAX; ++k) {
+                    if (k < kn) {
+                        const float wgt = mk[xi][k] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mk[xi][k] - mx);
+                        l += lk[xi][k] * wgt;
+                        acc_x += ak[xi][k] * wgt;
+                    }
+                }
+                if (k0 > 0) {
+                    const float wp = combine_m[xi] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(combine_m[xi] - mx);
+                    l += combine_l[xi] * wp;
+                    acc_x += combine_a[xi] * wp;
+                }
+                combine_m[xi] = mx;
+                combine_l[xi] = l;
+                combine_a[xi] = acc_x;
+                if (k0 + kn == nsl) *o = l > 0.f ? acc_x * (1.f / l) : 0.f;
             }
         }
-        if (npend < PMAX) ++npend;
-        else stores_pending = true;
+    };
+
+    // Write out or store every pending partial, count arrivals, combine the
+    // segments this block completes.  Block-uniform; waits for all memory
+    // traffic of the block.
+    auto flush = [&]() __attribute__((always_inline)) {
+#pragma unroll
+        for (int k = 0; k < PMAX; ++k) {
+            if (k >= npend) break;
+            if (li < GQ) {
+                if (pend_nsl[k] == 1) {
+                    const float inv = pend_l[k] > 0.f ? 1.f / pend_l[k] : 0.f;
+                    float* o = a.out + (size_t(pend_b[k]) * a.Hq + size_t(pend_h[k]) * GQ + li) * D + 4 * lg;
+#pragma unroll
+                    for (int kk = 0; kk < DPW; ++kk) {
+                        const f32x4_t v = pend_acc[k][kk] * inv;
+                        *reinterpret_cast<float4*>(o + 16 * (w * DPW + kk)) = make_float4(v[0], v[1], v[2], v[3]);
+                    }
+                } else {
+                    const size_t it = size_t(i_blk + pend_b[k] * H + pend_h[k]) * GQ + li;
+                    float* o = a.part_acc + it * D + 4 * lg;
+#pragma unroll
+                    for (int kk = 0; kk < DPW; ++kk)
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) st_dev(o + 16 * (w * DPW + kk) + r, pend_acc[k][kk][r]);
+                    if (w == 0 && lg == 0) {
+                        st_dev(a.part_ml + it * 2, pend_m[k]);
+                        st_dev(a.part_ml + it * 2 + 1, pend_l[k]);
+                    }
+                }
+            }
+        }
+        wait_vmcnt<0>();                           // this block's partials are complete
+        __syncthreads();
+        if (tid == 0) {                            // arrive; list the segments this block completes
+            int nt = 0;
+#pragma unroll
+            for (int k = 0; k < PMAX; ++k) {
+                if (k >= npend) break;
+                if (pend_nsl[k] > 1) {
+                    const unsigned old = atomicAdd(a.arrive + pend_b[k] * H + pend_h[k], 1u);
+                    if (int(old) + 1 == pend_nsl[k]) {
+                        ctask[nt] = make_int4(pend_b[k], pend_h[k], pend_first[k], pend_nsl[k]);
+                        ++nt;
+                    }
+                }
+            }
+            ctask_n = nt;
+        }
+        __syncthreads();
+        const int nt = __builtin_amdgcn_readfirstlane(ctask_n);
+#pragma unroll 1
+        for (int t = 0; t < nt; ++t) {
+            const int4 c = ctask[t];
+            const int cb = __builtin_amdgcn_readfirstlane(c.x), ch = __builtin_amdgcn_readfirstlane(c.y);
+            combine(cb, ch, __builtin_amdgcn_readfirstlane(c.z), __builtin_amdgcn_readfirstlane(c.w));
+            if (tid == 0)                          // ready for the next call
+                __hip_atomic_store(a.arrive + cb * H + ch, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        wait_vmcnt<0>();
+        __syncthreads();
+        npend = 0;
+    };
+
+    // segment end: merge the four waves' states through stage st (waves 0-1
+    // use its K slice, waves 2-3 its V slice)
+    auto finish_segment = [&](int st) __attribute__((always_inline)) {
+        const float lw = rows_sum(l_part);
+        block_lds_barrier();                       // every wave is done reading stage st
+        auto wbuf = [&](int v) __attribute__((always_inline)) {
+            return reinterpret_cast<float*>(&ring[v >> 1][st][0]) + (v & 1) * WBUF;
+        };
+        float* mine = wbuf(w);
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) mine[(dt * 4 + r) * 64 + lane] = acc[dt][r];
+        if (lg == 0) {
+            mlbuf[w][li][0] = m_ref;
+            mlbuf[w][li][1] = lw;
+        }
+        block_lds_barrier();
+        float mw[4], cw[4], mx = -INFINITY, lt = 0.f;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            mw[v] = mlbuf[v][li][0];
+            mx = fmaxf(mx, mw[v]);
+        }
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            cw[v] = mw[v] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mw[v] - mx);
+            lt += mlbuf[v][li][1] * cw[v];
+        }
+        f32x4_t merged[DPW];
+#pragma unroll
+        for (int kk = 0; kk < DPW; ++kk) {
+            const int dt = w * DPW + kk;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                float x = 0.f;
+#pragma unroll
+                for (int v = 0; v < 4; ++v) x += wbuf(v)[(dt * 4 + r) * 64 + lane] * cw[v];
+                merged[kk][r] = x;
+            }
+        }
+        if (npend == PMAX) flush();                // rare: many segments in one range
+#pragma unroll
+        for (int k = 0; k < PMAX; ++k) {
+            if (k == npend) {
+#pragma unroll
+                for (int kk = 0; kk < DPW; ++kk) pend_acc[k][kk] = merged[kk];
+                pend_m[k] = mx;
+                pend_l[k] = lt;
+                pend_b[k] = cc.seg.b;
+                pend_h[k] = cc.seg.h;
+                pend_first[k] = dq(cc.seg.start) + cc.seg.b * H + cc.seg.h;
+                pend_nsl[k] = seg_slots(cc.seg.start, cc.seg.n, dq);
+            }
+        }
+        ++npend;
         reset();
     };
 
-    PageCursor ic = start_c;                        // next page to issue
-    int issued = u0;
-    for (int k = 0; k < NS - 1 && issued < u1; ++k) {
-        fetch(ic, issued, (issued - u0) % NS);
-        cursor_next(a, np, ic);
-        ++issued;
-    }
-    PageCursor cc = start_c;                        // page being computed
-    int slot = base + (i_blk - dq(cc.seg.start));
-    int cur_ctx = ctx_of(a, cc.seg.b);
-    load_q(cc.seg.b, cc.seg.h);
-
-    for (int u = u0; u < u1; ++u) {
-        const int st = (u - u0) % NS;
-        if (stores_pending) { wait_vmcnt<0>(); stores_pending = false; }
-        else wait_pages(issued - u - 1);
-        // page u is in stage st for every wave, and every wave is done with page
-        // u-1, whose stage takes page u+NS-1
-        block_lds_barrier();
-        if (issued < u1) {
-            fetch(ic, issued, (issued - u0) % NS);
-            cursor_next(a, np, ic);
-            ++issued;
-        }
-
-        const int sl = slice_of(cc, u);
-        const int lim = sl >= 0 ? min(kPage, cur_ctx - cc.p * kPage) : 0;
-        const int glim = lim - 32 * grp;            // valid rows of this group's half page
-        const u32x4* kst = &ring[st][0];
-        const u32x4* vst = &ring[st][SLOTS];
-        {
-            // QK^T: token 32*grp + qt, head_dim half hd
-            const int t = 32 * grp + qt;
-            u32x4 krow[HCH];
+    int seg_k = 0;
+    load_q(seg_k, cc.seg.b, cc.seg.h);
+    reset();
+    const int tb = 16 * w + 4 * lg;                 // token of accumulator register r: tb + r
+    int meta_ring[NS];                              // meta of the pages in the ring, by stage
 #pragma unroll
-            for (int c = 0; c < HCH; ++c) krow[c] = kst[t * NCH + ((hd * HCH + c) ^ swz(t))];
-            const bool valid = qt < glim;
-            float pj[HPW];
-#pragma unroll
-            for (int r = 0; r < HPW; ++r) {
-                float sc4[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int c = 0; c < HCH; ++c) {
-                    sc4[0] = dot2_bf16(krow[c].x, qr[r][c].x, sc4[0]);
-                    sc4[1] = dot2_bf16(krow[c].y, qr[r][c].y, sc4[1]);
-                    sc4[2] = dot2_bf16(krow[c].z, qr[r][c].z, sc4[2]);
-                    sc4[3] = dot2_bf16(krow[c].w, qr[r][c].w, sc4[3]);
-                }
-                float sc = (sc4[0] + sc4[1]) + (sc4[2] + sc4[3]);
-                {                                   // add the other head_dim half (lane ^ 32)
-                    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(sc), __float_as_uint(sc),
-                                                                     false, false);
-                    sc = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
-                }
-                const float sj = valid ? sc * a.scale_log2 : -INFINITY;
-                const float mn = fmaxf(m_run[r], wave_max_uniform(sj));
-                if (mn > m_run[r]) {                // wave-uniform
-                    const float alpha = __builtin_amdgcn_exp2f(m_run[r] - mn);
-                    l_part[r] *= alpha;
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) acc[r][e] *= alpha;
-                    m_run[r] = mn;
-                }
-                pj[r] = valid ? __builtin_amdgcn_exp2f(sj - m_run[r]) : 0.f;
-                l_part[r] += pj[r];
-            }
-            // PV: rows 32*grp + i*TPI + tg (i < RPG), chunk cpv
-            auto pv_rows = [&](auto masked) {
-                u32x4 vrow[RPG];
-                float pt[HPW][RPG];
-#pragma unroll
-                for (int i = 0; i < RPG; ++i) vrow[i] = vst[(32 * grp + i * TPI + tg) * NCH + cpv];
-#pragma unroll
-                for (int r = 0; r < HPW; ++r)
-#pragma unroll
-                    for (int i = 0; i < RPG; ++i)
-                        pt[r][i] = __int_as_float(
-                            __builtin_amdgcn_ds_bpermute((i * TPI + tg) << 2, __float_as_int(pj[r])));
-#pragma unroll
-                for (int i = 0; i < RPG; ++i) {
-                    u32x4 vv = vrow[i];
-                    if constexpr (decltype(masked)::value) {
-                        // rows past the frontier hold stale bytes: never let them reach acc
-                        if (i * TPI + tg >= glim) vv = u32x4{0u, 0u, 0u, 0u};
-                    }
-                    float v[8];
-#pragma unroll
-                    for (int e2 = 0; e2 < 4; ++e2) {
-                        v[2 * e2] = __uint_as_float(vv[e2] << 16);
-                        v[2 * e2 + 1] = __uint_as_float(vv[e2] & 0xFFFF0000u);
-                    }
-#pragma unroll
-                    for (int r = 0; r < HPW; ++r)
-#pragma unroll
-                        for (int e = 0; e < 8; ++e) acc[r][e] += pt[r][i] * v[e];
-                }
-            };
-            if (glim < 32) pv_rows(std::true_type{});
-            else pv_rows(std::false_type{});
-        }
-
-        const bool more = u + 1 < u1;
-        if (cc.p + 1 == cc.seg.n || !more) {
-            finish_segment(slot);
-            if (more) {
-                base += seg_slots(cc.seg.start, cc.seg.n, dq);
-                cursor_next(a, np, cc);
-                slot = base + (i_blk - dq(cc.seg.start));
-                cur_ctx = ctx_of(a, cc.seg.b);
-                load_q(cc.seg.b, cc.seg.h);
-            }
+    for (int k = 0; k < NS - 1; ++k) {
+        if (k < npg) {
+            fetch(k, k);
+            meta_ring[k] = __builtin_amdgcn_readfirstlane(pinfo[k].y);
         } else {
-            cursor_next(a, np, cc);
+            meta_ring[k] = 0;
         }
     }
+    meta_ring[NS - 1] = 0;
 
-    if (grp == 0) {
-#pragma unroll
-        for (int k = 0; k < PMAX; ++k)
-            if (k < npend) store_partial(pend_slot[k], pend_acc[k], pend_m[k], pend_l[k]);
-    }
-}
+    // one page in stage J (compile time, so every LDS offset is an immediate)
+    auto step = [&](auto jc, int i) __attribute__((always_inline)) {
+        constexpr int J = decltype(jc)::value;
+        constexpr int FS = (J + NS - 1) % NS;
+        // page i is in stage J for every wave, and every wave is done with
+        // page i-1, whose stage takes page i+NS-1; the last NS-1 pages of
+        // the range wait for everything in flight (nothing is left to issue)
+        if (i + NS - 1 < npg) {
+            wait_vmcnt<LOADS_PER_PAGE * (NS - 2)>();
+            block_lds_barrier();
+            fetch(i + NS - 1, FS);
+            meta_ring[FS] = __builtin_amdgcn_readfirstlane(pinfo[i + NS - 1].y);
+        } else {
+            wait_vmcnt<0>();
+            block_lds_barrier();
+        }
 
-// Combine the stream partials of each (entry, query head), in block order.
-template <int D, int GQ>
-__global__ void __launch_bounds__(64) decode_stream_combine_kernel(DecodeArgs a, int G) {
-    constexpr int EPL = D / 64;
-    const int lane = int(threadIdx.x);
-    const int b = int(blockIdx.x) / a.Hq, j = int(blockIdx.x) % a.Hq;
-    const int h = j / GQ, jj = j % GQ;
-    const int H = a.pv.H;
-    const EntryPages np = entry_pages(a);
-    int total = 0;
-    for (int bb = 0; bb < a.B; ++bb) total += np(bb) * H;
-    float* o = a.out + (size_t(b) * a.Hq + j) * D + lane * EPL;
-    const int n = np(b);
-    if (n == 0) {
+        const int meta = meta_ring[J];
+        const int lim = meta & 255;
+        if (lim > 16 * w) {                         // this wave has valid rows in the page
+            const u32x4* kst = &ring[0][J][0];
+            f32x4_t s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) o[e] = 0.f;
-        return;
-    }
-    const int Q = (total + G - 1) / G;
-    const Divider dq(Q);
-    int base = 0, start = 0;
-    for (int bb = 0; bb <= b; ++bb) {
-        const int ns = np(bb);
-        const int hh_end = bb < b ? H : h;
-        for (int hh = 0; hh < hh_end; ++hh) {
-            base += seg_slots(start, ns, dq);
-            start += ns;
+            for (int c = 0; c < NC; ++c)
+                s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kst[koff[c]]), qb[c], s,
+                                                            0, 0, 0);
+            float sj[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) sj[r] = s[r] * a.scale_log2;
+            if (lim < kPage) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    if (tb + r >= lim) sj[r] = -INFINITY;
+            }
+            const float pm = rows_max(fmaxf(fmaxf(sj[0], sj[1]), fmaxf(sj[2], sj[3])));   // finite
+            if (__builtin_amdgcn_ballot_w64(pm > m_ref + kRescaleLog2)) {
+                const float mn = pm > m_ref + kRescaleLog2 ? pm : m_ref;
+                const float alpha = m_ref == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_ref - mn);
+                l_part *= alpha;
+#pragma unroll
+                for (int dt = 0; dt < NDT; ++dt) acc[dt] *= alpha;
+                m_ref = mn;
+            }
+            float p[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) p[r] = __builtin_amdgcn_exp2f(sj[r] - m_ref);
+            l_part += (p[0] + p[1]) + (p[2] + p[3]);
+            uint32_t h01, l01, h23, l23;
+            split_bf16(p[0], p[1], h01, l01);
+            split_bf16(p[2], p[3], h23, l23);
+            const s16x4_t phi = __builtin_bit_cast(s16x4_t, u32x2{h01, h23});
+            const s16x4_t plo = __builtin_bit_cast(s16x4_t, u32x2{l01, l23});
+            if (lim < kPage) {
+                // rows past the frontier hold stale bytes (possibly NaN): this
+                // wave clears its own rows of the V slice, which only it reads
+                const int r0 = max(lim, 16 * w), rows = 16 * w + 16 - r0;
+                u32x4* vrows = &ring[1][J][r0 * NCH];
+                for (int x = lane; x < rows * NCH; x += 64) vrows[x] = u32x4{0u, 0u, 0u, 0u};
+                wave_lds_sync();
+            }
+            const lds_byte_ptr vst = (lds_byte_ptr)(&ring[0][J][0]);   // voff includes the K-to-V distance
+#pragma unroll
+            for (int dt = 0; dt < NDT; ++dt) {
+                const s16x4_t va = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_ptr)(vst + voff[dt]));
+                acc[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, phi, acc[dt], 0, 0, 0);
+                acc[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, plo, acc[dt], 0, 0, 0);
+            }
+        }
+
+        if (meta & 256) {
+            finish_segment(J);
+            if (i + 1 < npg) {
+                cc.p = cc.seg.n - 1;
+                cursor_next(a, np, cc);
+                ++seg_k;
+                load_q(seg_k, cc.seg.b, cc.seg.h);
+            }
+        }
+    };
+
+    for (int i0 = 0; i0 < npg; i0 += NS) {
+        step(std::integral_constant<int, 0>{}, i0);
+        if (i0 + 1 < npg) step(std::integral_constant<int, 1>{}, i0 + 1);
+        if (i0 + 2 < npg) step(std::integral_constant<int, 2>{}, i0 + 2);
+        if (i0 + 3 < npg) step(std::integral_constant<int, 3>{}, i0 + 3);
+        if constexpr (NS == 8) {
+            if (i0 + 4 < npg) step(std::integral_constant<int, 4>{}, i0 + 4);
+            if (i0 + 5 < npg) step(std::integral_constant<int, 5>{}, i0 + 5);
+            if (i0 + 6 < npg) step(std::integral_constant<int, 6>{}, i0 + 6);
+            if (i0 + 7 < npg) step(std::integral_constant<int, 7>{}, i0 + 7);
         }
     }
-    const int cnt = seg_slots(start, n, dq);
-    float mx = -INFINITY;
-    for (int k = 0; k < cnt; ++k) mx = fmaxf(mx, a.part_ml[(size_t(base + k) * GQ + jj) * 2]);
-    float l = 0.f, acc[EPL];
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) acc[e] = 0.f;
-    for (int k = 0; k < cnt; ++k) {
-        const size_t it = size_t(base + k) * GQ + jj;
-        const float wgt = exp2f(a.part_ml[it * 2] - mx);
-        l += a.part_ml[it * 2 + 1] * wgt;
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) acc[e] += a.part_acc[it * D + lane * EPL + e] * wgt;
-    }
-    const float inv = 1.f / l;
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) o[e] = acc[e] * inv;
+    flush();
 }
 
 // Combine the chunks of each (entry, query head) in chunk order.
@@ -724,23 +878,28 @@ int chunk_pages() {
 }
 
 // Blocks of the page-stream kernel: one per compute unit (its LDS ring takes
-// the whole 160 KiB), every one streaming the same share of pages.
-int stream_grid() {
-    static const int g = [] {
-        int dev = 0, cus = 0;
+// most of the 160 KiB), every one streaming the same share of pages; more
+// when a share would exceed the kStreamPages a block lists in LDS.
+int stream_grid(const PoolView& pv, int B, int max_seq_len) {
+    static const int cus = [] {
+        int dev = 0, n = 0;
         if (hipGetDevice(&dev) != hipSuccess ||
-            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
-            cus = 256;
+            hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+            n = 256;
         const char* e = std::getenv("KVS_DECODE_STREAM_BLOCKS");
         const int v = e ? std::atoi(e) : 0;
-        return (v >= 1 && v <= 65536) ? v : cus;
+        return (v >= 1 && v <= 4096) ? v : n;
     }();
-    return g;
+    const long long bound = (long long)B * pv.H * ((max_seq_len + kPage - 1) / kPage);
+    const long long need = (bound + kStreamPages - 1) / kStreamPages;
+    return int(need > cus ? need : cus);
 }
 
-bool stream_path(const PoolView& pv, int gq) {
-    return pv.k_codec == CODEC_BF16 && pv.v_codec == CODEC_BF16 && (pv.D == 64 || pv.D == 128) &&
-           (gq == 4 || gq == 8);
+// The matrix-core page stream covers BF16 pages with D in {64, 128} and up to
+// eight entries per call; everything else takes the chunked split kernel.
+bool stream_path(const PoolView& pv, int B, int gq) {
+    return pv.k_codec == CODEC_BF16 && pv.v_codec == CODEC_BF16 && (pv.D == 64 || pv.D == 128) && B <= 8 &&
+           (gq == 1 || gq == 2 || gq == 4 || gq == 8);
 }
 
 int max_chunks_for(int max_seq_len) {
@@ -750,20 +909,16 @@ int max_chunks_for(int max_seq_len) {
 
 template <int D, int GQ>
 hipError_t launch_gq(const DecodeArgs& a, hipStream_t s) {
+    if constexpr (D == 64 || D == 128) {
+        if (stream_path(a.pv, a.B, GQ)) {
+            decode_bf16_mfma_kernel<D, GQ><<<dim3(unsigned(stream_grid(a.pv, a.B, a.max_ctx))), 256, 0, s>>>(a);
+            return hipGetLastError();
+        }
+    }
     const int items = a.B * a.pv.H * a.max_chunks;
     const dim3 grid(unsigned((items + 3) / 4));
     const int kc = a.pv.k_codec, vc = a.pv.v_codec;
     bool launched = false;
-    if constexpr ((D == 64 || D == 128) && (GQ == 4 || GQ == 8)) {
-        if (kc == CODEC_BF16 && vc == CODEC_BF16) {
-            const int G = stream_grid();
-            decode_bf16_ring_kernel<D, GQ><<<dim3(unsigned(G)), 512, 0, s>>>(a);
-            hipError_t e = hipGetLastError();
-            if (e != hipSuccess) return e;
-            decode_stream_combine_kernel<D, GQ><<<dim3(unsigned(a.B * a.Hq)), 64, 0, s>>>(a, G);
-            return hipGetLastError();
-        }
-    }
 #define KVS_DEC_CASE(K, V)                                                       \
     if (!launched && kc == K && vc == V) {                                      \
         if (items > 0) decode_split_kernel<D, GQ, K, V><<<grid, 256, 0, s>>>(a); \
@@ -801,20 +956,25 @@ bool decode_supported(const PoolView& pv, int Hq) {
     return (pv.D == 64 || pv.D == 128 || pv.D == 256) && (gq == 1 || gq == 2 || gq == 4 || gq == 8);
 }
 
-// partial (m, l) pairs first, then the accumulators from a 256-byte boundary
+// Workspace: [arrival counters][partial (m, l) pairs][partial accumulators],
+// each from a 256-byte boundary.  The counters (one per (table row, KV head),
+// sized by the pool so the layout does not move with B) must be zero before
+// the first call; every call leaves them zero.
+size_t arrive_bytes(const PoolView& pv) { return (size_t(pv.C) * pv.H * sizeof(uint32_t) + 255) / 256 * 256; }
+
 size_t ml_floats(size_t items, size_t gq) { return (items * gq * 2 + 63) / 64 * 64; }
 
 // partial slots: one per split (chunk path) or one per (block, touched
 // segment) of the page stream, at most G + B*H
 size_t partial_slots(const PoolView& pv, int B, int gq, int max_seq_len) {
-    if (stream_path(pv, gq)) return size_t(stream_grid()) + size_t(B) * pv.H;
+    if (stream_path(pv, B, gq)) return size_t(stream_grid(pv, B, max_seq_len)) + size_t(B) * pv.H;
     return size_t(B) * pv.H * max_chunks_for(max_seq_len);
 }
 
 size_t decode_workspace_bytes(const PoolView& pv, int B, int Hq, int max_seq_len) {
     const size_t gq = pv.H ? size_t(Hq / pv.H) : 0;
     const size_t items = partial_slots(pv, B, int(gq), max_seq_len);
-    return (ml_floats(items, gq) + items * gq * size_t(pv.D)) * sizeof(float);
+    return arrive_bytes(pv) + (ml_floats(items, gq) + items * gq * size_t(pv.D)) * sizeof(float);
 }
 
 hipError_t launch_decode(const PoolView& pv, int B, int Hq, const int32_t* table_rows, const int32_t* seq_lens,
@@ -833,7 +993,8 @@ hipError_t launch_decode(const PoolView& pv, int B, int Hq, const int32_t* table
     a.max_ctx = max_seq_len;
     const int gq = Hq / pv.H;
     const size_t items = partial_slots(pv, B, gq, max_seq_len);
-    a.part_ml = static_cast<float*>(ws);
+    a.arrive = static_cast<uint32_t*>(ws);
+    a.part_ml = reinterpret_cast<float*>(static_cast<char*>(ws) + arrive_bytes(pv));
     a.part_acc = a.part_ml + ml_floats(items, size_t(gq));
     a.scale_log2 = sm_scale * kLog2e;
     switch (pv.D) {

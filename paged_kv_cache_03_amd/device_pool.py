@@ -109,7 +109,9 @@ class DevicePool:
 
     def workspace(self, B: int, Hq: int, max_seq_len: int, max_q_len: int = 0) -> torch.Tensor:
         n = abi.paged_attn_workspace_bytes(self.handle, B, Hq, max_seq_len, max_q_len)
-        return torch.empty(max(n, 256), dtype=torch.uint8, device=self.device)
+        # zero once: decode's per-segment arrival counters start at zero, and
+        # every call leaves them zero again
+        return torch.zeros(max(n, 256), dtype=torch.uint8, device=self.device)
 
     def decode(self, layer: int, Hq: int, table_rows: torch.Tensor, seq_lens: torch.Tensor, max_seq_len: int,
                q: torch.Tensor, sm_scale: float, out: torch.Tensor, ws: torch.Tensor) -> None:
