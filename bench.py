@@ -31,6 +31,8 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0
 METRIC = "paged decode KV GB/s (% of HBM peak) + decode steps/s at C=8, 32K ctx"
+PROFILES = os.path.join(ROOT, "profiles")
+DECODE_SRC = os.path.join(ROOT, "paged_kv_cache_03_amd", "csrc", "decode.hip")
 
 
 def log(msg: str) -> None:
@@ -58,6 +60,51 @@ def kv_read_bytes(table, wl) -> tuple[int, int]:
             logical += c
     unique = int(np.sum(list(cols.values())))
     return unique * wl.H * bpth, logical * wl.H * bpth
+
+
+def decode_kernel_name(wl) -> str:
+    """The kernel that carries paged_attn_decode for this workload (as rocprofv3 names it)."""
+    gq = wl.Hq // wl.H
+    if wl.profile == "BF16" and wl.D in (64, 128) and gq in (1, 2, 4, 8) and wl.B <= 8:
+        return f"decode_bf16_mfma_kernel<{wl.D}, {gq}>"
+    return "decode_split_kernel + decode_combine_kernel"
+
+
+def measured_traffic(wl) -> int | None:
+    """HBM bytes per decode launch from the committed rocprofv3 counter summary
+    (FETCH_SIZE + WRITE_SIZE, each scaled by what the same counter reads for a
+    plain device copy of known size), or None when there is none for this
+    workload or the decode source has changed since it was taken."""
+    import hashlib
+    path = os.path.join(PROFILES, f"decode_traffic_{wl.name}.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    with open(DECODE_SRC, "rb") as f:
+        sha = hashlib.sha256(f.read()).hexdigest()
+    if kv.get("source_sha256") != sha or kv.get("kernel") != decode_kernel_name(wl):
+        return None
+    try:
+        return int(float(kv["traffic_bytes_per_dispatch"]))
+    except (KeyError, ValueError):
+        return None
+
+
+def copy_calibration(n_bytes: int = 1 << 30, reps: int = 4) -> int:
+    """A plain device-to-device copy of known size, for scaling the FETCH_SIZE /
+    WRITE_SIZE counters of the decode kernel (run under rocprofv3 --pmc)."""
+    import torch
+    src = torch.ones(n_bytes, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": n_bytes, "reps": reps}), flush=True)
+    return 0
 
 
 def cpu_baseline(wl, seconds_hint: float = 20.0) -> dict:
@@ -122,11 +169,16 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", type=int, default=2, help="workload number (decode workloads: 1-4)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a 1 GiB device copy (counter calibration under rocprofv3 --pmc)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("this build runs on one GPU only: --gpus must be 1 (the path's sharding is described in DESIGN.md)",
               file=sys.stderr)
         return 2
+
+    if args.copy_calibration:
+        return copy_calibration()
 
     import numpy as np
     import torch
@@ -211,9 +263,9 @@ def main() -> int:
         "steps_per_s": round(1000.0 / ms_per_step, 2),
         "hbm_frac": round(value / HBM_PEAK_GBS, 4),
         "kv_bytes_per_step": {"unique": wl.layers * unique, "logical": wl.layers * logical},
-        "roofline": {"kernel": "paged_attn_decode (split + combine launches)", "bound": "hbm",
+        "roofline": {"kernel": decode_kernel_name(wl), "bound": "hbm",
                      "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(wl),
                      "bytes_per_launch": per_decode, "launch_ms": round(dec_ms, 5)},
         "cpu_baseline": cpu,
     }
