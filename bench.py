@@ -66,7 +66,7 @@ def decode_kernel_name(wl) -> str:
     """The kernel that carries paged_attn_decode for this workload (as rocprofv3 names it)."""
     gq = wl.Hq // wl.H
     if wl.profile == "BF16" and wl.D in (64, 128) and gq in (1, 2, 4, 8) and wl.B <= 8:
-        return f"decode_bf16_mfma_kernel<{wl.D}, {gq}>"
+        return f"paged_stream_kernel<{wl.D}, {gq}, 1, false>"
     return "decode_split_kernel + decode_combine_kernel"
 
 

@@ -46,6 +46,13 @@ struct DecodeArgs {
     int32_t chunk_pages;
     int32_t max_chunks;
     int32_t max_ctx;    // host bound on seq_lens (<= max_context); larger values are clipped
+    // chunk mode (verify / chunked prefill through the page stream): entry b's
+    // query tokens are rows cu_q[b] .. cu_q[b+1]-1 at positions q_pos0[b] + i;
+    // entries with more than max_cols query columns (tokens x GQ) are left to
+    // another kernel
+    const int32_t* q_pos0;
+    const int32_t* cu_q;
+    int32_t max_cols;
 };
 
 // One 64-lane wave per work item (entry b, KV head h, chunk c).  QK: lane t
@@ -357,8 +364,50 @@ __device__ __forceinline__ void split_bf16(float x0, float x1, uint32_t& hi, uin
     lo = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{r0, r1}, bf16x2v_t));
 }
 
-template <int D, int GQ>
-__global__ void __launch_bounds__(256) decode_bf16_mfma_kernel(DecodeArgs a) {
+// Query columns of one entry for the page stream: keys [0, keys) exist; query
+// token i (row cu + i of q and out) sees keys [0, min(n0 + i + 1, keys)).
+// One query token per entry (decode) is n0 = ctx - 1, T = 1.  `owned` is false
+// for an entry a chunk-mode launch leaves to another kernel.
+struct EntryQ {
+    int n0, T, cu, keys;
+    bool owned;
+};
+
+template <bool CHUNK, int GQ>
+__device__ __forceinline__ EntryQ entry_q(const DecodeArgs& a, int b) {
+    const int row = ld_uniform(a.table_rows, b);
+    const bool ok = row >= 0 && row < a.pv.C;
+    if constexpr (!CHUNK) {
+        const int ctx = ok ? min(ld_uniform(a.seq_lens, b), a.max_ctx) : 0;
+        return EntryQ{ctx - 1, 1, b, ctx, true};
+    } else {
+        const int c0 = ld_uniform(a.cu_q, b), T = ld_uniform(a.cu_q, b + 1) - c0;
+        const int n0 = ld_uniform(a.q_pos0, b);
+        const int keys = ok ? max(0, min(n0 + T, a.max_ctx)) : 0;
+        return EntryQ{n0, T, c0, keys, T * GQ <= a.max_cols};
+    }
+}
+
+template <bool CHUNK, int GQ>
+__device__ __forceinline__ EntryPages stream_pages(const DecodeArgs& a) {
+    EntryPages e;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        int n = 0;
+        if (i < a.B) {
+            const EntryQ q = entry_q<CHUNK, GQ>(a, i);
+            n = (q.owned && q.T > 0) ? (q.keys + kPage - 1) >> kPageShift : 0;
+        }
+        e.n[i] = n;
+    }
+    return e;
+}
+
+// NCT column tiles of 16 query columns; column c = 16*ct + lane%16 holds query
+// token c / GQ and head c % GQ of the segment's KV head.  CHUNK: several query
+// tokens per entry (verify / chunked prefill) with a causal limit per column.
+template <int D, int GQ, int NCT, bool CHUNK>
+__global__ void __launch_bounds__(256) paged_stream_kernel(DecodeArgs a) {
     constexpr int NCH = D / 8;                     // 16-byte chunks per row
     constexpr int NT = 256;
     constexpr int SLOTS = 64 * NCH;                // chunks per page slice of one plane
@@ -370,10 +419,12 @@ __global__ void __launch_bounds__(256) decode_bf16_mfma_kernel(DecodeArgs a) {
     constexpr int NDT = D / 16;                    // PV tiles of 16 dims
     constexpr int DPW = NDT / 4;                   // tiles each wave merges and writes
     constexpr int WBUF = NDT * 4 * 64;             // floats of one wave's state in the merge area
-    constexpr int QSEG_RAW = 8192 / (GQ * D * 2);
+    constexpr int NCOL = 16 * NCT;                 // query columns (partial slot width)
+    constexpr int QCOL = CHUNK ? NCOL : GQ;        // query rows cached per segment
+    constexpr int QSEG_RAW = (CHUNK ? 16384 : 8192) / (QCOL * D * 2);
     constexpr int QSEG = QSEG_RAW < 1 ? 1 : (QSEG_RAW > 8 ? 8 : QSEG_RAW);   // segments with cached queries
-    constexpr int PMAX = 3;                        // merged partials held in registers
-    static_assert((D == 64 || D == 128) && GQ >= 1 && GQ <= 16, "shape");
+    constexpr int PMAX = NCT == 1 ? 3 : 2;         // merged partials held in registers
+    static_assert((D == 64 || D == 128) && GQ >= 1 && GQ <= 16 && GQ <= NCOL, "shape");
     static_assert(PER_T == 2 || PER_T == 4, "page fetch shapes");
     static_assert(NS * SLICE_BYTES == 0x10000, "V stages sit 64 KiB above the K stages");
     static_assert(LOADS_PER_PAGE * (NS - 1) < 64, "vmcnt range");
@@ -381,7 +432,7 @@ __global__ void __launch_bounds__(256) decode_bf16_mfma_kernel(DecodeArgs a) {
 
     __shared__ u32x4 ring[2][NS][SLOTS];           // [K | V][stage][slot]
     __shared__ int2 pinfo[kStreamPages];           // per page of the range: (slice g*H + h or -1, meta)
-    __shared__ u32x4 qcache[QSEG][GQ * NCH];       // query rows of the first QSEG segments
+    __shared__ u32x4 qcache[QSEG][QCOL * NCH];     // query rows of the first QSEG segments
     __shared__ float mlbuf[4][16][2];              // per-wave (m, l) of every column at a segment end
     __shared__ int4 ctask[PMAX];                   // segments the flushing block completes: (b, h, first slot, slots)
     __shared__ int ctask_n;
@@ -391,11 +442,14 @@ __global__ void __launch_bounds__(256) decode_bf16_mfma_kernel(DecodeArgs a) {
     const int lane = tid & 63, li = lane & 15, lg = lane >> 4;
     const int H = a.pv.H, M = a.pv.M, G = int(gridDim.x), i_blk = int(blockIdx.x);
 
-    const EntryPages np = entry_pages(a);
+    const EntryPages np = stream_pages<CHUNK, GQ>(a);
     if (i_blk == 0) {                              // entries with nothing to attend produce zeros
-        for (int b = 0; b < a.B; ++b)
-            if (np(b) == 0)
-                for (int x = tid; x < a.Hq * D; x += NT) a.out[size_t(b) * a.Hq * D + x] = 0.f;
+        for (int b = 0; b < a.B; ++b) {
+            if (np(b) != 0) continue;
+            const EntryQ e = entry_q<CHUNK, GQ>(a, b);
+            if (!e.owned) continue;
+            for (int x = tid; x < e.T * a.Hq * D; x += NT) a.out[size_t(e.cu) * a.Hq * D + x] = 0.f;
+        }
     }
     int total = 0;
     for (int b = 0; b < a.B; ++b) total += np(b) * H;
@@ -420,29 +474,35 @@ __global__ void __launch_bounds__(256) decode_bf16_mfma_kernel(DecodeArgs a) {
         }
     }
 
-    // Before the ring starts: every page's slice, valid rows and segment-end
-    // flag (meta = valid rows | 256 at a segment end), and the query rows of
-    // the first QSEG segments (later ones load theirs when they start).
+    // query row of column c of entry e (head h*GQ + c%GQ of token c/GQ)
+    auto q_row = [&](const EntryQ& e, int h, int c) __attribute__((always_inline)) {
+        return a.q + (size_t(e.cu + c / GQ) * a.Hq + size_t(h) * GQ + c % GQ) * D;
+    };
+
+    // Before the ring starts: every page's slice, valid rows, segment-end flag
+    // and page index (meta = valid rows | 256 at a segment end | page << 9),
+    // and the query rows of the first QSEG segments (later ones load theirs
+    // when they start).
     {
         PageCursor c = cc;
         int off = 0, k = 0;
         while (off < npg) {
             const int cnt = min(c.seg.n - c.p, npg - off);
             const int row = ld_uniform(a.table_rows, c.seg.b);
-            const int ctx = ctx_of(a, c.seg.b);
+            const EntryQ e = entry_q<CHUNK, GQ>(a, c.seg.b);
             const int32_t* trow = a.pv.table + size_t(row) * a.pv.L;
             for (int i = tid; i < cnt; i += NT) {
                 const int p = c.p + i;
                 const int g0 = trow[p];
                 const bool mapped = g0 >= 0 && g0 < M;
-                const int lim = mapped ? min(kPage, ctx - p * kPage) : 0;
+                const int lim = mapped ? min(kPage, e.keys - p * kPage) : 0;
                 const bool end = (p == c.seg.n - 1) || (off + i == npg - 1);
-                pinfo[off + i] = make_int2(mapped ? g0 * H + c.seg.h : -1, lim | (end ? 256 : 0));
+                pinfo[off + i] = make_int2(mapped ? g0 * H + c.seg.h : -1, lim | (end ? 256 : 0) | (p << 9));
             }
             if (k < QSEG) {
-                const u32x4* qg = reinterpret_cast<const u32x4*>(
-                    a.q + (size_t(c.seg.b) * a.Hq + size_t(c.seg.h) * GQ) * D);
-                for (int i = tid; i < GQ * NCH; i += NT) qcache[k][i] = qg[i];
+                const int ncol = min(e.T * GQ, QCOL);
+                for (int i = tid; i < ncol * NCH; i += NT)
+                    qcache[k][i] = reinterpret_cast<const u32x4*>(q_row(e, c.seg.h, i / NCH))[i % NCH];
             }
             ++k;
             off += cnt;
@@ -494,38 +554,59 @@ __global__ void __launch_bounds__(256) decode_bf16_mfma_kernel(DecodeArgs a) {
             voff[dt] = 0x10000 + tv * NCH * 16 + (((2 * dt + (qd >> 1)) ^ vswz(tv)) * 16) + 8 * (qd & 1);
     }
 
-    bf16x8_t qb[NC];                               // Q^T B operand: column li, chunk 4c + lg
-    auto load_q = [&](int k_seg, int b, int h) __attribute__((always_inline)) {
-        const int j = li < GQ ? li : GQ - 1;
+    bf16x8_t qb[NCT][NC];                          // Q^T B operand: column 16ct + li, chunk 4c + lg
+    int klim[NCT];                                 // keys this lane's column sees (0: padding column)
+    int kmin = 0;                                  // smallest limit of a real column of the segment
+    auto start_segment = [&](int k_seg, int b, int h) __attribute__((always_inline)) {
+        const EntryQ e = entry_q<CHUNK, GQ>(a, b);
+        const int ncol = e.T * GQ;
+        kmin = min(e.n0 + 1, e.keys);
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) {
+            const int col = 16 * ct + li;
+            klim[ct] = col < ncol ? min(e.n0 + col / GQ + 1, e.keys) : 0;
+        }
         if (k_seg < QSEG) {
 #pragma unroll
-            for (int c = 0; c < NC; ++c) {
-                const u32x4 v = qcache[k_seg][j * NCH + 4 * c + lg];
-                qb[c] = __builtin_bit_cast(bf16x8_t, li < GQ ? v : u32x4{0u, 0u, 0u, 0u});
+            for (int ct = 0; ct < NCT; ++ct) {
+                const int col = 16 * ct + li;
+                const int cq = min(col, QCOL - 1);
+#pragma unroll
+                for (int c = 0; c < NC; ++c) {
+                    const u32x4 v = qcache[k_seg][cq * NCH + 4 * c + lg];
+                    qb[ct][c] = __builtin_bit_cast(bf16x8_t, col < ncol ? v : u32x4{0u, 0u, 0u, 0u});
+                }
             }
         } else {
-            const u32x4* qg = reinterpret_cast<const u32x4*>(a.q + (size_t(b) * a.Hq + size_t(h) * GQ + j) * D);
 #pragma unroll
-            for (int c = 0; c < NC; ++c) {
-                const u32x4 v = qg[4 * c + lg];
-                qb[c] = __builtin_bit_cast(bf16x8_t, li < GQ ? v : u32x4{0u, 0u, 0u, 0u});
+            for (int ct = 0; ct < NCT; ++ct) {
+                const int col = 16 * ct + li;
+                const u32x4* qg = reinterpret_cast<const u32x4*>(q_row(e, h, col < ncol ? col : 0));
+#pragma unroll
+                for (int c = 0; c < NC; ++c) {
+                    const u32x4 v = qg[4 * c + lg];
+                    qb[ct][c] = __builtin_bit_cast(bf16x8_t, col < ncol ? v : u32x4{0u, 0u, 0u, 0u});
+                }
             }
             wait_vmcnt<0>();                       // drains the ring: only past the cached segments
         }
     };
 
-    f32x4_t acc[NDT];
-    float m_ref, l_part;
+    f32x4_t acc[NCT][NDT];
+    float m_ref[NCT], l_part[NCT];
     auto reset = [&]() __attribute__((always_inline)) {
-        m_ref = -INFINITY;
-        l_part = 0.f;
 #pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) acc[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        for (int ct = 0; ct < NCT; ++ct) {
+            m_ref[ct] = -INFINITY;
+            l_part[ct] = 0.f;
+#pragma unroll
+            for (int dt = 0; dt < NDT; ++dt) acc[ct][dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        }
     };
 
     // merged partials waiting for the end of the stream
-    f32x4_t pend_acc[PMAX][DPW];
-    float pend_m[PMAX], pend_l[PMAX];
+    f32x4_t pend_acc[PMAX][NCT][DPW];
+    float pend_m[PMAX][NCT], pend_l[PMAX][NCT];
     int pend_b[PMAX], pend_h[PMAX], pend_first[PMAX], pend_nsl[PMAX];   // pend_first: first slot of the segment
     int npend = 0;
 
@@ -541,60 +622,67 @@ __global__ void __launch_bounds__(256) decode_bf16_mfma_kernel(DecodeArgs a) {
     auto ld_dev = [](const float* p) __attribute__((always_inline)) {
         return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     };
-    float combine_m[(GQ * D + NT - 1) / NT], combine_l[(GQ * D + NT - 1) / NT], combine_a[(GQ * D + NT - 1) / NT];
-    // The combine issues every load of a thread before it uses any (one
-    // memory round trip for up to four partials per element).
+    // The combine issues the loads of four outputs of a thread before it uses
+    // any (one memory round trip for up to four partials per output).
     auto combine = [&](int b, int h, int first, int nsl) __attribute__((always_inline)) {
-        constexpr int CMAX = 4;
-        constexpr int XPT = (GQ * D + NT - 1) / NT;   // outputs per thread
-        for (int k0 = 0; k0 < nsl; k0 += CMAX) {     // more than CMAX partials: folded in rounds
-            const int kn = min(CMAX, nsl - k0);
-            float mk[XPT][CMAX], lk[XPT][CMAX], ak[XPT][CMAX];
+        constexpr int CMAX = 4, XB = 4;
+        const EntryQ e = entry_q<CHUNK, GQ>(a, b);
+        const int ncol = min(e.T * GQ, QCOL);
+#pragma unroll 1
+        for (int x0 = tid; x0 < ncol * D; x0 += XB * NT) {
+            float fm[XB], fl[XB], fa[XB];         // running fold of the earlier rounds
+#pragma unroll 1
+            for (int k0 = 0; k0 < nsl; k0 += CMAX) {   // more than CMAX partials: folded in rounds
+                const int kn = min(CMAX, nsl - k0);
+                float mk[XB][CMAX], lk[XB][CMAX], ak[XB][CMAX];
 #pragma unroll
-            for (int xi = 0; xi < XPT; ++xi) {
-                const int x = tid + xi * NT;
-                const int j = x / D, d = x % D;
+                for (int xb = 0; xb < XB; ++xb) {
+                    const int x = x0 + xb * NT;
+                    const int c = x / D, d = x % D;
 #pragma unroll
-                for (int k = 0; k < CMAX; ++k) {
-                    if (x < GQ * D && k < kn) {
-                        const size_t it = size_t(first + k0 + k) * GQ + j;
-                        mk[xi][k] = ld_dev(a.part_ml + it * 2);
-                        lk[xi][k] = ld_dev(a.part_ml + it * 2 + 1);
-                        ak[xi][k] = ld_dev(a.part_acc + it * D + d);
+                    for (int k = 0; k < CMAX; ++k) {
+                        if (x < ncol * D && k < kn) {
+                            const size_t it = size_t(first + k0 + k) * NCOL + c;
+                            mk[xb][k] = ld_dev(a.part_ml + it * 2);
+                            lk[xb][k] = ld_dev(a.part_ml + it * 2 + 1);
+                            ak[xb][k] = ld_dev(a.part_acc + it * D + d);
+                        }
                     }
+                }
+#pragma unroll
+                for (int xb = 0; xb < XB; ++xb) {
+                    const int x = x0 + xb * NT;
+                    if (x >= ncol * D) continue;
+                    float mx = k0 > 0 ? fm[xb] : -INFINITY;
+#pragma unroll
+                    for (int k = 0; k < CMAX; ++k)
+                        if (k < kn) mx = fmaxf(mx, mk[xb][k]);
+                    float l = 0.f, acc_x = 0.f;
+#pragma unroll
+                    for (int k = 0; k < CMAX; ++k) {
+                        if (k < kn) {
+                            const float wgt = mk[xb][k] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mk[xb][k] - mx);
+                            l += lk[xb][k] * wgt;
+                            acc_x += ak[xb][k] * wgt;
+                        }
+                    }
+                    if (k0 > 0) {
+                        const float wp = fm[xb] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(fm[xb] - mx);
+                        l += fl[xb] * wp;
+                        acc_x += fa[xb] * wp;
+                    }
+                    fm[xb] = mx;
+                    fl[xb] = l;
+                    fa[xb] = acc_x;
                 }
             }
 #pragma unroll
-            for (int xi = 0; xi < XPT; ++xi) {
-                const int x = tid + xi * NT;
-                if (x >= GQ * D) continue;
-                const int j = x / D, d = x % D;
-                float* o = a.out + (size_t(b) * a.Hq + size_t(h) * GQ + j) * D + d;
-                float mx = -INFINITY;
-#pragma unroll
-                for (int k = 0; k < CMAX; ++k)
-                    if (k < kn) mx = fmaxf(mx, mk[xi][k]);
-                float l = 0.f, acc_x = 0.f;
-                if (k0 > 0) {                          // fold in the earlier rounds
-                    mx = fmaxf(mx, combine_m[xi]);
-                }
-#pragma unroll
-                for (int k = 0; k < CMAX; ++k) {
-                    if (k < kn) {
-                        const float wgt = mk[xi][k] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mk[xi][k] - mx);
-                        l += lk[xi][k] * wgt;
-                        acc_x += ak[xi][k] * wgt;
-                    }
-                }
-                if (k0 > 0) {
-                    const float wp = combine_m[xi] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(combine_m[xi] - mx);
-                    l += combine_l[xi] * wp;
-                    acc_x += combine_a[xi] * wp;
-                }
-                combine_m[xi] = mx;
-                combine_l[xi] = l;
-                combine_a[xi] = acc_x;
-                if (k0 + kn == nsl) *o = l > 0.f ? acc_x * (1.f / l) : 0.f;
+            for (int xb = 0; xb < XB; ++xb) {
+                const int x = x0 + xb * NT;
+                if (x >= ncol * D) continue;
+                const int c = x / D, d = x % D;
+                float* o = a.out + (size_t(e.cu + c / GQ) * a.Hq + size_t(h) * GQ + c % GQ) * D + d;
+                *o = fl[xb] > 0.f ? fa[xb] * (1.f / fl[xb]) : 0.f;
             }
         }
     };
@@ -606,25 +694,30 @@ __global__ void __launch_bounds__(256) decode_bf16_mfma_kernel(DecodeArgs a) {
 #pragma unroll
         for (int k = 0; k < PMAX; ++k) {
             if (k >= npend) break;
-            if (li < GQ) {
+            const EntryQ e = entry_q<CHUNK, GQ>(a, pend_b[k]);
+            const int ncol = e.T * GQ;
+#pragma unroll
+            for (int ct = 0; ct < NCT; ++ct) {
+                const int c = 16 * ct + li;
+                if (c >= ncol) continue;
                 if (pend_nsl[k] == 1) {
-                    const float inv = pend_l[k] > 0.f ? 1.f / pend_l[k] : 0.f;
-                    float* o = a.out + (size_t(pend_b[k]) * a.Hq + size_t(pend_h[k]) * GQ + li) * D + 4 * lg;
+                    const float inv = pend_l[k][ct] > 0.f ? 1.f / pend_l[k][ct] : 0.f;
+                    float* o = a.out + (size_t(e.cu + c / GQ) * a.Hq + size_t(pend_h[k]) * GQ + c % GQ) * D + 4 * lg;
 #pragma unroll
                     for (int kk = 0; kk < DPW; ++kk) {
-                        const f32x4_t v = pend_acc[k][kk] * inv;
+                        const f32x4_t v = pend_acc[k][ct][kk] * inv;
                         *reinterpret_cast<float4*>(o + 16 * (w * DPW + kk)) = make_float4(v[0], v[1], v[2], v[3]);
                     }
                 } else {
-                    const size_t it = size_t(i_blk + pend_b[k] * H + pend_h[k]) * GQ + li;
+                    const size_t it = size_t(i_blk + pend_b[k] * H + pend_h[k]) * NCOL + c;
                     float* o = a.part_acc + it * D + 4 * lg;
 #pragma unroll
                     for (int kk = 0; kk < DPW; ++kk)
 #pragma unroll
-                        for (int r = 0; r < 4; ++r) st_dev(o + 16 * (w * DPW + kk) + r, pend_acc[k][kk][r]);
+                        for (int r = 0; r < 4; ++r) st_dev(o + 16 * (w * DPW + kk) + r, pend_acc[k][ct][kk][r]);
                     if (w == 0 && lg == 0) {
-                        st_dev(a.part_ml + it * 2, pend_m[k]);
-                        st_dev(a.part_ml + it * 2 + 1, pend_l[k]);
+                        st_dev(a.part_ml + it * 2, pend_m[k][ct]);
+                        st_dev(a.part_ml + it * 2 + 1, pend_l[k][ct]);
                     }
                 }
             }
@@ -662,54 +755,63 @@ __global__ void __launch_bounds__(256) decode_bf16_mfma_kernel(DecodeArgs a) {
     };
 
     // segment end: merge the four waves' states through stage st (waves 0-1
-    // use its K slice, waves 2-3 its V slice)
+    // use its K slice, waves 2-3 its V slice), one column tile at a time
     auto finish_segment = [&](int st) __attribute__((always_inline)) {
-        const float lw = rows_sum(l_part);
-        block_lds_barrier();                       // every wave is done reading stage st
         auto wbuf = [&](int v) __attribute__((always_inline)) {
             return reinterpret_cast<float*>(&ring[v >> 1][st][0]) + (v & 1) * WBUF;
         };
-        float* mine = wbuf(w);
+        f32x4_t merged[NCT][DPW];
+        float mxs[NCT], lts[NCT];
 #pragma unroll
-        for (int dt = 0; dt < NDT; ++dt)
+        for (int ct = 0; ct < NCT; ++ct) {
+            const float lw = rows_sum(l_part[ct]);
+            block_lds_barrier();                   // every wave is done with stage st (or the last round)
+            float* mine = wbuf(w);
 #pragma unroll
-            for (int r = 0; r < 4; ++r) mine[(dt * 4 + r) * 64 + lane] = acc[dt][r];
-        if (lg == 0) {
-            mlbuf[w][li][0] = m_ref;
-            mlbuf[w][li][1] = lw;
-        }
-        block_lds_barrier();
-        float mw[4], cw[4], mx = -INFINITY, lt = 0.f;
+            for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-            mw[v] = mlbuf[v][li][0];
-            mx = fmaxf(mx, mw[v]);
-        }
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-            cw[v] = mw[v] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mw[v] - mx);
-            lt += mlbuf[v][li][1] * cw[v];
-        }
-        f32x4_t merged[DPW];
-#pragma unroll
-        for (int kk = 0; kk < DPW; ++kk) {
-            const int dt = w * DPW + kk;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                float x = 0.f;
-#pragma unroll
-                for (int v = 0; v < 4; ++v) x += wbuf(v)[(dt * 4 + r) * 64 + lane] * cw[v];
-                merged[kk][r] = x;
+                for (int r = 0; r < 4; ++r) mine[(dt * 4 + r) * 64 + lane] = acc[ct][dt][r];
+            if (lg == 0) {
+                mlbuf[w][li][0] = m_ref[ct];
+                mlbuf[w][li][1] = lw;
             }
+            block_lds_barrier();
+            float mw[4], cw[4], mx = -INFINITY, lt = 0.f;
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                mw[v] = mlbuf[v][li][0];
+                mx = fmaxf(mx, mw[v]);
+            }
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                cw[v] = mw[v] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mw[v] - mx);
+                lt += mlbuf[v][li][1] * cw[v];
+            }
+#pragma unroll
+            for (int kk = 0; kk < DPW; ++kk) {
+                const int dt = w * DPW + kk;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    float x = 0.f;
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) x += wbuf(v)[(dt * 4 + r) * 64 + lane] * cw[v];
+                    merged[ct][kk][r] = x;
+                }
+            }
+            mxs[ct] = mx;
+            lts[ct] = lt;
         }
         if (npend == PMAX) flush();                // rare: many segments in one range
 #pragma unroll
         for (int k = 0; k < PMAX; ++k) {
             if (k == npend) {
 #pragma unroll
-                for (int kk = 0; kk < DPW; ++kk) pend_acc[k][kk] = merged[kk];
-                pend_m[k] = mx;
-                pend_l[k] = lt;
+                for (int ct = 0; ct < NCT; ++ct) {
+#pragma unroll
+                    for (int kk = 0; kk < DPW; ++kk) pend_acc[k][ct][kk] = merged[ct][kk];
+                    pend_m[k][ct] = mxs[ct];
+                    pend_l[k][ct] = lts[ct];
+                }
                 pend_b[k] = cc.seg.b;
                 pend_h[k] = cc.seg.h;
                 pend_first[k] = dq(cc.seg.start) + cc.seg.b * H + cc.seg.h;
@@ -721,7 +823,7 @@ __global__ void __launch_bounds__(256) decode_bf16_mfma_kernel(DecodeArgs a) {
     };
 
     int seg_k = 0;
-    load_q(seg_k, cc.seg.b, cc.seg.h);
+    start_segment(seg_k, cc.seg.b, cc.seg.h);
     reset();
     const int tb = 16 * w + 4 * lg;                 // token of accumulator register r: tb + r
     int meta_ring[NS];                              // meta of the pages in the ring, by stage
@@ -754,40 +856,55 @@ __global__ void __launch_bounds__(256) decode_bf16_mfma_kernel(DecodeArgs a) {
         }
 
         const int meta = meta_ring[J];
-        const int lim = meta & 255;
+        const int lim = meta & 255;                 // valid rows of the page
         if (lim > 16 * w) {                         // this wave has valid rows in the page
+            const int tok0 = (meta >> 9) * kPage;   // first key of the page
             const u32x4* kst = &ring[0][J][0];
-            f32x4_t s = {0.f, 0.f, 0.f, 0.f};
+            f32x4_t s[NCT];
 #pragma unroll
-            for (int c = 0; c < NC; ++c)
-                s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kst[koff[c]]), qb[c], s,
-                                                            0, 0, 0);
-            float sj[4];
+            for (int ct = 0; ct < NCT; ++ct) s[ct] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int r = 0; r < 4; ++r) sj[r] = s[r] * a.scale_log2;
-            if (lim < kPage) {
+            for (int c = 0; c < NC; ++c) {
+                const bf16x8_t kk = __builtin_bit_cast(bf16x8_t, kst[koff[c]]);
 #pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    if (tb + r >= lim) sj[r] = -INFINITY;
+                for (int ct = 0; ct < NCT; ++ct)
+                    s[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kk, qb[ct][c], s[ct], 0, 0, 0);
             }
-            const float pm = rows_max(fmaxf(fmaxf(sj[0], sj[1]), fmaxf(sj[2], sj[3])));   // finite
-            if (__builtin_amdgcn_ballot_w64(pm > m_ref + kRescaleLog2)) {
-                const float mn = pm > m_ref + kRescaleLog2 ? pm : m_ref;
-                const float alpha = m_ref == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_ref - mn);
-                l_part *= alpha;
+            const bool masked = tok0 + kPage > kmin;   // a real column's limit falls inside the page
+            s16x4_t phi[NCT], plo[NCT];
 #pragma unroll
-                for (int dt = 0; dt < NDT; ++dt) acc[dt] *= alpha;
-                m_ref = mn;
+            for (int ct = 0; ct < NCT; ++ct) {
+                float sj[4];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) sj[r] = s[ct][r] * a.scale_log2;
+                if (masked) {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        if (tok0 + tb + r >= klim[ct]) sj[r] = -INFINITY;
+                }
+                const float pm = rows_max(fmaxf(fmaxf(sj[0], sj[1]), fmaxf(sj[2], sj[3])));
+                if (__builtin_amdgcn_ballot_w64(pm > m_ref[ct] + kRescaleLog2)) {
+                    const float mn = pm > m_ref[ct] + kRescaleLog2 ? pm : m_ref[ct];
+                    const float alpha = m_ref[ct] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_ref[ct] - mn);
+                    l_part[ct] *= alpha;
+#pragma unroll
+                    for (int dt = 0; dt < NDT; ++dt) acc[ct][dt] *= alpha;
+                    m_ref[ct] = mn;
+                }
+                float p[4];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    p[r] = __builtin_amdgcn_exp2f(sj[r] - m_ref[ct]);
+                    // a column with no visible key yet (chunk mode) has no reference
+                    if constexpr (CHUNK) p[r] = m_ref[ct] == -INFINITY ? 0.f : p[r];
+                }
+                l_part[ct] += (p[0] + p[1]) + (p[2] + p[3]);
+                uint32_t h01, l01, h23, l23;
+                split_bf16(p[0], p[1], h01, l01);
+                split_bf16(p[2], p[3], h23, l23);
+                phi[ct] = __builtin_bit_cast(s16x4_t, u32x2{h01, h23});
+                plo[ct] = __builtin_bit_cast(s16x4_t, u32x2{l01, l23});
             }
-            float p[4];
-#pragma unroll
-            for (int r = 0; r < 4; ++r) p[r] = __builtin_amdgcn_exp2f(sj[r] - m_ref);
-            l_part += (p[0] + p[1]) + (p[2] + p[3]);
-            uint32_t h01, l01, h23, l23;
-            split_bf16(p[0], p[1], h01, l01);
-            split_bf16(p[2], p[3], h23, l23);
-            const s16x4_t phi = __builtin_bit_cast(s16x4_t, u32x2{h01, h23});
-            const s16x4_t plo = __builtin_bit_cast(s16x4_t, u32x2{l01, l23});
             if (lim < kPage) {
                 // rows past the frontier hold stale bytes (possibly NaN): this
                 // wave clears its own rows of the V slice, which only it reads
@@ -800,8 +917,11 @@ __global__ void __launch_bounds__(256) decode_bf16_mfma_kernel(DecodeArgs a) {
 #pragma unroll
             for (int dt = 0; dt < NDT; ++dt) {
                 const s16x4_t va = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_ptr)(vst + voff[dt]));
-                acc[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, phi, acc[dt], 0, 0, 0);
-                acc[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, plo, acc[dt], 0, 0, 0);
+#pragma unroll
+                for (int ct = 0; ct < NCT; ++ct) {
+                    acc[ct][dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, phi[ct], acc[ct][dt], 0, 0, 0);
+                    acc[ct][dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, plo[ct], acc[ct][dt], 0, 0, 0);
+                }
             }
         }
 
@@ -811,7 +931,7 @@ __global__ void __launch_bounds__(256) decode_bf16_mfma_kernel(DecodeArgs a) {
                 cc.p = cc.seg.n - 1;
                 cursor_next(a, np, cc);
                 ++seg_k;
-                load_q(seg_k, cc.seg.b, cc.seg.h);
+                start_segment(seg_k, cc.seg.b, cc.seg.h);
             }
         }
     };
@@ -911,7 +1031,7 @@ template <int D, int GQ>
 hipError_t launch_gq(const DecodeArgs& a, hipStream_t s) {
     if constexpr (D == 64 || D == 128) {
         if (stream_path(a.pv, a.B, GQ)) {
-            decode_bf16_mfma_kernel<D, GQ><<<dim3(unsigned(stream_grid(a.pv, a.B, a.max_ctx))), 256, 0, s>>>(a);
+            paged_stream_kernel<D, GQ, 1, false><<<dim3(unsigned(stream_grid(a.pv, a.B, a.max_ctx))), 256, 0, s>>>(a);
             return hipGetLastError();
         }
     }
@@ -971,10 +1091,61 @@ size_t partial_slots(const PoolView& pv, int B, int gq, int max_seq_len) {
     return size_t(B) * pv.H * max_chunks_for(max_seq_len);
 }
 
+// partial slot width: the page stream keeps one 16-column tile per slot
+size_t slot_cols(const PoolView& pv, int B, int gq) { return stream_path(pv, B, gq) ? 16 : size_t(gq); }
+
 size_t decode_workspace_bytes(const PoolView& pv, int B, int Hq, int max_seq_len) {
     const size_t gq = pv.H ? size_t(Hq / pv.H) : 0;
     const size_t items = partial_slots(pv, B, int(gq), max_seq_len);
-    return arrive_bytes(pv) + (ml_floats(items, gq) + items * gq * size_t(pv.D)) * sizeof(float);
+    const size_t cols = slot_cols(pv, B, int(gq));
+    return arrive_bytes(pv) + (ml_floats(items, cols) + items * cols * size_t(pv.D)) * sizeof(float);
+}
+
+bool stream_chunk_supported(const PoolView& pv, int B, int gq) { return stream_path(pv, B, gq); }
+
+size_t stream_chunk_workspace_bytes(const PoolView& pv, int B, int max_seq_len) {
+    const size_t items = size_t(stream_grid(pv, B, max_seq_len)) + size_t(B) * pv.H;
+    return arrive_bytes(pv) + (ml_floats(items, 32) + items * 32 * size_t(pv.D)) * sizeof(float);
+}
+
+template <int D>
+hipError_t launch_chunk_d(const DecodeArgs& a, int gq, hipStream_t s) {
+    const dim3 grid(unsigned(stream_grid(a.pv, a.B, a.max_ctx)));
+    switch (gq) {
+        case 1: paged_stream_kernel<D, 1, 2, true><<<grid, 256, 0, s>>>(a); break;
+        case 2: paged_stream_kernel<D, 2, 2, true><<<grid, 256, 0, s>>>(a); break;
+        case 4: paged_stream_kernel<D, 4, 2, true><<<grid, 256, 0, s>>>(a); break;
+        case 8: paged_stream_kernel<D, 8, 2, true><<<grid, 256, 0, s>>>(a); break;
+        default: return hipErrorNotSupported;
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_stream_chunk(const PoolView& pv, int B, int Hq, const int32_t* table_rows, const int32_t* q_pos0,
+                               const int32_t* cu_q, int max_seq_len, const void* q, float sm_scale, float* out,
+                               void* ws, int max_cols, hipStream_t s) {
+    DecodeArgs a{};
+    a.pv = pv;
+    a.table_rows = table_rows;
+    a.q_pos0 = q_pos0;
+    a.cu_q = cu_q;
+    a.max_cols = max_cols;
+    a.q = static_cast<const uint16_t*>(q);
+    a.out = out;
+    a.B = B;
+    a.Hq = Hq;
+    a.max_ctx = max_seq_len;
+    const int gq = Hq / pv.H;
+    const size_t items = size_t(stream_grid(pv, B, max_seq_len)) + size_t(B) * pv.H;
+    a.arrive = static_cast<uint32_t*>(ws);
+    a.part_ml = reinterpret_cast<float*>(static_cast<char*>(ws) + arrive_bytes(pv));
+    a.part_acc = a.part_ml + ml_floats(items, 32);
+    a.scale_log2 = sm_scale * kLog2e;
+    switch (pv.D) {
+        case 64: return launch_chunk_d<64>(a, gq, s);
+        case 128: return launch_chunk_d<128>(a, gq, s);
+    }
+    return hipErrorNotSupported;
 }
 
 hipError_t launch_decode(const PoolView& pv, int B, int Hq, const int32_t* table_rows, const int32_t* seq_lens,
@@ -995,7 +1166,7 @@ hipError_t launch_decode(const PoolView& pv, int B, int Hq, const int32_t* table
     const size_t items = partial_slots(pv, B, gq, max_seq_len);
     a.arrive = static_cast<uint32_t*>(ws);
     a.part_ml = reinterpret_cast<float*>(static_cast<char*>(ws) + arrive_bytes(pv));
-    a.part_acc = a.part_ml + ml_floats(items, size_t(gq));
+    a.part_acc = a.part_ml + ml_floats(items, slot_cols(pv, B, gq));
     a.scale_log2 = sm_scale * kLog2e;
     switch (pv.D) {
         case 64: return launch_d<64>(a, gq, s);

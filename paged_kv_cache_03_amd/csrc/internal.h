@@ -63,6 +63,15 @@ hipError_t launch_decode(const PoolView& pv, int B, int Hq, const int32_t* table
                          int max_seq_len, const void* q, float sm_scale, float* out, void* ws, size_t ws_bytes,
                          hipStream_t s);
 
+// The page stream in chunk mode (several query tokens per entry, causal):
+// entries with at most max_cols query columns (tokens x GQ); the workspace
+// layout matches decode's (arrival counters first).
+bool stream_chunk_supported(const PoolView& pv, int B, int gq);
+size_t stream_chunk_workspace_bytes(const PoolView& pv, int B, int max_seq_len);
+hipError_t launch_stream_chunk(const PoolView& pv, int B, int Hq, const int32_t* table_rows, const int32_t* q_pos0,
+                               const int32_t* cu_q, int max_seq_len, const void* q, float sm_scale, float* out,
+                               void* ws, int max_cols, hipStream_t s);
+
 bool verify_supported(const PoolView& pv, int Hq);
 size_t verify_workspace_bytes(const PoolView& pv, int B, int Hq, int max_seq_len, int max_q_len);
 hipError_t launch_verify(const PoolView& pv, int B, int Hq, const int32_t* table_rows, const int32_t* q_pos0,

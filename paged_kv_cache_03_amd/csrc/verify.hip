@@ -8,8 +8,11 @@
 // AttentionPairs = n0*T + T(T+1)/2 ("Resource Scheduling and Context Cache"
 // page, prefill-work equation).
 //
-// Reference path: one wave per (chunk token, KV head) streams the causal
-// range page by page with an online softmax and writes the output directly.
+// Two paths: chunks of at most 32 query columns (tokens x GQ; BF16, D in
+// {64, 128}) go through the matrix-core page stream in chunk mode (decode.hip),
+// which reads each page once for all of the entry's query tokens; other
+// entries take the per-token kernel below: one wave per (chunk token, KV head)
+// streams the causal range page by page with an online softmax.
 
 #include <hip/hip_runtime.h>
 
@@ -34,6 +37,7 @@ struct VerifyArgs {
     int32_t Hq;
     int32_t total_q;
     int32_t max_ctx;
+    int32_t min_cols;   // entries with at most this many query columns (tokens x GQ) are left to the page stream
 };
 
 template <int D, int GQ>
@@ -48,6 +52,7 @@ __global__ void __launch_bounds__(256) verify_scalar_kernel(VerifyArgs a) {
     const int r = item / H, h = item % H;
     int b = 0;
     while (b + 1 < a.B && r >= a.cu_q[b + 1]) ++b;
+    if ((a.cu_q[b + 1] - a.cu_q[b]) * GQ <= a.min_cols) return;
     const int row = a.table_rows[b];
     float* o = a.out + (size_t(r) * a.Hq + size_t(h) * GQ) * D;
     const int pos = a.q_pos0[b] + (r - a.cu_q[b]);
@@ -143,11 +148,26 @@ bool verify_supported(const PoolView& pv, int Hq) {
            (gq == 1 || gq == 2 || gq == 4 || gq == 8);
 }
 
-size_t verify_workspace_bytes(const PoolView&, int, int, int, int) { return 0; }
+// Entries with at most kStreamCols query columns (tokens x GQ, e.g. a short
+// verify chunk) go through the page stream, which reads each page once for all
+// of the entry's query tokens; longer chunks take the per-token kernel.
+constexpr int kStreamCols = 32;
+
+size_t verify_workspace_bytes(const PoolView& pv, int B, int Hq, int max_seq_len, int) {
+    const int gq = pv.H ? Hq / pv.H : 0;
+    return stream_chunk_supported(pv, B, gq) ? stream_chunk_workspace_bytes(pv, B, max_seq_len) : 0;
+}
 
 hipError_t launch_verify(const PoolView& pv, int B, int Hq, const int32_t* table_rows, const int32_t* q_pos0,
                          const int32_t* cu_q, int total_q, int /*max_q_len*/, int max_seq_len, const void* q,
-                         float sm_scale, float* out, void* /*ws*/, size_t /*ws_bytes*/, hipStream_t s) {
+                         float sm_scale, float* out, void* ws, size_t /*ws_bytes*/, hipStream_t s) {
+    const int gq0 = Hq / pv.H;
+    const bool stream = stream_chunk_supported(pv, B, gq0);
+    if (stream) {
+        hipError_t e = launch_stream_chunk(pv, B, Hq, table_rows, q_pos0, cu_q, max_seq_len, q, sm_scale, out, ws,
+                                           kStreamCols, s);
+        if (e != hipSuccess) return e;
+    }
     VerifyArgs a{};
     a.pv = pv;
     a.table_rows = table_rows;
@@ -160,7 +180,8 @@ hipError_t launch_verify(const PoolView& pv, int B, int Hq, const int32_t* table
     a.Hq = Hq;
     a.total_q = total_q;
     a.max_ctx = max_seq_len;
-    const int gq = Hq / pv.H;
+    a.min_cols = stream ? kStreamCols : 0;
+    const int gq = gq0;
     switch (pv.D) {
         case 64: return launch_d<64>(a, gq, s);
         case 128: return launch_d<128>(a, gq, s);
