@@ -162,6 +162,93 @@ def cpu_baseline(wl, seconds_hint: float = 20.0) -> dict:
                       f"heads, {reps} rep(s), {per_layer:.2f} s per layer (KV bytes read / time)"}
 
 
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+
+
+def verify_kernel_names(wl) -> str:
+    gq = wl.Hq // wl.H
+    if wl.profile == "BF16" and wl.D in (64, 128) and gq in (1, 2, 4, 8):
+        return f"verify_tile_kernel<{wl.D}, {gq}> + paged_stream_kernel<{wl.D}, {gq}, 2, true>"
+    return f"verify_scalar_kernel<{wl.D}, {gq}>"
+
+
+def bench_verify(wl, args) -> int:
+    """Verify / chunked-prefill step (the mixed batch of the workload): per layer,
+    kv_append of every chunk's rows, then paged_attn_verify.  The verify launch
+    is bound by the matrix cores (prefill chunks) and HBM (short chunks); the
+    roofline is reported on the algorithmic FLOPs 4*D*Hq*sum(n0*T + T(T+1)/2)."""
+    import numpy as np
+    import torch
+    from paged_kv_cache_03_amd.device_pool import i32
+    from workloads.device_driver import _dev, build_device
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    t0 = time.time()
+    log(f"workload {wl.name}: filling {wl.layers} layer(s) of history")
+    dp, _, step_inputs = build_device(wl, zero=False)
+    log(f"history resident after {time.time() - t0:.1f} s")
+    rows_t, pos0_t, cu_t = i32(wl.table_rows, dev), i32(wl.hist, dev), i32(wl.cu_q, dev)
+    total = int(wl.cu_q[-1])
+    msl, mql = max(wl.seq_lens), max(wl.step)
+    qs = [_dev(wl.q(layer), dev) for layer in range(wl.layers)]
+    out = torch.empty((total, wl.Hq, wl.D), dtype=torch.float32, device=dev)
+    ws = dp.workspace(wl.B, wl.Hq, msl, mql)
+
+    def step(events=None):
+        for layer in range(wl.layers):
+            kd, vd = step_inputs[layer]
+            dp.append(layer, rows_t, pos0_t, cu_t, total, kd, vd)
+            if events is not None:
+                events[layer][0].record()
+            dp.verify(layer, wl.Hq, rows_t, pos0_t, cu_t, total, mql, msl, qs[layer], wl.sm_scale, out, ws)
+            if events is not None:
+                events[layer][1].record()
+
+    steps = max(1, min(args.steps, 10))
+    for _ in range(min(args.warmup, 2)):
+        step()
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(steps):
+        step()
+    end.record()
+    torch.cuda.synchronize()
+    ms_per_step = start.elapsed_time(end) / steps
+    evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+            for _ in range(wl.layers)] for _ in range(steps)]
+    for s_ in range(steps):
+        step(evs[s_])
+    torch.cuda.synchronize()
+    ver_ms = float(np.mean([a.elapsed_time(b) for row in evs for (a, b) in row]))
+
+    pairs = sum(n0 * T + T * (T + 1) // 2 for n0, T in zip(wl.hist, wl.step))
+    flops = 4.0 * wl.D * wl.Hq * pairs                      # per layer
+    table = dp.table.cpu().numpy()
+    bpth = bytes_per_token_head(wl.profile, wl.D)
+    kv_bytes = sum(len({int(table[wl.table_rows[b], p]) for p in range((c + 63) // 64)}) * 64 * wl.H * bpth
+                   for b, c in enumerate(wl.seq_lens))
+    tflops = flops / (ver_ms * 1e-3) / 1e12
+    line = {
+        "metric": "paged verify/prefill TFLOP/s (mixed batch: verify T=5 + prefill T=512, C=4, 128K ctx)",
+        "value": round(flops * wl.layers / (ms_per_step * 1e-3) / 1e12, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": steps, "warmup": min(args.warmup, 2), "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": wl.name, "profile": wl.profile, "batch": wl.B, "layers": wl.layers,
+                   "q_heads": wl.Hq, "kv_heads": wl.H, "head_dim": wl.D, "chunk_tokens": list(wl.step),
+                   "frontiers": list(wl.hist), "page_size": 64, "pool_pages": wl.M},
+        "roofline": {"kernel": verify_kernel_names(wl), "bound": "mfma", "achieved": round(tflops, 2),
+                     "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+                     "traffic": None, "flops_per_launch": flops, "kv_bytes_per_launch": kv_bytes,
+                     "launch_ms": round(ver_ms, 5)},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(line), flush=True)
+    dp.close()
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -189,8 +276,7 @@ def main() -> int:
 
     wl = workloads.get(args.config)
     if wl.mode != "decode":
-        print("bench.py times the decode step; verify/prefill workloads are timed by their tests", file=sys.stderr)
-        return 2
+        return bench_verify(wl, args)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     t0 = time.time()

@@ -235,8 +235,9 @@ size_t paged_attn_workspace_bytes(const kv_pool* pool, uint32_t B, uint32_t Hq, 
  *   d_q   : bf16 [B][Hq][D];  d_out: fp32 [B][Hq][D].
  *   max_seq_len : host upper bound of d_seq_lens (sizes the split grid).
  *   d_ws / ws_bytes : >= paged_attn_workspace_bytes(pool, B, Hq, max_seq_len, 0).
- * KV_E_GEOMETRY on B > C or Hq % H != 0; KV_E_UNSUPPORTED for shapes with no
- * kernel instance (see paged_attn_supported). */
+ * KV_E_GEOMETRY on B > C or Hq % H != 0; KV_E_INVALID unless sm_scale is
+ * finite and > 0; KV_E_UNSUPPORTED for shapes with no kernel instance (see
+ * paged_attn_supported). */
 kv_status paged_attn_decode(const kv_pool* pool, uint32_t layer, uint32_t B, uint32_t Hq,
                             const int32_t* d_table_rows, const int32_t* d_seq_lens, uint32_t max_seq_len,
                             const void* d_q, float sm_scale, float* d_out, void* d_ws, size_t ws_bytes,
@@ -250,7 +251,10 @@ kv_status paged_attn_decode(const kv_pool* pool, uint32_t layer, uint32_t B, uin
  *   d_cu_q[B+1] : rows of entry b are [cu[b], cu[b+1]) of d_q / d_out.
  *   d_q   : bf16 [total_q][Hq][D];  d_out: fp32 [total_q][Hq][D].
  *   max_q_len, max_seq_len : host upper bounds (max T, max n0 + T).
- * Profiles: BF16 only in this build (KV_E_UNSUPPORTED otherwise). */
+ *   d_ws / ws_bytes : >= paged_attn_workspace_bytes(pool, B, Hq, max_seq_len,
+ *   max_q_len), zero-filled once after allocation (as for decode).
+ * KV_E_INVALID unless sm_scale is finite and > 0.  Profiles: BF16 only in
+ * this build (KV_E_UNSUPPORTED otherwise). */
 kv_status paged_attn_verify(const kv_pool* pool, uint32_t layer, uint32_t B, uint32_t Hq,
                             const int32_t* d_table_rows, const int32_t* d_q_pos0, const int32_t* d_cu_q,
                             uint32_t total_q, uint32_t max_q_len, uint32_t max_seq_len, const void* d_q,

@@ -29,10 +29,11 @@ SOURCES = ["pool.cpp", "table_kernels.hip", "append.hip", "decode.hip", "verify.
 COMMON = ["-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950", "-I", INCLUDE, "-I", CSRC,
           "-fhip-fp32-correctly-rounded-divide-sqrt", "-fno-gpu-flush-denormals-to-zero",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-Wno-unused-command-line-argument"]
-# decode: matrix-core accumulators in ordinary VGPRs (the softmax rescales
+# decode, verify: matrix-core accumulators in ordinary VGPRs (the softmax rescales
 # them with vector ALU ops; the accumulation-register form costs two copies
 # per touched register on every page)
-PER_FILE = {"append.hip": ["-ffp-contract=off"], "decode.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+PER_FILE = {"append.hip": ["-ffp-contract=off"], "decode.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+            "verify.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def hipcc() -> str:

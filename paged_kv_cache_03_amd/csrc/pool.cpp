@@ -14,6 +14,7 @@
 // stream.
 
 #include <algorithm>
+#include <cmath>
 #include <cstring>
 #include <deque>
 #include <new>
@@ -506,6 +507,7 @@ kv_status paged_attn_decode(const kv_pool* pool, uint32_t layer, uint32_t B, uin
     kv_status st = check_compute(pool, layer, B);
     if (st != KV_OK) return st;
     if (Hq == 0 || Hq % pool->geo.num_kv_heads) return fail(KV_E_GEOMETRY, "Hq must be a multiple of H");
+    if (!(sm_scale > 0.f) || !std::isfinite(sm_scale)) return fail(KV_E_INVALID, "sm_scale must be finite and > 0");
     if (B == 0) return ok();
     if (!d_table_rows || !d_seq_lens || !d_q || !d_out) return fail(KV_E_INVALID, "null device pointer");
     if (max_seq_len > pool->geo.max_context) return fail(KV_E_INVALID, "max_seq_len beyond max_context");
@@ -526,6 +528,7 @@ kv_status paged_attn_verify(const kv_pool* pool, uint32_t layer, uint32_t B, uin
     kv_status st = check_compute(pool, layer, B);
     if (st != KV_OK) return st;
     if (Hq == 0 || Hq % pool->geo.num_kv_heads) return fail(KV_E_GEOMETRY, "Hq must be a multiple of H");
+    if (!(sm_scale > 0.f) || !std::isfinite(sm_scale)) return fail(KV_E_INVALID, "sm_scale must be finite and > 0");
     if (B == 0 || total_q == 0) return ok();
     if (!d_table_rows || !d_q_pos0 || !d_cu_q || !d_q || !d_out) return fail(KV_E_INVALID, "null device pointer");
     if (max_seq_len > pool->geo.max_context) return fail(KV_E_INVALID, "max_seq_len beyond max_context");

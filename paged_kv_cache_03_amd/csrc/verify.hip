@@ -8,19 +8,22 @@
 // AttentionPairs = n0*T + T(T+1)/2 ("Resource Scheduling and Context Cache"
 // page, prefill-work equation).
 //
-// Two paths: chunks of at most 32 query columns (tokens x GQ; BF16, D in
-// {64, 128}) go through the matrix-core page stream in chunk mode (decode.hip),
-// which reads each page once for all of the entry's query tokens; other
-// entries take the per-token kernel below: one wave per (chunk token, KV head)
-// streams the causal range page by page with an online softmax.
+// BF16 pages with D in {64, 128}: chunks of at most 32 query columns (tokens
+// x GQ, e.g. a short verify) go through the matrix-core page stream in chunk
+// mode (decode.hip), which reads each page once for all of the entry's query
+// tokens; longer chunks (prefill) go to 128-column tiles on the matrix cores
+// (verify_tile_kernel).  Other shapes take the per-token kernel: one wave per
+// (chunk token, KV head) streams the causal range with an online softmax.
 
 #include <hip/hip_runtime.h>
 
 #include <cmath>
+#include <type_traits>
 
 #include "attn_common.h"
 #include "internal.h"
 #include "kv_read.h"
+#include "stream_common.h"
 
 namespace kvs {
 namespace {
@@ -126,6 +129,329 @@ __global__ void __launch_bounds__(256) verify_scalar_kernel(VerifyArgs a) {
     }
 }
 
+// ---------------------------------------------------------------------------
+// Long chunks (chunked prefill): a block of 512 threads owns a tile of 128
+// query columns -- consecutive chunk tokens x the GQ query heads of one KV
+// head -- and streams the tile's causal key range through an LDS ring of
+// direct-to-LDS page loads (issued by waves 0-3), NS-1 pages ahead.
+// Wave w owns columns [32(w%4), 32(w%4) + 32) (two 16-column tiles) and keys
+// [32(w/4), 32(w/4) + 32) of every page, so each wave reads half of a page
+// from LDS and two waves per SIMD overlap one's softmax with the other's
+// products:
+//  * S^T[32 keys x 32] = K . Q^T on v_mfma_f32_16x16x32_bf16;
+//  * PV on the same double-rate product with k = 32 keys: the A operand is
+//    V^T of two 16-key tiles (two transposing reads, concatenated) and the
+//    B operand the P^T registers of the same two tiles in the same order --
+//    the key order inside a product is free as long as A and B agree;
+//  * P as the bf16 pair p_hi + p_lo; lazy rescale; the causal mask only on
+//    the pages that reach a column's limit;
+//  * the two waves of a column range merge once, through LDS, at the end.
+// Tiles of one (entry, KV head) read the same pages: blocks are mapped so
+// that consecutive tiles run on one die (XCD) and share its L2.
+template <int D, int GQ>
+__global__ void __launch_bounds__(512) verify_tile_kernel(VerifyArgs a) {
+    constexpr int NCH = D / 8;                     // 16-byte chunks per row
+    constexpr int NT = 256;                        // threads that issue the page loads (waves 0-3)
+    constexpr int NB = 512;                        // threads of the block
+    constexpr int SLOTS = 64 * NCH;
+    constexpr int SLICE_BYTES = SLOTS * 16;
+    constexpr int PER_T = SLOTS / NT;
+    constexpr int NS = D == 128 ? 4 : 8;
+    constexpr int LOADS_PER_PAGE = 2 * PER_T;
+    constexpr int NC = D / 32;                     // QK products per key tile, k = 32 each
+    constexpr int NDT = D / 16;                    // PV tiles of 16 dims
+    constexpr int TCOL = 128;                      // query columns per tile
+    constexpr int WCT = 2;                         // 16-column tiles per wave
+    constexpr int TTOK = TCOL / GQ;                // chunk tokens per tile
+    static_assert((D == 64 || D == 128) && TCOL % GQ == 0, "shape");
+    static_assert(NS * SLICE_BYTES == 0x10000, "V stages sit 64 KiB above the K stages");
+    static_assert(LOADS_PER_PAGE * (NS - 1) < 64, "vmcnt range");
+    static_assert(4 * WCT * NDT * 4 * 64 * 4 <= 2 * NS * SLICE_BYTES, "the end merge fits the ring");
+
+    __shared__ u32x4 ring[2][NS][SLOTS];           // [K | V][stage][slot]
+    __shared__ float mlx[4][WCT][16][2];           // (m, l) of the key-half-1 waves at the end
+
+    const int tid = int(threadIdx.x);
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63, li = lane & 15, lg = lane >> 4;
+    const int cw = w & 3, kh = w >> 2;             // column range, key half
+    const int H = a.pv.H, M = a.pv.M;
+
+    // items are (entry, KV head, tile) in that order; die x takes items
+    // [x*per, (x+1)*per) so that the tiles of one (entry, head) share an L2
+    int n_items = 0;
+    for (int b = 0; b < a.B; ++b) {
+        const int T = ld_uniform(a.cu_q, b + 1) - ld_uniform(a.cu_q, b);
+        if (T * GQ > a.min_cols) n_items += H * ((T * GQ + TCOL - 1) / TCOL);
+    }
+    const int per = (n_items + 7) / 8;
+    const int i_blk = int(blockIdx.x);
+    if (i_blk / 8 >= per) return;
+    int item = (i_blk % 8) * per + i_blk / 8;
+    if (item >= n_items) return;
+    int b = 0, nt = 0;
+    for (; b < a.B; ++b) {
+        const int T = ld_uniform(a.cu_q, b + 1) - ld_uniform(a.cu_q, b);
+        nt = T * GQ > a.min_cols ? (T * GQ + TCOL - 1) / TCOL : 0;
+        if (item < H * nt) break;
+        item -= H * nt;
+    }
+    const int h = item / nt, t = item % nt;
+    const int row = ld_uniform(a.table_rows, b);
+    const int c0 = ld_uniform(a.cu_q, b), T = ld_uniform(a.cu_q, b + 1) - c0;
+    const int n0 = ld_uniform(a.q_pos0, b);
+    const int keys = (row >= 0 && row < a.pv.C) ? max(0, min(n0 + T, a.max_ctx)) : 0;
+    const int i0 = t * TTOK;                       // first chunk token of the tile
+    const int ncol = min(TCOL, (T - i0) * GQ);     // real columns of the tile
+    const int kmax = min(n0 + i0 + ncol / GQ, keys);   // largest key limit of the tile
+    const int kmin = min(n0 + i0 + 1, keys);           // smallest key limit of a real column
+    const int npages = kmax > 0 ? (kmax + kPage - 1) >> kPageShift : 0;
+
+    auto out_ptr = [&](int c) __attribute__((always_inline)) {
+        return a.out + (size_t(c0 + i0 + c / GQ) * a.Hq + size_t(h) * GQ + c % GQ) * D;
+    };
+    if (npages == 0) {                             // nothing to attend: zeros
+        for (int x = tid; x < ncol * D; x += NB) out_ptr(x / D)[x % D] = 0.f;
+        return;
+    }
+
+    // this lane's columns: c = 32cw + 16ct + li; key limits and Q^T operands
+    int klim[WCT];
+    bf16x8_t qb[WCT][NC];
+#pragma unroll
+    for (int ct = 0; ct < WCT; ++ct) {
+        const int c = 32 * cw + 16 * ct + li;
+        const bool real = c < ncol;
+        klim[ct] = real ? min(n0 + i0 + c / GQ + 1, keys) : 0;
+        const u32x4* qg = reinterpret_cast<const u32x4*>(
+            a.q + (size_t(c0 + i0 + (real ? c : 0) / GQ) * a.Hq + size_t(h) * GQ + (real ? c : 0) % GQ) * D);
+#pragma unroll
+        for (int k = 0; k < NC; ++k) {
+            const u32x4 v = qg[4 * k + lg];
+            qb[ct][k] = __builtin_bit_cast(bf16x8_t, real ? v : u32x4{0u, 0u, 0u, 0u});
+        }
+    }
+    wait_vmcnt<0>();
+
+    // stage layout and DMA sources as in the page stream (XOR-swizzled rows)
+    auto kswz = [](int r) __attribute__((always_inline)) { return NCH == 16 ? (r & 15) : ((r >> 1) & 7); };
+    auto vswz = [](int r) __attribute__((always_inline)) { return NCH == 16 ? ((r & 7) << 1) : (((r >> 1) & 3) << 1); };
+    const char* kplane = static_cast<const char*>(a.pv.lv.k_code);
+    const char* vplane = static_cast<const char*>(a.pv.lv.v_code);
+    uint32_t k_src[PER_T], v_src[PER_T];
+#pragma unroll
+    for (int k = 0; k < PER_T; ++k) {
+        const int sl = k * NT + (tid & (NT - 1));
+        const int r = sl / NCH, x = sl % NCH;
+        k_src[k] = uint32_t(r * NCH + (x ^ kswz(r))) * 16u;
+        v_src[k] = uint32_t(r * NCH + (x ^ vswz(r))) * 16u;
+    }
+    const uint32_t ring_lds = uint32_t(reinterpret_cast<uintptr_t>((lds_byte_ptr)(&ring[0][0][0])));
+    const int32_t* trow = a.pv.table + size_t(row) * a.pv.L;
+    auto slice_of = [&](int p) __attribute__((always_inline)) {
+        const int g0 = ld_uniform(trow, p);
+        return (g0 >= 0 && g0 < M) ? g0 * H + h : -1;
+    };
+    auto fetch = [&](int sl, int fs) __attribute__((always_inline)) {
+        if (w >= 4) return;                        // waves 0-3 load the pages
+        const uint32_t dst = ring_lds + uint32_t(fs * SLICE_BYTES + w * 1024);
+        const size_t off = size_t(sl < 0 ? 0 : sl) * SLICE_BYTES;
+        if constexpr (PER_T == 4) fetch_page4(dst, kplane + off, vplane + off, k_src, v_src);
+        else fetch_page2(dst, kplane + off, vplane + off, k_src, v_src);
+    };
+
+    // per-lane LDS offsets of this wave's first key tile in stage 0 (its
+    // second tile adds 16 rows, the stage an immediate): K A operand row li,
+    // chunk 4c + lg; V^T through the transposing read, rows 4lg + li/4,
+    // dims 16dt + 4(li%4)
+    const int kr0 = 32 * kh;                       // first key row of this wave
+    int koff[NC], voff[NDT];
+    {
+#pragma unroll
+        for (int c = 0; c < NC; ++c) koff[c] = (kr0 + li) * NCH + ((4 * c + lg) ^ kswz(li));
+        const int tv = 4 * lg + (li >> 2), qd = li & 3;
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt)
+            voff[dt] = 0x10000 + (kr0 + tv) * NCH * 16 + (((2 * dt + (qd >> 1)) ^ vswz(tv)) * 16) + 8 * (qd & 1);
+    }
+
+    f32x4_t acc[WCT][NDT];
+    float m_ref[WCT], l_part[WCT];
+#pragma unroll
+    for (int ct = 0; ct < WCT; ++ct) {
+        m_ref[ct] = -INFINITY;
+        l_part[ct] = 0.f;
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) acc[ct][dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    }
+
+    int slices[NS];                                // slice of the page in each stage
+#pragma unroll
+    for (int k = 0; k < NS; ++k) slices[k] = 0;
+#pragma unroll
+    for (int k = 0; k < NS - 1; ++k) {
+        if (k < npages) {
+            slices[k] = slice_of(k);
+            fetch(slices[k], k);
+        }
+    }
+    int next_slice = NS - 1 < npages ? slice_of(NS - 1) : 0;   // one page of lookahead on the table
+
+    auto step = [&](auto jc, int i) __attribute__((always_inline)) {
+        constexpr int J = decltype(jc)::value;
+        constexpr int FS = (J + NS - 1) % NS;
+        if (i + NS - 1 < npages) {
+            wait_vmcnt<LOADS_PER_PAGE * (NS - 2)>();
+            block_lds_barrier();
+            slices[FS] = next_slice;
+            fetch(next_slice, FS);
+            if (i + NS < npages) next_slice = slice_of(i + NS);
+        } else {
+            wait_vmcnt<0>();
+            block_lds_barrier();
+        }
+        const int tok0 = i * kPage;
+        const int lim = slices[J] >= 0 ? min(kPage, kmax - tok0) : 0;   // rows any column may see
+        if (lim <= 0) return;                      // unmapped page: nothing to read
+        if (lim < kPage) {
+            // rows past the last limit hold stale bytes (possibly NaN): clear
+            // them before any wave reads the stage
+            u32x4* vrows = &ring[1][J][lim * NCH];
+            for (int x = tid; x < (kPage - lim) * NCH; x += NB) vrows[x] = u32x4{0u, 0u, 0u, 0u};
+            block_lds_barrier();
+        }
+        if (lim <= kr0) return;                    // none of this wave's keys is visible
+        const bool masked = tok0 + kPage > kmin;
+        const u32x4* kst = &ring[0][J][0];
+        f32x4_t s[2][WCT];
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+            for (int ct = 0; ct < WCT; ++ct) s[kt][ct] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt) {
+#pragma unroll
+            for (int c = 0; c < NC; ++c) {
+                const bf16x8_t kk = __builtin_bit_cast(bf16x8_t, kst[koff[c] + kt * 16 * NCH]);
+#pragma unroll
+                for (int ct = 0; ct < WCT; ++ct)
+                    s[kt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kk, qb[ct][c], s[kt][ct], 0, 0, 0);
+            }
+        }
+        bf16x8_t phi[WCT], plo[WCT];
+#pragma unroll
+        for (int ct = 0; ct < WCT; ++ct) {
+            // raw scores; the scale (> 0) is applied in the exponent's fma
+            float sj[2][4];
+            float mx = -INFINITY;
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    float v = s[kt][ct][r];
+                    if (masked && tok0 + kr0 + 16 * kt + 4 * lg + r >= klim[ct]) v = -INFINITY;
+                    sj[kt][r] = v;
+                    mx = fmaxf(mx, v);
+                }
+            const float pm = rows_max(mx) * a.scale_log2;
+            if (__builtin_amdgcn_ballot_w64(pm > m_ref[ct] + kRescaleLog2)) {
+                const float mn = pm > m_ref[ct] + kRescaleLog2 ? pm : m_ref[ct];
+                const float alpha = m_ref[ct] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_ref[ct] - mn);
+                l_part[ct] *= alpha;
+#pragma unroll
+                for (int dt = 0; dt < NDT; ++dt) acc[ct][dt] *= alpha;
+                m_ref[ct] = mn;
+            }
+            // k order of the PV product: element e of lane group g is key
+            // 16*(e/4) + 4g + e%4 of this wave's 32 (the same for V^T below)
+            // a column whose keys in this half are all masked so far has no
+            // reference yet: offset 0 keeps its p at exp2(-inf) = 0, not NaN
+            const float moff = m_ref[ct] == -INFINITY ? 0.f : -m_ref[ct];
+            float p[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                p[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sj[e >> 2][e & 3], a.scale_log2, moff));
+            l_part[ct] += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
+            uint32_t hv[4], lv[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) split_bf16(p[2 * e], p[2 * e + 1], hv[e], lv[e]);
+            phi[ct] = __builtin_bit_cast(bf16x8_t, u32x4{hv[0], hv[1], hv[2], hv[3]});
+            plo[ct] = __builtin_bit_cast(bf16x8_t, u32x4{lv[0], lv[1], lv[2], lv[3]});
+        }
+        const lds_byte_ptr vst = (lds_byte_ptr)(&ring[0][J][0]);   // voff includes the K-to-V distance
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) {
+            const s16x4_t v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_ptr)(vst + voff[dt]));
+            const s16x4_t v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (lds_s16x4_ptr)(vst + voff[dt] + 16 * NCH * 16));
+            const bf16x8_t va = __builtin_bit_cast(
+                bf16x8_t, u32x4{__builtin_bit_cast(u32x2, v0)[0], __builtin_bit_cast(u32x2, v0)[1],
+                                __builtin_bit_cast(u32x2, v1)[0], __builtin_bit_cast(u32x2, v1)[1]});
+#pragma unroll
+            for (int ct = 0; ct < WCT; ++ct) {
+                acc[ct][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, phi[ct], acc[ct][dt], 0, 0, 0);
+                acc[ct][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, plo[ct], acc[ct][dt], 0, 0, 0);
+            }
+        }
+    };
+
+    for (int i0p = 0; i0p < npages; i0p += NS) {
+        step(std::integral_constant<int, 0>{}, i0p);
+        if (i0p + 1 < npages) step(std::integral_constant<int, 1>{}, i0p + 1);
+        if (i0p + 2 < npages) step(std::integral_constant<int, 2>{}, i0p + 2);
+        if (i0p + 3 < npages) step(std::integral_constant<int, 3>{}, i0p + 3);
+        if constexpr (NS == 8) {
+            if (i0p + 4 < npages) step(std::integral_constant<int, 4>{}, i0p + 4);
+            if (i0p + 5 < npages) step(std::integral_constant<int, 5>{}, i0p + 5);
+            if (i0p + 6 < npages) step(std::integral_constant<int, 6>{}, i0p + 6);
+            if (i0p + 7 < npages) step(std::integral_constant<int, 7>{}, i0p + 7);
+        }
+    }
+
+    // merge the two key halves of each column range (through the ring, free
+    // now), then wave cw writes its columns
+    float lw[WCT];
+#pragma unroll
+    for (int ct = 0; ct < WCT; ++ct) lw[ct] = rows_sum(l_part[ct]);
+    block_lds_barrier();                           // every wave is done with the ring
+    float* xb = reinterpret_cast<float*>(&ring[0][0][0]) + cw * (WCT * NDT * 4 * 64);
+    if (kh == 1) {
+#pragma unroll
+        for (int ct = 0; ct < WCT; ++ct) {
+#pragma unroll
+            for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) xb[((ct * NDT + dt) * 4 + r) * 64 + lane] = acc[ct][dt][r];
+            if (lg == 0) {
+                mlx[cw][ct][li][0] = m_ref[ct];
+                mlx[cw][ct][li][1] = lw[ct];
+            }
+        }
+    }
+    block_lds_barrier();
+    if (kh == 1) return;
+#pragma unroll
+    for (int ct = 0; ct < WCT; ++ct) {
+        const float m1 = mlx[cw][ct][li][0], l1 = mlx[cw][ct][li][1];
+        const float mx = fmaxf(m_ref[ct], m1);
+        const float w0 = m_ref[ct] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_ref[ct] - mx);
+        const float w1 = m1 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m1 - mx);
+        const float l = lw[ct] * w0 + l1 * w1;
+        const int c = 32 * cw + 16 * ct + li;
+        if (c >= ncol) continue;
+        const float inv = l > 0.f ? 1.f / l : 0.f;
+        float* o = out_ptr(c) + 4 * lg;
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) {
+            f32x4_t v;
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                v[r] = (acc[ct][dt][r] * w0 + xb[((ct * NDT + dt) * 4 + r) * 64 + lane] * w1) * inv;
+            *reinterpret_cast<float4*>(o + 16 * dt) = make_float4(v[0], v[1], v[2], v[3]);
+        }
+    }
+}
+
 template <int D>
 hipError_t launch_d(const VerifyArgs& a, int gq, hipStream_t s) {
     const dim3 grid(unsigned((a.total_q * a.pv.H + 3) / 4));
@@ -159,15 +485,9 @@ size_t verify_workspace_bytes(const PoolView& pv, int B, int Hq, int max_seq_len
 }
 
 hipError_t launch_verify(const PoolView& pv, int B, int Hq, const int32_t* table_rows, const int32_t* q_pos0,
-                         const int32_t* cu_q, int total_q, int /*max_q_len*/, int max_seq_len, const void* q,
+                         const int32_t* cu_q, int total_q, int max_q_len, int max_seq_len, const void* q,
                          float sm_scale, float* out, void* ws, size_t /*ws_bytes*/, hipStream_t s) {
-    const int gq0 = Hq / pv.H;
-    const bool stream = stream_chunk_supported(pv, B, gq0);
-    if (stream) {
-        hipError_t e = launch_stream_chunk(pv, B, Hq, table_rows, q_pos0, cu_q, max_seq_len, q, sm_scale, out, ws,
-                                           kStreamCols, s);
-        if (e != hipSuccess) return e;
-    }
+    const int gq = Hq / pv.H;
     VerifyArgs a{};
     a.pv = pv;
     a.table_rows = table_rows;
@@ -180,8 +500,29 @@ hipError_t launch_verify(const PoolView& pv, int B, int Hq, const int32_t* table
     a.Hq = Hq;
     a.total_q = total_q;
     a.max_ctx = max_seq_len;
-    a.min_cols = stream ? kStreamCols : 0;
-    const int gq = gq0;
+    if (stream_chunk_supported(pv, B, gq)) {
+        // short chunks: the page stream; long chunks: 128-column tiles
+        hipError_t e = launch_stream_chunk(pv, B, Hq, table_rows, q_pos0, cu_q, max_seq_len, q, sm_scale, out, ws,
+                                           kStreamCols, s);
+        if (e != hipSuccess) return e;
+        a.min_cols = kStreamCols;
+        if (max_q_len * gq <= kStreamCols) return hipSuccess;
+        const long long tiles = (long long)B * pv.H * ((max_q_len * gq + 127) / 128);
+        const dim3 grid(unsigned((tiles + 7) / 8 * 8));   // 512 threads each
+        switch (pv.D * 16 + gq) {
+            case 64 * 16 + 1: verify_tile_kernel<64, 1><<<grid, 512, 0, s>>>(a); break;
+            case 64 * 16 + 2: verify_tile_kernel<64, 2><<<grid, 512, 0, s>>>(a); break;
+            case 64 * 16 + 4: verify_tile_kernel<64, 4><<<grid, 512, 0, s>>>(a); break;
+            case 64 * 16 + 8: verify_tile_kernel<64, 8><<<grid, 512, 0, s>>>(a); break;
+            case 128 * 16 + 1: verify_tile_kernel<128, 1><<<grid, 512, 0, s>>>(a); break;
+            case 128 * 16 + 2: verify_tile_kernel<128, 2><<<grid, 512, 0, s>>>(a); break;
+            case 128 * 16 + 4: verify_tile_kernel<128, 4><<<grid, 512, 0, s>>>(a); break;
+            case 128 * 16 + 8: verify_tile_kernel<128, 8><<<grid, 512, 0, s>>>(a); break;
+            default: return hipErrorNotSupported;
+        }
+        return hipGetLastError();
+    }
+    a.min_cols = 0;
     switch (pv.D) {
         case 64: return launch_d<64>(a, gq, s);
         case 128: return launch_d<128>(a, gq, s);
