@@ -32,7 +32,17 @@ if ROOT not in sys.path:
 HBM_PEAK_GBS = 8000.0
 METRIC = "paged decode KV GB/s (% of HBM peak) + decode steps/s at C=8, 32K ctx"
 PROFILES = os.path.join(ROOT, "profiles")
-DECODE_SRC = os.path.join(ROOT, "paged_kv_cache_03_amd", "csrc", "decode.hip")
+# sources of the decode kernel; the traffic summary is valid for this exact text
+DECODE_SRC = [os.path.join(ROOT, "paged_kv_cache_03_amd", "csrc", f) for f in ("decode.hip", "stream_common.h")]
+
+
+def decode_source_sha256() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for path in DECODE_SRC:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
 def log(msg: str) -> None:
@@ -75,7 +85,6 @@ def measured_traffic(wl) -> int | None:
     (FETCH_SIZE + WRITE_SIZE, each scaled by what the same counter reads for a
     plain device copy of known size), or None when there is none for this
     workload or the decode source has changed since it was taken."""
-    import hashlib
     path = os.path.join(PROFILES, f"decode_traffic_{wl.name}.txt")
     if not os.path.exists(path):
         return None
@@ -84,9 +93,7 @@ def measured_traffic(wl) -> int | None:
         if ":" in line and not line.startswith("#"):
             k, v = line.split(":", 1)
             kv[k.strip()] = v.strip()
-    with open(DECODE_SRC, "rb") as f:
-        sha = hashlib.sha256(f.read()).hexdigest()
-    if kv.get("source_sha256") != sha or kv.get("kernel") != decode_kernel_name(wl):
+    if kv.get("source_sha256") != decode_source_sha256() or kv.get("kernel") != decode_kernel_name(wl):
         return None
     try:
         return int(float(kv["traffic_bytes_per_dispatch"]))
@@ -254,7 +261,7 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", type=int, default=2, help="workload number (decode workloads: 1-4)")
+    ap.add_argument("--config", type=int, default=2, help="workload number (1-4: decode, 5: verify/prefill)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a 1 GiB device copy (counter calibration under rocprofv3 --pmc)")
