@@ -2,9 +2,11 @@
 """Benchmark of the paged KV hot path on one MI355X.
 
 A step is one decode step of the whole batch through every layer:
-    for each layer: kv_append (one new token per sequence, quantized into its
-    page through the block table) + paged_attn_decode (split-K over pages and
-    the cross-split combine).
+    paged_attn_decode_plan (the batch state's work list: which pages each
+    block reads for which query columns, shared prefix pages once), then for
+    each layer: kv_append (one new token per sequence, quantized into its
+    page through the block table) + paged_attn_decode_run (split-K over pages
+    and the cross-split combine).
 Inputs are resident in HBM before timing; the step is idempotent (the same
 positions are re-appended, the same contexts decoded).
 
@@ -299,13 +301,17 @@ def main() -> int:
     out = torch.empty((wl.B, wl.Hq, wl.D), dtype=torch.float32, device=dev)
     ws = dp.workspace(wl.B, wl.Hq, max_ctx)
 
+    # one step: the work list of the batch state once (it depends only on the
+    # block table and the lengths), then per layer the append of the step's
+    # rows and the decode run
     def step(events=None):
+        dp.decode_plan(wl.Hq, rows_t, lens_t, max_ctx, ws)
         for layer in range(wl.layers):
             kd, vd = step_inputs[layer]
             dp.append(layer, rows_t, pos0_t, cu_t, total, kd, vd)
             if events is not None:
                 events[layer][0].record()
-            dp.decode(layer, wl.Hq, rows_t, lens_t, max_ctx, qs[layer], wl.sm_scale, out, ws)
+            dp.decode_run(layer, wl.B, wl.Hq, max_ctx, qs[layer], wl.sm_scale, out, ws)
             if events is not None:
                 events[layer][1].record()
 

@@ -215,11 +215,10 @@ kv_status kv_append(const kv_pool* pool, uint32_t layer, uint32_t B, const int32
                     const void* d_k, const void* d_v, hipStream_t stream);
 
 /* Workspace bytes paged_attn_decode / paged_attn_verify need for these bounds
- * (split-K partials plus per-segment arrival counters).  max_q_len 0 means
- * decode.  The caller owns the workspace; it must be zero-filled once after
- * allocation, and every call returns it with its counter area zero again, so
- * it can be reused by later calls on the same stream.  Calls that overlap in
- * time (other streams) need workspaces of their own. */
+ * (the batch state's plan and the split-K partials).  max_q_len 0 means
+ * decode.  The caller owns the workspace; it needs no initialization (every
+ * call writes what it reads).  Calls that overlap in time (other streams)
+ * need workspaces of their own. */
 size_t paged_attn_workspace_bytes(const kv_pool* pool, uint32_t B, uint32_t Hq, uint32_t max_seq_len,
                                   uint32_t max_q_len);
 
@@ -231,7 +230,9 @@ size_t paged_attn_workspace_bytes(const kv_pool* pool, uint32_t B, uint32_t Hq, 
  *     KV head of query head j = j / (Hq / H).
  * Pages are read through the block table, a page at a time; split-K over
  * pages with a deterministic cross-split combine, so results do not depend
- * on physical page ids.  seq_len 0 yields zeros.
+ * on physical page ids.  Leading pages that several entries' rows share are
+ * read once for all of them (the split then differs from that of private
+ * copies of the same pages, within rounding).  seq_len 0 yields zeros.
  *   d_q   : bf16 [B][Hq][D];  d_out: fp32 [B][Hq][D].
  *   max_seq_len : host upper bound of d_seq_lens (sizes the split grid).
  *   d_ws / ws_bytes : >= paged_attn_workspace_bytes(pool, B, Hq, max_seq_len, 0).
@@ -243,6 +244,34 @@ kv_status paged_attn_decode(const kv_pool* pool, uint32_t layer, uint32_t B, uin
                             const void* d_q, float sm_scale, float* d_out, void* d_ws, size_t ws_bytes,
                             hipStream_t stream);
 
+/* Decode split in two, for callers that run the same batch state over many
+ * layers (consumer rules: the op chooses its own split; the work list depends
+ * only on the block table and the lengths, which a step keeps for all
+ * layers).
+ *
+ * paged_attn_decode_plan writes the batch state's work list into d_ws: the
+ * entry table, and for the matrix-core page stream the page list of every
+ * block.  Entries whose table rows hold the same page groups over a leading
+ * run of logical blocks (forks: fork and tail copy-on-write) have that run
+ * read once, with the query heads of all of them in the matrix-core columns.
+ * Reads d_table_rows, d_seq_lens and the block table on the stream; the plan
+ * stays valid until any of them changes for an entry of the batch.
+ *
+ * paged_attn_decode_run computes layer `layer` from the plan in d_ws, with
+ * the same result definition as paged_attn_decode.  B, Hq, max_seq_len and
+ * d_ws must be those of the plan (a plan of another B, Hq or grid is
+ * detected on the device and turns every output of the call into NaN).  The
+ * workspace is as for paged_attn_decode (>= paged_attn_workspace_bytes(pool,
+ * B, Hq, max_seq_len, 0)); runs on one workspace must not
+ * overlap in time.  paged_attn_decode is exactly a plan followed by a run.
+ * Errors as for paged_attn_decode; the plan checks no sm_scale. */
+kv_status paged_attn_decode_plan(const kv_pool* pool, uint32_t B, uint32_t Hq, const int32_t* d_table_rows,
+                                 const int32_t* d_seq_lens, uint32_t max_seq_len, void* d_ws, size_t ws_bytes,
+                                 hipStream_t stream);
+kv_status paged_attn_decode_run(const kv_pool* pool, uint32_t layer, uint32_t B, uint32_t Hq, uint32_t max_seq_len,
+                                const void* d_q, float sm_scale, float* d_out, void* d_ws, size_t ws_bytes,
+                                hipStream_t stream);
+
 /* Multi-token verify / chunked prefill on paged KV (causal): chunk token i of
  * entry b sits at position d_q_pos0[b] + i and attends [0, d_q_pos0[b] + i]
  * (the chunk's own K/V are appended first; the mask starts at any in-page
@@ -252,7 +281,7 @@ kv_status paged_attn_decode(const kv_pool* pool, uint32_t layer, uint32_t B, uin
  *   d_q   : bf16 [total_q][Hq][D];  d_out: fp32 [total_q][Hq][D].
  *   max_q_len, max_seq_len : host upper bounds (max T, max n0 + T).
  *   d_ws / ws_bytes : >= paged_attn_workspace_bytes(pool, B, Hq, max_seq_len,
- *   max_q_len), zero-filled once after allocation (as for decode).
+ *   max_q_len).
  * KV_E_INVALID unless sm_scale is finite and > 0.  Profiles: BF16 only in
  * this build (KV_E_UNSUPPORTED otherwise). */
 kv_status paged_attn_verify(const kv_pool* pool, uint32_t layer, uint32_t B, uint32_t Hq,

@@ -27,7 +27,8 @@ KV_ROLE_K_CODE, KV_ROLE_K_SCALE, KV_ROLE_V_CODE, KV_ROLE_V_SCALE = range(4)
 EXPORTS = ["kv_profile_planes", "kv_plane_bytes", "kv_pool_create", "kv_pool_destroy", "kv_pool_stats",
            "kv_pool_table_host", "kv_pool_page_refs", "kv_seq_open", "kv_seq_fork", "kv_seq_ensure_mapped",
            "kv_seq_commit", "kv_seq_release", "kv_seq_info", "kv_cow_tail_page", "kv_append",
-           "paged_attn_workspace_bytes", "paged_attn_decode", "paged_attn_verify", "paged_attn_supported",
+           "paged_attn_workspace_bytes", "paged_attn_decode", "paged_attn_decode_plan", "paged_attn_decode_run",
+           "paged_attn_verify", "paged_attn_supported",
            "kv_last_error_message"]
 
 
@@ -81,6 +82,8 @@ def _load():
         "kv_append": (i32, [vp, u32, u32, vp, vp, vp, u32, vp, vp, vp]),
         "paged_attn_workspace_bytes": (sz, [vp, u32, u32, u32, u32]),
         "paged_attn_decode": (i32, [vp, u32, u32, u32, vp, vp, u32, vp, ctypes.c_float, vp, vp, sz, vp]),
+        "paged_attn_decode_plan": (i32, [vp, u32, u32, vp, vp, u32, vp, sz, vp]),
+        "paged_attn_decode_run": (i32, [vp, u32, u32, u32, u32, vp, ctypes.c_float, vp, vp, sz, vp]),
         "paged_attn_verify": (i32, [vp, u32, u32, u32, vp, vp, vp, u32, u32, u32, vp, ctypes.c_float, vp, vp, sz,
                                     vp]),
         "paged_attn_supported": (ctypes.c_int, [vp, u32, u32]),
@@ -207,6 +210,18 @@ def paged_attn_decode(pool: int, layer: int, B: int, Hq: int, d_table_rows: int,
                       stream: int = 0) -> None:
     _check(_lib.paged_attn_decode(pool, layer, B, Hq, d_table_rows, d_seq_lens, max_seq_len, d_q, sm_scale, d_out,
                                   d_ws or None, ws_bytes, stream or None))
+
+
+def paged_attn_decode_plan(pool: int, B: int, Hq: int, d_table_rows: int, d_seq_lens: int, max_seq_len: int,
+                           d_ws: int, ws_bytes: int, stream: int = 0) -> None:
+    _check(_lib.paged_attn_decode_plan(pool, B, Hq, d_table_rows, d_seq_lens, max_seq_len, d_ws or None, ws_bytes,
+                                       stream or None))
+
+
+def paged_attn_decode_run(pool: int, layer: int, B: int, Hq: int, max_seq_len: int, d_q: int, sm_scale: float,
+                          d_out: int, d_ws: int, ws_bytes: int, stream: int = 0) -> None:
+    _check(_lib.paged_attn_decode_run(pool, layer, B, Hq, max_seq_len, d_q, sm_scale, d_out, d_ws or None, ws_bytes,
+                                      stream or None))
 
 
 def paged_attn_verify(pool: int, layer: int, B: int, Hq: int, d_table_rows: int, d_q_pos0: int, d_cu_q: int,

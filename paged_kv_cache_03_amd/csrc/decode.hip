@@ -6,17 +6,19 @@
 // translation at page granularity, no gather-to-contiguous, free choice of
 // tile/split/wave/LDS scheme), wrapper validation and caller guarantees.
 //
-// Two kernels:
+// A decode is a plan of the batch state (stream_plan.hip; one per step, it
+// serves every layer) and a run:
 //  * the matrix-core page stream (BF16 pages, D in {64, 128}): every page of
-//    the call in one flat list, cut into equal ranges, one 256-thread block
-//    per compute unit, with the cross-range combine in the same launch;
+//    the plan in one flat list, cut into equal ranges, one 256-thread block
+//    per compute unit; leading pages that entries share are read once for
+//    all of them; then a combine launch for outputs with several pieces;
 //  * the split kernel (every other profile and shape): entry b's pages are
 //    cut into chunks of `chunk_pages` consecutive logical pages, one wave per
 //    (entry, KV head, chunk), then a combine launch.
-// In both, the split depends only on logical positions and the host-side
-// bounds, never on physical page ids, and the combine runs in a fixed order,
-// so outputs are bitwise identical under any permutation of page ids and for
-// shared versus private pages.
+// In both, the split depends only on logical positions, the host-side
+// bounds and which logical pages are shared, never on physical page ids, and
+// the combine runs in a fixed order, so outputs are bitwise identical under
+// any permutation of page ids.
 
 #include <hip/hip_runtime.h>
 
@@ -28,33 +30,33 @@
 #include "internal.h"
 #include "kv_read.h"
 #include "stream_common.h"
+#include "stream_plan.h"
 
 namespace kvs {
 namespace {
 
 struct DecodeArgs {
     PoolView pv;
-    const int32_t* table_rows;
-    const int32_t* seq_lens;
+    const int32_t* plan;   // the call's plan (stream_plan.h): entry table, page list
+    int32_t qcap;          // page slots per block in the plan's page list
+    int32_t G;             // blocks of the page stream
     const uint16_t* q;
     float* out;
     float* part_ml;     // [items][GQ][2]  (running max in log2 units, sum)
     float* part_acc;    // [items][GQ][D]  (unnormalized)
-    uint32_t* arrive;   // [C*H] partials delivered per segment (page stream)
     float scale_log2;   // sm_scale * log2(e)
     int32_t B;
     int32_t Hq;
     int32_t chunk_pages;
     int32_t max_chunks;
     int32_t max_ctx;    // host bound on seq_lens (<= max_context); larger values are clipped
-    // chunk mode (verify / chunked prefill through the page stream): entry b's
-    // query tokens are rows cu_q[b] .. cu_q[b+1]-1 at positions q_pos0[b] + i;
-    // entries with more than max_cols query columns (tokens x GQ) are left to
-    // another kernel
-    const int32_t* q_pos0;
-    const int32_t* cu_q;
-    int32_t max_cols;
 };
+
+// Entry table of the call's plan (row, keys, ...), read by every kernel of
+// the decode launch.
+__device__ __forceinline__ int plan_ent(const DecodeArgs& a, int b, int field) {
+    return a.plan[plan::kOffEnt + b * plan::kEntWords + field];
+}
 
 // One 64-lane wave per work item (entry b, KV head h, chunk c).  QK: lane t
 // owns token t of the page; PV: lane owns EPL = D/64 head_dim elements.
@@ -70,8 +72,8 @@ __global__ void __launch_bounds__(256) decode_split_kernel(DecodeArgs a) {
     const int c = item % a.max_chunks;
     const int bh = item / a.max_chunks;
     const int h = bh % H, b = bh / H;
-    const int row = a.table_rows[b];
-    const int ctx = (row >= 0 && row < a.pv.C) ? min(a.seq_lens[b], a.max_ctx) : 0;
+    const int row = plan_ent(a, b, plan::E_ROW);
+    const int ctx = plan_ent(a, b, plan::E_KEYS);
     const int n_pages = (ctx + kPage - 1) >> kPageShift;
     const int p0 = c * a.chunk_pages;
     const int p1 = min(p0 + a.chunk_pages, n_pages);
@@ -153,51 +155,8 @@ __global__ void __launch_bounds__(256) decode_split_kernel(DecodeArgs a) {
 
 
 
-// ---------------------------------------------------------------------------
-// Flat page stream (BF16).  The work of one decode call is the ordered list of
-// (entry b, KV head h, page p) for b < B, h < H, p < ceil(ctx_b / 64): segment
-// s = b*H + h holds ceil(ctx_b/64) consecutive pages.  Block i of G takes the
-// contiguous range [i*Q, min((i+1)*Q, total)), Q = ceil(total / G), so every
-// block streams the same number of pages whatever the length mix.  A block
-// writes one partial (m, l, acc) per segment it touches, in slot i + s: both
-// the block and the segment index only grow along the stream, so no two
-// touched (block, segment) pairs share a slot, and G + B*H slots suffice.
-// Segment s is covered by the blocks first(s)..last(s) and owns the slots
-// first(s)+s .. last(s)+s.  Ranges depend only on the context lengths, never
-// on page ids, and the combine adds the slots in block order: deterministic.
-struct Seg {
-    int b, h, n;       // entry, KV head, pages in the segment
-    int start;         // first global page index of the segment
-};
-
-
-__device__ __forceinline__ int ctx_of(const DecodeArgs& a, int b) {
-    const int row = ld_uniform(a.table_rows, b);
-    return (row >= 0 && row < a.pv.C) ? min(ld_uniform(a.seq_lens, b), a.max_ctx) : 0;
-}
-
-// Pages of every entry (B <= 8), read once: independent scalar loads instead
-// of a dependent chain per segment step.
-struct EntryPages {
-    int n[8];
-    __device__ __forceinline__ int operator()(int b) const {
-        int r = 0;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) r = (b == i) ? n[i] : r;
-        return r;
-    }
-};
-
-__device__ __forceinline__ EntryPages entry_pages(const DecodeArgs& a) {
-    EntryPages e;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) e.n[i] = i < a.B ? (ctx_of(a, i) + kPage - 1) >> kPageShift : 0;
-    return e;
-}
-
 // floor(x / Q) for 0 <= x < 2^24 through the fp32 reciprocal, corrected to
-// the exact quotient (an integer division is a long instruction sequence; the
-// segment walks below do many of them).
+// the exact quotient (an integer division is a long instruction sequence).
 struct Divider {
     int Q;
     float rq;
@@ -210,43 +169,19 @@ struct Divider {
     }
 };
 
-// partial slots owned by a segment of n pages starting at `start`
-__device__ __forceinline__ int seg_slots(int start, int n, const Divider& dq) {
-    return n > 0 ? dq(start + n - 1) - dq(start) + 1 : 0;
-}
-
-// Walker over the flat page list: (segment, page within it).
-struct PageCursor {
-    Seg seg;
-    int p;
-};
-
-__device__ __forceinline__ void cursor_next(const DecodeArgs& a, const EntryPages& np, PageCursor& c) {
-    if (++c.p < c.seg.n) return;
-    int b = c.seg.b, h = c.seg.h + 1;
-    const int start = c.seg.start + c.seg.n;
-    c.p = 0;
-    for (;;) {
-        if (h == a.pv.H) { h = 0; ++b; }
-        if (b >= a.B) { c.seg = Seg{b, 0, 0, start}; return; }
-        const int n = np(b);
-        if (n > 0) { c.seg = Seg{b, h, n, start}; return; }
-        h = a.pv.H;                                  // empty entry: skip its heads
-    }
-}
-
 // ---------------------------------------------------------------------------
-// Matrix-core page stream (BF16 pages, D in {64, 128}, 1..8 entries).
-//
-// One 256-thread block per compute unit streams its range of the flat page
-// list through an LDS ring of NS page stages filled by direct-to-LDS loads,
-// so NS-1 pages are in flight while one is computed.  Wave w owns tokens
-// [16w, 16w+16) of every page and keeps its own online-softmax state.
+// Matrix-core page stream (BF16 pages, D in {64, 128}, 1..8 entries): runs a
+// page-stream plan (stream_plan.h).  Block i streams the pages of stream
+// positions [i*Q, (i+1)*Q) through an LDS ring of NS page stages filled by
+// direct-to-LDS loads, so NS-1 pages are in flight while one is computed.
+// A unit (segment s, KV head h) carries the query columns of every entry in
+// the segment's mask: GQ heads per entry in decode (shared pages carry the
+// heads of all entries that share them), T x GQ (token, head) columns of one
+// entry in chunk mode; each column has its own causal key limit.  Wave w
+// owns tokens [16w, 16w+16) of every page and keeps its own online-softmax
+// state.
 //  * QK^T on the matrix cores: S^T[16 tokens x 16] = K . Q^T with
-//    v_mfma_f32_16x16x32_bf16; the GQ query heads of the page's KV head are
-//    the columns (the other columns are padding: a column of the product
-//    only ever depends on its own column of Q^T, and no padding column is
-//    read back).
+//    v_mfma_f32_16x16x32_bf16 (padding columns are zero and never read back).
 //  * The accumulator layout of S^T (lane l: column l%16, tokens 4(l/16)+r)
 //    is the B-operand layout of v_mfma_f32_16x16x16_bf16, so P^T feeds PV
 //    in place.
@@ -256,64 +191,24 @@ __device__ __forceinline__ void cursor_next(const DecodeArgs& a, const EntryPage
 //    addressed by lanes 4e + i/4).  P enters as two bf16 terms p_hi + p_lo
 //    (two products), about 2^-16 relative error instead of bf16's 2^-9.
 //  * Lazy rescaling: the exponent reference of a column moves only when a
-//    page's maximum exceeds it by more than 2^8, so the accumulators are
-//    rescaled a few times per segment instead of on every new maximum.
+//    page's maximum exceeds it by more than 2^8.
 //  * K rows are XOR-swizzled in 16-byte chunks, V rows in 32-byte units, so
 //    both reads are free of LDS bank conflicts.
-// Each page's slice, valid rows and segment-end flag are listed in LDS before
-// the ring starts.  When a segment ends, the four waves' states are merged
-// through the stage just consumed, and the merged partial waits in registers
-// until the stream ends (loads and stores share the vector-memory counter
-// that the ring waits on).  Then a segment that lies inside one block is
-// normalized and written out; the others are stored as partials, and the
-// block that brings the last partial of a segment (per-segment arrival
-// counter in the workspace) combines them in block order: one launch,
-// deterministic output.
-
-// Query columns of one entry for the page stream: keys [0, keys) exist; query
-// token i (row cu + i of q and out) sees keys [0, min(n0 + i + 1, keys)).
-// One query token per entry (decode) is n0 = ctx - 1, T = 1.  `owned` is false
-// for an entry a chunk-mode launch leaves to another kernel.
-struct EntryQ {
-    int n0, T, cu, keys;
-    bool owned;
-};
-
-template <bool CHUNK, int GQ>
-__device__ __forceinline__ EntryQ entry_q(const DecodeArgs& a, int b) {
-    const int row = ld_uniform(a.table_rows, b);
-    const bool ok = row >= 0 && row < a.pv.C;
-    if constexpr (!CHUNK) {
-        const int ctx = ok ? min(ld_uniform(a.seq_lens, b), a.max_ctx) : 0;
-        return EntryQ{ctx - 1, 1, b, ctx, true};
-    } else {
-        const int c0 = ld_uniform(a.cu_q, b), T = ld_uniform(a.cu_q, b + 1) - c0;
-        const int n0 = ld_uniform(a.q_pos0, b);
-        const int keys = ok ? max(0, min(n0 + T, a.max_ctx)) : 0;
-        return EntryQ{n0, T, c0, keys, T * GQ <= a.max_cols};
-    }
-}
-
-template <bool CHUNK, int GQ>
-__device__ __forceinline__ EntryPages stream_pages(const DecodeArgs& a) {
-    EntryPages e;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        int n = 0;
-        if (i < a.B) {
-            const EntryQ q = entry_q<CHUNK, GQ>(a, i);
-            n = (q.owned && q.T > 0) ? (q.keys + kPage - 1) >> kPageShift : 0;
-        }
-        e.n[i] = n;
-    }
-    return e;
-}
-
-// NCT column tiles of 16 query columns; column c = 16*ct + lane%16 holds query
-// token c / GQ and head c % GQ of the segment's KV head.  CHUNK: several query
-// tokens per entry (verify / chunked prefill) with a causal limit per column.
+// Before the ring starts, one round trip brings the plan's tables and the
+// block's page list into LDS; the query rows of the block's first units go
+// to LDS by direct-to-LDS loads ahead of the first pages.  When a unit ends,
+// the four waves' states are merged through the stage just consumed, and the
+// merged partial waits in registers until the stream ends (loads and stores
+// share the vector-memory counter that the ring waits on).  Then a column
+// whose (entry, KV head) has no other piece is normalized and written out;
+// the others are stored as partials in slot i + sigma, and the block that
+// brings the last piece of an (entry, KV head) (arrival counter in the
+// workspace) combines its pieces in unit and block order: one launch,
+// deterministic output.  Both the block index and sigma only grow along the
+// stream, so no two (block, unit) pieces share a slot.
 template <int D, int GQ, int NCT, bool CHUNK>
 __global__ void __launch_bounds__(256) paged_stream_kernel(DecodeArgs a) {
+    using namespace plan;
     constexpr int NCH = D / 8;                     // 16-byte chunks per row
     constexpr int NT = 256;
     constexpr int SLOTS = 64 * NCH;                // chunks per page slice of one plane
@@ -326,97 +221,91 @@ __global__ void __launch_bounds__(256) paged_stream_kernel(DecodeArgs a) {
     constexpr int DPW = NDT / 4;                   // tiles each wave merges and writes
     constexpr int WBUF = NDT * 4 * 64;             // floats of one wave's state in the merge area
     constexpr int NCOL = 16 * NCT;                 // query columns (partial slot width)
-    constexpr int QCOL = CHUNK ? NCOL : GQ;        // query rows cached per segment
-    constexpr int QSEG_RAW = (CHUNK ? 16384 : 8192) / (QCOL * D * 2);
-    constexpr int QSEG = QSEG_RAW < 1 ? 1 : (QSEG_RAW > 8 ? 8 : QSEG_RAW);   // segments with cached queries
+    constexpr int QCHUNKS = 1024;                  // query cache: 16 KiB of 16-byte chunks
+    constexpr int QSEG = QCHUNKS / (NCOL * NCH);   // units with cached queries
     constexpr int PMAX = NCT == 1 ? 3 : 2;         // merged partials held in registers
     static_assert((D == 64 || D == 128) && GQ >= 1 && GQ <= 16 && GQ <= NCOL, "shape");
     static_assert(PER_T == 2 || PER_T == 4, "page fetch shapes");
+    static_assert(QSEG >= 1 && QSEG * NCOL * NCH == QCHUNKS && QCHUNKS % NT == 0, "query cache shape");
     static_assert(NS * SLICE_BYTES == 0x10000, "V stages sit 64 KiB above the K stages");
-    static_assert(LOADS_PER_PAGE * (NS - 1) < 64, "vmcnt range");
+    static_assert(LOADS_PER_PAGE * (NS - 1) + QCHUNKS / NT < 64, "vmcnt range");
     static_assert(2 * WBUF * 4 <= SLICE_BYTES, "two waves' merge state fit one slice");
 
     __shared__ u32x4 ring[2][NS][SLOTS];           // [K | V][stage][slot]
-    __shared__ int2 pinfo[kStreamPages];           // per page of the range: (slice g*H + h or -1, meta)
-    __shared__ u32x4 qcache[QSEG][QCOL * NCH];     // query rows of the first QSEG segments
-    __shared__ float mlbuf[4][16][2];              // per-wave (m, l) of every column at a segment end
-    __shared__ int4 ctask[PMAX];                   // segments the flushing block completes: (b, h, first slot, slots)
-    __shared__ int ctask_n;
+    __shared__ int2 pinfo[kStreamPages];           // the block's pages: (slice g*H + h or -1, meta)
+    __shared__ u32x4 qcache[QCHUNKS];              // query rows of the first QSEG units: [unit][column][chunk]
+    __shared__ float mlbuf[4][16][2];              // per-wave (m, l) of every column at a unit's end
+    __shared__ int ent_s[kMaxEnt][kEntWords];
+    __shared__ int seg_s[kMaxSeg][kSegWords];
+    __shared__ int exp_s[kMaxEnt * kMaxH];         // pieces per (entry, KV head)
 
     const int tid = int(threadIdx.x);
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63, li = lane & 15, lg = lane >> 4;
-    const int H = a.pv.H, M = a.pv.M, G = int(gridDim.x), i_blk = int(blockIdx.x);
+    const int H = a.pv.H, i_blk = int(blockIdx.x), G = int(gridDim.x);
+    const int32_t* P = a.plan;
 
-    const EntryPages np = stream_pages<CHUNK, GQ>(a);
+    // one round trip: the plan's header and tables, this block's page list
+    const bool plan_ok = ld_uniform(P, H_MAGIC) == kMagic && ld_uniform(P, H_B) == a.B &&
+                         ld_uniform(P, H_H) == H && ld_uniform(P, H_GQ) == GQ && ld_uniform(P, H_G) == G &&
+                         ld_uniform(P, H_QCAP) == a.qcap && ld_uniform(P, H_CHUNK) == int(CHUNK);
+    const int Q = ld_uniform(P, H_Q), nseg = ld_uniform(P, H_NSEG), zero = ld_uniform(P, H_ZERO);
+    const int npg = ld_uniform(P, off_blk(H) + 2 * size_t(i_blk));
+    int sig = ld_uniform(P, off_blk(H) + 2 * size_t(i_blk) + 1);   // unit being computed
+    if (tid < kMaxEnt * kEntWords) ent_s[tid / kEntWords][tid % kEntWords] = P[kOffEnt + tid];
+    if (tid < kMaxSeg * kSegWords) seg_s[tid / kSegWords][tid % kSegWords] = P[kOffSeg + tid];
+    for (int x = tid; x < kMaxEnt * H; x += NT) exp_s[x] = P[kOffExp + x];
+    {
+        const int2* pl = reinterpret_cast<const int2*>(P + off_pages(H, G)) + size_t(i_blk) * a.qcap;
+        for (int x = tid; x < a.qcap; x += NT) pinfo[x] = pl[x];
+    }
+    block_lds_barrier();
+    if (!plan_ok) {                                // a plan of another batch shape: make it visible
+        if (!CHUNK && i_blk == 0)
+            for (int x = tid; x < a.B * a.Hq * D; x += NT) a.out[x] = __builtin_nanf("");
+        return;
+    }
     if (i_blk == 0) {                              // entries with nothing to attend produce zeros
         for (int b = 0; b < a.B; ++b) {
-            if (np(b) != 0) continue;
-            const EntryQ e = entry_q<CHUNK, GQ>(a, b);
-            if (!e.owned) continue;
-            for (int x = tid; x < e.T * a.Hq * D; x += NT) a.out[size_t(e.cu) * a.Hq * D + x] = 0.f;
+            if (!((zero >> b) & 1)) continue;
+            const size_t r0 = size_t(ent_s[b][E_CU]) * a.Hq * D;
+            for (int x = tid; x < ent_s[b][E_T] * a.Hq * D; x += NT) a.out[r0 + x] = 0.f;
         }
     }
-    int total = 0;
-    for (int b = 0; b < a.B; ++b) total += np(b) * H;
-    if (total == 0) return;
-    const int Q = (total + G - 1) / G;             // the host sizes G so that Q <= kStreamPages
-    const Divider dq(Q);
-    const int u0 = i_blk * Q;
-    const int npg = min(u0 + Q, total) - u0;       // pages of this block
     if (npg <= 0) return;
 
-    PageCursor cc{Seg{0, 0, 0, 0}, 0};             // the segment being computed
-    {
-        int st = 0;                                // first stream page of entry b
-        for (int b = 0; b < a.B; ++b) {
-            const int n = np(b);
-            if (n > 0 && u0 < st + n * H) {
-                const int h = (u0 - st) / n;
-                cc = PageCursor{Seg{b, h, n, st + h * n}, u0 - st - h * n};
-                break;
-            }
-            st += n * H;
-        }
-    }
-
-    // query row of column c of entry e (head h*GQ + c%GQ of token c/GQ)
-    auto q_row = [&](const EntryQ& e, int h, int c) __attribute__((always_inline)) {
-        return a.q + (size_t(e.cu + c / GQ) * a.Hq + size_t(h) * GQ + c % GQ) * D;
+    // column c of a unit of segment s: entry, query token, head within the group
+    struct Col {
+        int b, tok, j;
     };
-
-    // Before the ring starts: every page's slice, valid rows, segment-end flag
-    // and page index (meta = valid rows | 256 at a segment end | page << 9),
-    // and the query rows of the first QSEG segments (later ones load theirs
-    // when they start).
-    {
-        PageCursor c = cc;
-        int off = 0, k = 0;
-        while (off < npg) {
-            const int cnt = min(c.seg.n - c.p, npg - off);
-            const int row = ld_uniform(a.table_rows, c.seg.b);
-            const EntryQ e = entry_q<CHUNK, GQ>(a, c.seg.b);
-            const int32_t* trow = a.pv.table + size_t(row) * a.pv.L;
-            for (int i = tid; i < cnt; i += NT) {
-                const int p = c.p + i;
-                const int g0 = trow[p];
-                const bool mapped = g0 >= 0 && g0 < M;
-                const int lim = mapped ? min(kPage, e.keys - p * kPage) : 0;
-                const bool end = (p == c.seg.n - 1) || (off + i == npg - 1);
-                pinfo[off + i] = make_int2(mapped ? g0 * H + c.seg.h : -1, lim | (end ? 256 : 0) | (p << 9));
-            }
-            if (k < QSEG) {
-                const int ncol = min(e.T * GQ, QCOL);
-                for (int i = tid; i < ncol * NCH; i += NT)
-                    qcache[k][i] = reinterpret_cast<const u32x4*>(q_row(e, c.seg.h, i / NCH))[i % NCH];
-            }
-            ++k;
-            off += cnt;
-            c.p += cnt - 1;
-            cursor_next(a, np, c);
+    auto col_of = [&](int s, int c) __attribute__((always_inline)) {
+        if constexpr (CHUNK) {
+            return Col{seg_s[s][S_OWNER], c / GQ, c % GQ};
+        } else {
+            int m = seg_s[s][S_MASK];
+            for (int k = c / GQ; k > 0; --k) m &= m - 1;
+            return Col{__builtin_ctz(unsigned(m | 0x100)), 0, c % GQ};
         }
-        wait_vmcnt<0>();
-        block_lds_barrier();
+    };
+    auto ncol_of = [&](int s) __attribute__((always_inline)) {
+        return __builtin_popcount(unsigned(seg_s[s][S_MASK])) * seg_s[s][S_W];
+    };
+    auto q_row = [&](const Col& cl, int h) __attribute__((always_inline)) {
+        return a.q + (size_t(ent_s[cl.b][E_CU] + cl.tok) * a.Hq + size_t(h) * GQ + cl.j) * D;
+    };
+    auto unit_seg = [&](int sg) __attribute__((always_inline)) { return sg / H; };
+
+    // query rows of the first QSEG units, straight into LDS (columns past a
+    // unit's last read row 0 of the call; they are never used)
+    const uint32_t qcache_lds = uint32_t(reinterpret_cast<uintptr_t>((lds_byte_ptr)(&qcache[0])));
+#pragma unroll
+    for (int k = 0; k < QCHUNKS / NT; ++k) {
+        const int x = k * NT + tid;
+        const int u = x / (NCOL * NCH), c = (x / NCH) % NCOL, ch = x % NCH;
+        const int sg = sig + u, s = unit_seg(sg);
+        const u32x4* src = reinterpret_cast<const u32x4*>(a.q);
+        if (s < nseg && c < ncol_of(s)) src = reinterpret_cast<const u32x4*>(q_row(col_of(s, c), sg - s * H)) + ch;
+        fetch_chunk(qcache_lds + uint32_t((k * NT + w * 64) * 16), src);
     }
 
     // Stage layout: K slot s (row t = s / NCH, position x = s % NCH) holds
@@ -442,6 +331,10 @@ __global__ void __launch_bounds__(256) paged_stream_kernel(DecodeArgs a) {
         if constexpr (PER_T == 4) fetch_page4(dst, kplane + off, vplane + off, k_src, v_src);
         else fetch_page2(dst, kplane + off, vplane + off, k_src, v_src);
     };
+    // meta of page fi: the last page of the block also ends its unit here
+    auto meta_of = [&](int fi) __attribute__((always_inline)) {
+        return __builtin_amdgcn_readfirstlane(pinfo[fi].y) | (fi == npg - 1 ? 256 : 0);
+    };
 
     // Per-lane LDS offsets into stage 0, fixed for the whole stream (the
     // stage adds an immediate below 64 KiB).
@@ -462,39 +355,39 @@ __global__ void __launch_bounds__(256) paged_stream_kernel(DecodeArgs a) {
 
     bf16x8_t qb[NCT][NC];                          // Q^T B operand: column 16ct + li, chunk 4c + lg
     int klim[NCT];                                 // keys this lane's column sees (0: padding column)
-    int kmin = 0;                                  // smallest limit of a real column of the segment
-    auto start_segment = [&](int k_seg, int b, int h) __attribute__((always_inline)) {
-        const EntryQ e = entry_q<CHUNK, GQ>(a, b);
-        const int ncol = e.T * GQ;
-        kmin = min(e.n0 + 1, e.keys);
+    int kmin = 0;                                  // smallest limit of a real column of the unit
+    auto start_unit = [&](int k_unit, int sg) __attribute__((always_inline)) {
+        const int s = unit_seg(sg), h = sg - s * H;
+        const int ncol = ncol_of(s);
+        kmin = seg_s[s][S_KMIN];
 #pragma unroll
         for (int ct = 0; ct < NCT; ++ct) {
-            const int col = 16 * ct + li;
-            klim[ct] = col < ncol ? min(e.n0 + col / GQ + 1, e.keys) : 0;
+            const int c = 16 * ct + li;
+            const Col cl = col_of(s, c < ncol ? c : 0);
+            klim[ct] = c < ncol ? min(ent_s[cl.b][E_N0] + cl.tok + 1, ent_s[cl.b][E_KEYS]) : 0;
         }
-        if (k_seg < QSEG) {
+        if (k_unit < QSEG) {
 #pragma unroll
             for (int ct = 0; ct < NCT; ++ct) {
-                const int col = 16 * ct + li;
-                const int cq = min(col, QCOL - 1);
+                const int c = 16 * ct + li;
 #pragma unroll
-                for (int c = 0; c < NC; ++c) {
-                    const u32x4 v = qcache[k_seg][cq * NCH + 4 * c + lg];
-                    qb[ct][c] = __builtin_bit_cast(bf16x8_t, col < ncol ? v : u32x4{0u, 0u, 0u, 0u});
+                for (int k = 0; k < NC; ++k) {
+                    const u32x4 v = qcache[(k_unit * NCOL + c) * NCH + 4 * k + lg];
+                    qb[ct][k] = __builtin_bit_cast(bf16x8_t, c < ncol ? v : u32x4{0u, 0u, 0u, 0u});
                 }
             }
         } else {
 #pragma unroll
             for (int ct = 0; ct < NCT; ++ct) {
-                const int col = 16 * ct + li;
-                const u32x4* qg = reinterpret_cast<const u32x4*>(q_row(e, h, col < ncol ? col : 0));
+                const int c = 16 * ct + li;
+                const u32x4* qg = reinterpret_cast<const u32x4*>(q_row(col_of(s, c < ncol ? c : 0), h));
 #pragma unroll
-                for (int c = 0; c < NC; ++c) {
-                    const u32x4 v = qg[4 * c + lg];
-                    qb[ct][c] = __builtin_bit_cast(bf16x8_t, col < ncol ? v : u32x4{0u, 0u, 0u, 0u});
+                for (int k = 0; k < NC; ++k) {
+                    const u32x4 v = qg[4 * k + lg];
+                    qb[ct][k] = __builtin_bit_cast(bf16x8_t, c < ncol ? v : u32x4{0u, 0u, 0u, 0u});
                 }
             }
-            wait_vmcnt<0>();                       // drains the ring: only past the cached segments
+            wait_vmcnt<0>();                       // drains the ring: only past the cached units
         }
     };
 
@@ -513,156 +406,54 @@ __global__ void __launch_bounds__(256) paged_stream_kernel(DecodeArgs a) {
     // merged partials waiting for the end of the stream
     f32x4_t pend_acc[PMAX][NCT][DPW];
     float pend_m[PMAX][NCT], pend_l[PMAX][NCT];
-    int pend_b[PMAX], pend_h[PMAX], pend_first[PMAX], pend_nsl[PMAX];   // pend_first: first slot of the segment
+    int pend_sig[PMAX];
     int npend = 0;
 
-    // Partials cross blocks (and the L2s of different dies) as device-scope
-    // relaxed atomic stores and loads, which are coherent without cache
-    // write-back or invalidation (device-scope fences are L2-wide maintenance
-    // operations here, costly for every block on the die).  A block counts
-    // its arrival only after its partial stores completed (vmcnt 0), and the
-    // last block loads the partials only after its increment returned.
-    auto st_dev = [](float* p, float v) __attribute__((always_inline)) {
-        __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    };
-    auto ld_dev = [](const float* p) __attribute__((always_inline)) {
-        return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    };
-    // The combine issues the loads of four outputs of a thread before it uses
-    // any (one memory round trip for up to four partials per output).
-    auto combine = [&](int b, int h, int first, int nsl) __attribute__((always_inline)) {
-        constexpr int CMAX = 4, XB = 4;
-        const EntryQ e = entry_q<CHUNK, GQ>(a, b);
-        const int ncol = min(e.T * GQ, QCOL);
-#pragma unroll 1
-        for (int x0 = tid; x0 < ncol * D; x0 += XB * NT) {
-            float fm[XB], fl[XB], fa[XB];         // running fold of the earlier rounds
-#pragma unroll 1
-            for (int k0 = 0; k0 < nsl; k0 += CMAX) {   // more than CMAX partials: folded in rounds
-                const int kn = min(CMAX, nsl - k0);
-                float mk[XB][CMAX], lk[XB][CMAX], ak[XB][CMAX];
-#pragma unroll
-                for (int xb = 0; xb < XB; ++xb) {
-                    const int x = x0 + xb * NT;
-                    const int c = x / D, d = x % D;
-#pragma unroll
-                    for (int k = 0; k < CMAX; ++k) {
-                        if (x < ncol * D && k < kn) {
-                            const size_t it = size_t(first + k0 + k) * NCOL + c;
-                            mk[xb][k] = ld_dev(a.part_ml + it * 2);
-                            lk[xb][k] = ld_dev(a.part_ml + it * 2 + 1);
-                            ak[xb][k] = ld_dev(a.part_acc + it * D + d);
-                        }
-                    }
-                }
-#pragma unroll
-                for (int xb = 0; xb < XB; ++xb) {
-                    const int x = x0 + xb * NT;
-                    if (x >= ncol * D) continue;
-                    float mx = k0 > 0 ? fm[xb] : -INFINITY;
-#pragma unroll
-                    for (int k = 0; k < CMAX; ++k)
-                        if (k < kn) mx = fmaxf(mx, mk[xb][k]);
-                    float l = 0.f, acc_x = 0.f;
-#pragma unroll
-                    for (int k = 0; k < CMAX; ++k) {
-                        if (k < kn) {
-                            const float wgt = mk[xb][k] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mk[xb][k] - mx);
-                            l += lk[xb][k] * wgt;
-                            acc_x += ak[xb][k] * wgt;
-                        }
-                    }
-                    if (k0 > 0) {
-                        const float wp = fm[xb] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(fm[xb] - mx);
-                        l += fl[xb] * wp;
-                        acc_x += fa[xb] * wp;
-                    }
-                    fm[xb] = mx;
-                    fl[xb] = l;
-                    fa[xb] = acc_x;
-                }
-            }
-#pragma unroll
-            for (int xb = 0; xb < XB; ++xb) {
-                const int x = x0 + xb * NT;
-                if (x >= ncol * D) continue;
-                const int c = x / D, d = x % D;
-                float* o = a.out + (size_t(e.cu + c / GQ) * a.Hq + size_t(h) * GQ + c % GQ) * D + d;
-                *o = fl[xb] > 0.f ? fa[xb] * (1.f / fl[xb]) : 0.f;
-            }
-        }
-    };
-
-    // Write out or store every pending partial, count arrivals, combine the
-    // segments this block completes.  Block-uniform; waits for all memory
-    // traffic of the block.
+    // Write out or store every pending partial: a column whose (entry, KV
+    // head) has no other piece is normalized and written; the others go to
+    // slot i + sigma for the combine launch.  Block-uniform; waits for all
+    // memory traffic of the block.
     auto flush = [&]() __attribute__((always_inline)) {
 #pragma unroll
         for (int k = 0; k < PMAX; ++k) {
             if (k >= npend) break;
-            const EntryQ e = entry_q<CHUNK, GQ>(a, pend_b[k]);
-            const int ncol = e.T * GQ;
+            const int sg = pend_sig[k], s = unit_seg(sg), h = sg - s * H;
+            const int ncol = ncol_of(s);
 #pragma unroll
             for (int ct = 0; ct < NCT; ++ct) {
                 const int c = 16 * ct + li;
                 if (c >= ncol) continue;
-                if (pend_nsl[k] == 1) {
+                const Col cl = col_of(s, c);
+                if (exp_s[cl.b * H + h] == 1) {
                     const float inv = pend_l[k][ct] > 0.f ? 1.f / pend_l[k][ct] : 0.f;
-                    float* o = a.out + (size_t(e.cu + c / GQ) * a.Hq + size_t(pend_h[k]) * GQ + c % GQ) * D + 4 * lg;
+                    float* o = a.out + (size_t(ent_s[cl.b][E_CU] + cl.tok) * a.Hq + size_t(h) * GQ + cl.j) * D +
+                               4 * lg;
 #pragma unroll
                     for (int kk = 0; kk < DPW; ++kk) {
                         const f32x4_t v = pend_acc[k][ct][kk] * inv;
                         *reinterpret_cast<float4*>(o + 16 * (w * DPW + kk)) = make_float4(v[0], v[1], v[2], v[3]);
                     }
                 } else {
-                    const size_t it = size_t(i_blk + pend_b[k] * H + pend_h[k]) * NCOL + c;
+                    const size_t it = size_t(i_blk + sg) * NCOL + c;
                     float* o = a.part_acc + it * D + 4 * lg;
 #pragma unroll
                     for (int kk = 0; kk < DPW; ++kk)
-#pragma unroll
-                        for (int r = 0; r < 4; ++r) st_dev(o + 16 * (w * DPW + kk) + r, pend_acc[k][ct][kk][r]);
-                    if (w == 0 && lg == 0) {
-                        st_dev(a.part_ml + it * 2, pend_m[k][ct]);
-                        st_dev(a.part_ml + it * 2 + 1, pend_l[k][ct]);
-                    }
+                        *reinterpret_cast<float4*>(o + 16 * (w * DPW + kk)) =
+                            make_float4(pend_acc[k][ct][kk][0], pend_acc[k][ct][kk][1], pend_acc[k][ct][kk][2],
+                                        pend_acc[k][ct][kk][3]);
+                    if (w == 0 && lg == 0)
+                        *reinterpret_cast<float2*>(a.part_ml + it * 2) = make_float2(pend_m[k][ct], pend_l[k][ct]);
                 }
             }
-        }
-        wait_vmcnt<0>();                           // this block's partials are complete
-        __syncthreads();
-        if (tid == 0) {                            // arrive; list the segments this block completes
-            int nt = 0;
-#pragma unroll
-            for (int k = 0; k < PMAX; ++k) {
-                if (k >= npend) break;
-                if (pend_nsl[k] > 1) {
-                    const unsigned old = atomicAdd(a.arrive + pend_b[k] * H + pend_h[k], 1u);
-                    if (int(old) + 1 == pend_nsl[k]) {
-                        ctask[nt] = make_int4(pend_b[k], pend_h[k], pend_first[k], pend_nsl[k]);
-                        ++nt;
-                    }
-                }
-            }
-            ctask_n = nt;
-        }
-        __syncthreads();
-        const int nt = __builtin_amdgcn_readfirstlane(ctask_n);
-#pragma unroll 1
-        for (int t = 0; t < nt; ++t) {
-            const int4 c = ctask[t];
-            const int cb = __builtin_amdgcn_readfirstlane(c.x), ch = __builtin_amdgcn_readfirstlane(c.y);
-            combine(cb, ch, __builtin_amdgcn_readfirstlane(c.z), __builtin_amdgcn_readfirstlane(c.w));
-            if (tid == 0)                          // ready for the next call
-                __hip_atomic_store(a.arrive + cb * H + ch, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
         wait_vmcnt<0>();
         __syncthreads();
         npend = 0;
     };
 
-    // segment end: merge the four waves' states through stage st (waves 0-1
+    // unit end: merge the four waves' states through stage st (waves 0-1
     // use its K slice, waves 2-3 its V slice), one column tile at a time
-    auto finish_segment = [&](int st) __attribute__((always_inline)) {
+    auto finish_unit = [&](int st) __attribute__((always_inline)) {
         auto wbuf = [&](int v) __attribute__((always_inline)) {
             return reinterpret_cast<float*>(&ring[v >> 1][st][0]) + (v & 1) * WBUF;
         };
@@ -707,7 +498,7 @@ __global__ void __launch_bounds__(256) paged_stream_kernel(DecodeArgs a) {
             mxs[ct] = mx;
             lts[ct] = lt;
         }
-        if (npend == PMAX) flush();                // rare: many segments in one range
+        if (npend == PMAX) flush();                // rare: many units in one range
 #pragma unroll
         for (int k = 0; k < PMAX; ++k) {
             if (k == npend) {
@@ -718,18 +509,13 @@ __global__ void __launch_bounds__(256) paged_stream_kernel(DecodeArgs a) {
                     pend_m[k][ct] = mxs[ct];
                     pend_l[k][ct] = lts[ct];
                 }
-                pend_b[k] = cc.seg.b;
-                pend_h[k] = cc.seg.h;
-                pend_first[k] = dq(cc.seg.start) + cc.seg.b * H + cc.seg.h;
-                pend_nsl[k] = seg_slots(cc.seg.start, cc.seg.n, dq);
+                pend_sig[k] = sig;
             }
         }
         ++npend;
         reset();
     };
 
-    int seg_k = 0;
-    start_segment(seg_k, cc.seg.b, cc.seg.h);
     reset();
     const int tb = 16 * w + 4 * lg;                 // token of accumulator register r: tb + r
     int meta_ring[NS];                              // meta of the pages in the ring, by stage
@@ -737,12 +523,18 @@ __global__ void __launch_bounds__(256) paged_stream_kernel(DecodeArgs a) {
     for (int k = 0; k < NS - 1; ++k) {
         if (k < npg) {
             fetch(k, k);
-            meta_ring[k] = __builtin_amdgcn_readfirstlane(pinfo[k].y);
+            meta_ring[k] = meta_of(k);
         } else {
             meta_ring[k] = 0;
         }
     }
     meta_ring[NS - 1] = 0;
+    // the query cache and the first page have landed (loads complete in order)
+    if (npg >= NS - 1) wait_vmcnt<LOADS_PER_PAGE * (NS - 2)>();
+    else wait_vmcnt<0>();
+    block_lds_barrier();
+    int unit_k = 0;
+    start_unit(unit_k, sig);
 
     // one page in stage J (compile time, so every LDS offset is an immediate)
     auto step = [&](auto jc, int i) __attribute__((always_inline)) {
@@ -755,15 +547,15 @@ __global__ void __launch_bounds__(256) paged_stream_kernel(DecodeArgs a) {
             wait_vmcnt<LOADS_PER_PAGE * (NS - 2)>();
             block_lds_barrier();
             fetch(i + NS - 1, FS);
-            meta_ring[FS] = __builtin_amdgcn_readfirstlane(pinfo[i + NS - 1].y);
+            meta_ring[FS] = meta_of(i + NS - 1);
         } else {
             wait_vmcnt<0>();
             block_lds_barrier();
         }
 
         const int meta = meta_ring[J];
-        const int lim = meta & 255;                 // valid rows of the page
-        if (lim > 16 * w) {                         // this wave has valid rows in the page
+        const int lim = meta & 255;                 // rows any column of the unit may see
+        if (lim > 16 * w) {                         // this wave has such rows in the page
             const int tok0 = (meta >> 9) * kPage;   // first key of the page
             const u32x4* kst = &ring[0][J][0];
             f32x4_t s[NCT];
@@ -801,8 +593,8 @@ __global__ void __launch_bounds__(256) paged_stream_kernel(DecodeArgs a) {
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     p[r] = __builtin_amdgcn_exp2f(sj[r] - m_ref[ct]);
-                    // a column with no visible key yet (chunk mode) has no reference
-                    if constexpr (CHUNK) p[r] = m_ref[ct] == -INFINITY ? 0.f : p[r];
+                    // a column with no visible key in this wave yet has no reference
+                    p[r] = m_ref[ct] == -INFINITY ? 0.f : p[r];
                 }
                 l_part[ct] += (p[0] + p[1]) + (p[2] + p[3]);
                 uint32_t h01, l01, h23, l23;
@@ -812,8 +604,9 @@ __global__ void __launch_bounds__(256) paged_stream_kernel(DecodeArgs a) {
                 plo[ct] = __builtin_bit_cast(s16x4_t, u32x2{l01, l23});
             }
             if (lim < kPage) {
-                // rows past the frontier hold stale bytes (possibly NaN): this
-                // wave clears its own rows of the V slice, which only it reads
+                // rows past the last limit hold stale bytes (possibly NaN):
+                // this wave clears its own rows of the V slice, which only it
+                // reads
                 const int r0 = max(lim, 16 * w), rows = 16 * w + 16 - r0;
                 u32x4* vrows = &ring[1][J][r0 * NCH];
                 for (int x = lane; x < rows * NCH; x += 64) vrows[x] = u32x4{0u, 0u, 0u, 0u};
@@ -832,12 +625,11 @@ __global__ void __launch_bounds__(256) paged_stream_kernel(DecodeArgs a) {
         }
 
         if (meta & 256) {
-            finish_segment(J);
+            finish_unit(J);
             if (i + 1 < npg) {
-                cc.p = cc.seg.n - 1;
-                cursor_next(a, np, cc);
-                ++seg_k;
-                start_segment(seg_k, cc.seg.b, cc.seg.h);
+                ++sig;
+                ++unit_k;
+                start_unit(unit_k, sig);
             }
         }
     };
@@ -857,6 +649,94 @@ __global__ void __launch_bounds__(256) paged_stream_kernel(DecodeArgs a) {
     flush();
 }
 
+// Combine of the page stream: one wave per task of the plan -- an (entry,
+// KV head) whose outputs have more than one piece.  The task lists its
+// pieces (the (block, unit) partials of the entry's units in segment order,
+// each unit's slots in block order): a fixed order, so the result does not
+// depend on timing.  Every lane folds 8 consecutive outputs of one column
+// over all pieces, CMAX pieces per memory round; the task record is read with
+// scalar loads in the same round trip as the header.
+template <int D, int GQ, int NCOL>
+__global__ void __launch_bounds__(256) stream_combine_kernel(DecodeArgs a) {
+    using namespace plan;
+    constexpr int CMAX = 16;
+    const int lane = int(threadIdx.x) & 63;
+    const int w = __builtin_amdgcn_readfirstlane(int(threadIdx.x) >> 6);
+    const int H = a.pv.H;
+    const int t = int(blockIdx.x) * 4 + w;
+    const int32_t* P = a.plan;
+    const int32_t* rec = P + off_tasks(H, int(a.G)) + size_t(t) * kTaskWords;
+    const bool plan_ok = ld_uniform(P, H_MAGIC) == kMagic && ld_uniform(P, H_B) == a.B &&
+                         ld_uniform(P, H_H) == H && ld_uniform(P, H_GQ) == GQ;
+    const int ntask = ld_uniform(P, H_NTASK);
+    const int E = ld_uniform(rec, T_E), ncolb = ld_uniform(rec, T_NCOL), obase = ld_uniform(rec, T_OUT);
+    const int poff = ld_uniform(rec, T_POFF);
+    if (!plan_ok || t >= ntask) return;            // (a plan of another shape: the stream marked the outputs)
+    const int32_t* over_list = P + off_over(H, int(a.G));
+    auto piece = [&](int k) __attribute__((always_inline)) {
+        return k < kTaskInline ? ld_uniform(rec, T_PIECE + k) : ld_uniform(over_list, poff + k - kTaskInline);
+    };
+
+    // uniform trip counts: the pieces are wave-uniform scalar values
+#pragma unroll 1
+    for (int g0 = 0; g0 < ncolb * D; g0 += 64 * 8) {
+        const int e0 = g0 + lane * 8;
+        const bool act = e0 < ncolb * D;
+        const int c = act ? e0 / D : 0, d0 = act ? e0 % D : 0;
+        float fm = -INFINITY, fl = 0.f, fa[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) fa[e] = 0.f;
+#pragma unroll 1
+        for (int k0 = 0; k0 < E; k0 += CMAX) {
+            float2 ml[CMAX];
+            float4 av[CMAX][2];
+#pragma unroll
+            for (int kk = 0; kk < CMAX; ++kk) {
+                if (k0 + kk < E) {
+                    const size_t it = size_t(piece(k0 + kk)) + c;
+                    if (act) {
+                        ml[kk] = *reinterpret_cast<const float2*>(a.part_ml + it * 2);
+                        av[kk][0] = *reinterpret_cast<const float4*>(a.part_acc + it * D + d0);
+                        av[kk][1] = *reinterpret_cast<const float4*>(a.part_acc + it * D + d0 + 4);
+                    }
+                }
+            }
+            if (act) {
+                float mx = fm;
+#pragma unroll
+                for (int kk = 0; kk < CMAX; ++kk)
+                    if (k0 + kk < E) mx = fmaxf(mx, ml[kk].x);
+                const float wp = fm == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(fm - mx);
+                fl *= wp;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) fa[e] *= wp;
+#pragma unroll
+                for (int kk = 0; kk < CMAX; ++kk) {
+                    if (k0 + kk < E) {
+                        const float wgt = ml[kk].x == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ml[kk].x - mx);
+                        fl += ml[kk].y * wgt;
+                        fa[0] += av[kk][0].x * wgt;
+                        fa[1] += av[kk][0].y * wgt;
+                        fa[2] += av[kk][0].z * wgt;
+                        fa[3] += av[kk][0].w * wgt;
+                        fa[4] += av[kk][1].x * wgt;
+                        fa[5] += av[kk][1].y * wgt;
+                        fa[6] += av[kk][1].z * wgt;
+                        fa[7] += av[kk][1].w * wgt;
+                    }
+                }
+                fm = mx;
+            }
+        }
+        if (act) {
+            const float inv = fl > 0.f ? 1.f / fl : 0.f;
+            float* o = a.out + obase + size_t(c / GQ) * a.Hq * D + size_t(c % GQ) * D + d0;
+            *reinterpret_cast<float4*>(o) = make_float4(fa[0] * inv, fa[1] * inv, fa[2] * inv, fa[3] * inv);
+            *reinterpret_cast<float4*>(o + 4) = make_float4(fa[4] * inv, fa[5] * inv, fa[6] * inv, fa[7] * inv);
+        }
+    }
+}
+
 // Combine the chunks of each (entry, query head) in chunk order.
 template <int D, int GQ>
 __global__ void __launch_bounds__(64) decode_combine_kernel(DecodeArgs a) {
@@ -864,8 +744,7 @@ __global__ void __launch_bounds__(64) decode_combine_kernel(DecodeArgs a) {
     const int lane = int(threadIdx.x);
     const int b = int(blockIdx.x) / a.Hq, j = int(blockIdx.x) % a.Hq;
     const int h = j / GQ, jj = j % GQ;
-    const int row = a.table_rows[b];
-    const int ctx = (row >= 0 && row < a.pv.C) ? min(a.seq_lens[b], a.max_ctx) : 0;
+    const int ctx = plan_ent(a, b, plan::E_KEYS);
     const int n_pages = (ctx + kPage - 1) >> kPageShift;
     const int n_chunks = (n_pages + a.chunk_pages - 1) / a.chunk_pages;
     float* o = a.out + (size_t(b) * a.Hq + j) * D + lane * EPL;
@@ -916,16 +795,26 @@ int stream_grid(const PoolView& pv, int B, int max_seq_len) {
         const int v = e ? std::atoi(e) : 0;
         return (v >= 1 && v <= 4096) ? v : n;
     }();
-    const long long bound = (long long)B * pv.H * ((max_seq_len + kPage - 1) / kPage);
-    const long long need = (bound + kStreamPages - 1) / kStreamPages;
+    const long long need = (stream_bound(pv, B, max_seq_len) + kStreamPages - 1) / kStreamPages;
     return int(need > cus ? need : cus);
 }
 
-// The matrix-core page stream covers BF16 pages with D in {64, 128} and up to
-// eight entries per call; everything else takes the chunked split kernel.
+// Shared pages are read once per call unless KVS_STREAM_SHARE=0 (a tuning
+// knob read once per process, for measuring what the sharing saves).
+bool stream_share() {
+    static const bool on = [] {
+        const char* e = std::getenv("KVS_STREAM_SHARE");
+        return !(e && e[0] == '0');
+    }();
+    return on;
+}
+
+// The matrix-core page stream covers BF16 pages with D in {64, 128}, up to
+// eight entries per call and 64 KV heads; everything else takes the chunked
+// split kernel.
 bool stream_path(const PoolView& pv, int B, int gq) {
     return pv.k_codec == CODEC_BF16 && pv.v_codec == CODEC_BF16 && (pv.D == 64 || pv.D == 128) && B <= 8 &&
-           (gq == 1 || gq == 2 || gq == 4 || gq == 8);
+           pv.H <= plan::kMaxH && (gq == 1 || gq == 2 || gq == 4 || gq == 8);
 }
 
 int max_chunks_for(int max_seq_len) {
@@ -933,11 +822,67 @@ int max_chunks_for(int max_seq_len) {
     return (pages + chunk_pages() - 1) / chunk_pages();
 }
 
+// Workspace: [plan][partial (m, l) pairs][partial accumulators], each from a
+// 256-byte boundary.  Every call writes what it reads: no initialization.
+struct WsLayout {
+    bool stream;
+    int G, qcap;        // page stream: blocks, page slots per block
+    size_t plan, ml, acc, total;
+    size_t cols;        // partial slot width
+};
+
+size_t align256(size_t x) { return (x + 255) / 256 * 256; }
+
+WsLayout ws_layout(const PoolView& pv, int B, int gq, int max_seq_len, bool chunk) {
+    WsLayout l{};
+    l.stream = chunk || stream_path(pv, B, gq);
+    size_t slots;
+    if (l.stream) {
+        l.G = stream_grid(pv, B, max_seq_len);
+        const long long bound = stream_bound(pv, B, max_seq_len);
+        l.qcap = int(bound > 0 ? (bound + l.G - 1) / l.G : 1);
+        slots = size_t(l.G) + size_t(plan::kMaxSeg) * pv.H;     // (block, unit) pieces
+        l.cols = chunk ? 32 : 16;
+    } else {
+        slots = size_t(B) * pv.H * max_chunks_for(max_seq_len);  // one per split
+        l.cols = size_t(gq);
+    }
+    l.plan = 0;
+    l.ml = l.plan + plan::plan_bytes(pv.H, l.G, l.qcap);
+    l.acc = l.ml + align256(slots * l.cols * 2 * sizeof(float));
+    l.total = l.acc + slots * l.cols * size_t(pv.D) * sizeof(float);
+    return l;
+}
+
+DecodeArgs run_args(const PoolView& pv, const WsLayout& l, int B, int Hq, int max_seq_len, const void* q,
+                    float sm_scale, float* out, void* ws) {
+    DecodeArgs a{};
+    char* base = static_cast<char*>(ws);
+    a.pv = pv;
+    a.plan = reinterpret_cast<const int32_t*>(base + l.plan);
+    a.qcap = l.qcap;
+    a.G = l.G;
+    a.q = static_cast<const uint16_t*>(q);
+    a.out = out;
+    a.B = B;
+    a.Hq = Hq;
+    a.chunk_pages = chunk_pages();
+    a.max_chunks = max_chunks_for(max_seq_len);
+    a.max_ctx = max_seq_len;
+    a.part_ml = reinterpret_cast<float*>(base + l.ml);
+    a.part_acc = reinterpret_cast<float*>(base + l.acc);
+    a.scale_log2 = sm_scale * kLog2e;
+    return a;
+}
+
 template <int D, int GQ>
-hipError_t launch_gq(const DecodeArgs& a, hipStream_t s) {
+hipError_t launch_gq(const DecodeArgs& a, bool stream, hipStream_t s) {
     if constexpr (D == 64 || D == 128) {
-        if (stream_path(a.pv, a.B, GQ)) {
+        if (stream) {
             paged_stream_kernel<D, GQ, 1, false><<<dim3(unsigned(stream_grid(a.pv, a.B, a.max_ctx))), 256, 0, s>>>(a);
+            const hipError_t e = hipGetLastError();
+            if (e != hipSuccess) return e;
+            stream_combine_kernel<D, GQ, 16><<<dim3(unsigned((a.B * a.pv.H + 3) / 4)), 256, 0, s>>>(a);
             return hipGetLastError();
         }
     }
@@ -964,17 +909,42 @@ hipError_t launch_gq(const DecodeArgs& a, hipStream_t s) {
 }
 
 template <int D>
-hipError_t launch_d(const DecodeArgs& a, int gq, hipStream_t s) {
+hipError_t launch_d(const DecodeArgs& a, int gq, bool stream, hipStream_t s) {
     switch (gq) {
-        case 1: return launch_gq<D, 1>(a, s);
-        case 2: return launch_gq<D, 2>(a, s);
-        case 4: return launch_gq<D, 4>(a, s);
-        case 8: return launch_gq<D, 8>(a, s);
+        case 1: return launch_gq<D, 1>(a, stream, s);
+        case 2: return launch_gq<D, 2>(a, stream, s);
+        case 4: return launch_gq<D, 4>(a, stream, s);
+        case 8: return launch_gq<D, 8>(a, stream, s);
     }
     return hipErrorNotSupported;
 }
 
+template <int D>
+hipError_t launch_chunk_d(const DecodeArgs& a, int gq, int G, hipStream_t s) {
+    const dim3 grid(static_cast<unsigned>(G));
+    const dim3 cgrid(static_cast<unsigned>((a.B * a.pv.H + 3) / 4));
+    switch (gq) {
+#define KVS_CHUNK_CASE(GQ)                                                  \
+    case GQ:                                                                \
+        paged_stream_kernel<D, GQ, 2, true><<<grid, 256, 0, s>>>(a);        \
+        if (hipPeekAtLastError() == hipSuccess)                             \
+            stream_combine_kernel<D, GQ, 32><<<cgrid, 256, 0, s>>>(a);      \
+        break;
+        KVS_CHUNK_CASE(1)
+        KVS_CHUNK_CASE(2)
+        KVS_CHUNK_CASE(4)
+        KVS_CHUNK_CASE(8)
+#undef KVS_CHUNK_CASE
+        default: return hipErrorNotSupported;
+    }
+    return hipGetLastError();
+}
+
 }  // namespace
+
+long long stream_bound(const PoolView& pv, int B, int max_seq_len) {
+    return (long long)B * pv.H * ((max_seq_len + kPage - 1) / kPage);
+}
 
 bool decode_supported(const PoolView& pv, int Hq) {
     if (pv.H <= 0 || Hq % pv.H) return false;
@@ -982,102 +952,59 @@ bool decode_supported(const PoolView& pv, int Hq) {
     return (pv.D == 64 || pv.D == 128 || pv.D == 256) && (gq == 1 || gq == 2 || gq == 4 || gq == 8);
 }
 
-// Workspace: [arrival counters][partial (m, l) pairs][partial accumulators],
-// each from a 256-byte boundary.  The counters (one per (table row, KV head),
-// sized by the pool so the layout does not move with B) must be zero before
-// the first call; every call leaves them zero.
-size_t arrive_bytes(const PoolView& pv) { return (size_t(pv.C) * pv.H * sizeof(uint32_t) + 255) / 256 * 256; }
-
-size_t ml_floats(size_t items, size_t gq) { return (items * gq * 2 + 63) / 64 * 64; }
-
-// partial slots: one per split (chunk path) or one per (block, touched
-// segment) of the page stream, at most G + B*H
-size_t partial_slots(const PoolView& pv, int B, int gq, int max_seq_len) {
-    if (stream_path(pv, B, gq)) return size_t(stream_grid(pv, B, max_seq_len)) + size_t(B) * pv.H;
-    return size_t(B) * pv.H * max_chunks_for(max_seq_len);
-}
-
-// partial slot width: the page stream keeps one 16-column tile per slot
-size_t slot_cols(const PoolView& pv, int B, int gq) { return stream_path(pv, B, gq) ? 16 : size_t(gq); }
-
 size_t decode_workspace_bytes(const PoolView& pv, int B, int Hq, int max_seq_len) {
-    const size_t gq = pv.H ? size_t(Hq / pv.H) : 0;
-    const size_t items = partial_slots(pv, B, int(gq), max_seq_len);
-    const size_t cols = slot_cols(pv, B, int(gq));
-    return arrive_bytes(pv) + (ml_floats(items, cols) + items * cols * size_t(pv.D)) * sizeof(float);
+    const int gq = pv.H ? Hq / pv.H : 0;
+    return ws_layout(pv, B, gq, max_seq_len, false).total;
 }
 
-bool stream_chunk_supported(const PoolView& pv, int B, int gq) { return stream_path(pv, B, gq); }
-
-size_t stream_chunk_workspace_bytes(const PoolView& pv, int B, int max_seq_len) {
-    const size_t items = size_t(stream_grid(pv, B, max_seq_len)) + size_t(B) * pv.H;
-    return arrive_bytes(pv) + (ml_floats(items, 32) + items * 32 * size_t(pv.D)) * sizeof(float);
-}
-
-template <int D>
-hipError_t launch_chunk_d(const DecodeArgs& a, int gq, hipStream_t s) {
-    const dim3 grid(unsigned(stream_grid(a.pv, a.B, a.max_ctx)));
-    switch (gq) {
-        case 1: paged_stream_kernel<D, 1, 2, true><<<grid, 256, 0, s>>>(a); break;
-        case 2: paged_stream_kernel<D, 2, 2, true><<<grid, 256, 0, s>>>(a); break;
-        case 4: paged_stream_kernel<D, 4, 2, true><<<grid, 256, 0, s>>>(a); break;
-        case 8: paged_stream_kernel<D, 8, 2, true><<<grid, 256, 0, s>>>(a); break;
-        default: return hipErrorNotSupported;
-    }
-    return hipGetLastError();
-}
-
-hipError_t launch_stream_chunk(const PoolView& pv, int B, int Hq, const int32_t* table_rows, const int32_t* q_pos0,
-                               const int32_t* cu_q, int max_seq_len, const void* q, float sm_scale, float* out,
-                               void* ws, int max_cols, hipStream_t s) {
-    DecodeArgs a{};
-    a.pv = pv;
-    a.table_rows = table_rows;
-    a.q_pos0 = q_pos0;
-    a.cu_q = cu_q;
-    a.max_cols = max_cols;
-    a.q = static_cast<const uint16_t*>(q);
-    a.out = out;
-    a.B = B;
-    a.Hq = Hq;
-    a.max_ctx = max_seq_len;
+hipError_t launch_decode_plan(const PoolView& pv, int B, int Hq, const int32_t* table_rows, const int32_t* seq_lens,
+                              int max_seq_len, void* ws, hipStream_t s) {
     const int gq = Hq / pv.H;
-    const size_t items = size_t(stream_grid(pv, B, max_seq_len)) + size_t(B) * pv.H;
-    a.arrive = static_cast<uint32_t*>(ws);
-    a.part_ml = reinterpret_cast<float*>(static_cast<char*>(ws) + arrive_bytes(pv));
-    a.part_acc = a.part_ml + ml_floats(items, 32);
-    a.scale_log2 = sm_scale * kLog2e;
+    const WsLayout l = ws_layout(pv, B, gq, max_seq_len, false);
+    int32_t* planp = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + l.plan);
+    return launch_stream_plan(pv, B, gq, table_rows, seq_lens, nullptr, nullptr, max_seq_len, 0, false,
+                              l.stream && stream_share(), l.stream, l.G, l.qcap, planp, s);
+}
+
+hipError_t launch_decode_run(const PoolView& pv, int B, int Hq, int max_seq_len, const void* q, float sm_scale,
+                             float* out, void* ws, hipStream_t s) {
+    const int gq = Hq / pv.H;
+    const WsLayout l = ws_layout(pv, B, gq, max_seq_len, false);
+    const DecodeArgs a = run_args(pv, l, B, Hq, max_seq_len, q, sm_scale, out, ws);
     switch (pv.D) {
-        case 64: return launch_chunk_d<64>(a, gq, s);
-        case 128: return launch_chunk_d<128>(a, gq, s);
+        case 64: return launch_d<64>(a, gq, l.stream, s);
+        case 128: return launch_d<128>(a, gq, l.stream, s);
+        case 256: return launch_d<256>(a, gq, l.stream, s);
     }
     return hipErrorNotSupported;
 }
 
 hipError_t launch_decode(const PoolView& pv, int B, int Hq, const int32_t* table_rows, const int32_t* seq_lens,
-                         int max_seq_len, const void* q, float sm_scale, float* out, void* ws, size_t /*ws_bytes*/,
-                         hipStream_t s) {
-    DecodeArgs a{};
-    a.pv = pv;
-    a.table_rows = table_rows;
-    a.seq_lens = seq_lens;
-    a.q = static_cast<const uint16_t*>(q);
-    a.out = out;
-    a.B = B;
-    a.Hq = Hq;
-    a.chunk_pages = chunk_pages();
-    a.max_chunks = max_chunks_for(max_seq_len);
-    a.max_ctx = max_seq_len;
+                         int max_seq_len, const void* q, float sm_scale, float* out, void* ws, hipStream_t s) {
+    hipError_t e = launch_decode_plan(pv, B, Hq, table_rows, seq_lens, max_seq_len, ws, s);
+    if (e != hipSuccess) return e;
+    return launch_decode_run(pv, B, Hq, max_seq_len, q, sm_scale, out, ws, s);
+}
+
+bool stream_chunk_supported(const PoolView& pv, int B, int gq) { return stream_path(pv, B, gq); }
+
+size_t stream_chunk_workspace_bytes(const PoolView& pv, int B, int Hq, int max_seq_len) {
+    return ws_layout(pv, B, Hq / pv.H, max_seq_len, true).total;
+}
+
+hipError_t launch_stream_chunk(const PoolView& pv, int B, int Hq, const int32_t* table_rows, const int32_t* q_pos0,
+                               const int32_t* cu_q, int max_seq_len, const void* q, float sm_scale, float* out,
+                               void* ws, int max_cols, hipStream_t s) {
     const int gq = Hq / pv.H;
-    const size_t items = partial_slots(pv, B, gq, max_seq_len);
-    a.arrive = static_cast<uint32_t*>(ws);
-    a.part_ml = reinterpret_cast<float*>(static_cast<char*>(ws) + arrive_bytes(pv));
-    a.part_acc = a.part_ml + ml_floats(items, slot_cols(pv, B, gq));
-    a.scale_log2 = sm_scale * kLog2e;
+    const WsLayout l = ws_layout(pv, B, gq, max_seq_len, true);
+    int32_t* planp = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + l.plan);
+    hipError_t e = launch_stream_plan(pv, B, gq, table_rows, nullptr, q_pos0, cu_q, max_seq_len, max_cols, true,
+                                      false, true, l.G, l.qcap, planp, s);
+    if (e != hipSuccess) return e;
+    const DecodeArgs a = run_args(pv, l, B, Hq, max_seq_len, q, sm_scale, out, ws);
     switch (pv.D) {
-        case 64: return launch_d<64>(a, gq, s);
-        case 128: return launch_d<128>(a, gq, s);
-        case 256: return launch_d<256>(a, gq, s);
+        case 64: return launch_chunk_d<64>(a, gq, l.G, s);
+        case 128: return launch_chunk_d<128>(a, gq, l.G, s);
     }
     return hipErrorNotSupported;
 }

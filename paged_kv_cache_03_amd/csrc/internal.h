@@ -55,19 +55,34 @@ hipError_t launch_append(const PoolView& pv, int B, const int32_t* table_rows, c
                          const int32_t* cu_tokens, int total_tokens, const void* k, const void* v,
                          hipStream_t s);
 
-// Decode: split-K partials in ws, then a combine.  Returns hipErrorNotSupported
-// for shapes with no kernel instance.
+// Page-stream plans (stream_plan.hip): the work list of one batch state in
+// the workspace.  chunk: several query tokens per entry (entries with more
+// than max_cols columns are left out); dedup: shared leading pages are read
+// once; pages: write the page list (the split kernel reads only the entry
+// table).
+int stream_plan_blocks(int bound);
+long long stream_bound(const PoolView& pv, int B, int max_seq_len);   // B x H x ceil(max_seq_len / 64)
+hipError_t launch_stream_plan(const PoolView& pv, int B, int gq, const int32_t* table_rows, const int32_t* seq_lens,
+                              const int32_t* q_pos0, const int32_t* cu_q, int max_seq_len, int max_cols, bool chunk,
+                              bool dedup, bool pages, int G, int qcap, int32_t* plan, hipStream_t s);
+
+// Decode: a plan of the batch state, then the run (the page stream, or split
+// partials and a combine).  Returns hipErrorNotSupported for shapes with no
+// kernel instance.
 bool decode_supported(const PoolView& pv, int Hq);
 size_t decode_workspace_bytes(const PoolView& pv, int B, int Hq, int max_seq_len);
+hipError_t launch_decode_plan(const PoolView& pv, int B, int Hq, const int32_t* table_rows, const int32_t* seq_lens,
+                              int max_seq_len, void* ws, hipStream_t s);
+hipError_t launch_decode_run(const PoolView& pv, int B, int Hq, int max_seq_len, const void* q, float sm_scale,
+                             float* out, void* ws, hipStream_t s);
 hipError_t launch_decode(const PoolView& pv, int B, int Hq, const int32_t* table_rows, const int32_t* seq_lens,
-                         int max_seq_len, const void* q, float sm_scale, float* out, void* ws, size_t ws_bytes,
-                         hipStream_t s);
+                         int max_seq_len, const void* q, float sm_scale, float* out, void* ws, hipStream_t s);
 
 // The page stream in chunk mode (several query tokens per entry, causal):
 // entries with at most max_cols query columns (tokens x GQ); the workspace
-// layout matches decode's (arrival counters first).
+// layout matches decode's (arrival counters first, then the plan).
 bool stream_chunk_supported(const PoolView& pv, int B, int gq);
-size_t stream_chunk_workspace_bytes(const PoolView& pv, int B, int max_seq_len);
+size_t stream_chunk_workspace_bytes(const PoolView& pv, int B, int Hq, int max_seq_len);
 hipError_t launch_stream_chunk(const PoolView& pv, int B, int Hq, const int32_t* table_rows, const int32_t* q_pos0,
                                const int32_t* cu_q, int max_seq_len, const void* q, float sm_scale, float* out,
                                void* ws, int max_cols, hipStream_t s);

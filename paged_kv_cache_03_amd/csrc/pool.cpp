@@ -500,24 +500,67 @@ int paged_attn_supported(const kv_pool* pool, uint32_t Hq, uint32_t max_q_len) {
     return max_q_len == 0 ? int(decode_supported(pv, int(Hq))) : int(verify_supported(pv, int(Hq)));
 }
 
-kv_status paged_attn_decode(const kv_pool* pool, uint32_t layer, uint32_t B, uint32_t Hq,
-                            const int32_t* d_table_rows, const int32_t* d_seq_lens, uint32_t max_seq_len,
-                            const void* d_q, float sm_scale, float* d_out, void* d_ws, size_t ws_bytes,
-                            hipStream_t stream) {
+// Shared checks of the decode entry points; *skip is set when B == 0 (a
+// call with nothing to do).
+static kv_status check_decode(const kv_pool* pool, uint32_t layer, uint32_t B, uint32_t Hq, uint32_t max_seq_len,
+                              void* d_ws, size_t ws_bytes, bool* skip) {
+    *skip = false;
     kv_status st = check_compute(pool, layer, B);
     if (st != KV_OK) return st;
     if (Hq == 0 || Hq % pool->geo.num_kv_heads) return fail(KV_E_GEOMETRY, "Hq must be a multiple of H");
-    if (!(sm_scale > 0.f) || !std::isfinite(sm_scale)) return fail(KV_E_INVALID, "sm_scale must be finite and > 0");
-    if (B == 0) return ok();
-    if (!d_table_rows || !d_seq_lens || !d_q || !d_out) return fail(KV_E_INVALID, "null device pointer");
+    if (B == 0) {
+        *skip = true;
+        return ok();
+    }
     if (max_seq_len > pool->geo.max_context) return fail(KV_E_INVALID, "max_seq_len beyond max_context");
     PoolView pv = pool->view(layer);
     if (!decode_supported(pv, int(Hq))) return fail(KV_E_UNSUPPORTED, "no decode kernel for this shape");
     size_t need = decode_workspace_bytes(pv, int(B), int(Hq), int(max_seq_len));
     if (need && (!d_ws || ws_bytes < need)) return fail(KV_E_INVALID, "workspace too small");
-    hipError_t e = launch_decode(pv, int(B), int(Hq), d_table_rows, d_seq_lens, int(max_seq_len), d_q, sm_scale,
-                                 d_out, d_ws, ws_bytes, stream);
+    return ok();
+}
+
+kv_status paged_attn_decode(const kv_pool* pool, uint32_t layer, uint32_t B, uint32_t Hq,
+                            const int32_t* d_table_rows, const int32_t* d_seq_lens, uint32_t max_seq_len,
+                            const void* d_q, float sm_scale, float* d_out, void* d_ws, size_t ws_bytes,
+                            hipStream_t stream) {
+    bool skip = false;
+    kv_status st = check_decode(pool, layer, B, Hq, max_seq_len, d_ws, ws_bytes, &skip);
+    if (st != KV_OK) return st;
+    if (!(sm_scale > 0.f) || !std::isfinite(sm_scale)) return fail(KV_E_INVALID, "sm_scale must be finite and > 0");
+    if (skip) return ok();
+    if (!d_table_rows || !d_seq_lens || !d_q || !d_out) return fail(KV_E_INVALID, "null device pointer");
+    hipError_t e = launch_decode(pool->view(layer), int(B), int(Hq), d_table_rows, d_seq_lens, int(max_seq_len), d_q,
+                                 sm_scale, d_out, d_ws, stream);
     if (e != hipSuccess) return fail(KV_E_DEVICE, std::string("decode launch: ") + hipGetErrorString(e));
+    return ok();
+}
+
+kv_status paged_attn_decode_plan(const kv_pool* pool, uint32_t B, uint32_t Hq, const int32_t* d_table_rows,
+                                 const int32_t* d_seq_lens, uint32_t max_seq_len, void* d_ws, size_t ws_bytes,
+                                 hipStream_t stream) {
+    bool skip = false;
+    kv_status st = check_decode(pool, 0, B, Hq, max_seq_len, d_ws, ws_bytes, &skip);
+    if (st != KV_OK || skip) return st;
+    if (!d_table_rows || !d_seq_lens) return fail(KV_E_INVALID, "null device pointer");
+    hipError_t e = launch_decode_plan(pool->view(0), int(B), int(Hq), d_table_rows, d_seq_lens, int(max_seq_len),
+                                      d_ws, stream);
+    if (e != hipSuccess) return fail(KV_E_DEVICE, std::string("decode plan launch: ") + hipGetErrorString(e));
+    return ok();
+}
+
+kv_status paged_attn_decode_run(const kv_pool* pool, uint32_t layer, uint32_t B, uint32_t Hq, uint32_t max_seq_len,
+                                const void* d_q, float sm_scale, float* d_out, void* d_ws, size_t ws_bytes,
+                                hipStream_t stream) {
+    bool skip = false;
+    kv_status st = check_decode(pool, layer, B, Hq, max_seq_len, d_ws, ws_bytes, &skip);
+    if (st != KV_OK) return st;
+    if (!(sm_scale > 0.f) || !std::isfinite(sm_scale)) return fail(KV_E_INVALID, "sm_scale must be finite and > 0");
+    if (skip) return ok();
+    if (!d_q || !d_out) return fail(KV_E_INVALID, "null device pointer");
+    hipError_t e = launch_decode_run(pool->view(layer), int(B), int(Hq), int(max_seq_len), d_q, sm_scale, d_out,
+                                     d_ws, stream);
+    if (e != hipSuccess) return fail(KV_E_DEVICE, std::string("decode run launch: ") + hipGetErrorString(e));
     return ok();
 }
 

@@ -85,6 +85,21 @@ __device__ __forceinline__ void fetch_page4(uint32_t lds_k, const void* kb, cons
 #undef KVS_DMA_PAIR
 #undef KVS_DMA_NEXT
 
+// One 16-byte chunk per lane from its own address into LDS[M0 + 16*lane]
+// (query rows into the block's query cache), ordered with the page loads on
+// the same counter.
+__device__ __forceinline__ void fetch_chunk(uint32_t lds_wave, const void* src) {
+    uint32_t sv;
+    asm volatile("s_mov_b32 %[sv], m0\n\t"
+                 "s_mov_b32 m0, %[d]\n\t"
+                 "s_nop 0\n\t"
+                 "global_load_lds_dwordx4 %[a], off\n\t"
+                 "s_mov_b32 m0, %[sv]"
+                 : [sv] "=&s"(sv)
+                 : [d] "s"(lds_wave), [a] "v"(src)
+                 : "memory");
+}
+
 // op over the four 16-lane rows (lanes l%16 + 16k); identical in every lane
 __device__ __forceinline__ float rows_max(float x) {
     const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);

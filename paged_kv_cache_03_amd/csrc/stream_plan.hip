@@ -1,0 +1,447 @@
+// stream_plan.hip -- builds the page-stream plan of one batch state (layout
+// and structure in stream_plan.h).
+//
+// NInfer "Paged KV Context Store" page: PagedKVBatchLayerView (table_rows[b]
+// selects the block-table row of entry b), P=64 translation, fork and tail
+// copy-on-write (a fork shares its parent's leading pages), consumer rules
+// (the op chooses its own split; pages are read in place through the table).
+//
+// Every block of the launch derives the same entry, sharing and segment
+// tables (one lane per entry of wave 0), then writes its share of the page
+// list: stream positions [k * kPlanSpan, (k + 1) * kPlanSpan).  Block 0 also
+// writes the header, the tables, the per-(entry, KV head) piece counts, the
+// per-block ranges and the combine tasks with their piece lists.  Shared runs are found by comparing table
+// entries, so a plan is exact for any table: two entries read a page once
+// only where both rows hold the same mapped page group.
+
+#include <hip/hip_runtime.h>
+
+#include <climits>
+
+#include "attn_common.h"
+#include "internal.h"
+#include "stream_plan.h"
+
+namespace kvs {
+namespace {
+
+using namespace plan;
+
+constexpr int kPlanSpan = 1024;   // stream positions per plan block
+constexpr int kNT = 256;
+
+struct PlanArgs {
+    const int32_t* table;   // [C][L]
+    int32_t L, C, M, H;
+    const int32_t* table_rows;
+    const int32_t* seq_lens;  // decode
+    const int32_t* q_pos0;    // chunk mode
+    const int32_t* cu_q;      // chunk mode
+    int32_t B, gq, max_ctx, max_cols, G, qcap, chunk, emax, pages;
+    int32_t D, ncol;          // head dim, partial slot width (columns)
+    int32_t* plan;
+};
+
+// floor(x / q) for 0 <= x, 0 < q
+__device__ __forceinline__ int pieces(int start, int n, int Q) { return n > 0 ? (start + n - 1) / Q - start / Q + 1 : 0; }
+
+__global__ void __launch_bounds__(kNT) stream_plan_kernel(PlanArgs a) {
+    __shared__ int ent[kMaxEnt][kEntWords];
+    __shared__ int lcp[kMaxEnt][kMaxEnt];          // [i][j], j < i: leading pages rows i and j share
+    __shared__ int cand[kMaxEnt * kMaxEnt];        // pairs still to scan (i << 3 | j)
+    __shared__ int cpre[kMaxEnt * kMaxEnt + 1];    // scan positions before each pair
+    __shared__ int ncand_s;
+    __shared__ int clo[kMaxEnt][kMaxEnt], chi[kMaxEnt][kMaxEnt];   // [b][o]: pages of owner o carrying b
+    __shared__ int seg[kMaxSeg][kSegWords];
+    __shared__ int res_s[3];                       // segments, zero mask, total
+    __shared__ int ex[kMaxEnt * kMaxH];            // pieces per (entry, KV head)
+
+    const int tid = int(threadIdx.x);
+    const int H = a.H;
+
+    if (tid < kMaxEnt) {
+        const int b = tid;
+        int row = -1, keys = 0, n0 = 0, cu = 0, T = 0, owned = 0;
+        if (b < a.B) {
+            row = a.table_rows[b];
+            const bool ok = row >= 0 && row < a.C;
+            if (!a.chunk) {
+                keys = ok ? max(0, min(a.seq_lens[b], a.max_ctx)) : 0;
+                n0 = keys - 1;
+                cu = b;
+                T = 1;
+                owned = 1;
+            } else {
+                cu = a.cu_q[b];
+                T = a.cu_q[b + 1] - cu;
+                n0 = a.q_pos0[b];
+                keys = ok ? max(0, min(n0 + T, a.max_ctx)) : 0;
+                owned = T * a.gq <= a.max_cols ? 1 : 0;
+            }
+        }
+        ent[b][E_ROW] = row;
+        ent[b][E_KEYS] = keys;
+        ent[b][E_N0] = n0;
+        ent[b][E_CU] = cu;
+        ent[b][E_T] = T;
+        ent[b][E_NPAGES] = (owned && T > 0) ? (keys + kPage - 1) >> kPageShift : 0;
+        ent[b][E_OWNED] = owned;
+        ent[b][7] = 0;
+    }
+    __syncthreads();
+
+    // shared leading runs: pairs whose first pages agree are compared page by
+    // page; the first mismatch (or unmapped page) ends the run
+    if (a.emax > 1) {
+        if (tid < kMaxEnt * kMaxEnt) {
+            const int i = tid >> 3, j = tid & 7;
+            int v = 0;
+            if (j < i && ent[i][E_NPAGES] > 0 && ent[j][E_NPAGES] > 0) {
+                const int gi = a.table[size_t(ent[i][E_ROW]) * a.L], gj = a.table[size_t(ent[j][E_ROW]) * a.L];
+                if (gi == gj && gi >= 0 && gi < a.M) v = min(ent[i][E_NPAGES], ent[j][E_NPAGES]);
+            }
+            lcp[i][j] = v;
+        }
+        __syncthreads();
+        if (tid == 0) {
+            int n = 0, pre = 0;
+            for (int i = 1; i < kMaxEnt; ++i)
+                for (int j = 0; j < i; ++j)
+                    if (lcp[i][j] > 1) {
+                        cand[n] = i << 3 | j;
+                        cpre[n] = pre;
+                        pre += lcp[i][j] - 1;
+                        ++n;
+                    }
+            cpre[n] = pre;
+            ncand_s = n;
+        }
+        __syncthreads();
+        const int n = ncand_s, tot = cpre[n];
+        for (int base = tid; base < tot; base += kNT * 8) {
+            int gi[8], gj[8], pr[8], pp[8];
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                const int idx = base + kNT * k;
+                pr[k] = -1;
+                if (idx < tot) {
+                    int c = 0;
+                    while (c + 1 < n && cpre[c + 1] <= idx) ++c;
+                    const int i = cand[c] >> 3, j = cand[c] & 7;
+                    pp[k] = 1 + idx - cpre[c];
+                    pr[k] = cand[c];
+                    gi[k] = a.table[size_t(ent[i][E_ROW]) * a.L + pp[k]];
+                    gj[k] = a.table[size_t(ent[j][E_ROW]) * a.L + pp[k]];
+                }
+            }
+#pragma unroll
+            for (int k = 0; k < 8; ++k)
+                if (pr[k] >= 0 && (gi[k] != gj[k] || gi[k] < 0 || gi[k] >= a.M))
+                    atomicMin(&lcp[pr[k] >> 3][pr[k] & 7], pp[k]);
+        }
+        __syncthreads();
+    }
+
+    // sharing trees and segments: wave 0, lane = entry (B <= 8)
+    if (tid < 64) {
+        const int lane = tid;
+        const bool me = lane < a.B;
+        const int np = me ? ent[lane][E_NPAGES] : 0;
+        int par = -1, ell = 0, root = lane, tsize = 1;   // this lane's entry (tsize: as a root)
+        for (int b = 0; b < a.B; ++b) {
+            if (__builtin_amdgcn_readlane(np, b) == 0) continue;
+            // earlier entry with the longest shared run whose tree has room (ties: lowest index)
+            int key = -1;
+            const int ts = __shfl(tsize, root);
+            if (a.emax > 1 && lane < b && np > 0 && ts < a.emax && lcp[b][lane & 7] > 0)
+                key = lcp[b][lane & 7] * 8 + (7 - lane);
+#pragma unroll
+            for (int d = 1; d < 8; d <<= 1) key = max(key, __shfl_xor(key, d));
+            key = __builtin_amdgcn_readlane(key, 0);
+            if (key >= 0) {
+                const int bp = 7 - (key & 7);
+                const int r = __builtin_amdgcn_readlane(root, bp);
+                if (lane == b) {
+                    par = bp;
+                    ell = key >> 3;
+                    root = r;
+                }
+                if (lane == r) ++tsize;
+            }
+        }
+        // b's columns ride along owner o over pages [clo, chi): o = b for
+        // [l_b, n_b); up the chain, the pages below every l passed so far
+        if (lane < kMaxEnt * kMaxEnt) clo[lane >> 3][lane & 7] = chi[lane >> 3][lane & 7] = 0;
+        wave_lds_sync();
+        {
+            int o = lane & 7, hi = np;
+            bool done = np == 0;
+#pragma unroll
+            for (int step = 0; step < kMaxEnt; ++step) {
+                const int ell_o = __shfl(ell, o), par_o = __shfl(par, o);
+                if (!done) {
+                    if (ell_o < hi) {
+                        clo[lane][o] = ell_o;
+                        chi[lane][o] = hi;
+                    }
+                    if (par_o < 0) {
+                        done = true;
+                    } else {
+                        hi = min(hi, ell_o);
+                        o = par_o;
+                    }
+                }
+            }
+        }
+        wave_lds_sync();
+        // owner lane o: its range [l_o, n_o) cut where the carried set changes
+        int lo[kMaxEnt], hi[kMaxEnt], cut[kMaxEnt + 2];
+#pragma unroll
+        for (int b = 0; b < kMaxEnt; ++b) {
+            lo[b] = clo[b][lane & 7];
+            hi[b] = chi[b][lane & 7];
+        }
+        const bool owner = me && np > 0 && ell < np;
+        cut[0] = ell;
+        cut[1] = np;
+#pragma unroll
+        for (int b = 0; b < kMaxEnt; ++b) cut[2 + b] = hi[b] > lo[b] ? hi[b] : np;
+#pragma unroll
+        for (int x = 1; x < kMaxEnt + 2; ++x)        // insertion sort, fixed shape
+#pragma unroll
+            for (int y = x; y > 0; --y) {
+                const int u = min(cut[y - 1], cut[y]), v = max(cut[y - 1], cut[y]);
+                cut[y - 1] = u;
+                cut[y] = v;
+            }
+        int nown = 0;                                 // segments of this owner
+#pragma unroll
+        for (int x = 0; x + 1 < kMaxEnt + 2; ++x) nown += (owner && cut[x + 1] > cut[x]) ? 1 : 0;
+        const int pages = owner ? np - ell : 0;
+        // exclusive prefix sums over the lanes: segment index, pages
+        int sbase = nown, pbase = pages;
+#pragma unroll
+        for (int d = 1; d < 8; d <<= 1) {
+            const int s1 = __shfl_up(sbase, d), p1 = __shfl_up(pbase, d);
+            if ((lane & 7) >= d) {
+                sbase += s1;
+                pbase += p1;
+            }
+        }
+        const int nseg_all = __builtin_amdgcn_readlane(sbase, 7), pages_all = __builtin_amdgcn_readlane(pbase, 7);
+        sbase -= nown;
+        pbase -= pages;
+        if (owner) {
+            int si = sbase, pre = pbase * H;
+#pragma unroll
+            for (int x = 0; x + 1 < kMaxEnt + 2; ++x) {
+                const int c0 = cut[x], c1 = cut[x + 1];
+                if (c1 <= c0) continue;
+                int mask = 0, maxk = 0, kmin = INT_MAX;
+#pragma unroll
+                for (int b = 0; b < kMaxEnt; ++b)
+                    if (hi[b] > lo[b] && lo[b] <= c0 && c1 <= hi[b]) {
+                        mask |= 1 << b;
+                        maxk = max(maxk, ent[b][E_KEYS]);
+                        kmin = min(kmin, min(ent[b][E_N0] + 1, ent[b][E_KEYS]));
+                    }
+                seg[si][S_OWNER] = lane;
+                seg[si][S_P0] = c0;
+                seg[si][S_N] = c1 - c0;
+                seg[si][S_MASK] = mask;
+                seg[si][S_MAXKEYS] = maxk;
+                seg[si][S_KMIN] = kmin;
+                seg[si][S_PRE] = pre;
+                seg[si][S_W] = (a.chunk ? ent[lane][E_T] : 1) * a.gq;
+                pre += H * (c1 - c0);
+                ++si;
+            }
+        }
+        const uint64_t zb = __builtin_amdgcn_ballot_w64(me && np == 0 && ent[lane & 7][E_OWNED] && ent[lane & 7][E_T] > 0);
+        if (lane == 0) {
+            res_s[0] = nseg_all;
+            res_s[1] = int(zb & 0xff);
+            res_s[2] = pages_all * H;
+        }
+    }
+    __syncthreads();
+
+    const int nseg = res_s[0], total = res_s[2];
+    const int Q = total > 0 ? (total + a.G - 1) / a.G : 0;
+    // unit (segment s, head h) and page within it of stream position u
+    auto locate = [&](int u, int& s, int& h, int& pp) __attribute__((always_inline)) {
+        s = 0;
+        while (s + 1 < nseg && seg[s + 1][S_PRE] <= u) ++s;
+        const int off = u - seg[s][S_PRE], n = seg[s][S_N];
+        h = off / n;
+        pp = off - h * n;
+    };
+
+    int32_t* P = a.plan;
+    if (blockIdx.x == 0) {
+        if (tid < H_WORDS) {
+            int v = 0;
+            switch (tid) {
+                case H_MAGIC: v = kMagic; break;
+                case H_B: v = a.B; break;
+                case H_H: v = H; break;
+                case H_GQ: v = a.gq; break;
+                case H_G: v = a.G; break;
+                case H_QCAP: v = a.qcap; break;
+                case H_TOTAL: v = total; break;
+                case H_Q: v = Q; break;
+                case H_NSEG: v = nseg; break;
+                case H_ZERO: v = res_s[1]; break;
+                case H_CHUNK: v = a.chunk; break;
+                default: break;
+            }
+            if (tid != H_NTASK) P[tid] = v;      // written with the task list
+        }
+        if (tid < kMaxEnt * kEntWords) P[kOffEnt + tid] = ent[tid / kEntWords][tid % kEntWords];
+        if (tid < kMaxSeg * kSegWords)
+            P[kOffSeg + tid] = tid / kSegWords < nseg ? seg[tid / kSegWords][tid % kSegWords] : 0;
+        if (a.pages) {
+            // pieces (block, unit) that carry each (entry, KV head)
+            for (int x = tid; x < kMaxEnt * H; x += kNT) {
+                const int b = x / H, h = x - b * H;
+                int e = 0;
+                for (int s = 0; s < nseg; ++s)
+                    if ((seg[s][S_MASK] >> b) & 1) e += pieces(seg[s][S_PRE] + h * seg[s][S_N], seg[s][S_N], Q);
+                P[kOffExp + x] = e;
+                ex[x] = e;
+            }
+            int2* blk = reinterpret_cast<int2*>(P + off_blk(H));
+            for (int i = tid; i < a.G; i += kNT) {
+                const int u0 = i * Q;
+                const int npg = Q > 0 ? max(0, min(Q, total - u0)) : 0;
+                int s = 0, h = 0, pp = 0;
+                if (npg > 0) locate(u0, s, h, pp);
+                blk[i] = make_int2(npg, s * H + h);
+            }
+        }
+        __syncthreads();
+        if (tid < 64) {                            // wave 0: combine tasks, pairs with more than one piece
+            const int lane = tid;
+            const int n = a.pages ? a.B * H : 0, per = (n + 63) / 64;
+            int cnt = 0, over = 0;
+            for (int i = 0; i < per; ++i) {
+                const int x = lane * per + i;
+                if (x < n && ex[x] > 1) {
+                    ++cnt;
+                    over += max(0, ex[x] - kTaskInline);
+                }
+            }
+            int tb = cnt, ob = over;               // exclusive prefix sums over the lanes
+#pragma unroll
+            for (int d = 1; d < 64; d <<= 1) {
+                const int t1 = __shfl_up(tb, d), o1 = __shfl_up(ob, d);
+                if (lane >= d) {
+                    tb += t1;
+                    ob += o1;
+                }
+            }
+            const int ntask = __builtin_amdgcn_readlane(tb, 63);
+            tb -= cnt;
+            ob -= over;
+            int* over_list = P + off_over(H, a.G);
+            for (int i = 0; i < per; ++i) {
+                const int x = lane * per + i;
+                if (x >= n || ex[x] <= 1) continue;
+                const int b = x / H, h = x - b * H, E = ex[x];
+                int* rec = P + off_tasks(H, a.G) + size_t(tb) * kTaskWords;
+                rec[T_B] = b;
+                rec[T_H] = h;
+                rec[T_E] = E;
+                rec[T_OUT] = (ent[b][E_CU] * H * a.gq + h * a.gq) * a.D;
+                rec[T_NCOL] = ent[b][E_T] * a.gq;
+                rec[T_POFF] = ob;
+                int k = 0;
+                for (int s = 0; s < nseg; ++s) {
+                    const int mask = seg[s][S_MASK];
+                    if (!((mask >> b) & 1)) continue;
+                    const int ns = seg[s][S_N], start = seg[s][S_PRE] + h * ns;
+                    const int f = start / Q, nsl = (start + ns - 1) / Q - f + 1;
+                    const int colb = __builtin_popcount(unsigned(mask) & ((1u << b) - 1u)) * seg[s][S_W];
+                    for (int j = 0; j < nsl; ++j, ++k) {
+                        const int v = (f + j + s * H + h) * a.ncol + colb;
+                        if (k < kTaskInline) rec[T_PIECE + k] = v;
+                        else over_list[ob + k - kTaskInline] = v;
+                    }
+                }
+                ++tb;
+                ob += max(0, E - kTaskInline);
+            }
+            if (lane == 0) P[H_NTASK] = ntask;
+        }
+    }
+    if (!a.pages) return;
+
+    // page list: this block's span of stream positions, four per thread with
+    // the table reads issued together
+    int2* pages = reinterpret_cast<int2*>(P + off_pages(H, a.G));
+    const int u_end = min(total, (int(blockIdx.x) + 1) * kPlanSpan);
+    for (int u0 = int(blockIdx.x) * kPlanSpan + tid; u0 < u_end; u0 += 4 * kNT) {
+        int g[4], sl[4], meta[4], dst[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int u = u0 + k * kNT;
+            dst[k] = -1;
+            if (u < u_end) {
+                int s, h, pp;
+                locate(u, s, h, pp);
+                const int p = seg[s][S_P0] + pp;
+                const int row = ent[seg[s][S_OWNER]][E_ROW];
+                g[k] = a.table[size_t(row) * a.L + p];
+                sl[k] = h;
+                const int lim = min(kPage, seg[s][S_MAXKEYS] - p * kPage);
+                meta[k] = lim | (pp == seg[s][S_N] - 1 ? 256 : 0) | (p << 9);
+                const int i = u / Q;
+                dst[k] = i * a.qcap + (u - i * Q);
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+            if (dst[k] >= 0) {
+                const bool mapped = g[k] >= 0 && g[k] < a.M;
+                pages[dst[k]] = make_int2(mapped ? g[k] * H + sl[k] : -1, meta[k]);
+            }
+    }
+}
+
+}  // namespace
+
+int stream_plan_blocks(int bound) { return bound > 0 ? (bound + kPlanSpan - 1) / kPlanSpan : 1; }
+
+hipError_t launch_stream_plan(const PoolView& pv, int B, int gq, const int32_t* table_rows, const int32_t* seq_lens,
+                              const int32_t* q_pos0, const int32_t* cu_q, int max_seq_len, int max_cols, bool chunk,
+                              bool dedup, bool pages, int G, int qcap, int32_t* plan, hipStream_t s) {
+    PlanArgs a{};
+    a.table = pv.table;
+    a.L = pv.L;
+    a.C = pv.C;
+    a.M = pv.M;
+    a.H = pv.H;
+    a.table_rows = table_rows;
+    a.seq_lens = seq_lens;
+    a.q_pos0 = q_pos0;
+    a.cu_q = cu_q;
+    a.B = B;
+    a.gq = gq;
+    a.max_ctx = max_seq_len;
+    a.max_cols = max_cols;
+    a.G = G;
+    a.qcap = qcap;
+    a.chunk = chunk ? 1 : 0;
+    // a sharing tree stays within the 16 columns of one tile
+    a.emax = (dedup && !chunk) ? (16 / gq < kMaxEnt ? 16 / gq : kMaxEnt) : 1;
+    a.pages = pages ? 1 : 0;
+    a.D = pv.D;
+    a.ncol = chunk ? 32 : 16;
+    a.plan = plan;
+    const long long bound = (long long)B * pv.H * ((max_seq_len + kPage - 1) / kPage);
+    const int blocks = pages ? stream_plan_blocks(int(bound)) : 1;
+    stream_plan_kernel<<<dim3(unsigned(blocks)), kNT, 0, s>>>(a);
+    return hipGetLastError();
+}
+
+}  // namespace kvs

@@ -481,7 +481,7 @@ constexpr int kStreamCols = 32;
 
 size_t verify_workspace_bytes(const PoolView& pv, int B, int Hq, int max_seq_len, int) {
     const int gq = pv.H ? Hq / pv.H : 0;
-    return stream_chunk_supported(pv, B, gq) ? stream_chunk_workspace_bytes(pv, B, max_seq_len) : 0;
+    return stream_chunk_supported(pv, B, gq) ? stream_chunk_workspace_bytes(pv, B, Hq, max_seq_len) : 0;
 }
 
 hipError_t launch_verify(const PoolView& pv, int B, int Hq, const int32_t* table_rows, const int32_t* q_pos0,

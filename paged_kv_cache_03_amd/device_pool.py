@@ -109,14 +109,24 @@ class DevicePool:
 
     def workspace(self, B: int, Hq: int, max_seq_len: int, max_q_len: int = 0) -> torch.Tensor:
         n = abi.paged_attn_workspace_bytes(self.handle, B, Hq, max_seq_len, max_q_len)
-        # zero once: decode's per-segment arrival counters start at zero, and
-        # every call leaves them zero again
-        return torch.zeros(max(n, 256), dtype=torch.uint8, device=self.device)
+        # no initialization: every call writes the parts of it that it reads
+        return torch.empty(max(n, 256), dtype=torch.uint8, device=self.device)
 
     def decode(self, layer: int, Hq: int, table_rows: torch.Tensor, seq_lens: torch.Tensor, max_seq_len: int,
                q: torch.Tensor, sm_scale: float, out: torch.Tensor, ws: torch.Tensor) -> None:
         abi.paged_attn_decode(self.handle, layer, table_rows.numel(), Hq, ptr(table_rows), ptr(seq_lens),
                               max_seq_len, ptr(q), sm_scale, ptr(out), ptr(ws), ws.numel(), self.stream)
+
+    def decode_plan(self, Hq: int, table_rows: torch.Tensor, seq_lens: torch.Tensor, max_seq_len: int,
+                    ws: torch.Tensor) -> None:
+        """Work list of this batch state into ws (valid for every layer until the rows or lengths change)."""
+        abi.paged_attn_decode_plan(self.handle, table_rows.numel(), Hq, ptr(table_rows), ptr(seq_lens), max_seq_len,
+                                   ptr(ws), ws.numel(), self.stream)
+
+    def decode_run(self, layer: int, B: int, Hq: int, max_seq_len: int, q: torch.Tensor, sm_scale: float,
+                   out: torch.Tensor, ws: torch.Tensor) -> None:
+        abi.paged_attn_decode_run(self.handle, layer, B, Hq, max_seq_len, ptr(q), sm_scale, ptr(out), ptr(ws),
+                                  ws.numel(), self.stream)
 
     def verify(self, layer: int, Hq: int, table_rows: torch.Tensor, q_pos0: torch.Tensor, cu_q: torch.Tensor,
                total_q: int, max_q_len: int, max_seq_len: int, q: torch.Tensor, sm_scale: float, out: torch.Tensor,
