@@ -4,9 +4,10 @@
 A step is one decode step of the whole batch through every layer:
     paged_attn_decode_plan (the batch state's work list: which pages each
     block reads for which query columns, shared prefix pages once), then for
-    each layer: kv_append (one new token per sequence, quantized into its
-    page through the block table) + paged_attn_decode_run (split-K over pages
-    and the cross-split combine).
+    each layer: the append of one new token per sequence into its page
+    through the block table, and the decode (split-K over pages and the
+    cross-split combine).  On BF16 pages both are one call,
+    paged_attn_decode_append_run; otherwise kv_append + paged_attn_decode_run.
 Inputs are resident in HBM before timing; the step is idempotent (the same
 positions are re-appended, the same contexts decoded).
 
@@ -35,7 +36,7 @@ HBM_PEAK_GBS = 8000.0
 METRIC = "paged decode KV GB/s (% of HBM peak) + decode steps/s at C=8, 32K ctx"
 PROFILES = os.path.join(ROOT, "profiles")
 # sources of the decode kernel; the traffic summary is valid for this exact text
-DECODE_SRC = [os.path.join(ROOT, "paged_kv_cache_03_amd", "csrc", f) for f in ("decode.hip", "stream_common.h")]
+DECODE_SRC = [os.path.join(ROOT, "paged_kv_cache_03_amd", "csrc", f) for f in ("decode.hip", "stream_common.h", "stream_plan.h", "stream_plan.hip")]
 
 
 def decode_source_sha256() -> str:
@@ -303,15 +304,22 @@ def main() -> int:
 
     # one step: the work list of the batch state once (it depends only on the
     # block table and the lengths), then per layer the append of the step's
-    # rows and the decode run
+    # rows and the decode run -- one launch on the BF16 page stream, which
+    # appends the rows itself
+    fused = wl.profile == "BF16" and wl.D in (64, 128)
+
     def step(events=None):
         dp.decode_plan(wl.Hq, rows_t, lens_t, max_ctx, ws)
         for layer in range(wl.layers):
             kd, vd = step_inputs[layer]
-            dp.append(layer, rows_t, pos0_t, cu_t, total, kd, vd)
+            if not fused:
+                dp.append(layer, rows_t, pos0_t, cu_t, total, kd, vd)
             if events is not None:
                 events[layer][0].record()
-            dp.decode_run(layer, wl.B, wl.Hq, max_ctx, qs[layer], wl.sm_scale, out, ws)
+            if fused:
+                dp.decode_append_run(layer, wl.B, wl.Hq, max_ctx, kd, vd, qs[layer], wl.sm_scale, out, ws)
+            else:
+                dp.decode_run(layer, wl.B, wl.Hq, max_ctx, qs[layer], wl.sm_scale, out, ws)
             if events is not None:
                 events[layer][1].record()
 

@@ -272,6 +272,20 @@ kv_status paged_attn_decode_run(const kv_pool* pool, uint32_t layer, uint32_t B,
                                 const void* d_q, float sm_scale, float* d_out, void* d_ws, size_t ws_bytes,
                                 hipStream_t stream);
 
+/* paged_attn_decode_run with the step's rows appended by the run itself: the
+ * K and V row of entry b (bf16 d_k, d_v [B][H][D]) go to position
+ * seq_len[b] - 1 of its table row (the lengths of the plan; entries with
+ * seq_len 0 append nothing), and the decode attends them, as kv_append
+ * (pos0 = seq_len - 1, one token per entry) followed by
+ * paged_attn_decode_run would, with the same outputs and planes.  The page
+ * that receives a row must not be shared (fork and tail copy-on-write: copy
+ * the tail first), as for kv_append.  BF16 pages on the matrix-core stream
+ * only (D in {64, 128}, Hq / H in {1, 2, 4, 8}); KV_E_UNSUPPORTED otherwise
+ * (use kv_append and paged_attn_decode_run). */
+kv_status paged_attn_decode_append_run(const kv_pool* pool, uint32_t layer, uint32_t B, uint32_t Hq,
+                                       uint32_t max_seq_len, const void* d_k, const void* d_v, const void* d_q,
+                                       float sm_scale, float* d_out, void* d_ws, size_t ws_bytes, hipStream_t stream);
+
 /* Multi-token verify / chunked prefill on paged KV (causal): chunk token i of
  * entry b sits at position d_q_pos0[b] + i and attends [0, d_q_pos0[b] + i]
  * (the chunk's own K/V are appended first; the mask starts at any in-page

@@ -28,6 +28,7 @@ EXPORTS = ["kv_profile_planes", "kv_plane_bytes", "kv_pool_create", "kv_pool_des
            "kv_pool_table_host", "kv_pool_page_refs", "kv_seq_open", "kv_seq_fork", "kv_seq_ensure_mapped",
            "kv_seq_commit", "kv_seq_release", "kv_seq_info", "kv_cow_tail_page", "kv_append",
            "paged_attn_workspace_bytes", "paged_attn_decode", "paged_attn_decode_plan", "paged_attn_decode_run",
+           "paged_attn_decode_append_run",
            "paged_attn_verify", "paged_attn_supported",
            "kv_last_error_message"]
 
@@ -84,6 +85,7 @@ def _load():
         "paged_attn_decode": (i32, [vp, u32, u32, u32, vp, vp, u32, vp, ctypes.c_float, vp, vp, sz, vp]),
         "paged_attn_decode_plan": (i32, [vp, u32, u32, vp, vp, u32, vp, sz, vp]),
         "paged_attn_decode_run": (i32, [vp, u32, u32, u32, u32, vp, ctypes.c_float, vp, vp, sz, vp]),
+        "paged_attn_decode_append_run": (i32, [vp, u32, u32, u32, u32, vp, vp, vp, ctypes.c_float, vp, vp, sz, vp]),
         "paged_attn_verify": (i32, [vp, u32, u32, u32, vp, vp, vp, u32, u32, u32, vp, ctypes.c_float, vp, vp, sz,
                                     vp]),
         "paged_attn_supported": (ctypes.c_int, [vp, u32, u32]),
@@ -222,6 +224,13 @@ def paged_attn_decode_run(pool: int, layer: int, B: int, Hq: int, max_seq_len: i
                           d_out: int, d_ws: int, ws_bytes: int, stream: int = 0) -> None:
     _check(_lib.paged_attn_decode_run(pool, layer, B, Hq, max_seq_len, d_q, sm_scale, d_out, d_ws or None, ws_bytes,
                                       stream or None))
+
+
+def paged_attn_decode_append_run(pool: int, layer: int, B: int, Hq: int, max_seq_len: int, d_k: int, d_v: int,
+                                 d_q: int, sm_scale: float, d_out: int, d_ws: int, ws_bytes: int,
+                                 stream: int = 0) -> None:
+    _check(_lib.paged_attn_decode_append_run(pool, layer, B, Hq, max_seq_len, d_k, d_v, d_q, sm_scale, d_out,
+                                             d_ws or None, ws_bytes, stream or None))
 
 
 def paged_attn_verify(pool: int, layer: int, B: int, Hq: int, d_table_rows: int, d_q_pos0: int, d_cu_q: int,

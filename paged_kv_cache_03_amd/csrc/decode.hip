@@ -41,6 +41,8 @@ struct DecodeArgs {
     int32_t qcap;          // page slots per block in the plan's page list
     int32_t G;             // blocks of the page stream
     const uint16_t* q;
+    const uint16_t* k_new;  // decode with the step's rows: bf16 [B][H][D] K and V appended at keys - 1
+    const uint16_t* v_new;  // (nullptr: the rows are already in the planes)
     float* out;
     float* part_ml;     // [items][GQ][2]  (running max in log2 units, sum)
     float* part_acc;    // [items][GQ][D]  (unnormalized)
@@ -238,6 +240,8 @@ __global__ void __launch_bounds__(256) paged_stream_kernel(DecodeArgs a) {
     __shared__ int ent_s[kMaxEnt][kEntWords];
     __shared__ int seg_s[kMaxSeg][kSegWords];
     __shared__ int exp_s[kMaxEnt * kMaxH];         // pieces per (entry, KV head)
+    __shared__ int patch_s[kMaxPatch];             // the block's new-token rows: page | entry | head | row
+    __shared__ u32x4 pstage[NT];                   // their K and V chunks, staged before the ring starts
 
     const int tid = int(threadIdx.x);
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -250,8 +254,11 @@ __global__ void __launch_bounds__(256) paged_stream_kernel(DecodeArgs a) {
                          ld_uniform(P, H_H) == H && ld_uniform(P, H_GQ) == GQ && ld_uniform(P, H_G) == G &&
                          ld_uniform(P, H_QCAP) == a.qcap && ld_uniform(P, H_CHUNK) == int(CHUNK);
     const int Q = ld_uniform(P, H_Q), nseg = ld_uniform(P, H_NSEG), zero = ld_uniform(P, H_ZERO);
-    const int npg = ld_uniform(P, off_blk(H) + 2 * size_t(i_blk));
-    int sig = ld_uniform(P, off_blk(H) + 2 * size_t(i_blk) + 1);   // unit being computed
+    const int npg = ld_uniform(P, off_blk(H) + 4 * size_t(i_blk));
+    int sig = ld_uniform(P, off_blk(H) + 4 * size_t(i_blk) + 1);   // unit being computed
+    const bool append = !CHUNK && a.k_new != nullptr;
+    const int npatch = append ? ld_uniform(P, off_blk(H) + 4 * size_t(i_blk) + 2) : 0;
+    if (tid < kMaxPatch) patch_s[tid] = P[off_patch(H, G) + size_t(i_blk) * kMaxPatch + tid];
     if (tid < kMaxEnt * kEntWords) ent_s[tid / kEntWords][tid % kEntWords] = P[kOffEnt + tid];
     if (tid < kMaxSeg * kSegWords) seg_s[tid / kSegWords][tid % kSegWords] = P[kOffSeg + tid];
     for (int x = tid; x < kMaxEnt * H; x += NT) exp_s[x] = P[kOffExp + x];
@@ -295,6 +302,21 @@ __global__ void __launch_bounds__(256) paged_stream_kernel(DecodeArgs a) {
     };
     auto unit_seg = [&](int sg) __attribute__((always_inline)) { return sg / H; };
 
+    // new-token rows of this block (decode with the step's rows): chunk x of
+    // plane pl of staged row r_q at pstage[q * 2 * NCH + pl * NCH + x], issued
+    // first so that the first page's wait covers them
+    constexpr int PCH = 2 * NCH;                   // chunks of one staged row pair
+    if (npatch > 0) {
+        const int q = tid / PCH, pl = (tid / NCH) & 1, x = tid % NCH;
+        const u32x4* src = reinterpret_cast<const u32x4*>(a.q);
+        if (q < npatch) {
+            const int pe = patch_s[q];
+            const int b = (pe >> 12) & 7, h = (pe >> 15) & 63;
+            src = reinterpret_cast<const u32x4*>((pl ? a.v_new : a.k_new) + (size_t(b) * H + h) * D) + x;
+        }
+        fetch_chunk(uint32_t(reinterpret_cast<uintptr_t>((lds_byte_ptr)(&pstage[0]))) + uint32_t(w * 64 * 16), src);
+    }
+
     // query rows of the first QSEG units, straight into LDS (columns past a
     // unit's last read row 0 of the call; they are never used)
     const uint32_t qcache_lds = uint32_t(reinterpret_cast<uintptr_t>((lds_byte_ptr)(&qcache[0])));
@@ -314,6 +336,8 @@ __global__ void __launch_bounds__(256) paged_stream_kernel(DecodeArgs a) {
     auto vswz = [](int t) __attribute__((always_inline)) { return NCH == 16 ? ((t & 7) << 1) : (((t >> 1) & 3) << 1); };
     const char* kplane = static_cast<const char*>(a.pv.lv.k_code);
     const char* vplane = static_cast<const char*>(a.pv.lv.v_code);
+    char* kplane_w = static_cast<char*>(a.pv.lv.k_code);
+    char* vplane_w = static_cast<char*>(a.pv.lv.v_code);
     uint32_t k_src[PER_T], v_src[PER_T];           // source byte offsets within a page slice
 #pragma unroll
     for (int k = 0; k < PER_T; ++k) {
@@ -450,6 +474,18 @@ __global__ void __launch_bounds__(256) paged_stream_kernel(DecodeArgs a) {
         __syncthreads();
         npend = 0;
     };
+    // the staged new-token rows into their pages (nothing in this launch reads
+    // them from memory: the stream patched them into its stages)
+    auto store_rows = [&]() __attribute__((always_inline)) {
+        const int q = tid / PCH, pl = (tid / NCH) & 1, x = tid % NCH;
+        if (q < npatch) {
+            const int pe = patch_s[q];
+            const int sl = pinfo[pe & 0xfff].x, r = (pe >> 21) & 63;
+            if (sl >= 0)
+                *reinterpret_cast<u32x4*>((pl ? vplane_w : kplane_w) + size_t(sl) * SLICE_BYTES + r * NCH * 16 + x * 16) =
+                    pstage[tid];
+        }
+    };
 
     // unit end: merge the four waves' states through stage st (waves 0-1
     // use its K slice, waves 2-3 its V slice), one column tile at a time
@@ -554,9 +590,42 @@ __global__ void __launch_bounds__(256) paged_stream_kernel(DecodeArgs a) {
         }
 
         const int meta = meta_ring[J];
+        if (append && (meta & kPatchBit)) {
+            // an entry's new token lies in this page: its row goes into the
+            // stage from the staged copy (or, past the staged ones, from
+            // memory, which drains the ring once)
+            const int s = unit_seg(sig), h = sig - s * H, p = (meta >> 9) & 0x7fff;
+            const int mask = seg_s[s][S_MASK];
+#pragma unroll 1
+            for (int b = 0; b < kMaxEnt; ++b) {
+                const int keys = ent_s[b][E_KEYS];
+                if (!((mask >> b) & 1) || keys <= 0 || ((keys - 1) >> kPageShift) != p) continue;
+                const int r = (keys - 1) & 63;
+                int q = -1;
+                for (int k = 0; k < npatch; ++k) {
+                    const int pe = patch_s[k];
+                    if ((pe & 0xfff) == i && ((pe >> 12) & 7) == b) q = k;
+                }
+                if (tid < PCH) {
+                    const int pl = tid / NCH, x = tid % NCH;
+                    u32x4 v;
+                    if (q >= 0) {
+                        v = pstage[q * PCH + tid];
+                    } else {
+                        v = reinterpret_cast<const u32x4*>((pl ? a.v_new : a.k_new) + (size_t(b) * H + h) * D)[x];
+                        const int sl = pinfo[i].x;
+                        if (sl >= 0)
+                            *reinterpret_cast<u32x4*>((pl ? vplane_w : kplane_w) + size_t(sl) * SLICE_BYTES +
+                                                      r * NCH * 16 + x * 16) = v;
+                    }
+                    ring[pl][J][r * NCH + (x ^ (pl ? vswz(r) : kswz(r)))] = v;
+                }
+            }
+            block_lds_barrier();
+        }
         const int lim = meta & 255;                 // rows any column of the unit may see
         if (lim > 16 * w) {                         // this wave has such rows in the page
-            const int tok0 = (meta >> 9) * kPage;   // first key of the page
+            const int tok0 = ((meta >> 9) & 0x7fff) * kPage;   // first key of the page
             const u32x4* kst = &ring[0][J][0];
             f32x4_t s[NCT];
 #pragma unroll
@@ -647,6 +716,7 @@ __global__ void __launch_bounds__(256) paged_stream_kernel(DecodeArgs a) {
         }
     }
     flush();
+    if (npatch > 0) store_rows();
 }
 
 // Combine of the page stream: one wave per task of the plan -- an (entry,
@@ -810,11 +880,13 @@ bool stream_share() {
 }
 
 // The matrix-core page stream covers BF16 pages with D in {64, 128}, up to
-// eight entries per call and 64 KV heads; everything else takes the chunked
-// split kernel.
+// eight entries per call, 64 KV heads and 32768 logical pages per row (the
+// page index shares a word with the page's flags), and at most 4096 blocks;
+// everything else takes the chunked split kernel.
 bool stream_path(const PoolView& pv, int B, int gq) {
     return pv.k_codec == CODEC_BF16 && pv.v_codec == CODEC_BF16 && (pv.D == 64 || pv.D == 128) && B <= 8 &&
-           pv.H <= plan::kMaxH && (gq == 1 || gq == 2 || gq == 4 || gq == 8);
+           pv.H <= plan::kMaxH && pv.L <= 32768 && (long long)B * pv.H * pv.L <= 4096LL * kStreamPages &&
+           (gq == 1 || gq == 2 || gq == 4 || gq == 8);
 }
 
 int max_chunks_for(int max_seq_len) {
@@ -855,7 +927,7 @@ WsLayout ws_layout(const PoolView& pv, int B, int gq, int max_seq_len, bool chun
 }
 
 DecodeArgs run_args(const PoolView& pv, const WsLayout& l, int B, int Hq, int max_seq_len, const void* q,
-                    float sm_scale, float* out, void* ws) {
+                    float sm_scale, float* out, void* ws, const void* k_new = nullptr, const void* v_new = nullptr) {
     DecodeArgs a{};
     char* base = static_cast<char*>(ws);
     a.pv = pv;
@@ -863,6 +935,8 @@ DecodeArgs run_args(const PoolView& pv, const WsLayout& l, int B, int Hq, int ma
     a.qcap = l.qcap;
     a.G = l.G;
     a.q = static_cast<const uint16_t*>(q);
+    a.k_new = static_cast<const uint16_t*>(k_new);
+    a.v_new = static_cast<const uint16_t*>(v_new);
     a.out = out;
     a.B = B;
     a.Hq = Hq;
@@ -966,11 +1040,16 @@ hipError_t launch_decode_plan(const PoolView& pv, int B, int Hq, const int32_t* 
                               l.stream && stream_share(), l.stream, l.G, l.qcap, planp, s);
 }
 
+bool decode_append_supported(const PoolView& pv, int B, int Hq) {
+    return pv.H > 0 && Hq % pv.H == 0 && stream_path(pv, B, Hq / pv.H);
+}
+
 hipError_t launch_decode_run(const PoolView& pv, int B, int Hq, int max_seq_len, const void* q, float sm_scale,
-                             float* out, void* ws, hipStream_t s) {
+                             float* out, void* ws, hipStream_t s, const void* k_new, const void* v_new) {
     const int gq = Hq / pv.H;
     const WsLayout l = ws_layout(pv, B, gq, max_seq_len, false);
-    const DecodeArgs a = run_args(pv, l, B, Hq, max_seq_len, q, sm_scale, out, ws);
+    if (k_new && !l.stream) return hipErrorNotSupported;
+    const DecodeArgs a = run_args(pv, l, B, Hq, max_seq_len, q, sm_scale, out, ws, k_new, v_new);
     switch (pv.D) {
         case 64: return launch_d<64>(a, gq, l.stream, s);
         case 128: return launch_d<128>(a, gq, l.stream, s);

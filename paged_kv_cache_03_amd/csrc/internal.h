@@ -73,8 +73,12 @@ bool decode_supported(const PoolView& pv, int Hq);
 size_t decode_workspace_bytes(const PoolView& pv, int B, int Hq, int max_seq_len);
 hipError_t launch_decode_plan(const PoolView& pv, int B, int Hq, const int32_t* table_rows, const int32_t* seq_lens,
                               int max_seq_len, void* ws, hipStream_t s);
+// k_new / v_new (bf16 [B][H][D], or nullptr): the step's rows, appended at
+// position keys - 1 of each entry by the run itself (page stream only).
+bool decode_append_supported(const PoolView& pv, int B, int Hq);
 hipError_t launch_decode_run(const PoolView& pv, int B, int Hq, int max_seq_len, const void* q, float sm_scale,
-                             float* out, void* ws, hipStream_t s);
+                             float* out, void* ws, hipStream_t s, const void* k_new = nullptr,
+                             const void* v_new = nullptr);
 hipError_t launch_decode(const PoolView& pv, int B, int Hq, const int32_t* table_rows, const int32_t* seq_lens,
                          int max_seq_len, const void* q, float sm_scale, float* out, void* ws, hipStream_t s);
 

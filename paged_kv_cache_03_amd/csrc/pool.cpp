@@ -564,6 +564,24 @@ kv_status paged_attn_decode_run(const kv_pool* pool, uint32_t layer, uint32_t B,
     return ok();
 }
 
+kv_status paged_attn_decode_append_run(const kv_pool* pool, uint32_t layer, uint32_t B, uint32_t Hq,
+                                       uint32_t max_seq_len, const void* d_k, const void* d_v, const void* d_q,
+                                       float sm_scale, float* d_out, void* d_ws, size_t ws_bytes, hipStream_t stream) {
+    bool skip = false;
+    kv_status st = check_decode(pool, layer, B, Hq, max_seq_len, d_ws, ws_bytes, &skip);
+    if (st != KV_OK) return st;
+    if (!(sm_scale > 0.f) || !std::isfinite(sm_scale)) return fail(KV_E_INVALID, "sm_scale must be finite and > 0");
+    if (skip) return ok();
+    if (!d_k || !d_v || !d_q || !d_out) return fail(KV_E_INVALID, "null device pointer");
+    PoolView pv = pool->view(layer);
+    if (!decode_append_supported(pv, int(B), int(Hq)))
+        return fail(KV_E_UNSUPPORTED, "append in the decode run needs the BF16 page stream; use kv_append");
+    hipError_t e = launch_decode_run(pv, int(B), int(Hq), int(max_seq_len), d_q, sm_scale, d_out, d_ws, stream, d_k,
+                                     d_v);
+    if (e != hipSuccess) return fail(KV_E_DEVICE, std::string("decode run launch: ") + hipGetErrorString(e));
+    return ok();
+}
+
 kv_status paged_attn_verify(const kv_pool* pool, uint32_t layer, uint32_t B, uint32_t Hq,
                             const int32_t* d_table_rows, const int32_t* d_q_pos0, const int32_t* d_cu_q,
                             uint32_t total_q, uint32_t max_q_len, uint32_t max_seq_len, const void* d_q,

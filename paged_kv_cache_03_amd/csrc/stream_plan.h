@@ -102,13 +102,22 @@ enum : int {
 
 constexpr size_t align64w(size_t w) { return (w + 63) / 64 * 64; }
 
-// per block: int2 (pages, first unit)
+// Decode with the step's rows: the page that holds an entry's new token
+// (position keys - 1) carries bit kPatchBit in its meta, and its block finds
+// the row in its patch list: (page within the block | entry << 12 | KV head
+// << 15 | row << 21), at most kMaxPatch per block (more: the block loads the
+// row when it reaches the page).
+constexpr int kPatchBit = 1 << 24;
+constexpr int kMaxPatch = 16;
+
+// per block: int4 (pages, first unit, staged patches, 0)
 constexpr size_t off_blk(int H) { return align64w(size_t(kOffExp) + size_t(kMaxEnt) * H); }
-constexpr size_t off_tasks(int H, int G) { return off_blk(H) + align64w(2 * size_t(G)); }
+constexpr size_t off_patch(int H, int G) { return off_blk(H) + align64w(4 * size_t(G)); }
+constexpr size_t off_tasks(int H, int G) { return off_patch(H, G) + align64w(size_t(kMaxPatch) * G); }
 // overflow pieces: every (block, unit) piece carries at most kMaxEnt entries
 constexpr size_t max_pieces(int H, int G) { return (size_t(G) + size_t(kMaxSeg) * H) * kMaxEnt; }
 constexpr size_t off_over(int H, int G) { return off_tasks(H, G) + size_t(kTaskWords) * kMaxEnt * H; }
-// per block: qcap int2 (slice g*H + h or -1, valid rows | 256 at a unit's end | page << 9)
+// per block: qcap int2 (slice g*H + h or -1, valid rows | 256 at a unit's end | page << 9 | kPatchBit)
 constexpr size_t off_pages(int H, int G) { return off_over(H, G) + align64w(max_pieces(H, G)); }
 constexpr size_t plan_words(int H, int G, int qcap) { return off_pages(H, G) + 2 * size_t(G) * size_t(qcap); }
 constexpr size_t plan_bytes(int H, int G, int qcap) { return (plan_words(H, G, qcap) * 4 + 255) / 256 * 256; }

@@ -28,6 +28,7 @@ namespace {
 using namespace plan;
 
 constexpr int kPlanSpan = 1024;   // stream positions per plan block
+constexpr int kMaxStreamBlocks = 4096;
 constexpr int kNT = 256;
 
 struct PlanArgs {
@@ -55,6 +56,7 @@ __global__ void __launch_bounds__(kNT) stream_plan_kernel(PlanArgs a) {
     __shared__ int seg[kMaxSeg][kSegWords];
     __shared__ int res_s[3];                       // segments, zero mask, total
     __shared__ int ex[kMaxEnt * kMaxH];            // pieces per (entry, KV head)
+    __shared__ int pcnt[kMaxStreamBlocks];         // new-token pages per block
 
     const int tid = int(threadIdx.x);
     const int H = a.H;
@@ -310,13 +312,36 @@ __global__ void __launch_bounds__(kNT) stream_plan_kernel(PlanArgs a) {
                 P[kOffExp + x] = e;
                 ex[x] = e;
             }
-            int2* blk = reinterpret_cast<int2*>(P + off_blk(H));
+            // decode: the block that streams the page with an entry's new token
+            // (position keys - 1) at head h lists (page, entry, head, row)
+            const int maxp = min(kMaxPatch, 1024 / a.D);
+            for (int i = tid; i < a.G; i += kNT) pcnt[i] = 0;
+            __syncthreads();
+            if (!a.chunk) {
+                int* plist = P + off_patch(H, a.G);
+                for (int x = tid; x < a.B * H; x += kNT) {
+                    const int b = x / H, h = x - b * H, keys = ent[b][E_KEYS];
+                    if (ent[b][E_NPAGES] == 0) continue;
+                    const int p = (keys - 1) >> kPageShift;
+                    for (int s = 0; s < nseg; ++s) {
+                        if (!((seg[s][S_MASK] >> b) & 1) || p < seg[s][S_P0] || p >= seg[s][S_P0] + seg[s][S_N])
+                            continue;
+                        const int u = seg[s][S_PRE] + h * seg[s][S_N] + (p - seg[s][S_P0]);
+                        const int i = u / Q, o = u - i * Q;
+                        const int k = atomicAdd(&pcnt[i], 1);
+                        if (k < maxp) plist[size_t(i) * kMaxPatch + k] = o | (b << 12) | (h << 15) | (((keys - 1) & 63) << 21);
+                        break;
+                    }
+                }
+                __syncthreads();
+            }
+            int4* blk = reinterpret_cast<int4*>(P + off_blk(H));
             for (int i = tid; i < a.G; i += kNT) {
                 const int u0 = i * Q;
                 const int npg = Q > 0 ? max(0, min(Q, total - u0)) : 0;
                 int s = 0, h = 0, pp = 0;
                 if (npg > 0) locate(u0, s, h, pp);
-                blk[i] = make_int2(npg, s * H + h);
+                blk[i] = make_int4(npg, s * H + h, min(pcnt[i], maxp), 0);
             }
         }
         __syncthreads();
@@ -394,7 +419,14 @@ __global__ void __launch_bounds__(kNT) stream_plan_kernel(PlanArgs a) {
                 g[k] = a.table[size_t(row) * a.L + p];
                 sl[k] = h;
                 const int lim = min(kPage, seg[s][S_MAXKEYS] - p * kPage);
-                meta[k] = lim | (pp == seg[s][S_N] - 1 ? 256 : 0) | (p << 9);
+                int patch = 0;                     // decode: an entry's new token lies in this page
+                if (!a.chunk) {
+                    const int mask = seg[s][S_MASK];
+                    for (int b = 0; b < kMaxEnt; ++b)
+                        if (((mask >> b) & 1) && ent[b][E_KEYS] > 0 && ((ent[b][E_KEYS] - 1) >> kPageShift) == p)
+                            patch = kPatchBit;
+                }
+                meta[k] = lim | (pp == seg[s][S_N] - 1 ? 256 : 0) | (p << 9) | patch;
                 const int i = u / Q;
                 dst[k] = i * a.qcap + (u - i * Q);
             }

@@ -128,6 +128,12 @@ class DevicePool:
         abi.paged_attn_decode_run(self.handle, layer, B, Hq, max_seq_len, ptr(q), sm_scale, ptr(out), ptr(ws),
                                   ws.numel(), self.stream)
 
+    def decode_append_run(self, layer: int, B: int, Hq: int, max_seq_len: int, k: torch.Tensor, v: torch.Tensor,
+                          q: torch.Tensor, sm_scale: float, out: torch.Tensor, ws: torch.Tensor) -> None:
+        """Append each entry's step row at seq_len - 1, then decode (BF16 page stream)."""
+        abi.paged_attn_decode_append_run(self.handle, layer, B, Hq, max_seq_len, ptr(k), ptr(v), ptr(q), sm_scale,
+                                         ptr(out), ptr(ws), ws.numel(), self.stream)
+
     def verify(self, layer: int, Hq: int, table_rows: torch.Tensor, q_pos0: torch.Tensor, cu_q: torch.Tensor,
                total_q: int, max_q_len: int, max_seq_len: int, q: torch.Tensor, sm_scale: float, out: torch.Tensor,
                ws: torch.Tensor) -> None:

@@ -8,7 +8,10 @@ head grouping (tiles hold 16/GQ entries, so trees are capped differently),
 compare with the fp64 oracle, and with the same histories in private pages
 (a different split: equal within rounding, not bitwise).  The plan / run
 split must give exactly the one-call result on every layer, and a run on a
-plan of another batch shape must mark its outputs (NaN).  Bar: max-abs 2e-3.
+plan of another batch shape must mark its outputs (NaN).  A run that appends
+the step's rows itself must leave the same planes and outputs, bit for bit, as
+kv_append followed by a run, also when a block holds more new-token pages
+than it stages.  Bar: max-abs 2e-3.
 """
 
 import numpy as np
@@ -116,3 +119,56 @@ def test_decode_run_on_a_plan_of_another_batch_marks_outputs():
     torch.cuda.synchronize()
     assert bool(torch.isnan(out).all())
     dp.close()
+
+
+def _append_run_case(wl, tag):
+    """Pool without the step rows + decode_append_run == kv_append + decode_run, bitwise (outputs and planes)."""
+    import torch
+    from paged_kv_cache_03_amd.device_pool import i32
+    from workloads.device_driver import _dev, plane_np
+    pool, st, _ = build_oracle(wl)
+    dp_a, _, step_a = build_device(wl, step_append=False)
+    dp_b, _, _ = build_device(wl)
+    dev = dp_a.device
+    msl = max(wl.seq_lens)
+    rows, lens = i32(wl.table_rows, dev), i32(wl.seq_lens, dev)
+    ws_a, ws_b = dp_a.workspace(wl.B, wl.Hq, msl), dp_b.workspace(wl.B, wl.Hq, msl)
+    dp_a.decode_plan(wl.Hq, rows, lens, msl, ws_a)
+    dp_b.decode_plan(wl.Hq, rows, lens, msl, ws_b)
+    for layer in range(wl.layers):
+        q = _dev(wl.q(layer), dev)
+        k, v = step_a[layer]
+        out_a = torch.full((wl.B, wl.Hq, wl.D), float("nan"), dtype=torch.float32, device=dev)
+        out_b = torch.full((wl.B, wl.Hq, wl.D), float("nan"), dtype=torch.float32, device=dev)
+        dp_a.decode_append_run(layer, wl.B, wl.Hq, msl, k, v, q, wl.sm_scale, out_a, ws_a)
+        dp_b.decode_run(layer, wl.B, wl.Hq, msl, q, wl.sm_scale, out_b, ws_b)
+        torch.cuda.synchronize()
+        ga, gb = out_a.cpu().numpy(), out_b.cpu().numpy()
+        assert np.array_equal(ga.view(np.uint32), gb.view(np.uint32)), (tag, layer)
+        for role in dp_a.planes[layer]:
+            assert np.array_equal(plane_np(dp_a, layer, role), plane_np(dp_b, layer, role)), (tag, layer, role)
+        ref = A.paged_decode(st, layer, wl.table_rows, wl.seq_lens, wl.q(layer), wl.sm_scale)
+        err = float(np.max(np.abs(ga - ref)))
+        say(f"  {tag} layer {layer}: max abs err {err:.3g}")
+        assert err <= TOL
+    dp_a.close()
+    dp_b.close()
+
+
+@pytest.mark.parametrize("gq,D", [(4, 128), (2, 64)])
+def test_decode_append_run_matches_append_then_run(gq, D):
+    # forks with shared prefixes; new tokens at page starts, mid-page and page ends
+    hist = [2000, 2000, 1500, 3000, 1000, 640]
+    fork = [None, (0, 1024), (0, 1000), (1, 1900), None, (4, 640)]
+    wl = workloads.small(130 + gq + D, "BF16", hist=hist, fork=fork, C=6, S=4096, Hq=2 * gq, H=2, D=D, layers=2)
+    say(f"append in the run gq={gq} D={D}")
+    _append_run_case(wl, f"gq={gq} D={D}")
+
+
+def test_decode_append_run_more_new_rows_than_staged():
+    # seven one-page entries and one long one: the first block's range holds
+    # nine new-token pages, more than the eight it stages (D = 128)
+    hist = [10, 63, 0, 40, 1, 62, 30, 66000]
+    wl = workloads.small(131, "BF16", hist=hist, C=8, S=66048, Hq=8, H=2, D=128)
+    say("append in the run, more new rows than staged")
+    _append_run_case(wl, "many new rows")

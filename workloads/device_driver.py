@@ -21,11 +21,13 @@ def _dev(x: np.ndarray, device):
 
 
 def build_device(wl, free_order=None, privatize=False, layers=None, zero=True, hist_layers_from=None,
-                 chunk_tokens=16384):
+                 chunk_tokens=16384, step_append=True):
     """Device pool holding the workload's history and step rows.
 
     hist_layers_from: if set, every layer's history rows are the rows generated for
     that layer (used only where the values do not matter, e.g. timing).
+    step_append: False leaves the step's rows out of the planes (they are still
+    mapped and returned), for an op that appends them itself.
     """
     import torch
     from paged_kv_cache_03_amd.device_pool import DevicePool, i32
@@ -77,7 +79,8 @@ def build_device(wl, free_order=None, privatize=False, layers=None, zero=True, h
         k, v = wl.step_kv_all(layer)
         kd, vd = _dev(k, dev), _dev(v, dev)
         step_inputs[layer] = (kd, vd)
-        dp.append(layer, rows_t, pos0_t, cu_t, int(wl.cu_q[-1]), kd, vd)
+        if step_append:
+            dp.append(layer, rows_t, pos0_t, cu_t, int(wl.cu_q[-1]), kd, vd)
     torch.cuda.synchronize()
     return dp, seqs, step_inputs
 
