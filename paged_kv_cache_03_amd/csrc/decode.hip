@@ -250,21 +250,39 @@ __global__ void __launch_bounds__(256) paged_stream_kernel(DecodeArgs a) {
     const int32_t* P = a.plan;
 
     // one round trip: the plan's header and tables, this block's page list
-    const bool plan_ok = ld_uniform(P, H_MAGIC) == kMagic && ld_uniform(P, H_B) == a.B &&
-                         ld_uniform(P, H_H) == H && ld_uniform(P, H_GQ) == GQ && ld_uniform(P, H_G) == G &&
-                         ld_uniform(P, H_QCAP) == a.qcap && ld_uniform(P, H_CHUNK) == int(CHUNK);
+    const int magic = ld_uniform(P, H_MAGIC), pb = ld_uniform(P, H_B), ph = ld_uniform(P, H_H);
+    const int pgq = ld_uniform(P, H_GQ), pg = ld_uniform(P, H_G), pq = ld_uniform(P, H_QCAP);
+    const int pchunk = ld_uniform(P, H_CHUNK);
+    const bool plan_ok = (magic == kMagic) & (pb == a.B) & (ph == H) & (pgq == GQ) & (pg == G) & (pq == a.qcap) &
+                         (pchunk == int(CHUNK));
     const int Q = ld_uniform(P, H_Q), nseg = ld_uniform(P, H_NSEG), zero = ld_uniform(P, H_ZERO);
     const int npg = ld_uniform(P, off_blk(H) + 4 * size_t(i_blk));
     int sig = ld_uniform(P, off_blk(H) + 4 * size_t(i_blk) + 1);   // unit being computed
     const bool append = !CHUNK && a.k_new != nullptr;
     const int npatch = append ? ld_uniform(P, off_blk(H) + 4 * size_t(i_blk) + 2) : 0;
-    if (tid < kMaxPatch) patch_s[tid] = P[off_patch(H, G) + size_t(i_blk) * kMaxPatch + tid];
-    if (tid < kMaxEnt * kEntWords) ent_s[tid / kEntWords][tid % kEntWords] = P[kOffEnt + tid];
-    if (tid < kMaxSeg * kSegWords) seg_s[tid / kSegWords][tid % kSegWords] = P[kOffSeg + tid];
-    for (int x = tid; x < kMaxEnt * H; x += NT) exp_s[x] = P[kOffExp + x];
     {
+        // every load first (clamped indices, all inside the plan), then the
+        // LDS writes: one memory round trip
+        static_assert(kMaxEnt * kEntWords <= NT && kMaxSeg * kSegWords <= NT && kMaxPatch <= NT, "tables");
+        static_assert(kMaxEnt * kMaxH <= 2 * NT && kStreamPages == 4 * NT, "tables");
         const int2* pl = reinterpret_cast<const int2*>(P + off_pages(H, G)) + size_t(i_blk) * a.qcap;
-        for (int x = tid; x < a.qcap; x += NT) pinfo[x] = pl[x];
+        const int ne = kMaxEnt * H;
+        const int v_ent = P[kOffEnt + min(tid, kMaxEnt * kEntWords - 1)];
+        const int v_seg = P[kOffSeg + min(tid, kMaxSeg * kSegWords - 1)];
+        const int v_patch = P[off_patch(H, G) + size_t(i_blk) * kMaxPatch + min(tid, kMaxPatch - 1)];
+        const int v_exp0 = P[kOffExp + min(tid, ne - 1)];
+        const int v_exp1 = P[kOffExp + min(tid + NT, ne - 1)];
+        int2 v_pg[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) v_pg[k] = pl[min(tid + k * NT, a.qcap - 1)];
+        if (tid < kMaxEnt * kEntWords) ent_s[tid / kEntWords][tid % kEntWords] = v_ent;
+        if (tid < kMaxSeg * kSegWords) seg_s[tid / kSegWords][tid % kSegWords] = v_seg;
+        if (tid < kMaxPatch) patch_s[tid] = v_patch;
+        if (tid < ne) exp_s[tid] = v_exp0;
+        if (tid + NT < ne) exp_s[tid + NT] = v_exp1;
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+            if (tid + k * NT < a.qcap) pinfo[tid + k * NT] = v_pg[k];
     }
     block_lds_barrier();
     if (!plan_ok) {                                // a plan of another batch shape: make it visible
@@ -736,18 +754,16 @@ __global__ void __launch_bounds__(256) stream_combine_kernel(DecodeArgs a) {
     const int t = int(blockIdx.x) * 4 + w;
     const int32_t* P = a.plan;
     const int32_t* rec = P + off_tasks(H, int(a.G)) + size_t(t) * kTaskWords;
-    const bool plan_ok = ld_uniform(P, H_MAGIC) == kMagic && ld_uniform(P, H_B) == a.B &&
-                         ld_uniform(P, H_H) == H && ld_uniform(P, H_GQ) == GQ;
-    const int ntask = ld_uniform(P, H_NTASK);
+    // header and task record together (no branch between the loads)
+    const int magic = ld_uniform(P, H_MAGIC), pb = ld_uniform(P, H_B), ph = ld_uniform(P, H_H);
+    const int pgq = ld_uniform(P, H_GQ), ntask = ld_uniform(P, H_NTASK);
     const int E = ld_uniform(rec, T_E), ncolb = ld_uniform(rec, T_NCOL), obase = ld_uniform(rec, T_OUT);
     const int poff = ld_uniform(rec, T_POFF);
-    if (!plan_ok || t >= ntask) return;            // (a plan of another shape: the stream marked the outputs)
+    const bool run = (magic == kMagic) & (pb == a.B) & (ph == H) & (pgq == GQ) & (t < ntask);
+    if (!run) return;                              // (a plan of another shape: the stream marked the outputs)
     const int32_t* over_list = P + off_over(H, int(a.G));
-    auto piece = [&](int k) __attribute__((always_inline)) {
-        return k < kTaskInline ? ld_uniform(rec, T_PIECE + k) : ld_uniform(over_list, poff + k - kTaskInline);
-    };
 
-    // uniform trip counts: the pieces are wave-uniform scalar values
+    // uniform trip counts: every lane takes part in the readlane lookups
 #pragma unroll 1
     for (int g0 = 0; g0 < ncolb * D; g0 += 64 * 8) {
         const int e0 = g0 + lane * 8;
@@ -757,43 +773,45 @@ __global__ void __launch_bounds__(256) stream_combine_kernel(DecodeArgs a) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) fa[e] = 0.f;
 #pragma unroll 1
-        for (int k0 = 0; k0 < E; k0 += CMAX) {
-            float2 ml[CMAX];
-            float4 av[CMAX][2];
+        for (int w0 = 0; w0 < E; w0 += 64) {
+            // lane k: partial index of piece w0 + k
+            const int k = w0 + lane;
+            int pid = 0;
+            if (k < E) pid = k < kTaskInline ? rec[T_PIECE + k] : over_list[poff + k - kTaskInline];
+            const int wn = min(64, E - w0);
+#pragma unroll 1
+            for (int k0 = 0; k0 < wn; k0 += CMAX) {
+                // every load of the round in flight together: pieces past the
+                // window repeat its last one and get weight 0
+                float2 ml[CMAX];
+                float4 av0[CMAX], av1[CMAX];
 #pragma unroll
-            for (int kk = 0; kk < CMAX; ++kk) {
-                if (k0 + kk < E) {
-                    const size_t it = size_t(piece(k0 + kk)) + c;
-                    if (act) {
-                        ml[kk] = *reinterpret_cast<const float2*>(a.part_ml + it * 2);
-                        av[kk][0] = *reinterpret_cast<const float4*>(a.part_acc + it * D + d0);
-                        av[kk][1] = *reinterpret_cast<const float4*>(a.part_acc + it * D + d0 + 4);
-                    }
+                for (int kk = 0; kk < CMAX; ++kk) {
+                    const int kc = min(k0 + kk, wn - 1);
+                    const size_t it = size_t(__builtin_amdgcn_readlane(pid, kc)) + c;
+                    ml[kk] = *reinterpret_cast<const float2*>(a.part_ml + it * 2);
+                    av0[kk] = *reinterpret_cast<const float4*>(a.part_acc + it * D + d0);
+                    av1[kk] = *reinterpret_cast<const float4*>(a.part_acc + it * D + d0 + 4);
                 }
-            }
-            if (act) {
                 float mx = fm;
 #pragma unroll
-                for (int kk = 0; kk < CMAX; ++kk)
-                    if (k0 + kk < E) mx = fmaxf(mx, ml[kk].x);
+                for (int kk = 0; kk < CMAX; ++kk) mx = fmaxf(mx, ml[kk].x);   // repeats change nothing
                 const float wp = fm == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(fm - mx);
                 fl *= wp;
 #pragma unroll
                 for (int e = 0; e < 8; ++e) fa[e] *= wp;
 #pragma unroll
                 for (int kk = 0; kk < CMAX; ++kk) {
-                    if (k0 + kk < E) {
-                        const float wgt = ml[kk].x == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ml[kk].x - mx);
-                        fl += ml[kk].y * wgt;
-                        fa[0] += av[kk][0].x * wgt;
-                        fa[1] += av[kk][0].y * wgt;
-                        fa[2] += av[kk][0].z * wgt;
-                        fa[3] += av[kk][0].w * wgt;
-                        fa[4] += av[kk][1].x * wgt;
-                        fa[5] += av[kk][1].y * wgt;
-                        fa[6] += av[kk][1].z * wgt;
-                        fa[7] += av[kk][1].w * wgt;
-                    }
+                    const float wgt = (k0 + kk >= wn || ml[kk].x == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(ml[kk].x - mx);
+                    fl += ml[kk].y * wgt;
+                    fa[0] += av0[kk].x * wgt;
+                    fa[1] += av0[kk].y * wgt;
+                    fa[2] += av0[kk].z * wgt;
+                    fa[3] += av0[kk].w * wgt;
+                    fa[4] += av1[kk].x * wgt;
+                    fa[5] += av1[kk].y * wgt;
+                    fa[6] += av1[kk].z * wgt;
+                    fa[7] += av1[kk].w * wgt;
                 }
                 fm = mx;
             }
