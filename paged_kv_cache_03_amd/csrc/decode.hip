@@ -199,15 +199,12 @@ struct Divider {
 // Before the ring starts, one round trip brings the plan's tables and the
 // block's page list into LDS; the query rows of the block's first units go
 // to LDS by direct-to-LDS loads ahead of the first pages.  When a unit ends,
-// the four waves' states are merged through the stage just consumed, and the
-// merged partial waits in registers until the stream ends (loads and stores
-// share the vector-memory counter that the ring waits on).  Then a column
-// whose (entry, KV head) has no other piece is normalized and written out;
-// the others are stored as partials in slot i + sigma, and the block that
-// brings the last piece of an (entry, KV head) (arrival counter in the
-// workspace) combines its pieces in unit and block order: one launch,
-// deterministic output.  Both the block index and sigma only grow along the
-// stream, so no two (block, unit) pieces share a slot.
+// the four waves' states are merged through the stage just consumed; a
+// column whose (entry, KV head) has no other piece is normalized and written
+// out, the others are stored as partials in slot i + sigma for the combine
+// launch, which folds each (entry, KV head)'s pieces in unit and block
+// order: deterministic output.  Both the block index and sigma only grow
+// along the stream, so no two (block, unit) pieces share a slot.
 template <int D, int GQ, int NCT, bool CHUNK>
 __global__ void __launch_bounds__(256) paged_stream_kernel(DecodeArgs a) {
     using namespace plan;
@@ -225,7 +222,6 @@ __global__ void __launch_bounds__(256) paged_stream_kernel(DecodeArgs a) {
     constexpr int NCOL = 16 * NCT;                 // query columns (partial slot width)
     constexpr int QCHUNKS = 1024;                  // query cache: 16 KiB of 16-byte chunks
     constexpr int QSEG = QCHUNKS / (NCOL * NCH);   // units with cached queries
-    constexpr int PMAX = NCT == 1 ? 3 : 2;         // merged partials held in registers
     static_assert((D == 64 || D == 128) && GQ >= 1 && GQ <= 16 && GQ <= NCOL, "shape");
     static_assert(PER_T == 2 || PER_T == 4, "page fetch shapes");
     static_assert(QSEG >= 1 && QSEG * NCOL * NCH == QCHUNKS && QCHUNKS % NT == 0, "query cache shape");
@@ -445,53 +441,6 @@ __global__ void __launch_bounds__(256) paged_stream_kernel(DecodeArgs a) {
         }
     };
 
-    // merged partials waiting for the end of the stream
-    f32x4_t pend_acc[PMAX][NCT][DPW];
-    float pend_m[PMAX][NCT], pend_l[PMAX][NCT];
-    int pend_sig[PMAX];
-    int npend = 0;
-
-    // Write out or store every pending partial: a column whose (entry, KV
-    // head) has no other piece is normalized and written; the others go to
-    // slot i + sigma for the combine launch.  Block-uniform; waits for all
-    // memory traffic of the block.
-    auto flush = [&]() __attribute__((always_inline)) {
-#pragma unroll
-        for (int k = 0; k < PMAX; ++k) {
-            if (k >= npend) break;
-            const int sg = pend_sig[k], s = unit_seg(sg), h = sg - s * H;
-            const int ncol = ncol_of(s);
-#pragma unroll
-            for (int ct = 0; ct < NCT; ++ct) {
-                const int c = 16 * ct + li;
-                if (c >= ncol) continue;
-                const Col cl = col_of(s, c);
-                if (exp_s[cl.b * H + h] == 1) {
-                    const float inv = pend_l[k][ct] > 0.f ? 1.f / pend_l[k][ct] : 0.f;
-                    float* o = a.out + (size_t(ent_s[cl.b][E_CU] + cl.tok) * a.Hq + size_t(h) * GQ + cl.j) * D +
-                               4 * lg;
-#pragma unroll
-                    for (int kk = 0; kk < DPW; ++kk) {
-                        const f32x4_t v = pend_acc[k][ct][kk] * inv;
-                        *reinterpret_cast<float4*>(o + 16 * (w * DPW + kk)) = make_float4(v[0], v[1], v[2], v[3]);
-                    }
-                } else {
-                    const size_t it = size_t(i_blk + sg) * NCOL + c;
-                    float* o = a.part_acc + it * D + 4 * lg;
-#pragma unroll
-                    for (int kk = 0; kk < DPW; ++kk)
-                        *reinterpret_cast<float4*>(o + 16 * (w * DPW + kk)) =
-                            make_float4(pend_acc[k][ct][kk][0], pend_acc[k][ct][kk][1], pend_acc[k][ct][kk][2],
-                                        pend_acc[k][ct][kk][3]);
-                    if (w == 0 && lg == 0)
-                        *reinterpret_cast<float2*>(a.part_ml + it * 2) = make_float2(pend_m[k][ct], pend_l[k][ct]);
-                }
-            }
-        }
-        wait_vmcnt<0>();
-        __syncthreads();
-        npend = 0;
-    };
     // the staged new-token rows into their pages (nothing in this launch reads
     // them from memory: the stream patched them into its stages)
     auto store_rows = [&]() __attribute__((always_inline)) {
@@ -552,21 +501,36 @@ __global__ void __launch_bounds__(256) paged_stream_kernel(DecodeArgs a) {
             mxs[ct] = mx;
             lts[ct] = lt;
         }
-        if (npend == PMAX) flush();                // rare: many units in one range
+        // write: a column whose (entry, KV head) has no other piece is
+        // normalized into out; the others go to slot i + sigma for the
+        // combine launch.  Nothing waits for these stores: the ring's waits
+        // (one in-order vector-memory counter) cover them with a few
+        // operations to spare, and the combine is a later launch.
+        const int s = unit_seg(sig), h = sig - s * H;
+        const int ncol = ncol_of(s);
 #pragma unroll
-        for (int k = 0; k < PMAX; ++k) {
-            if (k == npend) {
+        for (int ct = 0; ct < NCT; ++ct) {
+            const int c = 16 * ct + li;
+            if (c >= ncol) continue;
+            const Col cl = col_of(s, c);
+            if (exp_s[cl.b * H + h] == 1) {
+                const float inv = lts[ct] > 0.f ? 1.f / lts[ct] : 0.f;
+                float* o = a.out + (size_t(ent_s[cl.b][E_CU] + cl.tok) * a.Hq + size_t(h) * GQ + cl.j) * D + 4 * lg;
 #pragma unroll
-                for (int ct = 0; ct < NCT; ++ct) {
-#pragma unroll
-                    for (int kk = 0; kk < DPW; ++kk) pend_acc[k][ct][kk] = merged[ct][kk];
-                    pend_m[k][ct] = mxs[ct];
-                    pend_l[k][ct] = lts[ct];
+                for (int kk = 0; kk < DPW; ++kk) {
+                    const f32x4_t v = merged[ct][kk] * inv;
+                    *reinterpret_cast<float4*>(o + 16 * (w * DPW + kk)) = make_float4(v[0], v[1], v[2], v[3]);
                 }
-                pend_sig[k] = sig;
+            } else {
+                const size_t it = size_t(i_blk + sig) * NCOL + c;
+                float* o = a.part_acc + it * D + 4 * lg;
+#pragma unroll
+                for (int kk = 0; kk < DPW; ++kk)
+                    *reinterpret_cast<float4*>(o + 16 * (w * DPW + kk)) =
+                        make_float4(merged[ct][kk][0], merged[ct][kk][1], merged[ct][kk][2], merged[ct][kk][3]);
+                if (w == 0 && lg == 0) *reinterpret_cast<float2*>(a.part_ml + it * 2) = make_float2(mxs[ct], lts[ct]);
             }
         }
-        ++npend;
         reset();
     };
 
@@ -733,7 +697,6 @@ __global__ void __launch_bounds__(256) paged_stream_kernel(DecodeArgs a) {
             if (i0 + 7 < npg) step(std::integral_constant<int, 7>{}, i0 + 7);
         }
     }
-    flush();
     if (npatch > 0) store_rows();
 }
 
