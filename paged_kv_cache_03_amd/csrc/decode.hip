@@ -40,6 +40,7 @@ struct DecodeArgs {
     const int32_t* plan;   // the call's plan (stream_plan.h): entry table, page list
     int32_t qcap;          // page slots per block in the plan's page list
     int32_t G;             // blocks of the page stream
+    int32_t cgroups;       // combine: waves per task (groups of 512 outputs)
     const uint16_t* q;
     const uint16_t* k_new;  // decode with the step's rows: bf16 [B][H][D] K and V appended at keys - 1
     const uint16_t* v_new;  // (nullptr: the rows are already in the planes)
@@ -701,7 +702,8 @@ __global__ void __launch_bounds__(256) paged_stream_kernel(DecodeArgs a) {
 }
 
 // Combine of the page stream: one wave per task of the plan -- an (entry,
-// KV head) whose outputs have more than one piece.  The task lists its
+// KV head) whose outputs have more than one piece -- and group of 512 of its
+// outputs.  The task lists its
 // pieces (the (block, unit) partials of the entry's units in segment order,
 // each unit's slots in block order): a fixed order, so the result does not
 // depend on timing.  Every lane folds 8 consecutive outputs of one column
@@ -714,7 +716,8 @@ __global__ void __launch_bounds__(256) stream_combine_kernel(DecodeArgs a) {
     const int lane = int(threadIdx.x) & 63;
     const int w = __builtin_amdgcn_readfirstlane(int(threadIdx.x) >> 6);
     const int H = a.pv.H;
-    const int t = int(blockIdx.x) * 4 + w;
+    const int tg = int(blockIdx.x) * 4 + w;
+    const int t = tg / a.cgroups, grp = tg - t * a.cgroups;   // task, its group of 512 outputs
     const int32_t* P = a.plan;
     const int32_t* rec = P + off_tasks(H, int(a.G)) + size_t(t) * kTaskWords;
     // header and task record together (no branch between the loads)
@@ -722,13 +725,14 @@ __global__ void __launch_bounds__(256) stream_combine_kernel(DecodeArgs a) {
     const int pgq = ld_uniform(P, H_GQ), ntask = ld_uniform(P, H_NTASK);
     const int E = ld_uniform(rec, T_E), ncolb = ld_uniform(rec, T_NCOL), obase = ld_uniform(rec, T_OUT);
     const int poff = ld_uniform(rec, T_POFF);
-    const bool run = (magic == kMagic) & (pb == a.B) & (ph == H) & (pgq == GQ) & (t < ntask);
+    const bool run = (magic == kMagic) & (pb == a.B) & (ph == H) & (pgq == GQ) & (t < ntask) & (grp * 512 < ncolb * D);
     if (!run) return;                              // (a plan of another shape: the stream marked the outputs)
     const int32_t* over_list = P + off_over(H, int(a.G));
 
-    // uniform trip counts: every lane takes part in the readlane lookups
-#pragma unroll 1
-    for (int g0 = 0; g0 < ncolb * D; g0 += 64 * 8) {
+    // this wave's group of 512 outputs; uniform trip counts: every lane takes
+    // part in the readlane lookups
+    {
+        const int g0 = grp * 512;
         const int e0 = g0 + lane * 8;
         const bool act = e0 < ncolb * D;
         const int c = act ? e0 / D : 0, d0 = act ? e0 % D : 0;
@@ -756,6 +760,9 @@ __global__ void __launch_bounds__(256) stream_combine_kernel(DecodeArgs a) {
                     av0[kk] = *reinterpret_cast<const float4*>(a.part_acc + it * D + d0);
                     av1[kk] = *reinterpret_cast<const float4*>(a.part_acc + it * D + d0 + 4);
                 }
+                // keep every load of the round above the fold (the scheduler
+                // would otherwise sink each one to its use, one round trip each)
+                __builtin_amdgcn_sched_barrier(0);
                 float mx = fm;
 #pragma unroll
                 for (int kk = 0; kk < CMAX; ++kk) mx = fmaxf(mx, ml[kk].x);   // repeats change nothing
@@ -870,6 +877,9 @@ bool stream_path(const PoolView& pv, int B, int gq) {
            (gq == 1 || gq == 2 || gq == 4 || gq == 8);
 }
 
+// waves per combine task: groups of 512 outputs of up to ncol columns
+constexpr int combine_groups(int ncol, int D) { return (ncol * D + 511) / 512; }
+
 int max_chunks_for(int max_seq_len) {
     const int pages = (max_seq_len + kPage - 1) / kPage;
     return (pages + chunk_pages() - 1) / chunk_pages();
@@ -937,7 +947,9 @@ hipError_t launch_gq(const DecodeArgs& a, bool stream, hipStream_t s) {
             paged_stream_kernel<D, GQ, 1, false><<<dim3(unsigned(stream_grid(a.pv, a.B, a.max_ctx))), 256, 0, s>>>(a);
             const hipError_t e = hipGetLastError();
             if (e != hipSuccess) return e;
-            stream_combine_kernel<D, GQ, 16><<<dim3(unsigned((a.B * a.pv.H + 3) / 4)), 256, 0, s>>>(a);
+            DecodeArgs c = a;
+            c.cgroups = combine_groups(GQ, D);
+            stream_combine_kernel<D, GQ, 16><<<dim3(unsigned((a.B * a.pv.H * c.cgroups + 3) / 4)), 256, 0, s>>>(c);
             return hipGetLastError();
         }
     }
@@ -977,13 +989,15 @@ hipError_t launch_d(const DecodeArgs& a, int gq, bool stream, hipStream_t s) {
 template <int D>
 hipError_t launch_chunk_d(const DecodeArgs& a, int gq, int G, hipStream_t s) {
     const dim3 grid(static_cast<unsigned>(G));
-    const dim3 cgrid(static_cast<unsigned>((a.B * a.pv.H + 3) / 4));
+    DecodeArgs c = a;
+    c.cgroups = combine_groups(32, D);
+    const dim3 cgrid(static_cast<unsigned>((a.B * a.pv.H * c.cgroups + 3) / 4));
     switch (gq) {
 #define KVS_CHUNK_CASE(GQ)                                                  \
     case GQ:                                                                \
         paged_stream_kernel<D, GQ, 2, true><<<grid, 256, 0, s>>>(a);        \
         if (hipPeekAtLastError() == hipSuccess)                             \
-            stream_combine_kernel<D, GQ, 32><<<cgrid, 256, 0, s>>>(a);      \
+            stream_combine_kernel<D, GQ, 32><<<cgrid, 256, 0, s>>>(c);      \
         break;
         KVS_CHUNK_CASE(1)
         KVS_CHUNK_CASE(2)
