@@ -31,35 +31,10 @@
 #include "kv_read.h"
 #include "stream_common.h"
 #include "stream_plan.h"
+#include "decode_common.h"
 
 namespace kvs {
 namespace {
-
-struct DecodeArgs {
-    PoolView pv;
-    const int32_t* plan;   // the call's plan (stream_plan.h): entry table, page list
-    int32_t qcap;          // page slots per block in the plan's page list
-    int32_t G;             // blocks of the page stream
-    int32_t cgroups;       // combine: waves per task (groups of 512 outputs)
-    const uint16_t* q;
-    const uint16_t* k_new;  // decode with the step's rows: bf16 [B][H][D] K and V appended at keys - 1
-    const uint16_t* v_new;  // (nullptr: the rows are already in the planes)
-    float* out;
-    float* part_ml;     // [items][GQ][2]  (running max in log2 units, sum)
-    float* part_acc;    // [items][GQ][D]  (unnormalized)
-    float scale_log2;   // sm_scale * log2(e)
-    int32_t B;
-    int32_t Hq;
-    int32_t chunk_pages;
-    int32_t max_chunks;
-    int32_t max_ctx;    // host bound on seq_lens (<= max_context); larger values are clipped
-};
-
-// Entry table of the call's plan (row, keys, ...), read by every kernel of
-// the decode launch.
-__device__ __forceinline__ int plan_ent(const DecodeArgs& a, int b, int field) {
-    return a.plan[plan::kOffEnt + b * plan::kEntWords + field];
-}
 
 // One 64-lane wave per work item (entry b, KV head h, chunk c).  QK: lane t
 // owns token t of the page; PV: lane owns EPL = D/64 head_dim elements.
@@ -157,20 +132,6 @@ __global__ void __launch_bounds__(256) decode_split_kernel(DecodeArgs a) {
 }
 
 
-
-// floor(x / Q) for 0 <= x < 2^24 through the fp32 reciprocal, corrected to
-// the exact quotient (an integer division is a long instruction sequence).
-struct Divider {
-    int Q;
-    float rq;
-    __device__ __forceinline__ explicit Divider(int q) : Q(q), rq(1.0f / float(q)) {}
-    __device__ __forceinline__ int operator()(int x) const {
-        int d = int(float(x) * rq);
-        d -= (d * Q > x) ? 1 : 0;
-        d += ((d + 1) * Q <= x) ? 1 : 0;
-        return d;
-    }
-};
 
 // ---------------------------------------------------------------------------
 // Matrix-core page stream (BF16 pages, D in {64, 128}, 1..8 entries): runs a
@@ -701,100 +662,6 @@ __global__ void __launch_bounds__(256) paged_stream_kernel(DecodeArgs a) {
     if (npatch > 0) store_rows();
 }
 
-// Combine of the page stream: one wave per task of the plan -- an (entry,
-// KV head) whose outputs have more than one piece -- and group of 512 of its
-// outputs.  The task lists its
-// pieces (the (block, unit) partials of the entry's units in segment order,
-// each unit's slots in block order): a fixed order, so the result does not
-// depend on timing.  Every lane folds 8 consecutive outputs of one column
-// over all pieces, CMAX pieces per memory round; the task record is read with
-// scalar loads in the same round trip as the header.
-template <int D, int GQ, int NCOL>
-__global__ void __launch_bounds__(256) stream_combine_kernel(DecodeArgs a) {
-    using namespace plan;
-    constexpr int CMAX = 16;
-    const int lane = int(threadIdx.x) & 63;
-    const int w = __builtin_amdgcn_readfirstlane(int(threadIdx.x) >> 6);
-    const int H = a.pv.H;
-    const int tg = int(blockIdx.x) * 4 + w;
-    const int t = tg / a.cgroups, grp = tg - t * a.cgroups;   // task, its group of 512 outputs
-    const int32_t* P = a.plan;
-    const int32_t* rec = P + off_tasks(H, int(a.G)) + size_t(t) * kTaskWords;
-    // header and task record together (no branch between the loads)
-    const int magic = ld_uniform(P, H_MAGIC), pb = ld_uniform(P, H_B), ph = ld_uniform(P, H_H);
-    const int pgq = ld_uniform(P, H_GQ), ntask = ld_uniform(P, H_NTASK);
-    const int E = ld_uniform(rec, T_E), ncolb = ld_uniform(rec, T_NCOL), obase = ld_uniform(rec, T_OUT);
-    const int poff = ld_uniform(rec, T_POFF);
-    const bool run = (magic == kMagic) & (pb == a.B) & (ph == H) & (pgq == GQ) & (t < ntask) & (grp * 512 < ncolb * D);
-    if (!run) return;                              // (a plan of another shape: the stream marked the outputs)
-    const int32_t* over_list = P + off_over(H, int(a.G));
-
-    // this wave's group of 512 outputs; uniform trip counts: every lane takes
-    // part in the readlane lookups
-    {
-        const int g0 = grp * 512;
-        const int e0 = g0 + lane * 8;
-        const bool act = e0 < ncolb * D;
-        const int c = act ? e0 / D : 0, d0 = act ? e0 % D : 0;
-        float fm = -INFINITY, fl = 0.f, fa[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) fa[e] = 0.f;
-#pragma unroll 1
-        for (int w0 = 0; w0 < E; w0 += 64) {
-            // lane k: partial index of piece w0 + k
-            const int k = w0 + lane;
-            int pid = 0;
-            if (k < E) pid = k < kTaskInline ? rec[T_PIECE + k] : over_list[poff + k - kTaskInline];
-            const int wn = min(64, E - w0);
-#pragma unroll 1
-            for (int k0 = 0; k0 < wn; k0 += CMAX) {
-                // every load of the round in flight together: pieces past the
-                // window repeat its last one and get weight 0
-                float2 ml[CMAX];
-                float4 av0[CMAX], av1[CMAX];
-#pragma unroll
-                for (int kk = 0; kk < CMAX; ++kk) {
-                    const int kc = min(k0 + kk, wn - 1);
-                    const size_t it = size_t(__builtin_amdgcn_readlane(pid, kc)) + c;
-                    ml[kk] = *reinterpret_cast<const float2*>(a.part_ml + it * 2);
-                    av0[kk] = *reinterpret_cast<const float4*>(a.part_acc + it * D + d0);
-                    av1[kk] = *reinterpret_cast<const float4*>(a.part_acc + it * D + d0 + 4);
-                }
-                // keep every load of the round above the fold (the scheduler
-                // would otherwise sink each one to its use, one round trip each)
-                __builtin_amdgcn_sched_barrier(0);
-                float mx = fm;
-#pragma unroll
-                for (int kk = 0; kk < CMAX; ++kk) mx = fmaxf(mx, ml[kk].x);   // repeats change nothing
-                const float wp = fm == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(fm - mx);
-                fl *= wp;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) fa[e] *= wp;
-#pragma unroll
-                for (int kk = 0; kk < CMAX; ++kk) {
-                    const float wgt = (k0 + kk >= wn || ml[kk].x == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(ml[kk].x - mx);
-                    fl += ml[kk].y * wgt;
-                    fa[0] += av0[kk].x * wgt;
-                    fa[1] += av0[kk].y * wgt;
-                    fa[2] += av0[kk].z * wgt;
-                    fa[3] += av0[kk].w * wgt;
-                    fa[4] += av1[kk].x * wgt;
-                    fa[5] += av1[kk].y * wgt;
-                    fa[6] += av1[kk].z * wgt;
-                    fa[7] += av1[kk].w * wgt;
-                }
-                fm = mx;
-            }
-        }
-        if (act) {
-            const float inv = fl > 0.f ? 1.f / fl : 0.f;
-            float* o = a.out + obase + size_t(c / GQ) * a.Hq * D + size_t(c % GQ) * D + d0;
-            *reinterpret_cast<float4*>(o) = make_float4(fa[0] * inv, fa[1] * inv, fa[2] * inv, fa[3] * inv);
-            *reinterpret_cast<float4*>(o + 4) = make_float4(fa[4] * inv, fa[5] * inv, fa[6] * inv, fa[7] * inv);
-        }
-    }
-}
-
 // Combine the chunks of each (entry, query head) in chunk order.
 template <int D, int GQ>
 __global__ void __launch_bounds__(64) decode_combine_kernel(DecodeArgs a) {
@@ -877,9 +744,6 @@ bool stream_path(const PoolView& pv, int B, int gq) {
            (gq == 1 || gq == 2 || gq == 4 || gq == 8);
 }
 
-// waves per combine task: groups of 512 outputs of up to ncol columns
-constexpr int combine_groups(int ncol, int D) { return (ncol * D + 511) / 512; }
-
 int max_chunks_for(int max_seq_len) {
     const int pages = (max_seq_len + kPage - 1) / kPage;
     return (pages + chunk_pages() - 1) / chunk_pages();
@@ -898,7 +762,7 @@ size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
 WsLayout ws_layout(const PoolView& pv, int B, int gq, int max_seq_len, bool chunk) {
     WsLayout l{};
-    l.stream = chunk || stream_path(pv, B, gq);
+    l.stream = chunk || stream_path(pv, B, gq) || qstream_path(pv, B, gq);
     size_t slots;
     if (l.stream) {
         l.G = stream_grid(pv, B, max_seq_len);
@@ -942,6 +806,7 @@ DecodeArgs run_args(const PoolView& pv, const WsLayout& l, int B, int Hq, int ma
 
 template <int D, int GQ>
 hipError_t launch_gq(const DecodeArgs& a, bool stream, hipStream_t s) {
+    if (stream && a.pv.k_codec != CODEC_BF16) return launch_qstream(a, GQ, s);
     if constexpr (D == 64 || D == 128) {
         if (stream) {
             paged_stream_kernel<D, GQ, 1, false><<<dim3(unsigned(stream_grid(a.pv, a.B, a.max_ctx))), 256, 0, s>>>(a);

@@ -100,6 +100,21 @@ __device__ __forceinline__ void fetch_chunk(uint32_t lds_wave, const void* src) 
                  : "memory");
 }
 
+// One 16-byte load per lane at base + voff into LDS[M0 + 16*lane], ordered
+// with the page loads on the same counter (pages whose planes do not fit the
+// fixed K/V stage pattern of fetch_page2/4).
+__device__ __forceinline__ void fetch_lds16(uint32_t lds_wave, const void* base, uint32_t voff) {
+    uint32_t sv;
+    asm volatile("s_mov_b32 %[sv], m0\n\t"
+                 "s_mov_b32 m0, %[d]\n\t"
+                 "s_nop 0\n\t"
+                 "global_load_lds_dwordx4 %[o], %[b]\n\t"
+                 "s_mov_b32 m0, %[sv]"
+                 : [sv] "=&s"(sv)
+                 : [d] "s"(lds_wave), [o] "v"(voff), [b] "s"(base)
+                 : "memory");
+}
+
 // op over the four 16-lane rows (lanes l%16 + 16k); identical in every lane
 __device__ __forceinline__ float rows_max(float x) {
     const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);

@@ -21,13 +21,15 @@ def _dev(x: np.ndarray, device):
 
 
 def build_device(wl, free_order=None, privatize=False, layers=None, zero=True, hist_layers_from=None,
-                 chunk_tokens=16384, step_append=True):
+                 chunk_tokens=16384, step_append=True, fill=None):
     """Device pool holding the workload's history and step rows.
 
     hist_layers_from: if set, every layer's history rows are the rows generated for
     that layer (used only where the values do not matter, e.g. timing).
     step_append: False leaves the step's rows out of the planes (they are still
     mapped and returned), for an op that appends them itself.
+    fill: if set, every byte of every plane starts as this value (rows no
+    append writes then hold it: 0xFF makes NaN codes and scales).
     """
     import torch
     from paged_kv_cache_03_amd.device_pool import DevicePool, i32
@@ -36,6 +38,11 @@ def build_device(wl, free_order=None, privatize=False, layers=None, zero=True, h
     dp = DevicePool(wl.profile, wl.H, wl.D, wl.layers, wl.S, wl.C, wl.M,
                     free_order=wl.free_order if free_order is None else free_order, zero=zero)
     dev = dp.device
+    if fill is not None:
+        for planes in dp.planes:
+            for t in planes.values():
+                t.view(torch.uint8).fill_(fill)
+        torch.cuda.synchronize()
     seqs = {}
     for b in wl.order():
         row = wl.table_rows[b]
