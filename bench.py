@@ -36,7 +36,9 @@ HBM_PEAK_GBS = 8000.0
 METRIC = "paged decode KV GB/s (% of HBM peak) + decode steps/s at C=8, 32K ctx"
 PROFILES = os.path.join(ROOT, "profiles")
 # sources of the decode kernel; the traffic summary is valid for this exact text
-DECODE_SRC = [os.path.join(ROOT, "paged_kv_cache_03_amd", "csrc", f) for f in ("decode.hip", "stream_common.h", "stream_plan.h", "stream_plan.hip")]
+DECODE_SRC = [os.path.join(ROOT, "paged_kv_cache_03_amd", "csrc", f)
+              for f in ("decode.hip", "decode_common.h", "qstream.hip", "stream_common.h", "stream_plan.h",
+                        "stream_plan.hip")]
 
 
 def decode_source_sha256() -> str:
@@ -78,8 +80,14 @@ def kv_read_bytes(table, wl) -> tuple[int, int]:
 def decode_kernel_name(wl) -> str:
     """The kernel that carries paged_attn_decode for this workload (as rocprofv3 names it)."""
     gq = wl.Hq // wl.H
-    if wl.profile == "BF16" and wl.D in (64, 128) and gq in (1, 2, 4, 8) and wl.B <= 8:
-        return f"paged_stream_kernel<{wl.D}, {gq}, 1, false>"
+    if gq in (1, 2, 4, 8) and wl.B <= 8:
+        if wl.profile == "BF16" and wl.D in (64, 128):
+            return f"paged_stream_kernel<{wl.D}, {gq}, 1, false>"
+        # codec numbers of the page-stream instances: INT8-G64 1, FP8-row 2, NVFP4-G16 3
+        sides = {"INT8_G64": (1, 1), "FP8_E4M3FN_ROW256": (2, 2), "NVFP4_G16": (3, 3), "K8V4": (2, 3)}
+        if wl.profile in sides and (wl.D in (128, 256) or (wl.D == 64 and 3 not in sides[wl.profile])):
+            kc, vc = sides[wl.profile]
+            return f"paged_qstream_kernel<{wl.D}, {kc}, {vc}>"
     return "decode_split_kernel + decode_combine_kernel"
 
 

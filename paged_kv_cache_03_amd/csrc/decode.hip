@@ -707,10 +707,12 @@ int chunk_pages() {
     return cp;
 }
 
-// Blocks of the page-stream kernel: one per compute unit (its LDS ring takes
-// most of the 160 KiB), every one streaming the same share of pages; more
-// when a share would exceed the kStreamPages a block lists in LDS.
-int stream_grid(const PoolView& pv, int B, int max_seq_len) {
+// Blocks of the page-stream kernel: bpc per compute unit (the BF16 stream's
+// LDS ring takes most of the 160 KiB: one; the quantized stream runs two
+// half-size blocks where its registers allow), every one streaming the same
+// share of pages; more when a share would exceed the kStreamPages / bpc
+// pages a block lists in LDS.
+int stream_grid(const PoolView& pv, int B, int max_seq_len, int bpc = 1) {
     static const int cus = [] {
         int dev = 0, n = 0;
         if (hipGetDevice(&dev) != hipSuccess ||
@@ -720,8 +722,9 @@ int stream_grid(const PoolView& pv, int B, int max_seq_len) {
         const int v = e ? std::atoi(e) : 0;
         return (v >= 1 && v <= 4096) ? v : n;
     }();
-    const long long need = (stream_bound(pv, B, max_seq_len) + kStreamPages - 1) / kStreamPages;
-    return int(need > cus ? need : cus);
+    const int per_block = kStreamPages / bpc;
+    const long long need = (stream_bound(pv, B, max_seq_len) + per_block - 1) / per_block;
+    return int(need > cus * bpc ? need : cus * bpc);
 }
 
 // Shared pages are read once per call unless KVS_STREAM_SHARE=0 (a tuning
@@ -765,7 +768,7 @@ WsLayout ws_layout(const PoolView& pv, int B, int gq, int max_seq_len, bool chun
     l.stream = chunk || stream_path(pv, B, gq) || qstream_path(pv, B, gq);
     size_t slots;
     if (l.stream) {
-        l.G = stream_grid(pv, B, max_seq_len);
+        l.G = stream_grid(pv, B, max_seq_len, !chunk && pv.k_codec != CODEC_BF16 ? qstream_blocks_per_cu(pv) : 1);
         const long long bound = stream_bound(pv, B, max_seq_len);
         l.qcap = int(bound > 0 ? (bound + l.G - 1) / l.G : 1);
         slots = size_t(l.G) + size_t(plan::kMaxSeg) * pv.H;     // (block, unit) pieces

@@ -149,6 +149,7 @@ __global__ void __launch_bounds__(256) stream_combine_kernel(DecodeArgs a) {
 // head sizes and shapes it covers, and its launch (the stream kernel, then
 // the combine).
 bool qstream_path(const PoolView& pv, int B, int gq);
+int qstream_blocks_per_cu(const PoolView& pv);   // its grid: this many blocks per compute unit
 hipError_t launch_qstream(const DecodeArgs& a, int gq, hipStream_t s);
 
 }  // namespace kvs

@@ -55,9 +55,16 @@ struct QRow {
     static constexpr int scale = C == CODEC_INT8_G64 ? 4 * (D / 64) : (C == CODEC_FP8_ROW ? 4 : D / 16);
 };
 
+// Blocks per compute unit: two for D <= 128 (two waves per SIMD hide each
+// other's LDS and matrix-core latencies; each block gets half of the LDS and
+// at most 256 registers per lane), one for D = 256 (its registers do not fit
+// twice).
+template <int D>
+constexpr int qstream_bpc() { return D <= 128 ? 2 : 1; }
+
 // LDS ring of the quantized stream: stage = [K codes | V codes | K scales |
 // V scales], at least 16 KiB (the unit merge passes through one stage)
-template <int KC, int VC, int D>
+template <int KC, int VC, int D, int BPC>
 struct QRing {
     static constexpr int KCB = 64 * QRow<KC, D>::code;
     static constexpr int VCB = 64 * QRow<VC, D>::code;
@@ -70,8 +77,9 @@ struct QRing {
     static constexpr int KL = KCB / 4096, VL = VCB / 4096; // 16-byte loads per thread and page
     static constexpr int SCW = (KSB + VSB) / 64;           // scale chunks per wave and page
     static constexpr int LPP = KL + VL + 1;                // loads per wave and page
-    static constexpr int FIXED = 8192 + 16384 + 4096;      // page list, query cache, tables (upper bound)
-    static constexpr int NS_LDS = (163840 - FIXED) / STRIDE;
+    static constexpr int LDS = 163840 / BPC;                // the block's share of the compute unit's LDS
+    static constexpr int FIXED = (8192 + 16384) / BPC + 4096;   // page list, query cache, tables (upper bound)
+    static constexpr int NS_LDS = (LDS - FIXED) / STRIDE;
     static constexpr int NS = NS_LDS > 8 ? 8 : NS_LDS;     // ring stages
 };
 
@@ -120,9 +128,10 @@ __device__ __forceinline__ void ring_round(F& step, int i0, int npg) {
 }
 
 template <int D, int KC, int VC>
-__global__ void __launch_bounds__(256) paged_qstream_kernel(DecodeArgs a) {
+__global__ void __launch_bounds__(256, qstream_bpc<D>()) paged_qstream_kernel(DecodeArgs a) {
     using namespace plan;
-    using R = QRing<KC, VC, D>;
+    constexpr int BPC = qstream_bpc<D>();
+    using R = QRing<KC, VC, D, BPC>;
     constexpr int NT = 256;
     constexpr int NS = R::NS;
     constexpr int STRIDE = R::STRIDE;
@@ -132,7 +141,8 @@ __global__ void __launch_bounds__(256) paged_qstream_kernel(DecodeArgs a) {
     constexpr int NDT = D / 16;                    // PV tiles
     constexpr int NP = NDT / 4;                    // merge passes, four tiles each
     constexpr int NCOL = 16;
-    constexpr int QCHUNKS = 1024;                  // query cache: 16 KiB of 16-byte chunks
+    constexpr int QCHUNKS = 1024 / BPC;            // query cache: 16 KiB / BPC of 16-byte chunks
+    constexpr int PAGES = kStreamPages / BPC;      // most pages a block takes
     constexpr int QSEG = QCHUNKS / (NCOL * NCH);   // units with cached queries
     constexpr int KROW = QRow<KC, D>::code, VROW = QRow<VC, D>::code;
     constexpr int KSROW = QRow<KC, D>::scale, VSROW = QRow<VC, D>::scale;
@@ -148,14 +158,14 @@ __global__ void __launch_bounds__(256) paged_qstream_kernel(DecodeArgs a) {
     static_assert(QSEG >= 1 && QSEG * NCOL * NCH == QCHUNKS, "query cache shape");
 
     __shared__ u32x4 ring[NS * STRIDE / 16];
-    __shared__ int2 pinfo[kStreamPages];           // the block's pages: (slice g*H + h or -1, meta)
+    __shared__ int2 pinfo[PAGES];                  // the block's pages: (slice g*H + h or -1, meta)
     __shared__ u32x4 qcache[QCHUNKS];              // query rows of the first QSEG units: [unit][column][chunk]
     __shared__ float mlbuf[4][16][2];              // per-wave (m, l) of every column at a unit's end
     __shared__ int ent_s[kMaxEnt][kEntWords];
     __shared__ int seg_s[kMaxSeg][kSegWords];
     __shared__ int exp_s[kMaxEnt * kMaxH];         // pieces per (entry, KV head)
     static_assert(NS * STRIDE + sizeof(pinfo) + sizeof(qcache) + sizeof(mlbuf) + sizeof(ent_s) + sizeof(seg_s) +
-                          sizeof(exp_s) <= 163840, "LDS");
+                          sizeof(exp_s) <= R::LDS, "LDS");
 
     const int tid = int(threadIdx.x);
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -176,22 +186,22 @@ __global__ void __launch_bounds__(256) paged_qstream_kernel(DecodeArgs a) {
     int sig = ld_uniform(P, off_blk(H) + 4 * size_t(i_blk) + 1);   // unit being computed
     {
         static_assert(kMaxEnt * kEntWords <= NT && kMaxSeg * kSegWords <= NT, "tables");
-        static_assert(kMaxEnt * kMaxH <= 2 * NT && kStreamPages == 4 * NT, "tables");
+        static_assert(kMaxEnt * kMaxH <= 2 * NT && PAGES % NT == 0, "tables");
         const int2* pl = reinterpret_cast<const int2*>(P + off_pages(H, G)) + size_t(i_blk) * a.qcap;
         const int ne = kMaxEnt * H;
         const int v_ent = P[kOffEnt + min(tid, kMaxEnt * kEntWords - 1)];
         const int v_seg = P[kOffSeg + min(tid, kMaxSeg * kSegWords - 1)];
         const int v_exp0 = P[kOffExp + min(tid, ne - 1)];
         const int v_exp1 = P[kOffExp + min(tid + NT, ne - 1)];
-        int2 v_pg[4];
+        int2 v_pg[PAGES / NT];
 #pragma unroll
-        for (int k = 0; k < 4; ++k) v_pg[k] = pl[min(tid + k * NT, a.qcap - 1)];
+        for (int k = 0; k < PAGES / NT; ++k) v_pg[k] = pl[min(tid + k * NT, a.qcap - 1)];
         if (tid < kMaxEnt * kEntWords) ent_s[tid / kEntWords][tid % kEntWords] = v_ent;
         if (tid < kMaxSeg * kSegWords) seg_s[tid / kSegWords][tid % kSegWords] = v_seg;
         if (tid < ne) exp_s[tid] = v_exp0;
         if (tid + NT < ne) exp_s[tid + NT] = v_exp1;
 #pragma unroll
-        for (int k = 0; k < 4; ++k)
+        for (int k = 0; k < PAGES / NT; ++k)
             if (tid + k * NT < a.qcap) pinfo[tid + k * NT] = v_pg[k];
     }
     block_lds_barrier();
@@ -449,6 +459,76 @@ __global__ void __launch_bounds__(256) paged_qstream_kernel(DecodeArgs a) {
             const int tok0 = ((meta >> 9) & 0x7fff) * kPage;
             const lds_byte_ptr sb = (lds_byte_ptr)(&ring[0]) + J * STRIDE;
 
+            // every LDS read of the page first, unconditionally (all inside
+            // the stage): one wait instead of one per dependent use
+            constexpr int NKW = KC == CODEC_NVFP4_G16 ? 2 : 4;    // K words per group and lane
+            constexpr int NVW = VI8 ? NU : (VF8 ? NDT / 4 : NDT / 8);   // V words per key and lane
+            constexpr int NKS = KI8 ? NU : (KF8 ? 1 : NU);        // K scales per lane
+            constexpr int NVS = VI8 ? NU : 1;                     // V scales per key
+            uint32_t kx[NU][NKW];
+#pragma unroll
+            for (int g = 0; g < NU; ++g) {
+                if constexpr (NKW == 2) {
+                    const u32x2 v = *reinterpret_cast<lds_cu32x2>(sb + koff[g]);
+                    kx[g][0] = v[0];
+                    kx[g][1] = v[1];
+                } else {
+                    const u32x4 v = *reinterpret_cast<lds_cu32x4>(sb + koff[g]);
+                    kx[g][0] = v[0];
+                    kx[g][1] = v[1];
+                    kx[g][2] = v[2];
+                    kx[g][3] = v[3];
+                }
+            }
+            float ksc[4][NKS];                     // INT8 / FP8: scales of key tk(r); NVFP4: of the lane's 16 dims
+            if constexpr (KC == CODEC_NVFP4_G16) {
+#pragma unroll
+                for (int g = 0; g < NU; ++g)
+                    ksc[0][g] = e4m3_f32(uint32_t(reinterpret_cast<lds_cu8>(sb)[R::OFF_KS + tq * KSROW + 4 * g + lg]));
+            } else {
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+#pragma unroll
+                    for (int g = 0; g < NKS; ++g)
+                        ksc[r][g] = reinterpret_cast<lds_cf32>(sb + R::OFF_KS + tk[r] * KSROW)[g];
+            }
+            float vsc[4][NVS];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                if constexpr (VC == CODEC_NVFP4_G16) {
+                    vsc[r][0] = e4m3_f32(uint32_t(reinterpret_cast<lds_cu8>(sb)[R::OFF_VS + tk[r] * VSROW + (NDT * li) / 16]));
+                } else {
+#pragma unroll
+                    for (int g = 0; g < NVS; ++g) vsc[r][g] = reinterpret_cast<lds_cf32>(sb + R::OFF_VS + tk[r] * VSROW)[g];
+                }
+            }
+            uint32_t vx[4][NVW];                   // INT8: word g = dims 64g + 4li .. +3; else the lane's NDT dims
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int t = tk[r];
+                if constexpr (VI8) {
+#pragma unroll
+                    for (int g = 0; g < NU; ++g)
+                        vx[r][g] = *reinterpret_cast<lds_cu32>(sb + R::OFF_V + t * VROW +
+                                                               16 * ((4 * g + (li >> 2)) ^ vswz(t)) + 4 * (li & 3));
+                } else {
+                    const int off = R::OFF_V + t * VROW + 4 * NVW * li;
+                    if constexpr (NVW == 4) {
+                        const u32x4 v = *reinterpret_cast<lds_cu32x4>(sb + off);
+                        vx[r][0] = v[0];
+                        vx[r][1] = v[1];
+                        vx[r][2] = v[2];
+                        vx[r][3] = v[3];
+                    } else if constexpr (NVW == 2) {
+                        const u32x2 v = *reinterpret_cast<lds_cu32x2>(sb + off);
+                        vx[r][0] = v[0];
+                        vx[r][1] = v[1];
+                    } else {
+                        vx[r][0] = *reinterpret_cast<lds_cu32>(sb + off);
+                    }
+                }
+            }
+
             // QK^T: S^T[16 keys x 16 columns], per K scale group for INT8
             f32x4_t sacc[NGK];
 #pragma unroll
@@ -457,35 +537,32 @@ __global__ void __launch_bounds__(256) paged_qstream_kernel(DecodeArgs a) {
             for (int g = 0; g < NU; ++g) {
                 u32x4 op0, op1;
                 if constexpr (KC == CODEC_NVFP4_G16) {
-                    const u32x2 x = *reinterpret_cast<lds_cu32x2>(sb + koff[g]);
-                    const float sc = e4m3_f32(uint32_t(reinterpret_cast<lds_cu8>(sb)[R::OFF_KS + tq * KSROW + 4 * g + lg]));
+                    const float sc = ksc[0][g];
                     uint32_t o[8];
 #pragma unroll
                     for (int b = 0; b < 4; ++b) {
-                        const f32x2_t f0 = fp4_pair(x[0], b);
-                        const f32x2_t f1 = fp4_pair(x[1], b);
+                        const f32x2_t f0 = fp4_pair(kx[g][0], b);
+                        const f32x2_t f1 = fp4_pair(kx[g][1], b);
                         o[b] = pk_bf16(f0[0] * sc, f0[1] * sc);
                         o[4 + b] = pk_bf16(f1[0] * sc, f1[1] * sc);
                     }
                     op0 = u32x4{o[0], o[1], o[2], o[3]};
                     op1 = u32x4{o[4], o[5], o[6], o[7]};
+                } else if constexpr (KI8) {
+                    const uint32_t* x = kx[g];
+                    op0 = u32x4{pk_bf16(i8f<0>(x[0]), i8f<1>(x[0])), pk_bf16(i8f<2>(x[0]), i8f<3>(x[0])),
+                                pk_bf16(i8f<0>(x[1]), i8f<1>(x[1])), pk_bf16(i8f<2>(x[1]), i8f<3>(x[1]))};
+                    op1 = u32x4{pk_bf16(i8f<0>(x[2]), i8f<1>(x[2])), pk_bf16(i8f<2>(x[2]), i8f<3>(x[2])),
+                                pk_bf16(i8f<0>(x[3]), i8f<1>(x[3])), pk_bf16(i8f<2>(x[3]), i8f<3>(x[3]))};
                 } else {
-                    const u32x4 x = *reinterpret_cast<lds_cu32x4>(sb + koff[g]);
-                    if constexpr (KI8) {
-                        op0 = u32x4{pk_bf16(i8f<0>(x[0]), i8f<1>(x[0])), pk_bf16(i8f<2>(x[0]), i8f<3>(x[0])),
-                                    pk_bf16(i8f<0>(x[1]), i8f<1>(x[1])), pk_bf16(i8f<2>(x[1]), i8f<3>(x[1]))};
-                        op1 = u32x4{pk_bf16(i8f<0>(x[2]), i8f<1>(x[2])), pk_bf16(i8f<2>(x[2]), i8f<3>(x[2])),
-                                    pk_bf16(i8f<0>(x[3]), i8f<1>(x[3])), pk_bf16(i8f<2>(x[3]), i8f<3>(x[3]))};
-                    } else {
-                        uint32_t o[8];
+                    uint32_t o[8];
 #pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            o[2 * e] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x[e], 1.0f, false));
-                            o[2 * e + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x[e], 1.0f, true));
-                        }
-                        op0 = u32x4{o[0], o[1], o[2], o[3]};
-                        op1 = u32x4{o[4], o[5], o[6], o[7]};
+                    for (int e = 0; e < 4; ++e) {
+                        o[2 * e] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(kx[g][e], 1.0f, false));
+                        o[2 * e + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(kx[g][e], 1.0f, true));
                     }
+                    op0 = u32x4{o[0], o[1], o[2], o[3]};
+                    op1 = u32x4{o[4], o[5], o[6], o[7]};
                 }
                 const int ga = KI8 ? g : 0;
                 sacc[ga] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, op0), qb[2 * g],
@@ -494,22 +571,18 @@ __global__ void __launch_bounds__(256) paged_qstream_kernel(DecodeArgs a) {
                                                                    sacc[ga], 0, 0, 0);
             }
             float sj[4];
-            if constexpr (KI8) {
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const lds_cf32 ks = reinterpret_cast<lds_cf32>(sb + R::OFF_KS + tk[r] * KSROW);
+            for (int r = 0; r < 4; ++r) {
+                if constexpr (KI8) {
                     float x = 0.f;
 #pragma unroll
-                    for (int g = 0; g < NU; ++g) x += sacc[g][r] * ks[g];
+                    for (int g = 0; g < NU; ++g) x += sacc[g][r] * ksc[r][g];
                     sj[r] = x * a.scale_log2;
+                } else if constexpr (KF8) {
+                    sj[r] = sacc[0][r] * ksc[r][0] * a.scale_log2;
+                } else {
+                    sj[r] = sacc[0][r] * a.scale_log2;
                 }
-            } else if constexpr (KF8) {
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    sj[r] = sacc[0][r] * *reinterpret_cast<lds_cf32>(sb + R::OFF_KS + tk[r] * KSROW) * a.scale_log2;
-            } else {
-#pragma unroll
-                for (int r = 0; r < 4; ++r) sj[r] = sacc[0][r] * a.scale_log2;
             }
             if (tok0 + kPage > kmin) {             // a real column's limit falls inside the page
 #pragma unroll
@@ -536,10 +609,16 @@ __global__ void __launch_bounds__(256) paged_qstream_kernel(DecodeArgs a) {
 
             // keys past the last limit hold stale bytes (possibly NaN codes or
             // scales): their V codes and scales count as zero
-            const bool stale = lim < kPage;
-            bool live[4];
+            if (lim < kPage) {
 #pragma unroll
-            for (int r = 0; r < 4; ++r) live[r] = !stale || tk[r] < lim;
+                for (int r = 0; r < 4; ++r) {
+                    const bool live = tk[r] < lim;
+#pragma unroll
+                    for (int e = 0; e < NVW; ++e) vx[r][e] = live ? vx[r][e] : 0u;
+#pragma unroll
+                    for (int g = 0; g < NVS; ++g) vsc[r][g] = live ? vsc[r][g] : 0.f;
+                }
+            }
 
             // P^T operands [P_hi; P_lo], one per V scale group
             bf16x8_t bop[NPV];
@@ -547,17 +626,7 @@ __global__ void __launch_bounds__(256) paged_qstream_kernel(DecodeArgs a) {
             for (int g = 0; g < NPV; ++g) {
                 float pv[4];
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    if constexpr (VI8) {
-                        const float vs = reinterpret_cast<lds_cf32>(sb + R::OFF_VS + tk[r] * VSROW)[g];
-                        pv[r] = live[r] ? p[r] * vs : 0.f;
-                    } else if constexpr (VF8) {
-                        const float vs = *reinterpret_cast<lds_cf32>(sb + R::OFF_VS + tk[r] * VSROW);
-                        pv[r] = live[r] ? p[r] * vs : 0.f;
-                    } else {
-                        pv[r] = p[r];
-                    }
-                }
+                for (int r = 0; r < 4; ++r) pv[r] = (VC == CODEC_NVFP4_G16) ? p[r] : p[r] * vsc[r][g];
                 uint32_t h01, l01, h23, l23;
                 split_bf16(pv[0], pv[1], h01, l01);
                 split_bf16(pv[2], pv[3], h23, l23);
@@ -572,43 +641,13 @@ __global__ void __launch_bounds__(256) paged_qstream_kernel(DecodeArgs a) {
             if constexpr (VI8) {
 #pragma unroll
                 for (int g = 0; g < NU; ++g) {
-                    uint32_t x[4];
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const int t = tk[r];
-                        const int off = R::OFF_V + t * VROW + 16 * ((4 * g + (li >> 2)) ^ vswz(t)) + 4 * (li & 3);
-                        x[r] = *reinterpret_cast<lds_cu32>(sb + off);
-                        x[r] = live[r] ? x[r] : 0u;
-                    }
-                    pv_tile(4 * g + 0, pk_bf16(i8f<0>(x[0]), i8f<0>(x[1])), pk_bf16(i8f<0>(x[2]), i8f<0>(x[3])), g);
-                    pv_tile(4 * g + 1, pk_bf16(i8f<1>(x[0]), i8f<1>(x[1])), pk_bf16(i8f<1>(x[2]), i8f<1>(x[3])), g);
-                    pv_tile(4 * g + 2, pk_bf16(i8f<2>(x[0]), i8f<2>(x[1])), pk_bf16(i8f<2>(x[2]), i8f<2>(x[3])), g);
-                    pv_tile(4 * g + 3, pk_bf16(i8f<3>(x[0]), i8f<3>(x[1])), pk_bf16(i8f<3>(x[2]), i8f<3>(x[3])), g);
+                    const uint32_t x0 = vx[0][g], x1 = vx[1][g], x2 = vx[2][g], x3 = vx[3][g];
+                    pv_tile(4 * g + 0, pk_bf16(i8f<0>(x0), i8f<0>(x1)), pk_bf16(i8f<0>(x2), i8f<0>(x3)), g);
+                    pv_tile(4 * g + 1, pk_bf16(i8f<1>(x0), i8f<1>(x1)), pk_bf16(i8f<1>(x2), i8f<1>(x3)), g);
+                    pv_tile(4 * g + 2, pk_bf16(i8f<2>(x0), i8f<2>(x1)), pk_bf16(i8f<2>(x2), i8f<2>(x3)), g);
+                    pv_tile(4 * g + 3, pk_bf16(i8f<3>(x0), i8f<3>(x1)), pk_bf16(i8f<3>(x2), i8f<3>(x3)), g);
                 }
             } else {
-                // the lane's NDT dims (FP8: NDT bytes; NVFP4: NDT/2 bytes) of each key
-                constexpr int NW = VF8 ? NDT / 4 : NDT / 8;   // 32-bit words per key
-                uint32_t x[4][NW];
-                float sc[4];
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int off = R::OFF_V + tk[r] * VROW + 4 * NW * li;
-                    if constexpr (NW == 4) {
-                        const u32x4 v = *reinterpret_cast<lds_cu32x4>(sb + off);
-                        x[r][0] = v[0]; x[r][1] = v[1]; x[r][2] = v[2]; x[r][3] = v[3];
-                    } else if constexpr (NW == 2) {
-                        const u32x2 v = *reinterpret_cast<lds_cu32x2>(sb + off);
-                        x[r][0] = v[0]; x[r][1] = v[1];
-                    } else {
-                        x[r][0] = *reinterpret_cast<lds_cu32>(sb + off);
-                    }
-#pragma unroll
-                    for (int e = 0; e < NW; ++e) x[r][e] = live[r] ? x[r][e] : 0u;
-                    if constexpr (!VF8) {
-                        const float s = e4m3_f32(uint32_t(reinterpret_cast<lds_cu8>(sb)[R::OFF_VS + tk[r] * VSROW + (NDT * li) / 16]));
-                        sc[r] = live[r] ? s : 0.f;
-                    }
-                }
                 // two tiles per step: dims 2q and 2q + 1 of the lane's run
 #pragma unroll
                 for (int q = 0; q < NDT / 2; ++q) {
@@ -616,10 +655,10 @@ __global__ void __launch_bounds__(256) paged_qstream_kernel(DecodeArgs a) {
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
                         if constexpr (VF8) {
-                            f[r] = fp8_pair(x[r][q / 2], q & 1);
+                            f[r] = fp8_pair(vx[r][q / 2], q & 1);
                         } else {
-                            f[r] = fp4_pair(x[r][q / 4], q & 3);
-                            f[r] = f[r] * sc[r];
+                            f[r] = fp4_pair(vx[r][q / 4], q & 3);
+                            f[r] = f[r] * vsc[r][0];
                         }
                     }
                     pv_tile(2 * q, pk_bf16(f[0][0], f[1][0]), pk_bf16(f[2][0], f[3][0]), 0);
@@ -676,7 +715,7 @@ hipError_t launch_d(const DecodeArgs& a, int gq, hipStream_t s) {
 
 // Profiles (the four quantized ones), D in {64, 128, 256} (NVFP4 sides: 128
 // and 256), and the plan's limits: eight entries, 64 KV heads, 32768 logical
-// pages per row, 4096 blocks.
+// pages per row, 4096 blocks of at most kStreamPages / (blocks per CU) pages.
 bool qstream_path(const PoolView& pv, int B, int gq) {
     const int kc = pv.k_codec, vc = pv.v_codec;
     const bool combo = (kc == CODEC_INT8_G64 && vc == CODEC_INT8_G64) || (kc == CODEC_FP8_ROW && vc == CODEC_FP8_ROW) ||
@@ -685,8 +724,11 @@ bool qstream_path(const PoolView& pv, int B, int gq) {
     const bool fp4 = kc == CODEC_NVFP4_G16 || vc == CODEC_NVFP4_G16;
     const bool dims = pv.D == 128 || pv.D == 256 || (pv.D == 64 && !fp4);
     return combo && dims && B <= plan::kMaxEnt && pv.H <= plan::kMaxH && pv.L <= 32768 &&
-           (long long)B * pv.H * pv.L <= 4096LL * kStreamPages && (gq == 1 || gq == 2 || gq == 4 || gq == 8);
+           (long long)B * pv.H * pv.L <= 4096LL * (kStreamPages / qstream_blocks_per_cu(pv)) &&
+           (gq == 1 || gq == 2 || gq == 4 || gq == 8);
 }
+
+int qstream_blocks_per_cu(const PoolView& pv) { return pv.D <= 128 ? qstream_bpc<128>() : qstream_bpc<256>(); }
 
 hipError_t launch_qstream(const DecodeArgs& a, int gq, hipStream_t s) {
     switch (a.pv.D) {
