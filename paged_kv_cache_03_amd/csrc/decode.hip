@@ -134,6 +134,488 @@ __global__ void __launch_bounds__(256) decode_split_kernel(DecodeArgs a) {
 
 
 // ---------------------------------------------------------------------------
+// Register-fed page stream (BF16 pages, D in {64, 128}, 1..8 entries): runs a
+// page-stream plan (stream_plan.h) like the LDS-ring stream below, with two
+// blocks per compute unit and no LDS ring.  Wave w owns keys [16w, 16w+16)
+// of every page of the block's range and loads them itself, straight into
+// the registers the matrix cores read, PF pages ahead (non-temporal loads: a
+// page is read once per call); waves never wait for each other between unit
+// ends.  Per page and wave:
+//  * K operand (S^T = K . Q^T, v_mfma_f32_16x16x32_bf16): lane (li, lg) loads
+//    key 16w + li, dims 8(4c + lg) .. +7 for product c -- a 16-byte row load
+//    each;
+//  * V^T operand: lane (li, lg) loads the D/16 dims starting at (D/16) li of
+//    keys 16w + 4lg + r, r = 0..3 -- the four keys whose probabilities the
+//    lane holds -- and pairs the bf16 values of two keys per dim with one byte
+//    permute each: that is the transpose.  Row m of tile j holds head dim
+//    (D/16) m + j;
+//  * PV: V^T . [P_hi; P_lo] as one k=32 product per tile (the lane's keys
+//    listed twice, against P_hi then P_lo).
+// The unit merge passes through a dedicated 16 KiB LDS buffer, four tiles at
+// a time.  Columns, limits, lazy rescaling, sharing, the append of the step's
+// rows and the partial slots are those of the LDS-ring stream.
+template <int D, int GQ, int NCT, bool CHUNK>
+__global__ void __launch_bounds__(256, 2) paged_vstream_kernel(DecodeArgs a) {
+    using namespace plan;
+    constexpr int BPC = 2;                         // blocks per compute unit
+    constexpr int NCH = D / 8;                     // 16-byte chunks per bf16 row
+    constexpr int NT = 256;
+    constexpr int NC = D / 32;                     // QK products, k = 32 each
+    constexpr int NDT = D / 16;                    // PV tiles of 16 dims
+    constexpr int NP = NDT / 4;                    // merge passes, four tiles each
+    constexpr int VW = D / 32;                     // 32-bit V words per key and lane (D/16 bf16 dims)
+    constexpr int NCOL = 16 * NCT;                 // query columns (partial slot width)
+    constexpr int QCHUNKS = 1024 / BPC;            // query cache: 16-byte chunks
+    constexpr int QSEG = QCHUNKS / (NCOL * NCH);   // units with cached queries
+    constexpr int PAGES = kStreamPages / BPC;      // most pages a block takes
+    constexpr int PF = NCT == 1 ? 3 : 2;           // page buffers per wave (PF - 1 pages in flight)
+    constexpr size_t SLICE = size_t(64) * D * 2;   // bytes of one plane's page slice
+    static_assert((D == 64 || D == 128) && GQ >= 1 && GQ <= 16 && GQ <= NCOL, "shape");
+    static_assert(QSEG >= 1 && QSEG * NCOL * NCH == QCHUNKS && QCHUNKS % NT == 0, "query cache shape");
+    static_assert(PAGES % NT == 0, "page list");
+    typedef unsigned int vrow_t __attribute__((ext_vector_type(VW)));
+
+    __shared__ int2 pinfo[PAGES];                  // the block's pages: (slice g*H + h or -1, meta)
+    __shared__ u32x4 qcache[QCHUNKS];              // query rows of the first QSEG units: [unit][column][chunk]
+    __shared__ float mbuf[4 * 16 * 64];            // unit merge: four waves x four tiles x 4 registers
+    __shared__ float mlbuf[4][16][2];              // per-wave (m, l) of every column at a unit's end
+    __shared__ int ent_s[kMaxEnt][kEntWords];
+    __shared__ int seg_s[kMaxSeg][kSegWords];
+    __shared__ int exp_s[kMaxEnt * kMaxH];         // pieces per (entry, KV head)
+    __shared__ int patch_s[kMaxPatch];             // the block's new-token rows: page | entry | head | row
+    __shared__ u32x4 pstage[NT];                   // their K and V chunks
+
+    const int tid = int(threadIdx.x);
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63, li = lane & 15, lg = lane >> 4;
+    const int H = a.pv.H, i_blk = int(blockIdx.x), G = int(gridDim.x);
+    const int32_t* P = a.plan;
+
+    // one round trip: the plan's header and tables, this block's page list
+    const int magic = ld_uniform(P, H_MAGIC), pb = ld_uniform(P, H_B), ph = ld_uniform(P, H_H);
+    const int pgq = ld_uniform(P, H_GQ), pg = ld_uniform(P, H_G), pq = ld_uniform(P, H_QCAP);
+    const int pchunk = ld_uniform(P, H_CHUNK);
+    const bool plan_ok = (magic == kMagic) & (pb == a.B) & (ph == H) & (pgq == GQ) & (pg == G) & (pq == a.qcap) &
+                         (pchunk == int(CHUNK));
+    const int nseg = ld_uniform(P, H_NSEG), zero = ld_uniform(P, H_ZERO);
+    const int npg = ld_uniform(P, off_blk(H) + 4 * size_t(i_blk));
+    int sig = ld_uniform(P, off_blk(H) + 4 * size_t(i_blk) + 1);   // unit being computed
+    const bool append = !CHUNK && a.k_new != nullptr;
+    const int npatch = append ? ld_uniform(P, off_blk(H) + 4 * size_t(i_blk) + 2) : 0;
+    {
+        static_assert(kMaxEnt * kEntWords <= NT && kMaxSeg * kSegWords <= NT && kMaxPatch <= NT, "tables");
+        static_assert(kMaxEnt * kMaxH <= 2 * NT, "tables");
+        const int2* pl = reinterpret_cast<const int2*>(P + off_pages(H, G)) + size_t(i_blk) * a.qcap;
+        const int ne = kMaxEnt * H;
+        const int v_ent = P[kOffEnt + min(tid, kMaxEnt * kEntWords - 1)];
+        const int v_seg = P[kOffSeg + min(tid, kMaxSeg * kSegWords - 1)];
+        const int v_patch = P[off_patch(H, G) + size_t(i_blk) * kMaxPatch + min(tid, kMaxPatch - 1)];
+        const int v_exp0 = P[kOffExp + min(tid, ne - 1)];
+        const int v_exp1 = P[kOffExp + min(tid + NT, ne - 1)];
+        int2 v_pg[PAGES / NT];
+#pragma unroll
+        for (int k = 0; k < PAGES / NT; ++k) v_pg[k] = pl[min(tid + k * NT, a.qcap - 1)];
+        if (tid < kMaxEnt * kEntWords) ent_s[tid / kEntWords][tid % kEntWords] = v_ent;
+        if (tid < kMaxSeg * kSegWords) seg_s[tid / kSegWords][tid % kSegWords] = v_seg;
+        if (tid < kMaxPatch) patch_s[tid] = v_patch;
+        if (tid < ne) exp_s[tid] = v_exp0;
+        if (tid + NT < ne) exp_s[tid + NT] = v_exp1;
+#pragma unroll
+        for (int k = 0; k < PAGES / NT; ++k)
+            if (tid + k * NT < a.qcap) pinfo[tid + k * NT] = v_pg[k];
+    }
+    block_lds_barrier();
+    if (!plan_ok) {                                // a plan of another batch shape: make it visible
+        if (!CHUNK && i_blk == 0)
+            for (int x = tid; x < a.B * a.Hq * D; x += NT) a.out[x] = __builtin_nanf("");
+        return;
+    }
+    if (i_blk == 0) {                              // entries with nothing to attend produce zeros
+        for (int b = 0; b < a.B; ++b) {
+            if (!((zero >> b) & 1)) continue;
+            const size_t r0 = size_t(ent_s[b][E_CU]) * a.Hq * D;
+            for (int x = tid; x < ent_s[b][E_T] * a.Hq * D; x += NT) a.out[r0 + x] = 0.f;
+        }
+    }
+    if (npg <= 0) return;
+
+    // column c of a unit of segment s: entry, query token, head within the group
+    struct Col {
+        int b, tok, j;
+    };
+    auto col_of = [&](int s, int c) __attribute__((always_inline)) {
+        if constexpr (CHUNK) {
+            return Col{seg_s[s][S_OWNER], c / GQ, c % GQ};
+        } else {
+            int m = seg_s[s][S_MASK];
+            for (int k = c / GQ; k > 0; --k) m &= m - 1;
+            return Col{__builtin_ctz(unsigned(m | 0x100)), 0, c % GQ};
+        }
+    };
+    auto ncol_of = [&](int s) __attribute__((always_inline)) {
+        return __builtin_popcount(unsigned(seg_s[s][S_MASK])) * seg_s[s][S_W];
+    };
+    auto q_row = [&](const Col& cl, int h) __attribute__((always_inline)) {
+        return a.q + (size_t(ent_s[cl.b][E_CU] + cl.tok) * a.Hq + size_t(h) * GQ + cl.j) * D;
+    };
+    auto unit_seg = [&](int sg) __attribute__((always_inline)) { return sg / H; };
+
+    const char* kplane = static_cast<const char*>(a.pv.lv.k_code);
+    const char* vplane = static_cast<const char*>(a.pv.lv.v_code);
+    char* kplane_w = static_cast<char*>(a.pv.lv.k_code);
+    char* vplane_w = static_cast<char*>(a.pv.lv.v_code);
+
+    // page buffers: K operand chunks and V rows of this wave's keys.  Buffer
+    // loads whose range ends at the page's last visible row: rows past it
+    // (stale bytes, possibly NaN) come back as zeros.
+    u32x4 kbuf[PF][NC];
+    vrow_t vbuf[PF][4];
+    int pmeta[PF];                                 // meta of the page in each buffer
+    const int krow = (16 * w + li) * (2 * D) + 16 * lg;           // byte offset of chunk lg of key 16w + li
+    const int vrow = (16 * w + 4 * lg) * (2 * D) + (D / 8) * li;  // byte offset of the lane's dims of key 16w + 4lg
+    // Every step issues the same loads: past the block's last page they
+    // have an empty range (zeros, no memory access), so the compiler's
+    // vector-memory wait counts stay exact across the unrolled loop.
+    auto load_page = [&](int fi, u32x4 (&kb)[NC], vrow_t (&vb)[4], int& meta) __attribute__((always_inline)) {
+        const bool live = fi < npg;
+        const int2 pi = pinfo[live ? fi : 0];
+        const int sl = live ? __builtin_amdgcn_readfirstlane(pi.x) : -1;
+        meta = live ? __builtin_amdgcn_readfirstlane(pi.y) | (fi == npg - 1 ? 256 : 0) : 0;
+        const int bytes = sl < 0 ? 0 : (meta & 255) * (2 * D);   // an unmapped block reads nothing
+        const size_t off = size_t(sl < 0 ? 0 : sl) * SLICE;
+        const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(kplane) + off, 0, bytes, kBufferWord3);
+        const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(vplane) + off, 0, bytes, kBufferWord3);
+#pragma unroll
+        for (int c = 0; c < NC; ++c)
+            kb[c] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, krow + 64 * c, 0, kNonTemporal));
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            if constexpr (VW == 4)
+                vb[r] = __builtin_bit_cast(vrow_t, __builtin_amdgcn_raw_buffer_load_b128(rv, vrow + r * 2 * D, 0, kNonTemporal));
+            else
+                vb[r] = __builtin_bit_cast(vrow_t, __builtin_amdgcn_raw_buffer_load_b64(rv, vrow + r * 2 * D, 0, kNonTemporal));
+        }
+    };
+
+    // the step's new-token rows (staged chunk x of plane pl of row q at
+    // pstage[q * PCH + pl * NCH + x]) and the query rows of the first QSEG
+    // units (columns past a unit's last read row 0 of the call; never used):
+    // loads first, then the first pages, then the LDS writes
+    constexpr int PCH = 2 * NCH;                   // chunks of one staged row pair
+    u32x4 prow = u32x4{0u, 0u, 0u, 0u};
+    if (npatch > 0) {
+        const int q = tid / PCH, pl = (tid / NCH) & 1, x = tid % NCH;
+        if (q < npatch) {
+            const int pe = patch_s[q];
+            const int b = (pe >> 12) & 7, h = (pe >> 15) & 63;
+            prow = reinterpret_cast<const u32x4*>((pl ? a.v_new : a.k_new) + (size_t(b) * H + h) * D)[x];
+        }
+    }
+    u32x4 qv[QCHUNKS / NT];
+#pragma unroll
+    for (int k = 0; k < QCHUNKS / NT; ++k) {
+        const int x = k * NT + tid;
+        const int u = x / (NCOL * NCH), c = (x / NCH) % NCOL, ch = x % NCH;
+        const int sg = sig + u, s = unit_seg(sg);
+        const u32x4* src = reinterpret_cast<const u32x4*>(a.q);
+        if (s < nseg && c < ncol_of(s)) src = reinterpret_cast<const u32x4*>(q_row(col_of(s, c), sg - s * H)) + ch;
+        qv[k] = *src;
+    }
+#pragma unroll
+    for (int k = 0; k < PF - 1; ++k) load_page(k, kbuf[k], vbuf[k], pmeta[k]);
+    pstage[tid] = prow;
+#pragma unroll
+    for (int k = 0; k < QCHUNKS / NT; ++k) qcache[k * NT + tid] = qv[k];
+    block_lds_barrier();
+
+    typedef const u32x4 __attribute__((address_space(1)))* glb_q_cptr;
+    bf16x8_t qb[NCT][NC];                          // Q^T B operand: column 16ct + li, chunk 4c + lg
+    int klim[NCT];                                 // keys this lane's column sees (0: padding column)
+    int kmin = 0;                                  // smallest limit of a real column of the unit
+    auto start_unit = [&](int k_unit, int sg) __attribute__((always_inline)) {
+        const int s = unit_seg(sg), h = sg - s * H;
+        const int ncol = ncol_of(s);
+        kmin = seg_s[s][S_KMIN];
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) {
+            const int c = 16 * ct + li;
+            const Col cl = col_of(s, c < ncol ? c : 0);
+            klim[ct] = c < ncol ? min(ent_s[cl.b][E_N0] + cl.tok + 1, ent_s[cl.b][E_KEYS]) : 0;
+        }
+        if (k_unit < QSEG) {
+#pragma unroll
+            for (int ct = 0; ct < NCT; ++ct) {
+                const int c = 16 * ct + li;
+#pragma unroll
+                for (int k = 0; k < NC; ++k) {
+                    const u32x4 v = qcache[(k_unit * NCOL + c) * NCH + 4 * k + lg];
+                    qb[ct][k] = __builtin_bit_cast(bf16x8_t, c < ncol ? v : u32x4{0u, 0u, 0u, 0u});
+                }
+            }
+        } else {
+#pragma unroll
+            for (int ct = 0; ct < NCT; ++ct) {
+                const int c = 16 * ct + li;
+                const glb_q_cptr qg = (glb_q_cptr)(q_row(col_of(s, c < ncol ? c : 0), h));
+#pragma unroll
+                for (int k = 0; k < NC; ++k) {
+                    const u32x4 v = qg[4 * k + lg];
+                    qb[ct][k] = __builtin_bit_cast(bf16x8_t, c < ncol ? v : u32x4{0u, 0u, 0u, 0u});
+                }
+            }
+        }
+    };
+
+    f32x4_t acc[NCT][NDT];
+    float m_ref[NCT], l_part[NCT];
+    auto reset = [&]() __attribute__((always_inline)) {
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) {
+            m_ref[ct] = -INFINITY;
+            l_part[ct] = 0.f;
+#pragma unroll
+            for (int dt = 0; dt < NDT; ++dt) acc[ct][dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        }
+    };
+
+    // the staged new-token rows into their pages (nothing in this launch reads
+    // them from memory: the waves patched them into their registers)
+    auto store_rows = [&]() __attribute__((always_inline)) {
+        const int q = tid / PCH, pl = (tid / NCH) & 1, x = tid % NCH;
+        if (q < npatch) {
+            const int pe = patch_s[q];
+            const int sl = pinfo[pe & 0xfff].x, r = (pe >> 21) & 63;
+            if (sl >= 0)
+                *reinterpret_cast<u32x4*>((pl ? vplane_w : kplane_w) + size_t(sl) * SLICE + r * NCH * 16 + x * 16) =
+                    pstage[tid];
+        }
+    };
+
+    // unit end: merge the four waves' states through mbuf, four tiles per
+    // pass; wave w folds accumulator register w, so each lane ends with four
+    // consecutive head dims of row 4lg + w of each pass
+    auto finish_unit = [&]() __attribute__((always_inline)) {
+        f32x4_t merged[NCT][NP];
+        float mxs[NCT], lts[NCT];
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) {
+            const float lw = rows_sum(l_part[ct]);
+            float cw[4], lt = 0.f, mx = -INFINITY;
+#pragma unroll
+            for (int p = 0; p < NP; ++p) {
+                block_lds_barrier();               // every wave read the previous pass
+                float* mine = mbuf + w * 1024;
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) mine[(jj * 4 + r) * 64 + lane] = acc[ct][4 * p + jj][r];
+                if (p == 0 && lg == 0) {
+                    mlbuf[w][li][0] = m_ref[ct];
+                    mlbuf[w][li][1] = lw;
+                }
+                block_lds_barrier();
+                if (p == 0) {
+                    float mw[4];
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) {
+                        mw[v] = mlbuf[v][li][0];
+                        mx = fmaxf(mx, mw[v]);
+                    }
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) {
+                        cw[v] = mw[v] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mw[v] - mx);
+                        lt += mlbuf[v][li][1] * cw[v];
+                    }
+                }
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) {
+                    float x = 0.f;
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) x += mbuf[v * 1024 + (jj * 4 + w) * 64 + lane] * cw[v];
+                    merged[ct][p][jj] = x;
+                }
+            }
+            mxs[ct] = mx;
+            lts[ct] = lt;
+        }
+        // write: a column whose (entry, KV head) has no other piece is
+        // normalized into out; the others go to slot i + sigma for the
+        // combine launch (stores are not waited for: the combine is a later
+        // launch)
+        const int s = unit_seg(sig), h = sig - s * H;
+        const int ncol = ncol_of(s);
+        const int m = 4 * lg + w;
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) {
+            const int c = 16 * ct + li;
+            if (c >= ncol) continue;
+            const Col cl = col_of(s, c);
+            if (exp_s[cl.b * H + h] == 1) {
+                const float inv = lts[ct] > 0.f ? 1.f / lts[ct] : 0.f;
+                float* o = a.out + (size_t(ent_s[cl.b][E_CU] + cl.tok) * a.Hq + size_t(h) * GQ + cl.j) * D;
+#pragma unroll
+                for (int p = 0; p < NP; ++p) {
+                    const f32x4_t v = merged[ct][p] * inv;
+                    *reinterpret_cast<float4*>(o + NDT * m + 4 * p) = make_float4(v[0], v[1], v[2], v[3]);
+                }
+            } else {
+                const size_t it = size_t(i_blk + sig) * NCOL + c;
+                float* o = a.part_acc + it * D;
+#pragma unroll
+                for (int p = 0; p < NP; ++p)
+                    *reinterpret_cast<float4*>(o + NDT * m + 4 * p) =
+                        make_float4(merged[ct][p][0], merged[ct][p][1], merged[ct][p][2], merged[ct][p][3]);
+                if (w == 0 && lg == 0) *reinterpret_cast<float2*>(a.part_ml + it * 2) = make_float2(mxs[ct], lts[ct]);
+            }
+        }
+        reset();
+    };
+
+    reset();
+    int unit_k = 0;
+    start_unit(unit_k, sig);
+    const int tb = 16 * w + 4 * lg;                 // key of accumulator register r: tb + r
+
+    // one page of this wave's keys: K operand chunks kb, V rows vb
+    auto compute = [&](const u32x4 (&kb)[NC], const vrow_t (&vb)[4], int meta) __attribute__((always_inline)) {
+        const int lim = meta & 255;                 // rows any column of the unit may see
+        if (lim <= 16 * w) return;                  // none of them among this wave's keys
+        const int tok0 = ((meta >> 9) & 0x7fff) * kPage;   // first key of the page
+        f32x4_t s[NCT];
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) s[ct] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+            const bf16x8_t kk = __builtin_bit_cast(bf16x8_t, kb[c]);
+#pragma unroll
+            for (int ct = 0; ct < NCT; ++ct) s[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kk, qb[ct][c], s[ct], 0, 0, 0);
+        }
+        const bool masked = tok0 + kPage > kmin;   // a real column's limit falls inside the page
+        bf16x8_t bop[NCT];
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) {
+            float sj[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) sj[r] = s[ct][r] * a.scale_log2;
+            if (masked) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    if (tok0 + tb + r >= klim[ct]) sj[r] = -INFINITY;
+            }
+            const float pm = rows_max(fmaxf(fmaxf(sj[0], sj[1]), fmaxf(sj[2], sj[3])));
+            if (__builtin_amdgcn_ballot_w64(pm > m_ref[ct] + kRescaleLog2)) {
+                const float mn = pm > m_ref[ct] + kRescaleLog2 ? pm : m_ref[ct];
+                const float alpha = m_ref[ct] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_ref[ct] - mn);
+                l_part[ct] *= alpha;
+#pragma unroll
+                for (int dt = 0; dt < NDT; ++dt) acc[ct][dt] *= alpha;
+                m_ref[ct] = mn;
+            }
+            float p[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                p[r] = __builtin_amdgcn_exp2f(sj[r] - m_ref[ct]);
+                // a column with no visible key in this wave yet has no reference
+                p[r] = m_ref[ct] == -INFINITY ? 0.f : p[r];
+            }
+            l_part[ct] += (p[0] + p[1]) + (p[2] + p[3]);
+            uint32_t h01, l01, h23, l23;
+            split_bf16(p[0], p[1], h01, l01);
+            split_bf16(p[2], p[3], h23, l23);
+            bop[ct] = __builtin_bit_cast(bf16x8_t, u32x4{h01, h23, l01, l23});
+        }
+        // V^T tiles: dims 2e and 2e + 1 of the lane's run from word e of the
+        // four keys, two keys per 32-bit pair
+#pragma unroll
+        for (int e = 0; e < VW; ++e) {
+            const uint32_t lo01 = __builtin_amdgcn_perm(vb[1][e], vb[0][e], 0x05040100u);
+            const uint32_t lo23 = __builtin_amdgcn_perm(vb[3][e], vb[2][e], 0x05040100u);
+            const uint32_t hi01 = __builtin_amdgcn_perm(vb[1][e], vb[0][e], 0x07060302u);
+            const uint32_t hi23 = __builtin_amdgcn_perm(vb[3][e], vb[2][e], 0x07060302u);
+            const bf16x8_t alo = __builtin_bit_cast(bf16x8_t, u32x4{lo01, lo23, lo01, lo23});
+            const bf16x8_t ahi = __builtin_bit_cast(bf16x8_t, u32x4{hi01, hi23, hi01, hi23});
+#pragma unroll
+            for (int ct = 0; ct < NCT; ++ct) {
+                acc[ct][2 * e] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(alo, bop[ct], acc[ct][2 * e], 0, 0, 0);
+                acc[ct][2 * e + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi, bop[ct], acc[ct][2 * e + 1], 0, 0, 0);
+            }
+        }
+    };
+
+    typedef const u32x4 __attribute__((address_space(3)))* lds_u32x4_cptr;
+    typedef const u32x4 __attribute__((address_space(1)))* glb_u32x4_cptr;
+    typedef const vrow_t __attribute__((address_space(3)))* lds_vrow_cptr;
+    typedef const vrow_t __attribute__((address_space(1)))* glb_vrow_cptr;
+    const lds_u32x4_cptr pst = (lds_u32x4_cptr)(&pstage[0]);
+
+    // page i from buffer set J (compile time, so the buffers stay registers)
+    auto step = [&](auto jc, int i) __attribute__((always_inline)) {
+        constexpr int J = decltype(jc)::value;
+        constexpr int FB = (J + PF - 1) % PF;
+        const int meta = pmeta[J];
+        load_page(i + PF - 1, kbuf[FB], vbuf[FB], pmeta[FB]);
+        if (append && (meta & kPatchBit)) {
+            // an entry's new token lies in this page: its row replaces the
+            // loaded one in the wave that owns the key (from the staged copy;
+            // past the staged ones from memory, and then that wave also
+            // writes it into the page)
+            const int s = unit_seg(sig), h = sig - s * H, pg_idx = (meta >> 9) & 0x7fff;
+            const int mask = seg_s[s][S_MASK];
+#pragma unroll 1
+            for (int b = 0; b < kMaxEnt; ++b) {
+                const int keys = ent_s[b][E_KEYS];
+                if (!((mask >> b) & 1) || keys <= 0 || ((keys - 1) >> kPageShift) != pg_idx) continue;
+                const int r = (keys - 1) & 63;
+                if ((r >> 4) != w) continue;
+                int q = -1;
+                for (int k = 0; k < npatch; ++k) {
+                    const int pe = patch_s[k];
+                    if ((pe & 0xfff) == i && ((pe >> 12) & 7) == b) q = k;
+                }
+                const int vx = (D / 8) * li;       // byte offset of the lane's dims within the row
+                u32x4 kr[NC];
+                vrow_t vr;
+                if (q >= 0) {
+#pragma unroll
+                    for (int c = 0; c < NC; ++c) kr[c] = pst[q * PCH + 4 * c + lg];
+                    vr = *(lds_vrow_cptr)((const char __attribute__((address_space(3)))*)(pst + q * PCH + NCH) + vx);
+                } else {
+                    const glb_u32x4_cptr kn = (glb_u32x4_cptr)(a.k_new + (size_t(b) * H + h) * D);
+                    const glb_u32x4_cptr vn = (glb_u32x4_cptr)(a.v_new + (size_t(b) * H + h) * D);
+#pragma unroll
+                    for (int c = 0; c < NC; ++c) kr[c] = kn[4 * c + lg];
+                    vr = *(glb_vrow_cptr)((const char __attribute__((address_space(1)))*)vn + vx);
+                    const int sl = pinfo[i].x;
+                    if (sl >= 0 && lane < PCH) {
+                        const int pl = lane / NCH, x = lane % NCH;
+                        const u32x4 v = pl ? vn[x] : kn[x];
+                        *reinterpret_cast<u32x4*>((pl ? vplane_w : kplane_w) + size_t(sl) * SLICE + r * NCH * 16 + x * 16) = v;
+                    }
+                }
+                const bool kl = li == (r & 15), vl = lg == ((r & 15) >> 2);
+#pragma unroll
+                for (int c = 0; c < NC; ++c) kbuf[J][c] = kl ? kr[c] : kbuf[J][c];
+#pragma unroll
+                for (int rr = 0; rr < 4; ++rr) vbuf[J][rr] = (vl && rr == (r & 3)) ? vr : vbuf[J][rr];
+            }
+        }
+        compute(kbuf[J], vbuf[J], meta);
+
+        if (meta & 256) {
+            finish_unit();
+            if (i + 1 < npg) {
+                ++sig;
+                ++unit_k;
+                start_unit(unit_k, sig);
+            }
+        }
+    };
+
+    for (int i0 = 0; i0 < npg; i0 += PF) ring_round<0, PF>(step, i0, npg);
+    if (npatch > 0) store_rows();
+}
+
+// ---------------------------------------------------------------------------
 // Matrix-core page stream (BF16 pages, D in {64, 128}, 1..8 entries): runs a
 // page-stream plan (stream_plan.h).  Block i streams the pages of stream
 // positions [i*Q, (i+1)*Q) through an LDS ring of NS page stages filled by
@@ -727,6 +1209,23 @@ int stream_grid(const PoolView& pv, int B, int max_seq_len, int bpc = 1) {
     return int(need > cus * bpc ? need : cus * bpc);
 }
 
+// BF16 pages take the register-fed stream (two blocks per compute unit)
+// unless KVS_STREAM_RING=1 selects the LDS-ring stream (one block per unit;
+// a tuning knob read once per process).
+bool ring_stream() {
+    static const bool on = [] {
+        const char* e = std::getenv("KVS_STREAM_RING");
+        return e && e[0] == '1';
+    }();
+    return on;
+}
+
+// blocks per compute unit of the page stream for these pages
+int stream_bpc(const PoolView& pv) {
+    if (pv.k_codec != CODEC_BF16) return qstream_blocks_per_cu(pv);
+    return ring_stream() ? 1 : 2;
+}
+
 // Shared pages are read once per call unless KVS_STREAM_SHARE=0 (a tuning
 // knob read once per process, for measuring what the sharing saves).
 bool stream_share() {
@@ -743,7 +1242,7 @@ bool stream_share() {
 // everything else takes the chunked split kernel.
 bool stream_path(const PoolView& pv, int B, int gq) {
     return pv.k_codec == CODEC_BF16 && pv.v_codec == CODEC_BF16 && (pv.D == 64 || pv.D == 128) && B <= 8 &&
-           pv.H <= plan::kMaxH && pv.L <= 32768 && (long long)B * pv.H * pv.L <= 4096LL * kStreamPages &&
+           pv.H <= plan::kMaxH && pv.L <= 32768 && (long long)B * pv.H * pv.L <= 4096LL * (kStreamPages / 2) &&
            (gq == 1 || gq == 2 || gq == 4 || gq == 8);
 }
 
@@ -768,7 +1267,7 @@ WsLayout ws_layout(const PoolView& pv, int B, int gq, int max_seq_len, bool chun
     l.stream = chunk || stream_path(pv, B, gq) || qstream_path(pv, B, gq);
     size_t slots;
     if (l.stream) {
-        l.G = stream_grid(pv, B, max_seq_len, !chunk && pv.k_codec != CODEC_BF16 ? qstream_blocks_per_cu(pv) : 1);
+        l.G = stream_grid(pv, B, max_seq_len, stream_bpc(pv));
         const long long bound = stream_bound(pv, B, max_seq_len);
         l.qcap = int(bound > 0 ? (bound + l.G - 1) / l.G : 1);
         slots = size_t(l.G) + size_t(plan::kMaxSeg) * pv.H;     // (block, unit) pieces
@@ -812,7 +1311,8 @@ hipError_t launch_gq(const DecodeArgs& a, bool stream, hipStream_t s) {
     if (stream && a.pv.k_codec != CODEC_BF16) return launch_qstream(a, GQ, s);
     if constexpr (D == 64 || D == 128) {
         if (stream) {
-            paged_stream_kernel<D, GQ, 1, false><<<dim3(unsigned(stream_grid(a.pv, a.B, a.max_ctx))), 256, 0, s>>>(a);
+            if (ring_stream()) paged_stream_kernel<D, GQ, 1, false><<<dim3(unsigned(a.G)), 256, 0, s>>>(a);
+            else paged_vstream_kernel<D, GQ, 1, false><<<dim3(unsigned(a.G)), 256, 0, s>>>(a);
             const hipError_t e = hipGetLastError();
             if (e != hipSuccess) return e;
             DecodeArgs c = a;
@@ -863,7 +1363,8 @@ hipError_t launch_chunk_d(const DecodeArgs& a, int gq, int G, hipStream_t s) {
     switch (gq) {
 #define KVS_CHUNK_CASE(GQ)                                                  \
     case GQ:                                                                \
-        paged_stream_kernel<D, GQ, 2, true><<<grid, 256, 0, s>>>(a);        \
+        if (ring_stream()) paged_stream_kernel<D, GQ, 2, true><<<grid, 256, 0, s>>>(a);   \
+        else paged_vstream_kernel<D, GQ, 2, true><<<grid, 256, 0, s>>>(a); \
         if (hipPeekAtLastError() == hipSuccess)                             \
             stream_combine_kernel<D, GQ, 32><<<cgrid, 256, 0, s>>>(c);      \
         break;

@@ -9,6 +9,7 @@
 
 #include <cmath>
 #include <cstdint>
+#include <type_traits>
 
 #include "attn_common.h"
 #include "internal.h"
@@ -41,6 +42,18 @@ struct DecodeArgs {
 // the decode launch.
 __device__ __forceinline__ int plan_ent(const DecodeArgs& a, int b, int field) {
     return a.plan[plan::kOffEnt + b * plan::kEntWords + field];
+}
+
+// pages [i0, i0 + NS) of a ring of NS stages or buffers, stage J for page
+// i0 + J, while they exist (J is a compile-time constant in step)
+template <int J, int NS, class F>
+__device__ __forceinline__ void ring_round(F& step, int i0, int npg) {
+    if constexpr (J < NS) {
+        if (i0 + J < npg) {
+            step(std::integral_constant<int, J>{}, i0 + J);
+            ring_round<J + 1, NS>(step, i0, npg);
+        }
+    }
 }
 
 // waves per combine task: groups of 512 outputs of up to ncol columns

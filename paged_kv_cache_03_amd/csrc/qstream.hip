@@ -116,17 +116,6 @@ __device__ __forceinline__ f32x2_t fp8_pair(uint32_t w, int h) {
     return h ? __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w, 1.0f, true) : __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w, 1.0f, false);
 }
 
-// pages [i0, i0 + NS) of the ring, stage J for page i0 + J, while they exist
-template <int J, int NS, class F>
-__device__ __forceinline__ void ring_round(F& step, int i0, int npg) {
-    if constexpr (J < NS) {
-        if (i0 + J < npg) {
-            step(std::integral_constant<int, J>{}, i0 + J);
-            ring_round<J + 1, NS>(step, i0, npg);
-        }
-    }
-}
-
 template <int D, int KC, int VC>
 __global__ void __launch_bounds__(256, qstream_bpc<D>()) paged_qstream_kernel(DecodeArgs a) {
     using namespace plan;

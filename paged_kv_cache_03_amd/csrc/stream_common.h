@@ -39,6 +39,10 @@ typedef s16x4_t __attribute__((address_space(3)))* lds_s16x4_ptr;
 typedef char __attribute__((address_space(3)))* lds_byte_ptr;
 
 constexpr int kStreamPages = 1024;     // most pages one block of the page stream takes
+// Buffer resources (raw, stride 0): word 3 of the descriptor for gfx9-family
+// parts, and the cache-policy bit of a load that does not expect reuse (NT).
+constexpr int kBufferWord3 = 0x00020000;
+constexpr int kNonTemporal = 2;
 constexpr float kRescaleLog2 = 8.f;    // lazy rescale: probabilities stay below 2^8
 
 // One page into a ring stage: PER_T direct-to-LDS loads of the K slice and
