@@ -154,10 +154,9 @@ __global__ void __launch_bounds__(256) decode_split_kernel(DecodeArgs a) {
 // The unit merge passes through a dedicated 16 KiB LDS buffer, four tiles at
 // a time.  Columns, limits, lazy rescaling, sharing, the append of the step's
 // rows and the partial slots are those of the LDS-ring stream.
-template <int D, int GQ, int NCT, bool CHUNK>
-__global__ void __launch_bounds__(256, 2) paged_vstream_kernel(DecodeArgs a) {
+template <int D, int GQ, int NCT, bool CHUNK, int BPC = 2, int PFV = 0>
+__global__ void __launch_bounds__(256, BPC) paged_vstream_kernel(DecodeArgs a) {
     using namespace plan;
-    constexpr int BPC = 2;                         // blocks per compute unit
     constexpr int NCH = D / 8;                     // 16-byte chunks per bf16 row
     constexpr int NT = 256;
     constexpr int NC = D / 32;                     // QK products, k = 32 each
@@ -165,10 +164,10 @@ __global__ void __launch_bounds__(256, 2) paged_vstream_kernel(DecodeArgs a) {
     constexpr int NP = NDT / 4;                    // merge passes, four tiles each
     constexpr int VW = D / 32;                     // 32-bit V words per key and lane (D/16 bf16 dims)
     constexpr int NCOL = 16 * NCT;                 // query columns (partial slot width)
-    constexpr int QCHUNKS = 1024 / BPC;            // query cache: 16-byte chunks
+    constexpr int QCHUNKS = BPC == 1 ? 1024 : 512; // query cache: 16-byte chunks
     constexpr int QSEG = QCHUNKS / (NCOL * NCH);   // units with cached queries
-    constexpr int PAGES = kStreamPages / BPC;      // most pages a block takes
-    constexpr int PF = NCT == 1 ? 3 : 2;           // page buffers per wave (PF - 1 pages in flight)
+    constexpr int PAGES = BPC == 1 ? kStreamPages : kStreamPages / 2;   // page list (>= kStreamPages / BPC)
+    constexpr int PF = PFV ? PFV : (NCT == 1 ? 3 : 2);   // page buffers per wave (PF - 1 pages in flight)
     constexpr size_t SLICE = size_t(64) * D * 2;   // bytes of one plane's page slice
     static_assert((D == 64 || D == 128) && GQ >= 1 && GQ <= 16 && GQ <= NCOL, "shape");
     static_assert(QSEG >= 1 && QSEG * NCOL * NCH == QCHUNKS && QCHUNKS % NT == 0, "query cache shape");
@@ -1220,10 +1219,22 @@ bool ring_stream() {
     return on;
 }
 
+// register-fed stream shape for decode at D = 128 (a tuning knob read once
+// per process): KVS_STREAM_OCC = 10 * blocks per CU + page buffers per wave
+int vstream_occ() {
+    static const int v = [] {
+        const char* e = std::getenv("KVS_STREAM_OCC");
+        const int x = e ? std::atoi(e) : 0;
+        return (x == 22 || x == 23) ? x : 23;
+    }();
+    return v;
+}
+
 // blocks per compute unit of the page stream for these pages
 int stream_bpc(const PoolView& pv) {
     if (pv.k_codec != CODEC_BF16) return qstream_blocks_per_cu(pv);
-    return ring_stream() ? 1 : 2;
+    if (ring_stream()) return 1;
+    return pv.D == 128 ? vstream_occ() / 10 : 2;
 }
 
 // Shared pages are read once per call unless KVS_STREAM_SHARE=0 (a tuning
@@ -1312,12 +1323,13 @@ hipError_t launch_gq(const DecodeArgs& a, bool stream, hipStream_t s) {
     if constexpr (D == 64 || D == 128) {
         if (stream) {
             if (ring_stream()) paged_stream_kernel<D, GQ, 1, false><<<dim3(unsigned(a.G)), 256, 0, s>>>(a);
-            else paged_vstream_kernel<D, GQ, 1, false><<<dim3(unsigned(a.G)), 256, 0, s>>>(a);
+            else if (D != 128 || vstream_occ() == 23) paged_vstream_kernel<D, GQ, 1, false><<<dim3(unsigned(a.G)), 256, 0, s>>>(a);
+            else paged_vstream_kernel<D, GQ, 1, false, 2, 2><<<dim3(unsigned(a.G)), 256, 0, s>>>(a);
             const hipError_t e = hipGetLastError();
             if (e != hipSuccess) return e;
             DecodeArgs c = a;
             c.cgroups = combine_groups(GQ, D);
-            stream_combine_kernel<D, GQ, 16><<<dim3(unsigned((a.B * a.pv.H * c.cgroups + 3) / 4)), 256, 0, s>>>(c);
+            stream_combine_kernel<D, GQ, 16><<<dim3(unsigned(a.B * a.pv.H * c.cgroups)), 64, 0, s>>>(c);
             return hipGetLastError();
         }
     }
@@ -1359,14 +1371,14 @@ hipError_t launch_chunk_d(const DecodeArgs& a, int gq, int G, hipStream_t s) {
     const dim3 grid(static_cast<unsigned>(G));
     DecodeArgs c = a;
     c.cgroups = combine_groups(32, D);
-    const dim3 cgrid(static_cast<unsigned>((a.B * a.pv.H * c.cgroups + 3) / 4));
+    const dim3 cgrid(static_cast<unsigned>(a.B * a.pv.H * c.cgroups));
     switch (gq) {
 #define KVS_CHUNK_CASE(GQ)                                                  \
     case GQ:                                                                \
         if (ring_stream()) paged_stream_kernel<D, GQ, 2, true><<<grid, 256, 0, s>>>(a);   \
         else paged_vstream_kernel<D, GQ, 2, true><<<grid, 256, 0, s>>>(a); \
         if (hipPeekAtLastError() == hipSuccess)                             \
-            stream_combine_kernel<D, GQ, 32><<<cgrid, 256, 0, s>>>(c);      \
+            stream_combine_kernel<D, GQ, 32><<<cgrid, 64, 0, s>>>(c);       \
         break;
         KVS_CHUNK_CASE(1)
         KVS_CHUNK_CASE(2)

@@ -56,29 +56,31 @@ __device__ __forceinline__ void ring_round(F& step, int i0, int npg) {
     }
 }
 
-// waves per combine task: groups of 512 outputs of up to ncol columns
-constexpr int combine_groups(int ncol, int D) { return (ncol * D + 511) / 512; }
+// single-wave combine blocks per task: groups of 128 outputs of up to ncol columns
+constexpr int combine_groups(int ncol, int D) { return (ncol * D + 127) / 128; }
 
 namespace {
 
 
-// Combine of the page stream: one wave per task of the plan -- an (entry,
-// KV head) whose outputs have more than one piece -- and group of 512 of its
-// outputs.  The task lists its
-// pieces (the (block, unit) partials of the entry's units in segment order,
-// each unit's slots in block order): a fixed order, so the result does not
-// depend on timing.  Every lane folds 8 consecutive outputs of one column
-// over all pieces, CMAX pieces per memory round; the task record is read with
-// scalar loads in the same round trip as the header.
+// Combine of the page stream: one single-wave block per task of the plan --
+// an (entry, KV head) whose outputs have more than one piece -- and group of
+// kCombineOut of its outputs, so the partial reads spread over every compute
+// unit.  The task lists its pieces (the (block, unit) partials of the entry's
+// units in segment order, each unit's slots in block order): a fixed order,
+// so the result does not depend on timing.  Every lane folds two consecutive
+// outputs of one column over all pieces, CMAX pieces per memory round; the
+// task record and its first CMAX piece ids are read with scalar loads in the
+// same round trip as the header.
+constexpr int kCombineOut = 128;
+
 template <int D, int GQ, int NCOL>
-__global__ void __launch_bounds__(256) stream_combine_kernel(DecodeArgs a) {
+__global__ void __launch_bounds__(64) stream_combine_kernel(DecodeArgs a) {
     using namespace plan;
     constexpr int CMAX = 16;
     const int lane = int(threadIdx.x) & 63;
-    const int w = __builtin_amdgcn_readfirstlane(int(threadIdx.x) >> 6);
     const int H = a.pv.H;
-    const int tg = int(blockIdx.x) * 4 + w;
-    const int t = tg / a.cgroups, grp = tg - t * a.cgroups;   // task, its group of 512 outputs
+    const int tg = int(blockIdx.x);
+    const int t = tg / a.cgroups, grp = tg - t * a.cgroups;   // task, its group of outputs
     const int32_t* P = a.plan;
     const int32_t* rec = P + off_tasks(H, int(a.G)) + size_t(t) * kTaskWords;
     // header and task record together (no branch between the loads)
@@ -86,73 +88,69 @@ __global__ void __launch_bounds__(256) stream_combine_kernel(DecodeArgs a) {
     const int pgq = ld_uniform(P, H_GQ), ntask = ld_uniform(P, H_NTASK);
     const int E = ld_uniform(rec, T_E), ncolb = ld_uniform(rec, T_NCOL), obase = ld_uniform(rec, T_OUT);
     const int poff = ld_uniform(rec, T_POFF);
-    const bool run = (magic == kMagic) & (pb == a.B) & (ph == H) & (pgq == GQ) & (t < ntask) & (grp * 512 < ncolb * D);
+    int sp[CMAX];                                  // the first CMAX piece ids, in the same round trip
+#pragma unroll
+    for (int kk = 0; kk < CMAX; ++kk) sp[kk] = ld_uniform(rec, T_PIECE + kk);
+    const bool run = (magic == kMagic) & (pb == a.B) & (ph == H) & (pgq == GQ) & (t < ntask) &
+                     (grp * kCombineOut < ncolb * D);
     if (!run) return;                              // (a plan of another shape: the stream marked the outputs)
     const int32_t* over_list = P + off_over(H, int(a.G));
 
-    // this wave's group of 512 outputs; uniform trip counts: every lane takes
+    // this wave's group of outputs; uniform trip counts: every lane takes
     // part in the readlane lookups
-    {
-        const int g0 = grp * 512;
-        const int e0 = g0 + lane * 8;
-        const bool act = e0 < ncolb * D;
-        const int c = act ? e0 / D : 0, d0 = act ? e0 % D : 0;
-        float fm = -INFINITY, fl = 0.f, fa[8];
+    const int e0 = grp * kCombineOut + lane * 2;
+    const bool act = e0 < ncolb * D;
+    const int c = act ? e0 / D : 0, d0 = act ? e0 % D : 0;
+    float fm = -INFINITY, fl = 0.f, fa0 = 0.f, fa1 = 0.f;
+    // one memory round of CMAX pieces (ids from pid_of; pieces from nvalid on
+    // repeat a valid one and get weight 0): every load in flight together,
+    // then the fold in piece order
+    auto round = [&](auto pid_of, int nvalid) __attribute__((always_inline)) {
+        float2 ml[CMAX], av[CMAX];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) fa[e] = 0.f;
-#pragma unroll 1
-        for (int w0 = 0; w0 < E; w0 += 64) {
-            // lane k: partial index of piece w0 + k
-            const int k = w0 + lane;
-            int pid = 0;
-            if (k < E) pid = k < kTaskInline ? rec[T_PIECE + k] : over_list[poff + k - kTaskInline];
-            const int wn = min(64, E - w0);
-#pragma unroll 1
-            for (int k0 = 0; k0 < wn; k0 += CMAX) {
-                // every load of the round in flight together: pieces past the
-                // window repeat its last one and get weight 0
-                float2 ml[CMAX];
-                float4 av0[CMAX], av1[CMAX];
-#pragma unroll
-                for (int kk = 0; kk < CMAX; ++kk) {
-                    const int kc = min(k0 + kk, wn - 1);
-                    const size_t it = size_t(__builtin_amdgcn_readlane(pid, kc)) + c;
-                    ml[kk] = *reinterpret_cast<const float2*>(a.part_ml + it * 2);
-                    av0[kk] = *reinterpret_cast<const float4*>(a.part_acc + it * D + d0);
-                    av1[kk] = *reinterpret_cast<const float4*>(a.part_acc + it * D + d0 + 4);
-                }
-                // keep every load of the round above the fold (the scheduler
-                // would otherwise sink each one to its use, one round trip each)
-                __builtin_amdgcn_sched_barrier(0);
-                float mx = fm;
-#pragma unroll
-                for (int kk = 0; kk < CMAX; ++kk) mx = fmaxf(mx, ml[kk].x);   // repeats change nothing
-                const float wp = fm == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(fm - mx);
-                fl *= wp;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) fa[e] *= wp;
-#pragma unroll
-                for (int kk = 0; kk < CMAX; ++kk) {
-                    const float wgt = (k0 + kk >= wn || ml[kk].x == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(ml[kk].x - mx);
-                    fl += ml[kk].y * wgt;
-                    fa[0] += av0[kk].x * wgt;
-                    fa[1] += av0[kk].y * wgt;
-                    fa[2] += av0[kk].z * wgt;
-                    fa[3] += av0[kk].w * wgt;
-                    fa[4] += av1[kk].x * wgt;
-                    fa[5] += av1[kk].y * wgt;
-                    fa[6] += av1[kk].z * wgt;
-                    fa[7] += av1[kk].w * wgt;
-                }
-                fm = mx;
-            }
+        for (int kk = 0; kk < CMAX; ++kk) {
+            const size_t it = size_t(pid_of(kk)) + c;
+            ml[kk] = *reinterpret_cast<const float2*>(a.part_ml + it * 2);
+            av[kk] = *reinterpret_cast<const float2*>(a.part_acc + it * D + d0);
         }
-        if (act) {
-            const float inv = fl > 0.f ? 1.f / fl : 0.f;
-            float* o = a.out + obase + size_t(c / GQ) * a.Hq * D + size_t(c % GQ) * D + d0;
-            *reinterpret_cast<float4*>(o) = make_float4(fa[0] * inv, fa[1] * inv, fa[2] * inv, fa[3] * inv);
-            *reinterpret_cast<float4*>(o + 4) = make_float4(fa[4] * inv, fa[5] * inv, fa[6] * inv, fa[7] * inv);
+        // keep every load of the round above the fold (the scheduler would
+        // otherwise sink each one to its use, one round trip each)
+        __builtin_amdgcn_sched_barrier(0);
+        float mx = fm;
+#pragma unroll
+        for (int kk = 0; kk < CMAX; ++kk) mx = fmaxf(mx, ml[kk].x);   // repeats change nothing
+        const float wp = fm == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(fm - mx);
+        fl *= wp;
+        fa0 *= wp;
+        fa1 *= wp;
+#pragma unroll
+        for (int kk = 0; kk < CMAX; ++kk) {
+            const float wgt = (kk >= nvalid || ml[kk].x == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(ml[kk].x - mx);
+            fl += ml[kk].y * wgt;
+            fa0 += av[kk].x * wgt;
+            fa1 += av[kk].y * wgt;
         }
+        fm = mx;
+    };
+    // pieces 0 .. CMAX-1 from the scalar ids
+    round([&](int kk) __attribute__((always_inline)) { return kk < E ? sp[kk] : sp[0]; }, E);
+    // the rest: lane k holds the id of piece w0 + k
+#pragma unroll 1
+    for (int w0 = CMAX; w0 < E; w0 += 64) {
+        const int k = w0 + lane;
+        int pid = 0;
+        if (k < E) pid = k < kTaskInline ? rec[T_PIECE + k] : over_list[poff + k - kTaskInline];
+        const int wn = min(64, E - w0);
+#pragma unroll 1
+        for (int k0 = 0; k0 < wn; k0 += CMAX)
+            round([&](int kk) __attribute__((always_inline)) {
+                return __builtin_amdgcn_readlane(pid, min(k0 + kk, wn - 1));
+            }, wn - k0);
+    }
+    if (act) {
+        const float inv = fl > 0.f ? 1.f / fl : 0.f;
+        float* o = a.out + obase + size_t(c / GQ) * a.Hq * D + size_t(c % GQ) * D + d0;
+        *reinterpret_cast<float2*>(o) = make_float2(fa0 * inv, fa1 * inv);
     }
 }
 

@@ -676,12 +676,12 @@ hipError_t launch_one(const DecodeArgs& a, int gq, hipStream_t s) {
     if (e != hipSuccess) return e;
     DecodeArgs c = a;
     c.cgroups = combine_groups(gq, D);
-    const dim3 cgrid(static_cast<unsigned>((a.B * a.pv.H * c.cgroups + 3) / 4));
+    const dim3 cgrid(static_cast<unsigned>(a.B * a.pv.H * c.cgroups));
     switch (gq) {
-        case 1: stream_combine_kernel<D, 1, 16><<<cgrid, 256, 0, s>>>(c); break;
-        case 2: stream_combine_kernel<D, 2, 16><<<cgrid, 256, 0, s>>>(c); break;
-        case 4: stream_combine_kernel<D, 4, 16><<<cgrid, 256, 0, s>>>(c); break;
-        case 8: stream_combine_kernel<D, 8, 16><<<cgrid, 256, 0, s>>>(c); break;
+        case 1: stream_combine_kernel<D, 1, 16><<<cgrid, 64, 0, s>>>(c); break;
+        case 2: stream_combine_kernel<D, 2, 16><<<cgrid, 64, 0, s>>>(c); break;
+        case 4: stream_combine_kernel<D, 4, 16><<<cgrid, 64, 0, s>>>(c); break;
+        case 8: stream_combine_kernel<D, 8, 16><<<cgrid, 64, 0, s>>>(c); break;
         default: return hipErrorNotSupported;
     }
     return hipGetLastError();
