@@ -82,7 +82,7 @@ def decode_kernel_name(wl) -> str:
     gq = wl.Hq // wl.H
     if gq in (1, 2, 4, 8) and wl.B <= 8:
         if wl.profile == "BF16" and wl.D in (64, 128):
-            return f"paged_stream_kernel<{wl.D}, {gq}, 1, false>"
+            return f"paged_vstream_kernel<{wl.D}, {gq}, 1, false>"
         # codec numbers of the page-stream instances: INT8-G64 1, FP8-row 2, NVFP4-G16 3
         sides = {"INT8_G64": (1, 1), "FP8_E4M3FN_ROW256": (2, 2), "NVFP4_G16": (3, 3), "K8V4": (2, 3)}
         if wl.profile in sides and (wl.D in (128, 256) or (wl.D == 64 and 3 not in sides[wl.profile])):
@@ -186,7 +186,7 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0
 def verify_kernel_names(wl) -> str:
     gq = wl.Hq // wl.H
     if wl.profile == "BF16" and wl.D in (64, 128) and gq in (1, 2, 4, 8):
-        return f"verify_tile_kernel<{wl.D}, {gq}> + paged_stream_kernel<{wl.D}, {gq}, 2, true>"
+        return f"verify_tile_kernel<{wl.D}, {gq}> + paged_vstream_kernel<{wl.D}, {gq}, 2, true>"
     return f"verify_scalar_kernel<{wl.D}, {gq}>"
 
 

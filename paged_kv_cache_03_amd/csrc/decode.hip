@@ -8,10 +8,11 @@
 //
 // A decode is a plan of the batch state (stream_plan.hip; one per step, it
 // serves every layer) and a run:
-//  * the matrix-core page stream (BF16 pages, D in {64, 128}): every page of
-//    the plan in one flat list, cut into equal ranges, one 256-thread block
-//    per compute unit; leading pages that entries share are read once for
-//    all of them; then a combine launch for outputs with several pieces;
+//  * the matrix-core page stream (BF16 pages, D in {64, 128}; quantized
+//    pages in qstream.hip): every page of the plan in one flat list, cut
+//    into equal ranges, two 256-thread blocks per compute unit; leading
+//    pages that entries share are read once for all of them; then a combine
+//    launch for outputs with several pieces;
 //  * the split kernel (every other profile and shape): entry b's pages are
 //    cut into chunks of `chunk_pages` consecutive logical pages, one wave per
 //    (entry, KV head, chunk), then a combine launch.
@@ -134,29 +135,47 @@ __global__ void __launch_bounds__(256) decode_split_kernel(DecodeArgs a) {
 
 
 // ---------------------------------------------------------------------------
-// Register-fed page stream (BF16 pages, D in {64, 128}, 1..8 entries): runs a
-// page-stream plan (stream_plan.h) like the LDS-ring stream below, with two
-// blocks per compute unit and no LDS ring.  Wave w owns keys [16w, 16w+16)
-// of every page of the block's range and loads them itself, straight into
-// the registers the matrix cores read, PF pages ahead (non-temporal loads: a
-// page is read once per call); waves never wait for each other between unit
-// ends.  Per page and wave:
-//  * K operand (S^T = K . Q^T, v_mfma_f32_16x16x32_bf16): lane (li, lg) loads
-//    key 16w + li, dims 8(4c + lg) .. +7 for product c -- a 16-byte row load
-//    each;
-//  * V^T operand: lane (li, lg) loads the D/16 dims starting at (D/16) li of
-//    keys 16w + 4lg + r, r = 0..3 -- the four keys whose probabilities the
-//    lane holds -- and pairs the bf16 values of two keys per dim with one byte
-//    permute each: that is the transpose.  Row m of tile j holds head dim
-//    (D/16) m + j;
-//  * PV: V^T . [P_hi; P_lo] as one k=32 product per tile (the lane's keys
-//    listed twice, against P_hi then P_lo).
-// The unit merge passes through a dedicated 16 KiB LDS buffer, four tiles at
-// a time.  Columns, limits, lazy rescaling, sharing, the append of the step's
-// rows and the partial slots are those of the LDS-ring stream.
-template <int D, int GQ, int NCT, bool CHUNK, int BPC = 2, int PFV = 0>
-__global__ void __launch_bounds__(256, BPC) paged_vstream_kernel(DecodeArgs a) {
+// Matrix-core page stream, register-fed (BF16 pages, D in {64, 128}, 1..8
+// entries): runs a page-stream plan (stream_plan.h).  Block i of two per
+// compute unit streams the pages of stream positions [i*Q, (i+1)*Q).  A unit
+// (segment s, KV head h) carries the query columns of every entry in the
+// segment's mask: GQ heads per entry in decode (shared pages carry the heads
+// of all entries that share them), T x GQ (token, head) columns of one entry
+// in chunk mode; each column has its own causal key limit.  Wave w owns keys
+// [16w, 16w+16) of every page, loads them itself straight into the registers
+// the matrix cores read, one page ahead (buffer loads whose range ends at
+// the page's last visible row, so stale rows read as zeros; non-temporal: a
+// page is read once per call), and keeps its own online-softmax state; the
+// waves meet only at unit ends.  Per page and wave:
+//  * QK^T: S^T[16 keys x 16 columns] = K . Q^T with v_mfma_f32_16x16x32_bf16;
+//    lane (li, lg) loads key 16w + li, dims 8(4c + lg) .. +7 for product c,
+//    a 16-byte row load each (padding columns are zero, never read back);
+//  * the accumulator layout of S^T (lane l: column l%16, keys 4(l/16) + r)
+//    is the operand layout of P^T, which enters as two bf16 terms
+//    p_hi + p_lo (about 2^-16 relative error instead of bf16's 2^-9);
+//  * PV: O^T[16 dims x 16 columns] += V^T . [P_hi; P_lo] as one k=32 product
+//    per tile (the lane's keys listed twice, against P_hi then P_lo).  Lane
+//    (li, lg) loads the D/16 dims starting at (D/16) li of keys 16w + 4lg + r,
+//    r = 0..3 -- the keys whose probabilities it holds -- and pairs the bf16
+//    values of two keys per dim with one byte permute each: the transpose.
+//    Row m of tile j holds head dim (D/16) m + j;
+//  * lazy rescaling: a column's exponent reference moves only when a page's
+//    maximum exceeds it by more than 2^8.
+// Before the first page, one round trip brings the plan's tables and the
+// block's page list into LDS, with the query rows of the block's first units
+// and its new-token rows (decode with the step's rows: the wave owning a new
+// row's key takes it from there instead of the loaded one, and the block
+// writes the rows into their pages at the end).  When a unit ends, the four
+// waves' states are merged through a 16 KiB LDS buffer, four tiles at a time;
+// a column whose (entry, KV head) has no other piece is normalized and
+// written out, the others are stored as partials in slot i + sigma for the
+// combine launch, which folds each (entry, KV head)'s pieces in unit and
+// block order: deterministic output.  Both the block index and sigma only
+// grow along the stream, so no two (block, unit) pieces share a slot.
+template <int D, int GQ, int NCT, bool CHUNK>
+__global__ void __launch_bounds__(256, 2) paged_vstream_kernel(DecodeArgs a) {
     using namespace plan;
+    constexpr int BPC = 2;                         // blocks per compute unit
     constexpr int NCH = D / 8;                     // 16-byte chunks per bf16 row
     constexpr int NT = 256;
     constexpr int NC = D / 32;                     // QK products, k = 32 each
@@ -164,10 +183,10 @@ __global__ void __launch_bounds__(256, BPC) paged_vstream_kernel(DecodeArgs a) {
     constexpr int NP = NDT / 4;                    // merge passes, four tiles each
     constexpr int VW = D / 32;                     // 32-bit V words per key and lane (D/16 bf16 dims)
     constexpr int NCOL = 16 * NCT;                 // query columns (partial slot width)
-    constexpr int QCHUNKS = BPC == 1 ? 1024 : 512; // query cache: 16-byte chunks
+    constexpr int QCHUNKS = 1024 / BPC;            // query cache: 16-byte chunks
     constexpr int QSEG = QCHUNKS / (NCOL * NCH);   // units with cached queries
-    constexpr int PAGES = BPC == 1 ? kStreamPages : kStreamPages / 2;   // page list (>= kStreamPages / BPC)
-    constexpr int PF = PFV ? PFV : (NCT == 1 ? 3 : 2);   // page buffers per wave (PF - 1 pages in flight)
+    constexpr int PAGES = kStreamPages / BPC;      // most pages a block takes
+    constexpr int PF = 2;                          // page buffers per wave: the next page is in flight
     constexpr size_t SLICE = size_t(64) * D * 2;   // bytes of one plane's page slice
     static_assert((D == 64 || D == 128) && GQ >= 1 && GQ <= 16 && GQ <= NCOL, "shape");
     static_assert(QSEG >= 1 && QSEG * NCOL * NCH == QCHUNKS && QCHUNKS % NT == 0, "query cache shape");
@@ -614,534 +633,6 @@ __global__ void __launch_bounds__(256, BPC) paged_vstream_kernel(DecodeArgs a) {
     if (npatch > 0) store_rows();
 }
 
-// ---------------------------------------------------------------------------
-// Matrix-core page stream (BF16 pages, D in {64, 128}, 1..8 entries): runs a
-// page-stream plan (stream_plan.h).  Block i streams the pages of stream
-// positions [i*Q, (i+1)*Q) through an LDS ring of NS page stages filled by
-// direct-to-LDS loads, so NS-1 pages are in flight while one is computed.
-// A unit (segment s, KV head h) carries the query columns of every entry in
-// the segment's mask: GQ heads per entry in decode (shared pages carry the
-// heads of all entries that share them), T x GQ (token, head) columns of one
-// entry in chunk mode; each column has its own causal key limit.  Wave w
-// owns tokens [16w, 16w+16) of every page and keeps its own online-softmax
-// state.
-//  * QK^T on the matrix cores: S^T[16 tokens x 16] = K . Q^T with
-//    v_mfma_f32_16x16x32_bf16 (padding columns are zero and never read back).
-//  * The accumulator layout of S^T (lane l: column l%16, tokens 4(l/16)+r)
-//    is the B-operand layout of v_mfma_f32_16x16x16_bf16, so P^T feeds PV
-//    in place.
-//  * PV on the matrix cores: O^T[16 dims x 16] += V^T . P^T per 16-dim tile,
-//    V^T read from LDS with the transposing 64-bit read (ds_read_b64_tr_b16:
-//    within a 16-lane row, lane i receives element i%4 of the 8-byte chunks
-//    addressed by lanes 4e + i/4).  P enters as two bf16 terms p_hi + p_lo
-//    (two products), about 2^-16 relative error instead of bf16's 2^-9.
-//  * Lazy rescaling: the exponent reference of a column moves only when a
-//    page's maximum exceeds it by more than 2^8.
-//  * K rows are XOR-swizzled in 16-byte chunks, V rows in 32-byte units, so
-//    both reads are free of LDS bank conflicts.
-// Before the ring starts, one round trip brings the plan's tables and the
-// block's page list into LDS; the query rows of the block's first units go
-// to LDS by direct-to-LDS loads ahead of the first pages.  When a unit ends,
-// the four waves' states are merged through the stage just consumed; a
-// column whose (entry, KV head) has no other piece is normalized and written
-// out, the others are stored as partials in slot i + sigma for the combine
-// launch, which folds each (entry, KV head)'s pieces in unit and block
-// order: deterministic output.  Both the block index and sigma only grow
-// along the stream, so no two (block, unit) pieces share a slot.
-template <int D, int GQ, int NCT, bool CHUNK>
-__global__ void __launch_bounds__(256) paged_stream_kernel(DecodeArgs a) {
-    using namespace plan;
-    constexpr int NCH = D / 8;                     // 16-byte chunks per row
-    constexpr int NT = 256;
-    constexpr int SLOTS = 64 * NCH;                // chunks per page slice of one plane
-    constexpr int SLICE_BYTES = SLOTS * 16;
-    constexpr int PER_T = SLOTS / NT;              // direct-to-LDS loads per thread and plane
-    constexpr int NS = D == 128 ? 4 : 8;           // ring stages
-    constexpr int LOADS_PER_PAGE = 2 * PER_T;
-    constexpr int NC = D / 32;                     // QK products, k = 32 each
-    constexpr int NDT = D / 16;                    // PV tiles of 16 dims
-    constexpr int DPW = NDT / 4;                   // tiles each wave merges and writes
-    constexpr int WBUF = NDT * 4 * 64;             // floats of one wave's state in the merge area
-    constexpr int NCOL = 16 * NCT;                 // query columns (partial slot width)
-    constexpr int QCHUNKS = 1024;                  // query cache: 16 KiB of 16-byte chunks
-    constexpr int QSEG = QCHUNKS / (NCOL * NCH);   // units with cached queries
-    static_assert((D == 64 || D == 128) && GQ >= 1 && GQ <= 16 && GQ <= NCOL, "shape");
-    static_assert(PER_T == 2 || PER_T == 4, "page fetch shapes");
-    static_assert(QSEG >= 1 && QSEG * NCOL * NCH == QCHUNKS && QCHUNKS % NT == 0, "query cache shape");
-    static_assert(NS * SLICE_BYTES == 0x10000, "V stages sit 64 KiB above the K stages");
-    static_assert(LOADS_PER_PAGE * (NS - 1) + QCHUNKS / NT < 64, "vmcnt range");
-    static_assert(2 * WBUF * 4 <= SLICE_BYTES, "two waves' merge state fit one slice");
-
-    __shared__ u32x4 ring[2][NS][SLOTS];           // [K | V][stage][slot]
-    __shared__ int2 pinfo[kStreamPages];           // the block's pages: (slice g*H + h or -1, meta)
-    __shared__ u32x4 qcache[QCHUNKS];              // query rows of the first QSEG units: [unit][column][chunk]
-    __shared__ float mlbuf[4][16][2];              // per-wave (m, l) of every column at a unit's end
-    __shared__ int ent_s[kMaxEnt][kEntWords];
-    __shared__ int seg_s[kMaxSeg][kSegWords];
-    __shared__ int exp_s[kMaxEnt * kMaxH];         // pieces per (entry, KV head)
-    __shared__ int patch_s[kMaxPatch];             // the block's new-token rows: page | entry | head | row
-    __shared__ u32x4 pstage[NT];                   // their K and V chunks, staged before the ring starts
-
-    const int tid = int(threadIdx.x);
-    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int lane = tid & 63, li = lane & 15, lg = lane >> 4;
-    const int H = a.pv.H, i_blk = int(blockIdx.x), G = int(gridDim.x);
-    const int32_t* P = a.plan;
-
-    // one round trip: the plan's header and tables, this block's page list
-    const int magic = ld_uniform(P, H_MAGIC), pb = ld_uniform(P, H_B), ph = ld_uniform(P, H_H);
-    const int pgq = ld_uniform(P, H_GQ), pg = ld_uniform(P, H_G), pq = ld_uniform(P, H_QCAP);
-    const int pchunk = ld_uniform(P, H_CHUNK);
-    const bool plan_ok = (magic == kMagic) & (pb == a.B) & (ph == H) & (pgq == GQ) & (pg == G) & (pq == a.qcap) &
-                         (pchunk == int(CHUNK));
-    const int Q = ld_uniform(P, H_Q), nseg = ld_uniform(P, H_NSEG), zero = ld_uniform(P, H_ZERO);
-    const int npg = ld_uniform(P, off_blk(H) + 4 * size_t(i_blk));
-    int sig = ld_uniform(P, off_blk(H) + 4 * size_t(i_blk) + 1);   // unit being computed
-    const bool append = !CHUNK && a.k_new != nullptr;
-    const int npatch = append ? ld_uniform(P, off_blk(H) + 4 * size_t(i_blk) + 2) : 0;
-    {
-        // every load first (clamped indices, all inside the plan), then the
-        // LDS writes: one memory round trip
-        static_assert(kMaxEnt * kEntWords <= NT && kMaxSeg * kSegWords <= NT && kMaxPatch <= NT, "tables");
-        static_assert(kMaxEnt * kMaxH <= 2 * NT && kStreamPages == 4 * NT, "tables");
-        const int2* pl = reinterpret_cast<const int2*>(P + off_pages(H, G)) + size_t(i_blk) * a.qcap;
-        const int ne = kMaxEnt * H;
-        const int v_ent = P[kOffEnt + min(tid, kMaxEnt * kEntWords - 1)];
-        const int v_seg = P[kOffSeg + min(tid, kMaxSeg * kSegWords - 1)];
-        const int v_patch = P[off_patch(H, G) + size_t(i_blk) * kMaxPatch + min(tid, kMaxPatch - 1)];
-        const int v_exp0 = P[kOffExp + min(tid, ne - 1)];
-        const int v_exp1 = P[kOffExp + min(tid + NT, ne - 1)];
-        int2 v_pg[4];
-#pragma unroll
-        for (int k = 0; k < 4; ++k) v_pg[k] = pl[min(tid + k * NT, a.qcap - 1)];
-        if (tid < kMaxEnt * kEntWords) ent_s[tid / kEntWords][tid % kEntWords] = v_ent;
-        if (tid < kMaxSeg * kSegWords) seg_s[tid / kSegWords][tid % kSegWords] = v_seg;
-        if (tid < kMaxPatch) patch_s[tid] = v_patch;
-        if (tid < ne) exp_s[tid] = v_exp0;
-        if (tid + NT < ne) exp_s[tid + NT] = v_exp1;
-#pragma unroll
-        for (int k = 0; k < 4; ++k)
-            if (tid + k * NT < a.qcap) pinfo[tid + k * NT] = v_pg[k];
-    }
-    block_lds_barrier();
-    if (!plan_ok) {                                // a plan of another batch shape: make it visible
-        if (!CHUNK && i_blk == 0)
-            for (int x = tid; x < a.B * a.Hq * D; x += NT) a.out[x] = __builtin_nanf("");
-        return;
-    }
-    if (i_blk == 0) {                              // entries with nothing to attend produce zeros
-        for (int b = 0; b < a.B; ++b) {
-            if (!((zero >> b) & 1)) continue;
-            const size_t r0 = size_t(ent_s[b][E_CU]) * a.Hq * D;
-            for (int x = tid; x < ent_s[b][E_T] * a.Hq * D; x += NT) a.out[r0 + x] = 0.f;
-        }
-    }
-    if (npg <= 0) return;
-
-    // column c of a unit of segment s: entry, query token, head within the group
-    struct Col {
-        int b, tok, j;
-    };
-    auto col_of = [&](int s, int c) __attribute__((always_inline)) {
-        if constexpr (CHUNK) {
-            return Col{seg_s[s][S_OWNER], c / GQ, c % GQ};
-        } else {
-            int m = seg_s[s][S_MASK];
-            for (int k = c / GQ; k > 0; --k) m &= m - 1;
-            return Col{__builtin_ctz(unsigned(m | 0x100)), 0, c % GQ};
-        }
-    };
-    auto ncol_of = [&](int s) __attribute__((always_inline)) {
-        return __builtin_popcount(unsigned(seg_s[s][S_MASK])) * seg_s[s][S_W];
-    };
-    auto q_row = [&](const Col& cl, int h) __attribute__((always_inline)) {
-        return a.q + (size_t(ent_s[cl.b][E_CU] + cl.tok) * a.Hq + size_t(h) * GQ + cl.j) * D;
-    };
-    auto unit_seg = [&](int sg) __attribute__((always_inline)) { return sg / H; };
-
-    // new-token rows of this block (decode with the step's rows): chunk x of
-    // plane pl of staged row r_q at pstage[q * 2 * NCH + pl * NCH + x], issued
-    // first so that the first page's wait covers them
-    constexpr int PCH = 2 * NCH;                   // chunks of one staged row pair
-    if (npatch > 0) {
-        const int q = tid / PCH, pl = (tid / NCH) & 1, x = tid % NCH;
-        const u32x4* src = reinterpret_cast<const u32x4*>(a.q);
-        if (q < npatch) {
-            const int pe = patch_s[q];
-            const int b = (pe >> 12) & 7, h = (pe >> 15) & 63;
-            src = reinterpret_cast<const u32x4*>((pl ? a.v_new : a.k_new) + (size_t(b) * H + h) * D) + x;
-        }
-        fetch_chunk(uint32_t(reinterpret_cast<uintptr_t>((lds_byte_ptr)(&pstage[0]))) + uint32_t(w * 64 * 16), src);
-    }
-
-    // query rows of the first QSEG units, straight into LDS (columns past a
-    // unit's last read row 0 of the call; they are never used)
-    const uint32_t qcache_lds = uint32_t(reinterpret_cast<uintptr_t>((lds_byte_ptr)(&qcache[0])));
-#pragma unroll
-    for (int k = 0; k < QCHUNKS / NT; ++k) {
-        const int x = k * NT + tid;
-        const int u = x / (NCOL * NCH), c = (x / NCH) % NCOL, ch = x % NCH;
-        const int sg = sig + u, s = unit_seg(sg);
-        const u32x4* src = reinterpret_cast<const u32x4*>(a.q);
-        if (s < nseg && c < ncol_of(s)) src = reinterpret_cast<const u32x4*>(q_row(col_of(s, c), sg - s * H)) + ch;
-        fetch_chunk(qcache_lds + uint32_t((k * NT + w * 64) * 16), src);
-    }
-
-    // Stage layout: K slot s (row t = s / NCH, position x = s % NCH) holds
-    // chunk x ^ kswz(t) of row t; V slot s holds chunk x ^ vswz(t).
-    auto kswz = [](int t) __attribute__((always_inline)) { return NCH == 16 ? (t & 15) : ((t >> 1) & 7); };
-    auto vswz = [](int t) __attribute__((always_inline)) { return NCH == 16 ? ((t & 7) << 1) : (((t >> 1) & 3) << 1); };
-    const char* kplane = static_cast<const char*>(a.pv.lv.k_code);
-    const char* vplane = static_cast<const char*>(a.pv.lv.v_code);
-    char* kplane_w = static_cast<char*>(a.pv.lv.k_code);
-    char* vplane_w = static_cast<char*>(a.pv.lv.v_code);
-    uint32_t k_src[PER_T], v_src[PER_T];           // source byte offsets within a page slice
-#pragma unroll
-    for (int k = 0; k < PER_T; ++k) {
-        const int s = k * NT + tid;
-        const int t = s / NCH, x = s % NCH;
-        k_src[k] = uint32_t(t * NCH + (x ^ kswz(t))) * 16u;
-        v_src[k] = uint32_t(t * NCH + (x ^ vswz(t))) * 16u;
-    }
-    const uint32_t ring_lds = uint32_t(reinterpret_cast<uintptr_t>((lds_byte_ptr)(&ring[0][0][0])));
-    // page fi of the range into stage fs
-    auto fetch = [&](int fi, int fs) __attribute__((always_inline)) {
-        const uint32_t dst = ring_lds + uint32_t(fs * SLICE_BYTES + w * 1024);
-        const int sl = __builtin_amdgcn_readfirstlane(pinfo[fi].x);
-        const size_t off = size_t(sl < 0 ? 0 : sl) * SLICE_BYTES;
-        if constexpr (PER_T == 4) fetch_page4(dst, kplane + off, vplane + off, k_src, v_src);
-        else fetch_page2(dst, kplane + off, vplane + off, k_src, v_src);
-    };
-    // meta of page fi: the last page of the block also ends its unit here
-    auto meta_of = [&](int fi) __attribute__((always_inline)) {
-        return __builtin_amdgcn_readfirstlane(pinfo[fi].y) | (fi == npg - 1 ? 256 : 0);
-    };
-
-    // Per-lane LDS offsets into stage 0, fixed for the whole stream (the
-    // stage adds an immediate below 64 KiB).
-    //  QK A operand (K): row 16w + li, chunk 4c + lg (u32x4 index)
-    //  PV A operand (V^T, transposing read): lane li of row group lg points at
-    //  token 16w + 4lg + li/4, dims 16dt + 4(li%4) .. +3 (byte offset from the
-    //  K stage 0, i.e. including the 64 KiB to the V stages)
-    int koff[NC], voff[NDT];
-    {
-        const int t = 16 * w + li;
-#pragma unroll
-        for (int c = 0; c < NC; ++c) koff[c] = t * NCH + ((4 * c + lg) ^ kswz(t));
-        const int tv = 16 * w + 4 * lg + (li >> 2), qd = li & 3;
-#pragma unroll
-        for (int dt = 0; dt < NDT; ++dt)
-            voff[dt] = 0x10000 + tv * NCH * 16 + (((2 * dt + (qd >> 1)) ^ vswz(tv)) * 16) + 8 * (qd & 1);
-    }
-
-    bf16x8_t qb[NCT][NC];                          // Q^T B operand: column 16ct + li, chunk 4c + lg
-    int klim[NCT];                                 // keys this lane's column sees (0: padding column)
-    int kmin = 0;                                  // smallest limit of a real column of the unit
-    auto start_unit = [&](int k_unit, int sg) __attribute__((always_inline)) {
-        const int s = unit_seg(sg), h = sg - s * H;
-        const int ncol = ncol_of(s);
-        kmin = seg_s[s][S_KMIN];
-#pragma unroll
-        for (int ct = 0; ct < NCT; ++ct) {
-            const int c = 16 * ct + li;
-            const Col cl = col_of(s, c < ncol ? c : 0);
-            klim[ct] = c < ncol ? min(ent_s[cl.b][E_N0] + cl.tok + 1, ent_s[cl.b][E_KEYS]) : 0;
-        }
-        if (k_unit < QSEG) {
-#pragma unroll
-            for (int ct = 0; ct < NCT; ++ct) {
-                const int c = 16 * ct + li;
-#pragma unroll
-                for (int k = 0; k < NC; ++k) {
-                    const u32x4 v = qcache[(k_unit * NCOL + c) * NCH + 4 * k + lg];
-                    qb[ct][k] = __builtin_bit_cast(bf16x8_t, c < ncol ? v : u32x4{0u, 0u, 0u, 0u});
-                }
-            }
-        } else {
-#pragma unroll
-            for (int ct = 0; ct < NCT; ++ct) {
-                const int c = 16 * ct + li;
-                const u32x4* qg = reinterpret_cast<const u32x4*>(q_row(col_of(s, c < ncol ? c : 0), h));
-#pragma unroll
-                for (int k = 0; k < NC; ++k) {
-                    const u32x4 v = qg[4 * k + lg];
-                    qb[ct][k] = __builtin_bit_cast(bf16x8_t, c < ncol ? v : u32x4{0u, 0u, 0u, 0u});
-                }
-            }
-            wait_vmcnt<0>();                       // drains the ring: only past the cached units
-        }
-    };
-
-    f32x4_t acc[NCT][NDT];
-    float m_ref[NCT], l_part[NCT];
-    auto reset = [&]() __attribute__((always_inline)) {
-#pragma unroll
-        for (int ct = 0; ct < NCT; ++ct) {
-            m_ref[ct] = -INFINITY;
-            l_part[ct] = 0.f;
-#pragma unroll
-            for (int dt = 0; dt < NDT; ++dt) acc[ct][dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-        }
-    };
-
-    // the staged new-token rows into their pages (nothing in this launch reads
-    // them from memory: the stream patched them into its stages)
-    auto store_rows = [&]() __attribute__((always_inline)) {
-        const int q = tid / PCH, pl = (tid / NCH) & 1, x = tid % NCH;
-        if (q < npatch) {
-            const int pe = patch_s[q];
-            const int sl = pinfo[pe & 0xfff].x, r = (pe >> 21) & 63;
-            if (sl >= 0)
-                *reinterpret_cast<u32x4*>((pl ? vplane_w : kplane_w) + size_t(sl) * SLICE_BYTES + r * NCH * 16 + x * 16) =
-                    pstage[tid];
-        }
-    };
-
-    // unit end: merge the four waves' states through stage st (waves 0-1
-    // use its K slice, waves 2-3 its V slice), one column tile at a time
-    auto finish_unit = [&](int st) __attribute__((always_inline)) {
-        auto wbuf = [&](int v) __attribute__((always_inline)) {
-            return reinterpret_cast<float*>(&ring[v >> 1][st][0]) + (v & 1) * WBUF;
-        };
-        f32x4_t merged[NCT][DPW];
-        float mxs[NCT], lts[NCT];
-#pragma unroll
-        for (int ct = 0; ct < NCT; ++ct) {
-            const float lw = rows_sum(l_part[ct]);
-            block_lds_barrier();                   // every wave is done with stage st (or the last round)
-            float* mine = wbuf(w);
-#pragma unroll
-            for (int dt = 0; dt < NDT; ++dt)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) mine[(dt * 4 + r) * 64 + lane] = acc[ct][dt][r];
-            if (lg == 0) {
-                mlbuf[w][li][0] = m_ref[ct];
-                mlbuf[w][li][1] = lw;
-            }
-            block_lds_barrier();
-            float mw[4], cw[4], mx = -INFINITY, lt = 0.f;
-#pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                mw[v] = mlbuf[v][li][0];
-                mx = fmaxf(mx, mw[v]);
-            }
-#pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                cw[v] = mw[v] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mw[v] - mx);
-                lt += mlbuf[v][li][1] * cw[v];
-            }
-#pragma unroll
-            for (int kk = 0; kk < DPW; ++kk) {
-                const int dt = w * DPW + kk;
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    float x = 0.f;
-#pragma unroll
-                    for (int v = 0; v < 4; ++v) x += wbuf(v)[(dt * 4 + r) * 64 + lane] * cw[v];
-                    merged[ct][kk][r] = x;
-                }
-            }
-            mxs[ct] = mx;
-            lts[ct] = lt;
-        }
-        // write: a column whose (entry, KV head) has no other piece is
-        // normalized into out; the others go to slot i + sigma for the
-        // combine launch.  Nothing waits for these stores: the ring's waits
-        // (one in-order vector-memory counter) cover them with a few
-        // operations to spare, and the combine is a later launch.
-        const int s = unit_seg(sig), h = sig - s * H;
-        const int ncol = ncol_of(s);
-#pragma unroll
-        for (int ct = 0; ct < NCT; ++ct) {
-            const int c = 16 * ct + li;
-            if (c >= ncol) continue;
-            const Col cl = col_of(s, c);
-            if (exp_s[cl.b * H + h] == 1) {
-                const float inv = lts[ct] > 0.f ? 1.f / lts[ct] : 0.f;
-                float* o = a.out + (size_t(ent_s[cl.b][E_CU] + cl.tok) * a.Hq + size_t(h) * GQ + cl.j) * D + 4 * lg;
-#pragma unroll
-                for (int kk = 0; kk < DPW; ++kk) {
-                    const f32x4_t v = merged[ct][kk] * inv;
-                    *reinterpret_cast<float4*>(o + 16 * (w * DPW + kk)) = make_float4(v[0], v[1], v[2], v[3]);
-                }
-            } else {
-                const size_t it = size_t(i_blk + sig) * NCOL + c;
-                float* o = a.part_acc + it * D + 4 * lg;
-#pragma unroll
-                for (int kk = 0; kk < DPW; ++kk)
-                    *reinterpret_cast<float4*>(o + 16 * (w * DPW + kk)) =
-                        make_float4(merged[ct][kk][0], merged[ct][kk][1], merged[ct][kk][2], merged[ct][kk][3]);
-                if (w == 0 && lg == 0) *reinterpret_cast<float2*>(a.part_ml + it * 2) = make_float2(mxs[ct], lts[ct]);
-            }
-        }
-        reset();
-    };
-
-    reset();
-    const int tb = 16 * w + 4 * lg;                 // token of accumulator register r: tb + r
-    int meta_ring[NS];                              // meta of the pages in the ring, by stage
-#pragma unroll
-    for (int k = 0; k < NS - 1; ++k) {
-        if (k < npg) {
-            fetch(k, k);
-            meta_ring[k] = meta_of(k);
-        } else {
-            meta_ring[k] = 0;
-        }
-    }
-    meta_ring[NS - 1] = 0;
-    // the query cache and the first page have landed (loads complete in order)
-    if (npg >= NS - 1) wait_vmcnt<LOADS_PER_PAGE * (NS - 2)>();
-    else wait_vmcnt<0>();
-    block_lds_barrier();
-    int unit_k = 0;
-    start_unit(unit_k, sig);
-
-    // one page in stage J (compile time, so every LDS offset is an immediate)
-    auto step = [&](auto jc, int i) __attribute__((always_inline)) {
-        constexpr int J = decltype(jc)::value;
-        constexpr int FS = (J + NS - 1) % NS;
-        // page i is in stage J for every wave, and every wave is done with
-        // page i-1, whose stage takes page i+NS-1; the last NS-1 pages of
-        // the range wait for everything in flight (nothing is left to issue)
-        if (i + NS - 1 < npg) {
-            wait_vmcnt<LOADS_PER_PAGE * (NS - 2)>();
-            block_lds_barrier();
-            fetch(i + NS - 1, FS);
-            meta_ring[FS] = meta_of(i + NS - 1);
-        } else {
-            wait_vmcnt<0>();
-            block_lds_barrier();
-        }
-
-        const int meta = meta_ring[J];
-        if (append && (meta & kPatchBit)) {
-            // an entry's new token lies in this page: its row goes into the
-            // stage from the staged copy (or, past the staged ones, from
-            // memory, which drains the ring once)
-            const int s = unit_seg(sig), h = sig - s * H, p = (meta >> 9) & 0x7fff;
-            const int mask = seg_s[s][S_MASK];
-#pragma unroll 1
-            for (int b = 0; b < kMaxEnt; ++b) {
-                const int keys = ent_s[b][E_KEYS];
-                if (!((mask >> b) & 1) || keys <= 0 || ((keys - 1) >> kPageShift) != p) continue;
-                const int r = (keys - 1) & 63;
-                int q = -1;
-                for (int k = 0; k < npatch; ++k) {
-                    const int pe = patch_s[k];
-                    if ((pe & 0xfff) == i && ((pe >> 12) & 7) == b) q = k;
-                }
-                if (tid < PCH) {
-                    const int pl = tid / NCH, x = tid % NCH;
-                    u32x4 v;
-                    if (q >= 0) {
-                        v = pstage[q * PCH + tid];
-                    } else {
-                        v = reinterpret_cast<const u32x4*>((pl ? a.v_new : a.k_new) + (size_t(b) * H + h) * D)[x];
-                        const int sl = pinfo[i].x;
-                        if (sl >= 0)
-                            *reinterpret_cast<u32x4*>((pl ? vplane_w : kplane_w) + size_t(sl) * SLICE_BYTES +
-                                                      r * NCH * 16 + x * 16) = v;
-                    }
-                    ring[pl][J][r * NCH + (x ^ (pl ? vswz(r) : kswz(r)))] = v;
-                }
-            }
-            block_lds_barrier();
-        }
-        const int lim = meta & 255;                 // rows any column of the unit may see
-        if (lim > 16 * w) {                         // this wave has such rows in the page
-            const int tok0 = ((meta >> 9) & 0x7fff) * kPage;   // first key of the page
-            const u32x4* kst = &ring[0][J][0];
-            f32x4_t s[NCT];
-#pragma unroll
-            for (int ct = 0; ct < NCT; ++ct) s[ct] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int c = 0; c < NC; ++c) {
-                const bf16x8_t kk = __builtin_bit_cast(bf16x8_t, kst[koff[c]]);
-#pragma unroll
-                for (int ct = 0; ct < NCT; ++ct)
-                    s[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kk, qb[ct][c], s[ct], 0, 0, 0);
-            }
-            const bool masked = tok0 + kPage > kmin;   // a real column's limit falls inside the page
-            s16x4_t phi[NCT], plo[NCT];
-#pragma unroll
-            for (int ct = 0; ct < NCT; ++ct) {
-                float sj[4];
-#pragma unroll
-                for (int r = 0; r < 4; ++r) sj[r] = s[ct][r] * a.scale_log2;
-                if (masked) {
-#pragma unroll
-                    for (int r = 0; r < 4; ++r)
-                        if (tok0 + tb + r >= klim[ct]) sj[r] = -INFINITY;
-                }
-                const float pm = rows_max(fmaxf(fmaxf(sj[0], sj[1]), fmaxf(sj[2], sj[3])));
-                if (__builtin_amdgcn_ballot_w64(pm > m_ref[ct] + kRescaleLog2)) {
-                    const float mn = pm > m_ref[ct] + kRescaleLog2 ? pm : m_ref[ct];
-                    const float alpha = m_ref[ct] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_ref[ct] - mn);
-                    l_part[ct] *= alpha;
-#pragma unroll
-                    for (int dt = 0; dt < NDT; ++dt) acc[ct][dt] *= alpha;
-                    m_ref[ct] = mn;
-                }
-                float p[4];
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    p[r] = __builtin_amdgcn_exp2f(sj[r] - m_ref[ct]);
-                    // a column with no visible key in this wave yet has no reference
-                    p[r] = m_ref[ct] == -INFINITY ? 0.f : p[r];
-                }
-                l_part[ct] += (p[0] + p[1]) + (p[2] + p[3]);
-                uint32_t h01, l01, h23, l23;
-                split_bf16(p[0], p[1], h01, l01);
-                split_bf16(p[2], p[3], h23, l23);
-                phi[ct] = __builtin_bit_cast(s16x4_t, u32x2{h01, h23});
-                plo[ct] = __builtin_bit_cast(s16x4_t, u32x2{l01, l23});
-            }
-            if (lim < kPage) {
-                // rows past the last limit hold stale bytes (possibly NaN):
-                // this wave clears its own rows of the V slice, which only it
-                // reads
-                const int r0 = max(lim, 16 * w), rows = 16 * w + 16 - r0;
-                u32x4* vrows = &ring[1][J][r0 * NCH];
-                for (int x = lane; x < rows * NCH; x += 64) vrows[x] = u32x4{0u, 0u, 0u, 0u};
-                wave_lds_sync();
-            }
-            const lds_byte_ptr vst = (lds_byte_ptr)(&ring[0][J][0]);   // voff includes the K-to-V distance
-#pragma unroll
-            for (int dt = 0; dt < NDT; ++dt) {
-                const s16x4_t va = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_ptr)(vst + voff[dt]));
-#pragma unroll
-                for (int ct = 0; ct < NCT; ++ct) {
-                    acc[ct][dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, phi[ct], acc[ct][dt], 0, 0, 0);
-                    acc[ct][dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, plo[ct], acc[ct][dt], 0, 0, 0);
-                }
-            }
-        }
-
-        if (meta & 256) {
-            finish_unit(J);
-            if (i + 1 < npg) {
-                ++sig;
-                ++unit_k;
-                start_unit(unit_k, sig);
-            }
-        }
-    };
-
-    for (int i0 = 0; i0 < npg; i0 += NS) {
-        step(std::integral_constant<int, 0>{}, i0);
-        if (i0 + 1 < npg) step(std::integral_constant<int, 1>{}, i0 + 1);
-        if (i0 + 2 < npg) step(std::integral_constant<int, 2>{}, i0 + 2);
-        if (i0 + 3 < npg) step(std::integral_constant<int, 3>{}, i0 + 3);
-        if constexpr (NS == 8) {
-            if (i0 + 4 < npg) step(std::integral_constant<int, 4>{}, i0 + 4);
-            if (i0 + 5 < npg) step(std::integral_constant<int, 5>{}, i0 + 5);
-            if (i0 + 6 < npg) step(std::integral_constant<int, 6>{}, i0 + 6);
-            if (i0 + 7 < npg) step(std::integral_constant<int, 7>{}, i0 + 7);
-        }
-    }
-    if (npatch > 0) store_rows();
-}
 
 // Combine the chunks of each (entry, query head) in chunk order.
 template <int D, int GQ>
@@ -1208,33 +699,9 @@ int stream_grid(const PoolView& pv, int B, int max_seq_len, int bpc = 1) {
     return int(need > cus * bpc ? need : cus * bpc);
 }
 
-// BF16 pages take the register-fed stream (two blocks per compute unit)
-// unless KVS_STREAM_RING=1 selects the LDS-ring stream (one block per unit;
-// a tuning knob read once per process).
-bool ring_stream() {
-    static const bool on = [] {
-        const char* e = std::getenv("KVS_STREAM_RING");
-        return e && e[0] == '1';
-    }();
-    return on;
-}
-
-// register-fed stream shape for decode at D = 128 (a tuning knob read once
-// per process): KVS_STREAM_OCC = 10 * blocks per CU + page buffers per wave
-int vstream_occ() {
-    static const int v = [] {
-        const char* e = std::getenv("KVS_STREAM_OCC");
-        const int x = e ? std::atoi(e) : 0;
-        return (x == 22 || x == 23) ? x : 23;
-    }();
-    return v;
-}
-
 // blocks per compute unit of the page stream for these pages
 int stream_bpc(const PoolView& pv) {
-    if (pv.k_codec != CODEC_BF16) return qstream_blocks_per_cu(pv);
-    if (ring_stream()) return 1;
-    return pv.D == 128 ? vstream_occ() / 10 : 2;
+    return pv.k_codec != CODEC_BF16 ? qstream_blocks_per_cu(pv) : 2;
 }
 
 // Shared pages are read once per call unless KVS_STREAM_SHARE=0 (a tuning
@@ -1322,9 +789,7 @@ hipError_t launch_gq(const DecodeArgs& a, bool stream, hipStream_t s) {
     if (stream && a.pv.k_codec != CODEC_BF16) return launch_qstream(a, GQ, s);
     if constexpr (D == 64 || D == 128) {
         if (stream) {
-            if (ring_stream()) paged_stream_kernel<D, GQ, 1, false><<<dim3(unsigned(a.G)), 256, 0, s>>>(a);
-            else if (D != 128 || vstream_occ() == 23) paged_vstream_kernel<D, GQ, 1, false><<<dim3(unsigned(a.G)), 256, 0, s>>>(a);
-            else paged_vstream_kernel<D, GQ, 1, false, 2, 2><<<dim3(unsigned(a.G)), 256, 0, s>>>(a);
+            paged_vstream_kernel<D, GQ, 1, false><<<dim3(unsigned(a.G)), 256, 0, s>>>(a);
             const hipError_t e = hipGetLastError();
             if (e != hipSuccess) return e;
             DecodeArgs c = a;
@@ -1375,8 +840,7 @@ hipError_t launch_chunk_d(const DecodeArgs& a, int gq, int G, hipStream_t s) {
     switch (gq) {
 #define KVS_CHUNK_CASE(GQ)                                                  \
     case GQ:                                                                \
-        if (ring_stream()) paged_stream_kernel<D, GQ, 2, true><<<grid, 256, 0, s>>>(a);   \
-        else paged_vstream_kernel<D, GQ, 2, true><<<grid, 256, 0, s>>>(a); \
+        paged_vstream_kernel<D, GQ, 2, true><<<grid, 256, 0, s>>>(a);      \
         if (hipPeekAtLastError() == hipSuccess)                             \
             stream_combine_kernel<D, GQ, 32><<<cgrid, 64, 0, s>>>(c);       \
         break;
