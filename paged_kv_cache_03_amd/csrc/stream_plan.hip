@@ -7,12 +7,16 @@
 // (the op chooses its own split; pages are read in place through the table).
 //
 // Every block of the launch derives the same entry, sharing and segment
-// tables (one lane per entry of wave 0), then writes its share of the page
-// list: stream positions [k * kPlanSpan, (k + 1) * kPlanSpan).  Block 0 also
-// writes the header, the tables, the per-(entry, KV head) piece counts, the
-// per-block ranges and the combine tasks with their piece lists.  Shared runs are found by comparing table
-// entries, so a plan is exact for any table: two entries read a page once
-// only where both rows hold the same mapped page group.
+// tables (one lane per entry of wave 0), then does one job: block k < nspan
+// writes its share of the page list (stream positions [k * kPlanSpan,
+// (k + 1) * kPlanSpan)); three more blocks write, in parallel, the header,
+// tables and piece counts; the combine tasks with their piece lists; the
+// new-token lists and the per-block ranges.  Shared runs
+// are found by comparing table entries, so a plan is exact for any table: two
+// entries read a page once only where both rows hold the same mapped page
+// group.  The kernel reads only its inputs from global memory and never reads
+// back what it writes, so its barriers order LDS traffic only (they do not
+// wait for the plan's stores to land).
 
 #include <hip/hip_runtime.h>
 
@@ -40,11 +44,27 @@ struct PlanArgs {
     const int32_t* cu_q;      // chunk mode
     int32_t B, gq, max_ctx, max_cols, G, qcap, chunk, emax, pages;
     int32_t D, ncol;          // head dim, partial slot width (columns)
+    int32_t nspan;            // blocks that write the page list
     int32_t* plan;
 };
 
-// floor(x / q) for 0 <= x, 0 < q
-__device__ __forceinline__ int pieces(int start, int n, int Q) { return n > 0 ? (start + n - 1) / Q - start / Q + 1 : 0; }
+// floor(x / q) for 0 <= x < 2^24 and 0 < q < 2^24 through the fp32
+// reciprocal, corrected to the exact quotient (an integer division is a long
+// instruction sequence on these parts)
+struct Div {
+    int q;
+    float rq;
+    __device__ __forceinline__ explicit Div(int q_) : q(q_ > 0 ? q_ : 1), rq(1.0f / float(q_ > 0 ? q_ : 1)) {}
+    __device__ __forceinline__ int operator()(int x) const {
+        int d = int(float(x) * rq);
+        d -= (d * q > x) ? 1 : 0;
+        d += ((d + 1) * q <= x) ? 1 : 0;
+        return d;
+    }
+};
+
+// blocks (of Q positions each) that stream positions [start, start + n) touch
+__device__ __forceinline__ int pieces(int start, int n, const Div& dq) { return n > 0 ? dq(start + n - 1) - dq(start) + 1 : 0; }
 
 __global__ void __launch_bounds__(kNT) stream_plan_kernel(PlanArgs a) {
     __shared__ int ent[kMaxEnt][kEntWords];
@@ -90,7 +110,7 @@ __global__ void __launch_bounds__(kNT) stream_plan_kernel(PlanArgs a) {
         ent[b][E_OWNED] = owned;
         ent[b][7] = 0;
     }
-    __syncthreads();
+    block_lds_barrier();
 
     // shared leading runs: pairs whose first pages agree are compared page by
     // page; the first mismatch (or unmapped page) ends the run
@@ -104,21 +124,30 @@ __global__ void __launch_bounds__(kNT) stream_plan_kernel(PlanArgs a) {
             }
             lcp[i][j] = v;
         }
-        __syncthreads();
-        if (tid == 0) {
-            int n = 0, pre = 0;
-            for (int i = 1; i < kMaxEnt; ++i)
-                for (int j = 0; j < i; ++j)
-                    if (lcp[i][j] > 1) {
-                        cand[n] = i << 3 | j;
-                        cpre[n] = pre;
-                        pre += lcp[i][j] - 1;
-                        ++n;
-                    }
-            cpre[n] = pre;
-            ncand_s = n;
+        block_lds_barrier();
+        if (tid < 64) {                            // wave 0, lane i*8 + j: pair (i, j), j < i, in that order
+            const int i = tid >> 3, j = tid & 7;
+            const int c = (j < i && lcp[i][j] > 1) ? 1 : 0;
+            const int len = c ? lcp[i][j] - 1 : 0;
+            int pc = c, pl = len;                  // inclusive prefix sums over the lanes
+#pragma unroll
+            for (int d = 1; d < 64; d <<= 1) {
+                const int c1 = __shfl_up(pc, d), l1 = __shfl_up(pl, d);
+                if (tid >= d) {
+                    pc += c1;
+                    pl += l1;
+                }
+            }
+            if (c) {
+                cand[pc - 1] = i << 3 | j;
+                cpre[pc - 1] = pl - len;
+            }
+            if (tid == 63) {
+                cpre[pc] = pl;
+                ncand_s = pc;
+            }
         }
-        __syncthreads();
+        block_lds_barrier();
         const int n = ncand_s, tot = cpre[n];
         for (int base = tid; base < tot; base += kNT * 8) {
             int gi[8], gj[8], pr[8], pp[8];
@@ -141,7 +170,7 @@ __global__ void __launch_bounds__(kNT) stream_plan_kernel(PlanArgs a) {
                 if (pr[k] >= 0 && (gi[k] != gj[k] || gi[k] < 0 || gi[k] >= a.M))
                     atomicMin(&lcp[pr[k] >> 3][pr[k] & 7], pp[k]);
         }
-        __syncthreads();
+        block_lds_barrier();
     }
 
     // sharing trees and segments: wave 0, lane = entry (B <= 8)
@@ -266,21 +295,36 @@ __global__ void __launch_bounds__(kNT) stream_plan_kernel(PlanArgs a) {
             res_s[2] = pages_all * H;
         }
     }
-    __syncthreads();
+    block_lds_barrier();
 
     const int nseg = res_s[0], total = res_s[2];
     const int Q = total > 0 ? (total + a.G - 1) / a.G : 0;
+    const Div dq(Q);
     // unit (segment s, head h) and page within it of stream position u
     auto locate = [&](int u, int& s, int& h, int& pp) __attribute__((always_inline)) {
-        s = 0;
-        while (s + 1 < nseg && seg[s + 1][S_PRE] <= u) ++s;
+        s = 0;                                     // binary search: last segment with S_PRE <= u
+#pragma unroll
+        for (int step = kMaxSeg / 2; step > 0; step >>= 1)
+            if (s + step < nseg && seg[s + step][S_PRE] <= u) s += step;
         const int off = u - seg[s][S_PRE], n = seg[s][S_N];
-        h = off / n;
+        h = Div(n)(off);
         pp = off - h * n;
     };
 
     int32_t* P = a.plan;
-    if (blockIdx.x == 0) {
+    // Roles: blocks [0, nspan) write the page list (span blockIdx.x); block
+    // nspan the header, the entry and segment tables and the piece counts;
+    // nspan + 1 the combine tasks; nspan + 2 the new-token lists and the
+    // per-block ranges.  Without a page list one block writes the tables.
+    const int role = a.pages ? int(blockIdx.x) - a.nspan : 0;
+    auto count_pieces = [&](int x) __attribute__((always_inline)) {   // pieces (block, unit) carrying (entry, head) x
+        const int b = x / H, h = x - b * H;
+        int e = 0;
+        for (int s = 0; s < nseg; ++s)
+            if ((seg[s][S_MASK] >> b) & 1) e += pieces(seg[s][S_PRE] + h * seg[s][S_N], seg[s][S_N], dq);
+        return e;
+    };
+    if (role == 0) {
         if (tid < H_WORDS) {
             int v = 0;
             switch (tid) {
@@ -302,52 +346,21 @@ __global__ void __launch_bounds__(kNT) stream_plan_kernel(PlanArgs a) {
         if (tid < kMaxEnt * kEntWords) P[kOffEnt + tid] = ent[tid / kEntWords][tid % kEntWords];
         if (tid < kMaxSeg * kSegWords)
             P[kOffSeg + tid] = tid / kSegWords < nseg ? seg[tid / kSegWords][tid % kSegWords] : 0;
-        if (a.pages) {
-            // pieces (block, unit) that carry each (entry, KV head)
-            for (int x = tid; x < kMaxEnt * H; x += kNT) {
-                const int b = x / H, h = x - b * H;
-                int e = 0;
-                for (int s = 0; s < nseg; ++s)
-                    if ((seg[s][S_MASK] >> b) & 1) e += pieces(seg[s][S_PRE] + h * seg[s][S_N], seg[s][S_N], Q);
-                P[kOffExp + x] = e;
-                ex[x] = e;
-            }
-            // decode: the block that streams the page with an entry's new token
-            // (position keys - 1) at head h lists (page, entry, head, row)
-            const int maxp = min(kMaxPatch, 1024 / a.D);
-            for (int i = tid; i < a.G; i += kNT) pcnt[i] = 0;
-            __syncthreads();
-            if (!a.chunk) {
-                int* plist = P + off_patch(H, a.G);
-                for (int x = tid; x < a.B * H; x += kNT) {
-                    const int b = x / H, h = x - b * H, keys = ent[b][E_KEYS];
-                    if (ent[b][E_NPAGES] == 0) continue;
-                    const int p = (keys - 1) >> kPageShift;
-                    for (int s = 0; s < nseg; ++s) {
-                        if (!((seg[s][S_MASK] >> b) & 1) || p < seg[s][S_P0] || p >= seg[s][S_P0] + seg[s][S_N])
-                            continue;
-                        const int u = seg[s][S_PRE] + h * seg[s][S_N] + (p - seg[s][S_P0]);
-                        const int i = u / Q, o = u - i * Q;
-                        const int k = atomicAdd(&pcnt[i], 1);
-                        if (k < maxp) plist[size_t(i) * kMaxPatch + k] = o | (b << 12) | (h << 15) | (((keys - 1) & 63) << 21);
-                        break;
-                    }
-                }
-                __syncthreads();
-            }
-            int4* blk = reinterpret_cast<int4*>(P + off_blk(H));
-            for (int i = tid; i < a.G; i += kNT) {
-                const int u0 = i * Q;
-                const int npg = Q > 0 ? max(0, min(Q, total - u0)) : 0;
-                int s = 0, h = 0, pp = 0;
-                if (npg > 0) locate(u0, s, h, pp);
-                blk[i] = make_int4(npg, s * H + h, min(pcnt[i], maxp), 0);
-            }
-        }
-        __syncthreads();
-        if (tid < 64) {                            // wave 0: combine tasks, pairs with more than one piece
+        if (a.pages)
+            for (int x = tid; x < kMaxEnt * H; x += kNT) P[kOffExp + x] = count_pieces(x);
+        if (!a.pages && tid == 0) P[H_NTASK] = 0;
+        return;
+    }
+    if (role == 1) {
+        // combine tasks: (entry, KV head) pairs with more than one piece, in
+        // pair order; a task lists its pieces in unit order, each unit's
+        // slots in block order
+        __shared__ int tpair[kMaxEnt * kMaxH], tpoff[kMaxEnt * kMaxH], ntask_s;
+        for (int x = tid; x < kMaxEnt * H; x += kNT) ex[x] = x < a.B * H ? count_pieces(x) : 0;
+        block_lds_barrier();
+        if (tid < 64) {                            // wave 0: task numbers and overflow offsets
             const int lane = tid;
-            const int n = a.pages ? a.B * H : 0, per = (n + 63) / 64;
+            const int n = a.B * H, per = (n + 63) / 64;
             int cnt = 0, over = 0;
             for (int i = 0; i < per; ++i) {
                 const int x = lane * per + i;
@@ -368,38 +381,87 @@ __global__ void __launch_bounds__(kNT) stream_plan_kernel(PlanArgs a) {
             const int ntask = __builtin_amdgcn_readlane(tb, 63);
             tb -= cnt;
             ob -= over;
-            int* over_list = P + off_over(H, a.G);
             for (int i = 0; i < per; ++i) {
                 const int x = lane * per + i;
                 if (x >= n || ex[x] <= 1) continue;
-                const int b = x / H, h = x - b * H, E = ex[x];
+                const int b = x / H, h = x - b * H;
                 int* rec = P + off_tasks(H, a.G) + size_t(tb) * kTaskWords;
                 rec[T_B] = b;
                 rec[T_H] = h;
-                rec[T_E] = E;
+                rec[T_E] = ex[x];
                 rec[T_OUT] = (ent[b][E_CU] * H * a.gq + h * a.gq) * a.D;
                 rec[T_NCOL] = ent[b][E_T] * a.gq;
                 rec[T_POFF] = ob;
-                int k = 0;
-                for (int s = 0; s < nseg; ++s) {
-                    const int mask = seg[s][S_MASK];
-                    if (!((mask >> b) & 1)) continue;
-                    const int ns = seg[s][S_N], start = seg[s][S_PRE] + h * ns;
-                    const int f = start / Q, nsl = (start + ns - 1) / Q - f + 1;
-                    const int colb = __builtin_popcount(unsigned(mask) & ((1u << b) - 1u)) * seg[s][S_W];
-                    for (int j = 0; j < nsl; ++j, ++k) {
-                        const int v = (f + j + s * H + h) * a.ncol + colb;
-                        if (k < kTaskInline) rec[T_PIECE + k] = v;
-                        else over_list[ob + k - kTaskInline] = v;
-                    }
-                }
+                tpair[tb] = x;
+                tpoff[tb] = ob;
                 ++tb;
-                ob += max(0, E - kTaskInline);
+                ob += max(0, ex[x] - kTaskInline);
             }
-            if (lane == 0) P[H_NTASK] = ntask;
+            if (lane == 0) {
+                P[H_NTASK] = ntask;
+                ntask_s = ntask;
+            }
         }
+        block_lds_barrier();
+        // piece lists: one thread per (task, segment) pair writes the pieces
+        // of that segment's unit, after those of the task's earlier segments
+        const int ntask = ntask_s;
+        int* over_list = P + off_over(H, a.G);
+        for (int y = tid; y < ntask * nseg; y += kNT) {
+            const int t = y / nseg, s = y - t * nseg;
+            const int x = tpair[t], b = x / H, h = x - b * H;
+            const int mask = seg[s][S_MASK];
+            if (!((mask >> b) & 1)) continue;
+            int k = 0;                             // pieces of the earlier segments
+            for (int s2 = 0; s2 < s; ++s2)
+                if ((seg[s2][S_MASK] >> b) & 1) k += pieces(seg[s2][S_PRE] + h * seg[s2][S_N], seg[s2][S_N], dq);
+            const int ns = seg[s][S_N], start = seg[s][S_PRE] + h * ns;
+            const int f = dq(start), nsl = dq(start + ns - 1) - f + 1;
+            const int colb = __builtin_popcount(unsigned(mask) & ((1u << b) - 1u)) * seg[s][S_W];
+            int* rec = P + off_tasks(H, a.G) + size_t(t) * kTaskWords;
+            const int ob = tpoff[t];
+            for (int j = 0; j < nsl; ++j, ++k) {
+                const int v = (f + j + s * H + h) * a.ncol + colb;
+                if (k < kTaskInline) rec[T_PIECE + k] = v;
+                else over_list[ob + k - kTaskInline] = v;
+            }
+        }
+        return;
     }
-    if (!a.pages) return;
+    if (role == 2) {
+        // decode: the block that streams the page with an entry's new token
+        // (position keys - 1) at head h lists (page, entry, head, row)
+        const int maxp = min(kMaxPatch, 1024 / a.D);
+        for (int i = tid; i < a.G; i += kNT) pcnt[i] = 0;
+        block_lds_barrier();
+        if (!a.chunk) {
+            int* plist = P + off_patch(H, a.G);
+            for (int x = tid; x < a.B * H; x += kNT) {
+                const int b = x / H, h = x - b * H, keys = ent[b][E_KEYS];
+                if (ent[b][E_NPAGES] == 0) continue;
+                const int p = (keys - 1) >> kPageShift;
+                for (int s = 0; s < nseg; ++s) {
+                    if (!((seg[s][S_MASK] >> b) & 1) || p < seg[s][S_P0] || p >= seg[s][S_P0] + seg[s][S_N])
+                        continue;
+                    const int u = seg[s][S_PRE] + h * seg[s][S_N] + (p - seg[s][S_P0]);
+                    const int i = dq(u), o = u - i * Q;
+                    const int k = atomicAdd(&pcnt[i], 1);
+                    if (k < maxp) plist[size_t(i) * kMaxPatch + k] = o | (b << 12) | (h << 15) | (((keys - 1) & 63) << 21);
+                    break;
+                }
+            }
+            block_lds_barrier();
+        }
+        int4* blk = reinterpret_cast<int4*>(P + off_blk(H));
+        for (int i = tid; i < a.G; i += kNT) {
+            const int u0 = i * Q;
+            const int npg = Q > 0 ? max(0, min(Q, total - u0)) : 0;
+            int s = 0, h = 0, pp = 0;
+            if (npg > 0) locate(u0, s, h, pp);
+            blk[i] = make_int4(npg, s * H + h, min(pcnt[i], maxp), 0);
+        }
+        return;
+    }
 
     // page list: this block's span of stream positions, four per thread with
     // the table reads issued together
@@ -427,7 +489,7 @@ __global__ void __launch_bounds__(kNT) stream_plan_kernel(PlanArgs a) {
                             patch = kPatchBit;
                 }
                 meta[k] = lim | (pp == seg[s][S_N] - 1 ? 256 : 0) | (p << 9) | patch;
-                const int i = u / Q;
+                const int i = dq(u);
                 dst[k] = i * a.qcap + (u - i * Q);
             }
         }
@@ -471,8 +533,8 @@ hipError_t launch_stream_plan(const PoolView& pv, int B, int gq, const int32_t* 
     a.ncol = chunk ? 32 : 16;
     a.plan = plan;
     const long long bound = (long long)B * pv.H * ((max_seq_len + kPage - 1) / kPage);
-    const int blocks = pages ? stream_plan_blocks(int(bound)) : 1;
-    stream_plan_kernel<<<dim3(unsigned(blocks)), kNT, 0, s>>>(a);
+    a.nspan = pages ? stream_plan_blocks(int(bound)) : 0;
+    stream_plan_kernel<<<dim3(unsigned(pages ? a.nspan + 3 : 1)), kNT, 0, s>>>(a);
     return hipGetLastError();
 }
 
