@@ -7,14 +7,16 @@
 // tile/split/wave/LDS scheme).
 //
 // It runs the same plan (stream_plan.hip), work split, online softmax, unit
-// merge and combine as the BF16 page stream of decode.hip; what differs is
-// how a page reaches the matrix cores.  A ring stage holds one page's raw
-// planes -- K codes, V codes, K scales, V scales -- brought in by
-// direct-to-LDS loads, and the codes become bf16 operands in registers:
+// merge and combine as the BF16 page stream of decode.hip, register-fed the
+// same way: wave w of each of two blocks per compute unit loads the codes and
+// scales of its 16 keys of every page straight into registers, one page
+// ahead, through buffer loads whose range ends at the page's last visible row
+// (codes and scales past it read as zeros, so stale bytes never reach the
+// products).  What differs is how the codes become matrix-core operands:
 //  * every code value is exact in bf16 (int8 in [-127, 127]; e4m3 has 4
 //    significant bits; e2m1 2), and so is an e2m1 value times its e4m3 group
 //    scale (at most 6 significant bits, inside bf16's exponent range), so
-//    NVFP4 pages are dequantized in full before the products;
+//    NVFP4 sides are dequantized in full before the products;
 //  * INT8-G64 and FP8-row scales are fp32 and do not fold into a bf16
 //    operand exactly, so they act on fp32 values: K scales multiply each
 //    key's per-group partial scores, V scales multiply the key's probability
@@ -23,14 +25,11 @@
 //  * PV runs V^T . [P_hi; P_lo] as one k=32 product per 16-dim tile: the
 //    lane's four keys appear twice in the V^T operand, once against P_hi,
 //    once against P_lo;
-//  * a V^T operand comes from four row reads per lane (the four keys whose
-//    probabilities the lane holds); packing the fp32 values of two keys into
-//    one bf16 pair is the transpose.  Row m of tile j then holds head dim
+//  * a V^T operand comes from the lane's row loads of the four keys whose
+//    probabilities it holds; packing the fp32 values of two keys into one
+//    bf16 pair is the transpose.  Row m of tile j then holds head dim
 //    64(j/4) + 4m + j%4 for INT8-G64 V (a tile stays in one scale group) and
 //    (D/16) m + j for the others.
-// Keys of a wave's 16-row band enter the score tile in the order
-// 4(m%4) + m/4 (row m), so that the four keys a V read touches at once are
-// consecutive rows, which the stage layout puts in different LDS banks.
 
 #include <hip/hip_runtime.h>
 
@@ -55,39 +54,11 @@ struct QRow {
     static constexpr int scale = C == CODEC_INT8_G64 ? 4 * (D / 64) : (C == CODEC_FP8_ROW ? 4 : D / 16);
 };
 
-// Blocks per compute unit: two for D <= 128 (two waves per SIMD hide each
-// other's LDS and matrix-core latencies; each block gets half of the LDS and
-// at most 256 registers per lane), one for D = 256 (its registers do not fit
-// twice).
-template <int D>
-constexpr int qstream_bpc() { return D <= 128 ? 2 : 1; }
-
-// LDS ring of the quantized stream: stage = [K codes | V codes | K scales |
-// V scales], at least 16 KiB (the unit merge passes through one stage)
-template <int KC, int VC, int D, int BPC>
-struct QRing {
-    static constexpr int KCB = 64 * QRow<KC, D>::code;
-    static constexpr int VCB = 64 * QRow<VC, D>::code;
-    static constexpr int KSB = 64 * QRow<KC, D>::scale;
-    static constexpr int VSB = 64 * QRow<VC, D>::scale;
-    static constexpr int OFF_V = KCB, OFF_KS = KCB + VCB, OFF_VS = OFF_KS + KSB;
-    static constexpr int DATA = OFF_VS + VSB;
-    static constexpr int MERGE = 4 * 16 * 64 * 4;          // four waves x four tiles of accumulators
-    static constexpr int STRIDE = DATA > MERGE ? DATA : MERGE;
-    static constexpr int KL = KCB / 4096, VL = VCB / 4096; // 16-byte loads per thread and page
-    static constexpr int SCW = (KSB + VSB) / 64;           // scale chunks per wave and page
-    static constexpr int LPP = KL + VL + 1;                // loads per wave and page
-    static constexpr int LDS = 163840 / BPC;                // the block's share of the compute unit's LDS
-    static constexpr int FIXED = (8192 + 16384) / BPC + 4096;   // page list, query cache, tables (upper bound)
-    static constexpr int NS_LDS = (LDS - FIXED) / STRIDE;
-    static constexpr int NS = NS_LDS > 8 ? 8 : NS_LDS;     // ring stages
-};
-
-typedef const uint8_t __attribute__((address_space(3)))* lds_cu8;
-typedef const uint32_t __attribute__((address_space(3)))* lds_cu32;
-typedef const u32x2 __attribute__((address_space(3)))* lds_cu32x2;
-typedef const u32x4 __attribute__((address_space(3)))* lds_cu32x4;
-typedef const float __attribute__((address_space(3)))* lds_cf32;
+// Blocks per compute unit: two (two waves per SIMD hide each other's
+// latencies; at most 256 registers per lane), one for INT8-G64 at D = 256
+// (its registers do not fit twice).
+template <int D, int KC>
+constexpr int qstream_bpc() { return (D == 256 && KC == CODEC_INT8_G64) ? 1 : 2; }
 
 __device__ __forceinline__ uint32_t pk_bf16(float a, float b) {
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{a, b}, bf16x2v_t));
@@ -117,44 +88,41 @@ __device__ __forceinline__ f32x2_t fp8_pair(uint32_t w, int h) {
 }
 
 template <int D, int KC, int VC>
-__global__ void __launch_bounds__(256, qstream_bpc<D>()) paged_qstream_kernel(DecodeArgs a) {
+__global__ void __launch_bounds__(256, (qstream_bpc<D, KC>())) paged_qstream_kernel(DecodeArgs a) {
     using namespace plan;
-    constexpr int BPC = qstream_bpc<D>();
-    using R = QRing<KC, VC, D, BPC>;
+    constexpr int BPC = qstream_bpc<D, KC>();
     constexpr int NT = 256;
-    constexpr int NS = R::NS;
-    constexpr int STRIDE = R::STRIDE;
-    constexpr int LPP = R::LPP;
     constexpr int NCH = D / 8;                     // 16-byte chunks of a bf16 query row
-    constexpr int NU = D / 64;                     // 64-dim groups: K reads of 16 dims per lane
+    constexpr int NU = D / 64;                     // 64-dim groups: K operand units of 16 dims per lane
     constexpr int NDT = D / 16;                    // PV tiles
     constexpr int NP = NDT / 4;                    // merge passes, four tiles each
     constexpr int NCOL = 16;
-    constexpr int QCHUNKS = 1024 / BPC;            // query cache: 16 KiB / BPC of 16-byte chunks
-    constexpr int PAGES = kStreamPages / BPC;      // most pages a block takes
+    constexpr int QCHUNKS = 1024 / BPC;            // query cache: 16-byte chunks
     constexpr int QSEG = QCHUNKS / (NCOL * NCH);   // units with cached queries
+    constexpr int PAGES = kStreamPages / BPC;      // most pages a block takes
     constexpr int KROW = QRow<KC, D>::code, VROW = QRow<VC, D>::code;
     constexpr int KSROW = QRow<KC, D>::scale, VSROW = QRow<VC, D>::scale;
-    constexpr int KCHR = KROW / 16;                // 16-byte chunks per K code row
-    constexpr bool KI8 = KC == CODEC_INT8_G64, KF8 = KC == CODEC_FP8_ROW;
+    constexpr bool KI8 = KC == CODEC_INT8_G64, KF8 = KC == CODEC_FP8_ROW, KF4 = KC == CODEC_NVFP4_G16;
     constexpr bool VI8 = VC == CODEC_INT8_G64, VF8 = VC == CODEC_FP8_ROW;
     constexpr int NGK = KI8 ? NU : 1;              // score accumulators: one per K scale group
     constexpr int NPV = VI8 ? NU : 1;              // copies of P: one per V scale group
+    constexpr int NKW = KF4 ? 2 : 4;               // K code words per group and lane
+    constexpr int NKS4 = KF4 ? (KSROW + 15) / 16 : (4 * KSROW) / 16;   // 16-byte K scale loads per lane
+    constexpr int NVW = VI8 ? NU : (VF8 ? NDT / 4 : NDT / 8);         // V code words per key and lane
+    constexpr int NVS4 = VI8 ? (4 * VSROW) / 16 : (VF8 ? 1 : 0);      // 16-byte V scale loads per lane
     static_assert(KC != CODEC_BF16 && VC != CODEC_BF16, "quantized sides only");
-    static_assert((D == 64 || D == 128 || D == 256) && R::KL >= 1 && R::VL >= 1, "shape");
-    static_assert(R::SCW >= 1 && R::SCW <= 64 && NS >= 3, "ring shape");
-    static_assert(LPP * (NS - 2) + QCHUNKS / NT < 64, "vmcnt range");
-    static_assert(QSEG >= 1 && QSEG * NCOL * NCH == QCHUNKS, "query cache shape");
+    static_assert(D == 64 || D == 128 || D == 256, "shape");
+    static_assert(NVW >= 1 && NKS4 >= 1 && (VI8 || VF8 || NVS4 == 0), "register layout");
+    static_assert(QSEG >= 1 && QSEG * NCOL * NCH == QCHUNKS && QCHUNKS % NT == 0 && PAGES % NT == 0, "LDS shapes");
+    typedef unsigned int vword_t __attribute__((ext_vector_type(NVW)));
 
-    __shared__ u32x4 ring[NS * STRIDE / 16];
     __shared__ int2 pinfo[PAGES];                  // the block's pages: (slice g*H + h or -1, meta)
     __shared__ u32x4 qcache[QCHUNKS];              // query rows of the first QSEG units: [unit][column][chunk]
+    __shared__ float mbuf[4 * 16 * 64];            // unit merge: four waves x four tiles x 4 registers
     __shared__ float mlbuf[4][16][2];              // per-wave (m, l) of every column at a unit's end
     __shared__ int ent_s[kMaxEnt][kEntWords];
     __shared__ int seg_s[kMaxSeg][kSegWords];
     __shared__ int exp_s[kMaxEnt * kMaxH];         // pieces per (entry, KV head)
-    static_assert(NS * STRIDE + sizeof(pinfo) + sizeof(qcache) + sizeof(mlbuf) + sizeof(ent_s) + sizeof(seg_s) +
-                          sizeof(exp_s) <= R::LDS, "LDS");
 
     const int tid = int(threadIdx.x);
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -174,8 +142,7 @@ __global__ void __launch_bounds__(256, qstream_bpc<D>()) paged_qstream_kernel(De
     const int npg = ld_uniform(P, off_blk(H) + 4 * size_t(i_blk));
     int sig = ld_uniform(P, off_blk(H) + 4 * size_t(i_blk) + 1);   // unit being computed
     {
-        static_assert(kMaxEnt * kEntWords <= NT && kMaxSeg * kSegWords <= NT, "tables");
-        static_assert(kMaxEnt * kMaxH <= 2 * NT && PAGES % NT == 0, "tables");
+        static_assert(kMaxEnt * kEntWords <= NT && kMaxSeg * kSegWords <= NT && kMaxEnt * kMaxH <= 2 * NT, "tables");
         const int2* pl = reinterpret_cast<const int2*>(P + off_pages(H, G)) + size_t(i_blk) * a.qcap;
         const int ne = kMaxEnt * H;
         const int v_ent = P[kOffEnt + min(tid, kMaxEnt * kEntWords - 1)];
@@ -225,9 +192,81 @@ __global__ void __launch_bounds__(256, qstream_bpc<D>()) paged_qstream_kernel(De
     };
     auto unit_seg = [&](int sg) __attribute__((always_inline)) { return sg / H; };
 
-    // query rows of the first QSEG units, straight into LDS (columns past a
-    // unit's last read row 0 of the call; they are never used)
-    const uint32_t qcache_lds = uint32_t(reinterpret_cast<uintptr_t>((lds_byte_ptr)(&qcache[0])));
+    // page buffers: this wave's K code units and scales, V code words and
+    // scales.  Buffer loads whose range ends at the page's last visible row:
+    // codes and scales past it (stale bytes, possibly NaN) come back as zeros.
+    //  K operand, group g: key 16w + li, dims 64g + 16lg .. +15
+    //  accumulator register r: key tk(r) = 16w + 4lg + r (score row 4lg + r)
+    char* kcp = static_cast<char*>(a.pv.lv.k_code);
+    char* vcp = static_cast<char*>(a.pv.lv.v_code);
+    char* ksp = static_cast<char*>(a.pv.lv.k_scale);
+    char* vsp = static_cast<char*>(a.pv.lv.v_scale);
+    const int kq = 16 * w + li, tk0 = 16 * w + 4 * lg;
+    u32x4 kbuf[2][NU];                             // K units (NVFP4: words 0-1)
+    u32x4 ksbuf[2][NKS4];                          // K scales: keys tk0 .. tk0+3 (NVFP4: key kq's row)
+    vword_t vbuf[2][4];                            // V code words of keys tk(r)
+    u32x4 vsbuf[2][NVS4 > 0 ? NVS4 : 1];           // V scales of keys tk(r) (INT8, FP8)
+    uint32_t vsb[2][4];                            // NVFP4 V: the word holding key tk(r)'s scale byte
+    int pmeta[2];
+    auto load_page = [&](int fi, int J) __attribute__((always_inline)) {
+        const bool live = fi < npg;
+        const int2 pi = pinfo[live ? fi : 0];
+        const int sl = live ? __builtin_amdgcn_readfirstlane(pi.x) : -1;
+        pmeta[J] = live ? __builtin_amdgcn_readfirstlane(pi.y) | (fi == npg - 1 ? 256 : 0) : 0;
+        const int rows = sl < 0 ? 0 : (pmeta[J] & 255);   // an unmapped block reads nothing
+        const size_t s0 = size_t(sl < 0 ? 0 : sl) * 64;
+        const __amdgpu_buffer_rsrc_t rkc = __builtin_amdgcn_make_buffer_rsrc(kcp + s0 * KROW, 0, rows * KROW, kBufferWord3);
+        const __amdgpu_buffer_rsrc_t rks = __builtin_amdgcn_make_buffer_rsrc(ksp + s0 * KSROW, 0, rows * KSROW, kBufferWord3);
+        const __amdgpu_buffer_rsrc_t rvc = __builtin_amdgcn_make_buffer_rsrc(vcp + s0 * VROW, 0, rows * VROW, kBufferWord3);
+        const __amdgpu_buffer_rsrc_t rvs = __builtin_amdgcn_make_buffer_rsrc(vsp + s0 * VSROW, 0, rows * VSROW, kBufferWord3);
+#pragma unroll
+        for (int g = 0; g < NU; ++g) {
+            if constexpr (KF4) {
+                const u32x2 x = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rkc, kq * KROW + 32 * g + 8 * lg, 0, kNonTemporal));
+                kbuf[J][g] = u32x4{x[0], x[1], 0u, 0u};
+            } else {
+                kbuf[J][g] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rkc, kq * KROW + 64 * g + 16 * lg, 0, kNonTemporal));
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < NKS4; ++k) {
+            if constexpr (KF4) {
+                if constexpr (KSROW == 8) {
+                    const u32x2 x = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rks, kq * KSROW, 0, kNonTemporal));
+                    ksbuf[J][k] = u32x4{x[0], x[1], 0u, 0u};
+                } else {
+                    ksbuf[J][k] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rks, kq * KSROW + 16 * k, 0, kNonTemporal));
+                }
+            } else {
+                ksbuf[J][k] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rks, tk0 * KSROW + 16 * k, 0, kNonTemporal));
+            }
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int t = tk0 + r;
+            if constexpr (VI8) {
+#pragma unroll
+                for (int g = 0; g < NU; ++g)
+                    vbuf[J][r][g] = __builtin_amdgcn_raw_buffer_load_b32(rvc, t * VROW + 64 * g + 4 * li, 0, kNonTemporal);
+            } else if constexpr (NVW == 4) {
+                vbuf[J][r] = __builtin_bit_cast(vword_t, __builtin_amdgcn_raw_buffer_load_b128(rvc, t * VROW + 16 * li, 0, kNonTemporal));
+            } else if constexpr (NVW == 2) {
+                vbuf[J][r] = __builtin_bit_cast(vword_t, __builtin_amdgcn_raw_buffer_load_b64(rvc, t * VROW + 8 * li, 0, kNonTemporal));
+            } else {
+                vbuf[J][r] = __builtin_bit_cast(vword_t, __builtin_amdgcn_raw_buffer_load_b32(rvc, t * VROW + 4 * li, 0, kNonTemporal));
+            }
+            if constexpr (!VI8 && !VF8)            // NVFP4: the aligned word holding byte (D/16) li / 16 of the row
+                vsb[J][r] = __builtin_amdgcn_raw_buffer_load_b32(rvs, t * VSROW + (((NDT * li) / 16) & ~3), 0, kNonTemporal);
+        }
+#pragma unroll
+        for (int k = 0; k < NVS4; ++k)
+            vsbuf[J][k] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rvs, tk0 * VSROW + 16 * k, 0, kNonTemporal));
+    };
+
+    // query rows of the first QSEG units (columns past a unit's last read
+    // row 0 of the call; they are never used): loads first, then the first
+    // page, then the LDS writes
+    u32x4 qv[QCHUNKS / NT];
 #pragma unroll
     for (int k = 0; k < QCHUNKS / NT; ++k) {
         const int x = k * NT + tid;
@@ -235,74 +274,14 @@ __global__ void __launch_bounds__(256, qstream_bpc<D>()) paged_qstream_kernel(De
         const int sg = sig + u, s = unit_seg(sg);
         const u32x4* src = reinterpret_cast<const u32x4*>(a.q);
         if (s < nseg && c < ncol_of(s)) src = reinterpret_cast<const u32x4*>(q_row(col_of(s, c), sg - s * H)) + ch;
-        fetch_chunk(qcache_lds + uint32_t((k * NT + w * 64) * 16), src);
+        qv[k] = *src;
     }
+    load_page(0, 0);
+#pragma unroll
+    for (int k = 0; k < QCHUNKS / NT; ++k) qcache[k * NT + tid] = qv[k];
+    block_lds_barrier();
 
-    // Stage layout: K code row t keeps its 16-byte chunk x at position
-    // x ^ kswz(t), so the 16 rows one K read touches spread over the banks;
-    // INT8 V rows move their 64-byte quarters by vswz(t) for the same reason.
-    auto kswz = [](int t) __attribute__((always_inline)) {
-        return (KROW >= 256 ? t : t / (256 / KROW)) & (KCHR - 1);
-    };
-    auto vswz = [](int t) __attribute__((always_inline)) {
-        if constexpr (VI8 && D == 128) return 4 * ((t >> 1) & 1);
-        else if constexpr (VI8 && D == 256) return 4 * (t & 3);
-        else return 0 * t;
-    };
-    constexpr int VCHR = VROW / 16;
-    uint32_t k_src[R::KL], v_src[R::VL];           // source byte offsets within a page slice
-#pragma unroll
-    for (int k = 0; k < R::KL; ++k) {
-        const int s = k * NT + tid, t = s / KCHR, x = s % KCHR;
-        k_src[k] = uint32_t(t * KCHR + (x ^ kswz(t))) * 16u;
-    }
-#pragma unroll
-    for (int k = 0; k < R::VL; ++k) {
-        const int s = k * NT + tid, t = s / VCHR, x = s % VCHR;
-        v_src[k] = uint32_t(t * VCHR + (x ^ vswz(t))) * 16u;
-    }
-    // this lane's scale chunk (lanes below SCW): chunk x of [K scales | V scales]
-    const int sc_x = w * R::SCW + lane;
-    const bool sc_k = sc_x < R::KSB / 16;
-    const uint32_t sc_off = uint32_t(sc_k ? sc_x : sc_x - R::KSB / 16) * 16u;
-    const char* kplane = static_cast<const char*>(a.pv.lv.k_code);
-    const char* vplane = static_cast<const char*>(a.pv.lv.v_code);
-    const char* ksplane = static_cast<const char*>(a.pv.lv.k_scale);
-    const char* vsplane = static_cast<const char*>(a.pv.lv.v_scale);
-    const uint32_t ring_lds = uint32_t(reinterpret_cast<uintptr_t>((lds_byte_ptr)(&ring[0])));
-    // page fi of the range into stage fs
-    auto fetch = [&](int fi, int fs) __attribute__((always_inline)) {
-        const int sl = __builtin_amdgcn_readfirstlane(pinfo[fi].x);
-        const size_t slc = size_t(sl < 0 ? 0 : sl);
-        const uint32_t dst = ring_lds + uint32_t(fs * STRIDE + w * 1024);
-#pragma unroll
-        for (int k = 0; k < R::KL; ++k) fetch_lds16(dst + k * 4096, kplane + slc * R::KCB, k_src[k]);
-#pragma unroll
-        for (int k = 0; k < R::VL; ++k) fetch_lds16(dst + R::OFF_V + k * 4096, vplane + slc * R::VCB, v_src[k]);
-        const char* src = sc_k ? ksplane + slc * R::KSB + sc_off : vsplane + slc * R::VSB + sc_off;
-        if (lane < R::SCW) fetch_chunk(ring_lds + uint32_t(fs * STRIDE + R::OFF_KS + w * R::SCW * 16), src);
-    };
-    // meta of page fi: the last page of the block also ends its unit here
-    auto meta_of = [&](int fi) __attribute__((always_inline)) {
-        return __builtin_amdgcn_readfirstlane(pinfo[fi].y) | (fi == npg - 1 ? 256 : 0);
-    };
-
-    // Per-lane LDS byte offsets within a stage, fixed for the whole stream.
-    //  K operand, group g: key tq = 16w + 4(li%4) + li/4, dims 64g + 16lg .. +15
-    //  accumulator register r: key tk(r) = 16w + 4r + lg (score row 4lg + r)
-    const int tq = 16 * w + 4 * (li & 3) + (li >> 2);
-    int koff[NU];
-#pragma unroll
-    for (int g = 0; g < NU; ++g) {
-        if constexpr (KC == CODEC_NVFP4_G16)
-            koff[g] = tq * KROW + 16 * ((2 * g + (lg >> 1)) ^ kswz(tq)) + 8 * (lg & 1);
-        else
-            koff[g] = tq * KROW + 16 * ((4 * g + lg) ^ kswz(tq));
-    }
-    int tk[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) tk[r] = 16 * w + 4 * r + lg;
-
+    typedef const u32x4 __attribute__((address_space(1)))* glb_q_cptr;
     bf16x8_t qb[D / 32];                           // Q^T operand: column li, dims 64(c/2) + 16lg + 8(c%2) .. +7
     int klim = 0;                                  // keys this lane's column sees (0: padding column)
     int kmin = 0;                                  // smallest limit of a real column of the unit
@@ -319,13 +298,12 @@ __global__ void __launch_bounds__(256, qstream_bpc<D>()) paged_qstream_kernel(De
                 qb[c] = __builtin_bit_cast(bf16x8_t, li < ncol ? v : u32x4{0u, 0u, 0u, 0u});
             }
         } else {
-            const u32x4* qg = reinterpret_cast<const u32x4*>(q_row(cl, h));
+            const glb_q_cptr qg = (glb_q_cptr)(q_row(cl, h));
 #pragma unroll
             for (int c = 0; c < D / 32; ++c) {
                 const u32x4 v = qg[8 * (c >> 1) + 2 * lg + (c & 1)];
                 qb[c] = __builtin_bit_cast(bf16x8_t, li < ncol ? v : u32x4{0u, 0u, 0u, 0u});
             }
-            wait_vmcnt<0>();                       // drains the ring: only past the cached units
         }
     };
 
@@ -338,18 +316,17 @@ __global__ void __launch_bounds__(256, qstream_bpc<D>()) paged_qstream_kernel(De
         for (int dt = 0; dt < NDT; ++dt) acc[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     };
 
-    // unit end: merge the four waves' states through stage st, four tiles
-    // per pass; wave w folds accumulator register w of the pass's tiles, so
-    // each lane ends with four consecutive head dims of row 4lg + w
-    auto finish_unit = [&](int st) __attribute__((always_inline)) {
-        float* buf = reinterpret_cast<float*>(reinterpret_cast<char*>(&ring[0]) + st * STRIDE);
+    // unit end: merge the four waves' states through mbuf, four tiles per
+    // pass; wave w folds accumulator register w, so each lane ends with four
+    // consecutive head dims of row 4lg + w of each pass
+    auto finish_unit = [&]() __attribute__((always_inline)) {
         const float lw = rows_sum(l_part);
         f32x4_t merged[NP];
         float cw[4], lt = 0.f, mx = -INFINITY;
 #pragma unroll
         for (int p = 0; p < NP; ++p) {
-            block_lds_barrier();                   // stage st is free, or every wave read the last pass
-            float* mine = buf + w * 1024;
+            block_lds_barrier();                   // every wave read the previous pass
+            float* mine = mbuf + w * 1024;
 #pragma unroll
             for (int jj = 0; jj < 4; ++jj)
 #pragma unroll
@@ -376,13 +353,13 @@ __global__ void __launch_bounds__(256, qstream_bpc<D>()) paged_qstream_kernel(De
             for (int jj = 0; jj < 4; ++jj) {
                 float x = 0.f;
 #pragma unroll
-                for (int v = 0; v < 4; ++v) x += buf[v * 1024 + (jj * 4 + w) * 64 + lane] * cw[v];
+                for (int v = 0; v < 4; ++v) x += mbuf[v * 1024 + (jj * 4 + w) * 64 + lane] * cw[v];
                 merged[p][jj] = x;
             }
         }
-        // write (stores are not waited for: the ring's waits cover them and
-        // the combine is a later launch); a column whose (entry, KV head) has
-        // no other piece is normalized into out, the others go to slot i + sigma
+        // write (not waited for: the combine is a later launch); a column
+        // whose (entry, KV head) has no other piece is normalized into out,
+        // the others go to slot i + sigma
         const int s = unit_seg(sig), h = sig - s * H;
         if (li < ncol_of(s)) {
             const Col cl = col_of(s, li);
@@ -410,254 +387,166 @@ __global__ void __launch_bounds__(256, qstream_bpc<D>()) paged_qstream_kernel(De
         reset();
     };
 
-    reset();
-    int meta_ring[NS];                             // meta of the pages in the ring, by stage
-#pragma unroll
-    for (int k = 0; k < NS - 1; ++k) {
-        if (k < npg) {
-            fetch(k, k);
-            meta_ring[k] = meta_of(k);
-        } else {
-            meta_ring[k] = 0;
-        }
-    }
-    meta_ring[NS - 1] = 0;
-    // the query cache and the first page have landed (loads complete in order)
-    if (npg >= NS - 1) wait_vmcnt<LPP * (NS - 2)>();
-    else wait_vmcnt<0>();
-    block_lds_barrier();
-    int unit_k = 0;
-    start_unit(unit_k, sig);
-
-    // one page in stage J (compile time: stage offsets fold into the reads)
-    auto step = [&](auto jc, int i) __attribute__((always_inline)) {
+    // one page of this wave's keys from buffer set J
+    auto compute = [&](auto jc) __attribute__((always_inline)) {
         constexpr int J = decltype(jc)::value;
-        constexpr int FS = (J + NS - 1) % NS;
-        if (i + NS - 1 < npg) {
-            wait_vmcnt<LPP * (NS - 2)>();
-            block_lds_barrier();
-            fetch(i + NS - 1, FS);
-            meta_ring[FS] = meta_of(i + NS - 1);
-        } else {
-            wait_vmcnt<0>();
-            block_lds_barrier();
-        }
-        const int meta = meta_ring[J];
+        const int meta = pmeta[J];
         const int lim = meta & 255;                // rows any column of the unit may see
-        if (lim > 16 * w) {
-            const int tok0 = ((meta >> 9) & 0x7fff) * kPage;
-            const lds_byte_ptr sb = (lds_byte_ptr)(&ring[0]) + J * STRIDE;
+        if (lim <= 16 * w) return;                 // none of them among this wave's keys
+        const int tok0 = ((meta >> 9) & 0x7fff) * kPage;
 
-            // every LDS read of the page first, unconditionally (all inside
-            // the stage): one wait instead of one per dependent use
-            constexpr int NKW = KC == CODEC_NVFP4_G16 ? 2 : 4;    // K words per group and lane
-            constexpr int NVW = VI8 ? NU : (VF8 ? NDT / 4 : NDT / 8);   // V words per key and lane
-            constexpr int NKS = KI8 ? NU : (KF8 ? 1 : NU);        // K scales per lane
-            constexpr int NVS = VI8 ? NU : 1;                     // V scales per key
-            uint32_t kx[NU][NKW];
+        // QK^T: S^T[16 keys x 16 columns], per K scale group for INT8
+        f32x4_t sacc[NGK];
 #pragma unroll
-            for (int g = 0; g < NU; ++g) {
-                if constexpr (NKW == 2) {
-                    const u32x2 v = *reinterpret_cast<lds_cu32x2>(sb + koff[g]);
-                    kx[g][0] = v[0];
-                    kx[g][1] = v[1];
-                } else {
-                    const u32x4 v = *reinterpret_cast<lds_cu32x4>(sb + koff[g]);
-                    kx[g][0] = v[0];
-                    kx[g][1] = v[1];
-                    kx[g][2] = v[2];
-                    kx[g][3] = v[3];
+        for (int g = 0; g < NGK; ++g) sacc[g] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int g = 0; g < NU; ++g) {
+            const u32x4 x = kbuf[J][g];
+            u32x4 op0, op1;
+            if constexpr (KF4) {
+                const uint32_t sw = ksbuf[J][0][(4 * g + lg) >> 2];
+                const float sc = e4m3_f32(sw >> (8 * ((4 * g + lg) & 3)));
+                uint32_t o[8];
+#pragma unroll
+                for (int b = 0; b < 4; ++b) {
+                    const f32x2_t f0 = fp4_pair(x[0], b);
+                    const f32x2_t f1 = fp4_pair(x[1], b);
+                    o[b] = pk_bf16(f0[0] * sc, f0[1] * sc);
+                    o[4 + b] = pk_bf16(f1[0] * sc, f1[1] * sc);
                 }
-            }
-            float ksc[4][NKS];                     // INT8 / FP8: scales of key tk(r); NVFP4: of the lane's 16 dims
-            if constexpr (KC == CODEC_NVFP4_G16) {
-#pragma unroll
-                for (int g = 0; g < NU; ++g)
-                    ksc[0][g] = e4m3_f32(uint32_t(reinterpret_cast<lds_cu8>(sb)[R::OFF_KS + tq * KSROW + 4 * g + lg]));
+                op0 = u32x4{o[0], o[1], o[2], o[3]};
+                op1 = u32x4{o[4], o[5], o[6], o[7]};
+            } else if constexpr (KI8) {
+                op0 = u32x4{pk_bf16(i8f<0>(x[0]), i8f<1>(x[0])), pk_bf16(i8f<2>(x[0]), i8f<3>(x[0])),
+                            pk_bf16(i8f<0>(x[1]), i8f<1>(x[1])), pk_bf16(i8f<2>(x[1]), i8f<3>(x[1]))};
+                op1 = u32x4{pk_bf16(i8f<0>(x[2]), i8f<1>(x[2])), pk_bf16(i8f<2>(x[2]), i8f<3>(x[2])),
+                            pk_bf16(i8f<0>(x[3]), i8f<1>(x[3])), pk_bf16(i8f<2>(x[3]), i8f<3>(x[3]))};
             } else {
+                uint32_t o[8];
 #pragma unroll
-                for (int r = 0; r < 4; ++r)
-#pragma unroll
-                    for (int g = 0; g < NKS; ++g)
-                        ksc[r][g] = reinterpret_cast<lds_cf32>(sb + R::OFF_KS + tk[r] * KSROW)[g];
-            }
-            float vsc[4][NVS];
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                if constexpr (VC == CODEC_NVFP4_G16) {
-                    vsc[r][0] = e4m3_f32(uint32_t(reinterpret_cast<lds_cu8>(sb)[R::OFF_VS + tk[r] * VSROW + (NDT * li) / 16]));
-                } else {
-#pragma unroll
-                    for (int g = 0; g < NVS; ++g) vsc[r][g] = reinterpret_cast<lds_cf32>(sb + R::OFF_VS + tk[r] * VSROW)[g];
+                for (int e = 0; e < 4; ++e) {
+                    o[2 * e] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x[e], 1.0f, false));
+                    o[2 * e + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x[e], 1.0f, true));
                 }
+                op0 = u32x4{o[0], o[1], o[2], o[3]};
+                op1 = u32x4{o[4], o[5], o[6], o[7]};
             }
-            uint32_t vx[4][NVW];                   // INT8: word g = dims 64g + 4li .. +3; else the lane's NDT dims
+            const int ga = KI8 ? g : 0;
+            sacc[ga] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, op0), qb[2 * g], sacc[ga], 0, 0, 0);
+            sacc[ga] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, op1), qb[2 * g + 1], sacc[ga], 0, 0, 0);
+        }
+        // K scales of key tk(r): float r*NU + g (INT8) or r (FP8) of the loaded run
+        auto kscale = [&](int r, int g) __attribute__((always_inline)) {
+            const int f = KI8 ? r * NU + g : r;
+            return __uint_as_float(ksbuf[J][f >> 2][f & 3]);
+        };
+        float sj[4];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int t = tk[r];
-                if constexpr (VI8) {
+        for (int r = 0; r < 4; ++r) {
+            if constexpr (KI8) {
+                float x = 0.f;
 #pragma unroll
-                    for (int g = 0; g < NU; ++g)
-                        vx[r][g] = *reinterpret_cast<lds_cu32>(sb + R::OFF_V + t * VROW +
-                                                               16 * ((4 * g + (li >> 2)) ^ vswz(t)) + 4 * (li & 3));
-                } else {
-                    const int off = R::OFF_V + t * VROW + 4 * NVW * li;
-                    if constexpr (NVW == 4) {
-                        const u32x4 v = *reinterpret_cast<lds_cu32x4>(sb + off);
-                        vx[r][0] = v[0];
-                        vx[r][1] = v[1];
-                        vx[r][2] = v[2];
-                        vx[r][3] = v[3];
-                    } else if constexpr (NVW == 2) {
-                        const u32x2 v = *reinterpret_cast<lds_cu32x2>(sb + off);
-                        vx[r][0] = v[0];
-                        vx[r][1] = v[1];
-                    } else {
-                        vx[r][0] = *reinterpret_cast<lds_cu32>(sb + off);
-                    }
-                }
+                for (int g = 0; g < NU; ++g) x += sacc[g][r] * kscale(r, g);
+                sj[r] = x * a.scale_log2;
+            } else if constexpr (KF8) {
+                sj[r] = sacc[0][r] * kscale(r, 0) * a.scale_log2;
+            } else {
+                sj[r] = sacc[0][r] * a.scale_log2;
             }
+        }
+        if (tok0 + kPage > kmin) {                 // a real column's limit falls inside the page
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                if (tok0 + tk0 + r >= klim) sj[r] = -INFINITY;
+        }
+        const float pm = rows_max(fmaxf(fmaxf(sj[0], sj[1]), fmaxf(sj[2], sj[3])));
+        if (__builtin_amdgcn_ballot_w64(pm > m_ref + kRescaleLog2)) {
+            const float mn = pm > m_ref + kRescaleLog2 ? pm : m_ref;
+            const float alpha = m_ref == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_ref - mn);
+            l_part *= alpha;
+#pragma unroll
+            for (int dt = 0; dt < NDT; ++dt) acc[dt] *= alpha;
+            m_ref = mn;
+        }
+        float p[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            p[r] = __builtin_amdgcn_exp2f(sj[r] - m_ref);
+            // a column with no visible key in this wave yet has no reference
+            p[r] = m_ref == -INFINITY ? 0.f : p[r];
+        }
+        l_part += (p[0] + p[1]) + (p[2] + p[3]);
 
-            // QK^T: S^T[16 keys x 16 columns], per K scale group for INT8
-            f32x4_t sacc[NGK];
+        // P^T operands [P_hi; P_lo], one per V scale group (keys past the
+        // last limit have zero codes and scales from the buffer range)
+        auto vscale = [&](int r, int g) __attribute__((always_inline)) {
+            const int f = VI8 ? r * NU + g : r;
+            return __uint_as_float(vsbuf[J][f >> 2][f & 3]);
+        };
+        bf16x8_t bop[NPV];
 #pragma unroll
-            for (int g = 0; g < NGK; ++g) sacc[g] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        for (int g = 0; g < NPV; ++g) {
+            float pv[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) pv[r] = (VI8 || VF8) ? p[r] * vscale(r, g) : p[r];
+            uint32_t h01, l01, h23, l23;
+            split_bf16(pv[0], pv[1], h01, l01);
+            split_bf16(pv[2], pv[3], h23, l23);
+            bop[g] = __builtin_bit_cast(bf16x8_t, u32x4{h01, h23, l01, l23});
+        }
+
+        // PV: O^T[16 dims x 16 columns] += V^T . P^T per tile
+        auto pv_tile = [&](int dt, uint32_t x01, uint32_t x23, int g) __attribute__((always_inline)) {
+            acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, u32x4{x01, x23, x01, x23}),
+                                                              bop[g], acc[dt], 0, 0, 0);
+        };
+        if constexpr (VI8) {
 #pragma unroll
             for (int g = 0; g < NU; ++g) {
-                u32x4 op0, op1;
-                if constexpr (KC == CODEC_NVFP4_G16) {
-                    const float sc = ksc[0][g];
-                    uint32_t o[8];
-#pragma unroll
-                    for (int b = 0; b < 4; ++b) {
-                        const f32x2_t f0 = fp4_pair(kx[g][0], b);
-                        const f32x2_t f1 = fp4_pair(kx[g][1], b);
-                        o[b] = pk_bf16(f0[0] * sc, f0[1] * sc);
-                        o[4 + b] = pk_bf16(f1[0] * sc, f1[1] * sc);
-                    }
-                    op0 = u32x4{o[0], o[1], o[2], o[3]};
-                    op1 = u32x4{o[4], o[5], o[6], o[7]};
-                } else if constexpr (KI8) {
-                    const uint32_t* x = kx[g];
-                    op0 = u32x4{pk_bf16(i8f<0>(x[0]), i8f<1>(x[0])), pk_bf16(i8f<2>(x[0]), i8f<3>(x[0])),
-                                pk_bf16(i8f<0>(x[1]), i8f<1>(x[1])), pk_bf16(i8f<2>(x[1]), i8f<3>(x[1]))};
-                    op1 = u32x4{pk_bf16(i8f<0>(x[2]), i8f<1>(x[2])), pk_bf16(i8f<2>(x[2]), i8f<3>(x[2])),
-                                pk_bf16(i8f<0>(x[3]), i8f<1>(x[3])), pk_bf16(i8f<2>(x[3]), i8f<3>(x[3]))};
-                } else {
-                    uint32_t o[8];
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        o[2 * e] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(kx[g][e], 1.0f, false));
-                        o[2 * e + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(kx[g][e], 1.0f, true));
-                    }
-                    op0 = u32x4{o[0], o[1], o[2], o[3]};
-                    op1 = u32x4{o[4], o[5], o[6], o[7]};
-                }
-                const int ga = KI8 ? g : 0;
-                sacc[ga] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, op0), qb[2 * g],
-                                                                   sacc[ga], 0, 0, 0);
-                sacc[ga] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, op1), qb[2 * g + 1],
-                                                                   sacc[ga], 0, 0, 0);
+                const uint32_t x0 = vbuf[J][0][g], x1 = vbuf[J][1][g], x2 = vbuf[J][2][g], x3 = vbuf[J][3][g];
+                pv_tile(4 * g + 0, pk_bf16(i8f<0>(x0), i8f<0>(x1)), pk_bf16(i8f<0>(x2), i8f<0>(x3)), g);
+                pv_tile(4 * g + 1, pk_bf16(i8f<1>(x0), i8f<1>(x1)), pk_bf16(i8f<1>(x2), i8f<1>(x3)), g);
+                pv_tile(4 * g + 2, pk_bf16(i8f<2>(x0), i8f<2>(x1)), pk_bf16(i8f<2>(x2), i8f<2>(x3)), g);
+                pv_tile(4 * g + 3, pk_bf16(i8f<3>(x0), i8f<3>(x1)), pk_bf16(i8f<3>(x2), i8f<3>(x3)), g);
             }
-            float sj[4];
+        } else {
+            float sc[4];
+            if constexpr (!VF8) {
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                if constexpr (KI8) {
-                    float x = 0.f;
-#pragma unroll
-                    for (int g = 0; g < NU; ++g) x += sacc[g][r] * ksc[r][g];
-                    sj[r] = x * a.scale_log2;
-                } else if constexpr (KF8) {
-                    sj[r] = sacc[0][r] * ksc[r][0] * a.scale_log2;
-                } else {
-                    sj[r] = sacc[0][r] * a.scale_log2;
-                }
+                for (int r = 0; r < 4; ++r) sc[r] = e4m3_f32(vsb[J][r] >> (8 * (((NDT * li) / 16) & 3)));
             }
-            if (tok0 + kPage > kmin) {             // a real column's limit falls inside the page
+            // two tiles per step: dims 2q and 2q + 1 of the lane's run
 #pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    if (tok0 + tk[r] >= klim) sj[r] = -INFINITY;
-            }
-            const float pm = rows_max(fmaxf(fmaxf(sj[0], sj[1]), fmaxf(sj[2], sj[3])));
-            if (__builtin_amdgcn_ballot_w64(pm > m_ref + kRescaleLog2)) {
-                const float mn = pm > m_ref + kRescaleLog2 ? pm : m_ref;
-                const float alpha = m_ref == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_ref - mn);
-                l_part *= alpha;
-#pragma unroll
-                for (int dt = 0; dt < NDT; ++dt) acc[dt] *= alpha;
-                m_ref = mn;
-            }
-            float p[4];
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                p[r] = __builtin_amdgcn_exp2f(sj[r] - m_ref);
-                // a column with no visible key in this wave yet has no reference
-                p[r] = m_ref == -INFINITY ? 0.f : p[r];
-            }
-            l_part += (p[0] + p[1]) + (p[2] + p[3]);
-
-            // keys past the last limit hold stale bytes (possibly NaN codes or
-            // scales): their V codes and scales count as zero
-            if (lim < kPage) {
+            for (int q = 0; q < NDT / 2; ++q) {
+                f32x2_t f[4];
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const bool live = tk[r] < lim;
-#pragma unroll
-                    for (int e = 0; e < NVW; ++e) vx[r][e] = live ? vx[r][e] : 0u;
-#pragma unroll
-                    for (int g = 0; g < NVS; ++g) vsc[r][g] = live ? vsc[r][g] : 0.f;
-                }
-            }
-
-            // P^T operands [P_hi; P_lo], one per V scale group
-            bf16x8_t bop[NPV];
-#pragma unroll
-            for (int g = 0; g < NPV; ++g) {
-                float pv[4];
-#pragma unroll
-                for (int r = 0; r < 4; ++r) pv[r] = (VC == CODEC_NVFP4_G16) ? p[r] : p[r] * vsc[r][g];
-                uint32_t h01, l01, h23, l23;
-                split_bf16(pv[0], pv[1], h01, l01);
-                split_bf16(pv[2], pv[3], h23, l23);
-                bop[g] = __builtin_bit_cast(bf16x8_t, u32x4{h01, h23, l01, l23});
-            }
-
-            // PV: O^T[16 dims x 16 columns] += V^T . P^T per tile
-            auto pv_tile = [&](int dt, uint32_t x01, uint32_t x23, int g) __attribute__((always_inline)) {
-                acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                    __builtin_bit_cast(bf16x8_t, u32x4{x01, x23, x01, x23}), bop[g], acc[dt], 0, 0, 0);
-            };
-            if constexpr (VI8) {
-#pragma unroll
-                for (int g = 0; g < NU; ++g) {
-                    const uint32_t x0 = vx[0][g], x1 = vx[1][g], x2 = vx[2][g], x3 = vx[3][g];
-                    pv_tile(4 * g + 0, pk_bf16(i8f<0>(x0), i8f<0>(x1)), pk_bf16(i8f<0>(x2), i8f<0>(x3)), g);
-                    pv_tile(4 * g + 1, pk_bf16(i8f<1>(x0), i8f<1>(x1)), pk_bf16(i8f<1>(x2), i8f<1>(x3)), g);
-                    pv_tile(4 * g + 2, pk_bf16(i8f<2>(x0), i8f<2>(x1)), pk_bf16(i8f<2>(x2), i8f<2>(x3)), g);
-                    pv_tile(4 * g + 3, pk_bf16(i8f<3>(x0), i8f<3>(x1)), pk_bf16(i8f<3>(x2), i8f<3>(x3)), g);
-                }
-            } else {
-                // two tiles per step: dims 2q and 2q + 1 of the lane's run
-#pragma unroll
-                for (int q = 0; q < NDT / 2; ++q) {
-                    f32x2_t f[4];
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        if constexpr (VF8) {
-                            f[r] = fp8_pair(vx[r][q / 2], q & 1);
-                        } else {
-                            f[r] = fp4_pair(vx[r][q / 4], q & 3);
-                            f[r] = f[r] * vsc[r][0];
-                        }
+                    if constexpr (VF8) {
+                        f[r] = fp8_pair(vbuf[J][r][q / 2], q & 1);
+                    } else {
+                        f[r] = fp4_pair(vbuf[J][r][q / 4], q & 3);
+                        f[r] = f[r] * sc[r];
                     }
-                    pv_tile(2 * q, pk_bf16(f[0][0], f[1][0]), pk_bf16(f[2][0], f[3][0]), 0);
-                    pv_tile(2 * q + 1, pk_bf16(f[0][1], f[1][1]), pk_bf16(f[2][1], f[3][1]), 0);
                 }
+                pv_tile(2 * q, pk_bf16(f[0][0], f[1][0]), pk_bf16(f[2][0], f[3][0]), 0);
+                pv_tile(2 * q + 1, pk_bf16(f[0][1], f[1][1]), pk_bf16(f[2][1], f[3][1]), 0);
             }
         }
+    };
 
+    reset();
+    int unit_k = 0;
+    start_unit(unit_k, sig);
+    // page i from buffer set J, the next page in flight in the other set; every
+    // step issues the same loads (empty ranges past the block's last page), so
+    // the compiler's vector-memory waits stay exact
+    auto step = [&](auto jc, int i) __attribute__((always_inline)) {
+        constexpr int J = decltype(jc)::value;
+        const int meta = pmeta[J];
+        load_page(i + 1, 1 - J);
+        compute(jc);
         if (meta & 256) {
-            finish_unit(J);
+            finish_unit();
             if (i + 1 < npg) {
                 ++sig;
                 ++unit_k;
@@ -665,8 +554,7 @@ __global__ void __launch_bounds__(256, qstream_bpc<D>()) paged_qstream_kernel(De
             }
         }
     };
-
-    for (int i0 = 0; i0 < npg; i0 += NS) ring_round<0, NS>(step, i0, npg);
+    for (int i0 = 0; i0 < npg; i0 += 2) ring_round<0, 2>(step, i0, npg);
 }
 
 template <int D, int KC, int VC>
@@ -717,7 +605,9 @@ bool qstream_path(const PoolView& pv, int B, int gq) {
            (gq == 1 || gq == 2 || gq == 4 || gq == 8);
 }
 
-int qstream_blocks_per_cu(const PoolView& pv) { return pv.D <= 128 ? qstream_bpc<128>() : qstream_bpc<256>(); }
+int qstream_blocks_per_cu(const PoolView& pv) {
+    return (pv.D == 256 && pv.k_codec == CODEC_INT8_G64) ? qstream_bpc<256, CODEC_INT8_G64>() : qstream_bpc<128, CODEC_FP8_ROW>();
+}
 
 hipError_t launch_qstream(const DecodeArgs& a, int gq, hipStream_t s) {
     switch (a.pv.D) {
