@@ -55,8 +55,8 @@ struct QRow {
 };
 
 // Blocks per compute unit: two (two waves per SIMD hide each other's
-// latencies; at most 256 registers per lane), one for INT8-G64 at D = 256
-// (its registers do not fit twice).
+// latencies; at most 256 registers per lane; three measured slower at
+// D = 128), one for INT8-G64 at D = 256 (its registers do not fit twice).
 template <int D, int KC>
 constexpr int qstream_bpc() { return (D == 256 && KC == CODEC_INT8_G64) ? 1 : 2; }
 
@@ -606,7 +606,8 @@ bool qstream_path(const PoolView& pv, int B, int gq) {
 }
 
 int qstream_blocks_per_cu(const PoolView& pv) {
-    return (pv.D == 256 && pv.k_codec == CODEC_INT8_G64) ? qstream_bpc<256, CODEC_INT8_G64>() : qstream_bpc<128, CODEC_FP8_ROW>();
+    if (pv.D <= 128) return qstream_bpc<128, CODEC_FP8_ROW>();
+    return pv.k_codec == CODEC_INT8_G64 ? qstream_bpc<256, CODEC_INT8_G64>() : qstream_bpc<256, CODEC_FP8_ROW>();
 }
 
 hipError_t launch_qstream(const DecodeArgs& a, int gq, hipStream_t s) {
