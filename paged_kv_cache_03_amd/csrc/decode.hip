@@ -570,8 +570,8 @@ __global__ void __launch_bounds__(256, 2) paged_vstream_kernel(DecodeArgs a) {
     auto step = [&](auto jc, int i) __attribute__((always_inline)) {
         constexpr int J = decltype(jc)::value;
         constexpr int FB = (J + PF - 1) % PF;
-        load_page(i + PF - 1, kbuf[FB], vbuf[FB], pmeta[FB]);
         const int meta = pmeta[J];
+        load_page(i + PF - 1, kbuf[FB], vbuf[FB], pmeta[FB]);
         if (append && (meta & kPatchBit)) {
             // an entry's new token lies in this page: its row replaces the
             // loaded one in the wave that owns the key (from the staged copy;
