@@ -1,10 +1,10 @@
 """GPU parity of the matrix-core page stream (BF16 decode) against the CPU oracle.
 
 Covers what the stream's own structure adds on top of the generic decode
-tests: a block range crossing more segments than the partials it holds in
-registers and than its cached query rows, the shapes it instantiates, bitwise
-invariance to physical page placement, and repeated calls on one
-workspace (the per-segment arrival counters must come back to zero).
+tests: a block range crossing more segments than its cached query rows, the
+shapes it instantiates (with NaN bytes in every row past the frontiers, which
+the page loads' ranges must keep out), bitwise invariance to physical page
+placement, and repeated calls on one workspace.
 Bar: max-abs 2e-3 against the fp64 oracle.
 """
 
@@ -20,9 +20,9 @@ pytestmark = pytest.mark.gpu
 TOL = 2e-3
 
 
-def _check(wl, tag):
+def _check(wl, tag, **kw):
     pool, st, _ = build_oracle(wl)
-    dp, _, _ = build_device(wl)
+    dp, _, _ = build_device(wl, **kw)
     assert np.array_equal(dp.table.cpu().numpy(), pool.table)
     got = device_decode(dp, wl, 0)
     ref = A.paged_decode(st, 0, wl.table_rows, wl.seq_lens, wl.q(0), wl.sm_scale)
@@ -45,13 +45,14 @@ def test_stream_block_crossing_many_segments():
 
 @pytest.mark.parametrize("gq,D", [(8, 128), (8, 64), (4, 64), (1, 128), (2, 64)])
 def test_stream_shapes(gq, D):
+    # planes start as 0xFF bytes (NaN bf16): rows past every frontier hold them
     H = 2
     hist = [0, 63, 64, 777, 1500, 1500, 5]
     fork = [None, None, None, None, None, (4, 1500), None]
     cow = [False] * 5 + [True, False]
     wl = workloads.small(70 + gq + D, "BF16", hist=hist, fork=fork, cow=cow, C=7, S=2048, Hq=H * gq, H=H, D=D)
-    say(f"decode BF16 gq={gq} D={D}")
-    dp, _ = _check(wl, f"gq={gq} D={D}")
+    say(f"decode BF16 gq={gq} D={D}, planes filled with 0xFF")
+    dp, _ = _check(wl, f"gq={gq} D={D}", fill=0xFF)
     dp.close()
 
 
