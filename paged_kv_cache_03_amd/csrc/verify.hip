@@ -162,6 +162,7 @@ __global__ void __launch_bounds__(512) verify_tile_kernel(VerifyArgs a) {
     constexpr int NDT = D / 16;                    // PV tiles of 16 dims
     constexpr int TCOL = 128;                      // query columns per tile
     constexpr int WCT = 2;                         // 16-column tiles per wave
+    constexpr int kValuPerTile = 48;               // vector instructions of one tile's probabilities
     constexpr int TTOK = TCOL / GQ;                // chunk tokens per tile
     static_assert((D == 64 || D == 128) && TCOL % GQ == 0, "shape");
     static_assert(NS * SLICE_BYTES == 0x10000, "V stages sit 64 KiB above the K stages");
@@ -321,8 +322,8 @@ __global__ void __launch_bounds__(512) verify_tile_kernel(VerifyArgs a) {
             block_lds_barrier();
         }
         if (lim <= kr0) return;                    // none of this wave's keys is visible
-        const bool masked = tok0 + kPage > kmin;
         const u32x4* kst = &ring[0][J][0];
+        const lds_byte_ptr vst = (lds_byte_ptr)(&ring[0][J][0]);   // voff includes the K-to-V distance
         f32x4_t s[2][WCT];
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt)
@@ -338,39 +339,68 @@ __global__ void __launch_bounds__(512) verify_tile_kernel(VerifyArgs a) {
                     s[kt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kk, qb[ct][c], s[kt][ct], 0, 0, 0);
             }
         }
-        bf16x8_t phi[WCT], plo[WCT];
+        // V^T of the wave's 32 keys (two transposing reads per 16 dims),
+        // read while the score products run.  k order of the PV product:
+        // element e of lane group g is key 16*(e/4) + 4g + e%4 of this wave's
+        // 32, the order of the score rows below
+        bf16x8_t va[NDT];
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) {
+            const s16x4_t v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_ptr)(vst + voff[dt]));
+            const s16x4_t v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (lds_s16x4_ptr)(vst + voff[dt] + 16 * NCH * 16));
+            va[dt] = __builtin_bit_cast(
+                bf16x8_t, u32x4{__builtin_bit_cast(u32x2, v0)[0], __builtin_bit_cast(u32x2, v0)[1],
+                                __builtin_bit_cast(u32x2, v1)[0], __builtin_bit_cast(u32x2, v1)[1]});
+        }
+        // the causal mask, only on the pages that reach some column's limit
+        // (every partly written page is one: its key limit lies inside it)
+        if (tok0 + kPage > kmin) {
+#pragma unroll
+            for (int ct = 0; ct < WCT; ++ct)
+#pragma unroll
+                for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        if (tok0 + kr0 + 16 * kt + 4 * lg + r >= klim[ct]) s[kt][ct][r] = -INFINITY;
+        }
+        // raw scores; the scale (> 0) is applied in the exponent's fma.  One
+        // lazy-rescale decision for both column tiles (a tile that does not
+        // need it keeps its reference: factor 1)
+        float pm[WCT];
+        bool grow = false;
 #pragma unroll
         for (int ct = 0; ct < WCT; ++ct) {
-            // raw scores; the scale (> 0) is applied in the exponent's fma
-            float sj[2][4];
             float mx = -INFINITY;
 #pragma unroll
             for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    float v = s[kt][ct][r];
-                    if (masked && tok0 + kr0 + 16 * kt + 4 * lg + r >= klim[ct]) v = -INFINITY;
-                    sj[kt][r] = v;
-                    mx = fmaxf(mx, v);
-                }
-            const float pm = rows_max(mx) * a.scale_log2;
-            if (__builtin_amdgcn_ballot_w64(pm > m_ref[ct] + kRescaleLog2)) {
-                const float mn = pm > m_ref[ct] + kRescaleLog2 ? pm : m_ref[ct];
+                for (int r = 0; r < 4; ++r) mx = fmaxf(mx, s[kt][ct][r]);
+            pm[ct] = rows_max(mx) * a.scale_log2;
+            grow |= pm[ct] > m_ref[ct] + kRescaleLog2;
+        }
+        if (__builtin_amdgcn_ballot_w64(grow)) {
+#pragma unroll
+            for (int ct = 0; ct < WCT; ++ct) {
+                const float mn = pm[ct] > m_ref[ct] + kRescaleLog2 ? pm[ct] : m_ref[ct];
                 const float alpha = m_ref[ct] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_ref[ct] - mn);
                 l_part[ct] *= alpha;
 #pragma unroll
                 for (int dt = 0; dt < NDT; ++dt) acc[ct][dt] *= alpha;
                 m_ref[ct] = mn;
             }
-            // k order of the PV product: element e of lane group g is key
-            // 16*(e/4) + 4g + e%4 of this wave's 32 (the same for V^T below)
-            // a column whose keys in this half are all masked so far has no
-            // reference yet: offset 0 keeps its p at exp2(-inf) = 0, not NaN
+        }
+        // probabilities as bf16 pairs p_hi + p_lo.  A column whose keys in
+        // this half are all masked so far has no reference yet: offset 0
+        // keeps its p at exp2(-inf) = 0, not NaN
+        bf16x8_t phi[WCT], plo[WCT];
+#pragma unroll
+        for (int ct = 0; ct < WCT; ++ct) {
             const float moff = m_ref[ct] == -INFINITY ? 0.f : -m_ref[ct];
             float p[8];
 #pragma unroll
             for (int e = 0; e < 8; ++e)
-                p[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sj[e >> 2][e & 3], a.scale_log2, moff));
+                p[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[e >> 2][ct][e & 3], a.scale_log2, moff));
             l_part[ct] += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
             uint32_t hv[4], lv[4];
 #pragma unroll
@@ -378,21 +408,27 @@ __global__ void __launch_bounds__(512) verify_tile_kernel(VerifyArgs a) {
             phi[ct] = __builtin_bit_cast(bf16x8_t, u32x4{hv[0], hv[1], hv[2], hv[3]});
             plo[ct] = __builtin_bit_cast(bf16x8_t, u32x4{lv[0], lv[1], lv[2], lv[3]});
         }
-        const lds_byte_ptr vst = (lds_byte_ptr)(&ring[0][J][0]);   // voff includes the K-to-V distance
+        // PV: the hi products of every 16-dim tile, then the lo ones (no
+        // product waits on the one before it)
 #pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) {
-            const s16x4_t v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_ptr)(vst + voff[dt]));
-            const s16x4_t v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (lds_s16x4_ptr)(vst + voff[dt] + 16 * NCH * 16));
-            const bf16x8_t va = __builtin_bit_cast(
-                bf16x8_t, u32x4{__builtin_bit_cast(u32x2, v0)[0], __builtin_bit_cast(u32x2, v0)[1],
-                                __builtin_bit_cast(u32x2, v1)[0], __builtin_bit_cast(u32x2, v1)[1]});
+        for (int ct = 0; ct < WCT; ++ct) {
 #pragma unroll
-            for (int ct = 0; ct < WCT; ++ct) {
-                acc[ct][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, phi[ct], acc[ct][dt], 0, 0, 0);
-                acc[ct][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, plo[ct], acc[ct][dt], 0, 0, 0);
-            }
+            for (int dt = 0; dt < NDT; ++dt)
+                acc[ct][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[dt], phi[ct], acc[ct][dt], 0, 0, 0);
+#pragma unroll
+            for (int dt = 0; dt < NDT; ++dt)
+                acc[ct][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[dt], plo[ct], acc[ct][dt], 0, 0, 0);
         }
+        // issue order: the first tile's probabilities, then its products one
+        // at a time between the second tile's vector work, then the second
+        // tile's products
+        __builtin_amdgcn_sched_group_barrier(0x002, kValuPerTile, 0);
+#pragma unroll
+        for (int k = 0; k < 2 * NDT; ++k) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, (kValuPerTile + 2 * NDT - 1) / (2 * NDT), 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 2 * NDT, 0);
     };
 
     for (int i0p = 0; i0p < npages; i0p += NS) {
