@@ -162,7 +162,7 @@ __global__ void __launch_bounds__(512) verify_tile_kernel(VerifyArgs a) {
     constexpr int NDT = D / 16;                    // PV tiles of 16 dims
     constexpr int TCOL = 128;                      // query columns per tile
     constexpr int WCT = 2;                         // 16-column tiles per wave
-    constexpr int kValuPerTile = 48;               // vector instructions of one tile's probabilities
+    constexpr float kHiOnly = 1.f / 64.f;          // largest weight of a page that takes p as one bf16 term
     constexpr int TTOK = TCOL / GQ;                // chunk tokens per tile
     static_assert((D == 64 || D == 128) && TCOL % GQ == 0, "shape");
     static_assert(NS * SLICE_BYTES == 0x10000, "V stages sit 64 KiB above the K stages");
@@ -277,11 +277,16 @@ __global__ void __launch_bounds__(512) verify_tile_kernel(VerifyArgs a) {
     }
 
     f32x4_t acc[WCT][NDT];
-    float m_ref[WCT], l_part[WCT];
+    // lsum[ct]: the column's sum of probabilities over this wave's keys, on
+    // the matrix cores (an all-ones A operand against P^T: every row of the
+    // result is the column sum of exactly the bf16 values PV uses)
+    f32x4_t lsum[WCT];
+    float m_ref[WCT];
+    const bf16x8_t ones = __builtin_bit_cast(bf16x8_t, u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u});
 #pragma unroll
     for (int ct = 0; ct < WCT; ++ct) {
         m_ref[ct] = -INFINITY;
-        l_part[ct] = 0.f;
+        lsum[ct] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt) acc[ct][dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     }
@@ -384,51 +389,69 @@ __global__ void __launch_bounds__(512) verify_tile_kernel(VerifyArgs a) {
             for (int ct = 0; ct < WCT; ++ct) {
                 const float mn = pm[ct] > m_ref[ct] + kRescaleLog2 ? pm[ct] : m_ref[ct];
                 const float alpha = m_ref[ct] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_ref[ct] - mn);
-                l_part[ct] *= alpha;
+                lsum[ct] *= alpha;
 #pragma unroll
                 for (int dt = 0; dt < NDT; ++dt) acc[ct][dt] *= alpha;
                 m_ref[ct] = mn;
             }
         }
-        // probabilities as bf16 pairs p_hi + p_lo.  A column whose keys in
-        // this half are all masked so far has no reference yet: offset 0
-        // keeps its p at exp2(-inf) = 0, not NaN
-        bf16x8_t phi[WCT], plo[WCT];
+        // P enters the PV product as one bf16 term once no key of the page
+        // can weigh much in its column: every column's largest probability
+        // on the page is at most kHiOnly of its running sum over this wave's
+        // keys (a lower bound of the column's sum).  The sum adds exactly the
+        // rounded values the product uses, so a rounding common to many keys
+        // cancels in the normalization; what remains is a relative 2^-9 per
+        // weight, independent across keys, on weights below kHiOnly.  Pages
+        // where some column fails the test (the first pages of every
+        // column, peaked distributions) add the second term p_lo.
+        bool need_lo = false;
+#pragma unroll
+        for (int ct = 0; ct < WCT; ++ct)
+            need_lo |= !(__builtin_amdgcn_exp2f(pm[ct] - m_ref[ct]) <= kHiOnly * lsum[ct][0]);
+        // probabilities; a column whose keys in this half are all masked so
+        // far has no reference yet: offset 0 keeps its p at exp2(-inf) = 0,
+        // not NaN
+        float p[WCT][8];
+        bf16x8_t phi[WCT];
 #pragma unroll
         for (int ct = 0; ct < WCT; ++ct) {
             const float moff = m_ref[ct] == -INFINITY ? 0.f : -m_ref[ct];
-            float p[8];
 #pragma unroll
             for (int e = 0; e < 8; ++e)
-                p[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[e >> 2][ct][e & 3], a.scale_log2, moff));
-            l_part[ct] += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
-            uint32_t hv[4], lv[4];
+                p[ct][e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[e >> 2][ct][e & 3], a.scale_log2, moff));
+            uint32_t hv[4];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) split_bf16(p[2 * e], p[2 * e + 1], hv[e], lv[e]);
+            for (int e = 0; e < 4; ++e)
+                hv[e] = __builtin_bit_cast(uint32_t,
+                                           __builtin_convertvector(f32x2_t{p[ct][2 * e], p[ct][2 * e + 1]}, bf16x2v_t));
             phi[ct] = __builtin_bit_cast(bf16x8_t, u32x4{hv[0], hv[1], hv[2], hv[3]});
-            plo[ct] = __builtin_bit_cast(bf16x8_t, u32x4{lv[0], lv[1], lv[2], lv[3]});
         }
-        // PV: the hi products of every 16-dim tile, then the lo ones (no
-        // product waits on the one before it)
 #pragma unroll
         for (int ct = 0; ct < WCT; ++ct) {
 #pragma unroll
             for (int dt = 0; dt < NDT; ++dt)
                 acc[ct][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[dt], phi[ct], acc[ct][dt], 0, 0, 0);
-#pragma unroll
-            for (int dt = 0; dt < NDT; ++dt)
-                acc[ct][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[dt], plo[ct], acc[ct][dt], 0, 0, 0);
+            lsum[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, phi[ct], lsum[ct], 0, 0, 0);
         }
-        // issue order: the first tile's probabilities, then its products one
-        // at a time between the second tile's vector work, then the second
-        // tile's products
-        __builtin_amdgcn_sched_group_barrier(0x002, kValuPerTile, 0);
+        if (__builtin_amdgcn_ballot_w64(need_lo)) {
+            // p_lo = rne(p - p_hi), the same products on it
 #pragma unroll
-        for (int k = 0; k < 2 * NDT; ++k) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x002, (kValuPerTile + 2 * NDT - 1) / (2 * NDT), 0);
+            for (int ct = 0; ct < WCT; ++ct) {
+                const u32x4 hu = __builtin_bit_cast(u32x4, phi[ct]);
+                uint32_t lv[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float r0 = p[ct][2 * e] - __uint_as_float(hu[e] << 16);
+                    const float r1 = p[ct][2 * e + 1] - __uint_as_float(hu[e] & 0xFFFF0000u);
+                    lv[e] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{r0, r1}, bf16x2v_t));
+                }
+                const bf16x8_t plo = __builtin_bit_cast(bf16x8_t, u32x4{lv[0], lv[1], lv[2], lv[3]});
+#pragma unroll
+                for (int dt = 0; dt < NDT; ++dt)
+                    acc[ct][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[dt], plo, acc[ct][dt], 0, 0, 0);
+                lsum[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, plo, lsum[ct], 0, 0, 0);
+            }
         }
-        __builtin_amdgcn_sched_group_barrier(0x008, 2 * NDT, 0);
     };
 
     for (int i0p = 0; i0p < npages; i0p += NS) {
@@ -448,7 +471,7 @@ __global__ void __launch_bounds__(512) verify_tile_kernel(VerifyArgs a) {
     // now), then wave cw writes its columns
     float lw[WCT];
 #pragma unroll
-    for (int ct = 0; ct < WCT; ++ct) lw[ct] = rows_sum(l_part[ct]);
+    for (int ct = 0; ct < WCT; ++ct) lw[ct] = lsum[ct][0];
     block_lds_barrier();                           // every wave is done with the ring
     float* xb = reinterpret_cast<float*>(&ring[0][0][0]) + cw * (WCT * NDT * 4 * 64);
     if (kh == 1) {

@@ -50,3 +50,20 @@ def test_verify_long_prefill_tiles_share_pages():
     wl = workloads.small(90, "BF16", hist=[3000, 2500], step=[300, 5], C=2, S=4096, Hq=8, H=2, D=128,
                          mode="verify")
     _check(wl, "prefill 300 + verify 5")
+
+
+def test_verify_long_histories_one_term_pages():
+    # long histories: past the first pages no key weighs more than 1/64 of its
+    # column's running sum, and the tiles take P as one bf16 term there
+    wl = workloads.small(91, "BF16", hist=[12000, 19937], step=[200, 141], C=2, S=20480, Hq=8, H=2, D=128,
+                         mode="verify")
+    _check(wl, "prefill 200 + 141 at 12K/20K keys")
+
+
+@pytest.mark.parametrize("scale_mul", [4.0, 16.0])
+def test_verify_peaked_softmax_keeps_two_terms(scale_mul):
+    # softmax scale x4 and x16: a few keys carry most of every column, the
+    # pages that hold them keep P as p_hi + p_lo
+    wl = workloads.small(92, "BF16", hist=[6000, 3001], step=[160, 64], C=2, S=8192, Hq=8, H=2, D=128,
+                         mode="verify", scale_mul=scale_mul)
+    _check(wl, f"peaked x{scale_mul}")

@@ -47,6 +47,7 @@ class Workload:
     cow: list                       # sequence copies its shared tail before the step
     mode: str = "decode"            # "decode" or "verify"
     outlier_frac: float = 0.0
+    scale_mul: float = 1.0          # softmax scale = scale_mul / sqrt(D) (> 1: peaked distributions)
     table_rows: list = field(default_factory=list)
     free_order: np.ndarray | None = None
 
@@ -65,7 +66,7 @@ class Workload:
 
     @property
     def sm_scale(self) -> float:
-        return float(np.float32(1.0) / np.sqrt(np.float32(self.D)))
+        return float(np.float32(self.scale_mul) / np.sqrt(np.float32(self.D)))
 
     @property
     def seq_lens(self) -> list:
@@ -225,7 +226,8 @@ def get(k: int) -> Workload:
 
 def small(seed: int, profile: str = "BF16", *, B: int = 3, C: int = 4, Hq: int = 8, H: int = 2,
           D: int = 128, S: int = 1024, layers: int = 1, mode: str = "decode", hist=None, step=None,
-          fork=None, cow=None, outlier_frac: float = 0.0, M: int | None = None) -> Workload:
+          fork=None, cow=None, outlier_frac: float = 0.0, M: int | None = None,
+          scale_mul: float = 1.0) -> Workload:
     """A randomized small case (several pages, ragged tails) the oracle finishes in seconds."""
     r = rng_for(5000 + seed, 9)
     if hist is None:
@@ -238,4 +240,4 @@ def small(seed: int, profile: str = "BF16", *, B: int = 3, C: int = 4, Hq: int =
     L = -(-S // 64)
     return Workload(f"small{seed}_{profile}", profile, C=C, S=S, M=M or C * L, layers=layers, Hq=Hq, H=H,
                     D=D, seed=5000 + seed, hist=list(hist), step=list(step), fork=list(fork), cow=list(cow),
-                    mode=mode, outlier_frac=outlier_frac)
+                    mode=mode, outlier_frac=outlier_frac, scale_mul=scale_mul)
