@@ -41,13 +41,21 @@ DECODE_SRC = [os.path.join(ROOT, "paged_kv_cache_03_amd", "csrc", f)
                         "stream_plan.hip")]
 
 
-def decode_source_sha256() -> str:
+# sources of one paged_attn_verify call: the tile kernel and the page stream in chunk mode
+VERIFY_SRC = [os.path.join(ROOT, "paged_kv_cache_03_amd", "csrc", "verify.hip")] + DECODE_SRC
+
+
+def source_sha256(paths) -> str:
     import hashlib
     h = hashlib.sha256()
-    for path in DECODE_SRC:
+    for path in paths:
         with open(path, "rb") as f:
             h.update(f.read())
     return h.hexdigest()
+
+
+def decode_source_sha256() -> str:
+    return source_sha256(DECODE_SRC)
 
 
 def log(msg: str) -> None:
@@ -91,12 +99,14 @@ def decode_kernel_name(wl) -> str:
     return "decode_split_kernel + decode_combine_kernel"
 
 
-def measured_traffic(wl) -> int | None:
-    """HBM bytes per decode launch from the committed rocprofv3 counter summary
-    (FETCH_SIZE + WRITE_SIZE, each scaled by what the same counter reads for a
-    plain device copy of known size), or None when there is none for this
-    workload or the decode source has changed since it was taken."""
-    path = os.path.join(PROFILES, f"decode_traffic_{wl.name}.txt")
+def measured_traffic(wl, kind: str = "decode") -> int | None:
+    """HBM bytes per decode launch (kind "decode") or per verify call (kind
+    "verify": every kernel of one paged_attn_verify call) from the committed
+    rocprofv3 counter summary (FETCH_SIZE + WRITE_SIZE, each scaled by what the
+    same counter reads for a plain device copy of known size), or None when
+    there is none for this workload or the sources have changed since it was
+    taken."""
+    path = os.path.join(PROFILES, f"{kind}_traffic_{wl.name}.txt")
     if not os.path.exists(path):
         return None
     kv = {}
@@ -104,7 +114,11 @@ def measured_traffic(wl) -> int | None:
         if ":" in line and not line.startswith("#"):
             k, v = line.split(":", 1)
             kv[k.strip()] = v.strip()
-    if kv.get("source_sha256") != decode_source_sha256() or kv.get("kernel") != decode_kernel_name(wl):
+    if kind == "decode":
+        sha, kernel = decode_source_sha256(), decode_kernel_name(wl)
+    else:
+        sha, kernel = source_sha256(VERIFY_SRC), verify_kernel_names(wl)
+    if kv.get("source_sha256") != sha or kv.get("kernel") != kernel:
         return None
     try:
         return int(float(kv["traffic_bytes_per_dispatch"]))
@@ -258,7 +272,8 @@ def bench_verify(wl, args) -> int:
                    "frontiers": list(wl.hist), "page_size": 64, "pool_pages": wl.M},
         "roofline": {"kernel": verify_kernel_names(wl), "bound": "mfma", "achieved": round(tflops, 2),
                      "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
-                     "traffic": None, "flops_per_launch": flops, "kv_bytes_per_launch": kv_bytes,
+                     "traffic": measured_traffic(wl, "verify"), "flops_per_launch": flops,
+                     "kv_bytes_per_launch": kv_bytes,
                      "launch_ms": round(ver_ms, 5)},
         "cpu_baseline": None,
     }
