@@ -8,7 +8,10 @@ Source: NInfer "Paged KV Context Store" maintainer page --
   * address-translation equations: b = floor(p/P), o = p mod P,
     g = block_table[b], addr = base + d*nb0 + o*nb1 + h*nb2 + g*nb3;
   * D256 payload table (bytes per token and KV head);
-  * PageBytes = sum over planes of PlaneBytesPerToken * P.
+  * PageBytes = sum over planes of PlaneBytesPerToken * P;
+  * physical pages per backend (capacity of the selected backend): an MTP
+    draft pool with window K holds M + C * ceil((K - 1) / P) pages, covering
+    each active row's provisional lead of one speculative round.
 """
 
 from __future__ import annotations
@@ -43,6 +46,15 @@ def m_bounds(S: int, C: int) -> tuple[int, int]:
     """(M_min, M_max) = (max(L, C), C*L) -- capacity geometry."""
     L = logical_pages(S)
     return max(L, C), C * L
+
+
+def draft_pool_pages(M: int, C: int, K: int) -> int:
+    """Physical pages of the MTP draft pool for draft window K >= 1 (backend
+    capacity list): the Main pool's M plus one provisional lead of K - 1
+    tokens per active row, in whole pages."""
+    if K < 1:
+        raise ValueError("draft window must be >= 1")
+    return M + C * ceil_div(K - 1, P)
 
 
 def explicit_capacity(k_main_tokens: int, S: int, C: int) -> int:

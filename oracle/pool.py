@@ -14,12 +14,26 @@ Source: NInfer "Paged KV Context Store" maintainer page --
     F = 1000 -> 15 full pages + 40 tail columns, frontier not rounded down;
   * writer-cardinality rules: a page with several address-space references
     is immutable; a write into a shared tail is refused until it is copied;
-  * finish/release rules: drop references, free a page on its last one.
+  * finish/release rules: drop references, free a page on its last one;
+  * speculative units: the accepted prefix is committed
+    (1 <= accepted <= produced for a row that is not cancelled, 0 for a
+    cancelled one), then the retained membership is
+    NeededPages = ceil(max(committed, provisional) / P): trailing mappings past
+    it are removed, the last partial page stays, and the removed device leases
+    go back to the address space's own active reservation, not to the global
+    available capacity; bytes past the frontier inside the kept page are not
+    in the valid domain and are overwritten by the next canonical write;
+  * the active reservation (growth entitlement) is released at finish.
 
 The free-list discipline is this build's reading (the pages leave it open and
 say correctness must not depend on it): pages are taken from the front of a
 FIFO seeded with a caller-given order of [0, M), and freed pages are appended
-at its back in logical-block order.  The C ABI follows the same rule, so block
+at its back in logical-block order.  A reservation is a FIFO of concrete page
+groups held by one address space: reserve() moves groups from the front of
+the pool's FIFO to the back of the reservation, a trim appends the removed
+groups there in logical-block order, a mapping takes from the reservation's
+front before the pool's, and release returns the reservation to the back of
+the pool's FIFO in its order.  The C ABI follows the same rules, so block
 tables can be compared bit for bit.
 """
 
@@ -32,7 +46,7 @@ import numpy as np
 
 from .geometry import P, ceil_div, logical_pages, m_bounds
 
-OK, CAPACITY, SHARED_WRITE, INVALID, STALE = "OK", "CAPACITY", "SHARED_WRITE", "INVALID", "STALE"
+OK, CAPACITY, SHARED_WRITE, INVALID, STALE, UNMAPPED = "OK", "CAPACITY", "SHARED_WRITE", "INVALID", "STALE", "UNMAPPED"
 
 
 @dataclass
@@ -40,6 +54,7 @@ class AddressSpace:
     row: int
     pages: list = field(default_factory=list)   # logical block -> page-group id
     frontier: int = 0                            # committed frontier (tokens)
+    reserve: deque = field(default_factory=deque)   # active reservation: held page groups
 
 
 class OraclePool:
@@ -59,12 +74,14 @@ class OraclePool:
 
     # --------------------------------------------------------- accounting --
     def stats(self) -> tuple[int, int, int]:
-        """(allocated, reserved, available); reserved is always 0 here."""
+        """(allocated, reserved, available): groups with references, groups
+        held in reservations, groups in the pool's free list."""
+        reserved = sum(len(s.reserve) for s in self.spaces.values())
         available = len(self.free)
-        return self.M - available, 0, available
+        return self.M - reserved - available, reserved, available
 
-    def _alloc(self) -> int:
-        g = self.free.popleft()
+    def _alloc(self, s: AddressSpace | None = None) -> int:
+        g = s.reserve.popleft() if s is not None and s.reserve else self.free.popleft()
         assert self.refs[g] == 0
         self.refs[g] = 1
         return g
@@ -120,13 +137,53 @@ class OraclePool:
         need = ceil_div(tokens, P) - len(s.pages)
         if need <= 0:
             return OK, 0
-        if need > len(self.free):
-            return CAPACITY, need - len(self.free)
+        have = len(s.reserve) + len(self.free)
+        if need > have:
+            return CAPACITY, need - have
         for _ in range(need):
-            g = self._alloc()
+            g = self._alloc(s)
             s.pages.append(g)
             self.table[s.row, len(s.pages) - 1] = g
         return OK, 0
+
+    def reserve(self, sid: int, n: int) -> tuple[str, int]:
+        """Move n page groups from the pool's free list into the address
+        space's reservation; a shortfall returns the deficit, moves nothing."""
+        s = self.spaces[sid]
+        if n > len(self.free):
+            return CAPACITY, n - len(self.free)
+        for _ in range(n):
+            s.reserve.append(self.free.popleft())
+        return OK, 0
+
+    def trim(self, sid: int, provisional: int) -> str:
+        """Keep NeededPages = ceil(max(frontier, provisional) / P) mappings;
+        the trailing ones are removed and their groups, once unreferenced, go
+        to the address space's reservation (in logical-block order)."""
+        s = self.spaces[sid]
+        if provisional > self.S:
+            return INVALID
+        keep = ceil_div(max(s.frontier, provisional), P)
+        for b in range(keep, len(s.pages)):
+            g = s.pages[b]
+            self.refs[g] -= 1
+            assert self.refs[g] >= 0
+            if self.refs[g] == 0:
+                s.reserve.append(g)
+            self.table[s.row, b] = -1
+        del s.pages[keep:]
+        return OK
+
+    def commit_accepted(self, sid: int, produced: int, accepted: int, cancelled: bool = False) -> str:
+        """Close a speculative unit that wrote `produced` rows from the
+        committed frontier: commit the accepted prefix, then trim to it."""
+        s = self.spaces[sid]
+        if produced < 1 or (accepted != 0 if cancelled else not 1 <= accepted <= produced):
+            return INVALID
+        if s.frontier + produced > P * len(s.pages):
+            return UNMAPPED
+        s.frontier += accepted
+        return self.trim(sid, s.frontier)
 
     def commit(self, sid: int, frontier: int) -> str:
         s = self.spaces[sid]
@@ -149,9 +206,9 @@ class OraclePool:
         g = s.pages[b]
         if self.refs[g] == 1:
             return OK, None
-        if not self.free:
+        if not s.reserve and not self.free:
             return CAPACITY, None
-        g2 = self._alloc()
+        g2 = self._alloc(s)
         s.pages[b] = g2
         self.table[s.row, b] = g2
         self._unref(g)
@@ -161,6 +218,7 @@ class OraclePool:
         s = self.spaces.pop(sid)
         for g in s.pages:
             self._unref(g)
+        self.free.extend(s.reserve)
         self.table[s.row, :] = -1
 
     # ------------------------------------------------------------ queries --
@@ -172,3 +230,6 @@ class OraclePool:
 
     def frontier_of(self, sid: int) -> int:
         return self.spaces[sid].frontier
+
+    def reserved_of(self, sid: int) -> list:
+        return list(self.spaces[sid].reserve)
