@@ -282,6 +282,111 @@ def bench_verify(wl, args) -> int:
     return 0
 
 
+def bench_spec(wl, args) -> int:
+    """Speculative rounds on the histories of the verify workload: per round and
+    entry, map T = 5 draft rows (from the entry's reservation first), append
+    them, one paged_attn_verify call for the batch (5-token chunks: the page
+    stream, bound by HBM), then commit a seeded accepted prefix (1..5 rows)
+    and trim the trailing pages into the entry's reservation.  The frontiers
+    advance by the accepted rows, so each round reads a slightly longer
+    history.  `value` is rounds per second; the roofline covers the verify
+    call (KV bytes of the four histories per launch)."""
+    import numpy as np
+    import torch
+    from paged_kv_cache_03_amd.device_pool import i32
+    from workloads.device_driver import _dev, build_device
+    from workloads.gen import bf16_normal, rng_for
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    t0 = time.time()
+    log(f"workload {wl.name}: filling the history for speculative rounds")
+    dp, seqs, _ = build_device(wl, zero=False, step_append=False)
+    log(f"history resident after {time.time() - t0:.1f} s")
+    T, B = 5, wl.B
+    rounds = max(1, min(args.steps, 40))
+    warm = min(args.warmup, 3)
+    total_rounds = warm + 2 * rounds
+    r = rng_for(7700, 0)
+    acc = r.integers(1, T + 1, size=(total_rounds, B))
+    if max(wl.hist) + int(acc.sum(axis=0).max()) + T > wl.S:
+        raise SystemExit("speculative rounds would pass the maximum context")
+    kd = _dev(bf16_normal(r, (B * T, wl.H, wl.D)), dev)
+    vd = _dev(bf16_normal(r, (B * T, wl.H, wl.D)), dev)
+    qd = _dev(bf16_normal(r, (B * T, wl.Hq, wl.D)), dev)
+    rows_t, cu_t = i32(wl.table_rows, dev), i32([T * b for b in range(B + 1)], dev)
+    out = torch.empty((B * T, wl.Hq, wl.D), dtype=torch.float32, device=dev)
+    max_ctx = wl.S
+    ws = dp.workspace(B, wl.Hq, max_ctx, T)
+    front = list(wl.hist)
+    # one pinned host buffer of frontiers per round, copied to the device in order
+    pos_host = torch.empty((total_rounds, B), dtype=torch.int32, pin_memory=True)
+    pos_dev = torch.empty((total_rounds, B), dtype=torch.int32, device=dev)
+    host_s = [0.0]
+
+    def one(k, events=None):
+        h0 = time.perf_counter()
+        for b in range(B):
+            dp.ensure_mapped(seqs[b], front[b] + T)
+        pos_host[k] = torch.tensor(front, dtype=torch.int32)
+        host_s[0] += time.perf_counter() - h0
+        pos_dev[k].copy_(pos_host[k], non_blocking=True)
+        dp.append(0, rows_t, pos_dev[k], cu_t, B * T, kd, vd)
+        if events is not None:
+            events[0].record()
+        dp.verify(0, wl.Hq, rows_t, pos_dev[k], cu_t, B * T, T, max_ctx, qd, wl.sm_scale, out, ws)
+        if events is not None:
+            events[1].record()
+        h0 = time.perf_counter()
+        for b in range(B):
+            dp.commit_accepted(seqs[b], T, int(acc[k, b]))
+            front[b] += int(acc[k, b])
+        host_s[0] += time.perf_counter() - h0
+
+    for k in range(warm):
+        one(k)
+    torch.cuda.synchronize()
+    host_s[0] = 0.0
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for k in range(warm, warm + rounds):
+        one(k)
+    end.record()
+    torch.cuda.synchronize()
+    ms_round = start.elapsed_time(end) / rounds
+    host_us = host_s[0] / rounds * 1e6
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(rounds)]
+    for i, k in enumerate(range(warm + rounds, warm + 2 * rounds)):
+        one(k, evs[i])
+    torch.cuda.synchronize()
+    ver_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    a_, res_, v_ = dp.stats()
+    reserved = [dp.reservation(seqs[b]) for b in range(B)]
+    bpth = bytes_per_token_head(wl.profile, wl.D)
+    kv_bytes = sum(front) * wl.H * bpth          # the last round's histories, about those of every round
+    achieved = kv_bytes / (ver_ms * 1e-3) / 1e9
+    line = {
+        "metric": "speculative verify rounds/s (C=4, T=5 drafts, commit accepted + trim, 128K ctx)",
+        "value": round(1000.0 / ms_round, 2), "unit": "rounds/s", "n_gpus": 1, "steps": rounds, "warmup": warm,
+        "ms_per_step": round(ms_round, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": wl.name + "_spec_rounds", "profile": wl.profile, "batch": B, "layers": 1,
+                   "q_heads": wl.Hq, "kv_heads": wl.H, "head_dim": wl.D, "draft_tokens": T,
+                   "accepted_mean": round(float(acc.mean()), 3), "frontiers_start": list(wl.hist),
+                   "page_size": 64, "pool_pages": wl.M},
+        "host_us_per_round": round(host_us, 1),
+        "pool_after": {"allocated": a_, "reserved": res_, "available": v_, "reserved_per_entry": reserved},
+        "roofline": {"kernel": "paged_vstream_kernel<%d, %d, 2, true>" % (wl.D, wl.Hq // wl.H), "bound": "hbm",
+                     "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None, "bytes_per_launch": kv_bytes,
+                     "launch_ms": round(ver_ms, 5)},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(line), flush=True)
+    dp.close()
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -289,6 +394,8 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", type=int, default=2, help="workload number (1-4: decode, 5: verify/prefill)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--spec", action="store_true",
+                    help="with --config 5: speculative rounds (draft, verify, commit the accepted prefix, trim)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a 1 GiB device copy (counter calibration under rocprofv3 --pmc)")
     args = ap.parse_args()
@@ -308,6 +415,11 @@ def main() -> int:
     from workloads.device_driver import _dev, build_device
 
     wl = workloads.get(args.config)
+    if args.spec:
+        if wl.mode != "verify":
+            print("--spec needs the verify workload (--config 5)", file=sys.stderr)
+            return 2
+        return bench_spec(wl, args)
     if wl.mode != "decode":
         return bench_verify(wl, args)
     dev = torch.device("cuda:0")

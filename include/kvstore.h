@@ -135,8 +135,10 @@ kv_status kv_pool_create(const KVPageGeometry* geo, const KVPlaneDesc* planes, u
  * caller's to free afterwards.  NULL is ignored. */
 void kv_pool_destroy(kv_pool* pool);
 
-/* Lease accounting: allocated + reserved + available == M.  Reserved is
- * always 0 here (no entitlement reservations in this build). */
+/* Lease accounting: allocated + reserved + available == M.  allocated:
+ * page groups with references; reserved: groups held in address spaces'
+ * active reservations (kv_seq_reserve, kv_seq_trim); available: the free
+ * list. */
 kv_status kv_pool_stats(const kv_pool* pool, uint32_t* allocated, uint32_t* reserved, uint32_t* available);
 
 /* Copy the host mirror of the block-table matrix, int32 [C][L], into out. */
@@ -180,6 +182,49 @@ kv_status kv_seq_commit(kv_pool* pool, kv_seq seq, uint32_t frontier);
  * freed on its last one), release its table row (set to -1 on `stream`) and
  * retire the handle (later use returns KV_E_STALE). */
 kv_status kv_seq_release(kv_pool* pool, kv_seq seq, hipStream_t stream);
+
+/* Active reservation (Paged KV Context Store page, lease accounting and
+ * active-reservation rules): move `pages` page groups from the front of the
+ * free list to the back of this address space's reservation, a FIFO of
+ * concrete groups that only this space maps from.  kv_seq_ensure_mapped and
+ * kv_cow_tail_page take from the reservation's front before the free list;
+ * kv_seq_release returns the reservation to the back of the free list, in
+ * its order.  Host metadata only.
+ *   *deficit : the missing count on KV_E_CAPACITY (nothing moves), else 0. */
+kv_status kv_seq_reserve(kv_pool* pool, kv_seq seq, uint32_t pages, uint32_t* deficit);
+
+/* Trim the membership of a speculative unit (Paged KV Context Store page,
+ * retained-membership equation and speculative termination): keep
+ * NeededPages = ceil(max(committed frontier, provisional) / 64) mappings;
+ * the trailing ones are removed from the row (-1, published on `stream`) and
+ * each group whose last reference this was goes to the back of this space's
+ * reservation, in logical-block order -- not to the free list, so no other
+ * address space can map it.  The last partial page stays mapped; its bytes
+ * past the frontier are outside the valid domain and the next append at the
+ * frontier overwrites them.  The publication is ordered after every kernel
+ * enqueued earlier on `stream` (a verify still reading the removed pages);
+ * work on other streams must be ordered by the caller.  A no-op when nothing
+ * trails.  KV_E_INVALID: provisional > max_context. */
+kv_status kv_seq_trim(kv_pool* pool, kv_seq seq, uint32_t provisional, hipStream_t stream);
+
+/* Close a speculative unit that wrote `produced` rows from the committed
+ * frontier (accepted-prefix commit, Engine Architecture page: a row that is
+ * not cancelled accepts 1 <= accepted <= produced, a cancelled row 0): the
+ * frontier advances by `accepted`, then kv_seq_trim(seq, new frontier).
+ * KV_E_INVALID on the bounds; KV_E_UNMAPPED if frontier + produced is past
+ * the mapping (nothing changes then). */
+kv_status kv_seq_commit_accepted(kv_pool* pool, kv_seq seq, uint32_t produced, uint32_t accepted, int cancelled,
+                                 hipStream_t stream);
+
+/* Page groups held in this address space's reservation. */
+kv_status kv_seq_reservation(const kv_pool* pool, kv_seq seq, uint32_t* pages);
+
+/* Physical pages of an MTP draft pool with draft window K >= 1 next to a Main
+ * pool of `main_pages` (Paged KV Context Store page, backend capacity list):
+ * main_pages + max_concurrency * ceil((K - 1) / 64), one provisional lead of
+ * K - 1 tokens per active row.  KV_E_INVALID if K == 0. */
+kv_status kv_draft_pool_pages(uint32_t main_pages, uint32_t max_concurrency, uint32_t draft_window,
+                              uint32_t* pages);
 
 /* Row, committed frontier and mapped page count of a live address space. */
 kv_status kv_seq_info(const kv_pool* pool, kv_seq seq, uint32_t* table_row, uint32_t* frontier,

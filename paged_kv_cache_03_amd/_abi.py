@@ -26,7 +26,8 @@ KV_ROLE_K_CODE, KV_ROLE_K_SCALE, KV_ROLE_V_CODE, KV_ROLE_V_SCALE = range(4)
 # exported symbols, in header order (the CPU test checks the header declares exactly these)
 EXPORTS = ["kv_profile_planes", "kv_plane_bytes", "kv_pool_create", "kv_pool_destroy", "kv_pool_stats",
            "kv_pool_table_host", "kv_pool_page_refs", "kv_seq_open", "kv_seq_fork", "kv_seq_ensure_mapped",
-           "kv_seq_commit", "kv_seq_release", "kv_seq_info", "kv_cow_tail_page", "kv_append",
+           "kv_seq_commit", "kv_seq_release", "kv_seq_reserve", "kv_seq_trim", "kv_seq_commit_accepted",
+           "kv_seq_reservation", "kv_draft_pool_pages", "kv_seq_info", "kv_cow_tail_page", "kv_append",
            "paged_attn_workspace_bytes", "paged_attn_decode", "paged_attn_decode_plan", "paged_attn_decode_run",
            "paged_attn_decode_append_run",
            "paged_attn_verify", "paged_attn_supported",
@@ -78,6 +79,11 @@ def _load():
         "kv_seq_ensure_mapped": (i32, [vp, ctypes.c_uint64, u32, P(u32), vp]),
         "kv_seq_commit": (i32, [vp, ctypes.c_uint64, u32]),
         "kv_seq_release": (i32, [vp, ctypes.c_uint64, vp]),
+        "kv_seq_reserve": (i32, [vp, ctypes.c_uint64, u32, P(u32)]),
+        "kv_seq_trim": (i32, [vp, ctypes.c_uint64, u32, vp]),
+        "kv_seq_commit_accepted": (i32, [vp, ctypes.c_uint64, u32, u32, ctypes.c_int, vp]),
+        "kv_seq_reservation": (i32, [vp, ctypes.c_uint64, P(u32)]),
+        "kv_draft_pool_pages": (i32, [u32, u32, u32, P(u32)]),
         "kv_seq_info": (i32, [vp, ctypes.c_uint64, P(u32), P(u32), P(u32)]),
         "kv_cow_tail_page": (i32, [vp, ctypes.c_uint64, vp]),
         "kv_append": (i32, [vp, u32, u32, vp, vp, vp, u32, vp, vp, vp]),
@@ -180,6 +186,33 @@ def kv_seq_commit(pool: int, seq: int, frontier: int) -> None:
 
 def kv_seq_release(pool: int, seq: int, stream: int = 0) -> None:
     _check(_lib.kv_seq_release(pool, seq, stream or None))
+
+
+def kv_seq_reserve(pool: int, seq: int, pages: int) -> None:
+    deficit = ctypes.c_uint32()
+    st = _lib.kv_seq_reserve(pool, seq, pages, ctypes.byref(deficit))
+    _check(st, deficit.value)
+
+
+def kv_seq_trim(pool: int, seq: int, provisional: int, stream: int = 0) -> None:
+    _check(_lib.kv_seq_trim(pool, seq, provisional, stream or None))
+
+
+def kv_seq_commit_accepted(pool: int, seq: int, produced: int, accepted: int, cancelled: bool = False,
+                           stream: int = 0) -> None:
+    _check(_lib.kv_seq_commit_accepted(pool, seq, produced, accepted, int(bool(cancelled)), stream or None))
+
+
+def kv_seq_reservation(pool: int, seq: int) -> int:
+    out = ctypes.c_uint32()
+    _check(_lib.kv_seq_reservation(pool, seq, ctypes.byref(out)))
+    return out.value
+
+
+def kv_draft_pool_pages(main_pages: int, max_concurrency: int, draft_window: int) -> int:
+    out = ctypes.c_uint32()
+    _check(_lib.kv_draft_pool_pages(main_pages, max_concurrency, draft_window, ctypes.byref(out)))
+    return out.value
 
 
 def kv_seq_info(pool: int, seq: int) -> tuple:

@@ -6,9 +6,13 @@
 //   - capacity geometry L = ceil(S/P), M in [max(L, C), C*L];
 //   - lease accounting allocated + reserved + available = capacity;
 //   - KVAddressSpace: ordered block -> page membership, committed frontier,
-//     execution-row lease; device block-table matrix [N_logical, C];
+//     execution-row lease, active reservation; device block-table matrix
+//     [N_logical, C];
 //   - ensure_mapped_to_tokens, Fork (+ worked example), writer cardinality,
-//     finish/release, mapping publication order.
+//     finish/release, mapping publication order;
+//   - speculative units: accepted-prefix commit, then the retained membership
+//     ceil(max(committed, provisional) / P); removed trailing leases go back
+//     to the address space's own reservation.
 // Allocator work never runs inside a kernel (GPU-unit stability list): every
 // mutation here is host metadata plus an ordered publication on the caller's
 // stream.
@@ -95,6 +99,7 @@ struct Space {
     uint32_t row = 0;
     uint32_t frontier = 0;
     std::vector<int32_t> pages;   // logical block -> page-group id
+    std::deque<int32_t> reserve;  // active reservation: page groups held for this space, FIFO
 };
 
 }  // namespace
@@ -141,6 +146,7 @@ struct kv_pool {
         s.row = row;
         s.frontier = 0;
         s.pages.clear();
+        s.reserve.clear();
         row_owner[row] = int32_t(slot);
         std::fill(h_table.begin() + size_t(row) * L, h_table.begin() + size_t(row + 1) * L, -1);
         *out = (uint64_t(s.gen) << 32) | uint64_t(slot);
@@ -148,11 +154,20 @@ struct kv_pool {
         return KV_OK;
     }
 
-    int32_t alloc() {
-        int32_t g = free_q.front();
-        free_q.pop_front();
+    // a page group for space s: from its reservation first, else the free list
+    int32_t alloc(Space* s = nullptr) {
+        std::deque<int32_t>& q = (s && !s->reserve.empty()) ? s->reserve : free_q;
+        int32_t g = q.front();
+        q.pop_front();
         refs[g] = 1;
         return g;
+    }
+
+    uint32_t reserved_total() const {
+        size_t n = 0;
+        for (const Space& s : spaces)
+            if (s.live) n += s.reserve.size();
+        return uint32_t(n);
     }
 
     void unref(int32_t g) {
@@ -321,9 +336,9 @@ void kv_pool_destroy(kv_pool* pool) {
 
 kv_status kv_pool_stats(const kv_pool* pool, uint32_t* allocated, uint32_t* reserved, uint32_t* available) {
     if (!pool) return fail(KV_E_INVALID, "null pool");
-    uint32_t avail = uint32_t(pool->free_q.size());
-    if (allocated) *allocated = pool->geo.num_page_groups - avail;
-    if (reserved) *reserved = 0;
+    uint32_t avail = uint32_t(pool->free_q.size()), held = pool->reserved_total();
+    if (allocated) *allocated = pool->geo.num_page_groups - avail - held;
+    if (reserved) *reserved = held;
     if (available) *available = avail;
     return ok();
 }
@@ -388,12 +403,13 @@ kv_status kv_seq_ensure_mapped(kv_pool* pool, kv_seq seq, uint32_t tokens, uint3
     uint32_t have = uint32_t(s->pages.size());
     if (need_pages <= have) return ok();
     uint32_t need = need_pages - have;
-    if (need > pool->free_q.size()) {
-        if (deficit) *deficit = need - uint32_t(pool->free_q.size());
+    uint32_t can = uint32_t(s->reserve.size() + pool->free_q.size());
+    if (need > can) {
+        if (deficit) *deficit = need - can;
         return fail(KV_E_CAPACITY, "not enough free page groups");
     }
     for (uint32_t i = 0; i < need; ++i) {
-        int32_t g = pool->alloc();
+        int32_t g = pool->alloc(s);
         s->pages.push_back(g);
         pool->h_table[size_t(s->row) * pool->L + s->pages.size() - 1] = g;
     }
@@ -416,11 +432,78 @@ kv_status kv_seq_release(kv_pool* pool, kv_seq seq, hipStream_t stream) {
     if (!s) return fail(KV_E_STALE, "stale or unknown handle");
     for (int32_t g : s->pages) pool->unref(g);
     s->pages.clear();
+    pool->free_q.insert(pool->free_q.end(), s->reserve.begin(), s->reserve.end());
+    s->reserve.clear();
     s->live = false;
     uint32_t row = s->row;
     pool->row_owner[row] = -1;
     std::fill(pool->h_table.begin() + size_t(row) * pool->L, pool->h_table.begin() + size_t(row + 1) * pool->L, -1);
     return pool->publish(row, 0, pool->L, stream);
+}
+
+kv_status kv_seq_reserve(kv_pool* pool, kv_seq seq, uint32_t pages, uint32_t* deficit) {
+    if (deficit) *deficit = 0;
+    if (!pool) return fail(KV_E_INVALID, "null pool");
+    Space* s = pool->lookup(seq);
+    if (!s) return fail(KV_E_STALE, "stale or unknown handle");
+    if (pages > pool->free_q.size()) {
+        if (deficit) *deficit = pages - uint32_t(pool->free_q.size());
+        return fail(KV_E_CAPACITY, "not enough free page groups to reserve");
+    }
+    for (uint32_t i = 0; i < pages; ++i) {
+        s->reserve.push_back(pool->free_q.front());
+        pool->free_q.pop_front();
+    }
+    return ok();
+}
+
+kv_status kv_seq_trim(kv_pool* pool, kv_seq seq, uint32_t provisional, hipStream_t stream) {
+    if (!pool) return fail(KV_E_INVALID, "null pool");
+    Space* s = pool->lookup(seq);
+    if (!s) return fail(KV_E_STALE, "stale or unknown handle");
+    if (provisional > pool->geo.max_context) return fail(KV_E_INVALID, "provisional extent beyond max_context");
+    const uint32_t keep = ceil_div(std::max(s->frontier, provisional), kPage);
+    const uint32_t have = uint32_t(s->pages.size());
+    if (keep >= have) return ok();
+    for (uint32_t b = keep; b < have; ++b) {
+        const int32_t g = s->pages[b];
+        if (--pool->refs[g] == 0) s->reserve.push_back(g);
+        pool->h_table[size_t(s->row) * pool->L + b] = -1;
+    }
+    s->pages.resize(keep);
+    return pool->publish(s->row, keep, have, stream);
+}
+
+kv_status kv_seq_commit_accepted(kv_pool* pool, kv_seq seq, uint32_t produced, uint32_t accepted, int cancelled,
+                                 hipStream_t stream) {
+    if (!pool) return fail(KV_E_INVALID, "null pool");
+    Space* s = pool->lookup(seq);
+    if (!s) return fail(KV_E_STALE, "stale or unknown handle");
+    if (produced < 1) return fail(KV_E_INVALID, "a speculative unit produces at least one row");
+    if (cancelled ? accepted != 0 : (accepted < 1 || accepted > produced))
+        return fail(KV_E_INVALID, "accepted rows outside [1, produced] (0 for a cancelled row)");
+    if (uint64_t(s->frontier) + produced > uint64_t(kPage) * s->pages.size())
+        return fail(KV_E_UNMAPPED, "produced rows beyond the mapping");
+    s->frontier += accepted;
+    return kv_seq_trim(pool, seq, s->frontier, stream);
+}
+
+kv_status kv_seq_reservation(const kv_pool* pool, kv_seq seq, uint32_t* pages) {
+    if (!pool || !pages) return fail(KV_E_INVALID, "null argument");
+    Space* s = const_cast<kv_pool*>(pool)->lookup(seq);
+    if (!s) return fail(KV_E_STALE, "stale or unknown handle");
+    *pages = uint32_t(s->reserve.size());
+    return ok();
+}
+
+kv_status kv_draft_pool_pages(uint32_t main_pages, uint32_t max_concurrency, uint32_t draft_window,
+                              uint32_t* pages) {
+    if (!pages) return fail(KV_E_INVALID, "null argument");
+    if (draft_window < 1) return fail(KV_E_INVALID, "draft window must be >= 1");
+    const uint64_t n = uint64_t(main_pages) + uint64_t(max_concurrency) * ceil_div(draft_window - 1, kPage);
+    if (n > UINT32_MAX) return fail(KV_E_GEOMETRY, "draft pool too large");
+    *pages = uint32_t(n);
+    return ok();
 }
 
 kv_status kv_seq_info(const kv_pool* pool, kv_seq seq, uint32_t* table_row, uint32_t* frontier,
@@ -443,8 +526,9 @@ kv_status kv_cow_tail_page(kv_pool* pool, kv_seq seq, hipStream_t stream) {
     uint32_t b = s->frontier / kPage;
     int32_t src = s->pages[b];
     if (pool->refs[src] == 1) return ok();
-    if (pool->free_q.empty()) return fail(KV_E_CAPACITY, "no free page group for the tail copy");
-    int32_t dst = pool->alloc();
+    if (s->reserve.empty() && pool->free_q.empty()) return fail(KV_E_CAPACITY, "no free page group for the tail copy");
+    const bool from_reserve = !s->reserve.empty();
+    int32_t dst = pool->alloc(s);
     if (pool->device()) {
         std::vector<CopyPlane> cp;
         cp.reserve(pool->planes.size());
@@ -452,7 +536,8 @@ kv_status kv_cow_tail_page(kv_pool* pool, kv_seq seq, hipStream_t stream) {
         hipError_t e = launch_cow_copy(cp.data(), int(cp.size()), int(pool->geo.num_kv_heads), src, dst, int(cols),
                                        stream);
         if (e != hipSuccess) {
-            pool->unref(dst);
+            pool->refs[dst] = 0;   // back to the front of the queue it came from
+            (from_reserve ? s->reserve : pool->free_q).push_front(dst);
             return fail(KV_E_DEVICE, std::string("tail copy: ") + hipGetErrorString(e));
         }
     }

@@ -95,6 +95,18 @@ class DevicePool:
     def release(self, seq: int) -> None:
         abi.kv_seq_release(self.handle, seq, self.stream)
 
+    def reserve(self, seq: int, pages: int) -> None:
+        abi.kv_seq_reserve(self.handle, seq, pages)
+
+    def trim(self, seq: int, provisional: int) -> None:
+        abi.kv_seq_trim(self.handle, seq, provisional, self.stream)
+
+    def commit_accepted(self, seq: int, produced: int, accepted: int, cancelled: bool = False) -> None:
+        abi.kv_seq_commit_accepted(self.handle, seq, produced, accepted, cancelled, self.stream)
+
+    def reservation(self, seq: int) -> int:
+        return abi.kv_seq_reservation(self.handle, seq)
+
     def info(self, seq: int):
         return abi.kv_seq_info(self.handle, seq)
 

@@ -124,7 +124,16 @@ def test_compute_calls_refuse_host_only_pool():
     abi.kv_pool_destroy(h)
 
 
-STATUS = {abi.KV_E_CAPACITY: "CAPACITY", abi.KV_E_SHARED_WRITE: "SHARED_WRITE", abi.KV_E_INVALID: "INVALID"}
+STATUS = {abi.KV_E_CAPACITY: "CAPACITY", abi.KV_E_SHARED_WRITE: "SHARED_WRITE", abi.KV_E_INVALID: "INVALID",
+          abi.KV_E_UNMAPPED: "UNMAPPED"}
+
+
+def _status(fn, *args):
+    try:
+        fn(*args)
+        return "OK", 0
+    except abi.KVError as e:
+        return STATUS[e.status], e.deficit
 
 
 def _run_both(rng, S, C, M, n_ops=300):
@@ -133,7 +142,7 @@ def _run_both(rng, S, C, M, n_ops=300):
     h = _host_pool(S, C, M, free_order=order)
     live = {}        # oracle sid -> abi handle
     for _ in range(n_ops):
-        op = int(rng.integers(0, 6))
+        op = int(rng.integers(0, 9))
         rows = [r for r in range(C) if r not in {o.row_of(s) for s in live}]
         if op == 0 and rows:
             sid = o.open(rows[0])
@@ -170,11 +179,33 @@ def _run_both(rng, S, C, M, n_ops=300):
             sid = list(live)[int(rng.integers(len(live)))]
             o.release(sid)
             abi.kv_seq_release(h, live.pop(sid))
+        elif op == 5 and live:
+            sid = list(live)[int(rng.integers(len(live)))]
+            n = int(rng.integers(0, 5))
+            assert _status(abi.kv_seq_reserve, h, live[sid], n) == o.reserve(sid, n)
+        elif op == 6 and live:
+            # a speculative unit: map the draft rows, then commit a prefix (or a bad count)
+            sid = list(live)[int(rng.integers(len(live)))]
+            T = int(rng.integers(1, 90))
+            F = o.frontier_of(sid)
+            if F + T <= S and o.ensure_mapped(sid, F + T)[0] == "OK":
+                abi.kv_seq_ensure_mapped(h, live[sid], F + T)
+            a = int(rng.integers(0, T + 2))
+            cancelled = bool(rng.integers(0, 8) == 0)
+            if cancelled:
+                a = int(rng.integers(0, 2))
+            st = o.commit_accepted(sid, T, a, cancelled)
+            assert _status(abi.kv_seq_commit_accepted, h, live[sid], T, a, cancelled)[0] == st
+        elif op == 7 and live:
+            sid = list(live)[int(rng.integers(len(live)))]
+            prov = int(rng.integers(0, S + 3))
+            assert _status(abi.kv_seq_trim, h, live[sid], prov)[0] == o.trim(sid, prov)
         # bit-exact state after every operation
         assert abi.kv_pool_stats(h) == o.stats()
         assert np.array_equal(np.array(abi.kv_pool_table_host(h, C * o.L)).reshape(C, o.L), o.table)
         for sid, hh in live.items():
             assert abi.kv_seq_info(h, hh) == (o.row_of(sid), o.frontier_of(sid), len(o.pages_of(sid)))
+            assert abi.kv_seq_reservation(h, hh) == len(o.reserved_of(sid))
     for g in range(M):
         assert abi.kv_pool_page_refs(h, g) == o.refs[g]
     abi.kv_pool_destroy(h)
@@ -208,4 +239,41 @@ def test_fork_worked_example_through_abi():
     assert np.array_equal(t2[1, :15], t[0, :15]) and t2[1, 15] != tail
     assert abi.kv_pool_page_refs(h, int(tail)) == 1
     abi.kv_seq_ensure_mapped(h, b, 1001)
+    abi.kv_pool_destroy(h)
+
+
+def test_draft_pool_pages_matches_oracle():
+    for M, C, K in [(4096, 8, 1), (4096, 8, 2), (4096, 8, 65), (4096, 8, 66), (16, 1, 200), (8192, 4, 7)]:
+        assert abi.kv_draft_pool_pages(M, C, K) == G.draft_pool_pages(M, C, K)
+    with pytest.raises(abi.KVError) as e:
+        abi.kv_draft_pool_pages(16, 1, 0)
+    assert e.value.status == abi.KV_E_INVALID
+
+
+def test_speculative_round_through_abi_reuses_the_reservation():
+    M = 32
+    order = np.random.default_rng(3).permutation(M)
+    h = _host_pool(2048, 2, M, free_order=order)
+    o = OraclePool(2048, 2, M, free_order=order)
+    a, sa = abi.kv_seq_open(h, 1), o.open(1)
+    for n in (700, 700 + 200):
+        abi.kv_seq_ensure_mapped(h, a, n)
+        o.ensure_mapped(sa, n)
+        if n == 700:
+            abi.kv_seq_commit(h, a, n)
+            o.commit(sa, n)
+    abi.kv_seq_commit_accepted(h, a, 200, 17)
+    o.commit_accepted(sa, 200, 17)
+    assert abi.kv_seq_info(h, a) == (1, 717, 12) and abi.kv_seq_reservation(h, a) == 3
+    assert abi.kv_pool_stats(h) == o.stats() == (12, 3, M - 15)
+    # a second sequence cannot take the reserved groups
+    b, sb = abi.kv_seq_open(h, 0), o.open(0)
+    with pytest.raises(abi.KVError) as e:
+        abi.kv_seq_ensure_mapped(h, b, 64 * (M - 14))
+    assert e.value.status == abi.KV_E_CAPACITY and e.value.deficit == 1
+    abi.kv_seq_release(h, a)
+    o.release(sa)
+    abi.kv_seq_ensure_mapped(h, b, 64 * (M - 14))
+    o.ensure_mapped(sb, 64 * (M - 14))
+    assert np.array_equal(np.array(abi.kv_pool_table_host(h, 2 * o.L)).reshape(2, o.L), o.table)
     abi.kv_pool_destroy(h)
