@@ -394,6 +394,8 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", type=int, default=2, help="workload number (1-4: decode, 5: verify/prefill)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--graph", action="store_true",
+                    help="decode configs: time replays of the step captured as one HIP graph")
     ap.add_argument("--spec", action="store_true",
                     help="with --config 5: speculative rounds (draft, verify, commit the accepted prefix, trim)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -462,6 +464,26 @@ def main() -> int:
         step()
     torch.cuda.synchronize()
 
+    graph = None
+    if args.graph:
+        # the same step as one HIP graph: plan, then per layer the append and the run
+        outs = [out] * wl.layers
+        ks = [step_inputs[layer][0] for layer in range(wl.layers)]
+        vs = [step_inputs[layer][1] for layer in range(wl.layers)]
+        graph = dp.step_graph(wl.B, wl.Hq, rows_t, lens_t, max_ctx, qs, wl.sm_scale, outs, ws, ks=ks, vs=vs,
+                              pos0=pos0_t, cu=cu_t, total_tokens=total)
+        eager_step = step
+
+        def step(events=None):
+            if events is not None:
+                eager_step(events)
+            else:
+                dp.graph_launch(graph)
+
+        for _ in range(args.warmup):
+            step()
+        torch.cuda.synchronize()
+
     # timed region: K whole steps, no probes inside
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -504,6 +526,7 @@ def main() -> int:
                    "page_size": 64, "pool_pages": wl.M},
         "steps_per_s": round(1000.0 / ms_per_step, 2),
         "hbm_frac": round(value / HBM_PEAK_GBS, 4),
+        "step_form": "hip_graph" if graph is not None else "eager",
         "kv_bytes_per_step": {"unique": wl.layers * unique, "logical": wl.layers * logical},
         "roofline": {"kernel": decode_kernel_name(wl), "bound": "hbm",
                      "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -512,6 +535,8 @@ def main() -> int:
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
+    if graph is not None:
+        dp.graph_destroy(graph)
     dp.close()
     return 0
 

@@ -348,6 +348,42 @@ kv_status paged_attn_verify(const kv_pool* pool, uint32_t layer, uint32_t B, uin
                             uint32_t total_q, uint32_t max_q_len, uint32_t max_seq_len, const void* d_q,
                             float sm_scale, float* d_out, void* d_ws, size_t ws_bytes, hipStream_t stream);
 
+/* One decode step of layers 0 .. n_layers-1 as a HIP graph (Paged KV Context
+ * Store page, graph-stable bases: plane and table bases stay fixed while page
+ * ids, table rows, lengths and positions are data; one graph per exact B).
+ * The graph holds exactly the work of an eager step: paged_attn_decode_plan,
+ * then per layer l the append of the step's rows and the decode run --
+ * paged_attn_decode_append_run(d_k[l], d_v[l]) where the BF16 page stream
+ * takes it (one row per entry: total_tokens == B), else
+ * kv_append(d_pos0, d_cu_tokens, total_tokens) then paged_attn_decode_run.
+ * d_k == d_v == NULL: runs only, nothing appended.
+ *   d_q[l], d_out[l], d_k[l], d_v[l] : host arrays of n_layers device
+ *       pointers, as for the eager calls; d_pos0 / d_cu_tokens [B] / [B+1]
+ *       device arrays (only for the kv_append form).
+ * Every pointer, B, Hq, max_seq_len, sm_scale and the workspace are fixed at
+ * capture; the contents they point to are read at each replay, so a caller
+ * updates lengths, rows, queries and step rows in place and maps new pages
+ * (kv_seq_ensure_mapped, publication on its stream) before launching.
+ * Capture runs on a private stream; nothing is enqueued on any caller stream.
+ * Errors of the captured calls are returned as they would be eagerly;
+ * KV_E_DEVICE if capture or instantiation fails. */
+typedef struct kv_step_graph kv_step_graph;
+kv_status kv_decode_step_graph_create(const kv_pool* pool, uint32_t B, uint32_t Hq, uint32_t max_seq_len,
+                                      const int32_t* d_table_rows, const int32_t* d_seq_lens, uint32_t n_layers,
+                                      const void* const* d_k, const void* const* d_v, const int32_t* d_pos0,
+                                      const int32_t* d_cu_tokens, uint32_t total_tokens, const void* const* d_q,
+                                      float sm_scale, float* const* d_out, void* d_ws, size_t ws_bytes,
+                                      kv_step_graph** out);
+
+/* Replay the step on `stream` (ordered after earlier work on it, like an
+ * eager step).  Replays on one graph share its workspace: they must not
+ * overlap in time. */
+kv_status kv_step_graph_launch(kv_step_graph* graph, hipStream_t stream);
+
+/* Free the graph (no device synchronization; the caller makes sure no replay
+ * is still running).  NULL is ignored. */
+void kv_step_graph_destroy(kv_step_graph* graph);
+
 /* 1 if decode (max_q_len == 0) or verify has a kernel for this pool and Hq. */
 int paged_attn_supported(const kv_pool* pool, uint32_t Hq, uint32_t max_q_len);
 

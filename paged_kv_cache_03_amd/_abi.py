@@ -30,7 +30,8 @@ EXPORTS = ["kv_profile_planes", "kv_plane_bytes", "kv_pool_create", "kv_pool_des
            "kv_seq_reservation", "kv_draft_pool_pages", "kv_seq_info", "kv_cow_tail_page", "kv_append",
            "paged_attn_workspace_bytes", "paged_attn_decode", "paged_attn_decode_plan", "paged_attn_decode_run",
            "paged_attn_decode_append_run",
-           "paged_attn_verify", "paged_attn_supported",
+           "paged_attn_verify", "kv_decode_step_graph_create", "kv_step_graph_launch", "kv_step_graph_destroy",
+           "paged_attn_supported",
            "kv_last_error_message"]
 
 
@@ -94,6 +95,10 @@ def _load():
         "paged_attn_decode_append_run": (i32, [vp, u32, u32, u32, u32, vp, vp, vp, ctypes.c_float, vp, vp, sz, vp]),
         "paged_attn_verify": (i32, [vp, u32, u32, u32, vp, vp, vp, u32, u32, u32, vp, ctypes.c_float, vp, vp, sz,
                                     vp]),
+        "kv_decode_step_graph_create": (i32, [vp, u32, u32, u32, vp, vp, u32, vp, vp, vp, vp, u32, vp,
+                                              ctypes.c_float, vp, vp, sz, P(vp)]),
+        "kv_step_graph_launch": (i32, [vp, vp]),
+        "kv_step_graph_destroy": (None, [vp]),
         "paged_attn_supported": (ctypes.c_int, [vp, u32, u32]),
         "kv_last_error_message": (ctypes.c_char_p, []),
     }
@@ -271,3 +276,32 @@ def paged_attn_verify(pool: int, layer: int, B: int, Hq: int, d_table_rows: int,
                       d_ws: int, ws_bytes: int, stream: int = 0) -> None:
     _check(_lib.paged_attn_verify(pool, layer, B, Hq, d_table_rows, d_q_pos0, d_cu_q, total_q, max_q_len,
                                   max_seq_len, d_q, sm_scale, d_out, d_ws or None, ws_bytes, stream or None))
+
+
+def _ptr_array(ptrs):
+    return (ctypes.c_void_p * len(ptrs))(*[int(p) for p in ptrs])
+
+
+def kv_decode_step_graph_create(pool: int, B: int, Hq: int, max_seq_len: int, d_table_rows: int, d_seq_lens: int,
+                                d_q: list, sm_scale: float, d_out: list, d_ws: int, ws_bytes: int,
+                                d_k: list | None = None, d_v: list | None = None, d_pos0: int = 0,
+                                d_cu_tokens: int = 0, total_tokens: int | None = None) -> int:
+    n = len(d_q)
+    assert len(d_out) == n and (d_k is None) == (d_v is None) and (d_k is None or len(d_k) == len(d_v) == n)
+    qa, oa = _ptr_array(d_q), _ptr_array(d_out)
+    ka = _ptr_array(d_k) if d_k is not None else None
+    va = _ptr_array(d_v) if d_v is not None else None
+    out = ctypes.c_void_p()
+    _check(_lib.kv_decode_step_graph_create(pool, B, Hq, max_seq_len, d_table_rows, d_seq_lens, n, ka, va,
+                                            d_pos0 or None, d_cu_tokens or None,
+                                            B if total_tokens is None else total_tokens, qa, sm_scale, oa, d_ws,
+                                            ws_bytes, ctypes.byref(out)))
+    return out.value
+
+
+def kv_step_graph_launch(graph: int, stream: int = 0) -> None:
+    _check(_lib.kv_step_graph_launch(graph, stream or None))
+
+
+def kv_step_graph_destroy(graph: int) -> None:
+    _lib.kv_step_graph_destroy(graph)

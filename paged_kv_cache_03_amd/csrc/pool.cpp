@@ -690,3 +690,101 @@ kv_status paged_attn_verify(const kv_pool* pool, uint32_t layer, uint32_t B, uin
 }
 
 }  // extern "C"
+
+// ------------------------------------------------------------ step graph --
+// One decode step of many layers as a HIP graph (Paged KV Context Store page:
+// plane and table bases stay stable across graph replays; page ids, table
+// rows, lengths and positions are data the kernels read on the device, not
+// part of what is captured; one graph per exact batch size).  The step is the
+// plan of the batch state and, per layer, the append of the step's rows with
+// the decode run -- the entry points of an eager step, recorded once on a
+// private stream.  Mapping publication stays outside: it carries host values
+// in its arguments and is host-side allocator work done before a step.
+struct kv_step_graph {
+    hipGraphExec_t exec = nullptr;
+};
+
+extern "C" {
+
+kv_status kv_decode_step_graph_create(const kv_pool* pool, uint32_t B, uint32_t Hq, uint32_t max_seq_len,
+                                      const int32_t* d_table_rows, const int32_t* d_seq_lens, uint32_t n_layers,
+                                      const void* const* d_k, const void* const* d_v, const int32_t* d_pos0,
+                                      const int32_t* d_cu_tokens, uint32_t total_tokens, const void* const* d_q,
+                                      float sm_scale, float* const* d_out, void* d_ws, size_t ws_bytes,
+                                      kv_step_graph** out) {
+    if (!out) return fail(KV_E_INVALID, "null argument");
+    *out = nullptr;
+    kv_status st = check_compute(pool, 0, B);
+    if (st != KV_OK) return st;
+    if (!d_q || !d_out || n_layers == 0 || n_layers > pool->geo.num_layers || B == 0)
+        return fail(KV_E_INVALID, "layers, batch or pointer arrays");
+    const bool append = d_k != nullptr;
+    if (append != (d_v != nullptr)) return fail(KV_E_INVALID, "d_k and d_v go together");
+    // the append inside the run where the page stream takes it, else kv_append + run
+    const bool fused = append && total_tokens == B && decode_append_supported(pool->view(0), int(B), int(Hq));
+    if (append && !fused && (!d_pos0 || !d_cu_tokens))
+        return fail(KV_E_INVALID, "kv_append in the step needs d_pos0 and d_cu_tokens");
+
+    hipStream_t s = nullptr;
+    if (hipStreamCreateWithFlags(&s, hipStreamNonBlocking) != hipSuccess)
+        return fail(KV_E_DEVICE, "capture stream");
+    if (hipStreamBeginCapture(s, hipStreamCaptureModeThreadLocal) != hipSuccess) {
+        (void)hipStreamDestroy(s);
+        return fail(KV_E_DEVICE, "begin capture");
+    }
+    st = paged_attn_decode_plan(pool, B, Hq, d_table_rows, d_seq_lens, max_seq_len, d_ws, ws_bytes, s);
+    std::string why = st == KV_OK ? "" : g_last_error;
+    for (uint32_t l = 0; l < n_layers && st == KV_OK; ++l) {
+        if (!d_q[l] || !d_out[l] || (append && (!d_k[l] || !d_v[l]))) {
+            st = KV_E_INVALID;
+            why = "null device pointer of a layer";
+            break;
+        }
+        if (fused) {
+            st = paged_attn_decode_append_run(pool, l, B, Hq, max_seq_len, d_k[l], d_v[l], d_q[l], sm_scale,
+                                              d_out[l], d_ws, ws_bytes, s);
+        } else {
+            if (append)
+                st = kv_append(pool, l, B, d_table_rows, d_pos0, d_cu_tokens, total_tokens, d_k[l], d_v[l], s);
+            if (st == KV_OK)
+                st = paged_attn_decode_run(pool, l, B, Hq, max_seq_len, d_q[l], sm_scale, d_out[l], d_ws, ws_bytes,
+                                           s);
+        }
+        if (st != KV_OK) why = g_last_error;
+    }
+    hipGraph_t graph = nullptr;
+    const hipError_t ec = hipStreamEndCapture(s, &graph);
+    (void)hipStreamDestroy(s);
+    if (st != KV_OK || ec != hipSuccess || !graph) {
+        if (graph) (void)hipGraphDestroy(graph);
+        if (st != KV_OK) return fail(st, "step graph: " + why);
+        return fail(KV_E_DEVICE, std::string("end capture: ") + hipGetErrorString(ec));
+    }
+    hipGraphExec_t exec = nullptr;
+    const hipError_t ei = hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0);
+    (void)hipGraphDestroy(graph);
+    if (ei != hipSuccess) return fail(KV_E_DEVICE, std::string("instantiate: ") + hipGetErrorString(ei));
+    kv_step_graph* g = new (std::nothrow) kv_step_graph();
+    if (!g) {
+        (void)hipGraphExecDestroy(exec);
+        return fail(KV_E_INVALID, "out of host memory");
+    }
+    g->exec = exec;
+    *out = g;
+    return ok();
+}
+
+kv_status kv_step_graph_launch(kv_step_graph* g, hipStream_t stream) {
+    if (!g || !g->exec) return fail(KV_E_INVALID, "null graph");
+    const hipError_t e = hipGraphLaunch(g->exec, stream);
+    if (e != hipSuccess) return fail(KV_E_DEVICE, std::string("graph launch: ") + hipGetErrorString(e));
+    return ok();
+}
+
+void kv_step_graph_destroy(kv_step_graph* g) {
+    if (!g) return;
+    if (g->exec) (void)hipGraphExecDestroy(g->exec);
+    delete g;
+}
+
+}  // extern "C"

@@ -135,6 +135,25 @@ class DevicePool:
         abi.paged_attn_decode_plan(self.handle, table_rows.numel(), Hq, ptr(table_rows), ptr(seq_lens), max_seq_len,
                                    ptr(ws), ws.numel(), self.stream)
 
+    def step_graph(self, B: int, Hq: int, table_rows: torch.Tensor, seq_lens: torch.Tensor, max_seq_len: int,
+                   qs: list, sm_scale: float, outs: list, ws: torch.Tensor, ks: list | None = None,
+                   vs: list | None = None, pos0: torch.Tensor | None = None, cu: torch.Tensor | None = None,
+                   total_tokens: int | None = None) -> int:
+        """One decode step of len(qs) layers captured as a HIP graph (handle); the
+        tensors must stay alive and in place for the graph's lifetime."""
+        return abi.kv_decode_step_graph_create(
+            self.handle, B, Hq, max_seq_len, ptr(table_rows), ptr(seq_lens), [ptr(q) for q in qs], sm_scale,
+            [ptr(o) for o in outs], ptr(ws), ws.numel(), None if ks is None else [ptr(k) for k in ks],
+            None if vs is None else [ptr(v) for v in vs], ptr(pos0) if pos0 is not None else 0,
+            ptr(cu) if cu is not None else 0, total_tokens)
+
+    def graph_launch(self, graph: int) -> None:
+        abi.kv_step_graph_launch(graph, self.stream)
+
+    @staticmethod
+    def graph_destroy(graph: int) -> None:
+        abi.kv_step_graph_destroy(graph)
+
     def decode_run(self, layer: int, B: int, Hq: int, max_seq_len: int, q: torch.Tensor, sm_scale: float,
                    out: torch.Tensor, ws: torch.Tensor) -> None:
         abi.paged_attn_decode_run(self.handle, layer, B, Hq, max_seq_len, ptr(q), sm_scale, ptr(out), ptr(ws),
