@@ -5,7 +5,9 @@ Source: NInfer "Paged KV Context Store" maintainer page -- page-group diagram
 [X, P, H, N] (C-order [M][H][P][X] here), P=64 translation (block =
 position >> 6, offset = position & 63, page = block_table[block]), and the
 tail-COW rule (copy the committed columns of the shared tail into a private
-page group for every plane).
+page group for every plane), and the host replica's logical-order packed
+layout (no device page ids or table holes; each page carries the payload of
+every grouped plane of the pool; full pages are copied).
 
 Planes are plain NumPy arrays indexed [g, h, o, x]; ``geometry.element_index``
 is the equivalent flat-address form, pinned against this indexing in tests.
@@ -88,3 +90,51 @@ class OracleStore:
             scale = lp[f"{side}_SCALE"][pages, h, offs, :] if f"{side}_SCALE" in lp else None
             out.append(codecs.dequantize(self.kinds[i], code, scale))
         return out[0], out[1]
+
+
+    # ------------------------------------------------------- host replica --
+    def replica_order(self) -> list:
+        """(layer, PlaneSpec) in the order a replica page stores them: layers
+        ascending, then K code, K scale, V code, V scale."""
+        return [(layer, spec) for layer in range(self.layers) for spec in self.schema]
+
+    def replica_page_bytes(self) -> int:
+        return sum(self.H * P * spec.x_extent * spec.elem_bytes for _, spec in self.replica_order())
+
+    def replica(self, sid: int) -> tuple[np.ndarray, int]:
+        """Logical-order packed copy of an address space's committed pages:
+        page i of the replica is logical block i, holding every plane's
+        [H][64][X] slice of its page group (all 64 rows), planes in
+        replica_order.  Returns (bytes, committed frontier)."""
+        n = self.pool.frontier_of(sid)
+        pages = self.pool.pages_of(sid)[: -(-n // P)]
+        out = []
+        for g in pages:
+            for layer, spec in self.replica_order():
+                out.append(np.ascontiguousarray(self.planes[layer][spec.role][g]).view(np.uint8).ravel())
+        data = np.concatenate(out) if out else np.zeros(0, np.uint8)
+        return data, n
+
+    def restore(self, row: int, data: np.ndarray, frontier: int) -> int:
+        """A new address space on `row` holding the replica's pages: map
+        ceil(frontier / 64) page groups, write each page's payload into them,
+        commit the frontier."""
+        pool = self.pool
+        n_pages = -(-frontier // P)
+        pb = self.replica_page_bytes()
+        if data.size < n_pages * pb:
+            raise ValueError("replica shorter than its pages")
+        sid = pool.open(row)
+        st, _ = pool.ensure_mapped(sid, frontier)
+        if st != "OK":
+            pool.release(sid)
+            raise ValueError(f"restore: {st}")
+        for i, g in enumerate(pool.pages_of(sid)):
+            off = i * pb
+            for layer, spec in self.replica_order():
+                arr = self.planes[layer][spec.role]
+                nb = self.H * P * spec.x_extent * spec.elem_bytes
+                arr[g] = data[off:off + nb].view(arr.dtype).reshape(arr.shape[1:])
+                off += nb
+        pool.commit(sid, frontier)
+        return sid
