@@ -33,6 +33,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+PCIE5_X16_GBS = 63.0
 METRIC = "paged decode KV GB/s (% of HBM peak) + decode steps/s at C=8, 32K ctx"
 PROFILES = os.path.join(ROOT, "profiles")
 # sources of the decode kernel; the traffic summary is valid for this exact text
@@ -387,6 +388,84 @@ def bench_spec(wl, args) -> int:
     return 0
 
 
+def bench_replica(wl, args) -> int:
+    """Host replica of the longest entry of a decode workload, every layer:
+    kv_seq_offload into pinned host memory (device to host), release, then
+    kv_seq_restore into the same row (host to device).  Reports the bytes of
+    full page payloads moved per second each way; a decode of the restored
+    row is checked against the original bit for bit."""
+    import numpy as np
+    import torch
+    from paged_kv_cache_03_amd.device_pool import i32
+    from workloads.device_driver import _dev, build_device
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    t0 = time.time()
+    log(f"workload {wl.name}: filling {wl.layers} layer(s) of history")
+    dp, seqs, _ = build_device(wl, zero=False)
+    log(f"history resident after {time.time() - t0:.1f} s")
+    # the longest entry that shares no pages (no fork source or fork)
+    private = [x for x in range(wl.B)
+               if wl.fork[x] is None and not any(fk is not None and fk[0] == x for fk in wl.fork)]
+    b = max(private, key=lambda x: wl.hist[x])
+    row, f = wl.table_rows[b], wl.hist[b]
+    n = -(-f // 64)
+    pb = dp.replica_page_bytes()
+    host = torch.empty(n * pb, dtype=torch.uint8, pin_memory=True)
+    q = _dev(wl.q(0)[b:b + 1], dev)
+    ws = dp.workspace(1, wl.Hq, f)
+
+    def decode(r_):
+        out = torch.empty((1, wl.Hq, wl.D), dtype=torch.float32, device=dev)
+        dp.decode(0, wl.Hq, i32([r_], dev), i32([f], dev), f, q, wl.sm_scale, out, ws)
+        return out
+
+    ref = decode(row)
+    reps = max(1, min(args.steps, 5))
+    d2h, h2d = [], []
+    seq = seqs[b]
+    for _ in range(reps + 1):
+        e0, e1, e2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+        torch.cuda.synchronize()
+        e0.record()
+        dp.offload(seq, host)
+        e1.record()
+        torch.cuda.synchronize()
+        dp.release(seq)
+        e1b = torch.cuda.Event(enable_timing=True)
+        e1b.record()
+        seq = dp.restore(row, host, f)
+        e2.record()
+        torch.cuda.synchronize()
+        d2h.append(e0.elapsed_time(e1))
+        h2d.append(e1b.elapsed_time(e2))
+    d2h, h2d = d2h[1:], h2d[1:]                   # the first round trip is warm-up
+    same = bool(torch.equal(decode(row), ref))
+    total = n * pb
+    line = {
+        "metric": "host replica GB/s (offload D2H / restore H2D of full page payloads, every layer)",
+        "value": round(total / (np.mean(d2h) * 1e-3) / 1e9, 2), "unit": "GB/s", "n_gpus": 1, "steps": reps,
+        "warmup": 1, "ms_per_step": round(float(np.mean(d2h) + np.mean(h2d)), 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bytes", "data": "synthetic",
+        "config": {"workload": wl.name + "_replica", "profile": wl.profile, "layers": wl.layers,
+                   "kv_heads": wl.H, "head_dim": wl.D, "entry_tokens": f, "pages": n, "page_bytes": pb},
+        "offload_gbs": round(total / (np.mean(d2h) * 1e-3) / 1e9, 2),
+        "restore_gbs": round(total / (np.mean(h2d) * 1e-3) / 1e9, 2),
+        "offload_ms": round(float(np.mean(d2h)), 4), "restore_ms": round(float(np.mean(h2d)), 4),
+        "restored_decode_bitwise_equal": same,
+        # the host link: PCIe 5.0 x16, 32 GT/s x 16 lanes with 128b/130b coding = 63.0 GB/s each way
+        "roofline": {"kernel": "replica_copy_kernel", "bound": "pcie",
+                     "achieved": round(total / (np.mean(d2h) * 1e-3) / 1e9, 2), "peak": PCIE5_X16_GBS,
+                     "unit": "GB/s", "frac": round(total / (np.mean(d2h) * 1e-3) / 1e9 / PCIE5_X16_GBS, 4),
+                     "traffic": None, "bytes_per_launch": total, "launch_ms": round(float(np.mean(d2h)), 4)},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(line), flush=True)
+    dp.close()
+    return 0 if same else 1
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -396,6 +475,8 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--graph", action="store_true",
                     help="decode configs: time replays of the step captured as one HIP graph")
+    ap.add_argument("--replica", action="store_true",
+                    help="decode configs: offload / restore of the longest entry's pages (host replica)")
     ap.add_argument("--spec", action="store_true",
                     help="with --config 5: speculative rounds (draft, verify, commit the accepted prefix, trim)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -424,6 +505,8 @@ def main() -> int:
         return bench_spec(wl, args)
     if wl.mode != "decode":
         return bench_verify(wl, args)
+    if args.replica:
+        return bench_replica(wl, args)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     t0 = time.time()

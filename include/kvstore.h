@@ -226,6 +226,36 @@ kv_status kv_seq_reservation(const kv_pool* pool, kv_seq seq, uint32_t* pages);
 kv_status kv_draft_pool_pages(uint32_t main_pages, uint32_t max_concurrency, uint32_t draft_window,
                               uint32_t* pages);
 
+/* Host replica (Paged KV Context Store page, host replica passage): the
+ * logical-order packed HostKVPageLayout.  Page i of a replica is logical
+ * block i of the address space; it holds, for every layer in ascending order
+ * and every plane of the layer in the order K code, K scale, V code, V scale,
+ * that plane's [H][64][X] slice of the page group (all 64 rows: the full
+ * page payload).  No device page id or table hole is stored; a replica of n
+ * pages takes n * page_bytes bytes. */
+kv_status kv_replica_page_bytes(const kv_pool* pool, uint64_t* bytes);
+
+/* Copy the committed pages [0, ceil(frontier / 64)) of `seq` into `host` in
+ * the replica layout (device to host, a kernel on `stream`).  host: pinned
+ * host memory (hipHostMalloc or a pinned tensor), 16-byte aligned,
+ * host_bytes >= pages * page_bytes.  *pages and *frontier receive the page
+ * count and the committed frontier the replica covers.  The copy completes
+ * in `stream` order: the caller keeps the address space unchanged (no
+ * append, trim, COW or release) and reads `host` only after it.
+ * KV_E_INVALID for memory that is not pinned or too small. */
+kv_status kv_seq_offload(kv_pool* pool, kv_seq seq, void* host, size_t host_bytes, uint32_t* pages,
+                         uint32_t* frontier, hipStream_t stream);
+
+/* A new address space on `table_row` from a replica: maps ceil(frontier /
+ * 64) page groups, copies each replica page into its group (host to device,
+ * a kernel on `stream`), then publishes the row on `stream` -- the row names
+ * the pages only after their payload has landed (replica publication order)
+ * -- and commits `frontier`.  `host` stays unchanged until the copy has
+ * completed.  KV_E_CAPACITY with *deficit when too few groups are free
+ * (nothing changes); KV_E_INVALID for a leased row or unpinned memory. */
+kv_status kv_seq_restore(kv_pool* pool, uint32_t table_row, const void* host, size_t host_bytes, uint32_t frontier,
+                         uint32_t* deficit, hipStream_t stream, kv_seq* out);
+
 /* Row, committed frontier and mapped page count of a live address space. */
 kv_status kv_seq_info(const kv_pool* pool, kv_seq seq, uint32_t* table_row, uint32_t* frontier,
                       uint32_t* mapped_pages);

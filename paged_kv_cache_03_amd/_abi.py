@@ -27,7 +27,8 @@ KV_ROLE_K_CODE, KV_ROLE_K_SCALE, KV_ROLE_V_CODE, KV_ROLE_V_SCALE = range(4)
 EXPORTS = ["kv_profile_planes", "kv_plane_bytes", "kv_pool_create", "kv_pool_destroy", "kv_pool_stats",
            "kv_pool_table_host", "kv_pool_page_refs", "kv_seq_open", "kv_seq_fork", "kv_seq_ensure_mapped",
            "kv_seq_commit", "kv_seq_release", "kv_seq_reserve", "kv_seq_trim", "kv_seq_commit_accepted",
-           "kv_seq_reservation", "kv_draft_pool_pages", "kv_seq_info", "kv_cow_tail_page", "kv_append",
+           "kv_seq_reservation", "kv_draft_pool_pages", "kv_replica_page_bytes", "kv_seq_offload",
+           "kv_seq_restore", "kv_seq_info", "kv_cow_tail_page", "kv_append",
            "paged_attn_workspace_bytes", "paged_attn_decode", "paged_attn_decode_plan", "paged_attn_decode_run",
            "paged_attn_decode_append_run",
            "paged_attn_verify", "kv_decode_step_graph_create", "kv_step_graph_launch", "kv_step_graph_destroy",
@@ -85,6 +86,9 @@ def _load():
         "kv_seq_commit_accepted": (i32, [vp, ctypes.c_uint64, u32, u32, ctypes.c_int, vp]),
         "kv_seq_reservation": (i32, [vp, ctypes.c_uint64, P(u32)]),
         "kv_draft_pool_pages": (i32, [u32, u32, u32, P(u32)]),
+        "kv_replica_page_bytes": (i32, [vp, P(ctypes.c_uint64)]),
+        "kv_seq_offload": (i32, [vp, ctypes.c_uint64, vp, sz, P(u32), P(u32), vp]),
+        "kv_seq_restore": (i32, [vp, u32, vp, sz, u32, P(u32), vp, P(ctypes.c_uint64)]),
         "kv_seq_info": (i32, [vp, ctypes.c_uint64, P(u32), P(u32), P(u32)]),
         "kv_cow_tail_page": (i32, [vp, ctypes.c_uint64, vp]),
         "kv_append": (i32, [vp, u32, u32, vp, vp, vp, u32, vp, vp, vp]),
@@ -217,6 +221,26 @@ def kv_seq_reservation(pool: int, seq: int) -> int:
 def kv_draft_pool_pages(main_pages: int, max_concurrency: int, draft_window: int) -> int:
     out = ctypes.c_uint32()
     _check(_lib.kv_draft_pool_pages(main_pages, max_concurrency, draft_window, ctypes.byref(out)))
+    return out.value
+
+
+def kv_replica_page_bytes(pool: int) -> int:
+    out = ctypes.c_uint64()
+    _check(_lib.kv_replica_page_bytes(pool, ctypes.byref(out)))
+    return out.value
+
+
+def kv_seq_offload(pool: int, seq: int, host: int, host_bytes: int, stream: int = 0) -> tuple:
+    n, f = ctypes.c_uint32(), ctypes.c_uint32()
+    _check(_lib.kv_seq_offload(pool, seq, host, host_bytes, ctypes.byref(n), ctypes.byref(f), stream or None))
+    return n.value, f.value
+
+
+def kv_seq_restore(pool: int, table_row: int, host: int, host_bytes: int, frontier: int, stream: int = 0) -> int:
+    deficit, out = ctypes.c_uint32(), ctypes.c_uint64()
+    st = _lib.kv_seq_restore(pool, table_row, host, host_bytes, frontier, ctypes.byref(deficit), stream or None,
+                             ctypes.byref(out))
+    _check(st, deficit.value)
     return out.value
 
 

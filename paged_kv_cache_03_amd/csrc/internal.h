@@ -51,6 +51,18 @@ struct CopyPlane {
 hipError_t launch_cow_copy(const CopyPlane* planes, int n_planes, int H, int src_g, int dst_g, int cols,
                            hipStream_t s);
 
+// Host replica copy (logical-order packed layout): page i of the replica is
+// pages[i], each plane's [H][64][X] slice at host + i * page_bytes +
+// plane.host_off.  to_host: device pages -> host; else host -> device pages.
+// `host` is the device-visible address of pinned host memory.
+struct ReplicaPlane {
+    void* base;          // device plane [M][H][64][X]
+    uint32_t slice_bytes;  // H * 64 * X * elem_bytes, a multiple of 16
+    uint64_t host_off;   // offset of this plane's slice inside a replica page
+};
+hipError_t launch_replica_copy(const ReplicaPlane* planes, int n_planes, const int32_t* pages, int n_pages,
+                               uint64_t page_bytes, char* host, bool to_host, hipStream_t s);
+
 hipError_t launch_append(const PoolView& pv, int B, const int32_t* table_rows, const int32_t* pos0,
                          const int32_t* cu_tokens, int total_tokens, const void* k, const void* v,
                          hipStream_t s);

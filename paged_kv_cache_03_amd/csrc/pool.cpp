@@ -506,6 +506,105 @@ kv_status kv_draft_pool_pages(uint32_t main_pages, uint32_t max_concurrency, uin
     return ok();
 }
 
+// ----------------------------------------------------------- host replica --
+// Planes of a replica page in their order (layers ascending, then K code,
+// K scale, V code, V scale) with each slice's offset inside the page.
+static uint64_t replica_planes(const kv_pool* pool, std::vector<ReplicaPlane>* out) {
+    out->clear();
+    uint64_t off = 0;
+    const uint32_t H = pool->geo.num_kv_heads;
+    for (uint32_t l = 0; l < pool->geo.num_layers; ++l) {
+        for (uint32_t role = 0; role < 4; ++role) {
+            for (const KVPlaneDesc& p : pool->planes) {
+                if (p.layer != l || p.role != role) continue;
+                const uint32_t slice = H * kPage * p.x_extent * p.elem_bytes;
+                out->push_back(ReplicaPlane{p.base, slice, off});
+                off += slice;
+            }
+        }
+    }
+    return off;
+}
+
+// The device-visible address of pinned host memory, or null.
+static char* host_device_ptr(const void* host) {
+    void* d = nullptr;
+    if (!host || (reinterpret_cast<uintptr_t>(host) & 15)) return nullptr;
+    if (hipHostGetDevicePointer(&d, const_cast<void*>(host), 0) != hipSuccess) {
+        (void)hipGetLastError();
+        return nullptr;
+    }
+    return static_cast<char*>(d);
+}
+
+kv_status kv_replica_page_bytes(const kv_pool* pool, uint64_t* bytes) {
+    if (!pool || !bytes) return fail(KV_E_INVALID, "null argument");
+    std::vector<ReplicaPlane> planes;
+    *bytes = replica_planes(pool, &planes);
+    return ok();
+}
+
+kv_status kv_seq_offload(kv_pool* pool, kv_seq seq, void* host, size_t host_bytes, uint32_t* pages,
+                         uint32_t* frontier, hipStream_t stream) {
+    if (!pool) return fail(KV_E_INVALID, "null pool");
+    if (!pool->device()) return fail(KV_E_INVALID, "host-only pool has no device planes");
+    Space* s = pool->lookup(seq);
+    if (!s) return fail(KV_E_STALE, "stale or unknown handle");
+    std::vector<ReplicaPlane> planes;
+    const uint64_t pb = replica_planes(pool, &planes);
+    const uint32_t n = ceil_div(s->frontier, kPage);
+    if (uint64_t(host_bytes) < pb * n) return fail(KV_E_INVALID, "host buffer smaller than the replica");
+    char* dhost = n ? host_device_ptr(host) : nullptr;
+    if (n && !dhost) return fail(KV_E_INVALID, "host buffer must be 16-byte aligned pinned memory (hipHostMalloc)");
+    if (pages) *pages = n;
+    if (frontier) *frontier = s->frontier;
+    if (n == 0) return ok();
+    const hipError_t e = launch_replica_copy(planes.data(), int(planes.size()), s->pages.data(), int(n), pb, dhost,
+                                             true, stream);
+    if (e != hipSuccess) return fail(KV_E_DEVICE, std::string("replica copy: ") + hipGetErrorString(e));
+    return ok();
+}
+
+kv_status kv_seq_restore(kv_pool* pool, uint32_t table_row, const void* host, size_t host_bytes, uint32_t frontier,
+                         uint32_t* deficit, hipStream_t stream, kv_seq* out) {
+    if (deficit) *deficit = 0;
+    if (!pool || !out) return fail(KV_E_INVALID, "null argument");
+    if (!pool->device()) return fail(KV_E_INVALID, "host-only pool has no device planes");
+    if (table_row >= pool->geo.max_concurrency || pool->row_owner[table_row] >= 0)
+        return fail(KV_E_INVALID, "table row out of range or leased");
+    if (frontier > pool->geo.max_context) return fail(KV_E_INVALID, "frontier beyond max_context");
+    std::vector<ReplicaPlane> planes;
+    const uint64_t pb = replica_planes(pool, &planes);
+    const uint32_t n = ceil_div(frontier, kPage);
+    if (uint64_t(host_bytes) < pb * n) return fail(KV_E_INVALID, "host buffer smaller than the replica");
+    char* dhost = n ? host_device_ptr(host) : nullptr;
+    if (n && !dhost) return fail(KV_E_INVALID, "host buffer must be 16-byte aligned pinned memory (hipHostMalloc)");
+    if (n > pool->free_q.size()) {
+        if (deficit) *deficit = n - uint32_t(pool->free_q.size());
+        return fail(KV_E_CAPACITY, "not enough free page groups for the replica");
+    }
+    Space* s;
+    kv_status st = pool->new_space(table_row, out, &s);
+    if (st != KV_OK) return st;
+    for (uint32_t i = 0; i < n; ++i) {
+        const int32_t g = pool->alloc(s);
+        s->pages.push_back(g);
+        pool->h_table[size_t(table_row) * pool->L + i] = g;
+    }
+    s->frontier = frontier;
+    // the payload lands before the row names the pages: copy, then publish
+    if (n) {
+        const hipError_t e = launch_replica_copy(planes.data(), int(planes.size()), s->pages.data(), int(n), pb,
+                                                 dhost, false, stream);
+        if (e != hipSuccess) {
+            (void)kv_seq_release(pool, *out, stream);
+            *out = 0;
+            return fail(KV_E_DEVICE, std::string("replica copy: ") + hipGetErrorString(e));
+        }
+    }
+    return pool->publish(table_row, 0, pool->L, stream);
+}
+
 kv_status kv_seq_info(const kv_pool* pool, kv_seq seq, uint32_t* table_row, uint32_t* frontier,
                       uint32_t* mapped_pages) {
     if (!pool) return fail(KV_E_INVALID, "null pool");

@@ -7,6 +7,12 @@
 // pinned staging buffer or memset node is involved, and a captured graph would
 // replay the same entries.
 //
+// Host replica (host replica passage): D2H / H2D copies of full page payloads
+// between the planes and a logical-order packed replica in pinned host
+// memory.  One block per (page, plane) slice, 16 bytes per lane; the page ids
+// travel in the argument block (chunks of kReplicaPages), so a restore copies
+// into page groups before any table row names them.
+//
 // Tail COW (Fork passage): the committed columns [0, F mod 64) of every plane
 // slice of the shared page group g are copied into the private group g'.  In
 // the page-major order [X, P, H, N] the first `cols` columns of slice (g, h)
@@ -70,7 +76,56 @@ __global__ void __launch_bounds__(256) cow_copy_kernel(CopyArgs a) {
     }
 }
 
+constexpr int kReplicaPlanes = 96;
+constexpr int kReplicaPages = 64;
+
+struct ReplicaArgs {
+    ReplicaPlane planes[kReplicaPlanes];
+    int32_t pages[kReplicaPages];
+    int32_t n_planes;
+    int32_t first_page;      // replica index of pages[0]
+    uint64_t page_bytes;
+    char* host;
+    int32_t to_host;
+};
+
+// grid (pages of the chunk, planes of the chunk); the slice of page group g
+// starts at base + g * slice_bytes (the H rows of a group are adjacent)
+__global__ void __launch_bounds__(256) replica_copy_kernel(ReplicaArgs a) {
+    const int pi = int(blockIdx.x), qi = int(blockIdx.y);
+    const ReplicaPlane pl = a.planes[qi];
+    const size_t n = pl.slice_bytes >> 4;
+    uint4* dev = reinterpret_cast<uint4*>(static_cast<char*>(pl.base) + size_t(a.pages[pi]) * pl.slice_bytes);
+    uint4* host = reinterpret_cast<uint4*>(a.host + size_t(a.first_page + pi) * a.page_bytes + pl.host_off);
+    if (a.to_host) {
+        for (size_t i = threadIdx.x; i < n; i += 256) host[i] = dev[i];
+    } else {
+        for (size_t i = threadIdx.x; i < n; i += 256) dev[i] = host[i];
+    }
+}
+
 }  // namespace
+
+hipError_t launch_replica_copy(const ReplicaPlane* planes, int n_planes, const int32_t* pages, int n_pages,
+                               uint64_t page_bytes, char* host, bool to_host, hipStream_t s) {
+    for (int p0 = 0; p0 < n_pages; p0 += kReplicaPages) {
+        for (int q0 = 0; q0 < n_planes; q0 += kReplicaPlanes) {
+            ReplicaArgs a;
+            a.n_planes = std::min(kReplicaPlanes, n_planes - q0);
+            for (int i = 0; i < a.n_planes; ++i) a.planes[i] = planes[q0 + i];
+            const int np = std::min(kReplicaPages, n_pages - p0);
+            for (int i = 0; i < np; ++i) a.pages[i] = pages[p0 + i];
+            a.first_page = p0;
+            a.page_bytes = page_bytes;
+            a.host = host;
+            a.to_host = to_host ? 1 : 0;
+            replica_copy_kernel<<<dim3(np, a.n_planes), 256, 0, s>>>(a);
+            const hipError_t e = hipGetLastError();
+            if (e != hipSuccess) return e;
+        }
+    }
+    return hipSuccess;
+}
 
 hipError_t launch_table_fill(int32_t* d_table, int32_t n, int32_t value, hipStream_t s) {
     if (n <= 0) return hipSuccess;

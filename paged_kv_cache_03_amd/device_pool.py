@@ -107,6 +107,23 @@ class DevicePool:
     def reservation(self, seq: int) -> int:
         return abi.kv_seq_reservation(self.handle, seq)
 
+    def replica_page_bytes(self) -> int:
+        return abi.kv_replica_page_bytes(self.handle)
+
+    def offload(self, seq: int, host: torch.Tensor) -> tuple:
+        """Committed pages of seq into a pinned host tensor (replica layout); (pages, frontier)."""
+        if not host.is_pinned():
+            raise ValueError("the replica buffer must be pinned host memory")
+        return abi.kv_seq_offload(self.handle, seq, host.data_ptr(), host.numel() * host.element_size(),
+                                  self.stream)
+
+    def restore(self, row: int, host: torch.Tensor, frontier: int) -> int:
+        """A new address space on row from a replica in a pinned host tensor."""
+        if not host.is_pinned():
+            raise ValueError("the replica buffer must be pinned host memory")
+        return abi.kv_seq_restore(self.handle, row, host.data_ptr(), host.numel() * host.element_size(), frontier,
+                                  self.stream)
+
     def info(self, seq: int):
         return abi.kv_seq_info(self.handle, seq)
 

@@ -277,3 +277,22 @@ def test_speculative_round_through_abi_reuses_the_reservation():
     o.ensure_mapped(sb, 64 * (M - 14))
     assert np.array_equal(np.array(abi.kv_pool_table_host(h, 2 * o.L)).reshape(2, o.L), o.table)
     abi.kv_pool_destroy(h)
+
+
+@pytest.mark.parametrize("profile,D", [("BF16", 128), ("INT8_G64", 128), ("FP8_E4M3FN_ROW256", 256),
+                                       ("NVFP4_G16", 64), ("K8V4", 256)])
+def test_replica_page_bytes_match_oracle(profile, D):
+    h = _host_pool(1024, 2, 16, H=8, D=D, profile=profile, layers=3)
+    assert abi.kv_replica_page_bytes(h) == G.page_bytes(profile, D, 8, 3)
+    abi.kv_pool_destroy(h)
+
+
+def test_replica_calls_refuse_host_only_pool():
+    h = _host_pool(1024, 2, 16)
+    s = abi.kv_seq_open(h, 0)
+    for call in (lambda: abi.kv_seq_offload(h, s, 0, 0), lambda: abi.kv_seq_restore(h, 1, 0, 0, 10)):
+        with pytest.raises(abi.KVError) as e:
+            call()
+        assert e.value.status == abi.KV_E_INVALID
+    assert abi.kv_pool_stats(h) == (0, 0, 16)
+    abi.kv_pool_destroy(h)

@@ -1,0 +1,112 @@
+"""GPU parity of the host replica (kv_seq_offload / kv_seq_restore).
+
+Planes start as 0xFF bytes, so rows past a frontier hold NaN codes; the
+replica copies full pages, and the comparison with the oracle's replica
+covers the rows before each frontier (the valid domain).  Bar: replica bytes,
+block tables and restored planes bit-exact; decode of a restored row equal to
+decode of the original bit for bit and to the oracle within 2e-3.
+"""
+
+import numpy as np
+import pytest
+
+import workloads
+from oracle import attention as A
+from oracle import geometry as G
+from tests.drivers import build_device, build_oracle, plane_np, say
+from workloads.device_driver import _dev
+
+pytestmark = pytest.mark.gpu
+
+TOL = 2e-3
+
+
+def _valid_mask(n_pages, frontier, page_bytes, plane_sizes, H):
+    """Bytes of a replica that lie before the frontier (per plane: [H][64][row])."""
+    m = np.zeros(n_pages * page_bytes, dtype=bool)
+    for i in range(n_pages):
+        rows = min(64, frontier - 64 * i)
+        off = i * page_bytes
+        for sz in plane_sizes:
+            row = sz // (H * 64)
+            blk = np.zeros((H, 64, row), dtype=bool)
+            blk[:, :rows, :] = True
+            m[off:off + sz] = blk.ravel()
+            off += sz
+    return m
+
+
+@pytest.mark.parametrize("profile,D", [("INT8_G64", 128), ("BF16", 64), ("K8V4", 256)])
+def test_offload_restore_round_trip(profile, D):
+    import torch
+    from paged_kv_cache_03_amd.device_pool import i32
+    H, layers = 2, 2
+    hist = [300, 1000, 63]
+    wl = workloads.small(140, profile, hist=hist, step=[1, 1, 1], C=6, S=2048, Hq=8, H=H, D=D, layers=layers,
+                         mode="decode")
+    pool, st, sids = build_oracle(wl)
+    dp, seqs, _ = build_device(wl, fill=0xFF)
+    pb = dp.replica_page_bytes()
+    assert pb == st.replica_page_bytes() == G.page_bytes(profile, D, H, layers)
+    sizes = [H * 64 * spec.x_extent * spec.elem_bytes for _, spec in st.replica_order()]
+    free_rows = [r for r in range(wl.C) if r not in wl.table_rows]
+    for b in range(wl.B):
+        ref, f = st.replica(sids[b])
+        n = -(-f // 64)
+        host = torch.empty(max(1, n * pb), dtype=torch.uint8, pin_memory=True)
+        assert dp.offload(seqs[b], host) == (n, f)
+        torch.cuda.synchronize()
+        got = host.numpy()[: n * pb]
+        m = _valid_mask(n, f, pb, sizes, H)
+        assert np.array_equal(got[m], ref[m]), f"entry {b}: replica bytes differ from the oracle's"
+        # restore into a free row: pages allocated in the same order on both sides
+        row = free_rows[b]
+        s_dev = dp.restore(row, host, f)
+        s_or = st.restore(row, ref, f)
+        torch.cuda.synchronize()
+        assert np.array_equal(dp.table.cpu().numpy(), pool.table)
+        assert dp.stats() == pool.stats()
+        assert dp.info(s_dev) == (row, f, n)
+        for layer in range(layers):
+            for role, arr in st.planes[layer].items():
+                dev_plane = plane_np(dp, layer, role)
+                for i, g in enumerate(pool.pages_of(s_or)):
+                    rows = min(64, f - 64 * i)
+                    assert np.array_equal(dev_plane[g][:, :rows], arr[g][:, :rows]), (layer, role, i)
+        # decode on the restored row: equal to the original row's, and to the oracle
+        if f > 0:
+            q = wl.q(0)[b:b + 1]
+            outs = []
+            for r_ in (wl.table_rows[b], row):
+                out = torch.empty((1, wl.Hq, D), dtype=torch.float32, device=dp.device)
+                ws = dp.workspace(1, wl.Hq, f)
+                dp.decode(0, wl.Hq, i32([r_], dp.device), i32([f], dp.device), f, _dev(q, dp.device), wl.sm_scale,
+                          out, ws)
+                torch.cuda.synchronize()
+                outs.append(out.cpu().numpy())
+            assert np.array_equal(outs[0], outs[1])
+            ref_out = A.paged_decode(st, 0, [row], [f], q, wl.sm_scale)
+            err = float(np.max(np.abs(outs[1] - ref_out)))
+            say(f"{profile} entry {b} f={f}: restored decode max abs err {err:.3g}")
+            assert err <= TOL
+        dp.release(s_dev)
+        pool.release(s_or)
+    torch.cuda.synchronize()
+    assert dp.stats() == pool.stats()
+    dp.close()
+
+
+def test_restore_shortfall_changes_nothing():
+    import torch
+    # M = 16 = L: one 961-token entry holds every page group
+    wl = workloads.small(141, "BF16", hist=[960], step=[1], C=2, S=1024, Hq=8, H=2, D=128, M=16, mode="decode")
+    dp, seqs, _ = build_device(wl)
+    pb = dp.replica_page_bytes()
+    host = torch.zeros(2 * pb, dtype=torch.uint8, pin_memory=True)
+    before = dp.stats()
+    assert before == (16, 0, 0)
+    with pytest.raises(Exception) as e:
+        dp.restore(1 - wl.table_rows[0], host, 100)         # 2 pages, none free
+    assert "CAPACITY" in str(e.value)
+    assert dp.stats() == before
+    dp.close()
