@@ -14,7 +14,13 @@ header they do not contain.  The reading implemented here:
   element is E2M1(x/value(S)) rounded half-to-even, saturating at +-6;
   element 2k is the low nibble of byte k; value(S) == 0 gives codes 0;
 * FP8/FP4 codes keep the sign of the quotient (so -0 encodes as the sign bit);
-* dequantization is one fp32 multiply: value(code) * scale.
+* dequantization is one fp32 multiply: value(code) * scale;
+* 2-byte scale planes (the D256 payload table's sizes): the INT8-G64 and
+  FP8-row scale is stored as IEEE binary16, s16 = f16(a/127) (or a/448),
+  the fp32 quotient rounded half-to-even to binary16 and saturated at the
+  largest finite binary16 (65504); the codes are taken against the stored
+  scale (x / float(s16)), so a code times its stored scale is the value the
+  consumer reconstructs; s16 == 0 gives codes 0.
 
 The two minifloat formats are taken from their published definitions (OCP
 8-bit floating point spec for E4M3FN: bias 7, no infinities, 0x7F/0xFF NaN,
@@ -102,36 +108,58 @@ def _absmax(xg: np.ndarray) -> np.ndarray:
     return np.max(np.abs(xg), axis=-1)
 
 
-def quant_int8_g64(x: np.ndarray):
-    """x float32 [..., D] -> (codes int8 [..., D], scales float32 [..., D/64])."""
+F16_MAX = F32(65504.0)
+
+
+def to_f16_bits(s32: np.ndarray) -> np.ndarray:
+    """fp32 scales -> binary16 bits (uint16), round half to even, saturated at 65504."""
+    return np.minimum(np.asarray(s32, dtype=np.float32), F16_MAX).astype(np.float16).view(np.uint16)
+
+
+def scale_values(scales: np.ndarray) -> np.ndarray:
+    """A scale plane's data as float32: fp32 as is, binary16 bits (uint16) widened exactly."""
+    scales = np.asarray(scales)
+    if scales.dtype == np.uint16:
+        return scales.view(np.float16).astype(np.float32)
+    return scales.astype(np.float32)
+
+
+def quant_int8_g64(x: np.ndarray, scale_bytes: int = 4):
+    """x float32 [..., D] -> (codes int8 [..., D], scales [..., D/64]: float32, or
+    binary16 bits (uint16) when scale_bytes == 2)."""
     x = np.asarray(x, dtype=np.float32)
     D = x.shape[-1]
     xg = x.reshape(x.shape[:-1] + (D // 64, 64))
     s = (_absmax(xg) / F32(127)).astype(np.float32)
+    stored = s if scale_bytes == 4 else to_f16_bits(s)
+    sv = scale_values(stored)
     with np.errstate(divide="ignore", invalid="ignore"):
-        qf = np.rint((xg / s[..., None]).astype(np.float32))
-    q = np.where(s[..., None] == 0, 0, np.clip(qf, -127, 127)).astype(np.int8)
-    return q.reshape(x.shape), s
+        qf = np.rint((xg / sv[..., None]).astype(np.float32))
+    q = np.where(sv[..., None] == 0, 0, np.clip(qf, -127, 127)).astype(np.int8)
+    return q.reshape(x.shape), stored
 
 
 def dequant_int8_g64(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
     D = codes.shape[-1]
     qg = codes.astype(np.float32).reshape(codes.shape[:-1] + (D // 64, 64))
-    return (qg * scales.astype(np.float32)[..., None]).astype(np.float32).reshape(codes.shape)
+    return (qg * scale_values(scales)[..., None]).astype(np.float32).reshape(codes.shape)
 
 
-def quant_fp8_row(x: np.ndarray):
-    """x float32 [..., D] -> (codes uint8 E4M3FN [..., D], scales float32 [..., 1])."""
+def quant_fp8_row(x: np.ndarray, scale_bytes: int = 4):
+    """x float32 [..., D] -> (codes uint8 E4M3FN [..., D], scales [..., 1]: float32,
+    or binary16 bits (uint16) when scale_bytes == 2)."""
     x = np.asarray(x, dtype=np.float32)
     s = (_absmax(x) / F32(E4M3FN_MAX)).astype(np.float32)[..., None]
+    stored = s if scale_bytes == 4 else to_f16_bits(s)
+    sv = scale_values(stored)
     with np.errstate(divide="ignore", invalid="ignore"):
-        y = (x / s).astype(np.float32)
-    codes = np.where(s == 0, np.uint8(0), encode_e4m3fn(np.where(s == 0, F32(0), y)))
-    return codes.astype(np.uint8), s
+        y = (x / sv).astype(np.float32)
+    codes = np.where(sv == 0, np.uint8(0), encode_e4m3fn(np.where(sv == 0, F32(0), y)))
+    return codes.astype(np.uint8), stored
 
 
 def dequant_fp8_row(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
-    return (decode_e4m3fn(codes) * scales.astype(np.float32)).astype(np.float32)
+    return (decode_e4m3fn(codes) * scale_values(scales)).astype(np.float32)
 
 
 def quant_nvfp4_g16(x: np.ndarray):
@@ -164,15 +192,16 @@ def dequant_nvfp4_g16(packed: np.ndarray, s_code: np.ndarray) -> np.ndarray:
     return (vg * decode_e4m3fn(s_code)[..., None]).astype(np.float32).reshape(vals.shape)
 
 
-def quantize(kind: str, x_bf16: np.ndarray) -> tuple[np.ndarray, np.ndarray | None]:
-    """Quantize bf16 rows [..., D] for one side; returns (code plane data, scale data)."""
+def quantize(kind: str, x_bf16: np.ndarray, scale_bytes: int = 4) -> tuple[np.ndarray, np.ndarray | None]:
+    """Quantize bf16 rows [..., D] for one side; returns (code plane data, scale data).
+    scale_bytes (4 or 2) applies to the INT8-G64 and FP8-row scales."""
     if kind == "bf16":
         return np.asarray(x_bf16, dtype=np.uint16).copy(), None
     x = bf16_to_f32(x_bf16)
     if kind == "int8_g64":
-        return quant_int8_g64(x)
+        return quant_int8_g64(x, scale_bytes)
     if kind == "fp8_row":
-        return quant_fp8_row(x)
+        return quant_fp8_row(x, scale_bytes)
     if kind == "nvfp4_g16":
         return quant_nvfp4_g16(x)
     raise ValueError(kind)

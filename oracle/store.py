@@ -26,15 +26,19 @@ _NP_DTYPE = {"bf16": np.uint16, "i8": np.int8, "e4m3fn": np.uint8, "e2m1x2": np.
 
 
 class OracleStore:
-    def __init__(self, pool: OraclePool, profile: str, H: int, D: int, layers: int):
+    def __init__(self, pool: OraclePool, profile: str, H: int, D: int, layers: int, scale_bytes: int = 4):
+        """scale_bytes: 4 (fp32) or 2 (binary16) INT8-G64 / FP8-row scale planes."""
+        if scale_bytes not in (2, 4):
+            raise ValueError("scale planes are 4 or 2 bytes")
         self.pool, self.profile, self.H, self.D, self.layers = pool, profile, H, D, layers
+        self.scale_bytes = scale_bytes
         self.kinds = PROFILE_SIDES[profile]
-        self.schema = plane_schema(profile, D, scale_bytes=4)
+        self.schema = plane_schema(profile, D, scale_bytes=scale_bytes)
         self.planes = []
         for _ in range(layers):
             lp = {}
             for spec in self.schema:
-                dt = np.float32 if spec.kind == "scale" else _NP_DTYPE[spec.kind]
+                dt = (np.float32 if scale_bytes == 4 else np.uint16) if spec.kind == "scale" else _NP_DTYPE[spec.kind]
                 lp[spec.role] = np.zeros((pool.M, H, P, spec.x_extent), dtype=dt)
             self.planes.append(lp)
 
@@ -49,7 +53,7 @@ class OracleStore:
         if np.any(pages < 0):
             raise ValueError("append into an unmapped logical block")
         for side, x in (("K", k_bf16), ("V", v_bf16)):
-            code, scale = codecs.quantize(self.kinds[0 if side == "K" else 1], x)
+            code, scale = codecs.quantize(self.kinds[0 if side == "K" else 1], x, self.scale_bytes)
             lp[f"{side}_CODE"][pages, :, offs, :] = code
             if scale is not None:
                 lp[f"{side}_SCALE"][pages, :, offs, :] = scale.reshape(T, self.H, -1)

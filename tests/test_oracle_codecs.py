@@ -197,3 +197,72 @@ def test_quantize_dispatch_shapes(kind):
         assert np.array_equal(back, Q.bf16_to_f32(xb))
     else:
         assert np.max(np.abs(back - Q.bf16_to_f32(xb))) < 1.0
+
+
+# ----------------------------------------------------- 2-byte scale planes --
+def test_f16_scale_rounding_matches_torch_half_conversion():
+    import torch
+    from oracle.codecs import to_f16_bits
+    rng = np.random.default_rng(11)
+    # random magnitudes over the binary16 range, exact midpoints between
+    # neighbouring binary16 values (ties), subnormals, zero
+    vals = [np.float32(x) for x in np.exp(rng.uniform(np.log(1e-9), np.log(6e4), 20000))]
+    h = np.arange(1, 0x7BFF, 37, dtype=np.uint16).view(np.float16).astype(np.float32)
+    mids = ((h[:-1].astype(np.float64) + h[1:].astype(np.float64)) / 2).astype(np.float32)
+    x = np.concatenate([np.array(vals, np.float32), h, mids, np.float32([0.0, 2.0 ** -25, 3 * 2.0 ** -26])])
+    want = torch.from_numpy(x).to(torch.float16).numpy().view(np.uint16)
+    assert np.array_equal(to_f16_bits(x), want)
+    # saturation at the largest finite value instead of infinity
+    assert to_f16_bits(np.float32([65520.0, 1e9]))[0] == 0x7BFF == to_f16_bits(np.float32([1e9]))[0]
+
+
+def test_int8_g64_f16_scale_equals_fp32_scale_when_exact():
+    from oracle.codecs import quant_int8_g64
+    rng = np.random.default_rng(12)
+    # absmax of every group exactly 127 * 2^k: a/127 is exact in binary16 and in fp32
+    amax = (127.0 * 2.0 ** rng.integers(-8, 6, size=(500, 2))).astype(np.float32)
+    x = (rng.uniform(-0.99, 0.99, (500, 2, 64)) * amax[..., None]).astype(np.float32)
+    j = rng.integers(0, 64, size=(500, 2))
+    np.put_along_axis(x, j[..., None], (amax * np.where(rng.random((500, 2)) < 0.5, -1, 1))[..., None], axis=-1)
+    x = x.reshape(500, 128)
+    q4, s4 = quant_int8_g64(x, 4)
+    q2, s2 = quant_int8_g64(x, 2)
+    assert np.array_equal(q4, q2)
+    assert np.array_equal(s2.view(np.float16).astype(np.float32), s4)
+
+
+def test_int8_g64_f16_scale_error_bound():
+    from oracle.codecs import dequant_int8_g64, quant_int8_g64, scale_values
+    rng = np.random.default_rng(13)
+    x = (rng.standard_normal((4000, 128)) * np.exp(rng.uniform(-6, 6, (4000, 1)))).astype(np.float32)
+    q, s16 = quant_int8_g64(x, 2)
+    sv = np.repeat(scale_values(s16), 64, axis=-1)
+    err = np.abs(dequant_int8_g64(q, s16) - x)
+    over = np.maximum(np.abs(x) - 127 * sv, 0)        # a scale rounded down clips at 127
+    assert np.all(err <= sv / 2 * (1 + 2 ** -20) + over + 1e-30)
+    normal = sv >= 2.0 ** -14                          # normal binary16 scales: half an ulp is 2^-11 relative
+    assert np.all(over[normal] <= 127 * sv[normal] * 2.0 ** -11 * 1.01)
+
+
+def test_fp8_row_f16_scale_equals_fp32_scale_when_exact():
+    from oracle.codecs import quant_fp8_row
+    rng = np.random.default_rng(14)
+    amax = (448.0 * 2.0 ** rng.integers(-10, 4, size=300)).astype(np.float32)
+    x = (rng.uniform(-0.99, 0.99, (300, 256)) * amax[:, None]).astype(np.float32)
+    x[np.arange(300), rng.integers(0, 256, size=300)] = amax
+    c4, s4 = quant_fp8_row(x, 4)
+    c2, s2 = quant_fp8_row(x, 2)
+    assert np.array_equal(c4, c2)
+    assert np.array_equal(s2.view(np.float16).astype(np.float32), s4)
+
+
+@pytest.mark.parametrize("profile,table_bytes", [("BF16", 1024), ("INT8_G64", 528), ("FP8_E4M3FN_ROW256", 516),
+                                                 ("NVFP4_G16", 288), ("K8V4", 402)])
+def test_store_with_two_byte_scales_reproduces_the_d256_payload_table(profile, table_bytes):
+    from oracle.pool import OraclePool
+    from oracle.store import OracleStore
+    pool = OraclePool(S=1024, C=1, M=16)
+    st = OracleStore(pool, profile, 2, 256, 1, scale_bytes=2)
+    per_token_head = sum(arr[0, 0, 0].nbytes for arr in st.planes[0].values())
+    assert per_token_head == table_bytes
+    assert st.replica_page_bytes() == table_bytes * 2 * 64
