@@ -63,16 +63,17 @@ def log(msg: str) -> None:
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def bytes_per_token_head(profile: str, D: int) -> int:
+def bytes_per_token_head(profile: str, D: int, scale_bytes: int = 4) -> int:
     from paged_kv_cache_03_amd import _abi as abi
-    return sum(p.x_extent * p.elem_bytes for p in abi.kv_profile_planes(abi.KV_PROFILE[profile], D))
+    dt = abi.KV_DT_F16 if scale_bytes == 2 else abi.KV_DT_F32
+    return sum(p.x_extent * p.elem_bytes for p in abi.kv_profile_planes(abi.KV_PROFILE[profile], D, dt))
 
 
 def kv_read_bytes(table, wl) -> tuple[int, int]:
     """(unique, logical) KV bytes decode reads: every valid (page, column) of every
     entry; a page shared by several entries counts once in `unique`."""
     import numpy as np
-    bpth = bytes_per_token_head(wl.profile, wl.D)
+    bpth = bytes_per_token_head(wl.profile, wl.D, wl.scale_bytes)
     cols = {}
     logical = 0
     for b, ctx in enumerate(wl.seq_lens):
@@ -154,7 +155,7 @@ def cpu_baseline(wl, seconds_hint: float = 20.0) -> dict:
         threads = 1
     log("cpu baseline: building the oracle's pool for layer 0")
     pool = OraclePool(wl.S, wl.C, wl.M, free_order=wl.free_order)
-    st = OracleStore(pool, wl.profile, wl.H, wl.D, 1)
+    st = OracleStore(pool, wl.profile, wl.H, wl.D, 1, scale_bytes=wl.scale_bytes)
     sids = {}
     for b in wl.order():
         row = wl.table_rows[b]
@@ -259,7 +260,7 @@ def bench_verify(wl, args) -> int:
     pairs = sum(n0 * T + T * (T + 1) // 2 for n0, T in zip(wl.hist, wl.step))
     flops = 4.0 * wl.D * wl.Hq * pairs                      # per layer
     table = dp.table.cpu().numpy()
-    bpth = bytes_per_token_head(wl.profile, wl.D)
+    bpth = bytes_per_token_head(wl.profile, wl.D, wl.scale_bytes)
     kv_bytes = sum(len({int(table[wl.table_rows[b], p]) for p in range((c + 63) // 64)}) * 64 * wl.H * bpth
                    for b, c in enumerate(wl.seq_lens))
     tflops = flops / (ver_ms * 1e-3) / 1e12
@@ -363,7 +364,7 @@ def bench_spec(wl, args) -> int:
     ver_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
     a_, res_, v_ = dp.stats()
     reserved = [dp.reservation(seqs[b]) for b in range(B)]
-    bpth = bytes_per_token_head(wl.profile, wl.D)
+    bpth = bytes_per_token_head(wl.profile, wl.D, wl.scale_bytes)
     kv_bytes = sum(front) * wl.H * bpth          # the last round's histories, about those of every round
     achieved = kv_bytes / (ver_ms * 1e-3) / 1e9
     line = {
@@ -473,6 +474,8 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", type=int, default=2, help="workload number (1-4: decode, 5: verify/prefill)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--scale-bytes", type=int, choices=(2, 4), default=4,
+                    help="INT8-G64 / FP8-row scale planes: 4 (fp32) or 2 (binary16, the page's D256 byte table)")
     ap.add_argument("--graph", action="store_true",
                     help="decode configs: time replays of the step captured as one HIP graph")
     ap.add_argument("--replica", action="store_true",
@@ -498,6 +501,9 @@ def main() -> int:
     from workloads.device_driver import _dev, build_device
 
     wl = workloads.get(args.config)
+    if args.scale_bytes != 4:
+        wl.scale_bytes = args.scale_bytes
+        wl.name += f"_scales{8 * args.scale_bytes}bit"
     if args.spec:
         if wl.mode != "verify":
             print("--spec needs the verify workload (--config 5)", file=sys.stderr)
@@ -588,7 +594,7 @@ def main() -> int:
 
     table = dp.table.cpu().numpy()
     unique, logical = kv_read_bytes(table, wl)
-    bpth = bytes_per_token_head(wl.profile, wl.D)
+    bpth = bytes_per_token_head(wl.profile, wl.D, wl.scale_bytes)
     qo_bytes = wl.B * wl.Hq * wl.D * (2 + 4)
     append_bytes = total * wl.H * (bpth + 2 * 2 * wl.D)
     per_decode = unique + qo_bytes
@@ -606,7 +612,7 @@ def main() -> int:
         "vs_baseline": None, "dtype": "bf16" if wl.profile == "BF16" else wl.profile.lower(), "data": "synthetic",
         "config": {"workload": wl.name, "profile": wl.profile, "batch": wl.B, "layers": wl.layers, "q_heads": wl.Hq,
                    "kv_heads": wl.H, "head_dim": wl.D, "ctx_sum": int(sum(wl.seq_lens)), "ctx_max": int(max_ctx),
-                   "page_size": 64, "pool_pages": wl.M},
+                   "page_size": 64, "pool_pages": wl.M, "scale_bytes": wl.scale_bytes},
         "steps_per_s": round(1000.0 / ms_per_step, 2),
         "hbm_frac": round(value / HBM_PEAK_GBS, 4),
         "step_form": "hip_graph" if graph is not None else "eager",

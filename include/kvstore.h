@@ -66,6 +66,8 @@ typedef int32_t kv_status;
 #define KV_DT_E2M1X2   3  /* two FP4 E2M1 codes per byte, element 2k in the low nibble */
 #define KV_DT_F32      4  /* fp32 scales (INT8-G64 per 64 elements, FP8-row per row) */
 #define KV_DT_U8_E4M3  5  /* NVFP4-G16 scales: one E4M3FN byte per 16 elements */
+#define KV_DT_F16      6  /* binary16 scales (INT8-G64, FP8-row): the 2-byte scale planes of the D256 payload
+                             table; scale = binary16(fp32 quotient), rounded half to even, saturated at 65504 */
 
 /* Plane roles; the K and V code planes and scale planes of one layer share a
  * page-group id (plane-grouping rule). */
@@ -111,6 +113,15 @@ typedef uint64_t kv_seq;          /* generation-tagged address-space handle; 0 i
  * KV_E_INVALID if the buffer is too small; KV_E_GEOMETRY if head_dim is not a
  * multiple of the profile's groups. */
 kv_status kv_profile_planes(uint32_t profile, uint32_t head_dim, KVPlaneDesc* out, uint32_t* n_inout);
+
+/* kv_profile_planes with the dtype of the INT8-G64 / FP8-row scale planes:
+ * KV_DT_F32 (as kv_profile_planes) or KV_DT_F16 (2-byte scales: bytes per
+ * token and KV head at D=256 are those of the page's D256 payload table,
+ * 1024 / 528 / 516 / 288 / 402).  NVFP4-G16 scales are E4M3 bytes either
+ * way.  A pool takes one scale dtype for all its planes.  KV_E_INVALID for
+ * another dtype. */
+kv_status kv_profile_planes_ex(uint32_t profile, uint32_t head_dim, uint32_t scale_dtype, KVPlaneDesc* out,
+                               uint32_t* n_inout);
 
 /* Bytes of one plane slab for a geometry: M * H * 64 * X * elem_bytes. */
 kv_status kv_plane_bytes(const KVPageGeometry* geo, const KVPlaneDesc* plane, uint64_t* bytes);

@@ -20,11 +20,11 @@ STATUS_NAMES = {0: "OK", 1: "INVALID", 2: "GEOMETRY", 3: "CAPACITY", 4: "STALE",
                 6: "UNMAPPED", 7: "DEVICE", 8: "UNSUPPORTED"}
 
 KV_PROFILE = {"BF16": 0, "INT8_G64": 1, "FP8_E4M3FN_ROW256": 2, "NVFP4_G16": 3, "K8V4": 4}
-KV_DT_BF16, KV_DT_I8, KV_DT_E4M3FN, KV_DT_E2M1X2, KV_DT_F32, KV_DT_U8_E4M3 = range(6)
+KV_DT_BF16, KV_DT_I8, KV_DT_E4M3FN, KV_DT_E2M1X2, KV_DT_F32, KV_DT_U8_E4M3, KV_DT_F16 = range(7)
 KV_ROLE_K_CODE, KV_ROLE_K_SCALE, KV_ROLE_V_CODE, KV_ROLE_V_SCALE = range(4)
 
 # exported symbols, in header order (the CPU test checks the header declares exactly these)
-EXPORTS = ["kv_profile_planes", "kv_plane_bytes", "kv_pool_create", "kv_pool_destroy", "kv_pool_stats",
+EXPORTS = ["kv_profile_planes", "kv_profile_planes_ex", "kv_plane_bytes", "kv_pool_create", "kv_pool_destroy", "kv_pool_stats",
            "kv_pool_table_host", "kv_pool_page_refs", "kv_seq_open", "kv_seq_fork", "kv_seq_ensure_mapped",
            "kv_seq_commit", "kv_seq_release", "kv_seq_reserve", "kv_seq_trim", "kv_seq_commit_accepted",
            "kv_seq_reservation", "kv_draft_pool_pages", "kv_replica_page_bytes", "kv_seq_offload",
@@ -70,6 +70,7 @@ def _load():
     P = ctypes.POINTER
     sig = {
         "kv_profile_planes": (i32, [u32, u32, P(KVPlaneDesc), P(u32)]),
+        "kv_profile_planes_ex": (i32, [u32, u32, u32, P(KVPlaneDesc), P(u32)]),
         "kv_plane_bytes": (i32, [P(KVPageGeometry), P(KVPlaneDesc), P(ctypes.c_uint64)]),
         "kv_pool_create": (i32, [P(KVPageGeometry), P(KVPlaneDesc), u32, vp, P(i32), vp, P(vp)]),
         "kv_pool_destroy": (None, [vp]),
@@ -124,10 +125,14 @@ def kv_last_error_message() -> str:
     return _lib.kv_last_error_message().decode()
 
 
-def kv_profile_planes(profile: int, head_dim: int) -> list:
+def kv_profile_planes(profile: int, head_dim: int, scale_dtype: int | None = None) -> list:
+    """The profile's plane schema; scale_dtype KV_DT_F16 for 2-byte INT8-G64 / FP8-row scales."""
     buf = (KVPlaneDesc * 4)()
     n = ctypes.c_uint32(4)
-    _check(_lib.kv_profile_planes(profile, head_dim, buf, ctypes.byref(n)))
+    if scale_dtype is None:
+        _check(_lib.kv_profile_planes(profile, head_dim, buf, ctypes.byref(n)))
+    else:
+        _check(_lib.kv_profile_planes_ex(profile, head_dim, scale_dtype, buf, ctypes.byref(n)))
     return [buf[i] for i in range(n.value)]
 
 

@@ -50,8 +50,29 @@ __device__ __forceinline__ void load_row(const uint16_t* src, int lane, float (&
     }
 }
 
+// A scale as stored: fp32 (SB = 4) or binary16 (SB = 2: the quotient saturated
+// at 65504, then rounded half to even).  Returns the value the codes are taken
+// against and writes it to scale element `idx`.
+template <int SB>
+__device__ __forceinline__ float store_scale(void* scale, size_t idx, float s32) {
+    if constexpr (SB == 4) {
+        static_cast<float*>(scale)[idx] = s32;
+        return s32;
+    } else {
+        const _Float16 h = static_cast<_Float16>(fminf(s32, 65504.0f));
+        static_cast<uint16_t*>(scale)[idx] = __builtin_bit_cast(uint16_t, h);
+        return static_cast<float>(h);
+    }
+}
+
+template <int SB>
+__device__ __forceinline__ float rounded_scale(float s32) {
+    if constexpr (SB == 4) return s32;
+    else return static_cast<float>(static_cast<_Float16>(fminf(s32, 65504.0f)));
+}
+
 // Quantize and store one row (EPL elements per lane) of one side.
-template <int D, int CODEC>
+template <int D, int CODEC, int SB>
 __device__ __forceinline__ void write_side(void* code, void* scale, size_t slot, const uint16_t* src, int lane) {
     constexpr int EPL = D / 64;
     float x[EPL];
@@ -67,7 +88,9 @@ __device__ __forceinline__ void write_side(void* code, void* scale, size_t slot,
 #pragma unroll
         for (int e = 0; e < EPL; ++e) a = fmaxf(a, __builtin_fabsf(x[e]));
         a = group_max<GL>(a);
-        const float s = a / 127.0f;
+        const float s32 = a / 127.0f;
+        const float s = lane % GL == 0 ? store_scale<SB>(scale, slot * (D / 64) + lane / GL, s32)
+                                       : rounded_scale<SB>(s32);
         int8_t* c = static_cast<int8_t*>(code) + slot * D + lane * EPL;
 #pragma unroll
         for (int e = 0; e < EPL; ++e) {
@@ -75,17 +98,16 @@ __device__ __forceinline__ void write_side(void* code, void* scale, size_t slot,
             if (s != 0.f) q = fminf(fmaxf(__builtin_rintf(x[e] / s), -127.f), 127.f);
             c[e] = int8_t(int(q));
         }
-        if (lane % GL == 0) static_cast<float*>(scale)[slot * (D / 64) + lane / GL] = s;
     } else if constexpr (CODEC == CODEC_FP8_ROW) {
         float a = 0.f;
 #pragma unroll
         for (int e = 0; e < EPL; ++e) a = fmaxf(a, __builtin_fabsf(x[e]));
         a = group_max<64>(a);
-        const float s = a / 448.0f;
+        const float s32 = a / 448.0f;
+        const float s = lane == 0 ? store_scale<SB>(scale, slot, s32) : rounded_scale<SB>(s32);
         uint8_t* c = static_cast<uint8_t*>(code) + slot * D + lane * EPL;
 #pragma unroll
         for (int e = 0; e < EPL; ++e) c[e] = uint8_t(s != 0.f ? f32_to_e4m3fn(x[e] / s) : 0u);
-        if (lane == 0) static_cast<float*>(scale)[slot] = s;
     } else {  // CODEC_NVFP4_G16
         constexpr int GL = 16 / EPL;                      // lanes per 16-element group
         float a = 0.f;
@@ -109,7 +131,7 @@ __device__ __forceinline__ void write_side(void* code, void* scale, size_t slot,
     }
 }
 
-template <int D, int KC, int VC>
+template <int D, int KC, int VC, int SB>
 __global__ void __launch_bounds__(256) append_kernel(AppendArgs a) {
     const int lane = threadIdx.x & 63;
     const int r = blockIdx.x * 4 + int(threadIdx.x >> 6);
@@ -127,20 +149,27 @@ __global__ void __launch_bounds__(256) append_kernel(AppendArgs a) {
     const int g = a.pv.table[size_t(row) * a.pv.L + blk];
     if (g < 0 || g >= a.pv.M) return;                      // unmapped: caller guarantee broken, skip
     const size_t slot = (size_t(g) * H + h) * kPage + o;   // row index of (g, h, o) in every plane
-    write_side<D, KC>(a.pv.lv.k_code, a.pv.lv.k_scale, slot, a.k + size_t(r) * D, lane);
-    write_side<D, VC>(a.pv.lv.v_code, a.pv.lv.v_scale, slot, a.v + size_t(r) * D, lane);
+    write_side<D, KC, SB>(a.pv.lv.k_code, a.pv.lv.k_scale, slot, a.k + size_t(r) * D, lane);
+    write_side<D, VC, SB>(a.pv.lv.v_code, a.pv.lv.v_scale, slot, a.v + size_t(r) * D, lane);
 }
 
 template <int D>
 hipError_t launch_d(const AppendArgs& a, dim3 grid, hipStream_t s) {
     const int kc = a.pv.k_codec, vc = a.pv.v_codec;
-#define KVS_APPEND_CASE(K, V) \
-    if (kc == K && vc == V) { append_kernel<D, K, V><<<grid, 256, 0, s>>>(a); return hipGetLastError(); }
-    KVS_APPEND_CASE(CODEC_BF16, CODEC_BF16)
-    KVS_APPEND_CASE(CODEC_INT8_G64, CODEC_INT8_G64)
-    KVS_APPEND_CASE(CODEC_FP8_ROW, CODEC_FP8_ROW)
-    KVS_APPEND_CASE(CODEC_NVFP4_G16, CODEC_NVFP4_G16)
-    KVS_APPEND_CASE(CODEC_FP8_ROW, CODEC_NVFP4_G16)
+    const bool s16 = a.pv.scale16 != 0;
+#define KVS_APPEND_CASE(K, V, SB)                                                                  \
+    if (kc == K && vc == V && s16 == (SB == 2)) {                                                  \
+        append_kernel<D, K, V, SB><<<grid, 256, 0, s>>>(a);                                       \
+        return hipGetLastError();                                                                  \
+    }
+    KVS_APPEND_CASE(CODEC_BF16, CODEC_BF16, 4)
+    KVS_APPEND_CASE(CODEC_INT8_G64, CODEC_INT8_G64, 4)
+    KVS_APPEND_CASE(CODEC_FP8_ROW, CODEC_FP8_ROW, 4)
+    KVS_APPEND_CASE(CODEC_NVFP4_G16, CODEC_NVFP4_G16, 4)
+    KVS_APPEND_CASE(CODEC_FP8_ROW, CODEC_NVFP4_G16, 4)
+    KVS_APPEND_CASE(CODEC_INT8_G64, CODEC_INT8_G64, 2)
+    KVS_APPEND_CASE(CODEC_FP8_ROW, CODEC_FP8_ROW, 2)
+    KVS_APPEND_CASE(CODEC_FP8_ROW, CODEC_NVFP4_G16, 2)
 #undef KVS_APPEND_CASE
     return hipErrorNotSupported;
 }

@@ -39,7 +39,7 @@ namespace {
 
 // One 64-lane wave per work item (entry b, KV head h, chunk c).  QK: lane t
 // owns token t of the page; PV: lane owns EPL = D/64 head_dim elements.
-template <int D, int GQ, int KC, int VC>
+template <int D, int GQ, int KC, int VC, int SB>
 __global__ void __launch_bounds__(256) decode_split_kernel(DecodeArgs a) {
     constexpr int EPL = D / 64;
     __shared__ float q_s[4][GQ][D];
@@ -84,7 +84,7 @@ __global__ void __launch_bounds__(256) decode_split_kernel(DecodeArgs a) {
         if (valid) {
             for (int d0 = 0; d0 < D; d0 += 8) {
                 float kv[8];
-                KVRow<KC, D>::load8(a.pv.lv.k_code, a.pv.lv.k_scale, slab + lane, d0, kv);
+                KVRow<KC, D, SB>::load8(a.pv.lv.k_code, a.pv.lv.k_scale, slab + lane, d0, kv);
 #pragma unroll
                 for (int j = 0; j < GQ; ++j)
 #pragma unroll
@@ -108,7 +108,7 @@ __global__ void __launch_bounds__(256) decode_split_kernel(DecodeArgs a) {
         for (int t = 0; t < nvalid; ++t) {
             float v[EPL];
 #pragma unroll
-            for (int e = 0; e < EPL; ++e) v[e] = KVRow<VC, D>::load1(a.pv.lv.v_code, a.pv.lv.v_scale, slab + t,
+            for (int e = 0; e < EPL; ++e) v[e] = KVRow<VC, D, SB>::load1(a.pv.lv.v_code, a.pv.lv.v_scale, slab + t,
                                                                       lane * EPL + e);
 #pragma unroll
             for (int j = 0; j < GQ; ++j) {
@@ -802,16 +802,20 @@ hipError_t launch_gq(const DecodeArgs& a, bool stream, hipStream_t s) {
     const dim3 grid(unsigned((items + 3) / 4));
     const int kc = a.pv.k_codec, vc = a.pv.v_codec;
     bool launched = false;
-#define KVS_DEC_CASE(K, V)                                                       \
-    if (!launched && kc == K && vc == V) {                                      \
-        if (items > 0) decode_split_kernel<D, GQ, K, V><<<grid, 256, 0, s>>>(a); \
-        launched = true;                                                         \
+    const bool s16 = a.pv.scale16 != 0;
+#define KVS_DEC_CASE(K, V, SB)                                                       \
+    if (!launched && kc == K && vc == V && s16 == (SB == 2)) {                      \
+        if (items > 0) decode_split_kernel<D, GQ, K, V, SB><<<grid, 256, 0, s>>>(a); \
+        launched = true;                                                             \
     }
-    KVS_DEC_CASE(CODEC_BF16, CODEC_BF16)
-    KVS_DEC_CASE(CODEC_INT8_G64, CODEC_INT8_G64)
-    KVS_DEC_CASE(CODEC_FP8_ROW, CODEC_FP8_ROW)
-    KVS_DEC_CASE(CODEC_NVFP4_G16, CODEC_NVFP4_G16)
-    KVS_DEC_CASE(CODEC_FP8_ROW, CODEC_NVFP4_G16)
+    KVS_DEC_CASE(CODEC_BF16, CODEC_BF16, 4)
+    KVS_DEC_CASE(CODEC_INT8_G64, CODEC_INT8_G64, 4)
+    KVS_DEC_CASE(CODEC_FP8_ROW, CODEC_FP8_ROW, 4)
+    KVS_DEC_CASE(CODEC_NVFP4_G16, CODEC_NVFP4_G16, 4)
+    KVS_DEC_CASE(CODEC_FP8_ROW, CODEC_NVFP4_G16, 4)
+    KVS_DEC_CASE(CODEC_INT8_G64, CODEC_INT8_G64, 2)
+    KVS_DEC_CASE(CODEC_FP8_ROW, CODEC_FP8_ROW, 2)
+    KVS_DEC_CASE(CODEC_FP8_ROW, CODEC_NVFP4_G16, 2)
 #undef KVS_DEC_CASE
     if (!launched) return hipErrorNotSupported;
     hipError_t e = hipGetLastError();

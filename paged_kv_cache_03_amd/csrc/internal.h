@@ -37,6 +37,7 @@ struct PoolView {
     int32_t M;
     int32_t k_codec;
     int32_t v_codec;
+    int32_t scale16;        // 1: INT8-G64 / FP8-row scale planes hold binary16 (2 bytes), else fp32
 };
 
 // Launchers (defined in the .hip files).  Each returns hipSuccess or the

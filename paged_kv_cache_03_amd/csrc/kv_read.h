@@ -15,17 +15,25 @@
 
 namespace kvs {
 
-template <int CODEC, int D>
+// scale element i of an INT8-G64 / FP8-row scale plane: fp32 (SB = 4) or
+// binary16 (SB = 2), widened exactly
+template <int SB>
+__device__ __forceinline__ float scale_at(const void* scale, size_t i) {
+    if constexpr (SB == 4) return static_cast<const float*>(scale)[i];
+    else return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<const uint16_t*>(scale)[i]));
+}
+
+template <int CODEC, int D, int SB = 4>
 struct KVRow {
     // element d of row `slot`
     static __device__ __forceinline__ float load1(const void* code, const void* scale, size_t slot, int d) {
         if constexpr (CODEC == CODEC_BF16) {
             return bf16_bits_to_f32(static_cast<const uint16_t*>(code)[slot * D + d]);
         } else if constexpr (CODEC == CODEC_INT8_G64) {
-            const float s = static_cast<const float*>(scale)[slot * (D / 64) + d / 64];
+            const float s = scale_at<SB>(scale, slot * (D / 64) + d / 64);
             return float(static_cast<const int8_t*>(code)[slot * D + d]) * s;
         } else if constexpr (CODEC == CODEC_FP8_ROW) {
-            const float s = static_cast<const float*>(scale)[slot];
+            const float s = scale_at<SB>(scale, slot);
             return e4m3fn_to_f32(static_cast<const uint8_t*>(code)[slot * D + d]) * s;
         } else {
             const float vs = e4m3fn_to_f32(static_cast<const uint8_t*>(scale)[slot * (D / 16) + d / 16]);
@@ -47,13 +55,13 @@ struct KVRow {
             }
         } else if constexpr (CODEC == CODEC_INT8_G64) {
             const uint2 u = *reinterpret_cast<const uint2*>(static_cast<const int8_t*>(code) + slot * D + d0);
-            const float s = static_cast<const float*>(scale)[slot * (D / 64) + d0 / 64];
+            const float s = scale_at<SB>(scale, slot * (D / 64) + d0 / 64);
             const uint32_t w[2] = {u.x, u.y};
 #pragma unroll
             for (int i = 0; i < 8; ++i) out[i] = float(int8_t((w[i / 4] >> (8 * (i % 4))) & 0xFFu)) * s;
         } else if constexpr (CODEC == CODEC_FP8_ROW) {
             const uint2 u = *reinterpret_cast<const uint2*>(static_cast<const uint8_t*>(code) + slot * D + d0);
-            const float s = static_cast<const float*>(scale)[slot];
+            const float s = scale_at<SB>(scale, slot);
             const uint32_t w[2] = {u.x, u.y};
 #pragma unroll
             for (int i = 0; i < 8; ++i) out[i] = e4m3fn_to_f32((w[i / 4] >> (8 * (i % 4))) & 0xFFu) * s;

@@ -47,6 +47,7 @@ uint32_t dtype_bytes(uint32_t dt) {
         case KV_DT_BF16: return 2;
         case KV_DT_I8: case KV_DT_E4M3FN: case KV_DT_E2M1X2: case KV_DT_U8_E4M3: return 1;
         case KV_DT_F32: return 4;
+        case KV_DT_F16: return 2;
         default: return 0;
     }
 }
@@ -57,14 +58,14 @@ struct SideSchema {
     uint32_t code_dt, code_x, scale_dt, scale_x;  // scale_dt == UINT32_MAX: no scale plane
 };
 
-bool side_schema(int codec, uint32_t D, SideSchema* s) {
+bool side_schema(int codec, uint32_t D, SideSchema* s, uint32_t scale_dt = KV_DT_F32) {
     s->codec = codec;
     switch (codec) {
         case CODEC_BF16: *s = {codec, KV_DT_BF16, D, UINT32_MAX, 0}; return true;
         case CODEC_INT8_G64:
             if (D % 64) return false;
-            *s = {codec, KV_DT_I8, D, KV_DT_F32, D / 64}; return true;
-        case CODEC_FP8_ROW: *s = {codec, KV_DT_E4M3FN, D, KV_DT_F32, 1}; return true;
+            *s = {codec, KV_DT_I8, D, scale_dt, D / 64}; return true;
+        case CODEC_FP8_ROW: *s = {codec, KV_DT_E4M3FN, D, scale_dt, 1}; return true;
         case CODEC_NVFP4_G16:
             if (D % 16) return false;
             *s = {codec, KV_DT_E2M1X2, D / 2, KV_DT_U8_E4M3, D / 16}; return true;
@@ -83,11 +84,13 @@ bool profile_codecs(uint32_t profile, int* kc, int* vc) {
     return false;
 }
 
-// Which codec a (code dtype, scale dtype, scale X) triple denotes.
+// Which codec a (code dtype, scale dtype, scale X) triple denotes (INT8-G64
+// and FP8-row scales may be fp32 or binary16).
 int codec_of(uint32_t code_dt, bool has_scale, uint32_t scale_dt, uint32_t scale_x, uint32_t D) {
+    const bool wide = scale_dt == KV_DT_F32 || scale_dt == KV_DT_F16;
     if (code_dt == KV_DT_BF16 && !has_scale) return CODEC_BF16;
-    if (code_dt == KV_DT_I8 && has_scale && scale_dt == KV_DT_F32 && scale_x == D / 64) return CODEC_INT8_G64;
-    if (code_dt == KV_DT_E4M3FN && has_scale && scale_dt == KV_DT_F32 && scale_x == 1) return CODEC_FP8_ROW;
+    if (code_dt == KV_DT_I8 && has_scale && wide && scale_x == D / 64) return CODEC_INT8_G64;
+    if (code_dt == KV_DT_E4M3FN && has_scale && wide && scale_x == 1) return CODEC_FP8_ROW;
     if (code_dt == KV_DT_E2M1X2 && has_scale && scale_dt == KV_DT_U8_E4M3 && scale_x == D / 16)
         return CODEC_NVFP4_G16;
     return -1;
@@ -108,6 +111,7 @@ struct kv_pool {
     KVPageGeometry geo{};
     uint32_t L = 0;
     int k_codec = 0, v_codec = 0;
+    int scale16 = 0;                      // INT8-G64 / FP8-row scale planes are binary16
     std::vector<LayerView> layers;
     std::vector<KVPlaneDesc> planes;
     int32_t* d_table = nullptr;           // null: host-only pool
@@ -185,6 +189,7 @@ struct kv_pool {
         pv.M = int32_t(geo.num_page_groups);
         pv.k_codec = k_codec;
         pv.v_codec = v_codec;
+        pv.scale16 = scale16;
         return pv;
     }
 };
@@ -194,11 +199,17 @@ extern "C" {
 const char* kv_last_error_message(void) { return g_last_error.c_str(); }
 
 kv_status kv_profile_planes(uint32_t profile, uint32_t head_dim, KVPlaneDesc* out, uint32_t* n_inout) {
+    return kv_profile_planes_ex(profile, head_dim, KV_DT_F32, out, n_inout);
+}
+
+kv_status kv_profile_planes_ex(uint32_t profile, uint32_t head_dim, uint32_t scale_dtype, KVPlaneDesc* out,
+                               uint32_t* n_inout) {
     if (!n_inout) return fail(KV_E_INVALID, "n_inout is null");
+    if (scale_dtype != KV_DT_F32 && scale_dtype != KV_DT_F16) return fail(KV_E_INVALID, "scale dtype is F32 or F16");
     int kc, vc;
     if (!profile_codecs(profile, &kc, &vc)) return fail(KV_E_INVALID, "unknown profile");
     SideSchema ks, vs;
-    if (head_dim == 0 || !side_schema(kc, head_dim, &ks) || !side_schema(vc, head_dim, &vs))
+    if (head_dim == 0 || !side_schema(kc, head_dim, &ks, scale_dtype) || !side_schema(vc, head_dim, &vs, scale_dtype))
         return fail(KV_E_GEOMETRY, "head_dim not divisible by the profile's groups");
     KVPlaneDesc tmp[4];
     uint32_t n = 0;
@@ -261,6 +272,7 @@ kv_status kv_pool_create(const KVPageGeometry* geo, const KVPlaneDesc* planes, u
         seen[k] = p;
     }
     int kc = -1, vc = -1;
+    int wide_dt = -1;                     // dtype of every INT8-G64 / FP8-row scale plane
     for (uint32_t l = 0; l < g.num_layers; ++l) {
         int codecs[2];
         for (int side = 0; side < 2; ++side) {
@@ -272,6 +284,11 @@ kv_status kv_pool_create(const KVPageGeometry* geo, const KVPlaneDesc* planes, u
             SideSchema ss;
             if (codec < 0 || !side_schema(codec, g.head_dim, &ss) || seen[c].x_extent != ss.code_x)
                 return fail(KV_E_INVALID, "plane inventory is not a closed profile");
+            if (codec == CODEC_INT8_G64 || codec == CODEC_FP8_ROW) {
+                if (wide_dt >= 0 && int(seen[s].dtype) != wide_dt)
+                    return fail(KV_E_INVALID, "the scale planes of one pool share one dtype");
+                wide_dt = int(seen[s].dtype);
+            }
             codecs[side] = codec;
         }
         if (l == 0) {
@@ -310,6 +327,7 @@ kv_status kv_pool_create(const KVPageGeometry* geo, const KVPlaneDesc* planes, u
     p->L = L;
     p->k_codec = kc;
     p->v_codec = vc;
+    p->scale16 = wide_dt == int(KV_DT_F16) ? 1 : 0;
     p->layers = std::move(layers);
     p->planes.assign(planes, planes + n_planes);
     p->d_table = d_block_tables;

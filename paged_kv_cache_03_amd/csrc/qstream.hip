@@ -47,12 +47,25 @@ namespace kvs {
 
 namespace {
 
-// bytes per page row (one key of one KV head) of a side's code and scale planes
-template <int C, int D>
+// bytes per page row (one key of one KV head) of a side's code and scale
+// planes; SB: bytes of an INT8-G64 / FP8-row scale (4: fp32, 2: binary16)
+template <int C, int D, int SB>
 struct QRow {
     static constexpr int code = C == CODEC_NVFP4_G16 ? D / 2 : D;
-    static constexpr int scale = C == CODEC_INT8_G64 ? 4 * (D / 64) : (C == CODEC_FP8_ROW ? 4 : D / 16);
+    static constexpr int scale = C == CODEC_INT8_G64 ? SB * (D / 64) : (C == CODEC_FP8_ROW ? SB : D / 16);
 };
+
+// scale f of a run of scales loaded into 16-byte registers: fp32 word f, or
+// binary16 half f widened exactly
+template <int SB, int N>
+__device__ __forceinline__ float scale_of(const u32x4 (&buf)[N], int f) {
+    if constexpr (SB == 4) {
+        return __uint_as_float(buf[f >> 2][f & 3]);
+    } else {
+        const uint32_t w = buf[f >> 3][(f >> 1) & 3];
+        return static_cast<float>(__builtin_bit_cast(_Float16, uint16_t((f & 1) ? (w >> 16) : (w & 0xFFFFu))));
+    }
+}
 
 // Blocks per compute unit: two (two waves per SIMD hide each other's
 // latencies; at most 256 registers per lane; three measured slower at
@@ -87,7 +100,7 @@ __device__ __forceinline__ f32x2_t fp8_pair(uint32_t w, int h) {
     return h ? __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w, 1.0f, true) : __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w, 1.0f, false);
 }
 
-template <int D, int KC, int VC>
+template <int D, int KC, int VC, int SB>
 __global__ void __launch_bounds__(256, (qstream_bpc<D, KC>())) paged_qstream_kernel(DecodeArgs a) {
     using namespace plan;
     constexpr int BPC = qstream_bpc<D, KC>();
@@ -100,16 +113,17 @@ __global__ void __launch_bounds__(256, (qstream_bpc<D, KC>())) paged_qstream_ker
     constexpr int QCHUNKS = 1024 / BPC;            // query cache: 16-byte chunks
     constexpr int QSEG = QCHUNKS / (NCOL * NCH);   // units with cached queries
     constexpr int PAGES = kStreamPages / BPC;      // most pages a block takes
-    constexpr int KROW = QRow<KC, D>::code, VROW = QRow<VC, D>::code;
-    constexpr int KSROW = QRow<KC, D>::scale, VSROW = QRow<VC, D>::scale;
+    constexpr int KROW = QRow<KC, D, SB>::code, VROW = QRow<VC, D, SB>::code;
+    constexpr int KSROW = QRow<KC, D, SB>::scale, VSROW = QRow<VC, D, SB>::scale;
     constexpr bool KI8 = KC == CODEC_INT8_G64, KF8 = KC == CODEC_FP8_ROW, KF4 = KC == CODEC_NVFP4_G16;
     constexpr bool VI8 = VC == CODEC_INT8_G64, VF8 = VC == CODEC_FP8_ROW;
     constexpr int NGK = KI8 ? NU : 1;              // score accumulators: one per K scale group
     constexpr int NPV = VI8 ? NU : 1;              // copies of P: one per V scale group
     constexpr int NKW = KF4 ? 2 : 4;               // K code words per group and lane
-    constexpr int NKS4 = KF4 ? (KSROW + 15) / 16 : (4 * KSROW) / 16;   // 16-byte K scale loads per lane
+    // K scale loads per lane: 16 bytes each (8 for a shorter run of four keys' scales)
+    constexpr int NKS4 = KF4 ? (KSROW + 15) / 16 : (4 * KSROW + 15) / 16;
     constexpr int NVW = VI8 ? NU : (VF8 ? NDT / 4 : NDT / 8);         // V code words per key and lane
-    constexpr int NVS4 = VI8 ? (4 * VSROW) / 16 : (VF8 ? 1 : 0);      // 16-byte V scale loads per lane
+    constexpr int NVS4 = (VI8 || VF8) ? (4 * VSROW + 15) / 16 : 0;   // V scale loads per lane, as for K
     static_assert(KC != CODEC_BF16 && VC != CODEC_BF16, "quantized sides only");
     static_assert(D == 64 || D == 128 || D == 256, "shape");
     static_assert(NVW >= 1 && NKS4 >= 1 && (VI8 || VF8 || NVS4 == 0), "register layout");
@@ -216,9 +230,14 @@ __global__ void __launch_bounds__(256, (qstream_bpc<D, KC>())) paged_qstream_ker
         const int rows = sl < 0 ? 0 : (pmeta[J] & 255);   // an unmapped block reads nothing
         const size_t s0 = size_t(sl < 0 ? 0 : sl) * 64;
         const __amdgpu_buffer_rsrc_t rkc = __builtin_amdgcn_make_buffer_rsrc(kcp + s0 * KROW, 0, rows * KROW, kBufferWord3);
-        const __amdgpu_buffer_rsrc_t rks = __builtin_amdgcn_make_buffer_rsrc(ksp + s0 * KSROW, 0, rows * KSROW, kBufferWord3);
+        // the range check of a buffer load works on whole dwords: 2-byte scale
+        // rows round their range up to one (the key past the last visible row
+        // that this lets through is zeroed where the scales are used)
+        const int ksr = SB == 2 && !KF4 ? (rows * KSROW + 3) & ~3 : rows * KSROW;
+        const int vsr = SB == 2 && (VI8 || VF8) ? (rows * VSROW + 3) & ~3 : rows * VSROW;
+        const __amdgpu_buffer_rsrc_t rks = __builtin_amdgcn_make_buffer_rsrc(ksp + s0 * KSROW, 0, ksr, kBufferWord3);
         const __amdgpu_buffer_rsrc_t rvc = __builtin_amdgcn_make_buffer_rsrc(vcp + s0 * VROW, 0, rows * VROW, kBufferWord3);
-        const __amdgpu_buffer_rsrc_t rvs = __builtin_amdgcn_make_buffer_rsrc(vsp + s0 * VSROW, 0, rows * VSROW, kBufferWord3);
+        const __amdgpu_buffer_rsrc_t rvs = __builtin_amdgcn_make_buffer_rsrc(vsp + s0 * VSROW, 0, vsr, kBufferWord3);
 #pragma unroll
         for (int g = 0; g < NU; ++g) {
             if constexpr (KF4) {
@@ -237,8 +256,11 @@ __global__ void __launch_bounds__(256, (qstream_bpc<D, KC>())) paged_qstream_ker
                 } else {
                     ksbuf[J][k] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rks, kq * KSROW + 16 * k, 0, kNonTemporal));
                 }
-            } else {
+            } else if constexpr (4 * KSROW >= 16) {
                 ksbuf[J][k] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rks, tk0 * KSROW + 16 * k, 0, kNonTemporal));
+            } else {
+                const u32x2 x = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rks, tk0 * KSROW, 0, kNonTemporal));
+                ksbuf[J][k] = u32x4{x[0], x[1], 0u, 0u};
             }
         }
 #pragma unroll
@@ -259,8 +281,14 @@ __global__ void __launch_bounds__(256, (qstream_bpc<D, KC>())) paged_qstream_ker
                 vsb[J][r] = __builtin_amdgcn_raw_buffer_load_b32(rvs, t * VSROW + (((NDT * li) / 16) & ~3), 0, kNonTemporal);
         }
 #pragma unroll
-        for (int k = 0; k < NVS4; ++k)
-            vsbuf[J][k] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rvs, tk0 * VSROW + 16 * k, 0, kNonTemporal));
+        for (int k = 0; k < NVS4; ++k) {
+            if constexpr (4 * VSROW >= 16) {
+                vsbuf[J][k] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rvs, tk0 * VSROW + 16 * k, 0, kNonTemporal));
+            } else {
+                const u32x2 x = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rvs, tk0 * VSROW, 0, kNonTemporal));
+                vsbuf[J][k] = u32x4{x[0], x[1], 0u, 0u};
+            }
+        }
     };
 
     // query rows of the first QSEG units (columns past a unit's last read
@@ -436,9 +464,10 @@ __global__ void __launch_bounds__(256, (qstream_bpc<D, KC>())) paged_qstream_ker
             sacc[ga] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, op1), qb[2 * g + 1], sacc[ga], 0, 0, 0);
         }
         // K scales of key tk(r): float r*NU + g (INT8) or r (FP8) of the loaded run
+        // (2-byte scales: a key at or past the page's last visible row counts 0)
         auto kscale = [&](int r, int g) __attribute__((always_inline)) {
-            const int f = KI8 ? r * NU + g : r;
-            return __uint_as_float(ksbuf[J][f >> 2][f & 3]);
+            const float sc = scale_of<SB>(ksbuf[J], KI8 ? r * NU + g : r);
+            return SB == 2 && tk0 + r >= lim ? 0.f : sc;
         };
         float sj[4];
 #pragma unroll
@@ -480,8 +509,8 @@ __global__ void __launch_bounds__(256, (qstream_bpc<D, KC>())) paged_qstream_ker
         // P^T operands [P_hi; P_lo], one per V scale group (keys past the
         // last limit have zero codes and scales from the buffer range)
         auto vscale = [&](int r, int g) __attribute__((always_inline)) {
-            const int f = VI8 ? r * NU + g : r;
-            return __uint_as_float(vsbuf[J][f >> 2][f & 3]);
+            const float sc = scale_of<SB>(vsbuf[J], VI8 ? r * NU + g : r);
+            return SB == 2 && tk0 + r >= lim ? 0.f : sc;
         };
         bf16x8_t bop[NPV];
 #pragma unroll
@@ -559,7 +588,15 @@ __global__ void __launch_bounds__(256, (qstream_bpc<D, KC>())) paged_qstream_ker
 
 template <int D, int KC, int VC>
 hipError_t launch_one(const DecodeArgs& a, int gq, hipStream_t s) {
-    paged_qstream_kernel<D, KC, VC><<<dim3(static_cast<unsigned>(a.G)), 256, 0, s>>>(a);
+    constexpr bool wide = KC == CODEC_INT8_G64 || KC == CODEC_FP8_ROW || VC == CODEC_INT8_G64 || VC == CODEC_FP8_ROW;
+    bool launched = false;
+    if constexpr (wide) {
+        if (a.pv.scale16) {
+            paged_qstream_kernel<D, KC, VC, 2><<<dim3(static_cast<unsigned>(a.G)), 256, 0, s>>>(a);
+            launched = true;
+        }
+    }
+    if (!launched) paged_qstream_kernel<D, KC, VC, 4><<<dim3(static_cast<unsigned>(a.G)), 256, 0, s>>>(a);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     DecodeArgs c = a;

@@ -12,7 +12,8 @@ import torch
 from . import _abi as abi
 
 _PLANE_TORCH = {abi.KV_DT_BF16: torch.int16, abi.KV_DT_I8: torch.int8, abi.KV_DT_E4M3FN: torch.uint8,
-                abi.KV_DT_E2M1X2: torch.uint8, abi.KV_DT_F32: torch.float32, abi.KV_DT_U8_E4M3: torch.uint8}
+                abi.KV_DT_E2M1X2: torch.uint8, abi.KV_DT_F32: torch.float32, abi.KV_DT_U8_E4M3: torch.uint8,
+                abi.KV_DT_F16: torch.int16}
 ROLE_NAMES = {abi.KV_ROLE_K_CODE: "K_CODE", abi.KV_ROLE_K_SCALE: "K_SCALE", abi.KV_ROLE_V_CODE: "V_CODE",
               abi.KV_ROLE_V_SCALE: "V_SCALE"}
 
@@ -33,12 +34,14 @@ class DevicePool:
     """Planes [M][H][64][X] per layer and role, the block table [C][L], and the pool handle."""
 
     def __init__(self, profile: str, H: int, D: int, layers: int, S: int, C: int, M: int, free_order=None,
-                 host_only: bool = False, zero: bool = True, device: str = "cuda"):
+                 host_only: bool = False, zero: bool = True, device: str = "cuda", scale_bytes: int = 4):
+        """scale_bytes: 4 (fp32) or 2 (binary16) INT8-G64 / FP8-row scale planes."""
         self.profile, self.H, self.D, self.layers, self.S, self.C, self.M = profile, H, D, layers, S, C, M
         self.L = -(-S // 64)
         self.host_only = host_only
         self.device = None if host_only else torch.device(device)
-        schema = abi.kv_profile_planes(abi.KV_PROFILE[profile], D)
+        schema = abi.kv_profile_planes(abi.KV_PROFILE[profile], D,
+                                       abi.KV_DT_F16 if scale_bytes == 2 else abi.KV_DT_F32)
         self.geo = abi.KVPageGeometry(64, H, D, layers, S, C, M)
         self.planes: list[dict] = []
         descs = []

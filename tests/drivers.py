@@ -25,7 +25,7 @@ def say(msg: str) -> None:
 def build_oracle(wl, free_order=None, privatize=False, layers=None):
     layers = range(wl.layers) if layers is None else layers
     pool = OraclePool(wl.S, wl.C, wl.M, free_order=wl.free_order if free_order is None else free_order)
-    st = OracleStore(pool, wl.profile, wl.H, wl.D, wl.layers)
+    st = OracleStore(pool, wl.profile, wl.H, wl.D, wl.layers, scale_bytes=wl.scale_bytes)
     sids = {}
     for b in wl.order():
         row = wl.table_rows[b]

@@ -296,3 +296,32 @@ def test_replica_calls_refuse_host_only_pool():
         assert e.value.status == abi.KV_E_INVALID
     assert abi.kv_pool_stats(h) == (0, 0, 16)
     abi.kv_pool_destroy(h)
+
+
+@pytest.mark.parametrize("profile,D,want", [("INT8_G64", 256, 528), ("FP8_E4M3FN_ROW256", 256, 516),
+                                            ("K8V4", 256, 402), ("NVFP4_G16", 256, 288), ("BF16", 256, 1024)])
+def test_two_byte_scale_schema_reproduces_the_d256_table(profile, D, want):
+    planes = abi.kv_profile_planes(abi.KV_PROFILE[profile], D, abi.KV_DT_F16)
+    assert sum(p.x_extent * p.elem_bytes for p in planes) == want
+    for p in planes:
+        if p.role in (abi.KV_ROLE_K_SCALE, abi.KV_ROLE_V_SCALE) and p.dtype != abi.KV_DT_U8_E4M3:
+            assert p.dtype == abi.KV_DT_F16 and p.elem_bytes == 2
+    # the pool takes it, and its replica page is the table's bytes x 64 rows x H x layers
+    geo = abi.KVPageGeometry(64, 2, D, 1, 1024, 2, 16)
+    h = abi.kv_pool_create(geo, planes, None)
+    assert abi.kv_replica_page_bytes(h) == want * 64 * 2
+    abi.kv_pool_destroy(h)
+
+
+def test_scale_planes_of_one_pool_share_a_dtype():
+    a = abi.kv_profile_planes(abi.KV_PROFILE["INT8_G64"], 128, abi.KV_DT_F16)
+    b = abi.kv_profile_planes(abi.KV_PROFILE["INT8_G64"], 128)
+    for p in b:
+        p.layer = 1
+    geo = abi.KVPageGeometry(64, 2, 128, 2, 1024, 2, 16)
+    with pytest.raises(abi.KVError) as e:
+        abi.kv_pool_create(geo, list(a) + list(b), None)
+    assert e.value.status == abi.KV_E_INVALID
+    with pytest.raises(abi.KVError) as e:
+        abi.kv_profile_planes(abi.KV_PROFILE["INT8_G64"], 128, abi.KV_DT_BF16)
+    assert e.value.status == abi.KV_E_INVALID

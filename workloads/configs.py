@@ -48,6 +48,7 @@ class Workload:
     mode: str = "decode"            # "decode" or "verify"
     outlier_frac: float = 0.0
     scale_mul: float = 1.0          # softmax scale = scale_mul / sqrt(D) (> 1: peaked distributions)
+    scale_bytes: int = 4            # INT8-G64 / FP8-row scale planes: 4 (fp32) or 2 (binary16)
     table_rows: list = field(default_factory=list)
     free_order: np.ndarray | None = None
 
@@ -227,7 +228,7 @@ def get(k: int) -> Workload:
 def small(seed: int, profile: str = "BF16", *, B: int = 3, C: int = 4, Hq: int = 8, H: int = 2,
           D: int = 128, S: int = 1024, layers: int = 1, mode: str = "decode", hist=None, step=None,
           fork=None, cow=None, outlier_frac: float = 0.0, M: int | None = None,
-          scale_mul: float = 1.0) -> Workload:
+          scale_mul: float = 1.0, scale_bytes: int = 4) -> Workload:
     """A randomized small case (several pages, ragged tails) the oracle finishes in seconds."""
     r = rng_for(5000 + seed, 9)
     if hist is None:
@@ -240,4 +241,4 @@ def small(seed: int, profile: str = "BF16", *, B: int = 3, C: int = 4, Hq: int =
     L = -(-S // 64)
     return Workload(f"small{seed}_{profile}", profile, C=C, S=S, M=M or C * L, layers=layers, Hq=Hq, H=H,
                     D=D, seed=5000 + seed, hist=list(hist), step=list(step), fork=list(fork), cow=list(cow),
-                    mode=mode, outlier_frac=outlier_frac, scale_mul=scale_mul)
+                    mode=mode, outlier_frac=outlier_frac, scale_mul=scale_mul, scale_bytes=scale_bytes)

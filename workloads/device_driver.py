@@ -36,7 +36,8 @@ def build_device(wl, free_order=None, privatize=False, layers=None, zero=True, h
 
     layers = list(range(wl.layers)) if layers is None else list(layers)
     dp = DevicePool(wl.profile, wl.H, wl.D, wl.layers, wl.S, wl.C, wl.M,
-                    free_order=wl.free_order if free_order is None else free_order, zero=zero)
+                    free_order=wl.free_order if free_order is None else free_order, zero=zero,
+                    scale_bytes=wl.scale_bytes)
     dev = dp.device
     if fill is not None:
         for planes in dp.planes:
