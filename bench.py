@@ -97,7 +97,9 @@ def decode_kernel_name(wl) -> str:
         sides = {"INT8_G64": (1, 1), "FP8_E4M3FN_ROW256": (2, 2), "NVFP4_G16": (3, 3), "K8V4": (2, 3)}
         if wl.profile in sides and (wl.D in (128, 256) or (wl.D == 64 and 3 not in sides[wl.profile])):
             kc, vc = sides[wl.profile]
-            return f"paged_qstream_kernel<{wl.D}, {kc}, {vc}>"
+            # last argument: bytes of an INT8-G64 / FP8-row scale
+            sb = 2 if wl.scale_bytes == 2 and wl.profile != "NVFP4_G16" else 4
+            return f"paged_qstream_kernel<{wl.D}, {kc}, {vc}, {sb}>"
     return "decode_split_kernel + decode_combine_kernel"
 
 
