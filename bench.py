@@ -469,6 +469,97 @@ def bench_replica(wl, args) -> int:
     return 0 if same else 1
 
 
+def bench_advance(wl, args) -> int:
+    """Advancing decode: K steps in which every entry's frontier moves by one
+    token.  Per step, on the host: commit the previous token and map the next
+    one (a new page group at each page crossing, published on the stream);
+    then the device step as in the default run -- the plan of the new batch
+    state and, per layer, the append of the new rows with the decode.  The
+    rows and queries are those of the workload's step (their values do not
+    change the work).  Reports the step rate next to the host time per step."""
+    import numpy as np
+    import torch
+    from paged_kv_cache_03_amd.device_pool import i32
+    from workloads.device_driver import _dev, build_device
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    if any(t != 1 for t in wl.step):
+        raise SystemExit("--advance takes a workload with one new token per entry")
+    t0 = time.time()
+    log(f"workload {wl.name}: filling {wl.layers} layer(s) of history")
+    dp, seqs, step_inputs = build_device(wl, zero=False)
+    log(f"history resident after {time.time() - t0:.1f} s")
+    steps = max(1, min(args.steps, 64))
+    warm = min(args.warmup, 5)
+    lens = list(wl.seq_lens)
+    if max(lens) + warm + steps > wl.S:
+        raise SystemExit("the advancing run would pass the maximum context")
+    bound = max(lens) + warm + steps               # grid bound for every step of the run
+    rows_t = i32(wl.table_rows, dev)
+    # per step, pinned host rows of (lengths, append positions) copied in stream order
+    lp_host = torch.empty((warm + steps, 2, wl.B), dtype=torch.int32, pin_memory=True)
+    lp_dev = torch.empty((warm + steps, 2, wl.B), dtype=torch.int32, device=dev)
+    cu_t = i32(list(range(wl.B + 1)), dev)
+    qs = [_dev(wl.q(layer), dev) for layer in range(wl.layers)]
+    out = torch.empty((wl.B, wl.Hq, wl.D), dtype=torch.float32, device=dev)
+    ws = dp.workspace(wl.B, wl.Hq, bound)
+    fused = wl.profile == "BF16" and wl.D in (64, 128)
+    host_s = [0.0]
+    crossings = [0]
+
+    def step(k):
+        h0 = time.perf_counter()
+        for b in range(wl.B):
+            dp.commit(seqs[b], lens[b])            # the previous step's token is committed
+            lens[b] += 1
+            if lens[b] % 64 == 1:
+                crossings[0] += 1
+            dp.ensure_mapped(seqs[b], lens[b])     # a new group only at a page crossing
+        lp_host[k] = torch.tensor([lens, [n - 1 for n in lens]], dtype=torch.int32)
+        host_s[0] += time.perf_counter() - h0
+        lp_dev[k].copy_(lp_host[k], non_blocking=True)
+        lens_k, pos_k = lp_dev[k, 0], lp_dev[k, 1]
+        dp.decode_plan(wl.Hq, rows_t, lens_k, bound, ws)
+        for layer in range(wl.layers):
+            kd, vd = step_inputs[layer]
+            if fused:
+                dp.decode_append_run(layer, wl.B, wl.Hq, bound, kd, vd, qs[layer], wl.sm_scale, out, ws)
+            else:
+                dp.append(layer, rows_t, pos_k, cu_t, wl.B, kd, vd)
+                dp.decode_run(layer, wl.B, wl.Hq, bound, qs[layer], wl.sm_scale, out, ws)
+
+    for k in range(warm):
+        step(k)
+    torch.cuda.synchronize()
+    host_s[0], crossings[0] = 0.0, 0
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for k in range(warm, warm + steps):
+        step(k)
+    end.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / steps
+    table = dp.table.cpu().numpy()
+    unique, _ = kv_read_bytes(table, wl)          # the histories at the start: within steps/ctx of every step's
+    bpth = bytes_per_token_head(wl.profile, wl.D, wl.scale_bytes)
+    per_step = wl.layers * (unique + wl.B * wl.Hq * wl.D * 6 + wl.B * wl.H * (bpth + 4 * wl.D))
+    line = {
+        "metric": METRIC + " (advancing: frontiers grow every step)", "value": round(per_step / (ms * 1e-3) / 1e9, 2),
+        "unit": "GB/s", "n_gpus": 1, "steps": steps, "warmup": warm, "ms_per_step": round(ms, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16" if wl.profile == "BF16" else wl.profile.lower(), "data": "synthetic",
+        "config": {"workload": wl.name + "_advancing", "profile": wl.profile, "batch": wl.B, "layers": wl.layers,
+                   "ctx_sum_start": int(sum(wl.seq_lens)), "page_crossings": crossings[0]},
+        "steps_per_s": round(1000.0 / ms, 2),
+        "host_us_per_step": round(host_s[0] / steps * 1e6, 1),
+        "roofline": None, "cpu_baseline": None,
+    }
+    print(json.dumps(line), flush=True)
+    dp.close()
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -480,6 +571,8 @@ def main() -> int:
                     help="INT8-G64 / FP8-row scale planes: 4 (fp32) or 2 (binary16, the page's D256 byte table)")
     ap.add_argument("--graph", action="store_true",
                     help="decode configs: time replays of the step captured as one HIP graph")
+    ap.add_argument("--advance", action="store_true",
+                    help="decode configs with one token per entry: frontiers grow every step (host mapping timed in)")
     ap.add_argument("--replica", action="store_true",
                     help="decode configs: offload / restore of the longest entry's pages (host replica)")
     ap.add_argument("--spec", action="store_true",
@@ -515,6 +608,8 @@ def main() -> int:
         return bench_verify(wl, args)
     if args.replica:
         return bench_replica(wl, args)
+    if args.advance:
+        return bench_advance(wl, args)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     t0 = time.time()
