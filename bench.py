@@ -198,6 +198,53 @@ def cpu_baseline(wl, seconds_hint: float = 20.0) -> dict:
                       f"heads, {reps} rep(s), {per_layer:.2f} s per layer (KV bytes read / time)"}
 
 
+def cpu_baseline_verify(wl, seconds_hint: float = 20.0) -> dict:
+    """The oracle, as it stands, on a bounded sample of the verify workload: the
+    first entry with a short chunk (a speculative verify, T = 5) over its whole
+    history, layer 0.  Reported as TFLOP/s of the same algorithmic work."""
+    import numpy as np
+    from oracle import attention as A
+    from oracle.pool import OraclePool
+    from oracle.store import OracleStore
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = 1
+    sample = [b for b in range(wl.B) if wl.step[b] <= 8 and wl.fork[b] is None][:1]
+    log(f"cpu baseline: the oracle's pool for entries {sample}")
+    pool = OraclePool(wl.S, wl.C, wl.M, free_order=wl.free_order)
+    st = OracleStore(pool, wl.profile, wl.H, wl.D, 1, scale_bytes=wl.scale_bytes)
+    for b in sample:
+        row = wl.table_rows[b]
+        sid = pool.open(row)
+        pool.ensure_mapped(sid, wl.hist[b] + wl.step[b])
+        k, v = wl.hist_kv(0, b)
+        st.append(0, row, 0, k, v)
+        pool.commit(sid, wl.hist[b])
+        st.append(0, row, wl.hist[b], *wl.step_kv(0, b))
+    q_all = wl.q(0)
+    rows = [wl.table_rows[b] for b in sample]
+    n0s = [wl.hist[b] for b in sample]
+    cu = [0]
+    for b in sample:
+        cu.append(cu[-1] + wl.step[b])
+    q = np.concatenate([q_all[wl.cu_q[b]:wl.cu_q[b + 1]] for b in sample])
+    log("cpu baseline: timing the oracle")
+    reps, elapsed = 0, 0.0
+    while reps == 0 or (elapsed < seconds_hint * 0.5 and reps < 3):
+        t0 = time.perf_counter()
+        A.paged_verify(st, 0, rows, n0s, cu, q, wl.sm_scale)
+        elapsed += time.perf_counter() - t0
+        reps += 1
+    pairs = sum(n0 * T + T * (T + 1) // 2 for n0, T in ((wl.hist[b], wl.step[b]) for b in sample))
+    flops = 4.0 * wl.D * wl.Hq * pairs
+    per = elapsed / reps
+    return {"value": round(flops / per / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"layer 0: one verify chunk of {wl.step[sample[0]]} tokens over its {n0s[0]}-token history, "
+                      f"all {wl.Hq} heads, {reps} rep(s), {per:.2f} s each"}
+
+
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 
 
@@ -279,7 +326,7 @@ def bench_verify(wl, args) -> int:
                      "traffic": measured_traffic(wl, "verify"), "flops_per_launch": flops,
                      "kv_bytes_per_launch": kv_bytes,
                      "launch_ms": round(ver_ms, 5)},
-        "cpu_baseline": None,
+        "cpu_baseline": None if args.no_cpu_baseline else cpu_baseline_verify(wl),
     }
     print(json.dumps(line), flush=True)
     dp.close()
