@@ -628,7 +628,7 @@ def main() -> int:
                     help="only run a 1 GiB device copy (counter calibration under rocprofv3 --pmc)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("this build runs on one GPU only: --gpus must be 1 (the path's sharding is described in DESIGN.md)",
+        print("one GPU only: --gpus must be 1 (the path runs on one GPU's share; no collectives)",
               file=sys.stderr)
         return 2
 

@@ -48,7 +48,7 @@ typedef int32_t kv_status;
                                 copy the tail first (kv_cow_tail_page) */
 #define KV_E_UNMAPPED     6  /* commit beyond the mapped pages */
 #define KV_E_DEVICE       7  /* a HIP runtime call failed */
-#define KV_E_UNSUPPORTED  8  /* valid request this build has no kernel for */
+#define KV_E_UNSUPPORTED  8  /* valid request this library has no kernel for */
 
 /* ------------------------------------------------ closed profiles / planes */
 /* Closed KV profiles (Paged KV Context Store page, closed-profile paragraph).
@@ -383,7 +383,7 @@ kv_status paged_attn_decode_append_run(const kv_pool* pool, uint32_t layer, uint
  *   d_ws / ws_bytes : >= paged_attn_workspace_bytes(pool, B, Hq, max_seq_len,
  *   max_q_len).
  * KV_E_INVALID unless sm_scale is finite and > 0.  Profiles: BF16 only in
- * this build (KV_E_UNSUPPORTED otherwise). */
+ * this library (KV_E_UNSUPPORTED otherwise). */
 kv_status paged_attn_verify(const kv_pool* pool, uint32_t layer, uint32_t B, uint32_t Hq,
                             const int32_t* d_table_rows, const int32_t* d_q_pos0, const int32_t* d_cu_q,
                             uint32_t total_q, uint32_t max_q_len, uint32_t max_seq_len, const void* d_q,

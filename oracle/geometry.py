@@ -70,7 +70,7 @@ def explicit_capacity(k_main_tokens: int, S: int, C: int) -> int:
 
 def check_geometry(*, page_size: int, S: int, C: int, M: int, H: int, D: int,
                    Hq: int | None = None, profile: str = "BF16") -> None:
-    """Raise ValueError for geometry the pages rule out (or this build does not take)."""
+    """Raise ValueError for geometry the pages rule out (or this library does not take)."""
     if page_size != P:
         raise ValueError("page size must be 64")
     if not 1 <= C <= 8:

@@ -25,7 +25,7 @@ Source: NInfer "Paged KV Context Store" maintainer page --
     in the valid domain and are overwritten by the next canonical write;
   * the active reservation (growth entitlement) is released at finish.
 
-The free-list discipline is this build's reading (the pages leave it open and
+The free-list discipline is this library's reading (the pages leave it open and
 say correctness must not depend on it): pages are taken from the front of a
 FIFO seeded with a caller-given order of [0, M), and freed pages are appended
 at its back in logical-block order.  A reservation is a FIFO of concrete page
