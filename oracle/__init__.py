@@ -21,9 +21,9 @@ headings were lost in extraction, so passages are named by what they hold):
   (F=1000), writer-cardinality rules, finish/release rules.
 * ``codecs``    -- the closed KV profiles' quantize/dequantize.  Same page:
   the closed-profile paragraph and X-extent list.  The exact rounding rules
-  live in a header the pages do not contain; the reading used here (fp32
-  arithmetic, round-half-even, saturating FP8/FP4, fp32 scales) is listed in
-  the design doc with every other reading.
+  live in a header the pages do not contain; the reading used here is fp32
+  arithmetic, round-half-even, saturating FP8/FP4, and fp32 or binary16
+  INT8-G64 / FP8-row scales (the module docstring states each rule).
 * ``store``     -- plane storage written and read through the block table.
 * ``attention`` -- dense causal GQA softmax attention in fp64 over the
   logically gathered (dequantized) K/V: the plain definition of what the

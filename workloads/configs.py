@@ -1,7 +1,6 @@
 """Workload shapes: the five named configurations and small randomized cases.
 
-Readings taken where the configuration text leaves a choice open (each is
-listed in the design doc):
+Readings taken where the workload descriptions leave a choice open:
 * tiny decode: S is not given; C=1 with M=16 forces L=16, so S=1024.  The
   300-token history is 4 full pages plus 44 columns; the step appends token 300.
 * 8-sequence decode (BF16 and INT8-G64): sequences 0-3 share the 4096-token
