@@ -76,6 +76,12 @@ typedef int32_t kv_status;
 #define KV_ROLE_V_CODE  2
 #define KV_ROLE_V_SCALE 3
 
+/* Plane orders (PagedKVStorageLayout passage: the closed physical orders and
+ * the address-translation equations; head-major swaps the head and
+ * page-group terms).  Every plane of one pool takes the same order. */
+#define KV_LAYOUT_PAGE_MAJOR 0   /* [X, P, H, N]: C-order [M][H][64][X] */
+#define KV_LAYOUT_HEAD_MAJOR 1   /* [X, P, N, H]: C-order [H][M][64][X] (the Draft Full order) */
+
 /* Expanded pool geometry (capacity-geometry equations):
  *   L = ceil(max_context / page_size), valid M in [max(L, C), C * L]. */
 typedef struct KVPageGeometry {
@@ -88,11 +94,17 @@ typedef struct KVPageGeometry {
     uint32_t num_page_groups;  /* M */
 } KVPageGeometry;
 
-/* One plane of the page-major closed order [X, P, H, N] (first extent
- * fastest), i.e. C-order [M][H][64][X]; element (x, o, h, g) lives at
- * base + elem_bytes * (x + X * (o + 64 * (h + H * g)))  (address-translation
- * equations with contiguous strides).  base is caller-owned device memory of
- * M * H * 64 * X * elem_bytes bytes, 256-byte aligned. */
+/* One plane in a closed order (first extent fastest) with contiguous
+ * strides (address-translation equations); element (x, o, h, g) lives at
+ *   page-major [X, P, H, N], C-order [M][H][64][X]:
+ *     base + elem_bytes * (x + X * (o + 64 * (h + H * g)))
+ *   head-major [X, P, N, H], C-order [H][M][64][X]:
+ *     base + elem_bytes * (x + X * (o + 64 * (g + M * h)))
+ * base is caller-owned device memory of M * H * 64 * X * elem_bytes bytes,
+ * 256-byte aligned.  layout is KV_LAYOUT_PAGE_MAJOR (0, what
+ * kv_profile_planes writes) or KV_LAYOUT_HEAD_MAJOR; every plane of a pool
+ * takes the same one (KV_E_INVALID otherwise).  Results of every call are
+ * the same in either order; only the addresses differ. */
 typedef struct KVPlaneDesc {
     uint32_t layer;
     uint32_t role;       /* KV_ROLE_* */
@@ -100,7 +112,7 @@ typedef struct KVPlaneDesc {
     uint32_t x_extent;   /* X: D for codes, D/2 packed FP4, D/64 INT8 scales, 1 FP8 row
                             scale, D/16 NVFP4 scales (X-extent list) */
     uint32_t elem_bytes; /* bytes per element of dtype */
-    uint32_t reserved;
+    uint32_t layout;     /* KV_LAYOUT_* */
     void*    base;       /* device pointer, caller-owned */
 } KVPlaneDesc;
 

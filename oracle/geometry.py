@@ -151,6 +151,17 @@ def element_index(d: int, o: int, h: int, g: int, X: int, H: int) -> int:
     return d * nb0 + o * nb1 + h * nb2 + g * nb3
 
 
+def element_index_head_major(d: int, o: int, h: int, g: int, X: int, M: int) -> int:
+    """Element offset of (d, o, h, g) in a head-major plane [X, P, N, H].
+
+    The head-major order swaps the head and page-group terms of the page-major
+    equation: with contiguous strides nb0 = 1, nb1 = X, nb2 = X*P (the page
+    group) and nb3 = X*P*M (the head).
+    """
+    nb0, nb1, nb2, nb3 = 1, X, X * P, X * P * M
+    return d * nb0 + o * nb1 + g * nb2 + h * nb3
+
+
 def translate(position: int, block_table_row) -> tuple[int, int, int]:
     """(b, o, g) for a logical position: b = floor(p/P), o = p mod P, g = table[b]."""
     b, o = divmod(position, P)

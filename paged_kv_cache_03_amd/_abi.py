@@ -22,6 +22,7 @@ STATUS_NAMES = {0: "OK", 1: "INVALID", 2: "GEOMETRY", 3: "CAPACITY", 4: "STALE",
 KV_PROFILE = {"BF16": 0, "INT8_G64": 1, "FP8_E4M3FN_ROW256": 2, "NVFP4_G16": 3, "K8V4": 4}
 KV_DT_BF16, KV_DT_I8, KV_DT_E4M3FN, KV_DT_E2M1X2, KV_DT_F32, KV_DT_U8_E4M3, KV_DT_F16 = range(7)
 KV_ROLE_K_CODE, KV_ROLE_K_SCALE, KV_ROLE_V_CODE, KV_ROLE_V_SCALE = range(4)
+KV_LAYOUT_PAGE_MAJOR, KV_LAYOUT_HEAD_MAJOR = range(2)
 
 # exported symbols, in header order (the CPU test checks the header declares exactly these)
 EXPORTS = ["kv_profile_planes", "kv_profile_planes_ex", "kv_plane_bytes", "kv_pool_create", "kv_pool_destroy", "kv_pool_stats",
@@ -44,7 +45,7 @@ class KVPageGeometry(ctypes.Structure):
 
 class KVPlaneDesc(ctypes.Structure):
     _fields_ = [("layer", ctypes.c_uint32), ("role", ctypes.c_uint32), ("dtype", ctypes.c_uint32),
-                ("x_extent", ctypes.c_uint32), ("elem_bytes", ctypes.c_uint32), ("reserved", ctypes.c_uint32),
+                ("x_extent", ctypes.c_uint32), ("elem_bytes", ctypes.c_uint32), ("layout", ctypes.c_uint32),
                 ("base", ctypes.c_void_p)]
 
 

@@ -148,7 +148,7 @@ __global__ void __launch_bounds__(256) append_kernel(AppendArgs a) {
     if (blk >= a.pv.L) return;
     const int g = a.pv.table[size_t(row) * a.pv.L + blk];
     if (g < 0 || g >= a.pv.M) return;                      // unmapped: caller guarantee broken, skip
-    const size_t slot = (size_t(g) * H + h) * kPage + o;   // row index of (g, h, o) in every plane
+    const size_t slot = (size_t(g) * a.pv.sg + size_t(h) * a.pv.sh) * kPage + o;   // row of (g, h, o) in every plane
     write_side<D, KC, SB>(a.pv.lv.k_code, a.pv.lv.k_scale, slot, a.k + size_t(r) * D, lane);
     write_side<D, VC, SB>(a.pv.lv.v_code, a.pv.lv.v_scale, slot, a.v + size_t(r) * D, lane);
 }

@@ -75,7 +75,7 @@ __global__ void __launch_bounds__(256) decode_split_kernel(DecodeArgs a) {
     for (int pg = p0; pg < p1; ++pg) {
         const int g = trow[pg];
         if (g < 0 || g >= a.pv.M) continue;       // unmapped block: caller guarantee broken, read nothing
-        const size_t slab = (size_t(g) * H + h) * kPage;
+        const size_t slab = (size_t(g) * a.pv.sg + size_t(h) * a.pv.sh) * kPage;
         const int tok = pg * kPage + lane;
         const bool valid = tok < ctx;
         float s[GQ];
@@ -193,7 +193,7 @@ __global__ void __launch_bounds__(256, 2) paged_vstream_kernel(DecodeArgs a) {
     static_assert(PAGES % NT == 0, "page list");
     typedef unsigned int vrow_t __attribute__((ext_vector_type(VW)));
 
-    __shared__ int2 pinfo[PAGES];                  // the block's pages: (slice g*H + h or -1, meta)
+    __shared__ int2 pinfo[PAGES];                  // the block's pages: (slice number of (g, h) or -1, meta)
     __shared__ u32x4 qcache[QCHUNKS];              // query rows of the first QSEG units: [unit][column][chunk]
     __shared__ float mbuf[4 * 16 * 64];            // unit merge: four waves x four tiles x 4 registers
     __shared__ float mlbuf[4][16][2];              // per-wave (m, l) of every column at a unit's end

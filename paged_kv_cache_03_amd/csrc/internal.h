@@ -38,6 +38,11 @@ struct PoolView {
     int32_t k_codec;
     int32_t v_codec;
     int32_t scale16;        // 1: INT8-G64 / FP8-row scale planes hold binary16 (2 bytes), else fp32
+    // slice (g, h) of every plane -- its 64 rows of X elements -- is slice
+    // number g * sg + h * sh: page-major [X, P, H, N] (sg, sh) = (H, 1),
+    // head-major [X, P, N, H] (1, M)
+    int32_t sg;
+    int32_t sh;
 };
 
 // Launchers (defined in the .hip files).  Each returns hipSuccess or the
@@ -49,20 +54,21 @@ struct CopyPlane {
     void* base;
     uint32_t row_bytes;   // X * elem_bytes (multiple of 4)
 };
-hipError_t launch_cow_copy(const CopyPlane* planes, int n_planes, int H, int src_g, int dst_g, int cols,
-                           hipStream_t s);
+hipError_t launch_cow_copy(const CopyPlane* planes, int n_planes, int H, int sg, int sh, int src_g, int dst_g,
+                           int cols, hipStream_t s);
 
 // Host replica copy (logical-order packed layout): page i of the replica is
-// pages[i], each plane's [H][64][X] slice at host + i * page_bytes +
-// plane.host_off.  to_host: device pages -> host; else host -> device pages.
-// `host` is the device-visible address of pinned host memory.
+// pages[i], each plane's [H][64][X] image at host + i * page_bytes +
+// plane.host_off, whatever the device layout (slice (g, h) of a plane at
+// slice number g * sg + h * sh).  to_host: device pages -> host; else host ->
+// device pages.  `host` is the device-visible address of pinned host memory.
 struct ReplicaPlane {
-    void* base;          // device plane [M][H][64][X]
-    uint32_t slice_bytes;  // H * 64 * X * elem_bytes, a multiple of 16
-    uint64_t host_off;   // offset of this plane's slice inside a replica page
+    void* base;          // device plane
+    uint32_t head_bytes; // 64 * X * elem_bytes, a multiple of 16: one (group, head) slice
+    uint64_t host_off;   // offset of this plane's image inside a replica page
 };
 hipError_t launch_replica_copy(const ReplicaPlane* planes, int n_planes, const int32_t* pages, int n_pages,
-                               uint64_t page_bytes, char* host, bool to_host, hipStream_t s);
+                               uint64_t page_bytes, int H, int sg, int sh, char* host, bool to_host, hipStream_t s);
 
 hipError_t launch_append(const PoolView& pv, int B, const int32_t* table_rows, const int32_t* pos0,
                          const int32_t* cu_tokens, int total_tokens, const void* k, const void* v,

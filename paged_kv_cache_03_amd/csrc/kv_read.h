@@ -1,9 +1,10 @@
-// kv_read.h -- dequantizing readers of page-major plane rows.
+// kv_read.h -- dequantizing readers of plane rows.
 //
 // A plane row is the X elements of one (page group g, KV head h, column o),
-// at row index slot = (g * H + h) * 64 + o of every plane of the layer (page
-// group diagram: one id selects slice g of every grouped plane; page-major
-// order [X, P, H, N]).  Dequantization is value(code) * scale as one fp32
+// at row index slot = (g * sg + h * sh) * 64 + o of every plane of the layer
+// (page group diagram: one id selects slice g of every grouped plane;
+// page-major order [X, P, H, N] has (sg, sh) = (H, 1), head-major [X, P, N, H]
+// (1, M)).  Dequantization is value(code) * scale as one fp32
 // multiply, the same value the persistent codec defines.
 #pragma once
 

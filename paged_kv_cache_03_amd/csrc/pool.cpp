@@ -112,6 +112,7 @@ struct kv_pool {
     uint32_t L = 0;
     int k_codec = 0, v_codec = 0;
     int scale16 = 0;                      // INT8-G64 / FP8-row scale planes are binary16
+    int32_t sg = 1, sh = 1;               // slice number of (g, h) in every plane: g * sg + h * sh
     std::vector<LayerView> layers;
     std::vector<KVPlaneDesc> planes;
     int32_t* d_table = nullptr;           // null: host-only pool
@@ -190,6 +191,8 @@ struct kv_pool {
         pv.k_codec = k_codec;
         pv.v_codec = v_codec;
         pv.scale16 = scale16;
+        pv.sg = sg;
+        pv.sh = sh;
         return pv;
     }
 };
@@ -259,6 +262,7 @@ kv_status kv_pool_create(const KVPageGeometry* geo, const KVPlaneDesc* planes, u
     std::vector<LayerView> layers(g.num_layers, LayerView{nullptr, nullptr, nullptr, nullptr});
     std::vector<KVPlaneDesc> seen(size_t(g.num_layers) * 4);
     std::vector<uint8_t> have(size_t(g.num_layers) * 4, 0);
+    int layout = -1;
     for (uint32_t i = 0; i < n_planes; ++i) {
         const KVPlaneDesc& p = planes[i];
         if (p.layer >= g.num_layers || p.role > 3) return fail(KV_E_INVALID, "plane layer/role out of range");
@@ -268,6 +272,10 @@ kv_status kv_pool_create(const KVPageGeometry* geo, const KVPlaneDesc* planes, u
             return fail(KV_E_INVALID, "bad plane dtype/elem_bytes");
         if (d_block_tables && (!p.base || (reinterpret_cast<uintptr_t>(p.base) & 255)))
             return fail(KV_E_INVALID, "plane base must be non-null and 256-byte aligned");
+        if (p.layout != KV_LAYOUT_PAGE_MAJOR && p.layout != KV_LAYOUT_HEAD_MAJOR)
+            return fail(KV_E_INVALID, "plane layout must be KV_LAYOUT_PAGE_MAJOR or KV_LAYOUT_HEAD_MAJOR");
+        if (layout >= 0 && int(p.layout) != layout) return fail(KV_E_INVALID, "the planes of one pool share one layout");
+        layout = int(p.layout);
         have[k] = 1;
         seen[k] = p;
     }
@@ -328,6 +336,9 @@ kv_status kv_pool_create(const KVPageGeometry* geo, const KVPlaneDesc* planes, u
     p->k_codec = kc;
     p->v_codec = vc;
     p->scale16 = wide_dt == int(KV_DT_F16) ? 1 : 0;
+    const bool head_major = layout == int(KV_LAYOUT_HEAD_MAJOR);
+    p->sg = head_major ? 1 : int32_t(g.num_kv_heads);
+    p->sh = head_major ? int32_t(g.num_page_groups) : 1;
     p->layers = std::move(layers);
     p->planes.assign(planes, planes + n_planes);
     p->d_table = d_block_tables;
@@ -535,9 +546,9 @@ static uint64_t replica_planes(const kv_pool* pool, std::vector<ReplicaPlane>* o
         for (uint32_t role = 0; role < 4; ++role) {
             for (const KVPlaneDesc& p : pool->planes) {
                 if (p.layer != l || p.role != role) continue;
-                const uint32_t slice = H * kPage * p.x_extent * p.elem_bytes;
-                out->push_back(ReplicaPlane{p.base, slice, off});
-                off += slice;
+                const uint32_t head = kPage * p.x_extent * p.elem_bytes;
+                out->push_back(ReplicaPlane{p.base, head, off});
+                off += uint64_t(H) * head;
             }
         }
     }
@@ -577,8 +588,8 @@ kv_status kv_seq_offload(kv_pool* pool, kv_seq seq, void* host, size_t host_byte
     if (pages) *pages = n;
     if (frontier) *frontier = s->frontier;
     if (n == 0) return ok();
-    const hipError_t e = launch_replica_copy(planes.data(), int(planes.size()), s->pages.data(), int(n), pb, dhost,
-                                             true, stream);
+    const hipError_t e = launch_replica_copy(planes.data(), int(planes.size()), s->pages.data(), int(n), pb,
+                                             int(pool->geo.num_kv_heads), pool->sg, pool->sh, dhost, true, stream);
     if (e != hipSuccess) return fail(KV_E_DEVICE, std::string("replica copy: ") + hipGetErrorString(e));
     return ok();
 }
@@ -613,7 +624,8 @@ kv_status kv_seq_restore(kv_pool* pool, uint32_t table_row, const void* host, si
     // the payload lands before the row names the pages: copy, then publish
     if (n) {
         const hipError_t e = launch_replica_copy(planes.data(), int(planes.size()), s->pages.data(), int(n), pb,
-                                                 dhost, false, stream);
+                                                 int(pool->geo.num_kv_heads), pool->sg, pool->sh, dhost, false,
+                                                 stream);
         if (e != hipSuccess) {
             (void)kv_seq_release(pool, *out, stream);
             *out = 0;
@@ -650,8 +662,8 @@ kv_status kv_cow_tail_page(kv_pool* pool, kv_seq seq, hipStream_t stream) {
         std::vector<CopyPlane> cp;
         cp.reserve(pool->planes.size());
         for (const KVPlaneDesc& p : pool->planes) cp.push_back(CopyPlane{p.base, p.x_extent * p.elem_bytes});
-        hipError_t e = launch_cow_copy(cp.data(), int(cp.size()), int(pool->geo.num_kv_heads), src, dst, int(cols),
-                                       stream);
+        hipError_t e = launch_cow_copy(cp.data(), int(cp.size()), int(pool->geo.num_kv_heads), pool->sg, pool->sh,
+                                       src, dst, int(cols), stream);
         if (e != hipSuccess) {
             pool->refs[dst] = 0;   // back to the front of the queue it came from
             (from_reserve ? s->reserve : pool->free_q).push_front(dst);

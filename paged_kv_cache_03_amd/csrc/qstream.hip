@@ -130,7 +130,7 @@ __global__ void __launch_bounds__(256, (qstream_bpc<D, KC>())) paged_qstream_ker
     static_assert(QSEG >= 1 && QSEG * NCOL * NCH == QCHUNKS && QCHUNKS % NT == 0 && PAGES % NT == 0, "LDS shapes");
     typedef unsigned int vword_t __attribute__((ext_vector_type(NVW)));
 
-    __shared__ int2 pinfo[PAGES];                  // the block's pages: (slice g*H + h or -1, meta)
+    __shared__ int2 pinfo[PAGES];                  // the block's pages: (slice number of (g, h) or -1, meta)
     __shared__ u32x4 qcache[QCHUNKS];              // query rows of the first QSEG units: [unit][column][chunk]
     __shared__ float mbuf[4 * 16 * 64];            // unit merge: four waves x four tiles x 4 registers
     __shared__ float mlbuf[4][16][2];              // per-wave (m, l) of every column at a unit's end

@@ -117,7 +117,7 @@ constexpr size_t off_tasks(int H, int G) { return off_patch(H, G) + align64w(siz
 // overflow pieces: every (block, unit) piece carries at most kMaxEnt entries
 constexpr size_t max_pieces(int H, int G) { return (size_t(G) + size_t(kMaxSeg) * H) * kMaxEnt; }
 constexpr size_t off_over(int H, int G) { return off_tasks(H, G) + size_t(kTaskWords) * kMaxEnt * H; }
-// per block: qcap int2 (slice g*H + h or -1, valid rows | 256 at a unit's end | page << 9 | kPatchBit)
+// per block: qcap int2 (slice number g*sg + h*sh or -1, valid rows | 256 at a unit's end | page << 9 | kPatchBit)
 constexpr size_t off_pages(int H, int G) { return off_over(H, G) + align64w(max_pieces(H, G)); }
 constexpr size_t plan_words(int H, int G, int qcap) { return off_pages(H, G) + 2 * size_t(G) * size_t(qcap); }
 constexpr size_t plan_bytes(int H, int G, int qcap) { return (plan_words(H, G, qcap) * 4 + 255) / 256 * 256; }

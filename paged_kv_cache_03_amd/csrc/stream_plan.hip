@@ -38,6 +38,7 @@ constexpr int kNT = 256;
 struct PlanArgs {
     const int32_t* table;   // [C][L]
     int32_t L, C, M, H;
+    int32_t sg, sh;           // slice number of (g, h): g * sg + h * sh
     const int32_t* table_rows;
     const int32_t* seq_lens;  // decode
     const int32_t* q_pos0;    // chunk mode
@@ -497,7 +498,7 @@ __global__ void __launch_bounds__(kNT) stream_plan_kernel(PlanArgs a) {
         for (int k = 0; k < 4; ++k)
             if (dst[k] >= 0) {
                 const bool mapped = g[k] >= 0 && g[k] < a.M;
-                pages[dst[k]] = make_int2(mapped ? g[k] * H + sl[k] : -1, meta[k]);
+                pages[dst[k]] = make_int2(mapped ? g[k] * a.sg + sl[k] * a.sh : -1, meta[k]);
             }
     }
 }
@@ -515,6 +516,8 @@ hipError_t launch_stream_plan(const PoolView& pv, int B, int gq, const int32_t* 
     a.C = pv.C;
     a.M = pv.M;
     a.H = pv.H;
+    a.sg = pv.sg;
+    a.sh = pv.sh;
     a.table_rows = table_rows;
     a.seq_lens = seq_lens;
     a.q_pos0 = q_pos0;

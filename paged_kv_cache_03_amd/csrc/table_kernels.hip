@@ -52,6 +52,7 @@ struct CopyArgs {
     CopyPlane planes[kCopyMaxPlanes];
     int32_t n_planes;
     int32_t H;
+    int32_t sg, sh;          // slice number of (g, h): g * sg + h * sh
     int32_t src_g;
     int32_t dst_g;
     int32_t cols;
@@ -62,8 +63,8 @@ __global__ void __launch_bounds__(256) cow_copy_kernel(CopyArgs a) {
     const int pi = blockIdx.x, h = blockIdx.y;
     const CopyPlane p = a.planes[pi];
     const size_t slab = size_t(p.row_bytes) * kPage;
-    const char* src = static_cast<const char*>(p.base) + (size_t(a.src_g) * a.H + h) * slab;
-    char* dst = static_cast<char*>(p.base) + (size_t(a.dst_g) * a.H + h) * slab;
+    const char* src = static_cast<const char*>(p.base) + (size_t(a.src_g) * a.sg + size_t(h) * a.sh) * slab;
+    char* dst = static_cast<char*>(p.base) + (size_t(a.dst_g) * a.sg + size_t(h) * a.sh) * slab;
     const size_t bytes = size_t(a.cols) * p.row_bytes;
     if ((bytes & 15) == 0) {
         const size_t n = bytes >> 4;
@@ -87,16 +88,20 @@ struct ReplicaArgs {
     uint64_t page_bytes;
     char* host;
     int32_t to_host;
+    int32_t H, sg, sh;       // heads; slice number of (g, h): g * sg + h * sh
 };
 
-// grid (pages of the chunk, planes of the chunk); the slice of page group g
-// starts at base + g * slice_bytes (the H rows of a group are adjacent)
+// grid (pages of the chunk, planes of the chunk, heads): slice (g, h) of a
+// plane starts at base + (g * sg + h * sh) * head_bytes (page-major: the H
+// slices of a group are adjacent), its host image at host_off + h * head_bytes
 __global__ void __launch_bounds__(256) replica_copy_kernel(ReplicaArgs a) {
-    const int pi = int(blockIdx.x), qi = int(blockIdx.y);
+    const int pi = int(blockIdx.x), qi = int(blockIdx.y), h = int(blockIdx.z);
     const ReplicaPlane pl = a.planes[qi];
-    const size_t n = pl.slice_bytes >> 4;
-    uint4* dev = reinterpret_cast<uint4*>(static_cast<char*>(pl.base) + size_t(a.pages[pi]) * pl.slice_bytes);
-    uint4* host = reinterpret_cast<uint4*>(a.host + size_t(a.first_page + pi) * a.page_bytes + pl.host_off);
+    const size_t n = pl.head_bytes >> 4;
+    const size_t slice = size_t(a.pages[pi]) * a.sg + size_t(h) * a.sh;
+    uint4* dev = reinterpret_cast<uint4*>(static_cast<char*>(pl.base) + slice * pl.head_bytes);
+    uint4* host = reinterpret_cast<uint4*>(a.host + size_t(a.first_page + pi) * a.page_bytes + pl.host_off +
+                                           size_t(h) * pl.head_bytes);
     if (a.to_host) {
         for (size_t i = threadIdx.x; i < n; i += 256) host[i] = dev[i];
     } else {
@@ -107,7 +112,7 @@ __global__ void __launch_bounds__(256) replica_copy_kernel(ReplicaArgs a) {
 }  // namespace
 
 hipError_t launch_replica_copy(const ReplicaPlane* planes, int n_planes, const int32_t* pages, int n_pages,
-                               uint64_t page_bytes, char* host, bool to_host, hipStream_t s) {
+                               uint64_t page_bytes, int H, int sg, int sh, char* host, bool to_host, hipStream_t s) {
     for (int p0 = 0; p0 < n_pages; p0 += kReplicaPages) {
         for (int q0 = 0; q0 < n_planes; q0 += kReplicaPlanes) {
             ReplicaArgs a;
@@ -119,7 +124,10 @@ hipError_t launch_replica_copy(const ReplicaPlane* planes, int n_planes, const i
             a.page_bytes = page_bytes;
             a.host = host;
             a.to_host = to_host ? 1 : 0;
-            replica_copy_kernel<<<dim3(np, a.n_planes), 256, 0, s>>>(a);
+            a.H = H;
+            a.sg = sg;
+            a.sh = sh;
+            replica_copy_kernel<<<dim3(np, a.n_planes, H), 256, 0, s>>>(a);
             const hipError_t e = hipGetLastError();
             if (e != hipSuccess) return e;
         }
@@ -146,13 +154,15 @@ hipError_t launch_table_publish(int32_t* d_dst, const int32_t* host_vals, int32_
     return hipSuccess;
 }
 
-hipError_t launch_cow_copy(const CopyPlane* planes, int n_planes, int H, int src_g, int dst_g, int cols,
-                           hipStream_t s) {
+hipError_t launch_cow_copy(const CopyPlane* planes, int n_planes, int H, int sg, int sh, int src_g, int dst_g,
+                           int cols, hipStream_t s) {
     for (int off = 0; off < n_planes; off += kCopyMaxPlanes) {
         CopyArgs a;
         a.n_planes = std::min(kCopyMaxPlanes, n_planes - off);
         for (int i = 0; i < a.n_planes; ++i) a.planes[i] = planes[off + i];
         a.H = H;
+        a.sg = sg;
+        a.sh = sh;
         a.src_g = src_g;
         a.dst_g = dst_g;
         a.cols = cols;

@@ -78,7 +78,7 @@ __global__ void __launch_bounds__(256) verify_scalar_kernel(VerifyArgs a) {
     for (int pg = 0; pg < n_pages; ++pg) {
         const int g = trow[pg];
         if (g < 0 || g >= a.pv.M) continue;
-        const size_t slab = (size_t(g) * H + h) * kPage;
+        const size_t slab = (size_t(g) * a.pv.sg + size_t(h) * a.pv.sh) * kPage;
         const bool valid = pg * kPage + lane < ctx;
         float s[GQ];
 #pragma unroll
@@ -251,7 +251,7 @@ __global__ void __launch_bounds__(512) verify_tile_kernel(VerifyArgs a) {
     const int32_t* trow = a.pv.table + size_t(row) * a.pv.L;
     auto slice_of = [&](int p) __attribute__((always_inline)) {
         const int g0 = ld_uniform(trow, p);
-        return (g0 >= 0 && g0 < M) ? g0 * H + h : -1;
+        return (g0 >= 0 && g0 < M) ? g0 * a.pv.sg + h * a.pv.sh : -1;
     };
     auto fetch = [&](int sl, int fs) __attribute__((always_inline)) {
         if (w >= 4) return;                        // waves 0-3 load the pages

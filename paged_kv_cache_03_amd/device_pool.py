@@ -34,11 +34,18 @@ class DevicePool:
     """Planes [M][H][64][X] per layer and role, the block table [C][L], and the pool handle."""
 
     def __init__(self, profile: str, H: int, D: int, layers: int, S: int, C: int, M: int, free_order=None,
-                 host_only: bool = False, zero: bool = True, device: str = "cuda", scale_bytes: int = 4):
-        """scale_bytes: 4 (fp32) or 2 (binary16) INT8-G64 / FP8-row scale planes."""
+                 host_only: bool = False, zero: bool = True, device: str = "cuda", scale_bytes: int = 4,
+                 head_major: bool = False):
+        """scale_bytes: 4 (fp32) or 2 (binary16) INT8-G64 / FP8-row scale planes.
+
+        head_major: planes in the head-major order [X, P, N, H] (storage [H][M][64][X]);
+        ``planes`` always holds [M][H][64][X] views of the storage.
+        """
         self.profile, self.H, self.D, self.layers, self.S, self.C, self.M = profile, H, D, layers, S, C, M
         self.L = -(-S // 64)
         self.host_only = host_only
+        self.head_major = head_major
+        layout = abi.KV_LAYOUT_HEAD_MAJOR if head_major else abi.KV_LAYOUT_PAGE_MAJOR
         self.device = None if host_only else torch.device(device)
         schema = abi.kv_profile_planes(abi.KV_PROFILE[profile], D,
                                        abi.KV_DT_F16 if scale_bytes == 2 else abi.KV_DT_F32)
@@ -51,9 +58,11 @@ class DevicePool:
             for p in schema:
                 t = None
                 if not host_only:
-                    t = alloc((M, H, 64, p.x_extent), dtype=_PLANE_TORCH[p.dtype], device=self.device)
-                lp[ROLE_NAMES[p.role]] = t
-                descs.append(abi.KVPlaneDesc(layer, p.role, p.dtype, p.x_extent, p.elem_bytes, 0, ptr(t) or None))
+                    shape = (H, M, 64, p.x_extent) if head_major else (M, H, 64, p.x_extent)
+                    t = alloc(shape, dtype=_PLANE_TORCH[p.dtype], device=self.device)
+                lp[ROLE_NAMES[p.role]] = t.permute(1, 0, 2, 3) if (head_major and t is not None) else t
+                descs.append(abi.KVPlaneDesc(layer, p.role, p.dtype, p.x_extent, p.elem_bytes, layout,
+                                             ptr(t) or None))
             self.planes.append(lp)
         self.table = None if host_only else torch.empty((C, self.L), dtype=torch.int32, device=self.device)
         self.handle = abi.kv_pool_create(self.geo, descs, ptr(self.table) or None, free_order, self.stream)

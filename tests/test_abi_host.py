@@ -84,6 +84,26 @@ def test_mixed_profile_inventory_rejected():
         abi.kv_pool_create(abi.KVPageGeometry(64, 2, 128, 1, 1024, 2, 16), [planes[0]] + v8, None)
 
 
+def test_plane_layouts_accepted_uniform_and_rejected_mixed():
+    geo = abi.KVPageGeometry(64, 2, 128, 2, 1024, 2, 16)
+
+    def planes(layouts):
+        out = []
+        for layer, lay in enumerate(layouts):
+            for p in abi.kv_profile_planes(abi.KV_PROFILE["INT8_G64"], 128):
+                assert p.layout == abi.KV_LAYOUT_PAGE_MAJOR         # what the schema call writes
+                p.layer, p.layout = layer, lay
+                out.append(p)
+        return out
+
+    for lay in (abi.KV_LAYOUT_PAGE_MAJOR, abi.KV_LAYOUT_HEAD_MAJOR):
+        abi.kv_pool_destroy(abi.kv_pool_create(geo, planes([lay, lay]), None))
+    for bad in ([abi.KV_LAYOUT_PAGE_MAJOR, abi.KV_LAYOUT_HEAD_MAJOR], [2, 2]):
+        with pytest.raises(abi.KVError) as e:
+            abi.kv_pool_create(geo, planes(bad), None)
+        assert e.value.status == abi.KV_E_INVALID
+
+
 def test_stale_handles_and_leased_rows():
     h = _host_pool(1024, 2, 16)
     a = abi.kv_seq_open(h, 0)

@@ -36,8 +36,9 @@ def _valid_mask(n_pages, frontier, page_bytes, plane_sizes, H):
     return m
 
 
-@pytest.mark.parametrize("profile,D", [("INT8_G64", 128), ("BF16", 64), ("K8V4", 256)])
-def test_offload_restore_round_trip(profile, D):
+@pytest.mark.parametrize("profile,D,head_major", [("INT8_G64", 128, False), ("BF16", 64, False), ("K8V4", 256, False),
+                                                  ("INT8_G64", 128, True), ("K8V4", 256, True)])
+def test_offload_restore_round_trip(profile, D, head_major):
     import torch
     from paged_kv_cache_03_amd.device_pool import i32
     H, layers = 2, 2
@@ -45,7 +46,7 @@ def test_offload_restore_round_trip(profile, D):
     wl = workloads.small(140, profile, hist=hist, step=[1, 1, 1], C=6, S=2048, Hq=8, H=H, D=D, layers=layers,
                          mode="decode")
     pool, st, sids = build_oracle(wl)
-    dp, seqs, _ = build_device(wl, fill=0xFF)
+    dp, seqs, _ = build_device(wl, fill=0xFF, head_major=head_major)
     pb = dp.replica_page_bytes()
     assert pb == st.replica_page_bytes() == G.page_bytes(profile, D, H, layers)
     sizes = [H * 64 * spec.x_extent * spec.elem_bytes for _, spec in st.replica_order()]

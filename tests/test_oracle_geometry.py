@@ -93,6 +93,23 @@ def test_element_index_matches_c_order_layout():
         assert G.element_index(d, o, h, g, X, H) == np.ravel_multi_index((g, h, o, d), (M, H, 64, X))
 
 
+def test_head_major_index_is_c_order_and_a_bijection():
+    # head-major [X, P, N, H] == C-order [H][M][P][X]; every element once, no gaps
+    M, H, X = 5, 3, 6
+    seen = np.zeros(M * H * 64 * X, dtype=np.int64)
+    for g in range(M):
+        for h in range(H):
+            for o in range(64):
+                for d in range(X):
+                    i = G.element_index_head_major(d, o, h, g, X, M)
+                    assert i == np.ravel_multi_index((h, g, o, d), (H, M, 64, X))
+                    seen[i] += 1
+    assert (seen == 1).all()
+    # the two orders agree only when there is one head (or one page group)
+    assert G.element_index_head_major(1, 2, 0, 3, X, M) == G.element_index(1, 2, 0, 3, X, 1)
+    assert G.element_index_head_major(1, 2, 1, 0, X, 1) == G.element_index(1, 2, 1, 0, X, H)
+
+
 def test_translation_shift_mask():
     p = np.arange(1 << 20)
     assert np.array_equal(p >> 6, p // 64) and np.array_equal(p & 63, p % 64)

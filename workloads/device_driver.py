@@ -21,7 +21,7 @@ def _dev(x: np.ndarray, device):
 
 
 def build_device(wl, free_order=None, privatize=False, layers=None, zero=True, hist_layers_from=None,
-                 chunk_tokens=16384, step_append=True, fill=None):
+                 chunk_tokens=16384, step_append=True, fill=None, head_major=False):
     """Device pool holding the workload's history and step rows.
 
     hist_layers_from: if set, every layer's history rows are the rows generated for
@@ -30,6 +30,7 @@ def build_device(wl, free_order=None, privatize=False, layers=None, zero=True, h
     mapped and returned), for an op that appends them itself.
     fill: if set, every byte of every plane starts as this value (rows no
     append writes then hold it: 0xFF makes NaN codes and scales).
+    head_major: planes in the head-major order (the pool's views stay [M][H][64][X]).
     """
     import torch
     from paged_kv_cache_03_amd.device_pool import DevicePool, i32
@@ -37,7 +38,7 @@ def build_device(wl, free_order=None, privatize=False, layers=None, zero=True, h
     layers = list(range(wl.layers)) if layers is None else list(layers)
     dp = DevicePool(wl.profile, wl.H, wl.D, wl.layers, wl.S, wl.C, wl.M,
                     free_order=wl.free_order if free_order is None else free_order, zero=zero,
-                    scale_bytes=wl.scale_bytes)
+                    scale_bytes=wl.scale_bytes, head_major=head_major)
     dev = dp.device
     if fill is not None:
         for planes in dp.planes:
