@@ -269,7 +269,7 @@ def bench_verify(wl, args) -> int:
     torch.cuda.set_device(dev)
     t0 = time.time()
     log(f"workload {wl.name}: filling {wl.layers} layer(s) of history")
-    dp, _, step_inputs = build_device(wl, zero=False)
+    dp, _, step_inputs = build_device(wl, zero=False, head_major=args.head_major)
     log(f"history resident after {time.time() - t0:.1f} s")
     rows_t, pos0_t, cu_t = i32(wl.table_rows, dev), i32(wl.hist, dev), i32(wl.cu_q, dev)
     total = int(wl.cu_q[-1])
@@ -616,6 +616,8 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--scale-bytes", type=int, choices=(2, 4), default=4,
                     help="INT8-G64 / FP8-row scale planes: 4 (fp32) or 2 (binary16, the page's D256 byte table)")
+    ap.add_argument("--head-major", action="store_true",
+                    help="decode and verify configs: planes in the head-major order [X, P, N, H]")
     ap.add_argument("--graph", action="store_true",
                     help="decode configs: time replays of the step captured as one HIP graph")
     ap.add_argument("--advance", action="store_true",
@@ -646,6 +648,11 @@ def main() -> int:
     if args.scale_bytes != 4:
         wl.scale_bytes = args.scale_bytes
         wl.name += f"_scales{8 * args.scale_bytes}bit"
+    if args.head_major:
+        if wl.mode not in ("decode", "verify") or args.spec or args.replica or args.advance:
+            print("--head-major applies to the plain decode and verify runs", file=sys.stderr)
+            return 2
+        wl.name += "_headmajor"
     if args.spec:
         if wl.mode != "verify":
             print("--spec needs the verify workload (--config 5)", file=sys.stderr)
@@ -661,7 +668,7 @@ def main() -> int:
     torch.cuda.set_device(dev)
     t0 = time.time()
     log(f"workload {wl.name}: filling {wl.layers} layer(s) of history")
-    dp, _, step_inputs = build_device(wl, zero=False)
+    dp, _, step_inputs = build_device(wl, zero=False, head_major=args.head_major)
     log(f"history resident after {time.time() - t0:.1f} s")
 
     rows_t, pos0_t, cu_t = i32(wl.table_rows, dev), i32(wl.hist, dev), i32(wl.cu_q, dev)
@@ -756,7 +763,8 @@ def main() -> int:
         "vs_baseline": None, "dtype": "bf16" if wl.profile == "BF16" else wl.profile.lower(), "data": "synthetic",
         "config": {"workload": wl.name, "profile": wl.profile, "batch": wl.B, "layers": wl.layers, "q_heads": wl.Hq,
                    "kv_heads": wl.H, "head_dim": wl.D, "ctx_sum": int(sum(wl.seq_lens)), "ctx_max": int(max_ctx),
-                   "page_size": 64, "pool_pages": wl.M, "scale_bytes": wl.scale_bytes},
+                   "page_size": 64, "pool_pages": wl.M, "scale_bytes": wl.scale_bytes,
+                   "plane_order": "head_major" if args.head_major else "page_major"},
         "steps_per_s": round(1000.0 / ms_per_step, 2),
         "hbm_frac": round(value / HBM_PEAK_GBS, 4),
         "step_form": "hip_graph" if graph is not None else "eager",
