@@ -6,7 +6,7 @@ page-group terms carries the larger stride.  Results do not depend on the
 order: planes (read back as [M][H][64][X]) are bit-exact against the oracle,
 decode and verify outputs are within 2e-3 of the fp64 oracle and bitwise
 equal to those of a page-major pool built from the same inputs, and the host
-replica (NEXT-3's packed logical layout) is covered in test_gpu_replica.py.
+replica (the packed logical-order host image) is covered in test_gpu_replica.py.
 """
 
 import numpy as np
