@@ -5,7 +5,8 @@ Source: NInfer "Paged KV Context Store" maintainer page -- page-group diagram
 [X, P, H, N] (C-order [M][H][P][X] here), P=64 translation (block =
 position >> 6, offset = position & 63, page = block_table[block]), and the
 tail-COW rule (copy the committed columns of the shared tail into a private
-page group for every plane), and the host replica's logical-order packed
+page group for every plane), the writer-cardinality rule (a write into a page
+that several address spaces reference is refused), and the host replica's logical-order packed
 layout (no device page ids or table holes; each page carries the payload of
 every grouped plane of the pool; full pages are copied).
 
@@ -52,6 +53,10 @@ class OracleStore:
         pages = self.pool.table[row, blocks]
         if np.any(pages < 0):
             raise ValueError("append into an unmapped logical block")
+        # writer-cardinality rule: a page referenced by several address spaces
+        # is immutable; its tail must be copied before a write
+        if np.any(self.pool.refs[pages] > 1):
+            raise ValueError("append into a page shared by several address spaces")
         for side, x in (("K", k_bf16), ("V", v_bf16)):
             code, scale = codecs.quantize(self.kinds[0 if side == "K" else 1], x, self.scale_bytes)
             lp[f"{side}_CODE"][pages, :, offs, :] = code

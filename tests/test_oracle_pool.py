@@ -312,3 +312,32 @@ def test_rejected_rows_past_the_frontier_are_outside_the_valid_domain():
         w = np.exp(s_ - s_.max())
         ref = (w / w.sum()) @ V[:, j // 2]
         assert np.max(np.abs(got[0, j] - ref)) < 1e-12
+
+
+def test_store_refuses_writes_into_shared_pages():
+    # writer-cardinality rule: a page two address spaces reference is immutable.
+    # Both a shared full page and a shared partial tail refuse a write; after
+    # the tail copy the fork writes its private page and the parent's bytes stay.
+    pool = OP.OraclePool(S=1024, C=2, M=32)
+    st = OracleStore(pool, "INT8_G64", H=1, D=64, layers=1)
+    a = pool.open(0)
+    pool.ensure_mapped(a, 100)
+    rng = rng_for(81)
+    k, v = bf16_normal(rng, (100, 1, 64)), bf16_normal(rng, (100, 1, 64))
+    st.append(0, 0, 0, k, v)
+    pool.commit(a, 100)
+    b = pool.fork(a, 100, 1)
+    row = bf16_normal(rng, (1, 1, 64))
+    with pytest.raises(ValueError, match="shared"):
+        st.append(0, 1, 10, row, row)          # a full page both rows map
+    with pytest.raises(ValueError, match="shared"):
+        st.append(0, 1, 100, row, row)         # the shared tail, at the fork's frontier
+    with pytest.raises(ValueError, match="shared"):
+        st.append(0, 0, 100, row, row)         # the parent may not write it either
+    before = {r: arr.copy() for r, arr in st.planes[0].items()}
+    _, (src, dst, cols) = pool.cow_tail(b)
+    st.cow_copy(src, dst, cols)
+    st.append(0, 1, 100, row, row)             # now private
+    st.append(0, 0, 100, row, row)
+    for r, arr in st.planes[0].items():
+        assert np.array_equal(arr[src, :, :100 - 64], before[r][src, :, :100 - 64])
