@@ -32,6 +32,27 @@ def attend(qvec: np.ndarray, K: np.ndarray, V: np.ndarray, sm_scale: float) -> n
     return (w @ V.astype(np.float64)) / w.sum()
 
 
+def attend_many(Qm: np.ndarray, limits, K: np.ndarray, V: np.ndarray, sm_scale: float) -> np.ndarray:
+    """Several query vectors against one K, V [n, D]: row r of Qm [m, D] attends
+    keys [0, limits[r]) -> fp64 [m, D].  The definition of ``attend`` for each
+    row (an empty range gives zeros); the scores of all rows come from one
+    product, which only saves time at long contexts."""
+    m = Qm.shape[0]
+    lim = np.asarray(limits, dtype=np.int64).reshape(m)
+    out = np.zeros((m, V.shape[-1]), dtype=np.float64)
+    n = int(lim.max()) if m else 0
+    if n == 0:
+        return out
+    s = (K[:n].astype(np.float64) @ Qm.astype(np.float64).T) * float(sm_scale)      # [n, m]
+    visible = np.arange(n)[:, None] < lim[None, :]
+    s = np.where(visible, s, -np.inf)
+    live = lim > 0
+    mx = np.where(live, s.max(axis=0, initial=-np.inf), 0.0)
+    w = np.where(visible, np.exp(s - mx[None, :]), 0.0)
+    out[live] = (w.T @ V[:n].astype(np.float64))[live] / w.sum(axis=0)[live, None]
+    return out
+
+
 def decode_dense(q_bf16: np.ndarray, K: np.ndarray, V: np.ndarray, sm_scale: float) -> np.ndarray:
     """q [Hq, D] bf16 bits, K/V [n, H, D] float -> fp64 [Hq, D] (last-token query)."""
     q = bf16_to_f32(q_bf16)

@@ -10,8 +10,8 @@ import pytest
 import workloads
 from oracle import attention as A
 from oracle import codecs as Q
-from tests.drivers import (build_device, build_oracle, device_decode, device_verify, oracle_pool_only,
-                           plane_np, say)
+from tests.drivers import (build_device, build_oracle, device_decode, device_verify, oracle_decode_all,
+                           oracle_pool_only, oracle_verify_rows, plane_np, say)
 
 pytestmark = pytest.mark.gpu
 
@@ -197,43 +197,40 @@ def test_gpu_decode_identical_before_and_after_tail_cow():
 
 
 # --------------------------------------------------------- full sizes ------
-def _sampled_decode_check(wl, layers, n_samples, seed):
+def _full_decode_check(wl, layers):
+    """Every decode output of the given layers against the fp64 oracle, and
+    every row the step appended (codes and scales, bit for bit), at the full
+    size, in the launch configuration the benchmark times (plan + run)."""
     import torch
     pool, _ = oracle_pool_only(wl)
-    dp, _, step_in = build_device(wl, layers=layers, zero=False)
+    dp, _, _ = build_device(wl, layers=layers, zero=False)
     assert np.array_equal(_table(dp), pool.table)
-    rng = np.random.default_rng(seed)
     kind_k, kind_v = KINDS[wl.profile]
-    g = wl.Hq // wl.H
     worst = 0.0
     for layer in layers:
         got = device_decode(dp, wl, layer)
-        q = wl.q(layer)
-        cache = {}
-        for _ in range(n_samples):
-            b = int(rng.integers(wl.B))
-            j = int(rng.integers(wl.Hq))
-            h = j // g
-            if b not in cache:
-                cache[b] = wl.logical_kv(layer, b, wl.seq_lens[b])
-            k, v = cache[b]
-            K = Q.dequantize(kind_k, *Q.quantize(kind_k, k[:, h]))
-            V = Q.dequantize(kind_v, *Q.quantize(kind_v, v[:, h]))
-            ref = A.attend(Q.bf16_to_f32(q[b, j]), K, V, wl.sm_scale)
-            worst = max(worst, float(np.max(np.abs(got[b, j] - ref))))
-        # sampled rows of the code planes: the step rows of every entry
+        say(f"  layer {layer}: device done, oracle reference of all {wl.B}x{wl.Hq} outputs")
+        ref = oracle_decode_all(wl, layer)
+        err = float(np.max(np.abs(got - ref)))
+        say(f"  layer {layer}: max abs err over every output {err:.3g}")
+        worst = max(worst, err)
+        # every appended row: its page through the table, codes and scales bit-exact
+        planes = {role: plane_np(dp, layer, role) for role in dp.planes[layer]}
         for b in range(wl.B):
-            pos = wl.hist[b] + wl.step[b] - 1
-            gg = pool.table[wl.table_rows[b], pos >> 6]
             k, v = wl.step_kv(layer, b)
-            for side, x in (("K", k[-1]), ("V", v[-1])):
-                kind = kind_k if side == "K" else kind_v
-                code, _ = Q.quantize(kind, x)
-                row = dp.planes[layer][f"{side}_CODE"][int(gg), :, pos & 63].cpu().numpy()
-                if row.dtype == np.int16:
-                    row = row.view(np.uint16)
-                assert np.array_equal(row, code)
-    say(f"  worst sampled abs err {worst:.3g}")
+            pos = wl.hist[b] + np.arange(wl.step[b])
+            gg = pool.table[wl.table_rows[b], pos >> 6]
+            for side, x, kind in (("K", k, kind_k), ("V", v, kind_v)):
+                code, scale = Q.quantize(kind, x, wl.scale_bytes)
+                got_c = planes[f"{side}_CODE"][gg, :, pos & 63]
+                assert np.array_equal(got_c, code), (layer, b, side)
+                if scale is not None:
+                    got_s = planes[f"{side}_SCALE"][gg, :, pos & 63]
+                    assert np.array_equal(got_s.view(np.uint8), scale.reshape(got_s.shape).view(np.uint8)), \
+                        (layer, b, side)
+        del planes
+        crossing = sum(int((wl.hist[b] >> 6) != ((wl.hist[b] + wl.step[b] - 1) >> 6)) for b in range(wl.B))
+        say(f"  layer {layer}: {sum(wl.step)} appended rows bit-exact ({crossing} entries cross a page)")
     assert worst <= TOL
     dp.close()
     torch.cuda.empty_cache()
@@ -242,22 +239,25 @@ def _sampled_decode_check(wl, layers, n_samples, seed):
 def test_full_bf16_decode_c8_32k():
     wl = workloads.get(2)
     say(f"workload {wl.name} (layers 0 and 31)")
-    _sampled_decode_check(wl, [0, 31], 12, 2)
+    _full_decode_check(wl, [0, 31])
 
 
 def test_full_int8_decode_c8_32k():
     wl = workloads.get(3)
     say(f"workload {wl.name} (layer 0)")
-    _sampled_decode_check(wl, [0], 12, 3)
+    _full_decode_check(wl, [0])
 
 
 def test_full_k8v4_decode_c8_64k():
     wl = workloads.get(4)
     say(f"workload {wl.name}")
-    _sampled_decode_check(wl, [0], 12, 4)
+    _full_decode_check(wl, [0])
 
 
 def test_full_verify_prefill_c4_128k():
+    """Every row of both 5-token verify chunks, and all 32 heads of the first
+    and last token of each 32-token (128-column) tile of both 512-token prefill
+    chunks, plus 16 more seeded tokens of each, against the fp64 oracle."""
     import torch
     wl = workloads.get(5)
     say(f"workload {wl.name}")
@@ -265,23 +265,22 @@ def test_full_verify_prefill_c4_128k():
     dp, _, _ = build_device(wl, zero=False)
     assert np.array_equal(_table(dp), pool.table)
     got = device_verify(dp, wl, 0)
-    q = wl.q(0)
-    rng = np.random.default_rng(5)
-    g = wl.Hq // wl.H
-    worst = 0.0
-    cache = {}
-    for _ in range(16):
-        b = int(rng.integers(wl.B))
-        i = int(rng.integers(wl.step[b]))
-        j = int(rng.integers(wl.Hq))
-        n = wl.hist[b] + i + 1
-        if b not in cache:
-            cache[b] = wl.logical_kv(0, b, wl.seq_lens[b])
-        k, v = cache[b][0][:n], cache[b][1][:n]
-        ref = A.attend(Q.bf16_to_f32(q[wl.cu_q[b] + i, j]), Q.bf16_to_f32(k[:, j // g]), Q.bf16_to_f32(v[:, j // g]),
-                       wl.sm_scale)
-        worst = max(worst, float(np.max(np.abs(got[wl.cu_q[b] + i, j] - ref))))
-    say(f"  worst sampled abs err {worst:.3g}")
-    assert worst <= TOL
     dp.close()
     torch.cuda.empty_cache()
+    rng = np.random.default_rng(5)
+    tokens = {}
+    for b in range(wl.B):
+        T = wl.step[b]
+        if T <= 32:
+            tokens[b] = list(range(T))
+        else:
+            sel = {x for t in range(0, T, 32) for x in (t, min(T, t + 32) - 1)}
+            sel |= {int(x) for x in rng.integers(0, T, 16)}
+            tokens[b] = sorted(sel)
+    say(f"  device done; oracle reference of {sum(len(t) for t in tokens.values())} tokens x {wl.Hq} heads")
+    ref = oracle_verify_rows(wl, 0, tokens)
+    worst = 0.0
+    for (b, i), r in ref.items():
+        worst = max(worst, float(np.max(np.abs(got[wl.cu_q[b] + i] - r))))
+    say(f"  max abs err over {len(ref)} tokens x {wl.Hq} heads {worst:.3g}")
+    assert worst <= TOL

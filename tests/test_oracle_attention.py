@@ -196,3 +196,27 @@ def test_planted_index_error_is_caught():
     bad = np.stack([A.attend(Q.bf16_to_f32(q[j]), K[:, 0], V[:, 0], 0.25) for j in range(4)])
     assert not np.allclose(good, bad)
     assert f32_to_bf16_bits(np.float32([1.0]))[0] == 0x3F80
+
+
+def test_attend_many_equals_attend_per_row_and_sdpa():
+    # each row is the per-vector definition over its own key range, including an
+    # empty range, one key and the whole of K; the explicit-mask SDPA of torch
+    # (fp64, CPU) is the library pin of the same thing
+    rng = np.random.default_rng(21)
+    n, D = 300, 32
+    K, V = rng.standard_normal((n, D)), rng.standard_normal((n, D))
+    Qm = rng.standard_normal((9, D)) * 3.0
+    lim = [0, 1, 2, 63, 64, 65, 200, 299, 300]
+    got = A.attend_many(Qm, lim, K, V, 0.2)
+    for r in range(len(lim)):
+        assert np.allclose(got[r], A.attend(Qm[r], K[:lim[r]], V[:lim[r]], 0.2), rtol=1e-12, atol=1e-13), r
+    assert np.array_equal(got[0], np.zeros(D))
+    assert np.array_equal(got[1], V[0])
+    mask = torch.arange(n)[None, :] < torch.tensor(lim[1:])[:, None]
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(Qm[1:])[None], torch.from_numpy(K)[None], torch.from_numpy(V)[None], attn_mask=mask[None],
+        scale=0.2)[0].numpy()
+    assert np.allclose(got[1:], ref, rtol=1e-12, atol=1e-13)
+    # a planted off-by-one in the limits is caught
+    bad = A.attend_many(Qm, [x + 1 if 0 < x < n else x for x in lim], K, V, 0.2)
+    assert not np.allclose(bad[2], got[2], atol=1e-6)
