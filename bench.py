@@ -63,6 +63,49 @@ def log(msg: str) -> None:
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
+class KernelEvents:
+    """HIP event pairs that the library records around the dominant kernel of
+    an attention call (kv_trace_next_kernel): the kernel's own time on the
+    stream it runs on, without the combine launch or launch gaps."""
+
+    def __init__(self, n: int):
+        import torch
+        self.pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                      for _ in range(n)]
+        for a, b in self.pairs:              # torch creates the HIP event at its first record
+            a.record()
+            b.record()
+        torch.cuda.synchronize()
+        self.used = 0
+
+    def arm(self) -> None:
+        from paged_kv_cache_03_amd import _abi as abi
+        a, b = self.pairs[self.used]
+        abi.kv_trace_next_kernel(a.cuda_event, b.cuda_event)
+        self.used += 1
+
+    def mean_ms(self) -> float:
+        import torch
+        torch.cuda.synchronize()
+        return sum(a.elapsed_time(b) for a, b in self.pairs[:self.used]) / max(1, self.used)
+
+
+def host_threads() -> dict:
+    """The host the oracle runs on: CPUs the process may use, and the BLAS
+    threads NumPy's matrix products use (the oracle's only parallel part)."""
+    try:
+        from threadpoolctl import threadpool_info
+        blas = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        blas = 1
+    try:
+        avail = len(os.sched_getaffinity(0))
+    except AttributeError:
+        avail = os.cpu_count() or 1
+    return {"cores": int(blas), "blas_threads": int(blas), "host_cpus": int(os.cpu_count() or 1),
+            "cpus_available": int(avail)}
+
+
 def bytes_per_token_head(profile: str, D: int, scale_bytes: int = 4) -> int:
     from paged_kv_cache_03_amd import _abi as abi
     dt = abi.KV_DT_F16 if scale_bytes == 2 else abi.KV_DT_F32
@@ -150,11 +193,7 @@ def cpu_baseline(wl, seconds_hint: float = 20.0) -> dict:
     from oracle import attention as A
     from oracle.pool import OraclePool
     from oracle.store import OracleStore
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:
-        threads = 1
+    threads = host_threads()
     log("cpu baseline: building the oracle's pool for layer 0")
     pool = OraclePool(wl.S, wl.C, wl.M, free_order=wl.free_order)
     st = OracleStore(pool, wl.profile, wl.H, wl.D, 1, scale_bytes=wl.scale_bytes)
@@ -193,7 +232,7 @@ def cpu_baseline(wl, seconds_hint: float = 20.0) -> dict:
         reps += 1
     unique, _ = kv_read_bytes(pool.table, wl)
     per_layer = elapsed / reps
-    return {"value": round(unique / per_layer / 1e9, 4), "unit": "GB/s", "cores": int(threads), "kind": "oracle",
+    return {"value": round(unique / per_layer / 1e9, 4), "unit": "GB/s", **threads, "kind": "oracle",
             "sample": f"layer 0 of {wl.layers}: append of the step rows + decode of all {wl.B} entries x {wl.Hq} "
                       f"heads, {reps} rep(s), {per_layer:.2f} s per layer (KV bytes read / time)"}
 
@@ -206,11 +245,7 @@ def cpu_baseline_verify(wl, seconds_hint: float = 20.0) -> dict:
     from oracle import attention as A
     from oracle.pool import OraclePool
     from oracle.store import OracleStore
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:
-        threads = 1
+    threads = host_threads()
     sample = [b for b in range(wl.B) if wl.step[b] <= 8 and wl.fork[b] is None][:1]
     log(f"cpu baseline: the oracle's pool for entries {sample}")
     pool = OraclePool(wl.S, wl.C, wl.M, free_order=wl.free_order)
@@ -240,12 +275,22 @@ def cpu_baseline_verify(wl, seconds_hint: float = 20.0) -> dict:
     pairs = sum(n0 * T + T * (T + 1) // 2 for n0, T in ((wl.hist[b], wl.step[b]) for b in sample))
     flops = 4.0 * wl.D * wl.Hq * pairs
     per = elapsed / reps
-    return {"value": round(flops / per / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+    return {"value": round(flops / per / 1e12, 6), "unit": "TFLOP/s", **threads, "kind": "oracle",
             "sample": f"layer 0: one verify chunk of {wl.step[sample[0]]} tokens over its {n0s[0]}-token history, "
                       f"all {wl.Hq} heads, {reps} rep(s), {per:.2f} s each"}
 
 
 MFMA_BF16_PEAK_TFLOPS = 2500.0
+
+
+def verify_dominant_kernel(wl) -> str:
+    """The kernel that carries most of a paged_attn_verify call (rocprofv3 name)."""
+    gq = wl.Hq // wl.H
+    if wl.profile == "BF16" and wl.D in (64, 128) and gq in (1, 2, 4, 8):
+        if max(wl.step) * gq > 32:
+            return f"verify_tile_kernel<{wl.D}, {gq}>"
+        return f"paged_vstream_kernel<{wl.D}, {gq}, 2, true>"
+    return f"verify_scalar_kernel<{wl.D}, {gq}>"
 
 
 def verify_kernel_names(wl) -> str:
@@ -278,12 +323,14 @@ def bench_verify(wl, args) -> int:
     out = torch.empty((total, wl.Hq, wl.D), dtype=torch.float32, device=dev)
     ws = dp.workspace(wl.B, wl.Hq, msl, mql)
 
-    def step(events=None):
+    def step(events=None, kern=None):
         for layer in range(wl.layers):
             kd, vd = step_inputs[layer]
             dp.append(layer, rows_t, pos0_t, cu_t, total, kd, vd)
             if events is not None:
                 events[layer][0].record()
+            if kern is not None:
+                kern.arm()
             dp.verify(layer, wl.Hq, rows_t, pos0_t, cu_t, total, mql, msl, qs[layer], wl.sm_scale, out, ws)
             if events is not None:
                 events[layer][1].record()
@@ -301,13 +348,22 @@ def bench_verify(wl, args) -> int:
     ms_per_step = start.elapsed_time(end) / steps
     evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
             for _ in range(wl.layers)] for _ in range(steps)]
+    kern = KernelEvents(wl.layers * steps)
     for s_ in range(steps):
-        step(evs[s_])
+        step(evs[s_], kern)
     torch.cuda.synchronize()
     ver_ms = float(np.mean([a.elapsed_time(b) for row in evs for (a, b) in row]))
+    kern_ms = kern.mean_ms()
 
     pairs = sum(n0 * T + T * (T + 1) // 2 for n0, T in zip(wl.hist, wl.step))
     flops = 4.0 * wl.D * wl.Hq * pairs                      # per layer
+    # the dominant kernel: the prefill tiles take the chunks wider than 32
+    # query columns (tokens x query heads per KV head); the rest go through
+    # the page stream in chunk mode before them
+    gq = wl.Hq // wl.H
+    wide = [(n0, T) for n0, T in zip(wl.hist, wl.step) if T * gq > 32]
+    kern_flops = 4.0 * wl.D * wl.Hq * sum(n0 * T + T * (T + 1) // 2 for n0, T in (wide or zip(wl.hist, wl.step)))
+    kern_tflops = kern_flops / (kern_ms * 1e-3) / 1e12
     table = dp.table.cpu().numpy()
     bpth = bytes_per_token_head(wl.profile, wl.D, wl.scale_bytes)
     kv_bytes = sum(len({int(table[wl.table_rows[b], p]) for p in range((c + 63) // 64)}) * 64 * wl.H * bpth
@@ -321,11 +377,14 @@ def bench_verify(wl, args) -> int:
         "config": {"workload": wl.name, "profile": wl.profile, "batch": wl.B, "layers": wl.layers,
                    "q_heads": wl.Hq, "kv_heads": wl.H, "head_dim": wl.D, "chunk_tokens": list(wl.step),
                    "frontiers": list(wl.hist), "page_size": 64, "pool_pages": wl.M},
-        "roofline": {"kernel": verify_kernel_names(wl), "bound": "mfma", "achieved": round(tflops, 2),
-                     "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
-                     "traffic": measured_traffic(wl, "verify"), "flops_per_launch": flops,
-                     "kv_bytes_per_launch": kv_bytes,
-                     "launch_ms": round(ver_ms, 5)},
+        "roofline": {"kernel": verify_dominant_kernel(wl), "bound": "mfma", "achieved": round(kern_tflops, 2),
+                     "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(kern_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+                     "traffic": measured_traffic(wl, "verify"), "flops_per_launch": kern_flops,
+                     "launch_ms": round(kern_ms, 5),
+                     "call": {"kernels": verify_kernel_names(wl), "flops": flops, "kv_bytes": kv_bytes,
+                              "ms": round(ver_ms, 5), "tflops": round(tflops, 2),
+                              "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4)}},
         "cpu_baseline": None if args.no_cpu_baseline else cpu_baseline_verify(wl),
     }
     print(json.dumps(line), flush=True)
@@ -385,6 +444,7 @@ def bench_spec(wl, args) -> int:
         dp.append(0, rows_t, pos_dev[k], cu_t, B * T, kd, vd)
         if events is not None:
             events[0].record()
+            kern.arm()
         dp.verify(0, wl.Hq, rows_t, pos_dev[k], cu_t, B * T, T, max_ctx, qd, wl.sm_scale, out, ws)
         if events is not None:
             events[1].record()
@@ -407,10 +467,12 @@ def bench_spec(wl, args) -> int:
     ms_round = start.elapsed_time(end) / rounds
     host_us = host_s[0] / rounds * 1e6
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(rounds)]
+    kern = KernelEvents(rounds)
     for i, k in enumerate(range(warm + rounds, warm + 2 * rounds)):
         one(k, evs[i])
     torch.cuda.synchronize()
-    ver_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    call_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    ver_ms = kern.mean_ms()
     a_, res_, v_ = dp.stats()
     reserved = [dp.reservation(seqs[b]) for b in range(B)]
     bpth = bytes_per_token_head(wl.profile, wl.D, wl.scale_bytes)
@@ -430,7 +492,7 @@ def bench_spec(wl, args) -> int:
         "roofline": {"kernel": "paged_vstream_kernel<%d, %d, 2, true>" % (wl.D, wl.Hq // wl.H), "bound": "hbm",
                      "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None, "bytes_per_launch": kv_bytes,
-                     "launch_ms": round(ver_ms, 5)},
+                     "launch_ms": round(ver_ms, 5), "call_ms": round(call_ms, 5)},
         "cpu_baseline": None,
     }
     print(json.dumps(line), flush=True)
@@ -514,6 +576,68 @@ def bench_replica(wl, args) -> int:
     print(json.dumps(line), flush=True)
     dp.close()
     return 0 if same else 1
+
+
+def bench_read_ceiling(args) -> int:
+    """The HBM read ceiling of the decode's access pattern (kv_read_probe): per
+    launch, 22,300 distinct random 16 KiB slices (365 MB, the BF16 K and V
+    slices one decode of the 8-sequence 32K workload reads) out of an 8 GiB
+    buffer, 32 different slice lists in rotation as the 32 layers of a step
+    rotate, so the launches stream from HBM rather than the 256 MB
+    Infinity Cache.  Sweeps blocks per compute unit (4 waves each); `value` is
+    the best mean rate.  A secondary denominator for the decode kernel."""
+    import numpy as np
+    import torch
+    from paged_kv_cache_03_amd import _abi as abi
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    slice_bytes, n, lists = 16384, 22300, 32
+    buf_bytes = 8 << 30
+    buf = torch.empty(buf_bytes, dtype=torch.uint8, device=dev)
+    buf.fill_(1)
+    r = np.random.default_rng(31)
+    ids = [torch.from_numpy(r.choice(buf_bytes // slice_bytes, n, replace=False).astype(np.int32)).to(dev)
+           for _ in range(lists)]
+    sink = torch.zeros(4096, dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream().cuda_stream
+    reps = max(1, min(args.steps, 20))
+    results = {}
+    for bpc in (1, 2, 4, 8):
+        def launch(i):
+            abi.kv_read_probe(buf.data_ptr(), ids[i % lists].data_ptr(), n, slice_bytes, bpc, sink.data_ptr(), stream)
+        for i in range(lists):
+            launch(i)
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(reps * lists)]
+        for i, (a, b) in enumerate(ev):
+            a.record()
+            launch(i)
+            b.record()
+        torch.cuda.synchronize()
+        ms = np.array([a.elapsed_time(b) for a, b in ev])
+        results[bpc] = {"mean_gbs": round(n * slice_bytes / (ms.mean() * 1e-3) / 1e9, 1),
+                        "best_gbs": round(n * slice_bytes / (ms.min() * 1e-3) / 1e9, 1),
+                        "mean_us": round(float(ms.mean()) * 1e3, 2)}
+        log(f"blocks per CU {bpc}: {results[bpc]}")
+    best = max(results, key=lambda k: results[k]["mean_gbs"])
+    value = results[best]["mean_gbs"]
+    line = {
+        "metric": "HBM read ceiling of the decode access pattern (random 16 KiB slices, read once)",
+        "value": value, "unit": "GB/s", "n_gpus": 1, "steps": reps, "warmup": 1,
+        "ms_per_step": round(results[best]["mean_us"] * 1e-3, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bytes", "data": "synthetic",
+        "config": {"workload": "read_probe_16k_slices_365MB", "slice_bytes": slice_bytes, "slices_per_launch": n,
+                   "slice_lists": lists, "buffer_bytes": buf_bytes},
+        "by_blocks_per_cu": results, "best_blocks_per_cu": best,
+        "roofline": {"kernel": f"read_probe_kernel<16>", "bound": "hbm", "achieved": value, "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(value / HBM_PEAK_GBS, 4), "traffic": None,
+                     "bytes_per_launch": n * slice_bytes, "launch_ms": round(results[best]["mean_us"] * 1e-3, 5)},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
 
 
 def bench_advance(wl, args) -> int:
@@ -626,6 +750,8 @@ def main() -> int:
                     help="decode configs: offload / restore of the longest entry's pages (host replica)")
     ap.add_argument("--spec", action="store_true",
                     help="with --config 5: speculative rounds (draft, verify, commit the accepted prefix, trim)")
+    ap.add_argument("--read-ceiling", action="store_true",
+                    help="only measure the HBM read ceiling of the decode's access pattern (kv_read_probe)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a 1 GiB device copy (counter calibration under rocprofv3 --pmc)")
     args = ap.parse_args()
@@ -636,6 +762,8 @@ def main() -> int:
 
     if args.copy_calibration:
         return copy_calibration()
+    if args.read_ceiling:
+        return bench_read_ceiling(args)
 
     import numpy as np
     import torch
@@ -685,7 +813,7 @@ def main() -> int:
     # appends the rows itself
     fused = wl.profile == "BF16" and wl.D in (64, 128)
 
-    def step(events=None):
+    def step(events=None, kern=None):
         dp.decode_plan(wl.Hq, rows_t, lens_t, max_ctx, ws)
         for layer in range(wl.layers):
             kd, vd = step_inputs[layer]
@@ -693,6 +821,8 @@ def main() -> int:
                 dp.append(layer, rows_t, pos0_t, cu_t, total, kd, vd)
             if events is not None:
                 events[layer][0].record()
+            if kern is not None:
+                kern.arm()
             if fused:
                 dp.decode_append_run(layer, wl.B, wl.Hq, max_ctx, kd, vd, qs[layer], wl.sm_scale, out, ws)
             else:
@@ -710,13 +840,14 @@ def main() -> int:
         outs = [out] * wl.layers
         ks = [step_inputs[layer][0] for layer in range(wl.layers)]
         vs = [step_inputs[layer][1] for layer in range(wl.layers)]
+        # the fused form (no positions: one row per entry at seq_len - 1) where the eager step uses it
         graph = dp.step_graph(wl.B, wl.Hq, rows_t, lens_t, max_ctx, qs, wl.sm_scale, outs, ws, ks=ks, vs=vs,
-                              pos0=pos0_t, cu=cu_t, total_tokens=total)
+                              pos0=None if fused else pos0_t, cu=None if fused else cu_t, total_tokens=total)
         eager_step = step
 
-        def step(events=None):
-            if events is not None:
-                eager_step(events)
+        def step(events=None, kern=None):
+            if events is not None or kern is not None:
+                eager_step(events, kern)
             else:
                 dp.graph_launch(graph)
 
@@ -735,13 +866,17 @@ def main() -> int:
     ms_per_step = start.elapsed_time(end) / args.steps
     log(f"{ms_per_step:.4f} ms per step")
 
-    # decode launch durations: events around every paged_attn_decode call of K steps
+    # the same K steps again, with HIP events around every decode call (the
+    # call: page stream, combine and their launches) and, recorded by the
+    # library on the stream it launches on, around the page-stream kernel alone
     evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
             for _ in range(wl.layers)] for _ in range(args.steps)]
+    kern = KernelEvents(wl.layers * args.steps)
     for s in range(args.steps):
-        step(evs[s])
+        step(evs[s], kern)
     torch.cuda.synchronize()
-    dec_ms = float(np.mean([a.elapsed_time(b) for row in evs for (a, b) in row]))
+    call_ms = float(np.mean([a.elapsed_time(b) for row in evs for (a, b) in row]))
+    dec_ms = kern.mean_ms()
 
     table = dp.table.cpu().numpy()
     unique, logical = kv_read_bytes(table, wl)
@@ -772,7 +907,9 @@ def main() -> int:
         "roofline": {"kernel": decode_kernel_name(wl), "bound": "hbm",
                      "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(wl),
-                     "bytes_per_launch": per_decode, "launch_ms": round(dec_ms, 5)},
+                     "bytes_per_launch": per_decode, "launch_ms": round(dec_ms, 5),
+                     "call_ms": round(call_ms, 5),
+                     "call_frac": round(per_decode / (call_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

@@ -405,14 +405,18 @@ kv_status paged_attn_verify(const kv_pool* pool, uint32_t layer, uint32_t B, uin
  * Store page, graph-stable bases: plane and table bases stay fixed while page
  * ids, table rows, lengths and positions are data; one graph per exact B).
  * The graph holds exactly the work of an eager step: paged_attn_decode_plan,
- * then per layer l the append of the step's rows and the decode run --
- * paged_attn_decode_append_run(d_k[l], d_v[l]) where the BF16 page stream
- * takes it (one row per entry: total_tokens == B), else
- * kv_append(d_pos0, d_cu_tokens, total_tokens) then paged_attn_decode_run.
+ * then per layer l the append of the step's rows and the decode run.  The
+ * caller picks the append's form:
+ *   d_pos0 == d_cu_tokens == NULL : paged_attn_decode_append_run(d_k[l],
+ *       d_v[l]) -- one row per entry at position seq_len - 1 (total_tokens
+ *       == B); BF16 pages on the matrix-core stream only, KV_E_UNSUPPORTED
+ *       otherwise;
+ *   both set : kv_append(d_pos0, d_cu_tokens, total_tokens) then
+ *       paged_attn_decode_run, for any rows and positions.
  * d_k == d_v == NULL: runs only, nothing appended.
  *   d_q[l], d_out[l], d_k[l], d_v[l] : host arrays of n_layers device
  *       pointers, as for the eager calls; d_pos0 / d_cu_tokens [B] / [B+1]
- *       device arrays (only for the kv_append form).
+ *       device arrays (the kv_append form).
  * Every pointer, B, Hq, max_seq_len, sm_scale and the workspace are fixed at
  * capture; the contents they point to are read at each replay, so a caller
  * updates lengths, rows, queries and step rows in place and maps new pages
@@ -439,6 +443,35 @@ void kv_step_graph_destroy(kv_step_graph* graph);
 
 /* 1 if decode (max_q_len == 0) or verify has a kernel for this pool and Hq. */
 int paged_attn_supported(const kv_pool* pool, uint32_t Hq, uint32_t max_q_len);
+
+/* Measurement hook.  The next paged_attn_decode, paged_attn_decode_run,
+ * paged_attn_decode_append_run or paged_attn_verify call made on this thread
+ * records `before` on its stream immediately before the launch of its
+ * dominant kernel and `after` immediately after that launch, then forgets
+ * both.  The dominant kernel is the page stream of a decode (the split kernel
+ * where the stream does not apply) and, for a verify, the prefill tile kernel
+ * when wide chunks are present, else the page stream in chunk mode (or the
+ * per-token kernel).  The events are the caller's (hipEventCreate, timing
+ * enabled); hipEventElapsedTime(before, after) is then that kernel's time on
+ * the stream.  Not for use under graph capture.  NULL, NULL clears;
+ * KV_E_INVALID if only one is NULL. */
+kv_status kv_trace_next_kernel(hipEvent_t before, hipEvent_t after);
+
+/* Measurement: the HBM read ceiling of the paged decode's access pattern
+ * (Paged KV Context Store page, consumer rules: pages are read in place, one
+ * (page group, KV head) slice at a time, in table order).  Reads slices
+ * i = 0 .. n_slices-1 of slice_bytes bytes at d_base + d_slice_ids[i] *
+ * slice_bytes once each, with 16-byte non-temporal loads, on blocks_per_cu
+ * blocks of four waves per compute unit, each block taking a contiguous
+ * share of the list as the page stream does, and writes one checksum word
+ * per block to d_sink (so no load is dead).  The caller times it.
+ *   slice_bytes   : 8192, 16384 (a BF16 D=128 K or V slice) or 32768.
+ *   blocks_per_cu : 1..8.
+ *   d_sink        : >= compute units * blocks_per_cu uint32.
+ * Every d_slice_ids[i] * slice_bytes + slice_bytes must lie inside the
+ * caller's buffer (not checked: device data).  KV_E_INVALID on other sizes. */
+kv_status kv_read_probe(const void* d_base, const int32_t* d_slice_ids, uint32_t n_slices, uint32_t slice_bytes,
+                        uint32_t blocks_per_cu, uint32_t* d_sink, hipStream_t stream);
 
 /* Detail of the last non-OK status on the calling thread ("" if none). */
 const char* kv_last_error_message(void);

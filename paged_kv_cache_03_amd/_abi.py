@@ -33,7 +33,7 @@ EXPORTS = ["kv_profile_planes", "kv_profile_planes_ex", "kv_plane_bytes", "kv_po
            "paged_attn_workspace_bytes", "paged_attn_decode", "paged_attn_decode_plan", "paged_attn_decode_run",
            "paged_attn_decode_append_run",
            "paged_attn_verify", "kv_decode_step_graph_create", "kv_step_graph_launch", "kv_step_graph_destroy",
-           "paged_attn_supported",
+           "paged_attn_supported", "kv_trace_next_kernel", "kv_read_probe",
            "kv_last_error_message"]
 
 
@@ -106,6 +106,8 @@ def _load():
         "kv_step_graph_launch": (i32, [vp, vp]),
         "kv_step_graph_destroy": (None, [vp]),
         "paged_attn_supported": (ctypes.c_int, [vp, u32, u32]),
+        "kv_trace_next_kernel": (i32, [vp, vp]),
+        "kv_read_probe": (i32, [vp, vp, u32, u32, u32, vp, vp]),
         "kv_last_error_message": (ctypes.c_char_p, []),
     }
     for name, (res, args) in sig.items():
@@ -124,6 +126,16 @@ def _check(st: int, deficit: int = 0) -> None:
 
 def kv_last_error_message() -> str:
     return _lib.kv_last_error_message().decode()
+
+
+def kv_read_probe(d_base: int, d_slice_ids: int, n_slices: int, slice_bytes: int, blocks_per_cu: int, d_sink: int,
+                  stream: int) -> None:
+    _check(_lib.kv_read_probe(d_base, d_slice_ids, n_slices, slice_bytes, blocks_per_cu, d_sink, stream or None))
+
+
+def kv_trace_next_kernel(before: int, after: int) -> None:
+    """Raw hipEvent_t handles (0, 0 clears)."""
+    _check(_lib.kv_trace_next_kernel(before or None, after or None))
 
 
 def kv_profile_planes(profile: int, head_dim: int, scale_dtype: int | None = None) -> list:

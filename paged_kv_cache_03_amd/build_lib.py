@@ -24,7 +24,8 @@ INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 OUT = os.path.join(HERE, "libkvstore.so")
 BUILD = os.path.join(HERE, "_build")
 
-SOURCES = ["pool.cpp", "table_kernels.hip", "append.hip", "decode.hip", "qstream.hip", "stream_plan.hip", "verify.hip"]
+SOURCES = ["pool.cpp", "table_kernels.hip", "append.hip", "decode.hip", "qstream.hip", "stream_plan.hip", "verify.hip",
+           "read_probe.hip"]
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950", "-I", INCLUDE, "-I", CSRC,
           "-fhip-fp32-correctly-rounded-divide-sqrt", "-fno-gpu-flush-denormals-to-zero",

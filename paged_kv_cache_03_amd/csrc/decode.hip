@@ -668,31 +668,22 @@ __global__ void __launch_bounds__(64) decode_combine_kernel(DecodeArgs a) {
     for (int e = 0; e < EPL; ++e) o[e] = acc[e] * inv;
 }
 
-// Pages per split.  KVS_DECODE_CHUNK_PAGES overrides the default (a tuning
-// knob read once per process); the split only depends on logical positions.
-int chunk_pages() {
-    static const int cp = [] {
-        const char* e = std::getenv("KVS_DECODE_CHUNK_PAGES");
-        const int v = e ? std::atoi(e) : 0;
-        return (v >= 1 && v <= 1024) ? v : 8;
-    }();
-    return cp;
-}
+// Pages per split of the chunked split kernel (the shapes the page stream
+// does not take); the split depends only on logical positions.
+constexpr int kChunkPages = 8;
+int chunk_pages() { return kChunkPages; }
 
-// Blocks of the page-stream kernel: bpc per compute unit (the BF16 stream's
-// LDS ring takes most of the 160 KiB: one; the quantized stream runs two
-// half-size blocks where its registers allow), every one streaming the same
-// share of pages; more when a share would exceed the kStreamPages / bpc
-// pages a block lists in LDS.
+// Blocks of the page stream: bpc per compute unit (two for the BF16 stream,
+// whose pages go straight into registers; the quantized stream runs one or
+// two by its register needs), every one streaming the same share of pages;
+// more when a share would exceed the kStreamPages / bpc pages a block lists.
 int stream_grid(const PoolView& pv, int B, int max_seq_len, int bpc = 1) {
     static const int cus = [] {
         int dev = 0, n = 0;
         if (hipGetDevice(&dev) != hipSuccess ||
             hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
             n = 256;
-        const char* e = std::getenv("KVS_DECODE_STREAM_BLOCKS");
-        const int v = e ? std::atoi(e) : 0;
-        return (v >= 1 && v <= 4096) ? v : n;
+        return n;
     }();
     const int per_block = kStreamPages / bpc;
     const long long need = (stream_bound(pv, B, max_seq_len) + per_block - 1) / per_block;
@@ -702,16 +693,6 @@ int stream_grid(const PoolView& pv, int B, int max_seq_len, int bpc = 1) {
 // blocks per compute unit of the page stream for these pages
 int stream_bpc(const PoolView& pv) {
     return pv.k_codec != CODEC_BF16 ? qstream_blocks_per_cu(pv) : 2;
-}
-
-// Shared pages are read once per call unless KVS_STREAM_SHARE=0 (a tuning
-// knob read once per process, for measuring what the sharing saves).
-bool stream_share() {
-    static const bool on = [] {
-        const char* e = std::getenv("KVS_STREAM_SHARE");
-        return !(e && e[0] == '0');
-    }();
-    return on;
 }
 
 // The matrix-core page stream covers BF16 pages with D in {64, 128}, up to
@@ -789,7 +770,9 @@ hipError_t launch_gq(const DecodeArgs& a, bool stream, hipStream_t s) {
     if (stream && a.pv.k_codec != CODEC_BF16) return launch_qstream(a, GQ, s);
     if constexpr (D == 64 || D == 128) {
         if (stream) {
+            trace_before(s);
             paged_vstream_kernel<D, GQ, 1, false><<<dim3(unsigned(a.G)), 256, 0, s>>>(a);
+            trace_after(s);
             const hipError_t e = hipGetLastError();
             if (e != hipSuccess) return e;
             DecodeArgs c = a;
@@ -803,6 +786,7 @@ hipError_t launch_gq(const DecodeArgs& a, bool stream, hipStream_t s) {
     const int kc = a.pv.k_codec, vc = a.pv.v_codec;
     bool launched = false;
     const bool s16 = a.pv.scale16 != 0;
+    trace_before(s);
 #define KVS_DEC_CASE(K, V, SB)                                                       \
     if (!launched && kc == K && vc == V && s16 == (SB == 2)) {                      \
         if (items > 0) decode_split_kernel<D, GQ, K, V, SB><<<grid, 256, 0, s>>>(a); \
@@ -817,6 +801,7 @@ hipError_t launch_gq(const DecodeArgs& a, bool stream, hipStream_t s) {
     KVS_DEC_CASE(CODEC_FP8_ROW, CODEC_FP8_ROW, 2)
     KVS_DEC_CASE(CODEC_FP8_ROW, CODEC_NVFP4_G16, 2)
 #undef KVS_DEC_CASE
+    trace_after(s);
     if (!launched) return hipErrorNotSupported;
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -836,7 +821,7 @@ hipError_t launch_d(const DecodeArgs& a, int gq, bool stream, hipStream_t s) {
 }
 
 template <int D>
-hipError_t launch_chunk_d(const DecodeArgs& a, int gq, int G, hipStream_t s) {
+hipError_t launch_chunk_d(const DecodeArgs& a, int gq, int G, bool trace, hipStream_t s) {
     const dim3 grid(static_cast<unsigned>(G));
     DecodeArgs c = a;
     c.cgroups = combine_groups(32, D);
@@ -844,7 +829,9 @@ hipError_t launch_chunk_d(const DecodeArgs& a, int gq, int G, hipStream_t s) {
     switch (gq) {
 #define KVS_CHUNK_CASE(GQ)                                                  \
     case GQ:                                                                \
+        if (trace) trace_before(s);                                         \
         paged_vstream_kernel<D, GQ, 2, true><<<grid, 256, 0, s>>>(a);      \
+        if (trace) trace_after(s);                                          \
         if (hipPeekAtLastError() == hipSuccess)                             \
             stream_combine_kernel<D, GQ, 32><<<cgrid, 64, 0, s>>>(c);       \
         break;
@@ -880,8 +867,8 @@ hipError_t launch_decode_plan(const PoolView& pv, int B, int Hq, const int32_t* 
     const int gq = Hq / pv.H;
     const WsLayout l = ws_layout(pv, B, gq, max_seq_len, false);
     int32_t* planp = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + l.plan);
-    return launch_stream_plan(pv, B, gq, table_rows, seq_lens, nullptr, nullptr, max_seq_len, 0, false,
-                              l.stream && stream_share(), l.stream, l.G, l.qcap, planp, s);
+    return launch_stream_plan(pv, B, gq, table_rows, seq_lens, nullptr, nullptr, max_seq_len, 0, false, l.stream,
+                              l.stream, l.G, l.qcap, planp, s);
 }
 
 bool decode_append_supported(const PoolView& pv, int B, int Hq) {
@@ -917,7 +904,7 @@ size_t stream_chunk_workspace_bytes(const PoolView& pv, int B, int Hq, int max_s
 
 hipError_t launch_stream_chunk(const PoolView& pv, int B, int Hq, const int32_t* table_rows, const int32_t* q_pos0,
                                const int32_t* cu_q, int max_seq_len, const void* q, float sm_scale, float* out,
-                               void* ws, int max_cols, hipStream_t s) {
+                               void* ws, int max_cols, bool trace, hipStream_t s) {
     const int gq = Hq / pv.H;
     const WsLayout l = ws_layout(pv, B, gq, max_seq_len, true);
     int32_t* planp = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + l.plan);
@@ -926,8 +913,8 @@ hipError_t launch_stream_chunk(const PoolView& pv, int B, int Hq, const int32_t*
     if (e != hipSuccess) return e;
     const DecodeArgs a = run_args(pv, l, B, Hq, max_seq_len, q, sm_scale, out, ws);
     switch (pv.D) {
-        case 64: return launch_chunk_d<64>(a, gq, l.G, s);
-        case 128: return launch_chunk_d<128>(a, gq, l.G, s);
+        case 64: return launch_chunk_d<64>(a, gq, l.G, trace, s);
+        case 128: return launch_chunk_d<128>(a, gq, l.G, trace, s);
     }
     return hipErrorNotSupported;
 }

@@ -45,6 +45,13 @@ struct PoolView {
     int32_t sh;
 };
 
+// Measurement hook (kv_trace_next_kernel): the events a caller asked to have
+// recorded around the dominant kernel of its next attention call on this
+// thread.  trace_before records the first event on the stream; trace_after
+// records the second and forgets both.  No-ops when nothing is set.
+void trace_before(hipStream_t s);
+void trace_after(hipStream_t s);
+
 // Launchers (defined in the .hip files).  Each returns hipSuccess or the
 // first launch error; argument validation happens in pool.cpp.
 hipError_t launch_table_fill(int32_t* d_table, int32_t n, int32_t value, hipStream_t s);
@@ -106,14 +113,21 @@ hipError_t launch_decode(const PoolView& pv, int B, int Hq, const int32_t* table
 // layout matches decode's (arrival counters first, then the plan).
 bool stream_chunk_supported(const PoolView& pv, int B, int gq);
 size_t stream_chunk_workspace_bytes(const PoolView& pv, int B, int Hq, int max_seq_len);
+// trace: the chunk stream is the call's dominant kernel (no tiles follow it).
 hipError_t launch_stream_chunk(const PoolView& pv, int B, int Hq, const int32_t* table_rows, const int32_t* q_pos0,
                                const int32_t* cu_q, int max_seq_len, const void* q, float sm_scale, float* out,
-                               void* ws, int max_cols, hipStream_t s);
+                               void* ws, int max_cols, bool trace, hipStream_t s);
 
 bool verify_supported(const PoolView& pv, int Hq);
 size_t verify_workspace_bytes(const PoolView& pv, int B, int Hq, int max_seq_len, int max_q_len);
 hipError_t launch_verify(const PoolView& pv, int B, int Hq, const int32_t* table_rows, const int32_t* q_pos0,
                          const int32_t* cu_q, int total_q, int max_q_len, int max_seq_len, const void* q,
                          float sm_scale, float* out, void* ws, size_t ws_bytes, hipStream_t s);
+
+// Read-ceiling probe (read_probe.hip): n slices of slice_bytes at
+// base + ids[i] * slice_bytes, read once each by `blocks` blocks.
+int read_probe_blocks(int blocks_per_cu);
+hipError_t launch_read_probe(const void* base, const int32_t* ids, int n, int slice_bytes, int blocks,
+                             uint32_t* sink, hipStream_t s);
 
 }  // namespace kvs

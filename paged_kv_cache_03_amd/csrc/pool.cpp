@@ -33,6 +33,10 @@ namespace {
 
 thread_local std::string g_last_error;
 
+// events of kv_trace_next_kernel, for the next attention call on this thread
+thread_local hipEvent_t g_trace_before = nullptr;
+thread_local hipEvent_t g_trace_after = nullptr;
+
 kv_status fail(kv_status st, const std::string& msg) {
     g_last_error = msg;
     return st;
@@ -197,9 +201,43 @@ struct kv_pool {
     }
 };
 
+namespace kvs {
+
+void trace_before(hipStream_t s) {
+    if (g_trace_before) (void)hipEventRecord(g_trace_before, s);
+}
+
+void trace_after(hipStream_t s) {
+    if (g_trace_after) (void)hipEventRecord(g_trace_after, s);
+    g_trace_before = g_trace_after = nullptr;
+}
+
+}  // namespace kvs
+
 extern "C" {
 
 const char* kv_last_error_message(void) { return g_last_error.c_str(); }
+
+kv_status kv_read_probe(const void* d_base, const int32_t* d_slice_ids, uint32_t n_slices, uint32_t slice_bytes,
+                        uint32_t blocks_per_cu, uint32_t* d_sink, hipStream_t stream) {
+    if (!d_base || !d_slice_ids || !d_sink) return fail(KV_E_INVALID, "null device pointer");
+    if (slice_bytes != 8192 && slice_bytes != 16384 && slice_bytes != 32768)
+        return fail(KV_E_INVALID, "slice_bytes must be 8192, 16384 or 32768");
+    if (blocks_per_cu < 1 || blocks_per_cu > 8) return fail(KV_E_INVALID, "blocks_per_cu must be 1..8");
+    if (n_slices == 0) return ok();
+    if (n_slices > (1u << 30)) return fail(KV_E_INVALID, "too many slices");
+    const hipError_t e = launch_read_probe(d_base, d_slice_ids, int(n_slices), int(slice_bytes),
+                                           read_probe_blocks(int(blocks_per_cu)), d_sink, stream);
+    if (e != hipSuccess) return fail(KV_E_DEVICE, std::string("read probe: ") + hipGetErrorString(e));
+    return ok();
+}
+
+kv_status kv_trace_next_kernel(hipEvent_t before, hipEvent_t after) {
+    if ((before == nullptr) != (after == nullptr)) return fail(KV_E_INVALID, "before and after go together");
+    g_trace_before = before;
+    g_trace_after = after;
+    return ok();
+}
 
 kv_status kv_profile_planes(uint32_t profile, uint32_t head_dim, KVPlaneDesc* out, uint32_t* n_inout) {
     return kv_profile_planes_ex(profile, head_dim, KV_DT_F32, out, n_inout);
@@ -849,10 +887,15 @@ kv_status kv_decode_step_graph_create(const kv_pool* pool, uint32_t B, uint32_t 
         return fail(KV_E_INVALID, "layers, batch or pointer arrays");
     const bool append = d_k != nullptr;
     if (append != (d_v != nullptr)) return fail(KV_E_INVALID, "d_k and d_v go together");
-    // the append inside the run where the page stream takes it, else kv_append + run
-    const bool fused = append && total_tokens == B && decode_append_supported(pool->view(0), int(B), int(Hq));
-    if (append && !fused && (!d_pos0 || !d_cu_tokens))
-        return fail(KV_E_INVALID, "kv_append in the step needs d_pos0 and d_cu_tokens");
+    // which append form: without positions, one row per entry at seq_len - 1
+    // inside the run (the BF16 page stream); with them, kv_append + run
+    if ((d_pos0 == nullptr) != (d_cu_tokens == nullptr))
+        return fail(KV_E_INVALID, "d_pos0 and d_cu_tokens go together");
+    const bool fused = append && !d_pos0;
+    if (fused && (total_tokens != B || !decode_append_supported(pool->view(0), int(B), int(Hq))))
+        return fail(KV_E_UNSUPPORTED,
+                    "the append inside the run takes one row per entry on the BF16 page stream; "
+                    "pass d_pos0 and d_cu_tokens for kv_append");
 
     hipStream_t s = nullptr;
     if (hipStreamCreateWithFlags(&s, hipStreamNonBlocking) != hipSuccess)

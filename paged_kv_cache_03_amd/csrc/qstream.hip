@@ -590,6 +590,7 @@ template <int D, int KC, int VC>
 hipError_t launch_one(const DecodeArgs& a, int gq, hipStream_t s) {
     constexpr bool wide = KC == CODEC_INT8_G64 || KC == CODEC_FP8_ROW || VC == CODEC_INT8_G64 || VC == CODEC_FP8_ROW;
     bool launched = false;
+    trace_before(s);
     if constexpr (wide) {
         if (a.pv.scale16) {
             paged_qstream_kernel<D, KC, VC, 2><<<dim3(static_cast<unsigned>(a.G)), 256, 0, s>>>(a);
@@ -597,6 +598,7 @@ hipError_t launch_one(const DecodeArgs& a, int gq, hipStream_t s) {
         }
     }
     if (!launched) paged_qstream_kernel<D, KC, VC, 4><<<dim3(static_cast<unsigned>(a.G)), 256, 0, s>>>(a);
+    trace_after(s);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     DecodeArgs c = a;

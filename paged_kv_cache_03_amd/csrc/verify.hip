@@ -561,13 +561,15 @@ hipError_t launch_verify(const PoolView& pv, int B, int Hq, const int32_t* table
     a.max_ctx = max_seq_len;
     if (stream_chunk_supported(pv, B, gq)) {
         // short chunks: the page stream; long chunks: 128-column tiles
+        const bool tiles_follow = max_q_len * gq > kStreamCols;
         hipError_t e = launch_stream_chunk(pv, B, Hq, table_rows, q_pos0, cu_q, max_seq_len, q, sm_scale, out, ws,
-                                           kStreamCols, s);
+                                           kStreamCols, !tiles_follow, s);
         if (e != hipSuccess) return e;
         a.min_cols = kStreamCols;
-        if (max_q_len * gq <= kStreamCols) return hipSuccess;
+        if (!tiles_follow) return hipSuccess;
         const long long tiles = (long long)B * pv.H * ((max_q_len * gq + 127) / 128);
         const dim3 grid(unsigned((tiles + 7) / 8 * 8));   // 512 threads each
+        trace_before(s);
         switch (pv.D * 16 + gq) {
             case 64 * 16 + 1: verify_tile_kernel<64, 1><<<grid, 512, 0, s>>>(a); break;
             case 64 * 16 + 2: verify_tile_kernel<64, 2><<<grid, 512, 0, s>>>(a); break;
@@ -579,15 +581,19 @@ hipError_t launch_verify(const PoolView& pv, int B, int Hq, const int32_t* table
             case 128 * 16 + 8: verify_tile_kernel<128, 8><<<grid, 512, 0, s>>>(a); break;
             default: return hipErrorNotSupported;
         }
+        trace_after(s);
         return hipGetLastError();
     }
     a.min_cols = 0;
+    hipError_t e = hipErrorNotSupported;
+    trace_before(s);
     switch (pv.D) {
-        case 64: return launch_d<64>(a, gq, s);
-        case 128: return launch_d<128>(a, gq, s);
-        case 256: return launch_d<256>(a, gq, s);
+        case 64: e = launch_d<64>(a, gq, s); break;
+        case 128: e = launch_d<128>(a, gq, s); break;
+        case 256: e = launch_d<256>(a, gq, s); break;
     }
-    return hipErrorNotSupported;
+    trace_after(s);
+    return e;
 }
 
 }  // namespace kvs
