@@ -609,14 +609,16 @@ def bench_read_ceiling(args) -> int:
         for i in range(lists):
             launch(i)
         torch.cuda.synchronize()
-        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-              for _ in range(reps * lists)]
-        for i, (a, b) in enumerate(ev):
+        # back-to-back launches of all 32 lists between one event pair (an
+        # event pair around each launch would add its own packets' time)
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        for a, b in ev:
             a.record()
-            launch(i)
+            for i in range(lists):
+                launch(i)
             b.record()
         torch.cuda.synchronize()
-        ms = np.array([a.elapsed_time(b) for a, b in ev])
+        ms = np.array([a.elapsed_time(b) for a, b in ev]) / lists
         results[bpc] = {"mean_gbs": round(n * slice_bytes / (ms.mean() * 1e-3) / 1e9, 1),
                         "best_gbs": round(n * slice_bytes / (ms.min() * 1e-3) / 1e9, 1),
                         "mean_us": round(float(ms.mean()) * 1e3, 2)}

@@ -446,9 +446,9 @@ int paged_attn_supported(const kv_pool* pool, uint32_t Hq, uint32_t max_q_len);
 
 /* Measurement hook.  The next paged_attn_decode, paged_attn_decode_run,
  * paged_attn_decode_append_run or paged_attn_verify call made on this thread
- * records `before` on its stream immediately before the launch of its
- * dominant kernel and `after` immediately after that launch, then forgets
- * both.  The dominant kernel is the page stream of a decode (the split kernel
+ * attaches `before` and `after` to the dispatch of its dominant kernel
+ * (hipExtLaunchKernel: the events mark that kernel's start and end on its
+ * stream, with no packets of their own), then forgets both.  The dominant kernel is the page stream of a decode (the split kernel
  * where the stream does not apply) and, for a verify, the prefill tile kernel
  * when wide chunks are present, else the page stream in chunk mode (or the
  * per-token kernel).  The events are the caller's (hipEventCreate, timing

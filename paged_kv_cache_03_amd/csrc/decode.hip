@@ -29,6 +29,7 @@
 
 #include "attn_common.h"
 #include "internal.h"
+#include "launch.h"
 #include "kv_read.h"
 #include "stream_common.h"
 #include "stream_plan.h"
@@ -770,10 +771,8 @@ hipError_t launch_gq(const DecodeArgs& a, bool stream, hipStream_t s) {
     if (stream && a.pv.k_codec != CODEC_BF16) return launch_qstream(a, GQ, s);
     if constexpr (D == 64 || D == 128) {
         if (stream) {
-            trace_before(s);
-            paged_vstream_kernel<D, GQ, 1, false><<<dim3(unsigned(a.G)), 256, 0, s>>>(a);
-            trace_after(s);
-            const hipError_t e = hipGetLastError();
+            const hipError_t e =
+                launch_kernel(true, paged_vstream_kernel<D, GQ, 1, false>, dim3(unsigned(a.G)), dim3(256), s, a);
             if (e != hipSuccess) return e;
             DecodeArgs c = a;
             c.cgroups = combine_groups(GQ, D);
@@ -786,11 +785,10 @@ hipError_t launch_gq(const DecodeArgs& a, bool stream, hipStream_t s) {
     const int kc = a.pv.k_codec, vc = a.pv.v_codec;
     bool launched = false;
     const bool s16 = a.pv.scale16 != 0;
-    trace_before(s);
-#define KVS_DEC_CASE(K, V, SB)                                                       \
-    if (!launched && kc == K && vc == V && s16 == (SB == 2)) {                      \
-        if (items > 0) decode_split_kernel<D, GQ, K, V, SB><<<grid, 256, 0, s>>>(a); \
-        launched = true;                                                             \
+#define KVS_DEC_CASE(K, V, SB)                                                                       \
+    if (!launched && kc == K && vc == V && s16 == (SB == 2)) {                                      \
+        if (items > 0) (void)launch_kernel(true, decode_split_kernel<D, GQ, K, V, SB>, grid, dim3(256), s, a); \
+        launched = true;                                                                             \
     }
     KVS_DEC_CASE(CODEC_BF16, CODEC_BF16, 4)
     KVS_DEC_CASE(CODEC_INT8_G64, CODEC_INT8_G64, 4)
@@ -801,7 +799,6 @@ hipError_t launch_gq(const DecodeArgs& a, bool stream, hipStream_t s) {
     KVS_DEC_CASE(CODEC_FP8_ROW, CODEC_FP8_ROW, 2)
     KVS_DEC_CASE(CODEC_FP8_ROW, CODEC_NVFP4_G16, 2)
 #undef KVS_DEC_CASE
-    trace_after(s);
     if (!launched) return hipErrorNotSupported;
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -829,9 +826,7 @@ hipError_t launch_chunk_d(const DecodeArgs& a, int gq, int G, bool trace, hipStr
     switch (gq) {
 #define KVS_CHUNK_CASE(GQ)                                                  \
     case GQ:                                                                \
-        if (trace) trace_before(s);                                         \
-        paged_vstream_kernel<D, GQ, 2, true><<<grid, 256, 0, s>>>(a);      \
-        if (trace) trace_after(s);                                          \
+        (void)launch_kernel(trace, paged_vstream_kernel<D, GQ, 2, true>, grid, dim3(256), s, a); \
         if (hipPeekAtLastError() == hipSuccess)                             \
             stream_combine_kernel<D, GQ, 32><<<cgrid, 64, 0, s>>>(c);       \
         break;

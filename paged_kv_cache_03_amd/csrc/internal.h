@@ -47,10 +47,9 @@ struct PoolView {
 
 // Measurement hook (kv_trace_next_kernel): the events a caller asked to have
 // recorded around the dominant kernel of its next attention call on this
-// thread.  trace_before records the first event on the stream; trace_after
-// records the second and forgets both.  No-ops when nothing is set.
-void trace_before(hipStream_t s);
-void trace_after(hipStream_t s);
+// thread.  take_trace hands them out once (false when none are set); the
+// launcher attaches them to that kernel's dispatch (launch.h).
+bool take_trace(hipEvent_t* before, hipEvent_t* after);
 
 // Launchers (defined in the .hip files).  Each returns hipSuccess or the
 // first launch error; argument validation happens in pool.cpp.

@@ -203,13 +203,12 @@ struct kv_pool {
 
 namespace kvs {
 
-void trace_before(hipStream_t s) {
-    if (g_trace_before) (void)hipEventRecord(g_trace_before, s);
-}
-
-void trace_after(hipStream_t s) {
-    if (g_trace_after) (void)hipEventRecord(g_trace_after, s);
+bool take_trace(hipEvent_t* before, hipEvent_t* after) {
+    if (!g_trace_before) return false;
+    *before = g_trace_before;
+    *after = g_trace_after;
     g_trace_before = g_trace_after = nullptr;
+    return true;
 }
 
 }  // namespace kvs

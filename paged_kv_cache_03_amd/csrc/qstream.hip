@@ -40,6 +40,7 @@
 #include "attn_common.h"
 #include "decode_common.h"
 #include "internal.h"
+#include "launch.h"
 #include "stream_common.h"
 #include "stream_plan.h"
 
@@ -590,16 +591,16 @@ template <int D, int KC, int VC>
 hipError_t launch_one(const DecodeArgs& a, int gq, hipStream_t s) {
     constexpr bool wide = KC == CODEC_INT8_G64 || KC == CODEC_FP8_ROW || VC == CODEC_INT8_G64 || VC == CODEC_FP8_ROW;
     bool launched = false;
-    trace_before(s);
+    hipError_t e = hipSuccess;
     if constexpr (wide) {
         if (a.pv.scale16) {
-            paged_qstream_kernel<D, KC, VC, 2><<<dim3(static_cast<unsigned>(a.G)), 256, 0, s>>>(a);
+            e = launch_kernel(true, paged_qstream_kernel<D, KC, VC, 2>, dim3(static_cast<unsigned>(a.G)), dim3(256), s,
+                              a);
             launched = true;
         }
     }
-    if (!launched) paged_qstream_kernel<D, KC, VC, 4><<<dim3(static_cast<unsigned>(a.G)), 256, 0, s>>>(a);
-    trace_after(s);
-    const hipError_t e = hipGetLastError();
+    if (!launched)
+        e = launch_kernel(true, paged_qstream_kernel<D, KC, VC, 4>, dim3(static_cast<unsigned>(a.G)), dim3(256), s, a);
     if (e != hipSuccess) return e;
     DecodeArgs c = a;
     c.cgroups = combine_groups(gq, D);

@@ -9,20 +9,20 @@
 //
 // Work split as in the page stream: block i of G takes a contiguous share of
 // the slice list; each of its four waves takes every fourth slice of the
-// share.  A wave issues all of a slice's 16-byte loads before folding them,
-// so a slice of S bytes keeps S / 1024 loads per lane in flight.
+// share.  A wave keeps the loads of its next slice in flight while it folds
+// the current one: a slice of S bytes is S / 1024 16-byte loads per lane.
 
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
 
 #include "internal.h"
+#include "stream_common.h"
 
 namespace kvs {
 namespace {
 
 constexpr int kProbeWaves = 4;   // waves per block (256 threads)
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 struct ProbeArgs {
     const uint8_t* base;
@@ -36,17 +36,38 @@ struct ProbeArgs {
 template <int LOADS>
 __global__ __launch_bounds__(256) void read_probe_kernel(ProbeArgs a) {
     const int lane = int(threadIdx.x) & 63;
-    const int wave = int(threadIdx.x) >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(int(threadIdx.x) >> 6);
     const int first = int(blockIdx.x) * a.per_block;
     const int last = min(a.n, first + a.per_block);
-    uint32_t acc = 0;
-    for (int i = first + wave; i < last; i += kProbeWaves) {
-        const u32x4* p = reinterpret_cast<const u32x4*>(a.base + int64_t(a.ids[i]) * a.slice_bytes) + lane;
-        u32x4 r[LOADS];
+    // a slice past the block's share gets an empty range: its loads return
+    // zeros without touching memory, so every step issues the same loads and
+    // the compiler's wait counts stay exact (one slice in flight while the
+    // previous one is folded)
+    auto rsrc_of = [&](int i) __attribute__((always_inline)) {
+        const bool in = i < last;
+        const int64_t id = in ? int64_t(__builtin_amdgcn_readfirstlane(a.ids[i])) : 0;
+        return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(a.base) + id * a.slice_bytes, 0,
+                                                 in ? int(a.slice_bytes) : 0, kBufferWord3);
+    };
+    auto load = [&](u32x4 (&r)[LOADS], __amdgpu_buffer_rsrc_t rs) __attribute__((always_inline)) {
 #pragma unroll
-        for (int j = 0; j < LOADS; ++j) r[j] = __builtin_nontemporal_load(p + 64 * j);
+        for (int j = 0; j < LOADS; ++j)
+            r[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, 16 * lane + 1024 * j, 0,
+                                                                                   kNonTemporal));
+    };
+    uint32_t acc = 0;
+    auto fold = [&](const u32x4 (&r)[LOADS]) __attribute__((always_inline)) {
 #pragma unroll
         for (int j = 0; j < LOADS; ++j) acc ^= r[j].x ^ r[j].y ^ r[j].z ^ r[j].w;
+    };
+    u32x4 r0[LOADS], r1[LOADS];
+    int i = first + wave;
+    load(r0, rsrc_of(i));
+    for (; i < last; i += 2 * kProbeWaves) {
+        load(r1, rsrc_of(i + kProbeWaves));
+        fold(r0);
+        load(r0, rsrc_of(i + 2 * kProbeWaves));
+        fold(r1);
     }
     // fold the block's checksum so every load has a use
     __shared__ uint32_t red[256];

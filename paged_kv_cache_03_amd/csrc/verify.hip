@@ -22,6 +22,7 @@
 
 #include "attn_common.h"
 #include "internal.h"
+#include "launch.h"
 #include "kv_read.h"
 #include "stream_common.h"
 
@@ -515,10 +516,10 @@ template <int D>
 hipError_t launch_d(const VerifyArgs& a, int gq, hipStream_t s) {
     const dim3 grid(unsigned((a.total_q * a.pv.H + 3) / 4));
     switch (gq) {
-        case 1: verify_scalar_kernel<D, 1><<<grid, 256, 0, s>>>(a); break;
-        case 2: verify_scalar_kernel<D, 2><<<grid, 256, 0, s>>>(a); break;
-        case 4: verify_scalar_kernel<D, 4><<<grid, 256, 0, s>>>(a); break;
-        case 8: verify_scalar_kernel<D, 8><<<grid, 256, 0, s>>>(a); break;
+        case 1: return launch_kernel(true, verify_scalar_kernel<D, 1>, grid, dim3(256), s, a);
+        case 2: return launch_kernel(true, verify_scalar_kernel<D, 2>, grid, dim3(256), s, a);
+        case 4: return launch_kernel(true, verify_scalar_kernel<D, 4>, grid, dim3(256), s, a);
+        case 8: return launch_kernel(true, verify_scalar_kernel<D, 8>, grid, dim3(256), s, a);
         default: return hipErrorNotSupported;
     }
     return hipGetLastError();
@@ -569,31 +570,27 @@ hipError_t launch_verify(const PoolView& pv, int B, int Hq, const int32_t* table
         if (!tiles_follow) return hipSuccess;
         const long long tiles = (long long)B * pv.H * ((max_q_len * gq + 127) / 128);
         const dim3 grid(unsigned((tiles + 7) / 8 * 8));   // 512 threads each
-        trace_before(s);
+        e = hipErrorNotSupported;
         switch (pv.D * 16 + gq) {
-            case 64 * 16 + 1: verify_tile_kernel<64, 1><<<grid, 512, 0, s>>>(a); break;
-            case 64 * 16 + 2: verify_tile_kernel<64, 2><<<grid, 512, 0, s>>>(a); break;
-            case 64 * 16 + 4: verify_tile_kernel<64, 4><<<grid, 512, 0, s>>>(a); break;
-            case 64 * 16 + 8: verify_tile_kernel<64, 8><<<grid, 512, 0, s>>>(a); break;
-            case 128 * 16 + 1: verify_tile_kernel<128, 1><<<grid, 512, 0, s>>>(a); break;
-            case 128 * 16 + 2: verify_tile_kernel<128, 2><<<grid, 512, 0, s>>>(a); break;
-            case 128 * 16 + 4: verify_tile_kernel<128, 4><<<grid, 512, 0, s>>>(a); break;
-            case 128 * 16 + 8: verify_tile_kernel<128, 8><<<grid, 512, 0, s>>>(a); break;
+            case 64 * 16 + 1: e = launch_kernel(true, verify_tile_kernel<64, 1>, grid, dim3(512), s, a); break;
+            case 64 * 16 + 2: e = launch_kernel(true, verify_tile_kernel<64, 2>, grid, dim3(512), s, a); break;
+            case 64 * 16 + 4: e = launch_kernel(true, verify_tile_kernel<64, 4>, grid, dim3(512), s, a); break;
+            case 64 * 16 + 8: e = launch_kernel(true, verify_tile_kernel<64, 8>, grid, dim3(512), s, a); break;
+            case 128 * 16 + 1: e = launch_kernel(true, verify_tile_kernel<128, 1>, grid, dim3(512), s, a); break;
+            case 128 * 16 + 2: e = launch_kernel(true, verify_tile_kernel<128, 2>, grid, dim3(512), s, a); break;
+            case 128 * 16 + 4: e = launch_kernel(true, verify_tile_kernel<128, 4>, grid, dim3(512), s, a); break;
+            case 128 * 16 + 8: e = launch_kernel(true, verify_tile_kernel<128, 8>, grid, dim3(512), s, a); break;
             default: return hipErrorNotSupported;
         }
-        trace_after(s);
-        return hipGetLastError();
+        return e;
     }
     a.min_cols = 0;
-    hipError_t e = hipErrorNotSupported;
-    trace_before(s);
     switch (pv.D) {
-        case 64: e = launch_d<64>(a, gq, s); break;
-        case 128: e = launch_d<128>(a, gq, s); break;
-        case 256: e = launch_d<256>(a, gq, s); break;
+        case 64: return launch_d<64>(a, gq, s);
+        case 128: return launch_d<128>(a, gq, s);
+        case 256: return launch_d<256>(a, gq, s);
     }
-    trace_after(s);
-    return e;
+    return hipErrorNotSupported;
 }
 
 }  // namespace kvs

@@ -11,7 +11,11 @@ decide the output bits.  Checked on the BF16, INT8-G64 and K8V4 streams:
 * plane order (PagedKVStorageLayout passage: the head-major order differs
   only in strides) -- a head-major pool gives bitwise-equal outputs;
 * sharing (fork passage) -- the same histories in private pages take another
-  split (shared pages are read once for every sharer), equal within 1e-5;
+  split (shared pages are read once for every sharer): the sums run in
+  another order, with other running maxima, so the two agree to rounding of
+  the value terms: within 1e-5 x max(1, max|v|), max|v| the largest
+  dequantized value (about 5 for N(0,1) values, about 90 with the INT8
+  workload's 1% of outliers x20);
 * the fp64 oracle over every output, within 2e-3.
 """
 
@@ -19,7 +23,7 @@ import numpy as np
 import pytest
 
 import workloads
-from tests.drivers import build_device, device_decode, oracle_decode_all, say
+from tests.drivers import build_device, device_decode, oracle_decode_all, oracle_logical, say
 
 pytestmark = pytest.mark.gpu
 
@@ -61,8 +65,9 @@ def test_decode_invariances_with_many_pages_per_block(profile, gq, D, H):
     private = device_decode(dp, wl, 0)
     dp.close()
     d = float(np.max(np.abs(private - outs[0])))
-    say(f"  private copies: max abs difference {d:.3g}")
-    assert d <= 1e-5
+    vmax = max(float(np.max(np.abs(oracle_logical(wl, 0, b, wl.seq_lens[b])[1]))) for b in range(wl.B))
+    say(f"  private copies: max abs difference {d:.3g} (max|v| {vmax:.3g})")
+    assert d <= 1e-5 * max(1.0, vmax)
     ref = oracle_decode_all(wl, 0)
     err = float(np.max(np.abs(outs[0] - ref)))
     say(f"  oracle: max abs err {err:.3g}")
