@@ -342,6 +342,23 @@ kv_status paged_attn_decode(const kv_pool* pool, uint32_t layer, uint32_t B, uin
                             const void* d_q, float sm_scale, float* d_out, void* d_ws, size_t ws_bytes,
                             hipStream_t stream);
 
+/* paged_attn_decode for callers that cannot allocate device memory or bring
+ * a workspace: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc.  The same plan and run as paged_attn_decode, with
+ * the library's own static device scratch (KV_DECODE_SCRATCH_BYTES per GPU,
+ * a file-scope device array that each GPU the library runs on holds until
+ * the process ends) in place of d_ws.  Calls no allocator.  The scratch
+ * needs no clearing (every call writes what it reads), but every call on
+ * one GPU shares it: calls that overlap in time on one GPU (other streams,
+ * other threads, other graphs) race, and the caller serializes them.
+ * KV_E_INVALID when paged_attn_workspace_bytes(pool, B, Hq, max_seq_len, 0)
+ * exceeds KV_DECODE_SCRATCH_BYTES (use paged_attn_decode then); other errors
+ * and results exactly as paged_attn_decode. */
+#define KV_DECODE_SCRATCH_BYTES (32u << 20)
+kv_status paged_attn_decode_noalloc(const kv_pool* pool, uint32_t layer, uint32_t B, uint32_t Hq,
+                                    const int32_t* d_table_rows, const int32_t* d_seq_lens, uint32_t max_seq_len,
+                                    const void* d_q, float sm_scale, float* d_out, hipStream_t stream);
+
 /* Decode split in two, for callers that run the same batch state over many
  * layers (consumer rules: the op chooses its own split; the work list depends
  * only on the block table and the lengths, which a step keeps for all

@@ -23,6 +23,7 @@ KV_PROFILE = {"BF16": 0, "INT8_G64": 1, "FP8_E4M3FN_ROW256": 2, "NVFP4_G16": 3, 
 KV_DT_BF16, KV_DT_I8, KV_DT_E4M3FN, KV_DT_E2M1X2, KV_DT_F32, KV_DT_U8_E4M3, KV_DT_F16 = range(7)
 KV_ROLE_K_CODE, KV_ROLE_K_SCALE, KV_ROLE_V_CODE, KV_ROLE_V_SCALE = range(4)
 KV_LAYOUT_PAGE_MAJOR, KV_LAYOUT_HEAD_MAJOR = range(2)
+KV_DECODE_SCRATCH_BYTES = 32 << 20      # the static scratch of paged_attn_decode_noalloc
 
 # exported symbols, in header order (the CPU test checks the header declares exactly these)
 EXPORTS = ["kv_profile_planes", "kv_profile_planes_ex", "kv_plane_bytes", "kv_pool_create", "kv_pool_destroy", "kv_pool_stats",
@@ -30,7 +31,7 @@ EXPORTS = ["kv_profile_planes", "kv_profile_planes_ex", "kv_plane_bytes", "kv_po
            "kv_seq_commit", "kv_seq_release", "kv_seq_reserve", "kv_seq_trim", "kv_seq_commit_accepted",
            "kv_seq_reservation", "kv_draft_pool_pages", "kv_replica_page_bytes", "kv_seq_offload",
            "kv_seq_restore", "kv_seq_info", "kv_cow_tail_page", "kv_append",
-           "paged_attn_workspace_bytes", "paged_attn_decode", "paged_attn_decode_plan", "paged_attn_decode_run",
+           "paged_attn_workspace_bytes", "paged_attn_decode", "paged_attn_decode_noalloc", "paged_attn_decode_plan", "paged_attn_decode_run",
            "paged_attn_decode_append_run",
            "paged_attn_verify", "kv_decode_step_graph_create", "kv_step_graph_launch", "kv_step_graph_destroy",
            "paged_attn_supported", "kv_trace_next_kernel", "kv_read_probe",
@@ -96,6 +97,7 @@ def _load():
         "kv_append": (i32, [vp, u32, u32, vp, vp, vp, u32, vp, vp, vp]),
         "paged_attn_workspace_bytes": (sz, [vp, u32, u32, u32, u32]),
         "paged_attn_decode": (i32, [vp, u32, u32, u32, vp, vp, u32, vp, ctypes.c_float, vp, vp, sz, vp]),
+        "paged_attn_decode_noalloc": (i32, [vp, u32, u32, u32, vp, vp, u32, vp, ctypes.c_float, vp, vp]),
         "paged_attn_decode_plan": (i32, [vp, u32, u32, vp, vp, u32, vp, sz, vp]),
         "paged_attn_decode_run": (i32, [vp, u32, u32, u32, u32, vp, ctypes.c_float, vp, vp, sz, vp]),
         "paged_attn_decode_append_run": (i32, [vp, u32, u32, u32, u32, vp, vp, vp, ctypes.c_float, vp, vp, sz, vp]),
@@ -292,6 +294,12 @@ def paged_attn_decode(pool: int, layer: int, B: int, Hq: int, d_table_rows: int,
                       stream: int = 0) -> None:
     _check(_lib.paged_attn_decode(pool, layer, B, Hq, d_table_rows, d_seq_lens, max_seq_len, d_q, sm_scale, d_out,
                                   d_ws or None, ws_bytes, stream or None))
+
+
+def paged_attn_decode_noalloc(pool: int, layer: int, B: int, Hq: int, d_table_rows: int, d_seq_lens: int,
+                              max_seq_len: int, d_q: int, sm_scale: float, d_out: int, stream: int = 0) -> None:
+    _check(_lib.paged_attn_decode_noalloc(pool, layer, B, Hq, d_table_rows, d_seq_lens, max_seq_len, d_q, sm_scale,
+                                          d_out, stream or None))
 
 
 def paged_attn_decode_plan(pool: int, B: int, Hq: int, d_table_rows: int, d_seq_lens: int, max_seq_len: int,

@@ -21,9 +21,12 @@
 #include <cmath>
 #include <cstring>
 #include <deque>
+#include <mutex>
 #include <new>
 #include <string>
 #include <vector>
+
+#include <hip/hip_runtime.h>
 
 #include "internal.h"
 
@@ -785,6 +788,64 @@ kv_status paged_attn_decode(const kv_pool* pool, uint32_t layer, uint32_t B, uin
                                  sm_scale, d_out, d_ws, stream);
     if (e != hipSuccess) return fail(KV_E_DEVICE, std::string("decode launch: ") + hipGetErrorString(e));
     return ok();
+}
+
+}  // extern "C"
+
+// ------------------------------------------------- decode without a workspace --
+// The scratch of paged_attn_decode_noalloc: a file-scope device array, one
+// copy per GPU the library runs on, held until the process ends.  In host
+// code `scratch` names a host-side stand-in, never the device memory: host
+// code uses only the address hipGetSymbolAddress returns for the current
+// device, kept per device.
+static __device__ __align__(256) unsigned char scratch[KV_DECODE_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxScratchDevices] = {};
+
+// The current device's copy of `scratch`, looked up once per device.
+kv_status scratch_of_current_device(void** out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxScratchDevices)
+        return fail(KV_E_DEVICE, "no current device for the decode scratch");
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p)
+            return fail(KV_E_DEVICE, std::string("decode scratch address: ") + hipGetErrorString(e));
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return KV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+kv_status paged_attn_decode_noalloc(const kv_pool* pool, uint32_t layer, uint32_t B, uint32_t Hq,
+                                    const int32_t* d_table_rows, const int32_t* d_seq_lens, uint32_t max_seq_len,
+                                    const void* d_q, float sm_scale, float* d_out, hipStream_t stream) {
+    kv_status st = check_compute(pool, layer, B);
+    if (st != KV_OK) return st;
+    if (Hq == 0 || Hq % pool->geo.num_kv_heads) return fail(KV_E_GEOMETRY, "Hq must be a multiple of H");
+    if (B == 0) return ok();
+    if (max_seq_len > pool->geo.max_context) return fail(KV_E_INVALID, "max_seq_len beyond max_context");
+    const size_t need = decode_workspace_bytes(pool->view(layer), int(B), int(Hq), int(max_seq_len));
+    if (need > size_t(KV_DECODE_SCRATCH_BYTES))
+        return fail(KV_E_INVALID, "this decode needs a workspace of " + std::to_string(need) +
+                                      " bytes, more than the static scratch of " +
+                                      std::to_string(size_t(KV_DECODE_SCRATCH_BYTES)) +
+                                      " bytes: use paged_attn_decode with a workspace");
+    void* ws = nullptr;
+    st = scratch_of_current_device(&ws);
+    if (st != KV_OK) return st;
+    return paged_attn_decode(pool, layer, B, Hq, d_table_rows, d_seq_lens, max_seq_len, d_q, sm_scale, d_out, ws,
+                             size_t(KV_DECODE_SCRATCH_BYTES), stream);
 }
 
 kv_status paged_attn_decode_plan(const kv_pool* pool, uint32_t B, uint32_t Hq, const int32_t* d_table_rows,

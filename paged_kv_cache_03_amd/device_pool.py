@@ -158,6 +158,12 @@ class DevicePool:
         abi.paged_attn_decode(self.handle, layer, table_rows.numel(), Hq, ptr(table_rows), ptr(seq_lens),
                               max_seq_len, ptr(q), sm_scale, ptr(out), ptr(ws), ws.numel(), self.stream)
 
+    def decode_noalloc(self, layer: int, Hq: int, table_rows: torch.Tensor, seq_lens: torch.Tensor,
+                       max_seq_len: int, q: torch.Tensor, sm_scale: float, out: torch.Tensor) -> None:
+        """decode on the library's static scratch (no workspace)."""
+        abi.paged_attn_decode_noalloc(self.handle, layer, table_rows.numel(), Hq, ptr(table_rows), ptr(seq_lens),
+                                      max_seq_len, ptr(q), sm_scale, ptr(out), self.stream)
+
     def decode_plan(self, Hq: int, table_rows: torch.Tensor, seq_lens: torch.Tensor, max_seq_len: int,
                     ws: torch.Tensor) -> None:
         """Work list of this batch state into ws (valid for every layer until the rows or lengths change)."""
