@@ -134,7 +134,7 @@ def decode_kernel_name(wl) -> str:
     """The kernel that carries paged_attn_decode for this workload (as rocprofv3 names it)."""
     gq = wl.Hq // wl.H
     if gq in (1, 2, 4, 8) and wl.B <= 8:
-        if wl.profile == "BF16" and wl.D in (64, 128):
+        if wl.profile == "BF16" and wl.D in (64, 128, 256):
             return f"paged_vstream_kernel<{wl.D}, {gq}, 1, false>"
         # codec numbers of the page-stream instances: INT8-G64 1, FP8-row 2, NVFP4-G16 3
         sides = {"INT8_G64": (1, 1), "FP8_E4M3FN_ROW256": (2, 2), "NVFP4_G16": (3, 3), "K8V4": (2, 3)}
@@ -677,7 +677,7 @@ def bench_advance(wl, args) -> int:
     qs = [_dev(wl.q(layer), dev) for layer in range(wl.layers)]
     out = torch.empty((wl.B, wl.Hq, wl.D), dtype=torch.float32, device=dev)
     ws = dp.workspace(wl.B, wl.Hq, bound)
-    fused = wl.profile == "BF16" and wl.D in (64, 128)
+    fused = wl.profile == "BF16" and wl.D in (64, 128, 256)
     host_s = [0.0]
     crossings = [0]
 
@@ -738,7 +738,8 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", type=int, default=2, help="workload number (1-4: decode, 5: verify/prefill)")
+    ap.add_argument("--config", type=int, default=2,
+                    help="workload number (1-4: decode, 5: verify/prefill; 6, 7: BF16 at head_dim 256)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--scale-bytes", type=int, choices=(2, 4), default=4,
                     help="INT8-G64 / FP8-row scale planes: 4 (fp32) or 2 (binary16, the page's D256 byte table)")
@@ -813,7 +814,7 @@ def main() -> int:
     # block table and the lengths), then per layer the append of the step's
     # rows and the decode run -- one launch on the BF16 page stream, which
     # appends the rows itself
-    fused = wl.profile == "BF16" and wl.D in (64, 128)
+    fused = wl.profile == "BF16" and wl.D in (64, 128, 256)
 
     def step(events=None, kern=None):
         dp.decode_plan(wl.Hq, rows_t, lens_t, max_ctx, ws)

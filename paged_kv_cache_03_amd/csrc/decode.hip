@@ -174,9 +174,9 @@ __global__ void __launch_bounds__(256) decode_split_kernel(DecodeArgs a) {
 // block order: deterministic output.  Both the block index and sigma only
 // grow along the stream, so no two (block, unit) pieces share a slot.
 template <int D, int GQ, int NCT, bool CHUNK>
-__global__ void __launch_bounds__(256, 2) paged_vstream_kernel(DecodeArgs a) {
+__global__ void __launch_bounds__(256, vstream_bpc(D)) paged_vstream_kernel(DecodeArgs a) {
     using namespace plan;
-    constexpr int BPC = 2;                         // blocks per compute unit
+    constexpr int BPC = vstream_bpc(D);            // blocks per compute unit
     constexpr int NCH = D / 8;                     // 16-byte chunks per bf16 row
     constexpr int NT = 256;
     constexpr int NC = D / 32;                     // QK products, k = 32 each
@@ -187,9 +187,9 @@ __global__ void __launch_bounds__(256, 2) paged_vstream_kernel(DecodeArgs a) {
     constexpr int QCHUNKS = 1024 / BPC;            // query cache: 16-byte chunks
     constexpr int QSEG = QCHUNKS / (NCOL * NCH);   // units with cached queries
     constexpr int PAGES = kStreamPages / BPC;      // most pages a block takes
-    constexpr int PF = 2;                          // page buffers per wave: the next page is in flight
+    constexpr int PF = vstream_buffers(D);         // page buffers per wave: PF - 1 pages in flight
     constexpr size_t SLICE = size_t(64) * D * 2;   // bytes of one plane's page slice
-    static_assert((D == 64 || D == 128) && GQ >= 1 && GQ <= 16 && GQ <= NCOL, "shape");
+    static_assert((D == 64 || D == 128 || (D == 256 && !CHUNK)) && GQ >= 1 && GQ <= 16 && GQ <= NCOL, "shape");
     static_assert(QSEG >= 1 && QSEG * NCOL * NCH == QCHUNKS && QCHUNKS % NT == 0, "query cache shape");
     static_assert(PAGES % NT == 0, "page list");
     typedef unsigned int vrow_t __attribute__((ext_vector_type(VW)));
@@ -309,10 +309,15 @@ __global__ void __launch_bounds__(256, 2) paged_vstream_kernel(DecodeArgs a) {
             kb[c] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, krow + 64 * c, 0, kNonTemporal));
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            if constexpr (VW == 4)
+            if constexpr (VW == 8) {
+                const u32x4 v0 = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rv, vrow + r * 2 * D, 0, kNonTemporal));
+                const u32x4 v1 = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rv, vrow + r * 2 * D + 16, 0, kNonTemporal));
+                vb[r] = vrow_t{v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+            } else if constexpr (VW == 4) {
                 vb[r] = __builtin_bit_cast(vrow_t, __builtin_amdgcn_raw_buffer_load_b128(rv, vrow + r * 2 * D, 0, kNonTemporal));
-            else
+            } else {
                 vb[r] = __builtin_bit_cast(vrow_t, __builtin_amdgcn_raw_buffer_load_b64(rv, vrow + r * 2 * D, 0, kNonTemporal));
+            }
         }
     };
 
@@ -693,7 +698,7 @@ int stream_grid(const PoolView& pv, int B, int max_seq_len, int bpc = 1) {
 
 // blocks per compute unit of the page stream for these pages
 int stream_bpc(const PoolView& pv) {
-    return pv.k_codec != CODEC_BF16 ? qstream_blocks_per_cu(pv) : 2;
+    return pv.k_codec != CODEC_BF16 ? qstream_blocks_per_cu(pv) : vstream_bpc(pv.D);
 }
 
 // The matrix-core page stream covers BF16 pages with D in {64, 128}, up to
@@ -701,10 +706,14 @@ int stream_bpc(const PoolView& pv) {
 // page index shares a word with the page's flags), and at most 4096 blocks;
 // everything else takes the chunked split kernel.
 bool stream_path(const PoolView& pv, int B, int gq) {
-    return pv.k_codec == CODEC_BF16 && pv.v_codec == CODEC_BF16 && (pv.D == 64 || pv.D == 128) && B <= 8 &&
-           pv.H <= plan::kMaxH && pv.L <= 32768 && (long long)B * pv.H * pv.L <= 4096LL * (kStreamPages / 2) &&
+    return pv.k_codec == CODEC_BF16 && pv.v_codec == CODEC_BF16 && (pv.D == 64 || pv.D == 128 || pv.D == 256) &&
+           B <= 8 && pv.H <= plan::kMaxH && pv.L <= 32768 &&
+           (long long)B * pv.H * pv.L <= 4096LL * (kStreamPages / vstream_bpc(pv.D)) &&
            (gq == 1 || gq == 2 || gq == 4 || gq == 8);
 }
+
+// chunk mode (several query tokens per entry) on the BF16 stream: D in {64, 128}
+bool chunk_path(const PoolView& pv, int B, int gq) { return stream_path(pv, B, gq) && pv.D <= 128; }
 
 int max_chunks_for(int max_seq_len) {
     const int pages = (max_seq_len + kPage - 1) / kPage;
@@ -769,7 +778,7 @@ DecodeArgs run_args(const PoolView& pv, const WsLayout& l, int B, int Hq, int ma
 template <int D, int GQ>
 hipError_t launch_gq(const DecodeArgs& a, bool stream, hipStream_t s) {
     if (stream && a.pv.k_codec != CODEC_BF16) return launch_qstream(a, GQ, s);
-    if constexpr (D == 64 || D == 128) {
+    {
         if (stream) {
             const hipError_t e =
                 launch_kernel(true, paged_vstream_kernel<D, GQ, 1, false>, dim3(unsigned(a.G)), dim3(256), s, a);
@@ -891,7 +900,7 @@ hipError_t launch_decode(const PoolView& pv, int B, int Hq, const int32_t* table
     return launch_decode_run(pv, B, Hq, max_seq_len, q, sm_scale, out, ws, s);
 }
 
-bool stream_chunk_supported(const PoolView& pv, int B, int gq) { return stream_path(pv, B, gq); }
+bool stream_chunk_supported(const PoolView& pv, int B, int gq) { return chunk_path(pv, B, gq); }
 
 size_t stream_chunk_workspace_bytes(const PoolView& pv, int B, int Hq, int max_seq_len) {
     return ws_layout(pv, B, Hq / pv.H, max_seq_len, true).total;

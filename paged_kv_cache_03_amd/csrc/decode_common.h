@@ -56,6 +56,13 @@ __device__ __forceinline__ void ring_round(F& step, int i0, int npg) {
     }
 }
 
+// The BF16 register-fed page stream: blocks of four waves per compute unit,
+// and page buffers per wave (buffers - 1 pages in flight while one is
+// computed).  At D = 256 a wave's page is twice the bytes and registers, so
+// one block per compute unit keeps two pages in flight per wave instead.
+constexpr int vstream_bpc(int D) { return D == 256 ? 1 : 2; }
+constexpr int vstream_buffers(int D) { return D == 256 ? 3 : 2; }
+
 // single-wave combine blocks per task: groups of 128 outputs of up to ncol columns
 constexpr int combine_groups(int ncol, int D) { return (ncol * D + 127) / 128; }
 

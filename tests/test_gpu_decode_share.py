@@ -45,7 +45,7 @@ def _decode_vs_oracle(wl, tag):
     return got
 
 
-@pytest.mark.parametrize("gq,D", [(4, 128), (8, 128), (1, 128), (2, 64), (4, 64)])
+@pytest.mark.parametrize("gq,D", [(4, 128), (8, 128), (1, 128), (2, 64), (4, 64), (4, 256), (2, 256)])
 def test_decode_fork_tree(gq, D):
     H = 2
     wl = workloads.small(110 + gq + D, "BF16", hist=TREE_HIST, fork=TREE_FORK, C=6, S=4096, Hq=H * gq, H=H, D=D)
@@ -155,7 +155,7 @@ def _append_run_case(wl, tag):
     dp_b.close()
 
 
-@pytest.mark.parametrize("gq,D", [(4, 128), (2, 64)])
+@pytest.mark.parametrize("gq,D", [(4, 128), (2, 64), (4, 256)])
 def test_decode_append_run_matches_append_then_run(gq, D):
     # forks with shared prefixes; new tokens at page starts, mid-page and page ends
     hist = [2000, 2000, 1500, 3000, 1000, 640]
@@ -165,10 +165,12 @@ def test_decode_append_run_matches_append_then_run(gq, D):
     _append_run_case(wl, f"gq={gq} D={D}")
 
 
-def test_decode_append_run_more_new_rows_than_staged():
+@pytest.mark.parametrize("D", [128, 256])
+def test_decode_append_run_more_new_rows_than_staged(D):
     # seven one-page entries and one long one: the first block's range holds
-    # nine new-token pages, more than the eight it stages (D = 128)
+    # nine new-token pages, more than it stages (eight rows at D = 128, four
+    # at D = 256)
     hist = [10, 63, 0, 40, 1, 62, 30, 66000]
-    wl = workloads.small(131, "BF16", hist=hist, C=8, S=66048, Hq=8, H=2, D=128)
+    wl = workloads.small(131, "BF16", hist=hist, C=8, S=66048, Hq=8, H=2, D=D)
     say("append in the run, more new rows than staged")
     _append_run_case(wl, "many new rows")

@@ -32,18 +32,19 @@ def _check(wl, tag, **kw):
     return dp, got
 
 
-def test_stream_block_crossing_many_segments():
+@pytest.mark.parametrize("D", [128, 256])
+def test_stream_block_crossing_many_segments(D):
     # one long entry and seven short ones: the block that reaches the short
     # entries crosses ~15 segments (past the partials kept in registers and
     # past the cached query rows)
     hist = [65000, 40, 10, 63, 64, 1, 100, 20]
-    wl = workloads.small(61, "BF16", hist=hist, C=8, S=65536, Hq=16, H=4, D=128, M=1100)
+    wl = workloads.small(61, "BF16", hist=hist, C=8, S=65536, Hq=16, H=4, D=D, M=1100)
     say(f"decode {wl.name} B={wl.B} H={wl.H}")
     dp, _ = _check(wl, "many segments")
     dp.close()
 
 
-@pytest.mark.parametrize("gq,D", [(8, 128), (8, 64), (4, 64), (1, 128), (2, 64)])
+@pytest.mark.parametrize("gq,D", [(8, 128), (8, 64), (4, 64), (1, 128), (2, 64), (4, 256), (1, 256), (8, 256)])
 def test_stream_shapes(gq, D):
     # planes start as 0xFF bytes (NaN bf16): rows past every frontier hold them
     H = 2

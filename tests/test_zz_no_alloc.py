@@ -56,16 +56,17 @@ def test_decode_noalloc_refuses_a_workspace_beyond_the_scratch():
     import torch
     from paged_kv_cache_03_amd import _abi as abi
     from paged_kv_cache_03_amd.device_pool import DevicePool, i32
-    # 64 KV heads x 8 entries at head_dim 256 over 32768-token contexts take
-    # the split kernel, whose partials exceed the scratch
-    dp = DevicePool("BF16", 64, 256, 1, 32768, 8, 512, zero=True)
-    need = abi._lib.paged_attn_workspace_bytes(dp.handle, 8, 128, 32768, 0)
+    # 72 KV heads (past the 64 the page stream's plan takes) x 8 entries at
+    # head_dim 256 over 32768-token contexts take the split kernel, whose
+    # partials exceed the scratch
+    dp = DevicePool("BF16", 72, 256, 1, 32768, 8, 512, zero=True)
+    need = abi._lib.paged_attn_workspace_bytes(dp.handle, 8, 144, 32768, 0)
     assert need > abi.KV_DECODE_SCRATCH_BYTES
     dev = dp.device
-    q = torch.zeros((8, 128, 256), dtype=torch.int16, device=dev)
-    out = torch.zeros((8, 128, 256), dtype=torch.float32, device=dev)
+    q = torch.zeros((8, 144, 256), dtype=torch.int16, device=dev)
+    out = torch.zeros((8, 144, 256), dtype=torch.float32, device=dev)
     with pytest.raises(abi.KVError) as ei:
-        dp.decode_noalloc(0, 128, i32(list(range(8)), dev), i32([0] * 8, dev), 32768, q, 0.0625, out)
+        dp.decode_noalloc(0, 144, i32(list(range(8)), dev), i32([0] * 8, dev), 32768, q, 0.0625, out)
     assert ei.value.status == abi.KV_E_INVALID and "scratch" in ei.value.message
     torch.cuda.synchronize()
     assert bool((out == 0).all())

@@ -15,6 +15,8 @@ Readings taken where the workload descriptions leave a choice open:
 * verify/prefill: n0 = 2039*64 + {35, 1, 63, 17}; sequences 0-1 verify 5
   tokens, 2-3 prefill a 512-token chunk.
 * one layer where the text gives no layer count.
+Two more measure BF16 pages at head_dim 256 (not among the named five): the
+K8V4 decode shapes, and the verify/prefill mix with 16 query / 2 KV heads.
 """
 
 from __future__ import annotations
@@ -211,12 +213,33 @@ def _cfg5() -> Workload:
                     cow=[False] * 4, mode="verify")
 
 
+def _cfg6() -> Workload:
+    # the K8V4 long-context shapes on BF16 pages (head_dim 256, the size the
+    # D256 payload table is written for): 65535-token histories, one token each
+    fork = [None] * 8
+    fork[1] = (0, 65535)
+    cow = [False] * 8
+    cow[1] = True
+    return Workload("bf16_d256_decode_c8_ctx64k", "BF16", C=8, S=65536, M=8 * 1024, layers=1, Hq=16, H=2,
+                    D=256, seed=1006, hist=[65535] * 8, step=[1] * 8, fork=fork, cow=cow)
+
+
+def _cfg7() -> Workload:
+    # the verify / prefill mix at head_dim 256 (16 query / 2 KV heads, as above)
+    n0 = [2039 * 64 + o for o in (35, 1, 63, 17)]
+    return Workload("bf16_d256_verify5_prefill512_c4_ctx128k", "BF16", C=4, S=131072, M=4 * 2048, layers=1,
+                    Hq=16, H=2, D=256, seed=1007, hist=n0, step=[5, 5, 512, 512], fork=[None] * 4,
+                    cow=[False] * 4, mode="verify")
+
+
 WORKLOADS = {
     1: _cfg1,
     2: lambda: _decode8(2, "BF16", 0.0, False),
     3: lambda: _decode8(3, "INT8_G64", 0.01, True),
     4: _cfg4,
     5: _cfg5,
+    6: _cfg6,
+    7: _cfg7,
 }
 
 
