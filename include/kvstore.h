@@ -411,8 +411,10 @@ kv_status paged_attn_decode_append_run(const kv_pool* pool, uint32_t layer, uint
  *   max_q_len, max_seq_len : host upper bounds (max T, max n0 + T).
  *   d_ws / ws_bytes : >= paged_attn_workspace_bytes(pool, B, Hq, max_seq_len,
  *   max_q_len).
- * KV_E_INVALID unless sm_scale is finite and > 0.  Profiles: BF16 only in
- * this library (KV_E_UNSUPPORTED otherwise). */
+ * KV_E_INVALID unless sm_scale is finite and > 0.  Every closed profile at
+ * D in {64, 128, 256} with Hq / H in {1, 2, 4, 8} (Paged KV Context Store
+ * page, pool sets: Main Text and MTP pages take the engine-selected
+ * profile); KV_E_UNSUPPORTED for other head groupings. */
 kv_status paged_attn_verify(const kv_pool* pool, uint32_t layer, uint32_t B, uint32_t Hq,
                             const int32_t* d_table_rows, const int32_t* d_q_pos0, const int32_t* d_cu_q,
                             uint32_t total_q, uint32_t max_q_len, uint32_t max_seq_len, const void* d_q,

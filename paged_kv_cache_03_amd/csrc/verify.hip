@@ -44,7 +44,7 @@ struct VerifyArgs {
     int32_t min_cols;   // entries with at most this many query columns (tokens x GQ) are left to the page stream
 };
 
-template <int D, int GQ>
+template <int D, int GQ, int KC, int VC, int SB>
 __global__ void __launch_bounds__(256) verify_scalar_kernel(VerifyArgs a) {
     constexpr int EPL = D / 64;
     __shared__ float q_s[4][GQ][D];
@@ -87,7 +87,7 @@ __global__ void __launch_bounds__(256) verify_scalar_kernel(VerifyArgs a) {
         if (valid) {
             for (int d0 = 0; d0 < D; d0 += 8) {
                 float kv[8];
-                KVRow<CODEC_BF16, D>::load8(a.pv.lv.k_code, nullptr, slab + lane, d0, kv);
+                KVRow<KC, D, SB>::load8(a.pv.lv.k_code, a.pv.lv.k_scale, slab + lane, d0, kv);
 #pragma unroll
                 for (int j = 0; j < GQ; ++j)
 #pragma unroll
@@ -112,7 +112,7 @@ __global__ void __launch_bounds__(256) verify_scalar_kernel(VerifyArgs a) {
             float v[EPL];
 #pragma unroll
             for (int e = 0; e < EPL; ++e)
-                v[e] = KVRow<CODEC_BF16, D>::load1(a.pv.lv.v_code, nullptr, slab + t, lane * EPL + e);
+                v[e] = KVRow<VC, D, SB>::load1(a.pv.lv.v_code, a.pv.lv.v_scale, slab + t, lane * EPL + e);
 #pragma unroll
             for (int j = 0; j < GQ; ++j) {
                 const float pj = p_s[wave][t][j];
@@ -512,17 +512,35 @@ __global__ void __launch_bounds__(512) verify_tile_kernel(VerifyArgs a) {
     }
 }
 
-template <int D>
-hipError_t launch_d(const VerifyArgs& a, int gq, hipStream_t s) {
+template <int D, int KC, int VC, int SB>
+hipError_t launch_scalar(const VerifyArgs& a, int gq, hipStream_t s) {
     const dim3 grid(unsigned((a.total_q * a.pv.H + 3) / 4));
     switch (gq) {
-        case 1: return launch_kernel(true, verify_scalar_kernel<D, 1>, grid, dim3(256), s, a);
-        case 2: return launch_kernel(true, verify_scalar_kernel<D, 2>, grid, dim3(256), s, a);
-        case 4: return launch_kernel(true, verify_scalar_kernel<D, 4>, grid, dim3(256), s, a);
-        case 8: return launch_kernel(true, verify_scalar_kernel<D, 8>, grid, dim3(256), s, a);
+        case 1: return launch_kernel(true, verify_scalar_kernel<D, 1, KC, VC, SB>, grid, dim3(256), s, a);
+        case 2: return launch_kernel(true, verify_scalar_kernel<D, 2, KC, VC, SB>, grid, dim3(256), s, a);
+        case 4: return launch_kernel(true, verify_scalar_kernel<D, 4, KC, VC, SB>, grid, dim3(256), s, a);
+        case 8: return launch_kernel(true, verify_scalar_kernel<D, 8, KC, VC, SB>, grid, dim3(256), s, a);
         default: return hipErrorNotSupported;
     }
-    return hipGetLastError();
+}
+
+// the per-token kernel for the pool's closed profile
+template <int D>
+hipError_t launch_d(const VerifyArgs& a, int gq, hipStream_t s) {
+    const int kc = a.pv.k_codec, vc = a.pv.v_codec;
+    const bool s16 = a.pv.scale16 != 0;
+#define KVS_VSC_CASE(K, V, SB) \
+    if (kc == K && vc == V && s16 == (SB == 2)) return launch_scalar<D, K, V, SB>(a, gq, s);
+    KVS_VSC_CASE(CODEC_BF16, CODEC_BF16, 4)
+    KVS_VSC_CASE(CODEC_INT8_G64, CODEC_INT8_G64, 4)
+    KVS_VSC_CASE(CODEC_FP8_ROW, CODEC_FP8_ROW, 4)
+    KVS_VSC_CASE(CODEC_NVFP4_G16, CODEC_NVFP4_G16, 4)
+    KVS_VSC_CASE(CODEC_FP8_ROW, CODEC_NVFP4_G16, 4)
+    KVS_VSC_CASE(CODEC_INT8_G64, CODEC_INT8_G64, 2)
+    KVS_VSC_CASE(CODEC_FP8_ROW, CODEC_FP8_ROW, 2)
+    KVS_VSC_CASE(CODEC_FP8_ROW, CODEC_NVFP4_G16, 2)
+#undef KVS_VSC_CASE
+    return hipErrorNotSupported;
 }
 
 }  // namespace
@@ -530,8 +548,7 @@ hipError_t launch_d(const VerifyArgs& a, int gq, hipStream_t s) {
 bool verify_supported(const PoolView& pv, int Hq) {
     if (pv.H <= 0 || Hq % pv.H) return false;
     const int gq = Hq / pv.H;
-    return pv.k_codec == CODEC_BF16 && pv.v_codec == CODEC_BF16 && (pv.D == 64 || pv.D == 128 || pv.D == 256) &&
-           (gq == 1 || gq == 2 || gq == 4 || gq == 8);
+    return (pv.D == 64 || pv.D == 128 || pv.D == 256) && (gq == 1 || gq == 2 || gq == 4 || gq == 8);
 }
 
 // Entries with at most kStreamCols query columns (tokens x GQ, e.g. a short
