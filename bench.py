@@ -283,21 +283,35 @@ def cpu_baseline_verify(wl, seconds_hint: float = 20.0) -> dict:
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 
 
+# codec numbers of the kernel instances: BF16 0, INT8-G64 1, FP8-row 2, NVFP4-G16 3
+CODECS = {"BF16": (0, 0), "INT8_G64": (1, 1), "FP8_E4M3FN_ROW256": (2, 2), "NVFP4_G16": (3, 3), "K8V4": (2, 3)}
+
+
+def gtile_name(wl) -> str:
+    kc, vc = CODECS[wl.profile]
+    sb = 2 if wl.scale_bytes == 2 and wl.profile in ("INT8_G64", "FP8_E4M3FN_ROW256", "K8V4") else 4
+    return f"verify_gtile_kernel<{wl.D}, {wl.Hq // wl.H}, {kc}, {vc}, {sb}>"
+
+
+def bf16_tiles(wl) -> bool:
+    return wl.profile == "BF16" and wl.D in (64, 128) and wl.Hq // wl.H in (1, 2, 4, 8)
+
+
 def verify_dominant_kernel(wl) -> str:
     """The kernel that carries most of a paged_attn_verify call (rocprofv3 name)."""
     gq = wl.Hq // wl.H
-    if wl.profile == "BF16" and wl.D in (64, 128) and gq in (1, 2, 4, 8):
+    if bf16_tiles(wl):
         if max(wl.step) * gq > 32:
             return f"verify_tile_kernel<{wl.D}, {gq}>"
         return f"paged_vstream_kernel<{wl.D}, {gq}, 2, true>"
-    return f"verify_scalar_kernel<{wl.D}, {gq}>"
+    return gtile_name(wl)
 
 
 def verify_kernel_names(wl) -> str:
     gq = wl.Hq // wl.H
-    if wl.profile == "BF16" and wl.D in (64, 128) and gq in (1, 2, 4, 8):
+    if bf16_tiles(wl):
         return f"verify_tile_kernel<{wl.D}, {gq}> + paged_vstream_kernel<{wl.D}, {gq}, 2, true>"
-    return f"verify_scalar_kernel<{wl.D}, {gq}>"
+    return gtile_name(wl) + " (+ gtile_combine_kernel when its tiles are split)"
 
 
 def bench_verify(wl, args) -> int:
@@ -361,7 +375,7 @@ def bench_verify(wl, args) -> int:
     # query columns (tokens x query heads per KV head); the rest go through
     # the page stream in chunk mode before them
     gq = wl.Hq // wl.H
-    wide = [(n0, T) for n0, T in zip(wl.hist, wl.step) if T * gq > 32]
+    wide = [(n0, T) for n0, T in zip(wl.hist, wl.step) if T * gq > 32] if bf16_tiles(wl) else []
     kern_flops = 4.0 * wl.D * wl.Hq * sum(n0 * T + T * (T + 1) // 2 for n0, T in (wide or zip(wl.hist, wl.step)))
     kern_tflops = kern_flops / (kern_ms * 1e-3) / 1e12
     table = dp.table.cpu().numpy()
@@ -370,7 +384,8 @@ def bench_verify(wl, args) -> int:
                    for b, c in enumerate(wl.seq_lens))
     tflops = flops / (ver_ms * 1e-3) / 1e12
     line = {
-        "metric": "paged verify/prefill TFLOP/s (mixed batch: verify T=5 + prefill T=512, C=4, 128K ctx)",
+        "metric": f"paged verify/prefill TFLOP/s (mixed batch: verify T=5 + prefill T=512, C=4, "
+                  f"{wl.S // 1024}K ctx, {wl.profile} pages)",
         "value": round(flops * wl.layers / (ms_per_step * 1e-3) / 1e12, 2), "unit": "TFLOP/s", "n_gpus": 1,
         "steps": steps, "warmup": min(args.warmup, 2), "ms_per_step": round(ms_per_step, 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
@@ -739,7 +754,8 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", type=int, default=2,
-                    help="workload number (1-4: decode, 5: verify/prefill; 6, 7: BF16 at head_dim 256)")
+                    help="workload number (1-4: decode, 5: verify/prefill; 6, 7: BF16 at head_dim 256; "
+                         "8, 9: verify/prefill on INT8-G64 and K8V4 pools)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--scale-bytes", type=int, choices=(2, 4), default=4,
                     help="INT8-G64 / FP8-row scale planes: 4 (fp32) or 2 (binary16, the page's D256 byte table)")

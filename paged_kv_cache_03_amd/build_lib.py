@@ -25,7 +25,7 @@ OUT = os.path.join(HERE, "libkvstore.so")
 BUILD = os.path.join(HERE, "_build")
 
 SOURCES = ["pool.cpp", "table_kernels.hip", "append.hip", "decode.hip", "qstream.hip", "stream_plan.hip", "verify.hip",
-           "read_probe.hip"]
+           "verify_gtile.hip", "read_probe.hip"]
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950", "-I", INCLUDE, "-I", CSRC,
           "-fhip-fp32-correctly-rounded-divide-sqrt", "-fno-gpu-flush-denormals-to-zero",
@@ -34,7 +34,8 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950", "-I", INCLUDE, 
 # them with vector ALU ops; the accumulation-register form costs two copies
 # per touched register on every page)
 PER_FILE = {"append.hip": ["-ffp-contract=off"], "decode.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
-            "qstream.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"], "verify.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+            "qstream.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"], "verify.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+            "verify_gtile.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def hipcc() -> str:

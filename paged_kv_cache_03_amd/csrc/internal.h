@@ -117,6 +117,16 @@ hipError_t launch_stream_chunk(const PoolView& pv, int B, int Hq, const int32_t*
                                const int32_t* cu_q, int max_seq_len, const void* q, float sm_scale, float* out,
                                void* ws, int max_cols, bool trace, hipStream_t s);
 
+// Matrix-core tiles for verify / prefill on quantized pools (D in {64, 128,
+// 256}) and BF16 pools at D = 256 (verify_gtile.hip): every entry of the call,
+// each tile's page range cut into parts when the tiles alone cannot fill the
+// chip; the workspace holds the parts' partial results.
+bool gtile_supported(const PoolView& pv, int gq);
+size_t gtile_workspace_bytes(const PoolView& pv, int B, int Hq, int max_seq_len, int max_q_len);
+hipError_t launch_gtile(const PoolView& pv, int B, int Hq, const int32_t* table_rows, const int32_t* q_pos0,
+                        const int32_t* cu_q, int max_q_len, int max_seq_len, const void* q, float sm_scale,
+                        float* out, void* ws, hipStream_t s);
+
 bool verify_supported(const PoolView& pv, int Hq);
 size_t verify_workspace_bytes(const PoolView& pv, int B, int Hq, int max_seq_len, int max_q_len);
 hipError_t launch_verify(const PoolView& pv, int B, int Hq, const int32_t* table_rows, const int32_t* q_pos0,

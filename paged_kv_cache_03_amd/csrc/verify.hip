@@ -12,8 +12,10 @@
 // x GQ, e.g. a short verify) go through the matrix-core page stream in chunk
 // mode (decode.hip), which reads each page once for all of the entry's query
 // tokens; longer chunks (prefill) go to 128-column tiles on the matrix cores
-// (verify_tile_kernel).  Other shapes take the per-token kernel: one wave per
-// (chunk token, KV head) streams the causal range with an online softmax.
+// (verify_tile_kernel).  Quantized pools and BF16 pools at D = 256 take the
+// tiles of verify_gtile.hip for every chunk.  The per-token kernel (one wave
+// per (chunk token, KV head) streams the causal range with an online softmax)
+// covers whatever else a pool and Hq allow.
 
 #include <hip/hip_runtime.h>
 
@@ -556,9 +558,11 @@ bool verify_supported(const PoolView& pv, int Hq) {
 // of the entry's query tokens; longer chunks take the per-token kernel.
 constexpr int kStreamCols = 32;
 
-size_t verify_workspace_bytes(const PoolView& pv, int B, int Hq, int max_seq_len, int) {
+size_t verify_workspace_bytes(const PoolView& pv, int B, int Hq, int max_seq_len, int max_q_len) {
     const int gq = pv.H ? Hq / pv.H : 0;
-    return stream_chunk_supported(pv, B, gq) ? stream_chunk_workspace_bytes(pv, B, Hq, max_seq_len) : 0;
+    if (stream_chunk_supported(pv, B, gq)) return stream_chunk_workspace_bytes(pv, B, Hq, max_seq_len);
+    if (gtile_supported(pv, gq)) return gtile_workspace_bytes(pv, B, Hq, max_seq_len, max_q_len);
+    return 0;
 }
 
 hipError_t launch_verify(const PoolView& pv, int B, int Hq, const int32_t* table_rows, const int32_t* q_pos0,
@@ -601,6 +605,8 @@ hipError_t launch_verify(const PoolView& pv, int B, int Hq, const int32_t* table
         }
         return e;
     }
+    if (gtile_supported(pv, gq))   // quantized pools, BF16 at D = 256: tiles for every entry
+        return launch_gtile(pv, B, Hq, table_rows, q_pos0, cu_q, max_q_len, max_seq_len, q, sm_scale, out, ws, s);
     a.min_cols = 0;
     switch (pv.D) {
         case 64: return launch_d<64>(a, gq, s);

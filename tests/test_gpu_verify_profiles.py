@@ -64,3 +64,21 @@ def test_verify_profiles_long_history_mid_page(profile, gq, D):
     err = float(np.max(np.abs(got - ref)))
     say(f"  max abs err {err:.3g}")
     assert err <= TOL
+
+
+def test_verify_tiles_without_page_split():
+    # 8 entries x 4 KV heads x 16 tiles of 512-token chunks: enough tiles to
+    # fill the chip, so every tile streams its whole range (no parts, no
+    # combine) -- the other cases here run split tiles
+    hist = [100, 700, 1000, 64, 0, 333, 1500, 63]
+    wl = workloads.small(780, "INT8_G64", hist=hist, step=[512] * 8, C=8, S=2048, Hq=16, H=4, D=128,
+                         mode="verify", outlier_frac=0.01)
+    say("verify INT8-G64, 512 tiles, no page split")
+    pool, st, _ = build_oracle(wl)
+    dp, _, _ = build_device(wl, fill=0xFF)
+    got = device_verify(dp, wl, 0)
+    dp.close()
+    ref = A.paged_verify(st, 0, wl.table_rows, wl.hist, wl.cu_q, wl.q(0), wl.sm_scale)
+    err = float(np.max(np.abs(got - ref)))
+    say(f"  max abs err {err:.3g}")
+    assert err <= TOL

@@ -15,8 +15,10 @@ Readings taken where the workload descriptions leave a choice open:
 * verify/prefill: n0 = 2039*64 + {35, 1, 63, 17}; sequences 0-1 verify 5
   tokens, 2-3 prefill a 512-token chunk.
 * one layer where the text gives no layer count.
-Two more measure BF16 pages at head_dim 256 (not among the named five): the
-K8V4 decode shapes, and the verify/prefill mix with 16 query / 2 KV heads.
+More workloads, not among the named five: BF16 pages at head_dim 256 (the
+K8V4 decode shapes; the verify/prefill mix with 16 query / 2 KV heads), and
+the verify/prefill mix on quantized pools (INT8-G64 with config 5's shapes,
+K8V4 with config 4's heads and head_dim at 64K contexts).
 """
 
 from __future__ import annotations
@@ -232,6 +234,22 @@ def _cfg7() -> Workload:
                     cow=[False] * 4, mode="verify")
 
 
+def _cfg8() -> Workload:
+    # the verify / prefill mix on an INT8-G64 pool (config 5's shapes)
+    n0 = [2039 * 64 + o for o in (35, 1, 63, 17)]
+    return Workload("int8g64_verify5_prefill512_c4_ctx128k", "INT8_G64", C=4, S=131072, M=4 * 2048, layers=1,
+                    Hq=32, H=8, D=128, seed=1008, hist=n0, step=[5, 5, 512, 512], fork=[None] * 4,
+                    cow=[False] * 4, mode="verify", outlier_frac=0.01)
+
+
+def _cfg9() -> Workload:
+    # the verify / prefill mix on a K8V4 pool (config 4's heads and head_dim, 64K contexts)
+    n0 = [1015 * 64 + o for o in (35, 1, 63, 17)]
+    return Workload("k8v4_verify5_prefill512_c4_ctx64k", "K8V4", C=4, S=65536, M=4 * 1024, layers=1, Hq=16, H=2,
+                    D=256, seed=1009, hist=n0, step=[5, 5, 512, 512], fork=[None] * 4, cow=[False] * 4,
+                    mode="verify")
+
+
 WORKLOADS = {
     1: _cfg1,
     2: lambda: _decode8(2, "BF16", 0.0, False),
@@ -240,6 +258,8 @@ WORKLOADS = {
     5: _cfg5,
     6: _cfg6,
     7: _cfg7,
+    8: _cfg8,
+    9: _cfg9,
 }
 
 
