@@ -190,7 +190,11 @@ __global__ void __launch_bounds__(512) verify_gtile_kernel(GTileArgs a) {
     constexpr int OFF_VH = PLANE, OFF_KL = 2 * PLANE, OFF_VL = (KLO ? 3 : 2) * PLANE;
     constexpr int NPL = 2 + (KLO ? 1 : 0) + (VLO ? 1 : 0);
     constexpr int MERGE = WCT * NDT * 4 * 64 * 4 / 16 * 4;   // u32x4 slots of the end merge (4 column ranges)
-    constexpr int SLOTS = NPL * PLANE > MERGE ? NPL * PLANE : MERGE;
+    // two stages of tiles where they fit in LDS (the next page is converted
+    // while the current one is computed), else one
+    constexpr int NSTG = 2 * NPL * PLANE * 16 <= 144 * 1024 ? 2 : 1;
+    constexpr int STAGE = NPL * PLANE;
+    constexpr int SLOTS = NSTG * STAGE > MERGE ? NSTG * STAGE : MERGE;
     static_assert(J >= 1 && 64 * NCH % NT == 0 && TCOL % GQ == 0, "shape");
 
     __shared__ u32x4 lds[SLOTS];
@@ -284,8 +288,9 @@ __global__ void __launch_bounds__(512) verify_gtile_kernel(GTileArgs a) {
         load_side<VC, D, SB, J, NT>(rv, vcp + s * RV::code, vsp + s * RV::scale, sl >= 0, tid);
         return sl;
     };
-    // the loaded page into the LDS tiles; rows at or past lim become zeros
-    auto convert = [&](int lim) __attribute__((always_inline)) {
+    // the loaded page into the LDS tiles of stage st; rows at or past lim become zeros
+    auto convert = [&](int lim, int st) __attribute__((always_inline)) {
+        u32x4* const tl = &lds[st * STAGE];
 #pragma unroll
         for (int k = 0; k < J; ++k) {
             int r, x;
@@ -317,10 +322,10 @@ __global__ void __launch_bounds__(512) verify_gtile_kernel(GTileArgs a) {
                 vlo = vis ? u32x4{lw[0], lw[1], lw[2], lw[3]} : u32x4{0u, 0u, 0u, 0u};
             }
             const int ks = r * NCH + (x ^ kswz(r)), vs = r * NCH + (x ^ vswz(r));
-            lds[ks] = khi;
-            lds[OFF_VH + vs] = vhi;
-            if constexpr (KLO) lds[OFF_KL + ks] = klo;
-            if constexpr (VLO) lds[OFF_VL + vs] = vlo;
+            tl[ks] = khi;
+            tl[OFF_VH + vs] = vhi;
+            if constexpr (KLO) tl[OFF_KL + ks] = klo;
+            if constexpr (VLO) tl[OFF_VL + vs] = vlo;
         }
     };
 
@@ -338,16 +343,17 @@ __global__ void __launch_bounds__(512) verify_gtile_kernel(GTileArgs a) {
 
     const lds_byte_ptr lbase = (lds_byte_ptr)(&lds[0]);
     auto read_vt = [&](int plane, int dt) __attribute__((always_inline)) {
-        const lds_byte_ptr vst = lbase + plane * 16;
+        const lds_byte_ptr vst = lbase + plane * 16;   // plane: slot offset of the tile (stage included)
         const s16x4_t v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_ptr)(vst + voff[dt]));
         const s16x4_t v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_ptr)(vst + voff[dt] + 16 * NCH * 16));
         return __builtin_bit_cast(bf16x8_t, u32x4{__builtin_bit_cast(u32x2, v0)[0], __builtin_bit_cast(u32x2, v0)[1],
                                                   __builtin_bit_cast(u32x2, v1)[0], __builtin_bit_cast(u32x2, v1)[1]});
     };
 
-    // one page from the LDS tiles
-    auto compute = [&](int i, int lim) __attribute__((always_inline)) {
+    // one page from the LDS tiles of stage st
+    auto compute = [&](int i, int lim, int st) __attribute__((always_inline)) {
         const int tok0 = i * kPage;
+        const int sb = st * STAGE;
         if (lim <= kr0) return;                    // none of this wave's keys is visible
         f32x4_t s[2][WCT];
 #pragma unroll
@@ -358,12 +364,12 @@ __global__ void __launch_bounds__(512) verify_gtile_kernel(GTileArgs a) {
         for (int kt = 0; kt < 2; ++kt) {
 #pragma unroll
             for (int c = 0; c < NC; ++c) {
-                const bf16x8_t kk = __builtin_bit_cast(bf16x8_t, lds[koff[c] + kt * 16 * NCH]);
+                const bf16x8_t kk = __builtin_bit_cast(bf16x8_t, lds[sb + koff[c] + kt * 16 * NCH]);
 #pragma unroll
                 for (int ct = 0; ct < WCT; ++ct)
                     s[kt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kk, qb[ct][c], s[kt][ct], 0, 0, 0);
                 if constexpr (KLO) {
-                    const bf16x8_t kl = __builtin_bit_cast(bf16x8_t, lds[OFF_KL + koff[c] + kt * 16 * NCH]);
+                    const bf16x8_t kl = __builtin_bit_cast(bf16x8_t, lds[sb + OFF_KL + koff[c] + kt * 16 * NCH]);
 #pragma unroll
                     for (int ct = 0; ct < WCT; ++ct)
                         s[kt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kl, qb[ct][c], s[kt][ct], 0, 0, 0);
@@ -424,12 +430,12 @@ __global__ void __launch_bounds__(512) verify_gtile_kernel(GTileArgs a) {
         }
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt) {
-            const bf16x8_t va = read_vt(OFF_VH, dt);
+            const bf16x8_t va = read_vt(sb + OFF_VH, dt);
 #pragma unroll
             for (int ct = 0; ct < WCT; ++ct)
                 acc[ct][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, phi[ct], acc[ct][dt], 0, 0, 0);
             if constexpr (VLO) {
-                const bf16x8_t vl = read_vt(OFF_VL, dt);
+                const bf16x8_t vl = read_vt(sb + OFF_VL, dt);
 #pragma unroll
                 for (int ct = 0; ct < WCT; ++ct)
                     acc[ct][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vl, phi[ct], acc[ct][dt], 0, 0, 0);
@@ -454,12 +460,12 @@ __global__ void __launch_bounds__(512) verify_gtile_kernel(GTileArgs a) {
             }
 #pragma unroll
             for (int dt = 0; dt < NDT; ++dt) {
-                const bf16x8_t va = read_vt(OFF_VH, dt);
+                const bf16x8_t va = read_vt(sb + OFF_VH, dt);
 #pragma unroll
                 for (int ct = 0; ct < WCT; ++ct)
                     acc[ct][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, plo[ct], acc[ct][dt], 0, 0, 0);
                 if constexpr (VLO) {
-                    const bf16x8_t vl = read_vt(OFF_VL, dt);
+                    const bf16x8_t vl = read_vt(sb + OFF_VL, dt);
 #pragma unroll
                     for (int ct = 0; ct < WCT; ++ct)
                         acc[ct][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vl, plo[ct], acc[ct][dt], 0, 0, 0);
@@ -471,16 +477,41 @@ __global__ void __launch_bounds__(512) verify_gtile_kernel(GTileArgs a) {
         }
     };
 
-    // pages [p0, p1): the next page's loads are in flight while one is computed
+    // pages [p0, p1); rows any column may see on page i: lim_of
+    auto lim_of = [&](int i, int sl) __attribute__((always_inline)) {
+        return sl >= 0 ? min(kPage, kmax - i * kPage) : 0;
+    };
     if (p0 < p1) {
-        int sl = load_page(p0);
-        for (int i = p0; i < p1; ++i) {
-            const int lim = sl >= 0 ? min(kPage, kmax - i * kPage) : 0;   // rows any column may see
-            convert(lim);
+        if constexpr (NSTG == 2) {
+            // page i+1 is converted into the other stage while page i is
+            // computed, page i+2's loads in flight: one barrier per page
+            int sl = load_page(p0);
+            int lim = lim_of(p0, sl);
+            convert(lim, 0);
+            if (p0 + 1 < p1) sl = load_page(p0 + 1);
             block_lds_barrier();
-            if (i + 1 < p1) sl = load_page(i + 1);
-            compute(i, lim);
-            block_lds_barrier();                   // every wave is done with the tiles
+            for (int i = p0; i < p1; ++i) {
+                const int st = (i - p0) & 1;
+                const int lim_next = i + 1 < p1 ? lim_of(i + 1, sl) : 0;
+                compute(i, lim, st);
+                if (i + 1 < p1) {
+                    convert(lim_next, st ^ 1);
+                    if (i + 2 < p1) sl = load_page(i + 2);
+                }
+                block_lds_barrier();               // stage st is free, stage st^1 is written
+                lim = lim_next;
+            }
+        } else {
+            // one stage: the next page's loads are in flight while one is computed
+            int sl = load_page(p0);
+            for (int i = p0; i < p1; ++i) {
+                const int lim = lim_of(i, sl);
+                convert(lim, 0);
+                block_lds_barrier();
+                if (i + 1 < p1) sl = load_page(i + 1);
+                compute(i, lim, 0);
+                block_lds_barrier();               // every wave is done with the tiles
+            }
         }
     }
 
