@@ -146,13 +146,13 @@ def decode_kernel_name(wl) -> str:
     return "decode_split_kernel + decode_combine_kernel"
 
 
-def measured_traffic(wl, kind: str = "decode") -> int | None:
-    """HBM bytes per decode launch (kind "decode") or per verify call (kind
-    "verify": every kernel of one paged_attn_verify call) from the committed
-    rocprofv3 counter summary (FETCH_SIZE + WRITE_SIZE, each scaled by what the
-    same counter reads for a plain device copy of known size), or None when
-    there is none for this workload or the sources have changed since it was
-    taken."""
+def measured_traffic(wl, kind: str = "decode", field: str = "traffic_bytes_per_dispatch") -> int | None:
+    """HBM bytes per launch of the dominant kernel of a decode (kind "decode")
+    or a verify call (kind "verify"; field "call_traffic_bytes": every kernel
+    of the call) from the committed rocprofv3 counter summary (FETCH_SIZE +
+    WRITE_SIZE, each scaled by what the same counter reads for a plain device
+    copy of known size), or None when there is none for this workload or the
+    sources have changed since it was taken."""
     path = os.path.join(PROFILES, f"{kind}_traffic_{wl.name}.txt")
     if not os.path.exists(path):
         return None
@@ -168,7 +168,7 @@ def measured_traffic(wl, kind: str = "decode") -> int | None:
     if kv.get("source_sha256") != sha or kv.get("kernel") != kernel:
         return None
     try:
-        return int(float(kv["traffic_bytes_per_dispatch"]))
+        return int(float(kv[field]))
     except (KeyError, ValueError):
         return None
 
@@ -398,6 +398,7 @@ def bench_verify(wl, args) -> int:
                      "traffic": measured_traffic(wl, "verify"), "flops_per_launch": kern_flops,
                      "launch_ms": round(kern_ms, 5),
                      "call": {"kernels": verify_kernel_names(wl), "flops": flops, "kv_bytes": kv_bytes,
+                              "traffic": measured_traffic(wl, "verify", "call_traffic_bytes"),
                               "ms": round(ver_ms, 5), "tflops": round(tflops, 2),
                               "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4)}},
         "cpu_baseline": None if args.no_cpu_baseline else cpu_baseline_verify(wl),

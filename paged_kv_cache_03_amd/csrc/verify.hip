@@ -165,7 +165,7 @@ __global__ void __launch_bounds__(512) verify_tile_kernel(VerifyArgs a) {
     constexpr int NDT = D / 16;                    // PV tiles of 16 dims
     constexpr int TCOL = 128;                      // query columns per tile
     constexpr int WCT = 2;                         // 16-column tiles per wave
-    constexpr float kHiOnly = 1.f / 64.f;          // largest weight of a page that takes p as one bf16 term
+    constexpr float kHiOnly = 1.f / 256.f;         // largest weight of a page that takes p as one bf16 term
     constexpr int TTOK = TCOL / GQ;                // chunk tokens per tile
     static_assert((D == 64 || D == 128) && TCOL % GQ == 0, "shape");
     static_assert(NS * SLICE_BYTES == 0x10000, "V stages sit 64 KiB above the K stages");
@@ -402,9 +402,11 @@ __global__ void __launch_bounds__(512) verify_tile_kernel(VerifyArgs a) {
         // can weigh much in its column: every column's largest probability
         // on the page is at most kHiOnly of its running sum over this wave's
         // keys (a lower bound of the column's sum).  The sum adds exactly the
-        // rounded values the product uses, so a rounding common to many keys
-        // cancels in the normalization; what remains is a relative 2^-9 per
-        // weight, independent across keys, on weights below kHiOnly.  Pages
+        // rounded values the product uses, so the output is the softmax of
+        // the rounded weights: a key's rounding (at most 2^-9 of its
+        // probability) moves the output by at most 2^-9 w |v - o|, w <= 2^-8
+        // its weight, i.e. at most 2^-17 |v - o| per key; the roundings of
+        // different keys are independent and add like a random walk.  Pages
         // where some column fails the test (the first pages of every
         // column, peaked distributions) add the second term p_lo.
         bool need_lo = false;

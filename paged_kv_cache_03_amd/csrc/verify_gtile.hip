@@ -184,7 +184,7 @@ __global__ void __launch_bounds__(512) verify_gtile_kernel(GTileArgs a) {
     constexpr int TCOL = gtile_cols<D>();          // query columns per tile
     constexpr int WCT = TCOL / 64;                 // 16-column tiles per wave
     constexpr int TTOK = TCOL / GQ;                // chunk tokens per tile
-    constexpr float kHiOnly = 1.f / 64.f;          // largest weight of a page that takes p as one bf16 term
+    constexpr float kHiOnly = 1.f / 256.f;         // largest weight of a page that takes p as one bf16 term
     constexpr bool KLO = GRow<KC, D, SB>::lo, VLO = GRow<VC, D, SB>::lo;
     constexpr int PLANE = 64 * NCH;                // u32x4 slots of one bf16 page tile
     constexpr int OFF_VH = PLANE, OFF_KL = 2 * PLANE, OFF_VL = (KLO ? 3 : 2) * PLANE;

@@ -53,11 +53,22 @@ def test_verify_long_prefill_tiles_share_pages():
 
 
 def test_verify_long_histories_one_term_pages():
-    # long histories: past the first pages no key weighs more than 1/64 of its
-    # column's running sum, and the tiles take P as one bf16 term there
+    # long histories: past the first pages no key weighs more than 1/256 of
+    # its column's running sum, and the tiles take P as one bf16 term there
     wl = workloads.small(91, "BF16", hist=[12000, 19937], step=[200, 141], C=2, S=20480, Hq=8, H=2, D=128,
                          mode="verify")
     _check(wl, "prefill 200 + 141 at 12K/20K keys")
+
+
+@pytest.mark.parametrize("scale_mul", [1.0, 4.0])
+def test_verify_one_term_pages_with_outlier_values(scale_mul):
+    # 1% of the K and V elements x20 (values up to about 90): a key on a
+    # one-term page moves its column by at most 2^-17 |v - o|, so even heavy
+    # values stay inside the bar; with the softmax scale x4 some columns are
+    # peaked as well
+    wl = workloads.small(93, "BF16", hist=[30000, 20011], step=[256, 97], C=2, S=32768, Hq=8, H=2, D=128,
+                         mode="verify", outlier_frac=0.01, scale_mul=scale_mul)
+    _check(wl, f"outliers x20, scale x{scale_mul}")
 
 
 @pytest.mark.parametrize("scale_mul", [4.0, 16.0])
