@@ -185,15 +185,22 @@ __global__ void __launch_bounds__(512) verify_gtile_kernel(GTileArgs a) {
     constexpr int WCT = TCOL / 64;                 // 16-column tiles per wave
     constexpr int TTOK = TCOL / GQ;                // chunk tokens per tile
     constexpr float kHiOnly = 1.f / 256.f;         // largest weight of a page that takes p as one bf16 term
-    constexpr bool KLO = GRow<KC, D, SB>::lo, VLO = GRow<VC, D, SB>::lo;
+    // INT8-G64 and FP8-row K: the K tile holds the codes (exact in bf16) and
+    // the scales act on each key's per-group partial scores; other sides hold
+    // dequantized values, V as a bf16 pair where they are not exact in bf16
+    constexpr bool KSC = KC == CODEC_INT8_G64 || KC == CODEC_FP8_ROW;
+    constexpr int NGK = KC == CODEC_INT8_G64 ? D / 64 : 1;   // score accumulators: one per K scale group
+    constexpr bool VLO = GRow<VC, D, SB>::lo;
     constexpr int PLANE = 64 * NCH;                // u32x4 slots of one bf16 page tile
-    constexpr int OFF_VH = PLANE, OFF_KL = 2 * PLANE, OFF_VL = (KLO ? 3 : 2) * PLANE;
-    constexpr int NPL = 2 + (KLO ? 1 : 0) + (VLO ? 1 : 0);
+    constexpr int OFF_VH = PLANE, OFF_VL = 2 * PLANE;
+    constexpr int NPL = 2 + (VLO ? 1 : 0);
+    constexpr int OFF_KS = NPL * PLANE;            // K scales [group][64 keys] as fp32
+    constexpr int KS_SLOTS = KSC ? NGK * 64 / 4 : 0;
     constexpr int MERGE = WCT * NDT * 4 * 64 * 4 / 16 * 4;   // u32x4 slots of the end merge (4 column ranges)
     // two stages of tiles where they fit in LDS (the next page is converted
     // while the current one is computed), else one
-    constexpr int NSTG = 2 * NPL * PLANE * 16 <= 144 * 1024 ? 2 : 1;
-    constexpr int STAGE = NPL * PLANE;
+    constexpr int STAGE = NPL * PLANE + KS_SLOTS;
+    constexpr int NSTG = 2 * STAGE * 16 <= 144 * 1024 ? 2 : 1;
     constexpr int SLOTS = NSTG * STAGE > MERGE ? NSTG * STAGE : MERGE;
     static_assert(J >= 1 && 64 * NCH % NT == 0 && TCOL % GQ == 0, "shape");
 
@@ -296,18 +303,40 @@ __global__ void __launch_bounds__(512) verify_gtile_kernel(GTileArgs a) {
             int r, x;
             job_of<NCH>(tid + NT * k, r, x);
             const bool vis = r < lim;
-            u32x4 khi, klo, vhi, vlo;
+            u32x4 khi, vhi, vlo;
             if constexpr (KC == CODEC_BF16) {
                 khi = vis ? rk.code[k] : u32x4{0u, 0u, 0u, 0u};
-                klo = khi;
-            } else {
+            } else if constexpr (KC == CODEC_INT8_G64) {
+                const u32x4 c = rk.code[k];
+                uint32_t w[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const uint32_t src = c[e >> 1] >> (16 * (e & 1));
+                    w[e] = __builtin_bit_cast(uint32_t, __builtin_convertvector(
+                        f32x2_t{float(int8_t(src & 0xFFu)), float(int8_t((src >> 8) & 0xFFu))}, bf16x2v_t));
+                }
+                khi = vis ? u32x4{w[0], w[1], w[2], w[3]} : u32x4{0u, 0u, 0u, 0u};
+            } else if constexpr (KC == CODEC_FP8_ROW) {
+                const u32x4 c = rk.code[k];
+                uint32_t w[4];
+#pragma unroll
+                for (int e = 0; e < 2; ++e) {
+                    w[2 * e] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c[e], 1.0f, false));
+                    w[2 * e + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c[e], 1.0f, true));
+                }
+                khi = vis ? u32x4{w[0], w[1], w[2], w[3]} : u32x4{0u, 0u, 0u, 0u};
+            } else {   // NVFP4 K: dequantized values, exact in bf16
                 float v[8];
                 dequant8<KC, SB>(rk.code[k], rk.scale[k], v);
                 uint32_t hw[4], lw[4];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) split_bf16(v[2 * e], v[2 * e + 1], hw[e], lw[e]);
                 khi = vis ? u32x4{hw[0], hw[1], hw[2], hw[3]} : u32x4{0u, 0u, 0u, 0u};
-                klo = vis ? u32x4{lw[0], lw[1], lw[2], lw[3]} : u32x4{0u, 0u, 0u, 0u};
+            }
+            if constexpr (KSC) {                   // the chunk that starts a scale group writes its scale
+                constexpr int GCH = KC == CODEC_INT8_G64 ? 8 : NCH;    // chunks per scale group
+                if (x % GCH == 0)
+                    reinterpret_cast<float*>(&tl[OFF_KS])[(x / GCH) * 64 + r] = vis ? wide_scale<SB>(rk.scale[k]) : 0.f;
             }
             if constexpr (VC == CODEC_BF16) {
                 vhi = vis ? rv.code[k] : u32x4{0u, 0u, 0u, 0u};
@@ -324,7 +353,6 @@ __global__ void __launch_bounds__(512) verify_gtile_kernel(GTileArgs a) {
             const int ks = r * NCH + (x ^ kswz(r)), vs = r * NCH + (x ^ vswz(r));
             tl[ks] = khi;
             tl[OFF_VH + vs] = vhi;
-            if constexpr (KLO) tl[OFF_KL + ks] = klo;
             if constexpr (VLO) tl[OFF_VL + vs] = vlo;
         }
     };
@@ -356,24 +384,46 @@ __global__ void __launch_bounds__(512) verify_gtile_kernel(GTileArgs a) {
         const int sb = st * STAGE;
         if (lim <= kr0) return;                    // none of this wave's keys is visible
         f32x4_t s[2][WCT];
+        {
+            // partial scores per K scale group (INT8-G64: 64 dims = two
+            // products of k = 32), then each key's scales applied in fp32
+            f32x4_t sg[NGK][2][WCT];
 #pragma unroll
-        for (int kt = 0; kt < 2; ++kt)
+            for (int g = 0; g < NGK; ++g)
 #pragma unroll
-            for (int ct = 0; ct < WCT; ++ct) s[kt][ct] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+                for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-        for (int kt = 0; kt < 2; ++kt) {
+                    for (int ct = 0; ct < WCT; ++ct) sg[g][kt][ct] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int c = 0; c < NC; ++c) {
-                const bf16x8_t kk = __builtin_bit_cast(bf16x8_t, lds[sb + koff[c] + kt * 16 * NCH]);
+            for (int kt = 0; kt < 2; ++kt) {
 #pragma unroll
-                for (int ct = 0; ct < WCT; ++ct)
-                    s[kt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kk, qb[ct][c], s[kt][ct], 0, 0, 0);
-                if constexpr (KLO) {
-                    const bf16x8_t kl = __builtin_bit_cast(bf16x8_t, lds[sb + OFF_KL + koff[c] + kt * 16 * NCH]);
+                for (int c = 0; c < NC; ++c) {
+                    constexpr int CPG = NGK > 1 ? NC / NGK : NC;
+                    const int g = NGK > 1 ? c / CPG : 0;
+                    const bf16x8_t kk = __builtin_bit_cast(bf16x8_t, lds[sb + koff[c] + kt * 16 * NCH]);
 #pragma unroll
                     for (int ct = 0; ct < WCT; ++ct)
-                        s[kt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kl, qb[ct][c], s[kt][ct], 0, 0, 0);
+                        sg[g][kt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kk, qb[ct][c], sg[g][kt][ct], 0, 0, 0);
                 }
+            }
+            if constexpr (KSC) {
+                const float* kst = reinterpret_cast<const float*>(&lds[sb + OFF_KS]);
+#pragma unroll
+                for (int kt = 0; kt < 2; ++kt) {
+#pragma unroll
+                    for (int ct = 0; ct < WCT; ++ct) s[kt][ct] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int g = 0; g < NGK; ++g) {
+                        const f32x4_t sc = *reinterpret_cast<const f32x4_t*>(kst + g * 64 + kr0 + 16 * kt + 4 * lg);
+#pragma unroll
+                        for (int ct = 0; ct < WCT; ++ct) s[kt][ct] += sg[g][kt][ct] * sc;
+                    }
+                }
+            } else {
+#pragma unroll
+                for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+                    for (int ct = 0; ct < WCT; ++ct) s[kt][ct] = sg[0][kt][ct];
             }
         }
         // the causal mask, only on the pages that reach some column's limit
