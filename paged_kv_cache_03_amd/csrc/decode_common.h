@@ -56,6 +56,18 @@ __device__ __forceinline__ void ring_round(F& step, int i0, int npg) {
     }
 }
 
+// pages [0, npg) through a ring of NS buffers: whole rounds in a loop, then
+// the last npg % NS pages after it.  A loop whose rounds may end early has a
+// path from a partial round back into the next one, along which the
+// compiler's vector-memory waits must also cover loads issued one stage
+// later: they would hold back the ring's deepest prefetch on every round.
+template <int NS, class F>
+__device__ __forceinline__ void ring_run(F& step, int npg) {
+    int i0 = 0;
+    for (; i0 + NS <= npg; i0 += NS) ring_round<0, NS>(step, i0, i0 + NS);
+    ring_round<0, NS>(step, i0, npg);
+}
+
 // The BF16 register-fed page stream: blocks of four waves per compute unit,
 // and page buffers per wave (buffers - 1 pages in flight while one is
 // computed).  At D = 256 a wave's page is twice the bytes and registers, so

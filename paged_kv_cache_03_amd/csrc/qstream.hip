@@ -22,14 +22,19 @@
 //    key's per-group partial scores, V scales multiply the key's probability
 //    (p * s, split into two bf16 terms like p itself), one copy of P per
 //    64-dim scale group;
-//  * PV runs V^T . [P_hi; P_lo] as one k=32 product per 16-dim tile: the
-//    lane's four keys appear twice in the V^T operand, once against P_hi,
-//    once against P_lo;
-//  * a V^T operand comes from the lane's row loads of the four keys whose
-//    probabilities it holds; packing the fp32 values of two keys into one
-//    bf16 pair is the transpose.  Row m of tile j then holds head dim
-//    64(j/4) + 4m + j%4 for INT8-G64 V (a tile stays in one scale group) and
-//    (D/16) m + j for the others.
+//  * PV runs V^T . P_hi and V^T . P_lo as two k=16 products per 16-dim tile
+//    on the same V^T operand: lane group lg's four keys are exactly the k
+//    slots 4lg .. 4lg+3 of a k=16 product;
+//  * a V^T operand holds the lane's four keys at the head dim of its tile
+//    row; packing the fp32 values of two keys into one bf16 pair is the
+//    transpose.  Row m of tile j holds head dim 64(j/4) + 4m + j%4 for
+//    INT8-G64 V (a tile stays in one scale group: four bytes per key, group
+//    and lane) and (D/16) m + j for the others (one row load per key);
+//  * the page's load instructions, more than its bytes, bound the stream:
+//    INT8-G64 V codes come as a few 16-byte loads per lane that the wave
+//    writes into its own LDS stage and reads back four bytes at a time, and
+//    the INT8-G64 / FP8-row scales of a 16-lane row's four keys come as one
+//    4-byte load per lane, each scale then broadcast within the row.
 
 #include <hip/hip_runtime.h>
 
@@ -56,14 +61,37 @@ struct QRow {
     static constexpr int scale = C == CODEC_INT8_G64 ? SB * (D / 64) : (C == CODEC_FP8_ROW ? SB : D / 16);
 };
 
-// scale f of a run of scales loaded into 16-byte registers: fp32 word f, or
-// binary16 half f widened exactly
-template <int SB, int N>
-__device__ __forceinline__ float scale_of(const u32x4 (&buf)[N], int f) {
+// word of lane k of this lane's 16-lane row (a row broadcast: one vector
+// move; k is a constant once the callers' loops are unrolled)
+__device__ __forceinline__ uint32_t row_word(uint32_t v, int k) {
+    switch (k & 15) {
+        case 0: return __builtin_amdgcn_mov_dpp(v, 0x150, 0xf, 0xf, false);
+        case 1: return __builtin_amdgcn_mov_dpp(v, 0x151, 0xf, 0xf, false);
+        case 2: return __builtin_amdgcn_mov_dpp(v, 0x152, 0xf, 0xf, false);
+        case 3: return __builtin_amdgcn_mov_dpp(v, 0x153, 0xf, 0xf, false);
+        case 4: return __builtin_amdgcn_mov_dpp(v, 0x154, 0xf, 0xf, false);
+        case 5: return __builtin_amdgcn_mov_dpp(v, 0x155, 0xf, 0xf, false);
+        case 6: return __builtin_amdgcn_mov_dpp(v, 0x156, 0xf, 0xf, false);
+        case 7: return __builtin_amdgcn_mov_dpp(v, 0x157, 0xf, 0xf, false);
+        case 8: return __builtin_amdgcn_mov_dpp(v, 0x158, 0xf, 0xf, false);
+        case 9: return __builtin_amdgcn_mov_dpp(v, 0x159, 0xf, 0xf, false);
+        case 10: return __builtin_amdgcn_mov_dpp(v, 0x15a, 0xf, 0xf, false);
+        case 11: return __builtin_amdgcn_mov_dpp(v, 0x15b, 0xf, 0xf, false);
+        case 12: return __builtin_amdgcn_mov_dpp(v, 0x15c, 0xf, 0xf, false);
+        case 13: return __builtin_amdgcn_mov_dpp(v, 0x15d, 0xf, 0xf, false);
+        case 14: return __builtin_amdgcn_mov_dpp(v, 0x15e, 0xf, 0xf, false);
+        default: return __builtin_amdgcn_mov_dpp(v, 0x15f, 0xf, 0xf, false);
+    }
+}
+
+// scale f (fp32 word f, or binary16 half f widened exactly) of a run of
+// scales spread one dword per lane over a 16-lane row
+template <int SB>
+__device__ __forceinline__ float row_scale(uint32_t v, int f) {
     if constexpr (SB == 4) {
-        return __uint_as_float(buf[f >> 2][f & 3]);
+        return __uint_as_float(row_word(v, f));
     } else {
-        const uint32_t w = buf[f >> 3][(f >> 1) & 3];
+        const uint32_t w = row_word(v, f >> 1);
         return static_cast<float>(__builtin_bit_cast(_Float16, uint16_t((f & 1) ? (w >> 16) : (w & 0xFFFFu))));
     }
 }
@@ -73,6 +101,13 @@ __device__ __forceinline__ float scale_of(const u32x4 (&buf)[N], int f) {
 // D = 128), one for INT8-G64 at D = 256 (its registers do not fit twice).
 template <int D, int KC>
 constexpr int qstream_bpc() { return (D == 256 && KC == CODEC_INT8_G64) ? 1 : 2; }
+
+// Page buffers per wave (PF - 1 pages in flight while one is computed).  A
+// third buffer (two pages in flight) measured no faster once the narrow loads
+// were gone: the page's load instructions, not the bytes in flight, bound
+// these streams.
+template <int D, int KC>
+constexpr int qstream_buffers() { return 2; }
 
 __device__ __forceinline__ uint32_t pk_bf16(float a, float b) {
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{a, b}, bf16x2v_t));
@@ -101,10 +136,48 @@ __device__ __forceinline__ f32x2_t fp8_pair(uint32_t w, int h) {
     return h ? __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w, 1.0f, true) : __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w, 1.0f, false);
 }
 
+// INT8-G64 V codes through LDS.  A wave's 16 rows of a page (16 x D bytes)
+// arrive as D/64 loads of 16 bytes per lane (a few wide loads in place of
+// 4 x D/64 four-byte ones: the narrow loads, not the bytes, bound the
+// stream); the wave writes them into its own LDS stage and each lane then
+// reads the four bytes of every (key, scale group) its PV tiles take.  Chunk
+// (row R, 16-byte column k) of the rows sits at slot R' * D/16 + k' of the
+// stage (lane l of load c holds slot 64 c + l), permuted so that every such
+// read (64 lanes, 16 rows x 4 chunks) hits 64 distinct banks:
+//   D = 64:  R' = 4 (R % 4) + R / 4,        k' = k
+//   D = 128: R' = 2 (R % 8) + R / 8,        k' = k ^ 4 ((R / 4) % 2)
+//   D = 256: R' = R,                        k' = k ^ 4 ((R / 4) % 4)
+template <int D>
+__device__ __forceinline__ uint32_t vstage_src(int slot) {   // byte offset within the 16 rows of the chunk at slot
+    constexpr int VCH = D / 16;
+    const int rp = slot / VCH, kp = slot % VCH;
+    int R, k;
+    if constexpr (D == 64) {
+        R = 4 * (rp % 4) + rp / 4;
+        k = kp;
+    } else if constexpr (D == 128) {
+        R = 8 * (rp % 2) + rp / 2;
+        k = kp ^ (4 * ((R / 4) % 2));
+    } else {
+        R = rp;
+        k = kp ^ (4 * ((R / 4) % 4));
+    }
+    return uint32_t(R * D + 16 * k);
+}
+// byte offset within the stage of the four bytes of key 4 lg + r (r = 0: add
+// 256 r for the others), dims 64 g + 4 li .. +3
+template <int D>
+__device__ __forceinline__ uint32_t vstage_dst(int li, int lg, int g) {
+    if constexpr (D == 64) return uint32_t(64 * lg + 4 * li);
+    else if constexpr (D == 128) return uint32_t(1024 * (lg % 2) + 128 * (lg / 2) + 64 * (g ^ (lg % 2)) + 4 * li);
+    else return uint32_t(1024 * lg + 64 * (g ^ lg) + 4 * li);
+}
+
 template <int D, int KC, int VC, int SB>
 __global__ void __launch_bounds__(256, (qstream_bpc<D, KC>())) paged_qstream_kernel(DecodeArgs a) {
     using namespace plan;
     constexpr int BPC = qstream_bpc<D, KC>();
+    constexpr int PF = qstream_buffers<D, KC>();
     constexpr int NT = 256;
     constexpr int NCH = D / 8;                     // 16-byte chunks of a bf16 query row
     constexpr int NU = D / 64;                     // 64-dim groups: K operand units of 16 dims per lane
@@ -122,14 +195,22 @@ __global__ void __launch_bounds__(256, (qstream_bpc<D, KC>())) paged_qstream_ker
     constexpr int NPV = VI8 ? NU : 1;              // copies of P: one per V scale group
     constexpr int NKW = KF4 ? 2 : 4;               // K code words per group and lane
     // K scale loads per lane: 16 bytes each (8 for a shorter run of four keys' scales)
-    constexpr int NKS4 = KF4 ? (KSROW + 15) / 16 : (4 * KSROW + 15) / 16;
+    constexpr int NKS4 = KF4 ? (KSROW + 15) / 16 : 1;
     constexpr int NVW = VI8 ? NU : (VF8 ? NDT / 4 : NDT / 8);         // V code words per key and lane
-    constexpr int NVS4 = (VI8 || VF8) ? (4 * VSROW + 15) / 16 : 0;   // V scale loads per lane, as for K
+    constexpr int NVS4 = (VI8 || VF8) ? 1 : 0;    // V scale loads per lane, as for K
+    // INT8-G64 / FP8-row scales: the four keys of a 16-lane row have at most
+    // 16 dwords of scales per side; lane li loads dword li of its row's run
+    // and each scale is broadcast from the lane that holds it
+    static_assert(KF4 || 4 * KSROW <= 64, "K scales per row");
+    static_assert(!(VI8 || VF8) || 4 * VSROW <= 64, "V scales per row");
     static_assert(KC != CODEC_BF16 && VC != CODEC_BF16, "quantized sides only");
     static_assert(D == 64 || D == 128 || D == 256, "shape");
     static_assert(NVW >= 1 && NKS4 >= 1 && (VI8 || VF8 || NVS4 == 0), "register layout");
     static_assert(QSEG >= 1 && QSEG * NCOL * NCH == QCHUNKS && QCHUNKS % NT == 0 && PAGES % NT == 0, "LDS shapes");
     typedef unsigned int vword_t __attribute__((ext_vector_type(NVW)));
+    constexpr bool VST = VI8;                      // V codes through an LDS stage
+    constexpr int NVL = D / 64;                    // 16-byte V loads per page and lane
+    constexpr int VSTAGE = 16 * D;                 // bytes of a wave's stage
 
     __shared__ int2 pinfo[PAGES];                  // the block's pages: (slice number of (g, h) or -1, meta)
     __shared__ u32x4 qcache[QCHUNKS];              // query rows of the first QSEG units: [unit][column][chunk]
@@ -138,6 +219,7 @@ __global__ void __launch_bounds__(256, (qstream_bpc<D, KC>())) paged_qstream_ker
     __shared__ int ent_s[kMaxEnt][kEntWords];
     __shared__ int seg_s[kMaxSeg][kSegWords];
     __shared__ int exp_s[kMaxEnt * kMaxH];         // pieces per (entry, KV head)
+    __shared__ __attribute__((aligned(16))) u32x4 vstage[VST ? 4 * VSTAGE / 16 : 1];   // [wave]
 
     const int tid = int(threadIdx.x);
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -217,12 +299,16 @@ __global__ void __launch_bounds__(256, (qstream_bpc<D, KC>())) paged_qstream_ker
     char* ksp = static_cast<char*>(a.pv.lv.k_scale);
     char* vsp = static_cast<char*>(a.pv.lv.v_scale);
     const int kq = 16 * w + li, tk0 = 16 * w + 4 * lg;
-    u32x4 kbuf[2][NU];                             // K units (NVFP4: words 0-1)
-    u32x4 ksbuf[2][NKS4];                          // K scales: keys tk0 .. tk0+3 (NVFP4: key kq's row)
-    vword_t vbuf[2][4];                            // V code words of keys tk(r)
-    u32x4 vsbuf[2][NVS4 > 0 ? NVS4 : 1];           // V scales of keys tk(r) (INT8, FP8)
-    uint32_t vsb[2][4];                            // NVFP4 V: the word holding key tk(r)'s scale byte
-    int pmeta[2];
+    u32x4 kbuf[PF][NU];                            // K units (NVFP4: words 0-1)
+    u32x4 ksbuf[KF4 ? PF : 1][NKS4];               // NVFP4 K scales: key kq's row
+    uint32_t ksw[PF], vsw[PF];                     // INT8 / FP8 scales: dword li of the row's run
+    vword_t vbuf[VST ? 1 : PF][4];                 // V code words of keys tk(r) (not for V through LDS)
+    u32x4 vwide[VST ? PF : 1][NVL];                // V codes for the stage: slots 64 c + lane
+    uint32_t vsb[PF][4];                           // NVFP4 V: the word holding key tk(r)'s scale byte
+    int pmeta[PF];
+    int vsrc[NVL];                                 // this lane's source offsets of the stage's chunks
+#pragma unroll
+    for (int c = 0; c < NVL; ++c) vsrc[c] = int(16 * w * VROW + vstage_src<D>(64 * c + lane));
     auto load_page = [&](int fi, int J) __attribute__((always_inline)) {
         const bool live = fi < npg;
         const int2 pi = pinfo[live ? fi : 0];
@@ -257,20 +343,20 @@ __global__ void __launch_bounds__(256, (qstream_bpc<D, KC>())) paged_qstream_ker
                 } else {
                     ksbuf[J][k] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rks, kq * KSROW + 16 * k, 0, kNonTemporal));
                 }
-            } else if constexpr (4 * KSROW >= 16) {
-                ksbuf[J][k] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rks, tk0 * KSROW + 16 * k, 0, kNonTemporal));
             } else {
-                const u32x2 x = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rks, tk0 * KSROW, 0, kNonTemporal));
-                ksbuf[J][k] = u32x4{x[0], x[1], 0u, 0u};
+                ksw[J] = __builtin_amdgcn_raw_buffer_load_b32(rks, tk0 * KSROW + 4 * li, 0, kNonTemporal);
             }
+        }
+        if constexpr (VST) {
+#pragma unroll
+            for (int c = 0; c < NVL; ++c)
+                vwide[J][c] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rvc, vsrc[c], 0, kNonTemporal));
         }
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int t = tk0 + r;
-            if constexpr (VI8) {
-#pragma unroll
-                for (int g = 0; g < NU; ++g)
-                    vbuf[J][r][g] = __builtin_amdgcn_raw_buffer_load_b32(rvc, t * VROW + 64 * g + 4 * li, 0, kNonTemporal);
+            if constexpr (VST) {
+                (void)t;
             } else if constexpr (NVW == 4) {
                 vbuf[J][r] = __builtin_bit_cast(vword_t, __builtin_amdgcn_raw_buffer_load_b128(rvc, t * VROW + 16 * li, 0, kNonTemporal));
             } else if constexpr (NVW == 2) {
@@ -281,15 +367,7 @@ __global__ void __launch_bounds__(256, (qstream_bpc<D, KC>())) paged_qstream_ker
             if constexpr (!VI8 && !VF8)            // NVFP4: the aligned word holding byte (D/16) li / 16 of the row
                 vsb[J][r] = __builtin_amdgcn_raw_buffer_load_b32(rvs, t * VSROW + (((NDT * li) / 16) & ~3), 0, kNonTemporal);
         }
-#pragma unroll
-        for (int k = 0; k < NVS4; ++k) {
-            if constexpr (4 * VSROW >= 16) {
-                vsbuf[J][k] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rvs, tk0 * VSROW + 16 * k, 0, kNonTemporal));
-            } else {
-                const u32x2 x = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rvs, tk0 * VSROW, 0, kNonTemporal));
-                vsbuf[J][k] = u32x4{x[0], x[1], 0u, 0u};
-            }
-        }
+        if constexpr (VI8 || VF8) vsw[J] = __builtin_amdgcn_raw_buffer_load_b32(rvs, tk0 * VSROW + 4 * li, 0, kNonTemporal);
     };
 
     // query rows of the first QSEG units (columns past a unit's last read
@@ -305,7 +383,8 @@ __global__ void __launch_bounds__(256, (qstream_bpc<D, KC>())) paged_qstream_ker
         if (s < nseg && c < ncol_of(s)) src = reinterpret_cast<const u32x4*>(q_row(col_of(s, c), sg - s * H)) + ch;
         qv[k] = *src;
     }
-    load_page(0, 0);
+#pragma unroll
+    for (int k = 0; k < PF - 1; ++k) load_page(k, k);
 #pragma unroll
     for (int k = 0; k < QCHUNKS / NT; ++k) qcache[k * NT + tid] = qv[k];
     block_lds_barrier();
@@ -420,9 +499,19 @@ __global__ void __launch_bounds__(256, (qstream_bpc<D, KC>())) paged_qstream_ker
     auto compute = [&](auto jc) __attribute__((always_inline)) {
         constexpr int J = decltype(jc)::value;
         const int meta = pmeta[J];
-        const int lim = meta & 255;                // rows any column of the unit may see
-        if (lim <= 16 * w) return;                 // none of them among this wave's keys
+        // rows any column of the unit may see; a wave whose keys all lie past
+        // them still runs the page (its codes read as zeros and its scores are
+        // masked, so it adds exact zeros): a skipped page would leave its
+        // loads pending on one path into the ring, and the compiler's waits
+        // after the merge would then cover the next page's loads as well
+        const int lim = meta & 255;
         const int tok0 = ((meta >> 9) & 0x7fff) * kPage;
+        if constexpr (VST) {                       // the page's V codes into this wave's stage
+            typedef u32x4 __attribute__((address_space(3)))* lds_u32x4_ptr;
+            const lds_u32x4_ptr sw = (lds_u32x4_ptr)(&vstage[0]) + w * (VSTAGE / 16);
+#pragma unroll
+            for (int c = 0; c < NVL; ++c) sw[64 * c + lane] = vwide[J][c];
+        }
 
         // QK^T: S^T[16 keys x 16 columns], per K scale group for INT8
         f32x4_t sacc[NGK];
@@ -467,7 +556,7 @@ __global__ void __launch_bounds__(256, (qstream_bpc<D, KC>())) paged_qstream_ker
         // K scales of key tk(r): float r*NU + g (INT8) or r (FP8) of the loaded run
         // (2-byte scales: a key at or past the page's last visible row counts 0)
         auto kscale = [&](int r, int g) __attribute__((always_inline)) {
-            const float sc = scale_of<SB>(ksbuf[J], KI8 ? r * NU + g : r);
+            const float sc = row_scale<SB>(ksw[J], KI8 ? r * NU + g : r);
             return SB == 2 && tk0 + r >= lim ? 0.f : sc;
         };
         float sj[4];
@@ -510,10 +599,10 @@ __global__ void __launch_bounds__(256, (qstream_bpc<D, KC>())) paged_qstream_ker
         // P^T operands [P_hi; P_lo], one per V scale group (keys past the
         // last limit have zero codes and scales from the buffer range)
         auto vscale = [&](int r, int g) __attribute__((always_inline)) {
-            const float sc = scale_of<SB>(vsbuf[J], VI8 ? r * NU + g : r);
+            const float sc = row_scale<SB>(vsw[J], VI8 ? r * NU + g : r);
             return SB == 2 && tk0 + r >= lim ? 0.f : sc;
         };
-        bf16x8_t bop[NPV];
+        s16x4_t bhi[NPV], blo[NPV];
 #pragma unroll
         for (int g = 0; g < NPV; ++g) {
             float pv[4];
@@ -522,18 +611,23 @@ __global__ void __launch_bounds__(256, (qstream_bpc<D, KC>())) paged_qstream_ker
             uint32_t h01, l01, h23, l23;
             split_bf16(pv[0], pv[1], h01, l01);
             split_bf16(pv[2], pv[3], h23, l23);
-            bop[g] = __builtin_bit_cast(bf16x8_t, u32x4{h01, h23, l01, l23});
+            bhi[g] = __builtin_bit_cast(s16x4_t, u32x2{h01, h23});
+            blo[g] = __builtin_bit_cast(s16x4_t, u32x2{l01, l23});
         }
 
-        // PV: O^T[16 dims x 16 columns] += V^T . P^T per tile
+        // PV: O^T[16 dims x 16 columns] += V^T . P_hi^T + V^T . P_lo^T per tile
         auto pv_tile = [&](int dt, uint32_t x01, uint32_t x23, int g) __attribute__((always_inline)) {
-            acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, u32x4{x01, x23, x01, x23}),
-                                                              bop[g], acc[dt], 0, 0, 0);
+            const s16x4_t vt = __builtin_bit_cast(s16x4_t, u32x2{x01, x23});
+            acc[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vt, bhi[g], acc[dt], 0, 0, 0);
+            acc[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vt, blo[g], acc[dt], 0, 0, 0);
         };
-        if constexpr (VI8) {
+        if constexpr (VST) {
+            typedef const uint32_t __attribute__((address_space(3)))* lds_u32_cptr;
+            const lds_u32_cptr st = (lds_u32_cptr)(&vstage[0]) + w * (VSTAGE / 4);
 #pragma unroll
             for (int g = 0; g < NU; ++g) {
-                const uint32_t x0 = vbuf[J][0][g], x1 = vbuf[J][1][g], x2 = vbuf[J][2][g], x3 = vbuf[J][3][g];
+                const lds_u32_cptr sg = st + vstage_dst<D>(li, lg, g) / 4;
+                const uint32_t x0 = sg[0], x1 = sg[64], x2 = sg[128], x3 = sg[192];
                 pv_tile(4 * g + 0, pk_bf16(i8f<0>(x0), i8f<0>(x1)), pk_bf16(i8f<0>(x2), i8f<0>(x3)), g);
                 pv_tile(4 * g + 1, pk_bf16(i8f<1>(x0), i8f<1>(x1)), pk_bf16(i8f<1>(x2), i8f<1>(x3)), g);
                 pv_tile(4 * g + 2, pk_bf16(i8f<2>(x0), i8f<2>(x1)), pk_bf16(i8f<2>(x2), i8f<2>(x3)), g);
@@ -567,13 +661,13 @@ __global__ void __launch_bounds__(256, (qstream_bpc<D, KC>())) paged_qstream_ker
     reset();
     int unit_k = 0;
     start_unit(unit_k, sig);
-    // page i from buffer set J, the next page in flight in the other set; every
-    // step issues the same loads (empty ranges past the block's last page), so
-    // the compiler's vector-memory waits stay exact
+    // page i from buffer set J, the next PF - 1 pages in flight in the others;
+    // every step issues the same loads (empty ranges past the block's last
+    // page), so the compiler's vector-memory waits stay exact
     auto step = [&](auto jc, int i) __attribute__((always_inline)) {
         constexpr int J = decltype(jc)::value;
         const int meta = pmeta[J];
-        load_page(i + 1, 1 - J);
+        load_page(i + PF - 1, (J + PF - 1) % PF);
         compute(jc);
         if (meta & 256) {
             finish_unit();
@@ -584,7 +678,7 @@ __global__ void __launch_bounds__(256, (qstream_bpc<D, KC>())) paged_qstream_ker
             }
         }
     };
-    for (int i0 = 0; i0 < npg; i0 += 2) ring_round<0, 2>(step, i0, npg);
+    ring_run<PF>(step, npg);
 }
 
 template <int D, int KC, int VC>

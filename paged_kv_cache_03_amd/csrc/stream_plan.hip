@@ -318,13 +318,30 @@ __global__ void __launch_bounds__(kNT) stream_plan_kernel(PlanArgs a) {
     // nspan + 1 the combine tasks; nspan + 2 the new-token lists and the
     // per-block ranges.  Without a page list one block writes the tables.
     const int role = a.pages ? int(blockIdx.x) - a.nspan : 0;
-    auto count_pieces = [&](int x) __attribute__((always_inline)) {   // pieces (block, unit) carrying (entry, head) x
-        const int b = x / H, h = x - b * H;
-        int e = 0;
-        for (int s = 0; s < nseg; ++s)
-            if ((seg[s][S_MASK] >> b) & 1) e += pieces(seg[s][S_PRE] + h * seg[s][S_N], seg[s][S_N], dq);
-        return e;
-    };
+    // roles 0 and 1: pieces (block, unit) of every unit (s, h), its first
+    // block, then the pieces carrying each (entry, KV head) x into ex
+    __shared__ int upc[kMaxSeg * kMaxH], ufirst[kMaxSeg * kMaxH];
+    if (a.pages && role <= 1) {
+        for (int y = tid; y < nseg * H; y += kNT) {
+            const int s = y / H, h = y - s * H;
+            const int n = seg[s][S_N], start = seg[s][S_PRE] + h * n;
+            upc[y] = pieces(start, n, dq);
+            ufirst[y] = dq(start);
+        }
+        block_lds_barrier();
+        int smask[kMaxSeg];
+#pragma unroll
+        for (int s = 0; s < kMaxSeg; ++s) smask[s] = s < nseg ? seg[s][S_MASK] : 0;
+        for (int x = tid; x < kMaxEnt * H; x += kNT) {
+            const int b = x / H, h = x - b * H;
+            int e = 0;
+#pragma unroll
+            for (int s = 0; s < kMaxSeg; ++s)
+                if ((smask[s] >> b) & 1) e += upc[s * H + h];
+            ex[x] = x < a.B * H ? e : 0;
+        }
+        block_lds_barrier();
+    }
     if (role == 0) {
         if (tid < H_WORDS) {
             int v = 0;
@@ -348,7 +365,7 @@ __global__ void __launch_bounds__(kNT) stream_plan_kernel(PlanArgs a) {
         if (tid < kMaxSeg * kSegWords)
             P[kOffSeg + tid] = tid / kSegWords < nseg ? seg[tid / kSegWords][tid % kSegWords] : 0;
         if (a.pages)
-            for (int x = tid; x < kMaxEnt * H; x += kNT) P[kOffExp + x] = count_pieces(x);
+            for (int x = tid; x < kMaxEnt * H; x += kNT) P[kOffExp + x] = ex[x];
         if (!a.pages && tid == 0) P[H_NTASK] = 0;
         return;
     }
@@ -356,32 +373,34 @@ __global__ void __launch_bounds__(kNT) stream_plan_kernel(PlanArgs a) {
         // combine tasks: (entry, KV head) pairs with more than one piece, in
         // pair order; a task lists its pieces in unit order, each unit's
         // slots in block order
-        __shared__ int tpair[kMaxEnt * kMaxH], tpoff[kMaxEnt * kMaxH], ntask_s;
-        for (int x = tid; x < kMaxEnt * H; x += kNT) ex[x] = x < a.B * H ? count_pieces(x) : 0;
-        block_lds_barrier();
-        if (tid < 64) {                            // wave 0: task numbers and overflow offsets
+        __shared__ int tpair[kMaxEnt * kMaxH], tpoff[kMaxEnt * kMaxH], tpre[kMaxEnt * kMaxH + 1], ntask_s;
+        if (tid < 64) {                            // wave 0: task numbers, piece and overflow offsets
             const int lane = tid;
             const int n = a.B * H, per = (n + 63) / 64;
-            int cnt = 0, over = 0;
+            int cnt = 0, over = 0, all = 0;
             for (int i = 0; i < per; ++i) {
                 const int x = lane * per + i;
                 if (x < n && ex[x] > 1) {
                     ++cnt;
                     over += max(0, ex[x] - kTaskInline);
+                    all += ex[x];
                 }
             }
-            int tb = cnt, ob = over;               // exclusive prefix sums over the lanes
+            int tb = cnt, ob = over, ab = all;     // exclusive prefix sums over the lanes
 #pragma unroll
             for (int d = 1; d < 64; d <<= 1) {
-                const int t1 = __shfl_up(tb, d), o1 = __shfl_up(ob, d);
+                const int t1 = __shfl_up(tb, d), o1 = __shfl_up(ob, d), a1 = __shfl_up(ab, d);
                 if (lane >= d) {
                     tb += t1;
                     ob += o1;
+                    ab += a1;
                 }
             }
             const int ntask = __builtin_amdgcn_readlane(tb, 63);
+            const int npiece = __builtin_amdgcn_readlane(ab, 63);
             tb -= cnt;
             ob -= over;
+            ab -= all;
             for (int i = 0; i < per; ++i) {
                 const int x = lane * per + i;
                 if (x >= n || ex[x] <= 1) continue;
@@ -395,37 +414,46 @@ __global__ void __launch_bounds__(kNT) stream_plan_kernel(PlanArgs a) {
                 rec[T_POFF] = ob;
                 tpair[tb] = x;
                 tpoff[tb] = ob;
+                tpre[tb] = ab;
                 ++tb;
                 ob += max(0, ex[x] - kTaskInline);
+                ab += ex[x];
             }
             if (lane == 0) {
                 P[H_NTASK] = ntask;
                 ntask_s = ntask;
+                tpre[ntask] = npiece;
             }
         }
         block_lds_barrier();
-        // piece lists: one thread per (task, segment) pair writes the pieces
-        // of that segment's unit, after those of the task's earlier segments
-        const int ntask = ntask_s;
+        // piece lists: one thread per piece; piece k of task t is slot j of
+        // the unit (s, h) that holds it, s the segment carrying the task's
+        // entry whose pieces cover k
+        const int ntask = ntask_s, npiece = tpre[ntask];
         int* over_list = P + off_over(H, a.G);
-        for (int y = tid; y < ntask * nseg; y += kNT) {
-            const int t = y / nseg, s = y - t * nseg;
+        int smask[kMaxSeg];
+#pragma unroll
+        for (int s = 0; s < kMaxSeg; ++s) smask[s] = s < nseg ? seg[s][S_MASK] : 0;
+        for (int idx = tid; idx < npiece; idx += kNT) {
+            int t = 0;                             // last task with tpre[t] <= idx
+            for (int step = kMaxEnt * kMaxH / 2; step > 0; step >>= 1)
+                if (t + step < ntask && tpre[t + step] <= idx) t += step;
+            const int k = idx - tpre[t];
             const int x = tpair[t], b = x / H, h = x - b * H;
-            const int mask = seg[s][S_MASK];
-            if (!((mask >> b) & 1)) continue;
-            int k = 0;                             // pieces of the earlier segments
-            for (int s2 = 0; s2 < s; ++s2)
-                if ((seg[s2][S_MASK] >> b) & 1) k += pieces(seg[s2][S_PRE] + h * seg[s2][S_N], seg[s2][S_N], dq);
-            const int ns = seg[s][S_N], start = seg[s][S_PRE] + h * ns;
-            const int f = dq(start), nsl = dq(start + ns - 1) - f + 1;
-            const int colb = __builtin_popcount(unsigned(mask) & ((1u << b) - 1u)) * seg[s][S_W];
-            int* rec = P + off_tasks(H, a.G) + size_t(t) * kTaskWords;
-            const int ob = tpoff[t];
-            for (int j = 0; j < nsl; ++j, ++k) {
-                const int v = (f + j + s * H + h) * a.ncol + colb;
-                if (k < kTaskInline) rec[T_PIECE + k] = v;
-                else over_list[ob + k - kTaskInline] = v;
+            int s = 0, j = k;
+            bool found = false;
+#pragma unroll
+            for (int s2 = 0; s2 < kMaxSeg; ++s2) {
+                if (found || !((smask[s2] >> b) & 1)) continue;
+                const int c = upc[s2 * H + h];
+                s = s2;
+                if (j < c) found = true;
+                else j -= c;
             }
+            const int colb = __builtin_popcount(unsigned(seg[s][S_MASK]) & ((1u << b) - 1u)) * seg[s][S_W];
+            const int v = (ufirst[s * H + h] + j + s * H + h) * a.ncol + colb;
+            if (k < kTaskInline) P[off_tasks(H, a.G) + size_t(t) * kTaskWords + T_PIECE + k] = v;
+            else over_list[tpoff[t] + k - kTaskInline] = v;
         }
         return;
     }
