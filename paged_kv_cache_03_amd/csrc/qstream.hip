@@ -164,6 +164,26 @@ __device__ __forceinline__ uint32_t vstage_src(int slot) {   // byte offset with
     }
     return uint32_t(R * D + 16 * k);
 }
+// NVFP4 V codes through the same kind of stage (D/2-byte rows, 16-byte chunks;
+// the D/32 bytes of key 4 lg + r that lane li takes are read at 256 r + a):
+//   D = 128: R' = 4 (R % 4) + R / 4                   (4-byte reads)
+//   D = 256: R' = 2 (R % 4) + (R / 4) % 2 + 8 (R / 8)   (8-byte reads)
+// and each 16-lane row's run of scale rows (16 x D/16 bytes) after the codes.
+template <int D>
+__device__ __forceinline__ uint32_t fp4_stage_src(int slot) {   // byte offset within the 16 rows of the chunk at slot
+    constexpr int VCH = D / 32;                  // 16-byte chunks of a row
+    const int rp = slot / VCH, k = slot % VCH;
+    int R;
+    if constexpr (D == 128) R = 4 * (rp % 4) + rp / 4;
+    else R = (rp % 8) / 2 + 4 * (rp % 2) + 8 * (rp / 8);
+    return uint32_t(R * (D / 2) + 16 * k);
+}
+template <int D>
+__device__ __forceinline__ uint32_t fp4_stage_dst(int li, int lg) {
+    if constexpr (D == 128) return uint32_t(64 * lg + 4 * li);
+    else return uint32_t(128 * (lg % 2) + 1024 * (lg / 2) + 8 * li);
+}
+
 // byte offset within the stage of the four bytes of key 4 lg + r (r = 0: add
 // 256 r for the others), dims 64 g + 4 li .. +3
 template <int D>
@@ -208,9 +228,11 @@ __global__ void __launch_bounds__(256, (qstream_bpc<D, KC>())) paged_qstream_ker
     static_assert(NVW >= 1 && NKS4 >= 1 && (VI8 || VF8 || NVS4 == 0), "register layout");
     static_assert(QSEG >= 1 && QSEG * NCOL * NCH == QCHUNKS && QCHUNKS % NT == 0 && PAGES % NT == 0, "LDS shapes");
     typedef unsigned int vword_t __attribute__((ext_vector_type(NVW)));
-    constexpr bool VST = VI8;                      // V codes through an LDS stage
-    constexpr int NVL = D / 64;                    // 16-byte V loads per page and lane
-    constexpr int VSTAGE = 16 * D;                 // bytes of a wave's stage
+    constexpr bool VF4 = !VI8 && !VF8;             // NVFP4 V
+    constexpr bool VST = VI8 || VF4;               // V codes through an LDS stage
+    constexpr int NVL = VI8 ? D / 64 : (VF4 ? D / 128 : 1);   // 16-byte V code loads per page and lane (staged V)
+    constexpr int VCODES = 16 * VROW;              // code bytes of a wave's stage, then NVFP4 scale rows
+    constexpr int VSTAGE = VF4 ? VCODES + 256 : VCODES;
 
     __shared__ int2 pinfo[PAGES];                  // the block's pages: (slice number of (g, h) or -1, meta)
     __shared__ u32x4 qcache[QCHUNKS];              // query rows of the first QSEG units: [unit][column][chunk]
@@ -304,11 +326,13 @@ __global__ void __launch_bounds__(256, (qstream_bpc<D, KC>())) paged_qstream_ker
     uint32_t ksw[PF], vsw[PF];                     // INT8 / FP8 scales: dword li of the row's run
     vword_t vbuf[VST ? 1 : PF][4];                 // V code words of keys tk(r) (not for V through LDS)
     u32x4 vwide[VST ? PF : 1][NVL];                // V codes for the stage: slots 64 c + lane
-    uint32_t vsb[PF][4];                           // NVFP4 V: the word holding key tk(r)'s scale byte
+    uint32_t vsb[VST ? 1 : PF][4];                 // NVFP4 V: the word holding key tk(r)'s scale byte (unstaged)
+    uint32_t vscw[VF4 ? PF : 1];                   // NVFP4 V, staged: dword lane of the wave's scale rows
     int pmeta[PF];
     int vsrc[NVL];                                 // this lane's source offsets of the stage's chunks
 #pragma unroll
-    for (int c = 0; c < NVL; ++c) vsrc[c] = int(16 * w * VROW + vstage_src<D>(64 * c + lane));
+    for (int c = 0; c < NVL; ++c)
+        vsrc[c] = int(16 * w * VROW + (VI8 ? vstage_src<D>(64 * c + lane) : fp4_stage_src<D>(64 * c + lane)));
     auto load_page = [&](int fi, int J) __attribute__((always_inline)) {
         const bool live = fi < npg;
         const int2 pi = pinfo[live ? fi : 0];
@@ -364,10 +388,11 @@ __global__ void __launch_bounds__(256, (qstream_bpc<D, KC>())) paged_qstream_ker
             } else {
                 vbuf[J][r] = __builtin_bit_cast(vword_t, __builtin_amdgcn_raw_buffer_load_b32(rvc, t * VROW + 4 * li, 0, kNonTemporal));
             }
-            if constexpr (!VI8 && !VF8)            // NVFP4: the aligned word holding byte (D/16) li / 16 of the row
+            if constexpr (VF4 && !VST)             // NVFP4: the aligned word holding byte (D/16) li / 16 of the row
                 vsb[J][r] = __builtin_amdgcn_raw_buffer_load_b32(rvs, t * VSROW + (((NDT * li) / 16) & ~3), 0, kNonTemporal);
         }
         if constexpr (VI8 || VF8) vsw[J] = __builtin_amdgcn_raw_buffer_load_b32(rvs, tk0 * VSROW + 4 * li, 0, kNonTemporal);
+        if constexpr (VF4 && VST) vscw[J] = __builtin_amdgcn_raw_buffer_load_b32(rvs, 16 * w * VSROW + 4 * lane, 0, kNonTemporal);
     };
 
     // query rows of the first QSEG units (columns past a unit's last read
@@ -511,6 +536,10 @@ __global__ void __launch_bounds__(256, (qstream_bpc<D, KC>())) paged_qstream_ker
             const lds_u32x4_ptr sw = (lds_u32x4_ptr)(&vstage[0]) + w * (VSTAGE / 16);
 #pragma unroll
             for (int c = 0; c < NVL; ++c) sw[64 * c + lane] = vwide[J][c];
+            if constexpr (VF4) {
+                typedef uint32_t __attribute__((address_space(3)))* lds_u32_ptr;
+                ((lds_u32_ptr)(sw + VCODES / 16))[lane] = vscw[J];
+            }
         }
 
         // QK^T: S^T[16 keys x 16 columns], per K scale group for INT8
@@ -621,7 +650,7 @@ __global__ void __launch_bounds__(256, (qstream_bpc<D, KC>())) paged_qstream_ker
             acc[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vt, bhi[g], acc[dt], 0, 0, 0);
             acc[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vt, blo[g], acc[dt], 0, 0, 0);
         };
-        if constexpr (VST) {
+        if constexpr (VI8) {                       // INT8-G64 V: four bytes per key, group and lane from the stage
             typedef const uint32_t __attribute__((address_space(3)))* lds_u32_cptr;
             const lds_u32_cptr st = (lds_u32_cptr)(&vstage[0]) + w * (VSTAGE / 4);
 #pragma unroll
@@ -635,9 +664,20 @@ __global__ void __launch_bounds__(256, (qstream_bpc<D, KC>())) paged_qstream_ker
             }
         } else {
             float sc[4];
-            if constexpr (!VF8) {
+            vword_t vrow[4];                       // the lane's code words of keys tk(r)
+            if constexpr (VF4) {
+                typedef const vword_t __attribute__((address_space(3)))* lds_vword_cptr;
+                typedef const uint8_t __attribute__((address_space(3)))* lds_u8_cptr;
+                typedef const char __attribute__((address_space(3)))* lds_byte_cptr;
+                const lds_byte_cptr sb = (lds_byte_cptr)(&vstage[0]) + w * VSTAGE;
 #pragma unroll
-                for (int r = 0; r < 4; ++r) sc[r] = e4m3_f32(vsb[J][r] >> (8 * (((NDT * li) / 16) & 3)));
+                for (int r = 0; r < 4; ++r) {
+                    vrow[r] = *(lds_vword_cptr)(sb + fp4_stage_dst<D>(li, lg) + 256 * r);
+                    sc[r] = e4m3_f32(*(lds_u8_cptr)(sb + VCODES + (tk0 - 16 * w + r) * VSROW + (NDT * li) / 16));
+                }
+            } else {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) vrow[r] = vbuf[J][r];
             }
             // two tiles per step: dims 2q and 2q + 1 of the lane's run
 #pragma unroll
@@ -646,9 +686,9 @@ __global__ void __launch_bounds__(256, (qstream_bpc<D, KC>())) paged_qstream_ker
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     if constexpr (VF8) {
-                        f[r] = fp8_pair(vbuf[J][r][q / 2], q & 1);
+                        f[r] = fp8_pair(vrow[r][q / 2], q & 1);
                     } else {
-                        f[r] = fp4_pair(vbuf[J][r][q / 4], q & 3);
+                        f[r] = fp4_pair(vrow[r][q / 4], q & 3);
                         f[r] = f[r] * sc[r];
                     }
                 }
