@@ -426,34 +426,42 @@ __global__ void __launch_bounds__(kNT) stream_plan_kernel(PlanArgs a) {
             }
         }
         block_lds_barrier();
-        // piece lists: one thread per piece; piece k of task t is slot j of
-        // the unit (s, h) that holds it, s the segment carrying the task's
-        // entry whose pieces cover k
-        const int ntask = ntask_s, npiece = tpre[ntask];
+        // piece lists: a group of nt threads per task (no search for the
+        // task); piece k of task t is slot j of the unit (s, h) that holds it,
+        // s the segment carrying the task's entry whose pieces cover k
+        const int ntask = ntask_s;
         int* over_list = P + off_over(H, a.G);
         int smask[kMaxSeg];
 #pragma unroll
         for (int s = 0; s < kMaxSeg; ++s) smask[s] = s < nseg ? seg[s][S_MASK] : 0;
-        for (int idx = tid; idx < npiece; idx += kNT) {
-            int t = 0;                             // last task with tpre[t] <= idx
-            for (int step = kMaxEnt * kMaxH / 2; step > 0; step >>= 1)
-                if (t + step < ntask && tpre[t + step] <= idx) t += step;
-            const int k = idx - tpre[t];
-            const int x = tpair[t], b = x / H, h = x - b * H;
-            int s = 0, j = k;
-            bool found = false;
+        const int nt = ntask > 0 ? max(1, kNT / ntask) : 1, ngroups = kNT / nt;
+        if (tid / nt < ngroups) {
+            for (int t = tid / nt; t < ntask; t += ngroups) {
+                const int x = tpair[t], b = x / H, h = x - b * H;
+                const int E = tpre[t + 1] - tpre[t];
+                int c[kMaxSeg];                    // pieces of each segment's unit carrying b
 #pragma unroll
-            for (int s2 = 0; s2 < kMaxSeg; ++s2) {
-                if (found || !((smask[s2] >> b) & 1)) continue;
-                const int c = upc[s2 * H + h];
-                s = s2;
-                if (j < c) found = true;
-                else j -= c;
+                for (int s2 = 0; s2 < kMaxSeg; ++s2) {
+                    const int v = upc[min(s2, max(nseg - 1, 0)) * H + h];
+                    c[s2] = (smask[s2] >> b) & 1 ? v : 0;
+                }
+                int* rec = P + off_tasks(H, a.G) + size_t(t) * kTaskWords;
+                for (int k = tid % nt; k < E; k += nt) {
+                    int s = 0, j = k;
+                    bool found = false;
+#pragma unroll
+                    for (int s2 = 0; s2 < kMaxSeg; ++s2) {
+                        if (found || c[s2] == 0) continue;
+                        s = s2;
+                        if (j < c[s2]) found = true;
+                        else j -= c[s2];
+                    }
+                    const int colb = __builtin_popcount(unsigned(seg[s][S_MASK]) & ((1u << b) - 1u)) * seg[s][S_W];
+                    const int v = (ufirst[s * H + h] + j + s * H + h) * a.ncol + colb;
+                    if (k < kTaskInline) rec[T_PIECE + k] = v;
+                    else over_list[tpoff[t] + k - kTaskInline] = v;
+                }
             }
-            const int colb = __builtin_popcount(unsigned(seg[s][S_MASK]) & ((1u << b) - 1u)) * seg[s][S_W];
-            const int v = (ufirst[s * H + h] + j + s * H + h) * a.ncol + colb;
-            if (k < kTaskInline) P[off_tasks(H, a.G) + size_t(t) * kTaskWords + T_PIECE + k] = v;
-            else over_list[tpoff[t] + k - kTaskInline] = v;
         }
         return;
     }
@@ -493,9 +501,18 @@ __global__ void __launch_bounds__(kNT) stream_plan_kernel(PlanArgs a) {
     }
 
     // page list: this block's span of stream positions, four per thread with
-    // the table reads issued together
+    // the table reads issued together; the segment starts, the entries' rows
+    // and their new-token pages in registers
     int2* pages = reinterpret_cast<int2*>(P + off_pages(H, a.G));
     const int u_end = min(total, (int(blockIdx.x) + 1) * kPlanSpan);
+    int pre[kMaxSeg], erow[kMaxEnt], enew[kMaxEnt];
+#pragma unroll
+    for (int t = 0; t < kMaxSeg; ++t) pre[t] = t < nseg ? seg[t][S_PRE] : INT_MAX;
+#pragma unroll
+    for (int b = 0; b < kMaxEnt; ++b) {
+        erow[b] = ent[b][E_ROW];
+        enew[b] = (!a.chunk && ent[b][E_KEYS] > 0) ? (ent[b][E_KEYS] - 1) >> kPageShift : -1;
+    }
     for (int u0 = int(blockIdx.x) * kPlanSpan + tid; u0 < u_end; u0 += 4 * kNT) {
         int g[4], sl[4], meta[4], dst[4];
 #pragma unroll
@@ -503,21 +520,24 @@ __global__ void __launch_bounds__(kNT) stream_plan_kernel(PlanArgs a) {
             const int u = u0 + k * kNT;
             dst[k] = -1;
             if (u < u_end) {
-                int s, h, pp;
-                locate(u, s, h, pp);
-                const int p = seg[s][S_P0] + pp;
-                const int row = ent[seg[s][S_OWNER]][E_ROW];
+                int s = 0;                         // last segment with S_PRE <= u (the starts increase)
+#pragma unroll
+                for (int t = 1; t < kMaxSeg; ++t) s += pre[t] <= u ? 1 : 0;
+                const int n = seg[s][S_N], p0 = seg[s][S_P0], owner = seg[s][S_OWNER];
+                const int mask = seg[s][S_MASK], maxk = seg[s][S_MAXKEYS];
+                const int off = u - seg[s][S_PRE];
+                const int h = Div(n)(off), pp = off - h * n;
+                const int p = p0 + pp;
+                int row = erow[0], patch = 0;      // patch: an entry's new token lies in this page (decode)
+#pragma unroll
+                for (int b = 0; b < kMaxEnt; ++b) {
+                    row = owner == b ? erow[b] : row;
+                    patch |= (((mask >> b) & 1) && enew[b] == p) ? kPatchBit : 0;
+                }
                 g[k] = a.table[size_t(row) * a.L + p];
                 sl[k] = h;
-                const int lim = min(kPage, seg[s][S_MAXKEYS] - p * kPage);
-                int patch = 0;                     // decode: an entry's new token lies in this page
-                if (!a.chunk) {
-                    const int mask = seg[s][S_MASK];
-                    for (int b = 0; b < kMaxEnt; ++b)
-                        if (((mask >> b) & 1) && ent[b][E_KEYS] > 0 && ((ent[b][E_KEYS] - 1) >> kPageShift) == p)
-                            patch = kPatchBit;
-                }
-                meta[k] = lim | (pp == seg[s][S_N] - 1 ? 256 : 0) | (p << 9) | patch;
+                const int lim = min(kPage, maxk - p * kPage);
+                meta[k] = lim | (pp == n - 1 ? 256 : 0) | (p << 9) | patch;
                 const int i = dq(u);
                 dst[k] = i * a.qcap + (u - i * Q);
             }
