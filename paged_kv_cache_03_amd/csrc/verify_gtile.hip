@@ -69,14 +69,13 @@ struct GTileArgs {
 };
 
 // bytes per page row (one key of one KV head) of a side's code and scale
-// planes, and whether its dequantized values need a second bf16 term
+// planes
 template <int C, int D, int SB>
 struct GRow {
     static constexpr int code = C == CODEC_BF16 ? 2 * D : (C == CODEC_NVFP4_G16 ? D / 2 : D);
     static constexpr int chunk = code / (D / 8);   // code bytes of one 8-dim chunk: 16, 8 or 4
     static constexpr int scale = C == CODEC_BF16 ? 0 : C == CODEC_INT8_G64 ? SB * (D / 64)
                                                     : C == CODEC_FP8_ROW  ? SB : D / 16;
-    static constexpr bool lo = C == CODEC_INT8_G64 || C == CODEC_FP8_ROW;
 };
 
 template <int D>
@@ -185,21 +184,26 @@ __global__ void __launch_bounds__(512) verify_gtile_kernel(GTileArgs a) {
     constexpr int WCT = TCOL / 64;                 // 16-column tiles per wave
     constexpr int TTOK = TCOL / GQ;                // chunk tokens per tile
     constexpr float kHiOnly = 1.f / 256.f;         // largest weight of a page that takes p as one bf16 term
-    // INT8-G64 and FP8-row K: the K tile holds the codes (exact in bf16) and
-    // the scales act on each key's per-group partial scores; other sides hold
-    // dequantized values, V as a bf16 pair where they are not exact in bf16
+    // INT8-G64 and FP8-row sides: the tile holds the codes (exact in bf16);
+    // the K scales act on each key's per-group partial scores, the V scales on
+    // the key's probability (one copy of P per V scale group, as p * s rounded
+    // to bf16 like p itself).  NVFP4 and BF16 sides hold their values (exact in
+    // bf16).
     constexpr bool KSC = KC == CODEC_INT8_G64 || KC == CODEC_FP8_ROW;
     constexpr int NGK = KC == CODEC_INT8_G64 ? D / 64 : 1;   // score accumulators: one per K scale group
-    constexpr bool VLO = GRow<VC, D, SB>::lo;
+    constexpr bool VSC = VC == CODEC_INT8_G64 || VC == CODEC_FP8_ROW;
+    constexpr int NGV = VC == CODEC_INT8_G64 ? D / 64 : 1;   // copies of P: one per V scale group
     constexpr int PLANE = 64 * NCH;                // u32x4 slots of one bf16 page tile
-    constexpr int OFF_VH = PLANE, OFF_VL = 2 * PLANE;
-    constexpr int NPL = 2 + (VLO ? 1 : 0);
+    constexpr int OFF_VH = PLANE;
+    constexpr int NPL = 2;
     constexpr int OFF_KS = NPL * PLANE;            // K scales [group][64 keys] as fp32
     constexpr int KS_SLOTS = KSC ? NGK * 64 / 4 : 0;
+    constexpr int OFF_VS = OFF_KS + KS_SLOTS;      // V scales [group][64 keys] as fp32
+    constexpr int VS_SLOTS = VSC ? NGV * 64 / 4 : 0;
     constexpr int MERGE = WCT * NDT * 4 * 64 * 4 / 16 * 4;   // u32x4 slots of the end merge (4 column ranges)
     // two stages of tiles where they fit in LDS (the next page is converted
     // while the current one is computed), else one
-    constexpr int STAGE = NPL * PLANE + KS_SLOTS;
+    constexpr int STAGE = NPL * PLANE + KS_SLOTS + VS_SLOTS;
     constexpr int NSTG = 2 * STAGE * 16 <= 144 * 1024 ? 2 : 1;
     constexpr int SLOTS = NSTG * STAGE > MERGE ? NSTG * STAGE : MERGE;
     static_assert(J >= 1 && 64 * NCH % NT == 0 && TCOL % GQ == 0, "shape");
@@ -303,7 +307,7 @@ __global__ void __launch_bounds__(512) verify_gtile_kernel(GTileArgs a) {
             int r, x;
             job_of<NCH>(tid + NT * k, r, x);
             const bool vis = r < lim;
-            u32x4 khi, vhi, vlo;
+            u32x4 khi, vhi;
             if constexpr (KC == CODEC_BF16) {
                 khi = vis ? rk.code[k] : u32x4{0u, 0u, 0u, 0u};
             } else if constexpr (KC == CODEC_INT8_G64) {
@@ -340,20 +344,41 @@ __global__ void __launch_bounds__(512) verify_gtile_kernel(GTileArgs a) {
             }
             if constexpr (VC == CODEC_BF16) {
                 vhi = vis ? rv.code[k] : u32x4{0u, 0u, 0u, 0u};
-                vlo = vhi;
-            } else {
+            } else if constexpr (VC == CODEC_INT8_G64) {
+                const u32x4 c = rv.code[k];
+                uint32_t w[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const uint32_t src = c[e >> 1] >> (16 * (e & 1));
+                    w[e] = __builtin_bit_cast(uint32_t, __builtin_convertvector(
+                        f32x2_t{float(int8_t(src & 0xFFu)), float(int8_t((src >> 8) & 0xFFu))}, bf16x2v_t));
+                }
+                vhi = vis ? u32x4{w[0], w[1], w[2], w[3]} : u32x4{0u, 0u, 0u, 0u};
+            } else if constexpr (VC == CODEC_FP8_ROW) {
+                const u32x4 c = rv.code[k];
+                uint32_t w[4];
+#pragma unroll
+                for (int e = 0; e < 2; ++e) {
+                    w[2 * e] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c[e], 1.0f, false));
+                    w[2 * e + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c[e], 1.0f, true));
+                }
+                vhi = vis ? u32x4{w[0], w[1], w[2], w[3]} : u32x4{0u, 0u, 0u, 0u};
+            } else {   // NVFP4 V: dequantized values, exact in bf16
                 float v[8];
                 dequant8<VC, SB>(rv.code[k], rv.scale[k], v);
                 uint32_t hw[4], lw[4];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) split_bf16(v[2 * e], v[2 * e + 1], hw[e], lw[e]);
                 vhi = vis ? u32x4{hw[0], hw[1], hw[2], hw[3]} : u32x4{0u, 0u, 0u, 0u};
-                vlo = vis ? u32x4{lw[0], lw[1], lw[2], lw[3]} : u32x4{0u, 0u, 0u, 0u};
+            }
+            if constexpr (VSC) {                   // the chunk that starts a V scale group writes its scale
+                constexpr int GCH = VC == CODEC_INT8_G64 ? 8 : NCH;    // chunks per scale group
+                if (x % GCH == 0)
+                    reinterpret_cast<float*>(&tl[OFF_VS])[(x / GCH) * 64 + r] = vis ? wide_scale<SB>(rv.scale[k]) : 0.f;
             }
             const int ks = r * NCH + (x ^ kswz(r)), vs = r * NCH + (x ^ vswz(r));
             tl[ks] = khi;
             tl[OFF_VH + vs] = vhi;
-            if constexpr (VLO) tl[OFF_VL + vs] = vlo;
         }
     };
 
@@ -464,7 +489,7 @@ __global__ void __launch_bounds__(512) verify_gtile_kernel(GTileArgs a) {
         for (int ct = 0; ct < WCT; ++ct)
             need_lo |= !(__builtin_amdgcn_exp2f(pm[ct] - m_ref[ct]) <= kHiOnly * lsum[ct][0]);
         float p[WCT][8];
-        bf16x8_t phi[WCT];
+        bf16x8_t phi[WCT];                         // rne(p): the column sums, and the PV weights without V scales
 #pragma unroll
         for (int ct = 0; ct < WCT; ++ct) {
             const float moff = m_ref[ct] == -INFINITY ? 0.f : -m_ref[ct];
@@ -478,47 +503,80 @@ __global__ void __launch_bounds__(512) verify_gtile_kernel(GTileArgs a) {
                                            __builtin_convertvector(f32x2_t{p[ct][2 * e], p[ct][2 * e + 1]}, bf16x2v_t));
             phi[ct] = __builtin_bit_cast(bf16x8_t, u32x4{hv[0], hv[1], hv[2], hv[3]});
         }
+        // V scales of this lane's keys kr0 + 16 kt + 4 lg + r, per group
+        f32x4_t vsc[NGV][2];
+        if constexpr (VSC) {
+            const float* vst = reinterpret_cast<const float*>(&lds[sb + OFF_VS]);
 #pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) {
-            const bf16x8_t va = read_vt(sb + OFF_VH, dt);
+            for (int g = 0; g < NGV; ++g)
 #pragma unroll
-            for (int ct = 0; ct < WCT; ++ct)
-                acc[ct][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, phi[ct], acc[ct][dt], 0, 0, 0);
-            if constexpr (VLO) {
-                const bf16x8_t vl = read_vt(sb + OFF_VL, dt);
+                for (int kt = 0; kt < 2; ++kt)
+                    vsc[g][kt] = *reinterpret_cast<const f32x4_t*>(vst + g * 64 + kr0 + 16 * kt + 4 * lg);
+        }
+        // the PV weights of V scale group g (term 0: rne(p * s); term 1: the remainder)
+        auto weights = [&](int g, int ct, bool lo_term) __attribute__((always_inline)) {
+            uint32_t hv[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                float x0 = p[ct][2 * e], x1 = p[ct][2 * e + 1];
+                if constexpr (VSC) {
+                    x0 *= vsc[g][(2 * e) >> 2][(2 * e) & 3];
+                    x1 *= vsc[g][(2 * e + 1) >> 2][(2 * e + 1) & 3];
+                }
+                uint32_t h, l;
+                split_bf16(x0, x1, h, l);
+                hv[e] = lo_term ? l : h;
+            }
+            return __builtin_bit_cast(bf16x8_t, u32x4{hv[0], hv[1], hv[2], hv[3]});
+        };
+        constexpr int DPG = NDT / NGV;             // PV tiles per V scale group
+#pragma unroll
+        for (int g = 0; g < NGV; ++g) {
+            bf16x8_t pw[WCT];
+#pragma unroll
+            for (int ct = 0; ct < WCT; ++ct) pw[ct] = VSC ? weights(g, ct, false) : phi[ct];
+#pragma unroll
+            for (int d = 0; d < DPG; ++d) {
+                const int dt = g * DPG + d;
+                const bf16x8_t va = read_vt(sb + OFF_VH, dt);
 #pragma unroll
                 for (int ct = 0; ct < WCT; ++ct)
-                    acc[ct][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vl, phi[ct], acc[ct][dt], 0, 0, 0);
+                    acc[ct][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pw[ct], acc[ct][dt], 0, 0, 0);
             }
         }
 #pragma unroll
         for (int ct = 0; ct < WCT; ++ct) lsum[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, phi[ct], lsum[ct], 0, 0, 0);
         if (__builtin_amdgcn_ballot_w64(need_lo)) {
-            // p_lo = rne(p - p_hi), the same products on it
-            bf16x8_t plo[WCT];
+            // the remainders rne(w - rne(w)) of the weights, the same products on them
 #pragma unroll
-            for (int ct = 0; ct < WCT; ++ct) {
-                const u32x4 hu = __builtin_bit_cast(u32x4, phi[ct]);
-                uint32_t lv[4];
+            for (int g = 0; g < NGV; ++g) {
+                bf16x8_t pw[WCT];
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const float r0 = p[ct][2 * e] - __uint_as_float(hu[e] << 16);
-                    const float r1 = p[ct][2 * e + 1] - __uint_as_float(hu[e] & 0xFFFF0000u);
-                    lv[e] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{r0, r1}, bf16x2v_t));
-                }
-                plo[ct] = __builtin_bit_cast(bf16x8_t, u32x4{lv[0], lv[1], lv[2], lv[3]});
-            }
+                for (int ct = 0; ct < WCT; ++ct) pw[ct] = weights(g, ct, true);
 #pragma unroll
-            for (int dt = 0; dt < NDT; ++dt) {
-                const bf16x8_t va = read_vt(sb + OFF_VH, dt);
-#pragma unroll
-                for (int ct = 0; ct < WCT; ++ct)
-                    acc[ct][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, plo[ct], acc[ct][dt], 0, 0, 0);
-                if constexpr (VLO) {
-                    const bf16x8_t vl = read_vt(sb + OFF_VL, dt);
+                for (int d = 0; d < DPG; ++d) {
+                    const int dt = g * DPG + d;
+                    const bf16x8_t va = read_vt(sb + OFF_VH, dt);
 #pragma unroll
                     for (int ct = 0; ct < WCT; ++ct)
-                        acc[ct][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vl, plo[ct], acc[ct][dt], 0, 0, 0);
+                        acc[ct][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pw[ct], acc[ct][dt], 0, 0, 0);
+                }
+            }
+            bf16x8_t plo[WCT];
+#pragma unroll
+            for (int ct = 0; ct < WCT; ++ct) plo[ct] = weights(0, ct, true);
+            if constexpr (VSC) {
+#pragma unroll
+                for (int ct = 0; ct < WCT; ++ct) {   // the column sums take the remainder of p itself
+                    const u32x4 hu = __builtin_bit_cast(u32x4, phi[ct]);
+                    uint32_t lv[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const float r0 = p[ct][2 * e] - __uint_as_float(hu[e] << 16);
+                        const float r1 = p[ct][2 * e + 1] - __uint_as_float(hu[e] & 0xFFFF0000u);
+                        lv[e] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{r0, r1}, bf16x2v_t));
+                    }
+                    plo[ct] = __builtin_bit_cast(bf16x8_t, u32x4{lv[0], lv[1], lv[2], lv[3]});
                 }
             }
 #pragma unroll
