@@ -71,13 +71,12 @@ __device__ __forceinline__ float rounded_scale(float s32) {
     else return static_cast<float>(static_cast<_Float16>(fminf(s32, 65504.0f)));
 }
 
-// Quantize and store one row (EPL elements per lane) of one side.
+// Quantize and store one row (EPL elements per lane, loaded by load_row) of
+// one side.
 template <int D, int CODEC, int SB>
-__device__ __forceinline__ void write_side(void* code, void* scale, size_t slot, const uint16_t* src, int lane) {
+__device__ __forceinline__ void write_side(void* code, void* scale, size_t slot, const float (&x)[D / 64],
+                                           const uint32_t (&bits)[D / 64], int lane) {
     constexpr int EPL = D / 64;
-    float x[EPL];
-    uint32_t bits[EPL];
-    load_row<EPL>(src, lane, x, bits);
     if constexpr (CODEC == CODEC_BF16) {
         uint16_t* c = static_cast<uint16_t*>(code) + slot * D + lane * EPL;
 #pragma unroll
@@ -133,24 +132,38 @@ __device__ __forceinline__ void write_side(void* code, void* scale, size_t slot,
 
 template <int D, int KC, int VC, int SB>
 __global__ void __launch_bounds__(256) append_kernel(AppendArgs a) {
+    constexpr int EPL = D / 64;
     const int lane = threadIdx.x & 63;
     const int r = blockIdx.x * 4 + int(threadIdx.x >> 6);
     const int H = a.pv.H;
     if (r >= a.total * H) return;
     const int t = r / H, h = r - (r / H) * H;
+    // the row's values first (they depend on nothing else), then the entry of
+    // token t: the entries k in [1, B) whose rows start at or before t (the
+    // starts do not decrease), one load per lane and a ballot for B <= 64
+    float kx[EPL], vx[EPL];
+    uint32_t kb[EPL], vb[EPL];
+    load_row<EPL>(a.k + size_t(r) * D, lane, kx, kb);
+    load_row<EPL>(a.v + size_t(r) * D, lane, vx, vb);
     int b = 0;
-    while (b + 1 < a.B && t >= a.cu[b + 1]) ++b;
-    if (t < a.cu[b] || t >= a.cu[b + 1]) return;
-    const int p = a.pos0[b] + (t - a.cu[b]);
-    const int row = a.table_rows[b];
+    if (a.B <= 64) {
+        const int start = lane < a.B ? a.cu[lane] : 0;     // cu[k]: first row of entry k
+        b = __builtin_popcountll(__builtin_amdgcn_ballot_w64(lane >= 1 && lane < a.B && start <= t));
+    } else {
+        while (b + 1 < a.B && t >= a.cu[b + 1]) ++b;
+    }
+    const int c0 = a.cu[b], c1 = a.cu[b + 1];
+    const int p0 = a.pos0[b], row = a.table_rows[b];
+    if (t < c0 || t >= c1) return;
+    const int p = p0 + (t - c0);
     if (p < 0 || row < 0 || row >= a.pv.C) return;
     const int blk = p >> kPageShift, o = p & (kPage - 1);
     if (blk >= a.pv.L) return;
     const int g = a.pv.table[size_t(row) * a.pv.L + blk];
     if (g < 0 || g >= a.pv.M) return;                      // unmapped: caller guarantee broken, skip
     const size_t slot = (size_t(g) * a.pv.sg + size_t(h) * a.pv.sh) * kPage + o;   // row of (g, h, o) in every plane
-    write_side<D, KC, SB>(a.pv.lv.k_code, a.pv.lv.k_scale, slot, a.k + size_t(r) * D, lane);
-    write_side<D, VC, SB>(a.pv.lv.v_code, a.pv.lv.v_scale, slot, a.v + size_t(r) * D, lane);
+    write_side<D, KC, SB>(a.pv.lv.k_code, a.pv.lv.k_scale, slot, kx, kb, lane);
+    write_side<D, VC, SB>(a.pv.lv.v_code, a.pv.lv.v_scale, slot, vx, vb, lane);
 }
 
 template <int D>
