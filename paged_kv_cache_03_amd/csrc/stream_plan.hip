@@ -179,26 +179,33 @@ __global__ void __launch_bounds__(kNT) stream_plan_kernel(PlanArgs a) {
         const int lane = tid;
         const bool me = lane < a.B;
         const int np = me ? ent[lane][E_NPAGES] : 0;
-        int par = -1, ell = 0, root = lane, tsize = 1;   // this lane's entry (tsize: as a root)
-        for (int b = 0; b < a.B; ++b) {
-            if (__builtin_amdgcn_readlane(np, b) == 0) continue;
-            // earlier entry with the longest shared run whose tree has room (ties: lowest index)
-            int key = -1;
-            const int ts = __shfl(tsize, root);
-            if (a.emax > 1 && lane < b && np > 0 && ts < a.emax && lcp[b][lane & 7] > 0)
-                key = lcp[b][lane & 7] * 8 + (7 - lane);
+        // this lane's entry: parent, shared run, root, size of its tree; the
+        // trees grow one entry at a time (entry b joins the tree of its
+        // parent), every member lane keeping the tree's size, so each step
+        // is register reads (readlane) and lane-local updates
+        int par = -1, ell = 0, root = lane, tsz = 1;
+        int lrow[kMaxEnt];                         // lcp[b][lane]: run this lane's entry shares with entry b
 #pragma unroll
-            for (int d = 1; d < 8; d <<= 1) key = max(key, __shfl_xor(key, d));
-            key = __builtin_amdgcn_readlane(key, 0);
-            if (key >= 0) {
-                const int bp = 7 - (key & 7);
+        for (int b = 0; b < kMaxEnt; ++b) lrow[b] = lcp[b][lane & 7];
+#pragma unroll
+        for (int b = 1; b < kMaxEnt; ++b) {
+            if (b >= a.B || __builtin_amdgcn_readlane(np, b) == 0) continue;
+            // earlier entry with the longest shared run whose tree has room (ties: lowest index)
+            const int key = (a.emax > 1 && lane < b && np > 0 && tsz < a.emax && lrow[b] > 0)
+                                ? lrow[b] * 8 + (7 - lane) : -1;
+            int best = -1;
+#pragma unroll
+            for (int j = 0; j < b; ++j) best = max(best, __builtin_amdgcn_readlane(key, j));
+            if (best >= 0) {
+                const int bp = 7 - (best & 7);
                 const int r = __builtin_amdgcn_readlane(root, bp);
+                const int size = __builtin_amdgcn_readlane(tsz, bp) + 1;
                 if (lane == b) {
                     par = bp;
-                    ell = key >> 3;
+                    ell = best >> 3;
                     root = r;
                 }
-                if (lane == r) ++tsize;
+                if (root == r) tsz = size;
             }
         }
         // b's columns ride along owner o over pages [clo, chi): o = b for
