@@ -6,7 +6,8 @@ A step is one decode step of the whole batch through every layer:
     block reads for which query columns, shared prefix pages once), then for
     each layer: the append of one new token per sequence into its page
     through the block table, and the decode (split-K over pages and the
-    cross-split combine).  On BF16 pages both are one call,
+    cross-split combine).  Where the matrix-core page streams cover the pool
+    (every closed profile at the configs' shapes) both are one call,
     paged_attn_decode_append_run; otherwise kv_append + paged_attn_decode_run.
 Inputs are resident in HBM before timing; the step is idempotent (the same
 positions are re-appended, the same contexts decoded).
@@ -38,12 +39,22 @@ METRIC = "paged decode KV GB/s (% of HBM peak) + decode steps/s at C=8, 32K ctx"
 PROFILES = os.path.join(ROOT, "profiles")
 # sources of the decode kernel; the traffic summary is valid for this exact text
 DECODE_SRC = [os.path.join(ROOT, "paged_kv_cache_03_amd", "csrc", f)
-              for f in ("decode.hip", "decode_common.h", "qstream.hip", "stream_common.h", "stream_plan.h",
-                        "stream_plan.hip")]
+              for f in ("decode.hip", "decode_common.h", "qstream.hip", "codec_write.h", "stream_common.h",
+                        "stream_plan.h", "stream_plan.hip")]
 
 
 # sources of one paged_attn_verify call: the tile kernel and the page stream in chunk mode
 VERIFY_SRC = [os.path.join(ROOT, "paged_kv_cache_03_amd", "csrc", "verify.hip")] + DECODE_SRC
+
+
+
+def fused_append(wl) -> bool:
+    """paged_attn_decode_append_run covers the pool: the page streams' shapes
+    (at most 8 entries, Hq / H in {1, 2, 4, 8}; NVFP4 sides at D 128 / 256)."""
+    gq = wl.Hq // wl.H
+    fp4 = wl.profile in ("NVFP4_G16", "K8V4")
+    dims = wl.D in ((128, 256) if fp4 else (64, 128, 256))
+    return dims and wl.B <= 8 and wl.Hq % wl.H == 0 and gq in (1, 2, 4, 8)
 
 
 def source_sha256(paths) -> str:
@@ -693,7 +704,7 @@ def bench_advance(wl, args) -> int:
     qs = [_dev(wl.q(layer), dev) for layer in range(wl.layers)]
     out = torch.empty((wl.B, wl.Hq, wl.D), dtype=torch.float32, device=dev)
     ws = dp.workspace(wl.B, wl.Hq, bound)
-    fused = wl.profile == "BF16" and wl.D in (64, 128, 256)
+    fused = fused_append(wl)
     host_s = [0.0]
     crossings = [0]
 
@@ -829,9 +840,9 @@ def main() -> int:
 
     # one step: the work list of the batch state once (it depends only on the
     # block table and the lengths), then per layer the append of the step's
-    # rows and the decode run -- one launch on the BF16 page stream, which
-    # appends the rows itself
-    fused = wl.profile == "BF16" and wl.D in (64, 128, 256)
+    # rows and the decode run -- one launch on the page streams, which
+    # append the rows themselves
+    fused = fused_append(wl)
 
     def step(events=None, kern=None):
         dp.decode_plan(wl.Hq, rows_t, lens_t, max_ctx, ws)

@@ -394,9 +394,10 @@ kv_status paged_attn_decode_run(const kv_pool* pool, uint32_t layer, uint32_t B,
  * (pos0 = seq_len - 1, one token per entry) followed by
  * paged_attn_decode_run would, with the same outputs and planes.  The page
  * that receives a row must not be shared (fork and tail copy-on-write: copy
- * the tail first), as for kv_append.  BF16 pages on the matrix-core stream
- * only (D in {64, 128}, Hq / H in {1, 2, 4, 8}); KV_E_UNSUPPORTED otherwise
- * (use kv_append and paged_attn_decode_run). */
+ * the tail first), as for kv_append.  Pages on the matrix-core streams: every
+ * closed profile at D in {64, 128, 256} (NVFP4 sides at 128 and 256) with
+ * Hq / H in {1, 2, 4, 8}, at most 8 entries; KV_E_UNSUPPORTED otherwise (use
+ * kv_append and paged_attn_decode_run). */
 kv_status paged_attn_decode_append_run(const kv_pool* pool, uint32_t layer, uint32_t B, uint32_t Hq,
                                        uint32_t max_seq_len, const void* d_k, const void* d_v, const void* d_q,
                                        float sm_scale, float* d_out, void* d_ws, size_t ws_bytes, hipStream_t stream);

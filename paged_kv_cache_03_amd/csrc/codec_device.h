@@ -15,25 +15,25 @@ namespace kvs {
 
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t u16) { return __uint_as_float(u16 << 16); }
 
-// fp32 -> E4M3FN, round half to even on the 3-bit mantissa, saturate to 448.
+// fp32 -> E4M3FN, round half to even on the 3-bit mantissa, saturate to 448
+// (NaN too).  Both the subnormal and the normal result are formed and one is
+// selected, so a wave takes no branch.
 __device__ __forceinline__ uint32_t f32_to_e4m3fn(float y) {
     const uint32_t u = __float_as_uint(y);
     const uint32_t sign = (u >> 24) & 0x80u;
     const uint32_t a = u & 0x7FFFFFFFu;
-    if (a >= 0x43E00000u) return sign | 0x7Eu;           // |y| >= 448 (or NaN): saturate
-    if (a < 0x3C800000u) {                                // |y| < 2^-6: subnormal step 2^-9
-        // |y| * 2^9 is exact (power-of-two scale of a value >= 2^-149 * 2^9)
-        const float m = __builtin_rintf(__uint_as_float(a) * 512.0f);
-        return sign | uint32_t(m);                        // m == 8 encodes 2^-6 (0x08)
-    }
-    // normal: exponent e in [-6, 8]; keep 3 of 23 mantissa bits, round half to even
-    uint32_t e = (a >> 23) - 127u + 7u;                   // biased E4M3 exponent, 1..15
-    uint32_t mant = a & 0x7FFFFFu;
-    uint32_t q = mant >> 20;
+    // |y| < 2^-6: subnormal step 2^-9; |y| * 2^9 is exact (a power-of-two
+    // scale of a value >= 2^-149 * 2^9), rounded half to even (code 8 is 2^-6)
+    const uint32_t sub = uint32_t(__builtin_rintf(__uint_as_float(a) * 512.0f));
+    // normal: exponent in [-6, 8]; keep 3 of 23 mantissa bits, round half to
+    // even; a carry out of the mantissa steps the exponent (e * 8 + 8)
+    const uint32_t e = (a >> 23) - 127u + 7u;             // biased E4M3 exponent, 1..15
+    const uint32_t mant = a & 0x7FFFFFu;
+    const uint32_t q = mant >> 20;
     const uint32_t rem = mant & 0xFFFFFu;
-    q += (rem > 0x80000u || (rem == 0x80000u && (q & 1u))) ? 1u : 0u;
-    if (q == 8u) { q = 0u; e += 1u; }
-    return sign | (e << 3) | q;                           // |y| < 448 keeps this <= 0x7E
+    const uint32_t nrm = (e << 3) + q + ((rem > 0x80000u || (rem == 0x80000u && (q & 1u))) ? 1u : 0u);
+    const uint32_t r = a >= 0x43E00000u ? 0x7Eu : (a < 0x3C800000u ? sub : nrm);   // |y| >= 448 (or NaN)
+    return sign | r;                                      // |y| < 448 keeps this <= 0x7E
 }
 
 // E4M3FN -> fp32 (NaN code never produced by the encoder).
@@ -46,19 +46,15 @@ __device__ __forceinline__ float e4m3fn_to_f32(uint32_t c) {
 }
 
 // fp32 -> E2M1 nibble (sign in bit 3): thresholds at the midpoints of the
-// grid, a tie goes to the neighbour with an even code.
+// grid, a tie goes to the neighbour with an even code.  The code counts the
+// thresholds |y| passes: above 0.25, from 0.75, above 1.25, from 1.75, above
+// 2.5, from 3.5, above 5; NaN passes all of them (6.0, as a saturation).
 __device__ __forceinline__ uint32_t f32_to_e2m1(float y) {
     const uint32_t sign = (__float_as_uint(y) >> 28) & 8u;
     const float a = __builtin_fabsf(y);
-    uint32_t c;
-    if (a <= 0.25f) c = 0;         // tie 0.25 -> 0 (code 0)
-    else if (a < 0.75f) c = 1;     // 0.5
-    else if (a <= 1.25f) c = 2;    // tie 0.75 -> 1.0 (code 2); tie 1.25 -> 1.0
-    else if (a < 1.75f) c = 3;     // 1.5
-    else if (a <= 2.5f) c = 4;     // tie 1.75 -> 2.0; tie 2.5 -> 2.0
-    else if (a < 3.5f) c = 5;      // 3.0
-    else if (a <= 5.0f) c = 6;     // tie 3.5 -> 4.0; tie 5 -> 4.0
-    else c = 7;                    // 6.0 and saturation
+    const uint32_t c = uint32_t(!(a <= 0.25f)) + uint32_t(!(a < 0.75f)) + uint32_t(!(a <= 1.25f)) +
+                       uint32_t(!(a < 1.75f)) + uint32_t(!(a <= 2.5f)) + uint32_t(!(a < 3.5f)) +
+                       uint32_t(!(a <= 5.0f));
     return sign | c;
 }
 

@@ -876,7 +876,7 @@ hipError_t launch_decode_plan(const PoolView& pv, int B, int Hq, const int32_t* 
 }
 
 bool decode_append_supported(const PoolView& pv, int B, int Hq) {
-    return pv.H > 0 && Hq % pv.H == 0 && stream_path(pv, B, Hq / pv.H);
+    return pv.H > 0 && Hq % pv.H == 0 && (stream_path(pv, B, Hq / pv.H) || qstream_path(pv, B, Hq / pv.H));
 }
 
 hipError_t launch_decode_run(const PoolView& pv, int B, int Hq, int max_seq_len, const void* q, float sm_scale,

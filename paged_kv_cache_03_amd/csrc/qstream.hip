@@ -35,6 +35,14 @@
 //    writes into its own LDS stage and reads back four bytes at a time, and
 //    the INT8-G64 / FP8-row scales of a 16-lane row's four keys come as one
 //    4-byte load per lane, each scale then broadcast within the row.
+//
+// With the step's rows (decode that appends): the wave that will load row r
+// of a page quantizes the new row that lands there (codec_write.h, the append
+// kernel's arithmetic) and stores it before it issues that page's loads.
+// Rows 16w .. 16w + 15 of every plane of a page reach the products only
+// through wave w's loads, and the vector memory operations of one wave take
+// effect in issue order, so the wave's later loads of the page read the new
+// row.
 
 #include <hip/hip_runtime.h>
 
@@ -43,6 +51,7 @@
 #include <type_traits>
 
 #include "attn_common.h"
+#include "codec_write.h"
 #include "decode_common.h"
 #include "internal.h"
 #include "launch.h"
@@ -260,6 +269,8 @@ __global__ void __launch_bounds__(256, (qstream_bpc<D, KC>())) paged_qstream_ker
     const int nseg = ld_uniform(P, H_NSEG), zero = ld_uniform(P, H_ZERO);
     const int npg = ld_uniform(P, off_blk(H) + 4 * size_t(i_blk));
     int sig = ld_uniform(P, off_blk(H) + 4 * size_t(i_blk) + 1);   // unit being computed
+    const bool append = a.k_new != nullptr;
+    const int npatch = append ? ld_uniform(P, off_blk(H) + 4 * size_t(i_blk) + 2) : 0;   // > 0: new rows here
     {
         static_assert(kMaxEnt * kEntWords <= NT && kMaxSeg * kSegWords <= NT && kMaxEnt * kMaxH <= 2 * NT, "tables");
         const int2* pl = reinterpret_cast<const int2*>(P + off_pages(H, G)) + size_t(i_blk) * a.qcap;
@@ -311,15 +322,129 @@ __global__ void __launch_bounds__(256, (qstream_bpc<D, KC>())) paged_qstream_ker
     };
     auto unit_seg = [&](int sg) __attribute__((always_inline)) { return sg / H; };
 
+    char* kcp = static_cast<char*>(a.pv.lv.k_code);
+    char* vcp = static_cast<char*>(a.pv.lv.v_code);
+    char* ksp = static_cast<char*>(a.pv.lv.k_scale);
+    char* vsp = static_cast<char*>(a.pv.lv.v_scale);
+
+    // the step's rows: the pages of the block's list that hold an entry's new
+    // token (position keys - 1) carry kPatchBit; the unit of page f is the
+    // block's first unit plus the unit ends before f.  A row goes in before
+    // the loads of its page by the wave that owns the row (see the top of the
+    // file).  Every wave scans the whole list in the same order, so all number
+    // the block's rows alike.  Row j (kRows of them at most) is quantized while
+    // the first page is in flight, its K side by wave 2j % 4 and its V side by
+    // wave (2j + 1) % 4, and handed over through mbuf (free until the first
+    // unit ends); after the prologue's barrier its owner stores it.  A row
+    // whose page is among the first PF - 1 pages, and rows past kRows, are
+    // written by their owner during the scan.
+    constexpr int EPL = D / 64;
+    constexpr int kRows = 8;                       // rows handed over through mbuf: 4 x 64 words each
+    constexpr int kHeld = kRows / 2;               // sides one wave quantizes
+    static_assert(kRows * 4 * 64 <= 4 * 16 * 64, "hand-over space");
+    __shared__ long long row_slot[kRows];          // plane row of hand-over row j
+    __shared__ int row_owner[kRows];               // and the wave that stores it
+    const bool vside = (w & 1) != 0;               // the side this wave quantizes: K (even waves) or V
+    int nrows = 0;                                 // rows handed over (the same in every wave)
+    int nheld = 0;                                 // this wave's sides to quantize
+    int hrow[kHeld];                               // their (entry, KV head) rows of k_new / v_new
+    int hidx[kHeld];                               // and their hand-over numbers
+#pragma unroll
+    for (int j = 0; j < kHeld; ++j) {
+        hrow[j] = 0;
+        hidx[j] = 0;
+    }
+    if (append && npatch > 0) {
+        // entry keys and segment masks in registers (lane b: entry b, lane s: segment s)
+        const int ekeys = lane < a.B ? ent_s[lane][E_KEYS] : 0;
+        const int smask = lane < kMaxSeg ? seg_s[lane][S_MASK] : 0;
+        int unit0 = sig;                           // unit of page c0
+        for (int c0 = 0; c0 < npg; c0 += 64) {
+            const int fi = c0 + lane;
+            const int2 pi = fi < npg ? pinfo[fi] : make_int2(-1, 0);
+            const uint64_t ends = __builtin_amdgcn_ballot_w64((pi.y & 256) != 0);
+            uint64_t todo = __builtin_amdgcn_ballot_w64((pi.y & kPatchBit) != 0);
+            const int sg_l = unit0 + int(__builtin_popcountll(ends & ((uint64_t(1) << lane) - 1)));
+            while (todo) {
+                const int k = int(__builtin_ctzll(todo));
+                todo &= todo - 1;
+                const int sg = __builtin_amdgcn_readlane(sg_l, k), meta = __builtin_amdgcn_readlane(pi.y, k);
+                const int sl = __builtin_amdgcn_readlane(pi.x, k);
+                const int s = unit_seg(sg), h = sg - s * H, pgi = (meta >> 9) & 0x7fff;
+                const int mask = __builtin_amdgcn_readlane(smask, s);
+                uint64_t ents = __builtin_amdgcn_ballot_w64(lane < a.B && ((mask >> lane) & 1) && ekeys > 0 &&
+                                                            ((ekeys - 1) >> kPageShift) == pgi && sl >= 0);
+                while (ents) {
+                    const int b = int(__builtin_ctzll(ents));
+                    ents &= ents - 1;
+                    const int r = (__builtin_amdgcn_readlane(ekeys, b) - 1) & (kPage - 1);
+                    const size_t slot = size_t(sl) * kPage + r;
+                    if (c0 + k >= PF - 1 && nrows < kRows) {
+                        const int j = nrows++;
+                        if (((2 * j) & 3) == w && lane == 0) {   // the K side's wave records it
+                            row_slot[j] = (long long)slot;
+                            row_owner[j] = r >> 4;
+                        }
+                        if (((2 * j + (vside ? 1 : 0)) & 3) == w) {
+#pragma unroll
+                            for (int t = 0; t < kHeld; ++t)
+                                if (t == nheld) {
+                                    hrow[t] = b * H + h;
+                                    hidx[t] = j;
+                                }
+                            ++nheld;
+                        }
+                        continue;
+                    }
+                    if ((r >> 4) != w) continue;   // its owner writes it now
+                    float kx[EPL], vx[EPL];
+                    row_floats<EPL>(load_row_bits<EPL>(a.k_new + (size_t(b) * H + h) * D, lane), kx);
+                    row_floats<EPL>(load_row_bits<EPL>(a.v_new + (size_t(b) * H + h) * D, lane), vx);
+                    store_side<D, KC, SB>(kcp, ksp, slot, quantize_side<D, KC, SB>(kx, lane), lane);
+                    store_side<D, VC, SB>(vcp, vsp, slot, quantize_side<D, VC, SB>(vx, lane), lane);
+                }
+            }
+            unit0 += int(__builtin_popcountll(ends));
+        }
+        asm volatile("" ::: "memory");             // the page loads stay after these stores
+    }
+    uint2 hx[kHeld];                               // the sides' bf16 bits
+    const uint16_t* const xnew = vside ? a.v_new : a.k_new;
+#pragma unroll
+    for (int j = 0; j < kHeld; ++j) {
+        hx[j] = make_uint2(0u, 0u);
+        if (j < nheld) hx[j] = load_row_bits<EPL>(xnew + size_t(hrow[j]) * D, lane);
+    }
+    uint32_t* const hand = reinterpret_cast<uint32_t*>(mbuf);   // [row][K code, K scale, V code, V scale][lane]
+    auto quantize_held = [&]() __attribute__((always_inline)) {
+#pragma unroll
+        for (int j = 0; j < kHeld; ++j) {          // fixed indices: the rows stay in registers
+            if (j >= nheld) continue;
+            float x[EPL];
+            row_floats<EPL>(hx[j], x);
+            const RowCode rc = vside ? quantize_side<D, VC, SB>(x, lane) : quantize_side<D, KC, SB>(x, lane);
+            uint32_t* const o = hand + hidx[j] * 256 + (vside ? 128 : 0) + lane;
+            o[0] = rc.code;
+            o[64] = rc.scale;
+        }
+    };
+    auto store_owned = [&]() __attribute__((always_inline)) {
+#pragma unroll 1
+        for (int j = 0; j < nrows; ++j) {
+            if (row_owner[j] != w) continue;
+            const uint32_t* const o = hand + j * 256 + lane;
+            const size_t slot = size_t(row_slot[j]);
+            store_side<D, KC, SB>(kcp, ksp, slot, RowCode{o[0], o[64]}, lane);
+            store_side<D, VC, SB>(vcp, vsp, slot, RowCode{o[128], o[192]}, lane);
+        }
+        asm volatile("" ::: "memory");             // the page loads stay after these stores
+    };
+
     // page buffers: this wave's K code units and scales, V code words and
     // scales.  Buffer loads whose range ends at the page's last visible row:
     // codes and scales past it (stale bytes, possibly NaN) come back as zeros.
     //  K operand, group g: key 16w + li, dims 64g + 16lg .. +15
     //  accumulator register r: key tk(r) = 16w + 4lg + r (score row 4lg + r)
-    char* kcp = static_cast<char*>(a.pv.lv.k_code);
-    char* vcp = static_cast<char*>(a.pv.lv.v_code);
-    char* ksp = static_cast<char*>(a.pv.lv.k_scale);
-    char* vsp = static_cast<char*>(a.pv.lv.v_scale);
     const int kq = 16 * w + li, tk0 = 16 * w + 4 * lg;
     u32x4 kbuf[PF][NU];                            // K units (NVFP4: words 0-1)
     u32x4 ksbuf[KF4 ? PF : 1][NKS4];               // NVFP4 K scales: key kq's row
@@ -410,9 +535,11 @@ __global__ void __launch_bounds__(256, (qstream_bpc<D, KC>())) paged_qstream_ker
     }
 #pragma unroll
     for (int k = 0; k < PF - 1; ++k) load_page(k, k);
+    if (nheld > 0) quantize_held();
 #pragma unroll
     for (int k = 0; k < QCHUNKS / NT; ++k) qcache[k * NT + tid] = qv[k];
     block_lds_barrier();
+    if (nrows > 0) store_owned();
 
     typedef const u32x4 __attribute__((address_space(1)))* glb_q_cptr;
     bf16x8_t qb[D / 32];                           // Q^T operand: column li, dims 64(c/2) + 16lg + 8(c%2) .. +7

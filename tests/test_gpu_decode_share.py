@@ -10,8 +10,9 @@ compare with the fp64 oracle, and with the same histories in private pages
 split must give exactly the one-call result on every layer, and a run on a
 plan of another batch shape must mark its outputs (NaN).  A run that appends
 the step's rows itself must leave the same planes and outputs, bit for bit, as
-kv_append followed by a run, also when a block holds more new-token pages
-than it stages.  Bar: max-abs 2e-3.
+kv_append followed by a run, on BF16 pages (also when a block holds more
+new-token pages than it stages) and on every quantized profile (also when a
+block writes many new rows).  Bar: max-abs 2e-3.
 """
 
 import numpy as np
@@ -163,6 +164,32 @@ def test_decode_append_run_matches_append_then_run(gq, D):
     wl = workloads.small(130 + gq + D, "BF16", hist=hist, fork=fork, C=6, S=4096, Hq=2 * gq, H=2, D=D, layers=2)
     say(f"append in the run gq={gq} D={D}")
     _append_run_case(wl, f"gq={gq} D={D}")
+
+
+@pytest.mark.parametrize("profile,gq,D,sb", [("INT8_G64", 4, 128, 4), ("INT8_G64", 2, 64, 4), ("INT8_G64", 8, 256, 4),
+                                           ("FP8_E4M3FN_ROW256", 4, 128, 4), ("FP8_E4M3FN_ROW256", 1, 64, 4), ("NVFP4_G16", 4, 128, 4),
+                                           ("NVFP4_G16", 2, 256, 4), ("K8V4", 8, 256, 4), ("K8V4", 4, 128, 4),
+                                           ("INT8_G64", 4, 128, 2), ("K8V4", 8, 256, 2)])
+def test_decode_append_run_quantized(profile, gq, D, sb):
+    # the quantized stream writes the step's rows itself (the append kernel's
+    # codec) before it loads their pages: planes and outputs bit for bit as
+    # kv_append + decode_run; forks, new tokens at page starts, mid-page and
+    # page ends, some in a fresh page
+    wl = workloads.small(140 + gq + D + sb, profile, hist=TREE_HIST, fork=TREE_FORK, C=6, S=4096, Hq=2 * gq, H=2,
+                         D=D, layers=2, scale_bytes=sb, outlier_frac=0.01 if profile == "INT8_G64" else 0.0)
+    say(f"append in the quantized run {profile} gq={gq} D={D} scale bytes {sb}")
+    _append_run_case(wl, f"{profile} gq={gq} D={D} sb={sb}")
+
+
+@pytest.mark.parametrize("profile,D", [("INT8_G64", 128), ("K8V4", 256)])
+def test_decode_append_run_quantized_many_new_rows_in_a_block(profile, D):
+    # seven short entries and one long one over 16 KV heads: the short
+    # entries' 112 one-page units share the first blocks' ranges, so a block
+    # writes many new rows, in every wave
+    hist = [10, 63, 0, 40, 1, 62, 30, 66000]
+    wl = workloads.small(141, profile, hist=hist, C=8, S=66048, Hq=16, H=16, D=D)
+    say(f"append in the quantized run, many new rows per block, {profile} D={D}")
+    _append_run_case(wl, f"{profile} many new rows")
 
 
 @pytest.mark.parametrize("D", [128, 256])

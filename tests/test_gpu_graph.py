@@ -5,8 +5,8 @@ advance (one of them across a page boundary, the new page mapped and published
 before the replay), queries and the step's rows change, and eager work runs
 between replays.  Every replay equals an eager step on the same inputs bit for
 bit (the same kernels on the same data) and the oracle within max-abs 2e-3;
-block tables stay bit-exact.  BF16 pages take the append inside the run,
-INT8-G64 pages kv_append + run.
+block tables stay bit-exact.  The step appends its rows inside the run (BF16,
+INT8-G64 and K8V4 pages) or through kv_append + run (INT8-G64 pages).
 """
 
 import numpy as np
@@ -23,8 +23,8 @@ pytestmark = pytest.mark.gpu
 TOL = 2e-3
 
 
-@pytest.mark.parametrize("profile", ["BF16", "INT8_G64"])
-def test_step_graph_replays_match_eager_and_oracle(profile):
+@pytest.mark.parametrize("profile,fused", [("BF16", True), ("INT8_G64", False), ("INT8_G64", True), ("K8V4", True)])
+def test_step_graph_replays_match_eager_and_oracle(profile, fused):
     import torch
     from paged_kv_cache_03_amd.device_pool import i32
     H, gq, D, layers = 2, 4, 128, 3
@@ -45,7 +45,6 @@ def test_step_graph_replays_match_eager_and_oracle(profile):
     out_e = [torch.empty_like(o) for o in out_g]
     msl = wl.S                                   # fixed bound: the grid does not change between replays
     ws = dp.workspace(B, Hq, msl)
-    fused = profile == "BF16"
 
     def eager(outs):
         dp.decode_plan(Hq, rows_t, lens_t, msl, ws)
@@ -56,7 +55,7 @@ def test_step_graph_replays_match_eager_and_oracle(profile):
                 dp.append(l, rows_t, pos0_t, cu_t, B, kbuf[l], vbuf[l])
                 dp.decode_run(l, B, Hq, msl, qbuf[l], wl.sm_scale, outs[l], ws)
 
-    # BF16: the append inside the run (no positions); INT8-G64: kv_append with positions
+    # fused: the append inside the run (no positions); otherwise kv_append with positions
     g = dp.step_graph(B, Hq, rows_t, lens_t, msl, qbuf, wl.sm_scale, out_g, ws, ks=kbuf, vs=vbuf,
                       pos0=None if fused else pos0_t, cu=None if fused else cu_t)
     r = rng_for(9300, 1)
@@ -163,11 +162,12 @@ def test_step_graph_kv_append_form_with_ragged_rows():
 
 
 def test_step_graph_fused_form_refuses_what_it_cannot_take():
-    # no positions asks for the append inside the run: INT8-G64 pages have none
+    # no positions asks for the append inside the run: NVFP4 pages at head_dim
+    # 64 decode on the split kernel, which has none
     import torch
     from paged_kv_cache_03_amd.device_pool import i32
     from paged_kv_cache_03_amd import _abi as abi
-    wl = workloads.small(132, "INT8_G64", hist=[100, 200], step=[1, 1], C=2, S=512, Hq=8, H=2, D=128)
+    wl = workloads.small(132, "NVFP4_G16", hist=[100, 200], step=[1, 1], C=2, S=512, Hq=8, H=2, D=64)
     dp, _, step_inputs = build_device(wl)
     dev = dp.device
     rows_t, lens_t = i32(wl.table_rows, dev), i32(wl.seq_lens, dev)
