@@ -87,15 +87,16 @@ namespace {
 // unit.  The task lists its pieces (the (block, unit) partials of the entry's
 // units in segment order, each unit's slots in block order): a fixed order,
 // so the result does not depend on timing.  Every lane folds two consecutive
-// outputs of one column over all pieces, CMAX pieces per memory round; the
-// task record and its first CMAX piece ids are read with scalar loads in the
-// same round trip as the header.
+// outputs of one column over all pieces, CMAX pieces per memory round (32:
+// the longest (entry, head) of a 32K-token batch has about 20 pieces, so one
+// round covers it); the task record and its first CMAX piece ids are read
+// with scalar loads in the same round trip as the header.
 constexpr int kCombineOut = 128;
 
 template <int D, int GQ, int NCOL>
 __global__ void __launch_bounds__(64) stream_combine_kernel(DecodeArgs a) {
     using namespace plan;
-    constexpr int CMAX = 16;
+    constexpr int CMAX = 32;
     const int lane = int(threadIdx.x) & 63;
     const int H = a.pv.H;
     const int tg = int(blockIdx.x);
@@ -112,6 +113,12 @@ __global__ void __launch_bounds__(64) stream_combine_kernel(DecodeArgs a) {
     for (int kk = 0; kk < CMAX; ++kk) sp[kk] = ld_uniform(rec, T_PIECE + kk);
     const bool run = (magic == kMagic) & (pb == a.B) & (ph == H) & (pgq == GQ) & (t < ntask) &
                      (grp * kCombineOut < ncolb * D);
+    // the piece ids and the partial and output pointers are needed only past
+    // the return below; the compiler would issue their loads there, one more
+    // round trip: these uses keep every scalar load above in one
+#pragma unroll
+    for (int kk = 0; kk < CMAX; ++kk) asm volatile("" ::"s"(sp[kk]));
+    asm volatile("" ::"s"(a.part_ml), "s"(a.part_acc), "s"(a.out));
     if (!run) return;                              // (a plan of another shape: the stream marked the outputs)
     const int32_t* over_list = P + off_over(H, int(a.G));
 
