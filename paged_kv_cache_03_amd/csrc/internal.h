@@ -89,7 +89,7 @@ int stream_plan_blocks(int bound);
 long long stream_bound(const PoolView& pv, int B, int max_seq_len);   // B x H x ceil(max_seq_len / 64)
 hipError_t launch_stream_plan(const PoolView& pv, int B, int gq, const int32_t* table_rows, const int32_t* seq_lens,
                               const int32_t* q_pos0, const int32_t* cu_q, int max_seq_len, int max_cols, bool chunk,
-                              bool dedup, bool pages, int G, int qcap, int32_t* plan, hipStream_t s);
+                              bool dedup, bool pages, int G, int qcap, int share, int32_t* plan, hipStream_t s);
 
 // Decode: a plan of the batch state, then the run (the page stream, or split
 // partials and a combine).  Returns hipErrorNotSupported for shapes with no

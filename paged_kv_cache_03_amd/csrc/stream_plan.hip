@@ -46,6 +46,7 @@ struct PlanArgs {
     int32_t B, gq, max_ctx, max_cols, G, qcap, chunk, emax, pages;
     int32_t D, ncol;          // head dim, partial slot width (columns)
     int32_t nspan;            // blocks that write the page list
+    int32_t share;            // per mille of the stream positions blocks [0, G/2) take (500: an even split)
     int32_t* plan;
 };
 
@@ -64,8 +65,32 @@ struct Div {
     }
 };
 
-// blocks (of Q positions each) that stream positions [start, start + n) touch
-__device__ __forceinline__ int pieces(int start, int n, const Div& dq) { return n > 0 ? dq(start + n - 1) - dq(start) + 1 : 0; }
+// The stream's positions over the blocks.  An even split gives every block
+// ceil(total / G) positions.  Otherwise blocks [0, na), na = G / 2, take qa
+// positions each (share per mille of the stream between them) and the others
+// qb; paged_attn_workspace_bytes sizes the page list for the larger of the two.
+struct Split {
+    int na, qa, qb, ua;                            // ua: positions of blocks [0, na)
+    Div da, db;
+    __device__ __forceinline__ Split(int total, int G, int share) : na(0), qa(0), qb(0), ua(0), da(1), db(1) {
+        na = (share != 500 && G >= 2) ? G / 2 : 0;
+        qa = na > 0 ? int((static_cast<long long>(total) * share + 1000LL * na - 1) / (1000LL * na)) : 0;
+        ua = min(total, na * qa);
+        qb = G - na > 0 ? (total - ua + (G - na) - 1) / (G - na) : 0;
+        da = Div(qa);
+        db = Div(qb);
+    }
+    __device__ __forceinline__ int block(int u) const { return u < ua ? da(u) : na + db(u - ua); }
+    __device__ __forceinline__ int start(int i) const { return i < na ? i * qa : ua + (i - na) * qb; }
+    __device__ __forceinline__ int count(int i, int total) const {
+        return max(0, min(i < na ? qa : qb, total - start(i)));
+    }
+};
+
+// blocks that stream positions [start, start + n) touch
+__device__ __forceinline__ int pieces(int start, int n, const Split& sp) {
+    return n > 0 ? sp.block(start + n - 1) - sp.block(start) + 1 : 0;
+}
 
 __global__ void __launch_bounds__(kNT) stream_plan_kernel(PlanArgs a) {
     __shared__ int ent[kMaxEnt][kEntWords];
@@ -306,8 +331,8 @@ __global__ void __launch_bounds__(kNT) stream_plan_kernel(PlanArgs a) {
     block_lds_barrier();
 
     const int nseg = res_s[0], total = res_s[2];
-    const int Q = total > 0 ? (total + a.G - 1) / a.G : 0;
-    const Div dq(Q);
+    const Split dq(total, a.G, a.share);
+    const int Q = max(dq.qa, dq.qb);               // most positions of a block
     // unit (segment s, head h) and page within it of stream position u
     auto locate = [&](int u, int& s, int& h, int& pp) __attribute__((always_inline)) {
         s = 0;                                     // binary search: last segment with S_PRE <= u
@@ -333,7 +358,7 @@ __global__ void __launch_bounds__(kNT) stream_plan_kernel(PlanArgs a) {
             const int s = y / H, h = y - s * H;
             const int n = seg[s][S_N], start = seg[s][S_PRE] + h * n;
             upc[y] = pieces(start, n, dq);
-            ufirst[y] = dq(start);
+            ufirst[y] = dq.block(start);
         }
         block_lds_barrier();
         int smask[kMaxSeg];
@@ -488,7 +513,7 @@ __global__ void __launch_bounds__(kNT) stream_plan_kernel(PlanArgs a) {
                     if (!((seg[s][S_MASK] >> b) & 1) || p < seg[s][S_P0] || p >= seg[s][S_P0] + seg[s][S_N])
                         continue;
                     const int u = seg[s][S_PRE] + h * seg[s][S_N] + (p - seg[s][S_P0]);
-                    const int i = dq(u), o = u - i * Q;
+                    const int i = dq.block(u), o = u - dq.start(i);
                     const int k = atomicAdd(&pcnt[i], 1);
                     if (k < maxp) plist[size_t(i) * kMaxPatch + k] = o | (b << 12) | (h << 15) | (((keys - 1) & 63) << 21);
                     break;
@@ -498,8 +523,8 @@ __global__ void __launch_bounds__(kNT) stream_plan_kernel(PlanArgs a) {
         }
         int4* blk = reinterpret_cast<int4*>(P + off_blk(H));
         for (int i = tid; i < a.G; i += kNT) {
-            const int u0 = i * Q;
-            const int npg = Q > 0 ? max(0, min(Q, total - u0)) : 0;
+            const int u0 = dq.start(i);
+            const int npg = dq.count(i, total);
             int s = 0, h = 0, pp = 0;
             if (npg > 0) locate(u0, s, h, pp);
             blk[i] = make_int4(npg, s * H + h, min(pcnt[i], maxp), 0);
@@ -545,8 +570,8 @@ __global__ void __launch_bounds__(kNT) stream_plan_kernel(PlanArgs a) {
                 sl[k] = h;
                 const int lim = min(kPage, maxk - p * kPage);
                 meta[k] = lim | (pp == n - 1 ? 256 : 0) | (p << 9) | patch;
-                const int i = dq(u);
-                dst[k] = i * a.qcap + (u - i * Q);
+                const int i = dq.block(u);
+                dst[k] = i * a.qcap + (u - dq.start(i));
             }
         }
 #pragma unroll
@@ -564,7 +589,7 @@ int stream_plan_blocks(int bound) { return bound > 0 ? (bound + kPlanSpan - 1) /
 
 hipError_t launch_stream_plan(const PoolView& pv, int B, int gq, const int32_t* table_rows, const int32_t* seq_lens,
                               const int32_t* q_pos0, const int32_t* cu_q, int max_seq_len, int max_cols, bool chunk,
-                              bool dedup, bool pages, int G, int qcap, int32_t* plan, hipStream_t s) {
+                              bool dedup, bool pages, int G, int qcap, int share, int32_t* plan, hipStream_t s) {
     PlanArgs a{};
     a.table = pv.table;
     a.L = pv.L;
@@ -589,6 +614,7 @@ hipError_t launch_stream_plan(const PoolView& pv, int B, int gq, const int32_t* 
     a.pages = pages ? 1 : 0;
     a.D = pv.D;
     a.ncol = chunk ? 32 : 16;
+    a.share = share;
     a.plan = plan;
     const long long bound = (long long)B * pv.H * ((max_seq_len + kPage - 1) / kPage);
     a.nspan = pages ? stream_plan_blocks(int(bound)) : 0;
