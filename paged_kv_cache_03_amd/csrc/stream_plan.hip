@@ -9,9 +9,10 @@
 // Every block of the launch derives the same entry, sharing and segment
 // tables (one lane per entry of wave 0), then does one job: block k < nspan
 // writes its share of the page list (stream positions [k * kPlanSpan,
-// (k + 1) * kPlanSpan)); three more blocks write, in parallel, the header,
-// tables and piece counts; the combine tasks with their piece lists; the
-// new-token lists and the per-block ranges.  Shared runs
+// (k + 1) * kPlanSpan)); the blocks after them write, in parallel, the
+// header, tables and piece counts; the combine tasks with their piece lists
+// (kTaskBlocks blocks, every kTaskBlocks-th task each); the new-token lists
+// and the per-block ranges.  Shared runs
 // are found by comparing table entries, so a plan is exact for any table: two
 // entries read a page once only where both rows hold the same mapped page
 // group.  The kernel reads only its inputs from global memory and never reads
@@ -34,6 +35,7 @@ using namespace plan;
 constexpr int kPlanSpan = 1024;   // stream positions per plan block
 constexpr int kMaxStreamBlocks = 4096;
 constexpr int kNT = 256;
+constexpr int kTaskBlocks = 4;    // blocks that write the combine tasks
 
 struct PlanArgs {
     const int32_t* table;   // [C][L]
@@ -182,8 +184,12 @@ __global__ void __launch_bounds__(kNT) stream_plan_kernel(PlanArgs a) {
                 const int idx = base + kNT * k;
                 pr[k] = -1;
                 if (idx < tot) {
+                    // the pair whose range holds idx: last c with cpre[c] <= idx
+                    // (cpre increases strictly; n <= 28 pairs)
                     int c = 0;
-                    while (c + 1 < n && cpre[c + 1] <= idx) ++c;
+#pragma unroll
+                    for (int step = 16; step > 0; step >>= 1)
+                        if (c + step < n && cpre[c + step] <= idx) c += step;
                     const int i = cand[c] >> 3, j = cand[c] & 7;
                     pp[k] = 1 + idx - cpre[c];
                     pr[k] = cand[c];
@@ -295,6 +301,12 @@ __global__ void __launch_bounds__(kNT) stream_plan_kernel(PlanArgs a) {
         const int nseg_all = __builtin_amdgcn_readlane(sbase, 7), pages_all = __builtin_amdgcn_readlane(pbase, 7);
         sbase -= nown;
         pbase -= pages;
+        int ekeys[kMaxEnt], elim[kMaxEnt];           // keys, and the causal limit of the entry's column
+#pragma unroll
+        for (int b = 0; b < kMaxEnt; ++b) {
+            ekeys[b] = ent[b][E_KEYS];
+            elim[b] = min(ent[b][E_N0] + 1, ekeys[b]);
+        }
         if (owner) {
             int si = sbase, pre = pbase * H;
 #pragma unroll
@@ -306,8 +318,8 @@ __global__ void __launch_bounds__(kNT) stream_plan_kernel(PlanArgs a) {
                 for (int b = 0; b < kMaxEnt; ++b)
                     if (hi[b] > lo[b] && lo[b] <= c0 && c1 <= hi[b]) {
                         mask |= 1 << b;
-                        maxk = max(maxk, ent[b][E_KEYS]);
-                        kmin = min(kmin, min(ent[b][E_N0] + 1, ent[b][E_KEYS]));
+                        maxk = max(maxk, ekeys[b]);
+                        kmin = min(kmin, elim[b]);
                     }
                 seg[si][S_OWNER] = lane;
                 seg[si][S_P0] = c0;
@@ -345,15 +357,17 @@ __global__ void __launch_bounds__(kNT) stream_plan_kernel(PlanArgs a) {
     };
 
     int32_t* P = a.plan;
-    // Roles: blocks [0, nspan) write the page list (span blockIdx.x); block
-    // nspan the header, the entry and segment tables and the piece counts;
-    // nspan + 1 the combine tasks; nspan + 2 the new-token lists and the
-    // per-block ranges.  Without a page list one block writes the tables.
+    // Roles: blocks [0, nspan) write the page list (span blockIdx.x; role < 0);
+    // block nspan the header, the entry and segment tables and the piece
+    // counts (role 0); the next kTaskBlocks blocks the combine tasks (roles
+    // 1 .. kTaskBlocks); the last the new-token lists and the per-block
+    // ranges.  Without a page list one block writes the tables.
+    constexpr int kRoleBlk = kTaskBlocks + 1;
     const int role = a.pages ? int(blockIdx.x) - a.nspan : 0;
-    // roles 0 and 1: pieces (block, unit) of every unit (s, h), its first
-    // block, then the pieces carrying each (entry, KV head) x into ex
+    // roles 0 .. kTaskBlocks: pieces (block, unit) of every unit (s, h), its
+    // first block, then the pieces carrying each (entry, KV head) x into ex
     __shared__ int upc[kMaxSeg * kMaxH], ufirst[kMaxSeg * kMaxH];
-    if (a.pages && role <= 1) {
+    if (a.pages && role >= 0 && role < kRoleBlk) {
         for (int y = tid; y < nseg * H; y += kNT) {
             const int s = y / H, h = y - s * H;
             const int n = seg[s][S_N], start = seg[s][S_PRE] + h * n;
@@ -401,10 +415,12 @@ __global__ void __launch_bounds__(kNT) stream_plan_kernel(PlanArgs a) {
         if (!a.pages && tid == 0) P[H_NTASK] = 0;
         return;
     }
-    if (role == 1) {
+    if (role >= 1 && role < kRoleBlk) {
         // combine tasks: (entry, KV head) pairs with more than one piece, in
         // pair order; a task lists its pieces in unit order, each unit's
-        // slots in block order
+        // slots in block order.  Every task block numbers all tasks alike and
+        // writes tasks r, r + kTaskBlocks, ... (r = role - 1)
+        const int r = role - 1;
         __shared__ int tpair[kMaxEnt * kMaxH], tpoff[kMaxEnt * kMaxH], tpre[kMaxEnt * kMaxH + 1], ntask_s;
         if (tid < 64) {                            // wave 0: task numbers, piece and overflow offsets
             const int lane = tid;
@@ -437,13 +453,15 @@ __global__ void __launch_bounds__(kNT) stream_plan_kernel(PlanArgs a) {
                 const int x = lane * per + i;
                 if (x >= n || ex[x] <= 1) continue;
                 const int b = x / H, h = x - b * H;
-                int* rec = P + off_tasks(H, a.G) + size_t(tb) * kTaskWords;
-                rec[T_B] = b;
-                rec[T_H] = h;
-                rec[T_E] = ex[x];
-                rec[T_OUT] = (ent[b][E_CU] * H * a.gq + h * a.gq) * a.D;
-                rec[T_NCOL] = ent[b][E_T] * a.gq;
-                rec[T_POFF] = ob;
+                if (tb % kTaskBlocks == r) {
+                    int* rec = P + off_tasks(H, a.G) + size_t(tb) * kTaskWords;
+                    rec[T_B] = b;
+                    rec[T_H] = h;
+                    rec[T_E] = ex[x];
+                    rec[T_OUT] = (ent[b][E_CU] * H * a.gq + h * a.gq) * a.D;
+                    rec[T_NCOL] = ent[b][E_T] * a.gq;
+                    rec[T_POFF] = ob;
+                }
                 tpair[tb] = x;
                 tpoff[tb] = ob;
                 tpre[tb] = ab;
@@ -452,7 +470,7 @@ __global__ void __launch_bounds__(kNT) stream_plan_kernel(PlanArgs a) {
                 ab += ex[x];
             }
             if (lane == 0) {
-                P[H_NTASK] = ntask;
+                if (r == 0) P[H_NTASK] = ntask;
                 ntask_s = ntask;
                 tpre[ntask] = npiece;
             }
@@ -466,9 +484,10 @@ __global__ void __launch_bounds__(kNT) stream_plan_kernel(PlanArgs a) {
         int smask[kMaxSeg];
 #pragma unroll
         for (int s = 0; s < kMaxSeg; ++s) smask[s] = s < nseg ? seg[s][S_MASK] : 0;
-        const int nt = ntask > 0 ? max(1, kNT / ntask) : 1, ngroups = kNT / nt;
+        const int mine = (ntask - r + kTaskBlocks - 1) / kTaskBlocks;   // tasks r, r + kTaskBlocks, ...
+        const int nt = mine > 0 ? max(1, kNT / mine) : 1, ngroups = kNT / nt;
         if (tid / nt < ngroups) {
-            for (int t = tid / nt; t < ntask; t += ngroups) {
+            for (int t = r + kTaskBlocks * (tid / nt); t < ntask; t += kTaskBlocks * ngroups) {
                 const int x = tpair[t], b = x / H, h = x - b * H;
                 const int E = tpre[t + 1] - tpre[t];
                 int c[kMaxSeg];                    // pieces of each segment's unit carrying b
@@ -497,7 +516,7 @@ __global__ void __launch_bounds__(kNT) stream_plan_kernel(PlanArgs a) {
         }
         return;
     }
-    if (role == 2) {
+    if (role == kRoleBlk) {
         // decode: the block that streams the page with an entry's new token
         // (position keys - 1) at head h lists (page, entry, head, row)
         const int maxp = min(kMaxPatch, 1024 / a.D);
@@ -618,7 +637,7 @@ hipError_t launch_stream_plan(const PoolView& pv, int B, int gq, const int32_t* 
     a.plan = plan;
     const long long bound = (long long)B * pv.H * ((max_seq_len + kPage - 1) / kPage);
     a.nspan = pages ? stream_plan_blocks(int(bound)) : 0;
-    stream_plan_kernel<<<dim3(unsigned(pages ? a.nspan + 3 : 1)), kNT, 0, s>>>(a);
+    stream_plan_kernel<<<dim3(unsigned(pages ? a.nspan + kTaskBlocks + 2 : 1)), kNT, 0, s>>>(a);
     return hipGetLastError();
 }
 
