@@ -87,10 +87,14 @@ namespace {
 // unit.  The task lists its pieces (the (block, unit) partials of the entry's
 // units in segment order, each unit's slots in block order): a fixed order,
 // so the result does not depend on timing.  Every lane folds two consecutive
-// outputs of one column over all pieces, CMAX pieces per memory round (32:
-// the longest (entry, head) of a 32K-token batch has about 20 pieces, so one
-// round covers it); the task record and its first CMAX piece ids are read
-// with scalar loads in the same round trip as the header.
+// outputs of one column over all pieces in as few memory rounds as the
+// record allows: the task record and its first CMAX piece ids are read with
+// scalar loads in the same round trip as the header, and the record's other
+// inline ids (one per lane) with a vector load beside them.  A task of at
+// most CMAX pieces (the longest (entry, head) of a 32K-token batch has about
+// 20) takes one round of CMAX; one of up to kTaskInline pieces (a 64K-token
+// entry over fewer heads spans 33-40 blocks) one round of kTaskInline; longer
+// lists continue from the overflow list.
 constexpr int kCombineOut = 128;
 
 template <int D, int GQ, int NCOL>
@@ -111,6 +115,9 @@ __global__ void __launch_bounds__(64) stream_combine_kernel(DecodeArgs a) {
     int sp[CMAX];                                  // the first CMAX piece ids, in the same round trip
 #pragma unroll
     for (int kk = 0; kk < CMAX; ++kk) sp[kk] = ld_uniform(rec, T_PIECE + kk);
+    constexpr int CV = kTaskInline - CMAX;         // the record's other inline ids: lane k holds piece CMAX + k
+    static_assert(CV > 0 && CV <= 64, "inline piece ids");
+    int pid2 = rec[T_PIECE + CMAX + min(lane, CV - 1)];
     const bool run = (magic == kMagic) & (pb == a.B) & (ph == H) & (pgq == GQ) & (t < ntask) &
                      (grp * kCombineOut < ncolb * D);
     // the piece ids and the partial and output pointers are needed only past
@@ -119,6 +126,7 @@ __global__ void __launch_bounds__(64) stream_combine_kernel(DecodeArgs a) {
 #pragma unroll
     for (int kk = 0; kk < CMAX; ++kk) asm volatile("" ::"s"(sp[kk]));
     asm volatile("" ::"s"(a.part_ml), "s"(a.part_acc), "s"(a.out));
+    asm volatile("" : "+v"(pid2));
     if (!run) return;                              // (a plan of another shape: the stream marked the outputs)
     const int32_t* over_list = P + off_over(H, int(a.G));
 
@@ -128,13 +136,14 @@ __global__ void __launch_bounds__(64) stream_combine_kernel(DecodeArgs a) {
     const bool act = e0 < ncolb * D;
     const int c = act ? e0 / D : 0, d0 = act ? e0 % D : 0;
     float fm = -INFINITY, fl = 0.f, fa0 = 0.f, fa1 = 0.f;
-    // one memory round of CMAX pieces (ids from pid_of; pieces from nvalid on
+    // one memory round of N pieces (ids from pid_of; pieces from nvalid on
     // repeat a valid one and get weight 0): every load in flight together,
     // then the fold in piece order
-    auto round = [&](auto pid_of, int nvalid) __attribute__((always_inline)) {
-        float2 ml[CMAX], av[CMAX];
+    auto round = [&](auto n_c, auto pid_of, int nvalid) __attribute__((always_inline)) {
+        constexpr int N = decltype(n_c)::value;
+        float2 ml[N], av[N];
 #pragma unroll
-        for (int kk = 0; kk < CMAX; ++kk) {
+        for (int kk = 0; kk < N; ++kk) {
             const size_t it = size_t(pid_of(kk)) + c;
             ml[kk] = *reinterpret_cast<const float2*>(a.part_ml + it * 2);
             av[kk] = *reinterpret_cast<const float2*>(a.part_acc + it * D + d0);
@@ -144,13 +153,13 @@ __global__ void __launch_bounds__(64) stream_combine_kernel(DecodeArgs a) {
         __builtin_amdgcn_sched_barrier(0);
         float mx = fm;
 #pragma unroll
-        for (int kk = 0; kk < CMAX; ++kk) mx = fmaxf(mx, ml[kk].x);   // repeats change nothing
+        for (int kk = 0; kk < N; ++kk) mx = fmaxf(mx, ml[kk].x);   // repeats change nothing
         const float wp = fm == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(fm - mx);
         fl *= wp;
         fa0 *= wp;
         fa1 *= wp;
 #pragma unroll
-        for (int kk = 0; kk < CMAX; ++kk) {
+        for (int kk = 0; kk < N; ++kk) {
             const float wgt = (kk >= nvalid || ml[kk].x == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(ml[kk].x - mx);
             fl += ml[kk].y * wgt;
             fa0 += av[kk].x * wgt;
@@ -158,18 +167,29 @@ __global__ void __launch_bounds__(64) stream_combine_kernel(DecodeArgs a) {
         }
         fm = mx;
     };
-    // pieces 0 .. CMAX-1 from the scalar ids
-    round([&](int kk) __attribute__((always_inline)) { return kk < E ? sp[kk] : sp[0]; }, E);
+    int w_rest;                                    // first piece past the first round
+    if (E <= CMAX) {                               // the scalar ids
+        round(std::integral_constant<int, CMAX>{},
+              [&](int kk) __attribute__((always_inline)) { return kk < E ? sp[kk] : sp[0]; }, E);
+        w_rest = CMAX;
+    } else {                                       // the scalar ids, then the lanes' inline ids
+        const int nv = min(E, kTaskInline);
+        round(std::integral_constant<int, kTaskInline>{},
+              [&](int kk) __attribute__((always_inline)) {
+                  return kk < CMAX ? sp[kk] : __builtin_amdgcn_readlane(pid2, min(kk - CMAX, nv - CMAX - 1));
+              }, nv);
+        w_rest = kTaskInline;
+    }
     // the rest: lane k holds the id of piece w0 + k
 #pragma unroll 1
-    for (int w0 = CMAX; w0 < E; w0 += 64) {
+    for (int w0 = w_rest; w0 < E; w0 += 64) {
         const int k = w0 + lane;
         int pid = 0;
         if (k < E) pid = k < kTaskInline ? rec[T_PIECE + k] : over_list[poff + k - kTaskInline];
         const int wn = min(64, E - w0);
 #pragma unroll 1
         for (int k0 = 0; k0 < wn; k0 += CMAX)
-            round([&](int kk) __attribute__((always_inline)) {
+            round(std::integral_constant<int, CMAX>{}, [&](int kk) __attribute__((always_inline)) {
                 return __builtin_amdgcn_readlane(pid, min(k0 + kk, wn - 1));
             }, wn - k0);
     }
