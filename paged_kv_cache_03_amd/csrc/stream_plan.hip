@@ -89,6 +89,25 @@ struct Split {
     }
 };
 
+// Inclusive prefix sum over lanes [0, n) of a wave (NL = 8 or 64; every lane
+// of the wave active): shifts within 16-lane rows (data-parallel moves, no
+// LDS round trip), then the rows' totals.  Lanes past n hold sums nothing reads.
+template <int NL>
+__device__ __forceinline__ int wave_scan(int v) {
+    static_assert(NL == 8 || NL == 64, "scan width");
+    v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, false);   // row_shr:1
+    v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, false);   // row_shr:2
+    v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, false);   // row_shr:4
+    if constexpr (NL == 64) {
+        v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, false);   // row_shr:8
+        const int lane = int(__lane_id());
+        const int r0 = __builtin_amdgcn_readlane(v, 15), r1 = __builtin_amdgcn_readlane(v, 31);
+        const int r2 = __builtin_amdgcn_readlane(v, 47);
+        v += (lane >= 16 ? r0 : 0) + (lane >= 32 ? r1 : 0) + (lane >= 48 ? r2 : 0);
+    }
+    return v;
+}
+
 // blocks that stream positions [start, start + n) touch
 __device__ __forceinline__ int pieces(int start, int n, const Split& sp) {
     return n > 0 ? sp.block(start + n - 1) - sp.block(start) + 1 : 0;
@@ -157,15 +176,7 @@ __global__ void __launch_bounds__(kNT) stream_plan_kernel(PlanArgs a) {
             const int i = tid >> 3, j = tid & 7;
             const int c = (j < i && lcp[i][j] > 1) ? 1 : 0;
             const int len = c ? lcp[i][j] - 1 : 0;
-            int pc = c, pl = len;                  // inclusive prefix sums over the lanes
-#pragma unroll
-            for (int d = 1; d < 64; d <<= 1) {
-                const int c1 = __shfl_up(pc, d), l1 = __shfl_up(pl, d);
-                if (tid >= d) {
-                    pc += c1;
-                    pl += l1;
-                }
-            }
+            const int pc = wave_scan<64>(c), pl = wave_scan<64>(len);   // inclusive prefix sums over the lanes
             if (c) {
                 cand[pc - 1] = i << 3 | j;
                 cpre[pc - 1] = pl - len;
@@ -176,30 +187,43 @@ __global__ void __launch_bounds__(kNT) stream_plan_kernel(PlanArgs a) {
             }
         }
         block_lds_barrier();
-        const int n = ncand_s, tot = cpre[n];
-        for (int base = tid; base < tot; base += kNT * 8) {
+        const int n = __builtin_amdgcn_readfirstlane(ncand_s);
+        const int tot = __builtin_amdgcn_readfirstlane(cpre[n]);
+        // every position's lookups run without branches (a position past tot
+        // repeats the last one and is not applied), so the eight of a thread
+        // overlap their LDS and table round trips
+        for (int base0 = 0; base0 < tot; base0 += kNT * 8) {
+            const int base = base0 + tid;
+            const int kn = min(8, (tot - base0 + kNT - 1) / kNT);   // positions per thread this round (uniform)
             int gi[8], gj[8], pr[8], pp[8];
 #pragma unroll
             for (int k = 0; k < 8; ++k) {
-                const int idx = base + kNT * k;
-                pr[k] = -1;
-                if (idx < tot) {
-                    // the pair whose range holds idx: last c with cpre[c] <= idx
-                    // (cpre increases strictly; n <= 28 pairs)
-                    int c = 0;
+                pr[k] = 0;
+                pp[k] = 0;
+                gi[k] = gj[k] = 0;
+                if (k >= kn) continue;
+                const int idx = min(base + kNT * k, tot - 1);
+                // the pair whose range holds idx: last c with cpre[c] <= idx
+                // (cpre increases strictly; n <= 28 pairs; steps past n skipped
+                // as a whole, the others select)
+                int c = 0;
 #pragma unroll
-                    for (int step = 16; step > 0; step >>= 1)
-                        if (c + step < n && cpre[c + step] <= idx) c += step;
-                    const int i = cand[c] >> 3, j = cand[c] & 7;
-                    pp[k] = 1 + idx - cpre[c];
-                    pr[k] = cand[c];
-                    gi[k] = a.table[size_t(ent[i][E_ROW]) * a.L + pp[k]];
-                    gj[k] = a.table[size_t(ent[j][E_ROW]) * a.L + pp[k]];
+                for (int step = 16; step > 0; step >>= 1) {
+                    if (step < n) {
+                        const int cs = c + step, v = cpre[min(cs, n - 1)];
+                        c = (cs < n && v <= idx) ? cs : c;
+                    }
                 }
+                const int pair = cand[c];
+                const int i = pair >> 3, j = pair & 7;
+                pp[k] = 1 + idx - cpre[c];
+                pr[k] = pair;
+                gi[k] = a.table[size_t(ent[i][E_ROW]) * a.L + pp[k]];
+                gj[k] = a.table[size_t(ent[j][E_ROW]) * a.L + pp[k]];
             }
 #pragma unroll
             for (int k = 0; k < 8; ++k)
-                if (pr[k] >= 0 && (gi[k] != gj[k] || gi[k] < 0 || gi[k] >= a.M))
+                if (k < kn && base + kNT * k < tot && (gi[k] != gj[k] || gi[k] < 0 || gi[k] >= a.M))
                     atomicMin(&lcp[pr[k] >> 3][pr[k] & 7], pp[k]);
         }
         block_lds_barrier();
@@ -289,15 +313,7 @@ __global__ void __launch_bounds__(kNT) stream_plan_kernel(PlanArgs a) {
         for (int x = 0; x + 1 < kMaxEnt + 2; ++x) nown += (owner && cut[x + 1] > cut[x]) ? 1 : 0;
         const int pages = owner ? np - ell : 0;
         // exclusive prefix sums over the lanes: segment index, pages
-        int sbase = nown, pbase = pages;
-#pragma unroll
-        for (int d = 1; d < 8; d <<= 1) {
-            const int s1 = __shfl_up(sbase, d), p1 = __shfl_up(pbase, d);
-            if ((lane & 7) >= d) {
-                sbase += s1;
-                pbase += p1;
-            }
-        }
+        int sbase = wave_scan<8>(nown), pbase = wave_scan<8>(pages);   // lanes 0-7 (owners are entries)
         const int nseg_all = __builtin_amdgcn_readlane(sbase, 7), pages_all = __builtin_amdgcn_readlane(pbase, 7);
         sbase -= nown;
         pbase -= pages;
@@ -377,13 +393,18 @@ __global__ void __launch_bounds__(kNT) stream_plan_kernel(PlanArgs a) {
         block_lds_barrier();
         int smask[kMaxSeg];
 #pragma unroll
-        for (int s = 0; s < kMaxSeg; ++s) smask[s] = s < nseg ? seg[s][S_MASK] : 0;
+        for (int s = 0; s < kMaxSeg; ++s) {
+            const int m = seg[s][S_MASK];
+            smask[s] = s < nseg ? m : 0;
+        }
         for (int x = tid; x < kMaxEnt * H; x += kNT) {
             const int b = x / H, h = x - b * H;
-            int e = 0;
+            int e = 0;                             // (every load issued, then selected: one LDS wait)
 #pragma unroll
-            for (int s = 0; s < kMaxSeg; ++s)
-                if ((smask[s] >> b) & 1) e += upc[s * H + h];
+            for (int s = 0; s < kMaxSeg; ++s) {
+                const int v = upc[min(s, max(nseg - 1, 0)) * H + h];
+                e += ((smask[s] >> b) & 1) ? v : 0;
+            }
             ex[x] = x < a.B * H ? e : 0;
         }
         block_lds_barrier();
@@ -434,16 +455,7 @@ __global__ void __launch_bounds__(kNT) stream_plan_kernel(PlanArgs a) {
                     all += ex[x];
                 }
             }
-            int tb = cnt, ob = over, ab = all;     // exclusive prefix sums over the lanes
-#pragma unroll
-            for (int d = 1; d < 64; d <<= 1) {
-                const int t1 = __shfl_up(tb, d), o1 = __shfl_up(ob, d), a1 = __shfl_up(ab, d);
-                if (lane >= d) {
-                    tb += t1;
-                    ob += o1;
-                    ab += a1;
-                }
-            }
+            int tb = wave_scan<64>(cnt), ob = wave_scan<64>(over), ab = wave_scan<64>(all);   // then exclusive:
             const int ntask = __builtin_amdgcn_readlane(tb, 63);
             const int npiece = __builtin_amdgcn_readlane(ab, 63);
             tb -= cnt;
@@ -483,7 +495,10 @@ __global__ void __launch_bounds__(kNT) stream_plan_kernel(PlanArgs a) {
         int* over_list = P + off_over(H, a.G);
         int smask[kMaxSeg];
 #pragma unroll
-        for (int s = 0; s < kMaxSeg; ++s) smask[s] = s < nseg ? seg[s][S_MASK] : 0;
+        for (int s = 0; s < kMaxSeg; ++s) {
+            const int m = seg[s][S_MASK];
+            smask[s] = s < nseg ? m : 0;
+        }
         const int mine = (ntask - r + kTaskBlocks - 1) / kTaskBlocks;   // tasks r, r + kTaskBlocks, ...
         const int nt = mine > 0 ? max(1, kNT / mine) : 1, ngroups = kNT / nt;
         if (tid / nt < ngroups) {
