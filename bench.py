@@ -57,6 +57,14 @@ def fused_append(wl) -> bool:
     return dims and wl.B <= 8 and wl.Hq % wl.H == 0 and gq in (1, 2, 4, 8)
 
 
+def step_append_fused(wl) -> bool:
+    """The step appends inside the run: that call writes one row per entry, at
+    seq_len - 1, so it stands for the step's append only where every entry
+    appends exactly one row; several rows per entry (config 3: 1-64, page
+    crossings included) go through kv_append."""
+    return fused_append(wl) and all(int(t) == 1 for t in wl.step)
+
+
 def source_sha256(paths) -> str:
     import hashlib
     h = hashlib.sha256()
@@ -842,7 +850,7 @@ def main() -> int:
     # block table and the lengths), then per layer the append of the step's
     # rows and the decode run -- one launch on the page streams, which
     # append the rows themselves
-    fused = fused_append(wl)
+    fused = step_append_fused(wl)
 
     def step(events=None, kern=None):
         dp.decode_plan(wl.Hq, rows_t, lens_t, max_ctx, ws)

@@ -37,22 +37,31 @@ __global__ void __launch_bounds__(256) append_kernel(AppendArgs a) {
     const int H = a.pv.H;
     if (r >= a.total * H) return;
     const int t = r / H, h = r - (r / H) * H;
-    // the row's values first (they depend on nothing else), then the entry of
-    // token t: the entries k in [1, B) whose rows start at or before t (the
-    // starts do not decrease), one load per lane and a ballot for B <= 64
+    // the row's values and every entry's row start, position and table row
+    // in one round trip (lane k holds entry k's; they depend on nothing
+    // else), then the entry of token t: the entries k in [1, B) whose rows
+    // start at or before t (the starts do not decrease), by a ballot
     float kx[EPL], vx[EPL];
     uint32_t kb[EPL], vb[EPL];
     load_row<EPL>(a.k + size_t(r) * D, lane, kx, kb);
     load_row<EPL>(a.v + size_t(r) * D, lane, vx, vb);
-    int b = 0;
-    if (a.B <= 64) {
-        const int start = lane < a.B ? a.cu[lane] : 0;     // cu[k]: first row of entry k
+    int b = 0, c0, c1, p0, row;
+    if (a.B < 64) {
+        const int start = lane <= a.B ? a.cu[lane] : 0;    // cu[k]: first row of entry k (cu[B]: the total)
+        const int pz = lane < a.B ? a.pos0[lane] : 0;
+        const int rw = lane < a.B ? a.table_rows[lane] : 0;
         b = __builtin_popcountll(__builtin_amdgcn_ballot_w64(lane >= 1 && lane < a.B && start <= t));
+        c0 = __builtin_amdgcn_readlane(start, b);
+        c1 = __builtin_amdgcn_readlane(start, b + 1);
+        p0 = __builtin_amdgcn_readlane(pz, b);
+        row = __builtin_amdgcn_readlane(rw, b);
     } else {
         while (b + 1 < a.B && t >= a.cu[b + 1]) ++b;
+        c0 = a.cu[b];
+        c1 = a.cu[b + 1];
+        p0 = a.pos0[b];
+        row = a.table_rows[b];
     }
-    const int c0 = a.cu[b], c1 = a.cu[b + 1];
-    const int p0 = a.pos0[b], row = a.table_rows[b];
     if (t < c0 || t >= c1) return;
     const int p = p0 + (t - c0);
     if (p < 0 || row < 0 || row >= a.pv.C) return;

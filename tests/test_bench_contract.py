@@ -7,6 +7,8 @@
   two 256-byte code rows, INT8-G64 D=128 two 128-byte code rows and two
   fp32 scales per side, K8V4 D=256 a 256-byte FP8 row plus one fp32 scale
   (K) and a 128-byte E2M1 row plus sixteen E4M3 scale bytes (V);
+* the append happens inside the decode run only where every entry appends
+  one row (the run writes one row per entry);
 * the committed HBM traffic summaries parse, name their kernel and source
   hash, and stay within a few percent above the algorithmic bytes they were
   measured against (traffic well above them would mean re-reads).  The bound
@@ -68,3 +70,15 @@ def test_traffic_summaries_are_consistent(path):
     assert traffic >= 0.95 * alg, (traffic, alg)
     if alg >= 64e6:
         assert traffic <= 1.10 * alg, (traffic, alg)
+
+
+def test_append_inside_the_run_only_for_one_row_per_entry():
+    # paged_attn_decode_append_run writes one row per entry at seq_len - 1:
+    # the step may stand on it only where every entry appends one row
+    import bench
+    import workloads
+    assert bench.step_append_fused(workloads.get(2))
+    assert bench.step_append_fused(workloads.get(4))
+    wl3 = workloads.get(3)
+    assert sum(wl3.step) > wl3.B
+    assert not bench.step_append_fused(wl3)
