@@ -429,8 +429,8 @@ kv_status paged_attn_verify(const kv_pool* pool, uint32_t layer, uint32_t B, uin
  * caller picks the append's form:
  *   d_pos0 == d_cu_tokens == NULL : paged_attn_decode_append_run(d_k[l],
  *       d_v[l]) -- one row per entry at position seq_len - 1 (total_tokens
- *       == B); BF16 pages on the matrix-core stream only, KV_E_UNSUPPORTED
- *       otherwise;
+ *       == B); the shapes paged_attn_decode_append_run takes,
+ *       KV_E_UNSUPPORTED otherwise;
  *   both set : kv_append(d_pos0, d_cu_tokens, total_tokens) then
  *       paged_attn_decode_run, for any rows and positions.
  * d_k == d_v == NULL: runs only, nothing appended.

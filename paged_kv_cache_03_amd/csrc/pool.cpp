@@ -887,7 +887,7 @@ kv_status paged_attn_decode_append_run(const kv_pool* pool, uint32_t layer, uint
     if (!d_k || !d_v || !d_q || !d_out) return fail(KV_E_INVALID, "null device pointer");
     PoolView pv = pool->view(layer);
     if (!decode_append_supported(pv, int(B), int(Hq)))
-        return fail(KV_E_UNSUPPORTED, "append in the decode run needs the BF16 page stream; use kv_append");
+        return fail(KV_E_UNSUPPORTED, "append in the decode run needs a matrix-core page stream; use kv_append");
     hipError_t e = launch_decode_run(pv, int(B), int(Hq), int(max_seq_len), d_q, sm_scale, d_out, d_ws, stream, d_k,
                                      d_v);
     if (e != hipSuccess) return fail(KV_E_DEVICE, std::string("decode run launch: ") + hipGetErrorString(e));
@@ -948,13 +948,13 @@ kv_status kv_decode_step_graph_create(const kv_pool* pool, uint32_t B, uint32_t 
     const bool append = d_k != nullptr;
     if (append != (d_v != nullptr)) return fail(KV_E_INVALID, "d_k and d_v go together");
     // which append form: without positions, one row per entry at seq_len - 1
-    // inside the run (the BF16 page stream); with them, kv_append + run
+    // inside the run (the matrix-core page streams); with them, kv_append + run
     if ((d_pos0 == nullptr) != (d_cu_tokens == nullptr))
         return fail(KV_E_INVALID, "d_pos0 and d_cu_tokens go together");
     const bool fused = append && !d_pos0;
     if (fused && (total_tokens != B || !decode_append_supported(pool->view(0), int(B), int(Hq))))
         return fail(KV_E_UNSUPPORTED,
-                    "the append inside the run takes one row per entry on the BF16 page stream; "
+                    "the append inside the run takes one row per entry on the matrix-core page streams; "
                     "pass d_pos0 and d_cu_tokens for kv_append");
 
     hipStream_t s = nullptr;

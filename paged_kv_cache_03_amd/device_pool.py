@@ -196,7 +196,7 @@ class DevicePool:
 
     def decode_append_run(self, layer: int, B: int, Hq: int, max_seq_len: int, k: torch.Tensor, v: torch.Tensor,
                           q: torch.Tensor, sm_scale: float, out: torch.Tensor, ws: torch.Tensor) -> None:
-        """Append each entry's step row at seq_len - 1, then decode (BF16 page stream)."""
+        """Append each entry's one step row at seq_len - 1, then decode (the matrix-core page streams)."""
         abi.paged_attn_decode_append_run(self.handle, layer, B, Hq, max_seq_len, ptr(k), ptr(v), ptr(q), sm_scale,
                                          ptr(out), ptr(ws), ws.numel(), self.stream)
 
