@@ -107,3 +107,16 @@ def test_stream_repeated_calls_on_one_workspace():
     ref_sub = A.paged_decode(st, 0, [wl.table_rows[b] for b in sub], sub_lens, wl.q(0)[sub], wl.sm_scale)
     assert float(np.max(np.abs(out.cpu().numpy() - ref_sub))) <= TOL
     dp.close()
+
+
+@pytest.mark.parametrize("profile", ["BF16", "INT8_G64"])
+@pytest.mark.parametrize("npages", [32, 33, 56, 57])
+def test_combine_piece_counts_at_round_edges(profile, npages):
+    # one entry of npages pages at two KV heads: 2 * npages stream positions
+    # over the 512 blocks of the run, one page each, so each (entry, head)
+    # output folds exactly npages pieces -- the combine's rounds end at 32
+    # (scalar ids) and 56 (the record's inline ids); 57 takes the overflow list
+    wl = workloads.small(90 + npages, profile, hist=[64 * npages - 7], C=1, S=4096, Hq=8, H=2, D=128)
+    say(f"decode {profile}: one entry of {npages} pages, {npages} pieces per output")
+    dp, _ = _check(wl, f"{npages} pieces")
+    dp.close()
