@@ -193,6 +193,10 @@ __global__ void __launch_bounds__(512) verify_gtile_kernel(GTileArgs a) {
     constexpr int NGK = KC == CODEC_INT8_G64 ? D / 64 : 1;   // score accumulators: one per K scale group
     constexpr bool VSC = VC == CODEC_INT8_G64 || VC == CODEC_FP8_ROW;
     constexpr int NGV = VC == CODEC_INT8_G64 ? D / 64 : 1;   // copies of P: one per V scale group
+    // the products at raised wave priority for INT8-G64 pages (the prefill
+    // mix on them 2.5% faster over two A/B pairs on one box; K8V4 1% and BF16
+    // at D = 256 4.5% slower, so those keep the default)
+    constexpr bool PRIO = KC == CODEC_INT8_G64;
     constexpr int PLANE = 64 * NCH;                // u32x4 slots of one bf16 page tile
     constexpr int OFF_VH = PLANE;
     constexpr int NPL = 2;
@@ -419,6 +423,7 @@ __global__ void __launch_bounds__(512) verify_gtile_kernel(GTileArgs a) {
                 for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
                     for (int ct = 0; ct < WCT; ++ct) sg[g][kt][ct] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            if constexpr (PRIO) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
             for (int kt = 0; kt < 2; ++kt) {
 #pragma unroll
@@ -431,6 +436,7 @@ __global__ void __launch_bounds__(512) verify_gtile_kernel(GTileArgs a) {
                         sg[g][kt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kk, qb[ct][c], sg[g][kt][ct], 0, 0, 0);
                 }
             }
+            if constexpr (PRIO) __builtin_amdgcn_s_setprio(0);
             if constexpr (KSC) {
                 const float* kst = reinterpret_cast<const float*>(&lds[sb + OFF_KS]);
 #pragma unroll
@@ -530,6 +536,7 @@ __global__ void __launch_bounds__(512) verify_gtile_kernel(GTileArgs a) {
             return __builtin_bit_cast(bf16x8_t, u32x4{hv[0], hv[1], hv[2], hv[3]});
         };
         constexpr int DPG = NDT / NGV;             // PV tiles per V scale group
+        if constexpr (PRIO) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int g = 0; g < NGV; ++g) {
             bf16x8_t pw[WCT];
@@ -583,6 +590,7 @@ __global__ void __launch_bounds__(512) verify_gtile_kernel(GTileArgs a) {
             for (int ct = 0; ct < WCT; ++ct)
                 lsum[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, plo[ct], lsum[ct], 0, 0, 0);
         }
+        if constexpr (PRIO) __builtin_amdgcn_s_setprio(0);
     };
 
     // pages [p0, p1); rows any column may see on page i: lim_of
