@@ -738,17 +738,21 @@ struct WsLayout {
 size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
 // Share (per mille) of the stream positions blocks [0, G/2) take.  The
-// quantized stream runs two blocks on every compute unit, and the block
-// dispatched first (blocks [0, G/2) of the grid: one per compute unit before
-// the second) gets the SIMDs' issue slots first.  With an even split it
-// streamed about 30% faster (per-block timestamps of the BF16 stream show
-// the same split: 40 against 52 us), and the second block then ran alone with
-// half the loads in flight for the last part of the launch.  57% measured best
-// for the quantized stream (INT8-G64 and K8V4 kernels 2.9% faster; 60% and
-// more slower); the BF16 stream measured no different and keeps an even split.
+// streams run two blocks on every compute unit (one at D = 256 for BF16 and
+// INT8-G64), and the block dispatched first (blocks [0, G/2) of the grid: one
+// per compute unit before the second) gets the SIMDs' issue slots first.
+// With an even split it streamed about 30% faster (per-block timestamps of
+// the BF16 stream: 40 against 52 us), and the second block then ran alone
+// with half the loads in flight for the last part of the launch.  57%
+// measured best for the quantized streams (INT8-G64 and K8V4 kernels 2.9%
+// faster; 60% and more slower), 53% for the BF16 stream (config 2 step
+// 0.8-1.0% faster in two sweeps of 52-56% on two boxes; 56% no different).
 // The split fixes which block reads which pages, so results stay independent
 // of timing.
-int stream_share(const PoolView& pv) { return (pv.k_codec != CODEC_BF16 && stream_bpc(pv) == 2) ? 570 : 500; }
+int stream_share(const PoolView& pv) {
+    if (stream_bpc(pv) != 2) return 500;
+    return pv.k_codec != CODEC_BF16 ? 570 : 530;
+}
 
 // page slots a block needs under that split for at most `bound` positions
 int split_qcap(long long bound, int G, int share) {
