@@ -771,6 +771,11 @@ __global__ void __launch_bounds__(256, (qstream_bpc<D, KC>())) paged_qstream_ker
             blo[g] = __builtin_bit_cast(s16x4_t, u32x2{l01, l23});
         }
 
+        // INT8-G64 V: the value products and their operands at raised wave
+        // priority (config 3 kernel 0.8% faster in two A/B pairs on one box;
+        // K8V4 0.8% slower, and the score loop at raised priority slower for
+        // both, so those keep the default)
+        if constexpr (VI8) __builtin_amdgcn_s_setprio(1);
         // PV: O^T[16 dims x 16 columns] += V^T . P_hi^T + V^T . P_lo^T per tile
         auto pv_tile = [&](int dt, uint32_t x01, uint32_t x23, int g) __attribute__((always_inline)) {
             const s16x4_t vt = __builtin_bit_cast(s16x4_t, u32x2{x01, x23});
@@ -823,6 +828,7 @@ __global__ void __launch_bounds__(256, (qstream_bpc<D, KC>())) paged_qstream_ker
                 pv_tile(2 * q + 1, pk_bf16(f[0][1], f[1][1]), pk_bf16(f[2][1], f[3][1]), 0);
             }
         }
+        if constexpr (VI8) __builtin_amdgcn_s_setprio(0);
     };
 
     reset();
